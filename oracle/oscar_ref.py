@@ -1,0 +1,411 @@
+"""Plain CPU oracle for the OSCAR INT2 KV-cache hot path (numpy, fp64).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import or call this
+module: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py`` use it.  It shares no code, table or constant generator with the
+HIP library; the only thing both sides share is the seeded input generator
+(``workloads``), which holds none of the method's arithmetic.
+
+Sources (the text of five web pages about the method; cited below by key):
+
+  P1  gen-hub.ru, "Together AI открывает OSCAR: сжатие KV-кэша до 2 бит без
+      потери точности"
+  P2  encorp.ai, "KV cache compression е инфраструктурно решение, не спор за модела"
+  P3  bigsaas.top, "Revolução no Serviço de LLMs: Together AI Lança OSCAR para
+      Contextos Extensos"
+  P4  aiforradalom.hu, "Az Apple, a Google és a NYU új technikái felezik az
+      LLM-ek memóriaigényét"
+  P5  ru.arsentev.ai, "Гонка за сжатие памяти ИИ на длинном контексте"
+
+The pages describe the method in prose only.  Where they leave a step open the
+plainest reading is taken (each listed in the repository's design notes):
+uncentred second moments; eigenvectors as columns, sorted by descending
+eigenvalue, sign fixed so the largest-magnitude entry of each is positive;
+value weights = total softmax mass each calibration token receives; Sylvester
+Hadamard scaled by 1/sqrt(d); R = P_br . (H/sqrt d) . U^T acting on column
+vectors; one quantisation group = the 128 rotated channels of one token; float
+zero point = group minimum; fp16 RNE for scale and zero; codes rounded half to
+even from the stored fp16 scale/zero, clamped to [0, 3].
+
+Precision.  Rotations, covariances, eigenproblems and attention are fp64.  The
+integer decisions of the encoder (min/max, scale, zero, codes) are taken in
+fp32 arithmetic on the fp32-rounded exact rotation, i.e. in the precision of
+the device encoder, as no precision is fixed by the pages.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_*.py`` against
+closed forms, library routines on special cases, invariants and brute force;
+none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Page-block layout (per page, per KV head, 1152 bytes)
+#   [   0,  512)  K codes: 16 token rows x 32 B; channel c of a row at bit 2c
+#   [ 512, 1024)  V codes: 128 channel words x 4 B; token slot j at bit 2j
+#   [1024, 1056)  K scale fp16[16]     [1056, 1088)  K zero fp16[16]
+#   [1088, 1120)  V scale fp16[16]     [1120, 1152)  V zero fp16[16]
+# Pool = uint8 [n_pages][Hkv][1152].  Window ring = bf16 [B][W][Hkv][d], slot pos % W.
+# bf16 comparator pool = bf16 [n_pages][Hkv][2 (K, V)][16][d].
+# ---------------------------------------------------------------------------
+D = 128
+PAGE = 16
+K_CODES, V_CODES, K_SCALE, K_ZERO, V_SCALE, V_ZERO, BLOCK = 0, 512, 1024, 1056, 1088, 1120, 1152
+
+
+# ---------------------------------------------------------------------------
+# floating-point formats
+# ---------------------------------------------------------------------------
+
+def _round_binary(x, p: int, emin: int) -> np.ndarray:
+    """Round fp64 ``x`` to the nearest value of a binary format with ``p``
+    significant bits and minimum normal exponent ``emin`` (ties to even),
+    subnormals included.  Exact: only power-of-two scalings and np.rint."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e2 = np.frexp(np.abs(x))          # |x| = m * 2**e2, m in [0.5, 1)
+    e = np.maximum(e2.astype(np.int64) - 1, emin)
+    q = np.ldexp(1.0, (e - (p - 1)).astype(np.int64))
+    return np.rint(x / q) * q
+
+
+def fp16_rne(x) -> np.ndarray:
+    """IEEE binary16 round-to-nearest-even of fp64 values (returned as fp64)."""
+    r = _round_binary(x, 11, -14)
+    if np.any(np.abs(r) > 65504.0):
+        raise OverflowError("fp16 overflow")
+    return r
+
+
+def bf16_rne(x) -> np.ndarray:
+    """bfloat16 round-to-nearest-even of fp64 values (returned as fp64)."""
+    return _round_binary(x, 8, -126)
+
+
+def fp16_bits(x) -> np.ndarray:
+    return fp16_rne(x).astype(np.float16).view(np.uint16)
+
+
+def bf16_bits(x) -> np.ndarray:
+    return (bf16_rne(x).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def fp16_to_f64(bits) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# the fixed transforms: Hadamard and bit reversal  [P1 «Что придумали в
+# Together AI»: after the eigenbasis, a Hadamard to even out channel importance,
+# then a bit-reversal permutation so every quantisation group gets an even share
+# of the importance order; P4 «OSCAR: figyelem-tudatos és bevetésre kész»]
+# ---------------------------------------------------------------------------
+
+def hadamard(d: int = D) -> np.ndarray:
+    """Sylvester Hadamard matrix, closed form H[i, j] = (-1)^popcount(i & j)."""
+    i = np.arange(d)
+    pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i[:, None] & i[None, :])
+    return np.where(pc % 2 == 0, 1.0, -1.0)
+
+
+def bit_reverse_index(d: int = D) -> np.ndarray:
+    """br(i): i with its log2(d) bits reversed."""
+    nb = int(round(math.log2(d)))
+    assert 1 << nb == d
+    return np.array([int(format(i, f"0{nb}b")[::-1], 2) for i in range(d)], dtype=np.int64)
+
+
+def apply_bitrev_rows(m: np.ndarray) -> np.ndarray:
+    """P_br . m, where (P_br y)_i = y_{br(i)} (rows permuted)."""
+    return m[bit_reverse_index(m.shape[0])]
+
+
+# ---------------------------------------------------------------------------
+# calibration  [P1 «Что придумали в Together AI»: keys are rotated into the
+# eigenbasis of the empirical query covariance (it weights the error of the
+# logits Q K^T); values into the eigenbasis of the value covariance weighted by
+# attention scores (it weights the error of S V).  P1 «Открытый код — это
+# серьёзно» and P3 «Como Funciona o OSCAR?»: offline, once per model.]
+# ---------------------------------------------------------------------------
+
+def eig_desc(s: np.ndarray):
+    """Eigen-decomposition of a symmetric matrix: eigenvalues descending,
+    eigenvectors as columns, each with its largest-|entry| positive (first index
+    on ties).  numpy.linalg.eigh is the textbook routine."""
+    s = 0.5 * (np.asarray(s, dtype=np.float64) + np.asarray(s, dtype=np.float64).T)
+    w, u = np.linalg.eigh(s)
+    order = np.argsort(-w, kind="stable")
+    w, u = w[order], u[:, order]
+    idx = np.argmax(np.abs(u), axis=0)
+    sgn = np.sign(u[idx, np.arange(u.shape[1])])
+    sgn[sgn == 0] = 1.0
+    return w, u * sgn[None, :]
+
+
+def query_covariance(q: np.ndarray) -> np.ndarray:
+    """E[q q^T] over the calibration queries (uncentred)."""
+    q = np.asarray(q, dtype=np.float64)
+    return q.T @ q / q.shape[0]
+
+
+def score_weights(q: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """a_j = sum_i softmax_j(q_i . k_j / sqrt(d)): attention mass token j gets."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    logits = q @ k.T / math.sqrt(q.shape[1])
+    logits -= logits.max(axis=1, keepdims=True)
+    p = np.exp(logits)
+    p /= p.sum(axis=1, keepdims=True)
+    return p.sum(axis=0)
+
+
+def value_covariance(v: np.ndarray, a: np.ndarray) -> np.ndarray:
+    """sum_j a_j v_j v_j^T / sum_j a_j."""
+    v = np.asarray(v, dtype=np.float64)
+    return (v.T * a[None, :]) @ v / a.sum()
+
+
+def rotation_from_basis(u: np.ndarray) -> np.ndarray:
+    """R = P_br . (H / sqrt d) . U^T, acting on column vectors (x' = R x)."""
+    d = u.shape[0]
+    return apply_bitrev_rows(hadamard(d) / math.sqrt(d) @ u.T)
+
+
+def calibrate_ref(q_cal, k_cal, v_cal):
+    """Per KV head: (R_K, R_V) fp64 [Hkv][d][d], eigenvalues [Hkv][d] each.
+    q_cal [Hkv][n_q][d]; k_cal, v_cal [Hkv][n_kv][d]."""
+    hkv, _, d = np.shape(q_cal)
+    rk, rv = np.empty((hkv, d, d)), np.empty((hkv, d, d))
+    ek, ev = np.empty((hkv, d)), np.empty((hkv, d))
+    for h in range(hkv):
+        ek[h], uq = eig_desc(query_covariance(q_cal[h]))
+        a = score_weights(q_cal[h], k_cal[h])
+        ev[h], us = eig_desc(value_covariance(v_cal[h], a))
+        rk[h] = rotation_from_basis(uq)
+        rv[h] = rotation_from_basis(us)
+    return rk, rv, ek, ev
+
+
+# ---------------------------------------------------------------------------
+# encoder: rotate -> asymmetric 2-bit quantise -> pack
+# [P1 «Почему INT2 раньше не работал»: 2 bits = four levels; P1 «Что это даёт
+#  на практике»: paged KV-cache systems; group size 128 and fp16 scale/zero are
+#  the benchmark configuration's parameters]
+# ---------------------------------------------------------------------------
+
+def rotate(r: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """x' = R x for every vector in x [..., d] (fp64; exact for bf16 data)."""
+    return np.einsum("ij,...j->...i", np.asarray(r, np.float64), np.asarray(x, np.float64))
+
+
+def quantize(xr: np.ndarray):
+    """Asymmetric INT2 codes of each group (last axis = the 128 rotated channels).
+
+    Steps, all on the fp32 value of the rotation: m = min, M = max;
+    s = fp16(fp32((M - m) / 3)); z = fp16(m); t = fp32((x' - z) / s);
+    c = clamp(round_half_even(t), 0, 3); a zero scale gives all-zero codes.
+    Returns codes int64, s and z as fp64 values, and the fp32 pre-rounding values
+    (sigma, m, t) that the parity rule uses."""
+    x32 = np.asarray(xr, dtype=np.float64).astype(np.float32)
+    m = x32.min(axis=-1)
+    mx = x32.max(axis=-1)
+    sigma = ((mx - m).astype(np.float32) / np.float32(3.0)).astype(np.float32)
+    s = fp16_rne(sigma.astype(np.float64))
+    z = fp16_rne(m.astype(np.float64))
+    s32 = s.astype(np.float32)
+    z32 = z.astype(np.float32)
+    safe = np.where(s32 == 0, np.float32(1.0), s32)
+    t = ((x32 - z32[..., None]).astype(np.float32) / safe[..., None]).astype(np.float32)
+    c = np.clip(np.rint(t), 0, 3).astype(np.int64)
+    c = np.where((s32 == 0)[..., None], 0, c)
+    return c, s, z, dict(sigma=sigma, m=m, t=t)
+
+
+def pack_k_row(codes: np.ndarray) -> np.ndarray:
+    """[..., 128] codes -> [..., 32] bytes; channel c at bit 2c of the row."""
+    c = np.asarray(codes, dtype=np.uint8).reshape(*np.shape(codes)[:-1], 32, 4)
+    return (c[..., 0] | (c[..., 1] << 2) | (c[..., 2] << 4) | (c[..., 3] << 6)).astype(np.uint8)
+
+
+def unpack_k_rows(rows: np.ndarray) -> np.ndarray:
+    """[..., 32] bytes -> [..., 128] codes."""
+    r = np.asarray(rows, dtype=np.uint8)[..., None]
+    return ((r >> (2 * np.arange(4, dtype=np.uint8))) & 3).reshape(*r.shape[:-2], 128).astype(np.int64)
+
+
+def v_words(block: np.ndarray) -> np.ndarray:
+    """uint32 view [..., 128] of the V-code region of page blocks [..., 1152]."""
+    return np.ascontiguousarray(block[..., V_CODES:V_CODES + 512]).view("<u4")
+
+
+def unpack_v_words(words: np.ndarray) -> np.ndarray:
+    """[..., 128] channel words -> codes [..., 16 slots, 128 channels]."""
+    w = np.asarray(words, dtype=np.uint32)[..., None, :]
+    sh = (2 * np.arange(16, dtype=np.uint32))[:, None]
+    return ((w >> sh) & 3).astype(np.int64)
+
+
+def _put_fp16(block, off, slot, bits):
+    block[off + 2 * slot: off + 2 * slot + 2] = np.array([bits], dtype=np.uint16).view(np.uint8)
+
+
+def append_ref(r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,
+               pool, win_k, win_v, window: int):
+    """Write each token into the paged INT2 cache and, if recent, the bf16 window.
+
+    r_k, r_v: fp64 [Hkv][d][d] (bf16 values as data); k_new, v_new: bf16 bits
+    [T][Hkv][d]; pool uint8 [n_pages][Hkv][1152] and windows bf16 bits
+    [B][W][Hkv][d] are updated in place.  Token i lands in page
+    block_table[b][pos // 16], slot pos % 16; its raw bf16 k/v also go to window
+    slot pos % W when pos >= seq_len_after[b] - W  [P2 «OSCAR има значение…»,
+    P4 «OSCAR: figyelem-tudatos…»: recent tokens stay bf16, history is INT2]."""
+    k_new = np.asarray(k_new)
+    hkv = k_new.shape[1]
+    # x'[t, h] = R[h] x[t, h]
+    kr = np.einsum("hij,thj->thi", np.asarray(r_k, np.float64), bf16_to_f64(k_new))
+    vr = np.einsum("hij,thj->thi", np.asarray(r_v, np.float64), bf16_to_f64(v_new))
+    kc, ks, kz, _ = quantize(kr)
+    vc, vs, vz, _ = quantize(vr)
+    ksb, kzb, vsb, vzb = fp16_bits(ks), fp16_bits(kz), fp16_bits(vs), fp16_bits(vz)
+    krow = pack_k_row(kc)                                   # [T][Hkv][32]
+    for i in range(k_new.shape[0]):
+        b, p = int(seq_idx[i]), int(pos[i])
+        page = int(block_table[b][p // PAGE])
+        assert page >= 0, "position outside the block table"
+        slot = p % PAGE
+        for h in range(hkv):
+            blk = pool[page, h]
+            blk[K_CODES + 32 * slot: K_CODES + 32 * slot + 32] = krow[i, h]
+            words = v_words(blk).copy()
+            words &= ~np.uint32(3 << (2 * slot))
+            words |= (vc[i, h].astype(np.uint32) << np.uint32(2 * slot))
+            blk[V_CODES:V_CODES + 512] = words.astype("<u4").view(np.uint8)
+            _put_fp16(blk, K_SCALE, slot, ksb[i, h])
+            _put_fp16(blk, K_ZERO, slot, kzb[i, h])
+            _put_fp16(blk, V_SCALE, slot, vsb[i, h])
+            _put_fp16(blk, V_ZERO, slot, vzb[i, h])
+        if window > 0 and p >= int(seq_len_after[b]) - window:
+            win_k[b, p % window] = k_new[i]
+            win_v[b, p % window] = v_new[i]
+
+
+def read_history(pool, block_table_row, hist: int, h: int):
+    """Dequantised rotated history of one (sequence, KV head): (k', v') fp64 [hist][d].
+    x' = z + c s with the stored fp16 z, s."""
+    n_pg = -(-hist // PAGE)
+    pages = np.asarray(block_table_row[:n_pg], dtype=np.int64)
+    assert np.all(pages >= 0)
+    blk = pool[pages, h]                                    # [n_pg][1152]
+    kc = unpack_k_rows(blk[:, K_CODES:K_CODES + 512].reshape(n_pg, PAGE, 32))
+    vc = unpack_v_words(v_words(blk))                       # [n_pg][16][128]
+    f16 = lambda off: fp16_to_f64(np.ascontiguousarray(blk[:, off:off + 32]).view(np.uint16))
+    ks, kz, vs, vz = f16(K_SCALE), f16(K_ZERO), f16(V_SCALE), f16(V_ZERO)
+    k = kz[..., None] + kc * ks[..., None]
+    v = vz[..., None] + vc * vs[..., None]
+    return k.reshape(-1, D)[:hist], v.reshape(-1, D)[:hist]
+
+
+# ---------------------------------------------------------------------------
+# decode attention on the mixed-precision cache
+# [P1 «Что придумали в Together AI»: keys in the query eigenbasis, so q is
+#  rotated by the key transform; values are un-rotated by the value transform;
+#  P2 «OSCAR има значение…», P4 «OSCAR: figyelem-tudatos…»: bf16 recent
+#  tokens + INT2 history on paged storage]
+# ---------------------------------------------------------------------------
+
+def decode_ref(r_k, r_v, q_bits, seq_lens, block_table, pool, win_k, win_v,
+               window: int, pairs=None):
+    """Softmax attention of one query token per (sequence, q head) over the
+    dequantised cache, fp64.  Positions [0, n - w) come from the INT2 pages
+    (rotated domain: scores q'.k'/sqrt d with q' = R_K q; values un-rotated by
+    R_V^T), positions [n - w, n), w = min(n, W), from the bf16 window (plain
+    domain).  ``pairs``: iterable of (b, kv_head) to compute (default all);
+    other outputs are NaN."""
+    q = bf16_to_f64(q_bits)
+    bsz, hq, d = q.shape
+    hkv = np.shape(r_k)[0]
+    g = hq // hkv
+    out = np.full((bsz, hq, d), np.nan)
+    if pairs is None:
+        pairs = [(b, h) for b in range(bsz) for h in range(hkv)]
+    for b, h in pairs:
+        n = int(seq_lens[b])
+        w = min(n, window)
+        hist = n - w
+        kh, vh = read_history(pool, block_table[b], hist, h) if hist > 0 else (np.zeros((0, d)), np.zeros((0, d)))
+        wpos = np.arange(hist, n) % window if w > 0 else np.zeros(0, dtype=np.int64)
+        kw = bf16_to_f64(win_k[b, wpos, h]) if w > 0 else np.zeros((0, d))
+        vw = bf16_to_f64(win_v[b, wpos, h]) if w > 0 else np.zeros((0, d))
+        for j in range(g):
+            qq = q[b, h * g + j]
+            qr = np.asarray(r_k[h], np.float64) @ qq
+            s = np.concatenate([kh @ qr, kw @ qq]) / math.sqrt(d)
+            p = np.exp(s - s.max())
+            o_rot = p[:hist] @ vh
+            o = np.asarray(r_v[h], np.float64).T @ o_rot + p[hist:] @ vw
+            out[b, h * g + j] = o / p.sum()
+    return out
+
+
+def append_bf16_ref(k_new, v_new, seq_idx, pos, block_table, kv_pool):
+    """Scatter bf16 k/v [T][Hkv][d] into the comparator pool [n_pages][Hkv][2][16][d]."""
+    for i in range(np.shape(k_new)[0]):
+        b, p = int(seq_idx[i]), int(pos[i])
+        page = int(block_table[b][p // PAGE])
+        assert page >= 0
+        kv_pool[page, :, 0, p % PAGE] = k_new[i]
+        kv_pool[page, :, 1, p % PAGE] = v_new[i]
+
+
+def decode_bf16_ref(q_bits, seq_lens, block_table, kv_pool, n_kv_heads: int, pairs=None):
+    """Textbook softmax attention over a bf16 paged cache (the comparator), fp64."""
+    q = bf16_to_f64(q_bits)
+    bsz, hq, d = q.shape
+    g = hq // n_kv_heads
+    out = np.full((bsz, hq, d), np.nan)
+    if pairs is None:
+        pairs = [(b, h) for b in range(bsz) for h in range(n_kv_heads)]
+    for b, h in pairs:
+        n = int(seq_lens[b])
+        n_pg = -(-n // PAGE)
+        pages = np.asarray(block_table[b][:n_pg], dtype=np.int64)
+        assert np.all(pages >= 0)
+        k = bf16_to_f64(kv_pool[pages, h, 0]).reshape(-1, d)[:n]
+        v = bf16_to_f64(kv_pool[pages, h, 1]).reshape(-1, d)[:n]
+        for j in range(g):
+            s = k @ q[b, h * g + j] / math.sqrt(d)
+            p = np.exp(s - s.max())
+            out[b, h * g + j] = (p @ v) / p.sum()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# byte accounting  [P3 «Resultados e Métricas de Desempenho»: about 2.28 bits per
+# KV element; P2 «OSCAR има значение…»: about 0.24 % of tokens stay bf16 at 128K;
+# P2 «KV cache compression става болезнен…»: Llama-3.1-70B bf16 KV about
+# 0.31 MB per token, 40 GB at 128K, over 300 GB at 1M; P1 «Что это даёт на
+# практике»: 2 bits is 4x below FP8 and 2x below INT4]
+# ---------------------------------------------------------------------------
+
+def int2_bytes_per_token_head(d: int = D, group: int = 128, meta_bytes: int = 2) -> int:
+    """K + V bytes of one token of one KV head in the INT2 cache: codes plus an
+    fp16 scale and zero per group."""
+    return 2 * (d * 2 // 8 + 2 * meta_bytes * (d // group))
+
+
+def int2_bits_per_element(d: int = D, group: int = 128) -> float:
+    return int2_bytes_per_token_head(d, group) * 8 / (2 * d)
+
+
+def effective_bits(bf16_share: float, d: int = D, group: int = 128) -> float:
+    return int2_bits_per_element(d, group) * (1.0 - bf16_share) + 16.0 * bf16_share
+
+
+def bf16_kv_bytes_per_token(n_layers: int, n_kv_heads: int, d: int) -> int:
+    return 2 * n_layers * n_kv_heads * d * 2

@@ -1,0 +1,156 @@
+"""Pins of the oracle's decode attention (CPU only).
+
+(i)   brute force on tiny inputs: un-rotate the dequantised history with an exactly
+      orthogonal R and run textbook softmax attention in pure Python loops over
+      the original token order (no pool, no ring) -- this also pins the page /
+      slot / window-ring addressing of append_ref and decode_ref;
+(ii)  n <= W: equals torch's scaled_dot_product_attention in fp64 on the bf16 K/V;
+(iii) n = 1, W = 0: o = R_V^T v';
+(iv)  identical keys, W = 0: o = mean of the un-rotated dequantised values;
+(v)   the bf16 comparator equals torch SDPA.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import oscar_ref as ref
+
+
+def orthogonal(rng, hkv):
+    return np.stack([np.linalg.qr(rng.standard_normal((128, 128)))[0] for _ in range(hkv)])
+
+
+def build(rng, lens, window, hq=8, hkv=2, cfg=1, rot=None):
+    s = wl.spec(cfg, batch=len(lens))
+    s.seq_lens = np.asarray(lens, dtype=np.int32)
+    s.window = window
+    s.n_q_heads, s.n_kv_heads = hq, hkv
+    bt, n_pages = wl.page_table(s)
+    pool = np.zeros((n_pages, hkv, ref.BLOCK), dtype=np.uint8)
+    win_k = np.zeros((len(lens), max(window, 1), hkv, 128), dtype=np.uint16)
+    win_v = np.zeros_like(win_k)
+    rk, rv = rot if rot is not None else (orthogonal(rng, hkv), orthogonal(rng, hkv))
+    kv = {}
+    for b in range(len(lens)):
+        k, v = wl.context_kv(s, b)
+        k, v = k[:, :hkv], v[:, :hkv]
+        n = k.shape[0]
+        ref.append_ref(rk, rv, k, v, np.full(n, b, np.int32), np.arange(n, dtype=np.int32),
+                       bt, s.seq_lens, pool, win_k, win_v, window)
+        kv[b] = (k, v)
+    q = wl.decode_queries(s)[:, :hq]
+    return s, bt, pool, win_k, win_v, rk, rv, kv, q
+
+
+def brute_force(q_bits, kv, lens, window, rk, rv, hkv):
+    """Pure-Python textbook attention over the dequantised, un-rotated cache."""
+    bsz, hq, d = q_bits.shape
+    g = hq // hkv
+    out = np.zeros((bsz, hq, d))
+    for b in range(bsz):
+        k_bits, v_bits = kv[b]
+        n = int(lens[b])
+        hist = n - min(n, window)
+        for j in range(hq):
+            h = j // g
+            kx = ref.bf16_to_f64(k_bits[:, h])
+            vx = ref.bf16_to_f64(v_bits[:, h])
+            ck, sk, zk, _ = ref.quantize(ref.rotate(rk[h], kx))
+            cv, sv, zv, _ = ref.quantize(ref.rotate(rv[h], vx))
+            keys, vals = [], []
+            for t in range(n):
+                if t < hist:
+                    kr = zk[t] + ck[t] * sk[t]
+                    vr = zv[t] + cv[t] * sv[t]
+                    keys.append(rk[h].T @ kr)
+                    vals.append(rv[h].T @ vr)
+                else:
+                    keys.append(kx[t])
+                    vals.append(vx[t])
+            qq = ref.bf16_to_f64(q_bits[b, j])
+            logits = [sum(float(qq[c]) * float(kk[c]) for c in range(d)) / math.sqrt(d) for kk in keys]
+            mx = max(logits)
+            w = [math.exp(x - mx) for x in logits]
+            den = sum(w)
+            for c in range(d):
+                out[b, j, c] = sum(w[t] * vals[t][c] for t in range(n)) / den
+    return out
+
+
+def test_decode_matches_brute_force(rng):
+    lens, window = (37, 5, 20), 16          # several pages, ragged tail, n < W case
+    s, bt, pool, wk, wv, rk, rv, kv, q = build(rng, lens, window)
+    got = ref.decode_ref(rk, rv, q, s.seq_lens, bt, pool, wk, wv, window)
+    want = brute_force(q, kv, lens, window, rk, rv, 2)
+    assert np.abs(got - want).max() <= 1e-11 * np.abs(want).max()
+
+
+def test_decode_pure_window_is_sdpa(rng):
+    lens, window = (9, 16), 16
+    s, bt, pool, wk, wv, rk, rv, kv, q = build(rng, lens, window)
+    got = ref.decode_ref(rk, rv, q, s.seq_lens, bt, pool, wk, wv, window)
+    for b in range(2):
+        k, v = kv[b]
+        kk = torch.from_numpy(ref.bf16_to_f64(k)).permute(1, 0, 2)      # [Hkv][n][d]
+        vv = torch.from_numpy(ref.bf16_to_f64(v)).permute(1, 0, 2)
+        qq = torch.from_numpy(ref.bf16_to_f64(q[b])).view(2, 4, 1, 128)  # [Hkv][G][1][d]
+        o = torch.nn.functional.scaled_dot_product_attention(qq, kk[:, None], vv[:, None])
+        assert np.allclose(got[b], o.reshape(8, 128).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_decode_single_int2_token(rng):
+    s, bt, pool, wk, wv, rk, rv, kv, q = build(rng, (1,), 0)
+    got = ref.decode_ref(rk, rv, q, s.seq_lens, bt, pool, wk, wv, 0)
+    for h in range(2):
+        _, vh = ref.read_history(pool, bt[0], 1, h)
+        for j in range(4):
+            assert np.allclose(got[0, h * 4 + j], rv[h].T @ vh[0], atol=1e-13)
+
+
+def test_decode_identical_keys_average_values(rng):
+    s = wl.spec(1, batch=1)
+    s.seq_lens = np.array([50], np.int32)
+    s.n_kv_heads = 1
+    bt, n_pages = wl.page_table(s)
+    pool = np.zeros((n_pages, 1, ref.BLOCK), np.uint8)
+    wk = np.zeros((1, 1, 1, 128), np.uint16)
+    rk, rv = orthogonal(rng, 1), orthogonal(rng, 1)
+    k, v = wl.context_kv(s, 0)
+    k = np.repeat(k[:1, :1], 50, axis=0)
+    v = v[:, :1]
+    ref.append_ref(rk, rv, k, v, np.zeros(50, np.int32), np.arange(50, dtype=np.int32), bt,
+                   s.seq_lens, pool, wk, wk.copy(), 0)
+    q = wl.decode_queries(s)[:, :3]
+    got = ref.decode_ref(rk, rv, q, s.seq_lens, bt, pool, wk, wk, 0)
+    _, vh = ref.read_history(pool, bt[0], 50, 0)
+    want = rv[0].T @ vh.mean(axis=0)
+    assert np.allclose(got[0], want[None, :], atol=1e-12)
+
+
+def test_decode_sampled_pairs_match_full(rng):
+    lens, window = (40, 33), 8
+    s, bt, pool, wk, wv, rk, rv, kv, q = build(rng, lens, window)
+    full = ref.decode_ref(rk, rv, q, s.seq_lens, bt, pool, wk, wv, window)
+    part = ref.decode_ref(rk, rv, q, s.seq_lens, bt, pool, wk, wv, window, pairs=[(1, 0)])
+    assert np.array_equal(part[1, :4], full[1, :4])
+    assert np.isnan(part[0]).all() and np.isnan(part[1, 4:]).all()
+
+
+def test_bf16_comparator_is_sdpa(rng):
+    s = wl.spec(1, batch=2)
+    s.seq_lens = np.array([45, 17], np.int32)
+    bt, n_pages = wl.page_table(s)
+    pool = np.zeros((n_pages, 8, 2, 16, 128), np.uint16)
+    q = wl.decode_queries(s)
+    for b in range(2):
+        k, v, si, pos = wl.prefill_tokens(s, b)
+        ref.append_bf16_ref(k, v, si, pos, bt, pool)
+        got = ref.decode_bf16_ref(q, s.seq_lens, bt, pool, 8)
+        kk = torch.from_numpy(ref.bf16_to_f64(k)).permute(1, 0, 2)[:, None]
+        vv = torch.from_numpy(ref.bf16_to_f64(v)).permute(1, 0, 2)[:, None]
+        qq = torch.from_numpy(ref.bf16_to_f64(q[b])).view(8, 4, 1, 128)
+        o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv).reshape(32, 128).numpy()
+        assert np.allclose(got[b], o, rtol=1e-12, atol=1e-13)
