@@ -1,0 +1,290 @@
+"""Benchmark of the OSCAR INT2 KV-cache decode step on one MI355X.
+
+Workload: long-context decode, batch 8, 100000 tokens per sequence, 32 q / 8 KV
+heads, head_dim 128, INT2 history + 128-token bf16 window, 16-token pages
+scattered in a shared pool (synthetic Gaussian K/V with 4 key outlier channels
+x20, seeded).  One step = append the current token of every sequence
+(oscar_quantize_append) + decode attention over the whole context
+(oscar_decode_attn).  Calibration runs once beforehand (it is an offline,
+once-per-model step).  The same step on a bf16 paged cache (oscar_bf16_append +
+oscar_bf16_decode_attn) on identical inputs is timed in the same session.
+
+Every step reads a different one of ``--layers`` independent caches, as the
+layers of a model would, so no step finds the previous step's cache in the
+256 MB Infinity Cache.
+
+Prints one JSON line (rank 0).  ``value`` = algorithmic HBM bytes of the INT2
+step / step time (GB/s).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+DECODE_SRC = os.path.join(ROOT, "kv_cache_int2_amd", "csrc", "decode.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "int2_split_counters_longctx_b8_n100000.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(path=DECODE_SRC) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(split_launch_bytes_alg: float):
+    """HBM bytes per launch of the INT2 split kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    kv = {}
+    for line in open(COUNTERS):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("decode_source_sha") != source_sha():
+        return None
+    try:
+        fetch = float(kv["fetch_bytes_per_launch"])
+        write = float(kv["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+    return fetch + write
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--cpu-units", type=int, default=3, help="(sequence, KV head) units the oracle times")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kv_cache_int2_amd as K
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s = wl.spec(args.config)
+    B, HQ, HKV, W = s.batch, s.n_q_heads, s.n_kv_heads, s.window
+    lens = s.seq_lens.astype(np.int64)
+    nmax = int(lens.max())
+    shape = K.make_shape(HQ, HKV, W)
+
+    def T(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    # ---- offline calibration (host, once) ----
+    t0 = time.time()
+    qc, kc, vc = wl.calibration_set(s)
+    rk, rv, _, _ = K.oscar_calibrate(shape, qc, kc, vc)
+    rkd, rvd = T(rk), T(rv)
+    log(f"calibration {time.time() - t0:.1f}s")
+
+    # ---- caches: L independent layers, INT2 and bf16, identical K/V ----
+    L = args.layers
+    bt, n_pages = wl.page_table(s)
+    btd, lensd = T(bt), T(lens.astype(np.int32))
+    pools = [torch.zeros((n_pages, HKV, K.BLOCK_BYTES), dtype=torch.uint8, device=dev) for _ in range(L)]
+    wks = [torch.zeros((B, W, HKV, 128), dtype=torch.int16, device=dev) for _ in range(L)]
+    wvs = [torch.zeros((B, W, HKV, 128), dtype=torch.int16, device=dev) for _ in range(L)]
+    kvp = [] if args.no_bf16 else [torch.zeros((n_pages, HKV, 2, 16, 128), dtype=torch.int16, device=dev)
+                                   for _ in range(L)]
+    cur_k = np.empty((B, HKV, 128), np.uint16)
+    cur_v = np.empty((B, HKV, 128), np.uint16)
+    t0 = time.time()
+    for b in range(B):
+        k, v, si, ps = wl.prefill_tokens(s, b)
+        cur_k[b], cur_v[b] = k[-1], v[-1]
+        kd, vd, sid, psd = T(k), T(v), T(si), T(ps)
+        for l in range(L):
+            K.oscar_quantize_append(shape, rkd, rvd, kd, vd, sid, psd, btd, lensd, pools[l], wks[l], wvs[l])
+            if kvp:
+                K.oscar_bf16_append(shape, kd, vd, sid, psd, btd, kvp[l])
+        del kd, vd
+    torch.cuda.synchronize()
+    log(f"caches built ({L} layers) {time.time() - t0:.1f}s")
+
+    q = T(wl.decode_queries(s))
+    cur_kd, cur_vd = T(cur_k), T(cur_v)
+    cur_si = T(np.arange(B, dtype=np.int32))
+    cur_pos = T((lens - 1).astype(np.int32))
+    ws = torch.empty(K.oscar_decode_workspace_bytes(shape, B, nmax), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, HQ, 128), dtype=torch.float32, device=dev)
+
+    def step_int2(i):
+        l = i % L
+        K.oscar_quantize_append(shape, rkd, rvd, cur_kd, cur_vd, cur_si, cur_pos, btd, lensd, pools[l], wks[l], wvs[l])
+        K.oscar_decode_attn(shape, rkd, rvd, q, lensd, nmax, btd, pools[l], wks[l], wvs[l], out, ws)
+
+    def step_bf16(i):
+        l = i % L
+        K.oscar_bf16_append(shape, cur_kd, cur_vd, cur_si, cur_pos, btd, kvp[l])
+        K.oscar_bf16_decode_attn(shape, q, lensd, nmax, btd, kvp[l], out, ws)
+
+    def timed(step, kind):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        cap = 4 * args.steps + 8
+        K.oscar_timing_begin(cap)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(args.steps):
+            step(args.warmup + i)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t) / args.steps
+        ms, kinds = K.oscar_timing_end(cap)
+        kern = [m for m, k in zip(ms, kinds) if k == kind]
+        return dt, float(np.mean(kern)) / 1e3 if kern else None, kern
+
+    # ---- in-session HBM probe (streaming copy, 2 GiB each way) ----
+    nb = 2 << 30
+    a = torch.empty(nb, dtype=torch.uint8, device=dev)
+    c = torch.empty(nb, dtype=torch.uint8, device=dev)
+    K.oscar_hbm_copy(a, c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        K.oscar_hbm_copy(a, c)
+    e1.record()
+    torch.cuda.synchronize()
+    probe_gbs = 2 * nb * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del a, c
+    log(f"HBM copy probe: {probe_gbs:.0f} GB/s (read + write)")
+
+    # ---- algorithmic bytes ----
+    hist = np.maximum(lens - W, 0)
+    win = np.minimum(lens, W)
+    b_hist = float(hist.sum() * HKV * 72)
+    b_win = float(win.sum() * HKV * 512)
+    b_rot = 2 * HKV * 128 * 128 * 2
+    b_q_out = B * HQ * 128 * (2 + 4)
+    b_bt = float(sum(-(-int(n) // 16) for n in lens) * 4)
+    b_append = B * HKV * (2 * 256 + 72 + 2 * 256) + b_rot
+    step_bytes_int2 = b_hist + b_win + b_rot + b_q_out + b_bt + b_append
+    b_bf16_kv = float(lens.sum() * HKV * 512)
+    step_bytes_bf16 = b_bf16_kv + b_q_out + b_bt + B * HKV * 2 * 2 * 256
+
+    dt, split_s, split_all = timed(step_int2, 1)
+    log(f"INT2 step {dt * 1e3:.3f} ms, split kernel {split_s * 1e3 if split_s else float('nan'):.3f} ms")
+    res_bf16 = None
+    if kvp:
+        dtb, split_b, _ = timed(step_bf16, 2)
+        log(f"bf16 step {dtb * 1e3:.3f} ms, split kernel {split_b * 1e3 if split_b else float('nan'):.3f} ms")
+        res_bf16 = {
+            "ms_per_step": dtb * 1e3,
+            "decode_tokens_per_s": B / dtb,
+            "hbm_gbs": step_bytes_bf16 / dtb / 1e9,
+            "split_kernel_ms": split_b * 1e3 if split_b else None,
+            "split_kernel_gbs": b_bf16_kv / split_b / 1e9 if split_b else None,
+        }
+    assert torch.isfinite(out).all()
+
+    achieved = b_hist / split_s / 1e9 if split_s else None
+    traffic = load_traffic(b_hist)
+    line = {
+        "metric": "INT2 decode-attn HBM GB/s (% of peak) + decode tokens/s at 100K ctx vs bf16 KV",
+        "value": step_bytes_int2 / dt / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dt * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int2 codes / fp32 math",
+        "data": "synthetic (seeded Gaussian K/V, 4 key outlier channels x20; no dataset exists for this path)",
+        "config": {"workload": f"long-context decode step: append 1 token/seq + INT2 decode, B={B}, n={nmax}, "
+                               f"{HQ}q/{HKV}kv heads, d=128, group 128, 16-token scattered pages, bf16 window {W}",
+                   "layers_rotated": L, "pct_of_hbm_peak": 100 * step_bytes_int2 / dt / 1e9 / PEAK_HBM_GBS,
+                   "decode_tokens_per_s": B / dt, "step_bytes": step_bytes_int2},
+        "bf16_kv": res_bf16,
+        "speedup_vs_bf16": (res_bf16["ms_per_step"] / (dt * 1e3)) if res_bf16 else None,
+        "hbm_probe_copy_gbs": probe_gbs,
+        "roofline": {
+            "kernel": "int2_split_kernel",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS if achieved else None,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": b_hist,
+            "avg_launch_ms": split_s * 1e3 if split_s else None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(s, rk, rv, args.cpu_units, step_bytes_int2)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(s, rk_bits, rv_bits, units: int, step_bytes: float):
+    """The oracle (numpy fp64, untuned) decoding a bounded sample of the same
+    workload on the host: ``units`` (sequence, KV head) pairs at full context,
+    each from an oracle-built pool, BLAS pinned to one thread."""
+    from threadpoolctl import threadpool_limits
+
+    import workloads as wl
+    from oracle import oscar_ref as ref
+
+    rkf, rvf = ref.bf16_to_f64(rk_bits), ref.bf16_to_f64(rv_bits)
+    q = wl.decode_queries(s)
+    total_t = 0.0
+    total_bytes = 0.0
+    with threadpool_limits(limits=1):
+        for u in range(units):
+            b, h = u % s.batch, (3 * u) % s.n_kv_heads
+            n = int(s.seq_lens[b])
+            k, v = wl.context_kv(s, b)
+            s1 = wl.Spec(cfg=s.cfg, name=s.name, batch=1, n_q_heads=s.gqa, n_kv_heads=1,
+                         seq_lens=np.array([n], np.int32), window=s.window)
+            bt, n_pages = wl.page_table(s1)
+            pool = np.zeros((n_pages, 1, ref.BLOCK), np.uint8)
+            wk = np.zeros((1, s.window, 1, 128), np.uint16)
+            wv = np.zeros_like(wk)
+            ref.append_sequence_ref(rkf[h:h + 1], rvf[h:h + 1], k[:, h:h + 1], v[:, h:h + 1], bt[0], pool, wk[0],
+                                    wv[0], s.window)
+            qq = q[b:b + 1, h * s.gqa:(h + 1) * s.gqa]
+            t = time.perf_counter()
+            ref.decode_ref(rkf[h:h + 1], rvf[h:h + 1], qq, np.array([n]), bt, pool, wk, wv, s.window)
+            total_t += time.perf_counter() - t
+            w = min(n, s.window)
+            total_bytes += (n - w) * 72 + w * 512
+    units_per_step = s.batch * s.n_kv_heads
+    gbs = total_bytes / total_t / 1e9
+    return {"value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{units} of {units_per_step} (sequence, KV head) decode units at n={int(s.seq_lens.max())} "
+                      f"(oracle decode_ref: unpack pool bytes + fp64 attention), {total_t:.1f}s",
+            "decode_tokens_per_s_equiv": s.batch / (total_t / units * units_per_step)}
+
+
+if __name__ == "__main__":
+    main()

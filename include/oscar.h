@@ -1,0 +1,208 @@
+/*
+ * oscar.h -- C ABI of the MI355X (gfx950) OSCAR-style INT2 KV-cache library.
+ *
+ * The method (sources: the text of five web pages; cited by key):
+ *   P1 gen-hub.ru, "Together AI открывает OSCAR: сжатие KV-кэша до 2 бит без
+ *      потери точности"
+ *   P2 encorp.ai, "KV cache compression е инфраструктурно решение, не спор за модела"
+ *   P3 bigsaas.top, "Revolução no Serviço de LLMs: Together AI Lança OSCAR para
+ *      Contextos Extensos"
+ *   P4 aiforradalom.hu, "Az Apple, a Google és a NYU új technikái felezik az
+ *      LLM-ek memóriaigényét"
+ * Keys are rotated into the eigenbasis of the calibration query covariance and
+ * values into the eigenbasis of the attention-score-weighted value covariance,
+ * each followed by a Hadamard transform and a bit-reversal permutation
+ * (P1 «Что придумали в Together AI»; P4 «OSCAR: figyelem-tudatos és bevetésre
+ * kész»).  Rotated vectors are stored as 2-bit codes (P1 «Почему INT2 раньше не
+ * работал») in a paged cache; recent tokens stay bf16 (P2 «OSCAR има значение,
+ * защото някой реално е доставил мръсната работа»).  Calibration is an offline,
+ * once-per-model step (P1 «Открытый код — это серьёзно»; P3 «Como Funciona o
+ * OSCAR?»).
+ *
+ * Conventions shared by every entry point
+ *   - All sizes are element counts unless named *_bytes.
+ *   - bf16 and fp16 values are passed as their uint16_t bit patterns.
+ *   - "device" pointers are HIP device memory (e.g. from torch) on the current
+ *     device; "host" pointers are ordinary CPU memory.  The caller owns every
+ *     buffer; the library never allocates or frees caller memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Entry points that
+ *     take a stream only validate arguments on the host and enqueue kernels;
+ *     they return before the work completes.
+ *   - Every entry point returns an oscar_status.  Host-detectable argument
+ *     errors are reported before anything is enqueued.  Device-side data
+ *     (page ids, positions, lengths) is the caller's contract: entries outside
+ *     the pool are skipped by the kernels rather than written.
+ *
+ * Supported shape (anything else returns OSCAR_EUNSUPPORTED): head_dim 128,
+ * group_size 128 (one INT2 group per token vector), page_size 16,
+ * n_q_heads = G * n_kv_heads with G in {1, 2, 4, 8, 16}, 0 <= window <= 1024.
+ *
+ * Page block (one per page and KV head, 1152 bytes, 128-byte aligned within a
+ * 128-byte aligned pool; pool = uint8 [n_pages][n_kv_heads][1152]):
+ *   [   0,  512)  K codes: 16 token rows x 32 B; channel c at bit 2c of the row
+ *   [ 512, 1024)  V codes: 128 channel words (uint32, little endian); token slot
+ *                 j of the page at bits 2j..2j+1
+ *   [1024, 1056)  K scale fp16[16]   [1056, 1088)  K zero fp16[16]
+ *   [1088, 1120)  V scale fp16[16]   [1120, 1152)  V zero fp16[16]
+ * A token at position pos of sequence b lives in page block_table[b][pos / 16],
+ * slot pos % 16.  Dequantised rotated value of channel c: zero + code * scale.
+ * bf16 window ring: [batch][window][n_kv_heads][128], position pos in slot pos % window.
+ */
+#ifndef OSCAR_H
+#define OSCAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum oscar_status {
+  OSCAR_OK = 0,
+  OSCAR_EINVAL = -1,        /* null pointer, negative size, inconsistent arguments */
+  OSCAR_EUNSUPPORTED = -2,  /* shape outside the supported set above */
+  OSCAR_EHIP = -3,          /* a HIP runtime call or kernel launch failed */
+  OSCAR_ENOSPACE = -4       /* workspace too small, or max_seq_len exceeds the block table */
+} oscar_status;
+
+typedef struct oscar_shape {
+  int32_t n_q_heads;   /* query heads (G * n_kv_heads) */
+  int32_t n_kv_heads;  /* key/value heads */
+  int32_t head_dim;    /* d; must be 128 */
+  int32_t group_size;  /* channels per INT2 group; must be 128 */
+  int32_t page_size;   /* tokens per page; must be 16 */
+  int32_t window;      /* most recent tokens also kept in bf16 (0 = none) */
+} oscar_shape;
+
+#define OSCAR_HEAD_DIM 128
+#define OSCAR_PAGE_SIZE 16
+#define OSCAR_BLOCK_BYTES 1152
+
+/*
+ * Offline calibration, host only, synchronous (P1 «Что придумали в Together AI»,
+ * «Открытый код — это серьёзно»).  Per KV head h:
+ *   Sigma_Q = (1/n_q) sum_i q_i q_i^T over q_cal[h] (uncentred);
+ *   a_j     = sum_i softmax_j(q_i . k_j / sqrt(d)) over k_cal[h];
+ *   Sigma_S = sum_j a_j v_j v_j^T / sum_j a_j over v_cal[h];
+ *   U_Q, U_S = eigenvectors (columns), eigenvalues descending, each column's
+ *              largest-magnitude entry positive;
+ *   R_K = P_br (H/sqrt d) U_Q^T,  R_V = P_br (H/sqrt d) U_S^T, with H the
+ *   Sylvester Hadamard matrix, (P_br y)_i = y_{bitrev7(i)}; x' = R x.
+ * Arguments (all host memory, row-major):
+ *   q_cal  float [n_kv_heads][n_q][128]   calibration queries, pooled over the G
+ *                                         query heads of each KV head
+ *   k_cal, v_cal float [n_kv_heads][n_kv][128]
+ *   r_k, r_v  out, bf16 bits [n_kv_heads][128][128] (RNE from fp64)
+ *   eig_k, eig_v out, double [n_kv_heads][128] eigenvalues, descending; may be NULL
+ * Computation is fp64 with the library's own cyclic Jacobi eigensolver.
+ * Errors: OSCAR_EINVAL (null inputs, n_q < 1, n_kv < 1, non-finite input),
+ * OSCAR_EUNSUPPORTED (shape).
+ */
+int oscar_calibrate(const oscar_shape* shape, const float* q_cal, int64_t n_q,
+                    const float* k_cal, const float* v_cal, int64_t n_kv,
+                    uint16_t* r_k, uint16_t* r_v, double* eig_k, double* eig_v);
+
+/*
+ * Online rotate -> quantise -> pack of new tokens into the paged INT2 cache,
+ * plus the bf16 window (P1 «Что придумали в Together AI», «Почему INT2 раньше не
+ * работал»; P2 «OSCAR има значение…»; P4 «OSCAR: figyelem-tudatos…»).
+ * For each token i (any order; positions must be distinct per sequence):
+ *   b = seq_idx[i], p = pos[i]; for each KV head h and for K (R = r_k) and V (r_v):
+ *   x' = R[h] x (bf16 inputs, fp32 accumulation on the matrix cores);
+ *   m = min x', M = max x'; scale = fp16_rne((M - m) / 3); zero = fp16_rne(m);
+ *   code_c = clamp(rint((x'_c - zero) / scale), 0, 3) (all 0 if scale == 0);
+ *   written to page block_table[b][p / 16], slot p % 16, in the layout above.
+ *   If p >= seq_len_after[b] - window, the raw bf16 k/v also go to window slot
+ *   p % window.
+ * Arguments (device memory unless noted):
+ *   r_k, r_v     bf16 [n_kv_heads][128][128]
+ *   k_new, v_new bf16 [n_tokens][n_kv_heads][128]
+ *   seq_idx, pos int32 [n_tokens]
+ *   block_table  int32 [batch][max_pages_per_seq]
+ *   seq_len_after int32 [batch]: sequence length once this call's tokens are in
+ *   pool         uint8 [n_pages][n_kv_heads][1152], updated in place (other slots kept)
+ *   win_k, win_v bf16 [batch][window][n_kv_heads][128] (may be NULL if window == 0)
+ * n_tokens == 0 is a no-op.  Errors: OSCAR_EINVAL, OSCAR_EUNSUPPORTED, OSCAR_EHIP.
+ */
+int oscar_quantize_append(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
+                          const uint16_t* k_new, const uint16_t* v_new, int64_t n_tokens,
+                          const int32_t* seq_idx, const int32_t* pos, int32_t batch,
+                          const int32_t* block_table, int32_t max_pages_per_seq,
+                          const int32_t* seq_len_after, uint8_t* pool, int64_t n_pages,
+                          uint16_t* win_k, uint16_t* win_v, void* stream);
+
+/*
+ * Workspace bytes oscar_decode_attn and oscar_bf16_decode_attn need for this
+ * batch and longest sequence (split partials and rotated queries).  0 on
+ * invalid arguments.
+ */
+size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int32_t max_seq_len);
+
+/*
+ * Decode attention for one query token per sequence over the mixed-precision
+ * cache (P1 «Что придумали в Together AI»: q is rotated by the key transform and
+ * the output un-rotated by the value transform; P2 «OSCAR има значение…»: bf16
+ * recent window + INT2 history).  With n = seq_lens[b], w = min(n, window):
+ *   history t < n - w: s_t = (R_K q) . (zero + code * scale)_t / sqrt(d)  (INT2 K)
+ *   window  t >= n - w: s_t = q . k_t / sqrt(d)                           (bf16 K)
+ *   out = (R_V^T sum_hist p_t v'_t + sum_win p_t v_t) / sum_all p_t,
+ *   p = exp(s - max s); query head j uses KV head j / G.
+ * Arguments (device memory):
+ *   r_k, r_v bf16 [n_kv_heads][128][128]; q bf16 [batch][n_q_heads][128]
+ *   seq_lens int32 [batch], each in [1, max_seq_len] (host max_seq_len)
+ *   block_table, pool, win_k, win_v as for oscar_quantize_append
+ *   out float [batch][n_q_heads][128]
+ *   workspace >= oscar_decode_workspace_bytes(shape, batch, max_seq_len) bytes
+ * Errors: OSCAR_EINVAL, OSCAR_EUNSUPPORTED, OSCAR_ENOSPACE, OSCAR_EHIP.
+ */
+int oscar_decode_attn(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
+                      const uint16_t* q, int32_t batch, const int32_t* seq_lens, int32_t max_seq_len,
+                      const int32_t* block_table, int32_t max_pages_per_seq,
+                      const uint8_t* pool, int64_t n_pages, const uint16_t* win_k,
+                      const uint16_t* win_v, float* out, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * bf16-KV comparator (not part of the method; the baseline the INT2 decode is
+ * measured against, P2 «OSCAR има значение…» and P3 «Resultados e Métricas de
+ * Desempenho» quote decode speed against a BF16 cache).  Paged bf16 pool:
+ * uint16 [n_pages][n_kv_heads][2 (K, V)][16][128], same block table semantics.
+ * oscar_bf16_append scatters k_new/v_new [n_tokens][n_kv_heads][128] into it;
+ * oscar_bf16_decode_attn is plain softmax attention over all seq_lens[b]
+ * positions, fp32 output [batch][n_q_heads][128], same workspace rule.
+ */
+int oscar_bf16_append(const oscar_shape* shape, const uint16_t* k_new, const uint16_t* v_new,
+                      int64_t n_tokens, const int32_t* seq_idx, const int32_t* pos, int32_t batch,
+                      const int32_t* block_table, int32_t max_pages_per_seq, uint16_t* kv_pool,
+                      int64_t n_pages, void* stream);
+int oscar_bf16_decode_attn(const oscar_shape* shape, const uint16_t* q, int32_t batch,
+                           const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
+                           int32_t max_pages_per_seq, const uint16_t* kv_pool, int64_t n_pages,
+                           float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement helpers (not part of the method).
+ * oscar_hbm_copy: plain streaming copy of `bytes` (multiple of 16, both pointers
+ *   16-byte aligned) from src to dst on the device; used to calibrate HBM
+ *   counters and as an in-session bandwidth probe.
+ * oscar_timing_begin(capacity): from now on every append / decode call also
+ *   records a pair of HIP events on its stream around its main kernel, up to
+ *   `capacity` pairs.  oscar_timing_end copies the elapsed milliseconds and the
+ *   kernel kind (1 INT2 decode split kernel, 2 bf16 decode split kernel,
+ *   3 INT2 append) of each recorded pair into ms/kinds (host arrays of
+ *   `capacity`), sets *n, synchronises the events and stops recording.
+ *   Not thread-safe; meant for one benchmarking thread.
+ */
+int oscar_hbm_copy(const void* src, void* dst, size_t bytes, void* stream);
+int oscar_timing_begin(int32_t capacity);
+int oscar_timing_end(float* ms, int32_t* kinds, int32_t capacity, int32_t* n);
+
+/* Static description of a status code. */
+const char* oscar_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSCAR_H */

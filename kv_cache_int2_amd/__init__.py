@@ -1,0 +1,168 @@
+"""Python binding of the MI355X OSCAR INT2 KV-cache library (include/oscar.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP library
+(``libkv_cache_int2_amd.so``).  Device buffers are torch tensors (torch is used
+for device memory and streams); host buffers of ``oscar_calibrate`` are numpy
+arrays.  Functions keep the C names; a non-zero status raises ``OscarError``.
+bf16 / fp16 buffers may be ``torch.bfloat16``, ``torch.int16`` or ``torch.uint16``
+tensors holding the bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+
+from ._lib import OscarShape, lib
+
+__all__ = [
+    "OscarError", "OscarShape", "make_shape", "oscar_calibrate", "oscar_quantize_append",
+    "oscar_decode_workspace_bytes", "oscar_decode_attn", "oscar_bf16_append",
+    "oscar_bf16_decode_attn", "oscar_hbm_copy", "oscar_timing_begin", "oscar_timing_end",
+    "oscar_strerror", "BLOCK_BYTES", "PAGE_SIZE", "HEAD_DIM",
+]
+
+BLOCK_BYTES = 1152
+PAGE_SIZE = 16
+HEAD_DIM = 128
+
+
+class OscarError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {lib.oscar_strerror(status).decode()} (status {status})")
+        self.status = status
+
+
+def make_shape(n_q_heads: int, n_kv_heads: int, window: int = 128, head_dim: int = 128,
+               group_size: int = 128, page_size: int = 16) -> OscarShape:
+    return OscarShape(n_q_heads, n_kv_heads, head_dim, group_size, page_size, window)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise OscarError(fn, status)
+
+
+def _dev(t, dtypes, name):
+    """Device pointer of a contiguous torch tensor (None -> NULL)."""
+    if t is None:
+        return None
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    return t.data_ptr()
+
+
+def _dt():
+    import torch
+
+    b16 = (torch.bfloat16, torch.int16, torch.uint16, torch.float16)
+    return b16, (torch.int32,), (torch.uint8,), (torch.float32,)
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def oscar_calibrate(shape: OscarShape, q_cal: np.ndarray, k_cal: np.ndarray, v_cal: np.ndarray):
+    """Host calibration.  q_cal float32 [Hkv][n_q][128]; k_cal, v_cal float32
+    [Hkv][n_kv][128].  Returns (r_k, r_v) uint16 [Hkv][128][128] bf16 bits and
+    (eig_k, eig_v) float64 [Hkv][128]."""
+    q = np.ascontiguousarray(q_cal, dtype=np.float32)
+    k = np.ascontiguousarray(k_cal, dtype=np.float32)
+    v = np.ascontiguousarray(v_cal, dtype=np.float32)
+    hkv = shape.n_kv_heads
+    if q.ndim != 3 or k.shape != v.shape or k.ndim != 3 or q.shape[0] != hkv or k.shape[0] != hkv:
+        raise ValueError("calibration arrays must be [Hkv][n][128]")
+    rk = np.empty((hkv, 128, 128), np.uint16)
+    rv = np.empty_like(rk)
+    ek = np.empty((hkv, 128), np.float64)
+    ev = np.empty_like(ek)
+    _check("oscar_calibrate", lib.oscar_calibrate(
+        C.byref(shape), q.ctypes.data, q.shape[1], k.ctypes.data, v.ctypes.data, k.shape[1],
+        rk.ctypes.data, rv.ctypes.data, ek.ctypes.data, ev.ctypes.data))
+    return rk, rv, ek, ev
+
+
+def oscar_quantize_append(shape, r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,
+                          pool, win_k=None, win_v=None, stream=None) -> None:
+    b16, i32, u8, _ = _dt()
+    _check("oscar_quantize_append", lib.oscar_quantize_append(
+        C.byref(shape), _dev(r_k, b16, "r_k"), _dev(r_v, b16, "r_v"), _dev(k_new, b16, "k_new"),
+        _dev(v_new, b16, "v_new"), int(k_new.shape[0]), _dev(seq_idx, i32, "seq_idx"),
+        _dev(pos, i32, "pos"), int(block_table.shape[0]), _dev(block_table, i32, "block_table"),
+        int(block_table.shape[1]), _dev(seq_len_after, i32, "seq_len_after"), _dev(pool, u8, "pool"),
+        int(pool.shape[0]), _dev(win_k, b16, "win_k"), _dev(win_v, b16, "win_v"), _stream(stream)))
+
+
+def oscar_decode_workspace_bytes(shape, batch: int, max_seq_len: int) -> int:
+    n = lib.oscar_decode_workspace_bytes(C.byref(shape), int(batch), int(max_seq_len))
+    if n == 0:
+        raise OscarError("oscar_decode_workspace_bytes", -1)
+    return int(n)
+
+
+def oscar_decode_attn(shape, r_k, r_v, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v,
+                      out, workspace, stream=None) -> None:
+    b16, i32, u8, f32 = _dt()
+    _check("oscar_decode_attn", lib.oscar_decode_attn(
+        C.byref(shape), _dev(r_k, b16, "r_k"), _dev(r_v, b16, "r_v"), _dev(q, b16, "q"),
+        int(q.shape[0]), _dev(seq_lens, i32, "seq_lens"), int(max_seq_len),
+        _dev(block_table, i32, "block_table"), int(block_table.shape[1]), _dev(pool, u8, "pool"),
+        int(pool.shape[0]), _dev(win_k, b16, "win_k"), _dev(win_v, b16, "win_v"),
+        _dev(out, f32, "out"), _dev(workspace, u8, "workspace"), int(workspace.numel()),
+        _stream(stream)))
+
+
+def oscar_bf16_append(shape, k_new, v_new, seq_idx, pos, block_table, kv_pool, stream=None) -> None:
+    b16, i32, _, _ = _dt()
+    _check("oscar_bf16_append", lib.oscar_bf16_append(
+        C.byref(shape), _dev(k_new, b16, "k_new"), _dev(v_new, b16, "v_new"), int(k_new.shape[0]),
+        _dev(seq_idx, i32, "seq_idx"), _dev(pos, i32, "pos"), int(block_table.shape[0]),
+        _dev(block_table, i32, "block_table"), int(block_table.shape[1]),
+        _dev(kv_pool, b16, "kv_pool"), int(kv_pool.shape[0]), _stream(stream)))
+
+
+def oscar_bf16_decode_attn(shape, q, seq_lens, max_seq_len, block_table, kv_pool, out, workspace,
+                           stream=None) -> None:
+    b16, i32, u8, f32 = _dt()
+    _check("oscar_bf16_decode_attn", lib.oscar_bf16_decode_attn(
+        C.byref(shape), _dev(q, b16, "q"), int(q.shape[0]), _dev(seq_lens, i32, "seq_lens"),
+        int(max_seq_len), _dev(block_table, i32, "block_table"), int(block_table.shape[1]),
+        _dev(kv_pool, b16, "kv_pool"), int(kv_pool.shape[0]), _dev(out, f32, "out"),
+        _dev(workspace, u8, "workspace"), int(workspace.numel()), _stream(stream)))
+
+
+def oscar_hbm_copy(src, dst, nbytes: int | None = None, stream=None) -> None:
+    n = int(src.numel() * src.element_size()) if nbytes is None else int(nbytes)
+    if src.device.type != "cuda" or dst.device.type != "cuda":
+        raise ValueError("oscar_hbm_copy: tensors must be on the GPU")
+    _check("oscar_hbm_copy", lib.oscar_hbm_copy(src.data_ptr(), dst.data_ptr(), n, _stream(stream)))
+
+
+def oscar_timing_begin(capacity: int) -> None:
+    _check("oscar_timing_begin", lib.oscar_timing_begin(int(capacity)))
+
+
+def oscar_timing_end(capacity: int):
+    """Returns (ms, kinds) lists for the recorded main-kernel launches."""
+    ms = (C.c_float * capacity)()
+    kinds = (C.c_int32 * capacity)()
+    n = C.c_int32(0)
+    _check("oscar_timing_end", lib.oscar_timing_end(ms, kinds, int(capacity), C.byref(n)))
+    return list(ms[:n.value]), list(kinds[:n.value])
+
+
+def oscar_strerror(status: int) -> str:
+    return lib.oscar_strerror(int(status)).decode()

@@ -1,0 +1,89 @@
+// Internal helpers shared by the library's translation units (host and device).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "oscar.h"
+
+namespace oscar {
+
+constexpr int kD = 128;          // head dim
+constexpr int kPage = 16;        // tokens per page
+constexpr int kBlock = 1152;     // bytes per (page, KV head) block
+constexpr int kKCodes = 0, kVCodes = 512, kKScale = 1024, kKZero = 1056, kVScale = 1088, kVZero = 1120;
+constexpr int kMaxWindow = 1024;
+constexpr int kPartStride = 2 + kD;  // (m, l, acc[128]) per (batch, q head, split)
+
+// Host-side shape check.  Returns OSCAR_OK or an error.
+inline int check_shape(const oscar_shape* s) {
+  if (!s) return OSCAR_EINVAL;
+  if (s->n_kv_heads < 1 || s->n_q_heads < 1 || s->window < 0) return OSCAR_EINVAL;
+  if (s->head_dim != kD || s->group_size != kD || s->page_size != kPage) return OSCAR_EUNSUPPORTED;
+  if (s->n_q_heads % s->n_kv_heads) return OSCAR_EINVAL;
+  int g = s->n_q_heads / s->n_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return OSCAR_EUNSUPPORTED;
+  if (s->window > kMaxWindow) return OSCAR_EUNSUPPORTED;
+  return OSCAR_OK;
+}
+
+// Split plan of the decode: every (sequence, KV head) history is cut into
+// `n_splits` page-aligned ranges of `split` tokens; one workgroup per range.
+struct SplitPlan {
+  int split;     // tokens per split (multiple of 64)
+  int n_splits;  // splits for the longest sequence
+};
+
+inline SplitPlan plan_splits(int batch, int n_kv_heads, int max_tokens) {
+  // Aim for ~2048 workgroups on the longest sequence; clamp the split between
+  // 256 and 2048 tokens so ragged batches neither starve nor over-split.
+  long units = (long)batch * n_kv_heads;
+  long want = (long)max_tokens * units / 2048;
+  long s = want < 256 ? 256 : (want > 2048 ? 2048 : want);
+  s = (s + 63) / 64 * 64;
+  int n = max_tokens <= 0 ? 1 : (int)((max_tokens + s - 1) / s);
+  return SplitPlan{(int)s, n < 1 ? 1 : n};
+}
+
+// Workspace layout: [qrot: B*Hq*128 fp32][partials: B*Hq*n_splits*130 fp32]
+inline size_t workspace_bytes(int batch, int n_q_heads, const SplitPlan& p) {
+  size_t q = (size_t)batch * n_q_heads * kD * sizeof(float);
+  size_t parts = (size_t)batch * n_q_heads * p.n_splits * kPartStride * sizeof(float);
+  return ((q + 255) / 256 * 256) + parts;
+}
+
+inline size_t qrot_bytes(int batch, int n_q_heads) {
+  return ((size_t)batch * n_q_heads * kD * sizeof(float) + 255) / 256 * 256;
+}
+
+// Event-pair recording around main kernels (measurement only).
+void timing_record_begin(hipStream_t st, int kind, int* slot);
+void timing_record_end(hipStream_t st, int slot);
+
+}  // namespace oscar
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+namespace oscar {
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float h2f(uint16_t b) {
+  _Float16 h = __builtin_bit_cast(_Float16, b);
+  return (float)h;
+}
+__device__ __forceinline__ uint16_t f2h_bits(float x) {  // round to nearest even
+  _Float16 h = (_Float16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace oscar
+#endif

@@ -306,8 +306,9 @@ def read_history(pool, block_table_row, hist: int, h: int):
     vc = unpack_v_words(v_words(blk))                       # [n_pg][16][128]
     f16 = lambda off: fp16_to_f64(np.ascontiguousarray(blk[:, off:off + 32]).view(np.uint16))
     ks, kz, vs, vz = f16(K_SCALE), f16(K_ZERO), f16(V_SCALE), f16(V_ZERO)
-    k = kz[..., None] + kc * ks[..., None]
-    v = vz[..., None] + vc * vs[..., None]
+    with np.errstate(invalid="ignore", over="ignore"):  # unused slots of the last page
+        k = kz[..., None] + kc * ks[..., None]
+        v = vz[..., None] + vc * vs[..., None]
     return k.reshape(-1, D)[:hist], v.reshape(-1, D)[:hist]
 
 
@@ -409,3 +410,77 @@ def effective_bits(bf16_share: float, d: int = D, group: int = 128) -> float:
 
 def bf16_kv_bytes_per_token(n_layers: int, n_kv_heads: int, d: int) -> int:
     return 2 * n_layers * n_kv_heads * d * 2
+
+
+def decode_direct_ref(r_k, r_v, q_bits, k_bits, v_bits, n: int, window: int, kv_head: int):
+    """Decode of one (sequence, KV head) straight from its token sequence, with
+    no pool or ring: the history positions [0, n - w) are encoded with
+    ``quantize`` (the cache's content by definition), the last w = min(n, W)
+    positions are the raw bf16 tokens.  Same attention as ``decode_ref``.
+    q_bits [G][d] (the G query heads of this KV head); k_bits, v_bits [>= n][d].
+    Returns fp64 [G][d]."""
+    d = D
+    w = min(n, window)
+    hist = n - w
+    rk = np.asarray(r_k[kv_head], np.float64)
+    rv = np.asarray(r_v[kv_head], np.float64)
+    kx = bf16_to_f64(np.asarray(k_bits)[:n])
+    vx = bf16_to_f64(np.asarray(v_bits)[:n])
+    ck, sk, zk, _ = quantize(rotate(rk, kx[:hist]))
+    cv, sv, zv, _ = quantize(rotate(rv, vx[:hist]))
+    kh = zk[:, None] + ck * sk[:, None]
+    vh = zv[:, None] + cv * sv[:, None]
+    q = bf16_to_f64(q_bits)
+    out = np.empty((q.shape[0], d))
+    for j in range(q.shape[0]):
+        s = np.concatenate([kh @ (rk @ q[j]), kx[hist:] @ q[j]]) / math.sqrt(d)
+        p = np.exp(s - s.max())
+        out[j] = (rv.T @ (p[:hist] @ vh) + p[hist:] @ vx[hist:]) / p.sum()
+    return out
+
+
+def append_sequence_ref(r_k, r_v, k_bits, v_bits, block_row, pool, win_k, win_v, window: int):
+    """Bulk form of ``append_ref`` for positions 0..n-1 of one sequence appended
+    in order (seq_len_after = n): whole pages are packed at once.  Produces the
+    same bytes as ``append_ref`` (pinned by a test).  k_bits, v_bits [n][Hkv][d];
+    block_row int32 [max_pages]; pool [n_pages][Hkv][1152]; win_k, win_v
+    [W][Hkv][d] (this sequence's ring)."""
+    k_bits = np.asarray(k_bits)
+    n, hkv, _ = k_bits.shape
+    kr = np.empty((n, hkv, D))
+    vr = np.empty((n, hkv, D))
+    for h in range(hkv):   # x' = R x for every token (library matmul per head)
+        kr[:, h] = bf16_to_f64(k_bits[:, h]) @ np.asarray(r_k[h], np.float64).T
+        vr[:, h] = bf16_to_f64(np.asarray(v_bits)[:, h]) @ np.asarray(r_v[h], np.float64).T
+    kc, ks, kz, _ = quantize(kr)
+    vc, vs, vz, _ = quantize(vr)
+    del kr, vr
+    n_pg = -(-n // PAGE)
+    pad = n_pg * PAGE - n
+    padt = lambda a: np.concatenate([a, np.zeros((pad,) + a.shape[1:], a.dtype)]) if pad else a
+    kc, vc = padt(kc), padt(vc)
+    bits = {o: padt(fp16_bits(x)) for o, x in ((K_SCALE, ks), (K_ZERO, kz), (V_SCALE, vs), (V_ZERO, vz))}
+    pages = np.asarray(block_row[:n_pg], np.int64)
+    assert np.all(pages >= 0)
+    krow = pack_k_row(kc).reshape(n_pg, PAGE, hkv, 32)             # [pg][slot][h][32]
+    vcode = vc.reshape(n_pg, PAGE, hkv, D).astype(np.uint32)       # [pg][slot][h][c]
+    slots = np.arange(PAGE)
+    nslot = np.full(n_pg, PAGE)
+    nslot[-1] = PAGE - pad
+    for j, pg in enumerate(pages):
+        m = slots < nslot[j]
+        blk = pool[pg]                                              # [Hkv][1152]
+        kb = blk[:, K_CODES:K_CODES + 512].reshape(hkv, PAGE, 32)
+        kb[:, m] = krow[j][m].transpose(1, 0, 2)
+        words = np.ascontiguousarray(blk[:, V_CODES:V_CODES + 512]).view("<u4").copy()  # [Hkv][128]
+        keep = ~np.uint32(sum(3 << (2 * int(t)) for t in slots[m]))
+        words &= keep
+        words |= np.bitwise_or.reduce((vcode[j][m] << (2 * slots[m])[:, None, None].astype(np.uint32)), axis=0)
+        blk[:, V_CODES:V_CODES + 512] = words.astype("<u4").view(np.uint8).reshape(hkv, 512)
+        for off, b in bits.items():
+            f = blk[:, off:off + 32].reshape(hkv, PAGE, 2)
+            f[:, m] = np.ascontiguousarray(b[j * PAGE:(j + 1) * PAGE][m].T).view(np.uint8).reshape(hkv, -1, 2)
+    if window > 0:
+        for p in range(max(0, n - window), n):
+            win_k[p % window] = k_bits[p]
+            win_v[p % window] = v_bits[p]

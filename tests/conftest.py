@@ -16,3 +16,7 @@ def pytest_configure(config):
 def rng():
     import numpy as np
     return np.random.default_rng(12345)
+
+TESTS = os.path.dirname(os.path.abspath(__file__))
+if TESTS not in sys.path:
+    sys.path.insert(0, TESTS)

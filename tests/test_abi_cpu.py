@@ -1,0 +1,135 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/oscar.h declares, rejects bad arguments on the host before any launch,
+and its host-side calibration matches the oracle."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import oscar_ref as ref
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oscar.h")
+
+K = pytest.importorskip("kv_cache_int2_amd", reason="library not built")
+from kv_cache_int2_amd import _lib  # noqa: E402
+
+EINVAL, EUNSUP, ENOSPACE = -1, -2, -4
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(oscar_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared()
+    assert len(names) >= 10
+    lib = C.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_strerror():
+    assert K.oscar_strerror(0) == "ok"
+    assert "invalid" in K.oscar_strerror(EINVAL)
+    assert "unsupported" in K.oscar_strerror(EUNSUP)
+
+
+def bad_shapes():
+    return [K.make_shape(32, 8, head_dim=64), K.make_shape(32, 8, group_size=32),
+            K.make_shape(32, 8, page_size=32), K.make_shape(24, 8), K.make_shape(32, 8, window=4096)]
+
+
+def test_host_validation_before_launch():
+    lib = _lib.lib
+    good = K.make_shape(32, 8)
+    for s in bad_shapes():
+        st = lib.oscar_quantize_append(C.byref(s), *([None] * 4), 1, None, None, 1, None, 1, None, None, 1,
+                                       None, None, None)
+        assert st in (EINVAL, EUNSUP)
+        assert lib.oscar_decode_workspace_bytes(C.byref(s), 1, 100) == 0
+    assert lib.oscar_quantize_append(C.byref(K.make_shape(32, 8, head_dim=64)), *([None] * 4), 1, None, None,
+                                     1, None, 1, None, None, 1, None, None, None) == EUNSUP
+    # null pointers
+    assert lib.oscar_quantize_append(C.byref(good), *([None] * 4), 5, None, None, 1, None, 1, None, None, 1,
+                                     None, None, None) == EINVAL
+    # zero tokens is a no-op
+    assert lib.oscar_quantize_append(C.byref(good), *([None] * 4), 0, None, None, 1, None, 1, None, None, 1,
+                                     None, None, None) == 0
+    ws = lib.oscar_decode_workspace_bytes(C.byref(good), 8, 100000)
+    assert ws > 8 * 32 * 128 * 4
+    # workspace too small / sequence longer than the block table
+    fake = C.c_void_p(256)
+    args = [C.byref(good), fake, fake, fake, 8, fake, 100000, fake, 100000 // 16 + 1, fake, 1, fake, fake, fake,
+            fake]
+    assert lib.oscar_decode_attn(*args, ws - 1, None) == ENOSPACE
+    args[8] = 100
+    assert lib.oscar_decode_attn(*args, ws, None) == ENOSPACE
+    assert lib.oscar_decode_attn(C.byref(good), None, None, None, 8, None, 10, None, 1, None, 1, None, None,
+                                 None, None, 0, None) == EINVAL
+    assert lib.oscar_hbm_copy(fake, fake, 17, None) == EINVAL
+    assert lib.oscar_timing_end(None, None, 0, None) == EINVAL
+
+
+def test_calibrate_rejects_bad_input():
+    s = K.make_shape(32, 8)
+    q = np.zeros((8, 4, 128), np.float32)
+    k = np.zeros((8, 4, 128), np.float32)
+    q[0, 0, 0] = np.nan
+    with pytest.raises(K.OscarError):
+        K.oscar_calibrate(s, q, k, k)
+    with pytest.raises(K.OscarError):
+        K.oscar_calibrate(K.make_shape(32, 8, head_dim=64), q * 0, k, k)
+
+
+def near_bf16_midpoint(x, rel=1e-9):
+    """True where x lies within rel*|x| of a bf16 rounding midpoint."""
+    lo = ref.bf16_rne(x * (1 - rel))
+    hi = ref.bf16_rne(x * (1 + rel))
+    return lo != hi
+
+
+def test_calibrate_matches_oracle():
+    """Host Jacobi calibration vs the oracle (numpy eigh) on the config-1
+    calibration set: eigenvalues to 1e-9 relative; R bf16 bits equal wherever the
+    oracle's fp64 value is not within 1e-9 of a bf16 midpoint (eigenvectors of
+    distinct eigenvalues are unique once the sign convention is fixed)."""
+    s = wl.spec(1)
+    qc, kc, vc = wl.calibration_set(s)
+    shape = K.make_shape(32, 8)
+    rk, rv, ek, ev = K.oscar_calibrate(shape, qc, kc, vc)
+    rk_ref, rv_ref, ek_ref, ev_ref = ref.calibrate_ref(qc, kc, vc)
+    assert np.allclose(ek, ek_ref, rtol=1e-9, atol=1e-12 * ek_ref.max())
+    assert np.allclose(ev, ev_ref, rtol=1e-9, atol=1e-12 * ev_ref.max())
+    for got, want in ((rk, rk_ref), (rv, rv_ref)):
+        ok = ~near_bf16_midpoint(want)
+        assert ok.mean() > 0.999
+        assert np.array_equal(got[ok], ref.bf16_bits(want)[ok])
+        # the bf16 R is orthogonal to bf16 precision
+        r = ref.bf16_to_f64(got)
+        assert np.abs(np.einsum("hij,hkj->hik", r, r) - np.eye(128)).max() < 2e-2
+
+
+def test_calibrate_special_case_diagonal():
+    """Queries along the coordinate axes with distinct energies: U_Q = I up to
+    order, so R_K = P_br (H / sqrt d) P where P sorts the axes by energy."""
+    d = 128
+    shape = K.make_shape(1, 1)
+    energy = np.linspace(2.0, 1.0, d)
+    perm = np.random.default_rng(3).permutation(d)
+    q = np.zeros((1, d, d), np.float32)
+    q[0, np.arange(d), perm] = np.sqrt(d * energy).astype(np.float32)
+    k = np.random.default_rng(4).standard_normal((1, 64, d)).astype(np.float32)
+    rk, _, ek, _ = K.oscar_calibrate(shape, q, k, k)
+    want_e = np.sort((q[0].astype(np.float64) ** 2).sum(0) / d)[::-1]
+    assert np.allclose(ek[0], want_e, rtol=1e-12)
+    u = np.zeros((d, d))
+    u[perm, np.arange(d)] = 1.0  # eigenvector k is axis perm[k] (energies sorted descending)
+    want = ref.apply_bitrev_rows(ref.hadamard(d) / np.sqrt(d) @ u.T)
+    assert np.array_equal(rk[0], ref.bf16_bits(want))

@@ -1,0 +1,465 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Rotations come from the oracle's calibration (as data for both sides).  Small
+cases compare every output; the full-size workloads (run in the same launch
+configuration as bench.py) compare sampled outputs and size-independent
+properties.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import workloads as wl  # noqa: E402
+from oracle import oscar_ref as ref  # noqa: E402
+import parity as P  # noqa: E402
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def K():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import kv_cache_int2_amd as K
+
+    return K
+
+
+DEV = "cuda:0"
+
+
+def D(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def H(t, dtype=None):
+    a = t.cpu().numpy()
+    if dtype is not None:
+        a = a.view(dtype)
+    return a
+
+
+@functools.lru_cache(maxsize=None)
+def rotations(cfg, hkv=8):
+    s = wl.spec(cfg)
+    qc, kc, vc = wl.calibration_set(s)
+    rk, rv, _, _ = ref.calibrate_ref(qc[:hkv], kc[:hkv], vc[:hkv])
+    return ref.bf16_bits(rk), ref.bf16_bits(rv)
+
+
+def make_spec(cfg, lens, window=128, hq=None, hkv=8):
+    s = wl.spec(cfg, batch=len(lens))
+    s.seq_lens = np.asarray(lens, np.int32)
+    s.window = window
+    if hq is not None:
+        s.n_q_heads = hq
+    s.n_kv_heads = hkv
+    return s
+
+
+def token_list(s, order="inorder", rng=None):
+    ks, vs, si, ps = [], [], [], []
+    for b in range(s.batch):
+        k, v, i, p = wl.prefill_tokens(s, b)
+        ks.append(k[:, :s.n_kv_heads])
+        vs.append(v[:, :s.n_kv_heads])
+        si.append(i)
+        ps.append(p)
+    k, v, si, ps = (np.concatenate(x) for x in (ks, vs, si, ps))
+    if order == "shuffled":
+        o = rng.permutation(len(ps))
+        k, v, si, ps = k[o], v[o], si[o], ps[o]
+    return np.ascontiguousarray(k), np.ascontiguousarray(v), si, ps
+
+
+def run_append(K, s, rk, rv, k, v, si, ps, bt, pool0, wk0, wv0, lens_after):
+    shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window)
+    pool = D(pool0)
+    wk = D(wk0) if s.window > 0 else None
+    wv = D(wv0) if s.window > 0 else None
+    K.oscar_quantize_append(shape, D(rk), D(rv), D(k), D(v), D(si), D(ps), D(bt), D(lens_after),
+                            pool, wk, wv)
+    torch.cuda.synchronize()
+    return H(pool), (H(wk, np.uint16) if wk is not None else None), (H(wv, np.uint16) if wv is not None else None)
+
+
+def append_case(K, s, order="inorder", split_at=None, seed=0):
+    rng = np.random.default_rng(seed)
+    rk, rv = rotations(s.cfg, s.n_kv_heads)
+    rkf, rvf = ref.bf16_to_f64(rk), ref.bf16_to_f64(rv)
+    bt, n_pages = wl.page_table(s)
+    pool0 = rng.integers(0, 256, (n_pages, s.n_kv_heads, ref.BLOCK), dtype=np.uint8)
+    wsh = (s.batch, max(s.window, 1), s.n_kv_heads, 128)
+    wk0 = rng.integers(0, 65536, wsh, dtype=np.uint16)
+    wv0 = rng.integers(0, 65536, wsh, dtype=np.uint16)
+    k, v, si, ps = token_list(s, order, rng)
+    chunks = [(0, len(ps))] if split_at is None else [(0, split_at), (split_at, len(ps))]
+    pool_ref, wk_ref, wv_ref = pool0.copy(), wk0.copy(), wv0.copy()
+    pool_g, wk_g, wv_g = pool0, wk0, wv0
+    for a, b in chunks:
+        pool_g, wk_g2, wv_g2 = run_append(K, s, rk, rv, k[a:b], v[a:b], si[a:b], ps[a:b], bt, pool_g, wk_g, wv_g,
+                                          s.seq_lens)
+        if s.window > 0:
+            wk_g, wv_g = wk_g2, wv_g2
+        ref.append_ref(rkf, rvf, k[a:b], v[a:b], si[a:b], ps[a:b], bt, s.seq_lens, pool_ref, wk_ref, wv_ref,
+                       s.window)
+    mism, excl, stray = P.check_append(pool0, pool_g, rkf, rvf, k, v, si, ps, bt)
+    log(f"append {s.cfg} lens={list(s.seq_lens)} W={s.window} {order}: mismatches={mism} excluded={excl} stray={stray}")
+    assert mism == 0 and stray == 0
+    if s.window > 0:
+        assert np.array_equal(wk_g, wk_ref) and np.array_equal(wv_g, wv_ref)
+    return excl
+
+
+def test_append_inorder_ragged(K):
+    append_case(K, make_spec(1, [300]))
+
+
+def test_append_shuffled_multi_sequence(K):
+    append_case(K, make_spec(1, [300, 37, 129], window=100), order="shuffled", seed=1)
+
+
+def test_append_continuation_mid_page(K):
+    append_case(K, make_spec(1, [300, 70]), split_at=20, seed=2)
+
+
+def test_append_no_window(K):
+    append_case(K, make_spec(1, [77, 200], window=0), seed=3)
+
+
+def test_append_single_tokens(K):
+    s = make_spec(5, [40, 17, 1, 99, 64], hq=64)
+    rng = np.random.default_rng(4)
+    rk, rv = rotations(5)
+    rkf, rvf = ref.bf16_to_f64(rk), ref.bf16_to_f64(rv)
+    bt, n_pages = wl.page_table(s)
+    pool0 = rng.integers(0, 256, (n_pages, 8, ref.BLOCK), dtype=np.uint8)
+    wk0 = rng.integers(0, 65536, (5, 128, 8, 128), dtype=np.uint16)
+    wv0 = wk0.copy()
+    k, v = wl.step_tokens(s, 1)
+    si = np.arange(5, dtype=np.int32)
+    ps = (s.seq_lens - 1).astype(np.int32)
+    pool_g, wk_g, wv_g = run_append(K, s, rk, rv, k, v, si, ps, bt, pool0, wk0, wv0, s.seq_lens)
+    mism, excl, stray = P.check_append(pool0, pool_g, rkf, rvf, k, v, si, ps, bt)
+    assert mism == 0 and stray == 0
+    wk_ref, wv_ref = wk0.copy(), wv0.copy()
+    pool_ref = pool0.copy()
+    ref.append_ref(rkf, rvf, k, v, si, ps, bt, s.seq_lens, pool_ref, wk_ref, wv_ref, 128)
+    assert np.array_equal(wk_g, wk_ref) and np.array_equal(wv_g, wv_ref)
+
+
+def test_append_empty_is_noop(K):
+    s = make_spec(1, [16])
+    shape = K.make_shape(32, 8, 128)
+    pool = torch.zeros((1, 8, K.BLOCK_BYTES), dtype=torch.uint8, device=DEV)
+    e = torch.zeros((0, 8, 128), dtype=torch.int16, device=DEV)
+    i = torch.zeros((0,), dtype=torch.int32, device=DEV)
+    rk, rv = rotations(1)
+    K.oscar_quantize_append(shape, D(rk), D(rv), e, e, i, i, D(np.zeros((1, 1), np.int32)),
+                            D(np.array([16], np.int32)), pool, None, None)
+    torch.cuda.synchronize()
+    assert int(pool.sum()) == 0
+
+
+# ---------------------------------------------------------------------------
+# decode on oracle-built caches
+# ---------------------------------------------------------------------------
+
+def oracle_cache(s, seed=0):
+    rk, rv = rotations(s.cfg, s.n_kv_heads)
+    rkf, rvf = ref.bf16_to_f64(rk), ref.bf16_to_f64(rv)
+    bt, n_pages = wl.page_table(s)
+    rng = np.random.default_rng(seed)
+    # unused slots hold random bytes (the decode must never read them)
+    pool = rng.integers(0, 256, (n_pages, s.n_kv_heads, ref.BLOCK), dtype=np.uint8)
+    wk = np.zeros((s.batch, max(s.window, 1), s.n_kv_heads, 128), np.uint16)
+    wv = np.zeros_like(wk)
+    k, v, si, ps = token_list(s)
+    ref.append_ref(rkf, rvf, k, v, si, ps, bt, s.seq_lens, pool, wk, wv, s.window)
+    q = wl.decode_queries(s)[:, :s.n_q_heads]
+    return rk, rv, rkf, rvf, bt, pool, wk, wv, q
+
+
+def run_decode(K, s, rk, rv, q, bt, pool, wk, wv, max_len=None):
+    shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window)
+    max_len = int(s.seq_lens.max()) if max_len is None else max_len
+    ws = torch.empty(K.oscar_decode_workspace_bytes(shape, s.batch, max_len), dtype=torch.uint8, device=DEV)
+    out = torch.full((s.batch, s.n_q_heads, 128), float("nan"), dtype=torch.float32, device=DEV)
+    K.oscar_decode_attn(shape, D(rk), D(rv), D(q), D(s.seq_lens), max_len, D(bt), D(pool),
+                        D(wk) if s.window > 0 else None, D(wv) if s.window > 0 else None, out, ws)
+    torch.cuda.synchronize()
+    return H(out)
+
+
+@pytest.mark.parametrize("cfg,lens,window,hq", [
+    (1, [1000, 777], 128, 32),        # several splits, ragged tails
+    (5, [600, 129, 128], 128, 64),     # G = 8; n = W + 1; n = W
+    (1, [1, 50], 128, 32),             # pure window
+    (1, [300], 0, 32),                 # no window
+    (1, [700, 333], 100, 8),           # G = 1, window not a multiple of 16
+    (1, [515], 128, 16),               # G = 2
+    (1, [260, 1030], 128, 128),        # G = 16
+    (1, [4100, 2500, 16], 128, 32),    # longer, splits of 256+ tokens
+])
+def test_decode_small(K, cfg, lens, window, hq):
+    s = make_spec(cfg, lens, window, hq)
+    rk, rv, rkf, rvf, bt, pool, wk, wv, q = oracle_cache(s)
+    got = run_decode(K, s, rk, rv, q, bt, pool, wk, wv)
+    want = ref.decode_ref(rkf, rvf, q, s.seq_lens, bt, pool, wk, wv, window)
+    err = P.attn_rel_err(got, want)
+    log(f"decode lens={lens} W={window} Hq={hq}: max rel err {err.max():.3e}")
+    assert np.isfinite(got).all()
+    assert err.max() <= P.ATTN_TOL
+
+
+def test_decode_max_len_above_actual(K):
+    """The split plan follows the host max_seq_len; shorter sequences still work."""
+    s = make_spec(1, [900, 20])
+    rk, rv, rkf, rvf, bt, pool, wk, wv, q = oracle_cache(s)
+    bt2 = np.full((2, 400), -1, np.int32)
+    bt2[:, :bt.shape[1]] = bt
+    got = run_decode(K, s, rk, rv, q, bt2, pool, wk, wv, max_len=6000)
+    want = ref.decode_ref(rkf, rvf, q, s.seq_lens, bt, pool, wk, wv, 128)
+    assert P.attn_rel_err(got, want).max() <= P.ATTN_TOL
+
+
+def test_bf16_comparator_small(K):
+    s = make_spec(1, [1000, 77])
+    bt, n_pages = wl.page_table(s)
+    kv = np.zeros((n_pages, 8, 2, 16, 128), np.uint16)
+    k, v, si, ps = token_list(s)
+    ref.append_bf16_ref(k, v, si, ps, bt, kv)
+    q = wl.decode_queries(s)
+    shape = K.make_shape(32, 8, 128)
+    kvd = torch.zeros((n_pages, 8, 2, 16, 128), dtype=torch.int16, device=DEV)
+    K.oscar_bf16_append(shape, D(k), D(v), D(si), D(ps), D(bt), kvd)
+    torch.cuda.synchronize()
+    assert np.array_equal(H(kvd, np.uint16), kv)
+    ws = torch.empty(K.oscar_decode_workspace_bytes(shape, 2, 1000), dtype=torch.uint8, device=DEV)
+    out = torch.empty((2, 32, 128), dtype=torch.float32, device=DEV)
+    K.oscar_bf16_decode_attn(shape, D(q), D(s.seq_lens), 1000, D(bt), kvd, out, ws)
+    torch.cuda.synchronize()
+    want = ref.decode_bf16_ref(q, s.seq_lens, bt, kv, 8)
+    assert P.attn_rel_err(H(out), want).max() <= P.ATTN_TOL
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads (sampled checks)
+# ---------------------------------------------------------------------------
+
+def full_cache(K, s, keep=()):
+    """Prefill every sequence of workload s through the HIP append; returns the
+    device state and the host token arrays of the sequences in ``keep``."""
+    shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window)
+    rk, rv = rotations(s.cfg)
+    rkd, rvd = D(rk), D(rv)
+    bt, n_pages = wl.page_table(s)
+    btd, lensd = D(bt), D(s.seq_lens)
+    pool = torch.zeros((n_pages, 8, K.BLOCK_BYTES), dtype=torch.uint8, device=DEV)
+    wk = torch.zeros((s.batch, s.window, 8, 128), dtype=torch.int16, device=DEV)
+    wv = torch.zeros_like(wk)
+    kept = {}
+    for b in range(s.batch):
+        k, v, si, ps = wl.prefill_tokens(s, b)
+        K.oscar_quantize_append(shape, rkd, rvd, D(k), D(v), D(si), D(ps), btd, lensd, pool, wk, wv)
+        if b in keep:
+            kept[b] = (k, v)
+    torch.cuda.synchronize()
+    return dict(shape=shape, rk=rk, rv=rv, rkd=rkd, rvd=rvd, bt=bt, btd=btd, pool=pool, wk=wk, wv=wv, kept=kept)
+
+
+def decode_full(K, s, c, q, lens):
+    ws = torch.empty(K.oscar_decode_workspace_bytes(c["shape"], s.batch, int(lens.max())), dtype=torch.uint8,
+                     device=DEV)
+    out = torch.empty((s.batch, s.n_q_heads, 128), dtype=torch.float32, device=DEV)
+    K.oscar_decode_attn(c["shape"], c["rkd"], c["rvd"], D(q), D(lens), int(lens.max()), c["btd"], c["pool"],
+                        c["wk"], c["wv"], out, ws)
+    torch.cuda.synchronize()
+    return H(out)
+
+
+def oracle_overwrite(s, c, b, extra=None):
+    """Encode sequence b with the oracle (its tokens plus ``extra``) and upload
+    the bytes of its pages and its window ring into the device cache, so the
+    device decode of b runs on exactly the oracle's cache.  Returns the oracle's
+    local copy (pool rows of b's pages, window ring) for ``decode_ref``."""
+    k, v = c["kept"][b]
+    if extra is not None:
+        k = np.concatenate([k, extra[0]])
+        v = np.concatenate([v, extra[1]])
+    n = len(k)
+    n_pg = -(-n // 16)
+    pages = torch.from_numpy(c["bt"][b][:n_pg].astype(np.int64)).to(DEV)
+    local = H(c["pool"].index_select(0, pages))
+    wk = np.zeros((s.window, 8, 128), np.uint16)
+    wv = np.zeros_like(wk)
+    ref.append_sequence_ref(ref.bf16_to_f64(c["rk"]), ref.bf16_to_f64(c["rv"]), k, v, np.arange(n_pg, dtype=np.int32),
+                            local, wk, wv, s.window)
+    c["pool"].index_copy_(0, pages, D(local))
+    c["wk"][b] = D(wk)
+    c["wv"][b] = D(wv)
+    torch.cuda.synchronize()
+    return local, wk, wv, n
+
+
+def check_sampled(s, c, q, got, pairs, oracle):
+    """oracle: {b: (local pool, window k, window v, n)} from oracle_overwrite."""
+    rkf, rvf = ref.bf16_to_f64(c["rk"]), ref.bf16_to_f64(c["rv"])
+    g = s.gqa
+    worst = 0.0
+    for b, h in pairs:
+        local, wk, wv, n = oracle[b]
+        row = np.arange(local.shape[0], dtype=np.int32)[None]
+        want = ref.decode_ref(rkf, rvf, q[b:b + 1], np.array([n]), row, local, wk[None], wv[None], s.window,
+                              pairs=[(0, h)])[0, h * g:(h + 1) * g]
+        err = P.attn_rel_err(got[b, h * g:(h + 1) * g], want)
+        worst = max(worst, float(err.max()))
+    log(f"config {s.cfg}: sampled pairs {pairs}: max rel err {worst:.3e}")
+    assert worst <= P.ATTN_TOL
+
+
+def sampled_append_check(s, c, b, n_sample=512, seed=0):
+    rng = np.random.default_rng(seed)
+    k, v = c["kept"][b]
+    idx = rng.choice(len(k), size=min(n_sample, len(k)), replace=False)
+    pool = H(c["pool"])
+    pos = np.arange(len(k), dtype=np.int32)
+    si = np.full(len(k), b, np.int32)
+    mism, excl, _ = P.check_append(None, pool, ref.bf16_to_f64(c["rk"]), ref.bf16_to_f64(c["rv"]), k, v, si, pos,
+                                   c["bt"], sample=idx)
+    log(f"config {s.cfg} seq {b}: {len(idx)} sampled tokens, mismatches={mism} excluded={excl}")
+    assert mism == 0
+    return pool
+
+
+def codes_span_levels(pool, bt, lens, hkv=8):
+    """Every written group holds codes 0 and 3 (its min and max), any size."""
+    for b in range(len(lens)):
+        n = int(lens[b])
+        pages = bt[b][:(n + 15) // 16]
+        for c0 in range(0, len(pages), 256):
+            pg = pages[c0:c0 + 256]
+            blk = pool[pg]                                                   # [np][hkv][1152]
+            kc = ref.unpack_k_rows(blk[..., :512].reshape(len(pg), hkv, 16, 32)).astype(np.int8)
+            vc = ref.unpack_v_words(ref.v_words(blk)).astype(np.int8)       # [np][hkv][16][128]
+            ntok = min(16 * len(pg), n - 16 * c0)
+            for cc in (kc, vc):
+                cc = cc.transpose(0, 2, 1, 3).reshape(-1, hkv, 128)[:ntok]
+                assert (cc.min(-1) == 0).all() and (cc.max(-1) == 3).all()
+
+
+def test_full_config1(K):
+    s = wl.spec(1)
+    log("config 1 full: building cache")
+    c = full_cache(K, s, keep=(0,))
+    q = wl.decode_queries(s)
+    pool = sampled_append_check(s, c, 0, n_sample=2048)
+    codes_span_levels(pool, c["bt"], s.seq_lens)
+    oracle = {0: oracle_overwrite(s, c, 0)}
+    got = decode_full(K, s, c, q, s.seq_lens)
+    check_sampled(s, c, q, got, [(0, h) for h in range(8)], oracle)
+
+
+def test_full_config4_append(K):
+    s = wl.spec(4)
+    log("config 4 full: appending 65536 tokens")
+    c = full_cache(K, s, keep=(0,))
+    pool = sampled_append_check(s, c, 0, n_sample=1024, seed=4)
+    codes_span_levels(pool, c["bt"], s.seq_lens)
+    k, v = c["kept"][0]
+    assert np.array_equal(H(c["wk"], np.uint16)[0][np.arange(65536 - 128, 65536) % 128], k[-128:])
+    assert np.array_equal(H(c["wv"], np.uint16)[0][np.arange(65536 - 128, 65536) % 128], v[-128:])
+
+
+def test_full_config2(K):
+    s = wl.spec(2)
+    log("config 2 full: building cache")
+    c = full_cache(K, s, keep=(3, 11))
+    q = wl.decode_queries(s)
+    sampled_append_check(s, c, 11, n_sample=512, seed=2)
+    oracle = {b: oracle_overwrite(s, c, b) for b in (3, 11)}
+    got = decode_full(K, s, c, q, s.seq_lens)
+    assert np.isfinite(got).all()
+    check_sampled(s, c, q, got, [(3, 0), (3, 5), (11, 7)], oracle)
+
+
+def test_full_config3(K):
+    s = wl.spec(3)
+    log("config 3 full: building cache")
+    c = full_cache(K, s, keep=(2, 7))
+    q = wl.decode_queries(s)
+    sampled_append_check(s, c, 7, n_sample=512, seed=3)
+    oracle = {b: oracle_overwrite(s, c, b) for b in (2, 7)}
+    got = decode_full(K, s, c, q, s.seq_lens)
+    assert np.isfinite(got).all()
+    check_sampled(s, c, q, got, [(2, 1), (7, 6)], oracle)
+
+
+def test_full_config5_two_steps(K):
+    s = wl.spec(5)
+    log(f"config 5 full: lens sum {int(s.seq_lens.sum())} max {int(s.seq_lens.max())}")
+    longest = int(np.argmax(s.seq_lens))
+    keep = (0, longest)
+    c = full_cache(K, s, keep=keep)
+    q0 = wl.decode_queries(s, 0)
+    sampled_append_check(s, c, longest, n_sample=256, seed=5)
+    oracle = {b: oracle_overwrite(s, c, b) for b in keep}
+    got0 = decode_full(K, s, c, q0, s.seq_lens)
+    check_sampled(s, c, q0, got0, [(0, 3), (longest, 5)], oracle)
+    # append one token per sequence through the device, then decode again
+    lens1 = (s.seq_lens + 1).astype(np.int32)
+    k1, v1 = wl.step_tokens(s, 1)
+    pool_before = H(c["pool"])
+    K.oscar_quantize_append(c["shape"], c["rkd"], c["rvd"], D(k1), D(v1), D(np.arange(s.batch, dtype=np.int32)),
+                            D(s.seq_lens), c["btd"], D(lens1), c["pool"], c["wk"], c["wv"])
+    torch.cuda.synchronize()
+    mism, excl, stray = P.check_append(pool_before, H(c["pool"]), ref.bf16_to_f64(c["rk"]), ref.bf16_to_f64(c["rv"]),
+                                       k1, v1, np.arange(s.batch), s.seq_lens, c["bt"])
+    assert mism == 0 and stray == 0
+    q1 = wl.decode_queries(s, 1)
+    oracle = {b: oracle_overwrite(s, c, b, extra=(k1[b:b + 1], v1[b:b + 1])) for b in keep}
+    got1 = decode_full(K, s, c, q1, lens1)
+    check_sampled(s, c, q1, got1, [(0, 0), (longest, 7)], oracle)
+
+
+def test_full_config3_bf16_comparator(K):
+    s = wl.spec(3)
+    shape = K.make_shape(32, 8, 128)
+    bt, n_pages = wl.page_table(s)
+    btd = D(bt)
+    kv = torch.zeros((n_pages, 8, 2, 16, 128), dtype=torch.int16, device=DEV)
+    kept = {}
+    for b in range(s.batch):
+        k, v, si, ps = wl.prefill_tokens(s, b)
+        K.oscar_bf16_append(shape, D(k), D(v), D(si), D(ps), btd, kv)
+        if b in (5,):
+            kept[b] = (k, v)
+    q = wl.decode_queries(s)
+    ws = torch.empty(K.oscar_decode_workspace_bytes(shape, 8, 100000), dtype=torch.uint8, device=DEV)
+    out = torch.empty((8, 32, 128), dtype=torch.float32, device=DEV)
+    K.oscar_bf16_decode_attn(shape, D(q), D(s.seq_lens), 100000, btd, kv, out, ws)
+    torch.cuda.synchronize()
+    k, v = kept[5]
+    got = H(out)
+    worst = 0.0
+    for h in (0, 4):
+        kk = ref.bf16_to_f64(k[:, h])
+        vv = ref.bf16_to_f64(v[:, h])
+        for j in range(4):
+            qq = ref.bf16_to_f64(q[5, 4 * h + j])
+            sc = kk @ qq / np.sqrt(128)
+            p = np.exp(sc - sc.max())
+            want = (p @ vv) / p.sum()
+            worst = max(worst, np.abs(got[5, 4 * h + j] - want).max() / np.abs(want).max())
+    log(f"bf16 comparator config 3 sampled: max rel err {worst:.3e}")
+    assert worst <= P.ATTN_TOL

@@ -171,3 +171,27 @@ def test_append_ref_keeps_other_slots_and_skips_old_window_positions(rng):
     assert not wk_before[0].any()
     for p in range(24, 40):
         assert np.array_equal(win_k[0, p % 16], k[p])
+
+
+def test_bulk_sequence_append_equals_per_token_append(rng):
+    """append_sequence_ref is byte-identical to append_ref for an in-order prefill."""
+    for n, window in ((37, 16), (64, 128), (1, 4)):
+        s, bt, pool, win_k, win_v = small_cache(batch=1, lens=(n,), window=window)
+        rk, rv = random_rotations(rng, s.n_kv_heads)
+        k, v, si, pos = wl.prefill_tokens(s, 0)
+        pool_a, wk_a, wv_a = pool.copy(), win_k.copy(), win_v.copy()
+        ref.append_ref(rk, rv, k, v, si, pos, bt, s.seq_lens, pool_a, wk_a, wv_a, window)
+        pool_b = rng.integers(0, 256, pool.shape, dtype=np.uint8)
+        used = np.zeros(pool.shape[0], bool)
+        used[bt[0][bt[0] >= 0]] = True
+        pool_b0 = pool_b.copy()
+        wk_b, wv_b = win_k.copy(), win_v.copy()
+        ref.append_sequence_ref(rk, rv, k, v, bt[0], pool_b, wk_b[0], wv_b[0], window)
+        # written slots equal; unwritten bytes of the last page keep their old values
+        kh_a, vh_a = ref.read_history(pool_a, bt[0], n, 2)
+        kh_b, vh_b = ref.read_history(pool_b, bt[0], n, 2)
+        assert np.array_equal(kh_a, kh_b) and np.array_equal(vh_a, vh_b)
+        pool_c = pool_b0.copy()
+        ref.append_ref(rk, rv, k, v, si, pos, bt, s.seq_lens, pool_c, win_k.copy(), win_v.copy(), window)
+        assert np.array_equal(pool_b, pool_c)
+        assert np.array_equal(wk_b, wk_a) and np.array_equal(wv_b, wv_a)

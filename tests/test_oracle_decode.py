@@ -154,3 +154,15 @@ def test_bf16_comparator_is_sdpa(rng):
         qq = torch.from_numpy(ref.bf16_to_f64(q[b])).view(8, 4, 1, 128)
         o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv).reshape(32, 128).numpy()
         assert np.allclose(got[b], o, rtol=1e-12, atol=1e-13)
+
+
+def test_direct_decode_equals_paged_decode(rng):
+    lens, window = (300, 20, 129), 128
+    s, bt, pool, wk, wv, rk, rv, kv, q = build(rng, lens, window)
+    full = ref.decode_ref(rk, rv, q, s.seq_lens, bt, pool, wk, wv, window)
+    for b in range(3):
+        k, v = kv[b]
+        for h in range(2):
+            got = ref.decode_direct_ref(rk, rv, q[b, 4 * h:4 * h + 4], k[:, h], v[:, h], lens[b], window, h)
+            assert np.array_equal(got, full[b, 4 * h:4 * h + 4]) or np.allclose(got, full[b, 4 * h:4 * h + 4],
+                                                                              rtol=1e-13, atol=1e-15)
