@@ -42,8 +42,8 @@
  *   [   0,  512)  K codes: 16 token rows x 32 B; channel c at bit 2c of the row
  *   [ 512, 1024)  V codes: 128 channel words (uint32, little endian); token slot
  *                 j of the page at bits 2j..2j+1
- *   [1024, 1056)  K scale fp16[16]   [1056, 1088)  K zero fp16[16]
- *   [1088, 1120)  V scale fp16[16]   [1120, 1152)  V zero fp16[16]
+ *   [1024, 1152)  16 token records of 8 bytes, slot j at 1024 + 8j:
+ *                 fp16 K scale, K zero, V scale, V zero
  * A token at position pos of sequence b lives in page block_table[b][pos / 16],
  * slot pos % 16.  Dequantised rotated value of channel c: zero + code * scale.
  * bf16 window ring: [batch][window][n_kv_heads][128], position pos in slot pos % window.

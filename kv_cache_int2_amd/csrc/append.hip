@@ -142,8 +142,7 @@ __device__ __forceinline__ void process_tile(const AppendParams& p, const uint4*
       if (g == 2) out = make_uint2(dw[4], dw[5]);
       if (g == 3) out = make_uint2(dw[6], dw[7]);
       *reinterpret_cast<uint2*>(ti.blk + kKCodes + 32 * ti.slot + 8 * g) = out;
-      if (g == 0) *reinterpret_cast<uint16_t*>(ti.blk + kKScale + 2 * ti.slot) = sb;
-      if (g == 1) *reinterpret_cast<uint16_t*>(ti.blk + kKZero + 2 * ti.slot) = zb;
+      if (g == 0) *reinterpret_cast<uint32_t*>(ti.blk + kMeta + 8 * ti.slot) = (uint32_t)sb | ((uint32_t)zb << 16);
     }
   } else {
     // acc[m][i] = x'[token t0 + 4g + i][channel 16m + r]
@@ -218,8 +217,8 @@ __device__ __forceinline__ void process_tile(const AppendParams& p, const uint4*
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (!tblk[i]) continue;
-      if (r == i) *reinterpret_cast<uint16_t*>(tblk[i] + kVScale + 2 * tslot[i]) = sbits[i];
-      if (r == 4 + i) *reinterpret_cast<uint16_t*>(tblk[i] + kVZero + 2 * tslot[i]) = zbits[i];
+      if (r == i)
+        *reinterpret_cast<uint32_t*>(tblk[i] + kMeta + 8 * tslot[i] + 4) = (uint32_t)sbits[i] | ((uint32_t)zbits[i] << 16);
     }
   }
 }

@@ -13,7 +13,7 @@ namespace oscar {
 constexpr int kD = 128;          // head dim
 constexpr int kPage = 16;        // tokens per page
 constexpr int kBlock = 1152;     // bytes per (page, KV head) block
-constexpr int kKCodes = 0, kVCodes = 512, kKScale = 1024, kKZero = 1056, kVScale = 1088, kVZero = 1120;
+constexpr int kKCodes = 0, kVCodes = 512, kMeta = 1024;  // token t's record {Ks, Kz, Vs, Vz} fp16 at kMeta + 8t
 constexpr int kMaxWindow = 1024;
 constexpr int kPartStride = 2 + kD;  // (m, l, acc[128]) per (batch, q head, split)
 
@@ -47,15 +47,19 @@ inline SplitPlan plan_splits(int batch, int n_kv_heads, int max_tokens) {
   return SplitPlan{(int)s, n < 1 ? 1 : n};
 }
 
-// Workspace layout: [qrot: B*Hq*128 fp32][partials: B*Hq*n_splits*130 fp32]
-inline size_t workspace_bytes(int batch, int n_q_heads, const SplitPlan& p) {
-  size_t q = (size_t)batch * n_q_heads * kD * sizeof(float);
-  size_t parts = (size_t)batch * n_q_heads * p.n_splits * kPartStride * sizeof(float);
-  return ((q + 255) / 256 * 256) + parts;
+// Workspace layout (bytes, each region 256-aligned):
+//   qsum  float [B][Hq]                          sum of the rotated query's channels
+//   qop   int   [B][Hkv][ceil(G/4)][64][9]       per-lane fp8 score operand (8 dwords) + E8M0 scale
+//   part  float [B][Hq][n_splits][130]           split partials (m, l, acc[128])
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+inline size_t qsum_bytes(int batch, int n_q_heads) { return align256((size_t)batch * n_q_heads * sizeof(float)); }
+inline int q_combos(int n_q_heads, int n_kv_heads) { return (n_q_heads / n_kv_heads + 3) / 4; }
+inline size_t qop_bytes(int batch, int n_q_heads, int n_kv_heads) {
+  return align256((size_t)batch * n_kv_heads * q_combos(n_q_heads, n_kv_heads) * 64 * 9 * sizeof(int));
 }
-
-inline size_t qrot_bytes(int batch, int n_q_heads) {
-  return ((size_t)batch * n_q_heads * kD * sizeof(float) + 255) / 256 * 256;
+inline size_t workspace_bytes(int batch, int n_q_heads, int n_kv_heads, const SplitPlan& p) {
+  size_t parts = (size_t)batch * n_q_heads * p.n_splits * kPartStride * sizeof(float);
+  return qsum_bytes(batch, n_q_heads) + qop_bytes(batch, n_q_heads, n_kv_heads) + parts;
 }
 
 // Event-pair recording around main kernels (measurement only).

@@ -7,20 +7,40 @@
 // history, paged attention).
 //
 // Kernels (one call = three launches on the caller's stream):
-//   rotate_q      grid (B, Hkv):            q' = R_K q for the G heads of a KV head
-//   int2_split    grid (splits, Hkv, B):    online softmax over one history range,
-//                                           partial (m, l, acc'[128]) per q head
-//   merge_window  grid (B, Hkv):            log-sum-exp merge of the splits,
-//                                           R_V^T acc', bf16 window, normalise
+//   prep_q        grid (B, Hkv):          q' = R_K q for the G heads of a KV head,
+//                                         its channel sums and fp8 score operands
+//   int2_split    grid (splits, Hkv, B):  online softmax over one history range,
+//                                         partial (m, l, acc'[128]) per q head
+//   merge         grid (B, Hkv):          log-sum-exp merge of the splits,
+//                                         R_V^T acc', bf16 window, normalise
 // Scores are kept in the log2 domain: logit * log2(e) / sqrt(d).
 //
-// The score of a history token factorises over its group: with dequantised
-// k'_c = zero + code_c * scale,  q'.k' = zero * sum_c q'_c + scale * sum_c q'_c code_c.
-// The value sum is split around the group midpoint mid = zero + 1.5 scale:
-// sum_t p_t v'_t = sum_t p_t mid_t + sum_t (p_t scale_t)(code_t - 1.5).  Both
-// parts then stay of the size of the result; the plain split (p zero and
-// p scale code) makes two terms ~2.5 sigma sum p that cancel to a long-context
-// output ~sigma sum p / sqrt(n), and fp32 rounding of the big terms would be
+// INT2 split kernel.  Both contractions of a 128-token tile (8 pages) run on the
+// matrix cores as v_mfma_scale_f32_16x16x128_f8f6f4 with the packed 2-bit codes
+// as the fp4 (e2m1) operand: a code c zero-extended to a nibble is exactly the
+// e2m1 value c/2, so (w & 0x33333333) and ((w >> 2) & 0x33333333) turn 16 packed
+// codes into two ready operand dwords.  The other operand (q' for the scores,
+// softmax weights for the values) is carried as four fp8 (e4m3) terms
+// x = t0 + t1/16 + t2/256 + t3/4096 (each the RNE of the remaining residual),
+// one term per MFMA row, with the power-of-two factors in the E8M0 operand
+// scales: about 16 significant bits.  Rows are (head, term): 4 heads per MFMA.
+//   scores: A = q' terms [(head, term) x 128 channels], B = K codes [128 x 16 tokens]
+//   values: A = w terms  [(head, term) x 128 tokens],  B = V codes [128 x 16 channels]
+// The score output leaves one (head, token) per lane after an in-lane sum of
+// the four term rows, so the softmax runs on full lanes.  The w terms go to a
+// per-wave LDS tile to reach the A-operand layout.
+//
+// gfx950 operand layout of this instruction (16 x 16 output, lane l: column
+// l % 16, rows 4 (l / 16) + i): an 8-bit operand lane in group g holds k in
+// [16g, 16g + 16) then [64 + 16g, 64 + 16g + 16); a 4-bit operand lane holds k in
+// [32g, 32g + 32), low nibble first; the E8M0 scale of k-block b of row / column
+// r comes from lane 16b + r.
+//
+// Value accumulation is split around each group's midpoint mid = zero + 1.5 scale:
+//   sum_t p_t v'_t = sum_t p_t mid_t + sum_t (p_t scale_t)(code_t - 1.5),
+// the -1.5 sum_t w_t being folded into the accumulator once per tile.  The plain
+// split (p zero + p scale code) makes two terms ~2.5 sigma sum p that cancel to a
+// long-context output ~ sigma sum p / sqrt(n); their fp32 rounding would be
 // amplified by that ratio (~300x at 100K tokens).
 #include "common.h"
 
@@ -29,37 +49,145 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kScaleOne = 127;   // E8M0 1.0
+constexpr int kScaleCode = 128;  // E8M0 2.0: an fp4 code nibble c reads as c / 2
+
+__device__ __forceinline__ f32x4 mfma_f8_f4(const i32x8& a, const i32x8& b, f32x4 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0 /*A e4m3*/, 4 /*B e2m1*/, 0, sa, 0, sb);
+}
+
+// k index of byte e (0..31) of an 8-bit operand lane in lane group g
+__device__ __forceinline__ int k_of_fp8(int g, int e) { return e < 16 ? 16 * g + e : 48 + 16 * g + e; }
+
+// channel of element k of the K-code operand: lane group g = k / 32 holds the
+// row bytes 8g .. 8g + 7 as dwords w0, w1 and presents lo(w0), hi(w0), lo(w1), hi(w1)
+__device__ __forceinline__ int k_channel(int k) {
+  const int g = k >> 5, e = k & 31, d = e >> 3, m = e & 7;
+  return 32 * g + 16 * (d >> 1) + 2 * m + (d & 1);
+}
+
+// A sequence length is clamped to what its block-table row can hold.
+__device__ __forceinline__ int clamp_len(int n, int max_pages) {
+  return n < 0 ? 0 : (n > max_pages * kPage ? max_pages * kPage : n);
+}
+
+__device__ __forceinline__ int clamp_scale(int s) { return s < 1 ? 1 : (s > 254 ? 254 : s); }
+
+// Four e4m3 terms of a pair of values (|x| < 128): term j of a in byte 0 and of
+// b in byte 1 of out[j].
+__device__ __forceinline__ void split4(float a, float b, uint32_t out[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    out[j] = (uint32_t)pk & 0xffffu;
+    if (j < 3) {
+      a = (a - __builtin_amdgcn_cvt_f32_fp8(pk, 0)) * 16.f;
+      b = (b - __builtin_amdgcn_cvt_f32_fp8(pk, 1)) * 16.f;
+    }
+  }
+}
+
+__device__ __forceinline__ int exponent_above(float x) {  // E with |x| < 2^E (0 for x == 0)
+  int e = 0;
+  frexpf(x, &e);
+  return e;
+}
+
 // ---------------------------------------------------------------------------
-// q' = R_K[h] q for the G query heads of KV head h
+// Query preparation, once per (sequence, KV head):
+//   q' = R_K[h] q for its G query heads (thread pair (c, half): 64 inputs of
+//   output channel c from 8 x 16-byte loads of R's row);
+//   qsum[head] = sum_c q'_c;
+//   the fp8 score operand of every 4-head group: lane (lg, lr) holds term lr%4 of
+//   q'_(head lr/4) at the 32 channels its k-slots map to, plus the row's E8M0
+//   scale (2^(E - 7 - 4 term), |q'| < 2^E), exactly as the split kernel's MFMA
+//   consumes it.
 // ---------------------------------------------------------------------------
 template <int G>
-__global__ __launch_bounds__(128) void rotate_q_kernel(const uint16_t* __restrict__ r_k,
-                                                       const uint16_t* __restrict__ q, float* __restrict__ qrot,
-                                                       int hq, int hkv) {
+__global__ __launch_bounds__(256) void prep_q_kernel(const uint16_t* __restrict__ r_k,
+                                                     const uint16_t* __restrict__ q, float* __restrict__ qsum_out,
+                                                     int* __restrict__ qop, int hq, int hkv) {
+  constexpr int NCB = (G + 3) / 4;  // 4-head operand groups
   __shared__ float qs[G][kD];
-  __shared__ uint32_t rrow[kD][65];
-  const int b = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
+  __shared__ int qexp[G];
+  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  {
+    const int c = tid >> 1, half = tid & 1;
+    const uint4* rrow = reinterpret_cast<const uint4*>(r_k + ((int64_t)h * kD + c) * kD + 64 * half);
+    uint4 rv[8];
 #pragma unroll
-  for (int j = 0; j < G; ++j) qs[j][c] = bf16_to_f32(q[((int64_t)b * hq + h * G + j) * kD + c]);
-  const uint32_t* r32 = reinterpret_cast<const uint32_t*>(r_k + (int64_t)h * kD * kD);
-  for (int i = c; i < kD * 64; i += 128) rrow[i >> 6][i & 63] = r32[i];
-  __syncthreads();
-  float acc[G];
+    for (int i = 0; i < 8; ++i) rv[i] = rrow[i];
+    __shared__ float qraw[G][kD];
+    for (int e = tid; e < G * kD; e += 256) qraw[e / kD][e % kD] = bf16_to_f32(q[((int64_t)b * hq + h * G) * kD + e]);
+    __syncthreads();
+#pragma unroll 1
+    for (int j = 0; j < G; ++j) {
+      float acc = 0.f;
 #pragma unroll
-  for (int j = 0; j < G; ++j) acc[j] = 0.f;
-  for (int k = 0; k < 64; ++k) {
-    uint32_t w = rrow[c][k];
-    float lo = bf16lo(w), hi = bf16hi(w);
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t w[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
 #pragma unroll
-    for (int j = 0; j < G; ++j) acc[j] = fmaf(lo, qs[j][2 * k], fmaf(hi, qs[j][2 * k + 1], acc[j]));
+        for (int u = 0; u < 4; ++u) {
+          const float2 qv = *reinterpret_cast<const float2*>(&qraw[j][64 * half + 8 * i + 2 * u]);
+          acc = fmaf(bf16lo(w[u]), qv.x, fmaf(bf16hi(w[u]), qv.y, acc));
+        }
+      }
+      acc += __shfl_xor(acc, 1);
+      if (half == 0) qs[j][c] = acc;
+    }
   }
+  __syncthreads();
+  if (tid < G * 16) {  // 16 threads per head: sum and max |q'|
+    const int g = tid >> 4, j = tid & 15;
+    float s = 0.f, mx = 0.f;
 #pragma unroll
-  for (int j = 0; j < G; ++j) qrot[((int64_t)b * hq + h * G + j) * kD + c] = acc[j];
+    for (int c = 0; c < 8; ++c) {
+      s += qs[g][8 * j + c];
+      mx = fmaxf(mx, fabsf(qs[g][8 * j + c]));
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      s += __shfl_xor(s, o);
+      mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
+    if (j == 0) {
+      qsum_out[(int64_t)b * hq + h * G + g] = s;
+      qexp[g] = exponent_above(mx);
+    }
+  }
+  __syncthreads();
+  const int wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+  for (int cb = wave; cb < NCB; cb += 4) {
+    const int head = 4 * cb + (lr >> 2), term = lr & 3;
+    int op[9];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) op[i] = 0;
+    op[8] = kScaleOne;
+    if (head < G) {
+      const int E = qexp[head];
+      op[8] = clamp_scale(kScaleOne + E - 7 - 4 * term);
+#pragma unroll
+      for (int e = 0; e < 32; e += 2) {
+        const float a = ldexpf(qs[head][k_channel(k_of_fp8(lg, e))], 7 - E);
+        const float c = ldexpf(qs[head][k_channel(k_of_fp8(lg, e + 1))], 7 - E);
+        uint32_t t[4];
+        split4(a, c, t);
+        op[e >> 2] |= (int)(t[term] << (8 * (e & 3)));
+      }
+    }
+    int* dst = qop + ((((int64_t)b * hkv + h) * NCB + cb) * 64 + lane) * 9;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) dst[i] = op[i];
+  }
 }
 
 struct SplitParams {
-  const float* qrot;          // [B][Hq][128] (INT2) -- unused by bf16
-  const uint16_t* q;          // [B][Hq][128] bf16 (bf16 comparator)
+  const float* qsum;          // [B][Hq]      (INT2 path)
+  const int* qop;             // [B][Hkv][ceil(G/4)][64][9] (INT2 path)
+  const uint16_t* q;          // [B][Hq][128] bf16 queries (bf16 comparator)
   const int32_t* seq_lens;
   const int32_t* block_table;
   const uint8_t* pool;        // INT2 pool
@@ -67,26 +195,29 @@ struct SplitParams {
   float* part;                // [B][Hq][n_splits][130]
   int64_t n_pages;
   int hq, hkv, max_pages, window, split, n_splits;
+  int gsub;                   // workgroups per KV head, each taking G of its query heads
+  int gw;                     // query heads a workgroup really has (<= G of its instantiation)
   float scale_log2;           // log2(e) / sqrt(d)
 };
 
-// Combine the 4 waves' (m, l, acc) into the workgroup partial and store it.
+// Combine the 4 waves' (m, l, acc) partials (LDS) into the workgroup partial.
 template <int G>
-__device__ __forceinline__ void combine_and_store(const SplitParams& p, float (*cm)[G], float (*cl)[G],
-                                                  float (*cacc)[G][kD], int b, int h, int sp) {
-  __syncthreads();
+__device__ __forceinline__ void combine_and_store(const SplitParams& p, const float* cm, const float* cl,
+                                                  const float* cacc, int b, int hq0, int sp, int gw = G) {
   const int tid = threadIdx.x;
-  for (int e = tid; e < G * kD; e += 256) {
+  for (int e = tid; e < gw * kD; e += 256) {
     const int g = e / kD, c = e % kD;
-    float M = fmaxf(fmaxf(cm[0][g], cm[1][g]), fmaxf(cm[2][g], cm[3][g]));
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, cm[w * G + g]);
     float acc = 0.f, L = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      float f = M == kNegInf ? 0.f : exp2f(cm[w][g] - M);
-      acc += f * cacc[w][g][c];
-      L += f * cl[w][g];
+      const float f = cm[w * G + g] == kNegInf ? 0.f : exp2f(cm[w * G + g] - M);
+      acc += f * cacc[(w * G + g) * kD + c];
+      L += f * cl[w * G + g];
     }
-    float* dst = p.part + (((int64_t)b * p.hq + h * G + g) * p.n_splits + sp) * kPartStride;
+    float* dst = p.part + (((int64_t)b * p.hq + hq0 + g) * p.n_splits + sp) * kPartStride;
     dst[2 + c] = acc;
     if (c == 0) {
       dst[0] = M;
@@ -95,134 +226,281 @@ __device__ __forceinline__ void combine_and_store(const SplitParams& p, float (*
   }
 }
 
+// Raw bytes of one 128-token tile (8 pages) as one lane needs them.
+struct Tile {
+  uint2 kc[8];    // K row bytes 8lg..8lg+7 of token lr, per page
+  uint2 meta[8];  // token lr's record {Ks, Kz, Vs, Vz}, zero past the history end
+  uint4 vlo[2], vhi[2];  // V words of channels 8lr..8lr+7, pages 2lg and 2lg+1
+  uint32_t page_ok;      // bit pp: page pp of the tile exists in this split and in the pool
+};
+
+// All loads of a tile are issued back to back with no branches: lanes 0..7 read
+// the tile's block-table entries, every page index is broadcast with readlane,
+// and a missing page (past the split or the table, or out of the pool) is read
+// as page 0 and masked, so the memory system sees the whole tile at once.
+__device__ __forceinline__ void load_tile(const SplitParams& p, const int* btr, int h, int pbase, int P1,
+                                          int t_end, int lg, int lr, Tile& t) {
+  const int lane = threadIdx.x & 63;
+  const int pgl = pbase + (lane & 7);
+  int ent = pgl <= P1 ? btr[pgl] : -1;
+  if (ent >= p.n_pages) ent = -1;
+  t.page_ok = (uint32_t)__ballot(ent >= 0) & 0xffu;
+  int pages[8];
+#pragma unroll
+  for (int pp = 0; pp < 8; ++pp) {
+    const int e = __builtin_amdgcn_readlane(ent, pp);
+    pages[pp] = e < 0 ? 0 : e;
+  }
+#pragma unroll
+  for (int pp = 0; pp < 8; ++pp) {
+    const uint8_t* blk = p.pool + ((int64_t)pages[pp] * p.hkv + h) * kBlock;
+    t.kc[pp] = *reinterpret_cast<const uint2*>(blk + kKCodes + 32 * lr + 8 * lg);
+    t.meta[pp] = *reinterpret_cast<const uint2*>(blk + kMeta + 8 * lr);
+  }
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    const int pv = lg == 0 ? pages[qq] : lg == 1 ? pages[2 + qq] : lg == 2 ? pages[4 + qq] : pages[6 + qq];
+    const uint8_t* blk = p.pool + ((int64_t)pv * p.hkv + h) * kBlock + kVCodes + 32 * lr;
+    t.vlo[qq] = *reinterpret_cast<const uint4*>(blk);
+    t.vhi[qq] = *reinterpret_cast<const uint4*>(blk + 16);
+  }
+  // slots past the history end or on a missing page may hold anything: their
+  // record must not reach the per-tile scale exponent or the sums
+#pragma unroll
+  for (int pp = 0; pp < 8; ++pp) {
+    const bool live = ((t.page_ok >> pp) & 1u) && (pbase + pp) * 16 + lr < t_end;
+    if (!live) t.meta[pp] = make_uint2(0, 0);
+  }
+}
+
+// Pins a value at this point of the program.  The matrix instructions read
+// their operands across all 64 lanes, so they must run with every lane active:
+// without the pin the compiler may sink an MFMA whose result is only used under
+// a per-lane condition into that condition's branch.
+__device__ __forceinline__ float pin(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Running state of one wave: accumulators, running max, partial sums.
+template <int NRG>
+struct WaveState {
+  f32x4 acc[NRG][8];
+  float m_run[NRG], l_part[NRG], az_part[NRG];
+};
+
+template <int G, int NRG>
+__device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t, int pbase, int t_end, int lg,
+                                             int lr, const i32x8* qa, const int* qsc, const float* qsr,
+                                             uint8_t* wt, WaveState<NRG>& st) {
+  const int slot_pos = 8 * (lr & 1) + (lr >> 1);  // k position of token lr within its page's 16
+  // ---- scores: raw[rg][pp] = q'_(4rg+lg) . code(token lr of page pp) ----
+  float raw[NRG][8];
+#pragma unroll
+  for (int pp = 0; pp < 8; ++pp) {
+    i32x8 bk;
+    bk[0] = (int)(t.kc[pp].x & 0x33333333u);
+    bk[1] = (int)((t.kc[pp].x >> 2) & 0x33333333u);
+    bk[2] = (int)(t.kc[pp].y & 0x33333333u);
+    bk[3] = (int)((t.kc[pp].y >> 2) & 0x33333333u);
+    bk[4] = bk[5] = bk[6] = bk[7] = 0;
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg) {
+      const f32x4 c = mfma_f8_f4(qa[rg], bk, f32x4{0.f, 0.f, 0.f, 0.f}, qsc[rg], kScaleCode);
+      raw[rg][pp] = pin((c[0] + c[1]) + (c[2] + c[3]));
+    }
+  }
+  // ---- online softmax, weights, w terms -> LDS ----
+  float wsum[NRG];
+  float vsmax = 0.f;
+#pragma unroll
+  for (int pp = 0; pp < 8; ++pp) vsmax = fmaxf(vsmax, h2f((uint16_t)(t.meta[pp].y & 0xffffu)));
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) vsmax = fmaxf(vsmax, __shfl_xor(vsmax, o));
+  const int wexp = exponent_above(vsmax);  // every w = p vs <= vsmax < 2^wexp
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg) {
+    const bool hv = 4 * rg + lg < p.gw;
+    float lgt[8];
+    float mx = kNegInf;
+#pragma unroll
+    for (int pp = 0; pp < 8; ++pp) {
+      const int tok = (pbase + pp) * 16 + lr;
+      const bool ok = hv && tok < t_end && ((t.page_ok >> pp) & 1u);
+      const float ks = h2f((uint16_t)(t.meta[pp].x & 0xffffu));
+      const float kz = h2f((uint16_t)(t.meta[pp].x >> 16));
+      lgt[pp] = ok ? (kz * qsr[rg] + ks * raw[rg][pp]) * p.scale_log2 : kNegInf;
+      mx = fmaxf(mx, lgt[pp]);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float m_new = fmaxf(st.m_run[rg], mx);
+    if (__any(m_new > st.m_run[rg])) {
+      const float alpha = (m_new == kNegInf) ? 1.f : exp2f(st.m_run[rg] - m_new);
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn) st.acc[rg][nn] *= alpha;
+      st.l_part[rg] *= alpha;
+      st.az_part[rg] *= alpha;
+      st.m_run[rg] = m_new;
+    }
+    float w[8];
+    float ws = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < 8; ++pp) {
+      const float pv = lgt[pp] == kNegInf ? 0.f : exp2f(lgt[pp] - st.m_run[rg]);
+      const float vs = h2f((uint16_t)(t.meta[pp].y & 0xffffu));
+      const float vz = h2f((uint16_t)(t.meta[pp].y >> 16));
+      st.l_part[rg] += pv;
+      st.az_part[rg] = fmaf(pv, fmaf(1.5f, vs, vz), st.az_part[rg]);
+      w[pp] = pv * vs;
+      ws += w[pp];
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) ws += __shfl_xor(ws, o);
+    wsum[rg] = ws;
+    uint8_t* tile_rg = wt + rg * 2048;
+#pragma unroll
+    for (int pp = 0; pp < 8; pp += 2) {
+      uint32_t tt[4];
+      split4(ldexpf(w[pp], 7 - wexp), ldexpf(w[pp + 1], 7 - wexp), tt);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint8_t* row = tile_rg + (4 * lg + j) * 128 + slot_pos;
+        row[16 * pp] = (uint8_t)(tt[j] & 0xffu);
+        row[16 * (pp + 1)] = (uint8_t)(tt[j] >> 8);
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // ---- values: acc[rg][nn] += w terms x V codes (channels 8lr + nn) ----
+  const int wsc = clamp_scale(kScaleOne + wexp - 7 - 4 * (lr & 3));
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg) {
+    const uint8_t* row = wt + rg * 2048 + lr * 128;
+    const uint4 a0 = *reinterpret_cast<const uint4*>(row + 16 * lg);
+    const uint4 a1 = *reinterpret_cast<const uint4*>(row + 64 + 16 * lg);
+    i32x8 wa;
+    wa[0] = (int)a0.x;
+    wa[1] = (int)a0.y;
+    wa[2] = (int)a0.z;
+    wa[3] = (int)a0.w;
+    wa[4] = (int)a1.x;
+    wa[5] = (int)a1.y;
+    wa[6] = (int)a1.z;
+    wa[7] = (int)a1.w;
+    const float corr = 1.5f * wsum[rg];
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn) {
+      const uint32_t v0 = nn < 4 ? (&t.vlo[0].x)[nn] : (&t.vhi[0].x)[nn - 4];
+      const uint32_t v1 = nn < 4 ? (&t.vlo[1].x)[nn] : (&t.vhi[1].x)[nn - 4];
+      i32x8 bv;
+      bv[0] = (int)(v0 & 0x33333333u);
+      bv[1] = (int)((v0 >> 2) & 0x33333333u);
+      bv[2] = (int)(v1 & 0x33333333u);
+      bv[3] = (int)((v1 >> 2) & 0x33333333u);
+      bv[4] = bv[5] = bv[6] = bv[7] = 0;
+      st.acc[rg][nn] = mfma_f8_f4(wa, bv, st.acc[rg][nn], wsc, kScaleCode);
+      st.acc[rg][nn][0] -= corr;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 // ---------------------------------------------------------------------------
-// INT2 history split (VALU): lane = (token of the page, channel quarter) for
-// the scores, lane = 2 channels for the value accumulation.
+// INT2 history split on the matrix cores.  Lane l = 16 lg + lr.
+//   score MFMA output: head 4 rg + lg, token lr of the page;
+//   value accumulators: head 4 rg + lg, channels 8 lr + n (n = 0..7);
+//   loads per tile: K row bytes 8lg..8lg+7 of token lr and its metadata record
+//   for each of the 8 pages; V words of channels 8lr..8lr+7 for pages 2lg, 2lg+1.
+// The waves of a workgroup take the split's tiles round robin; each wave keeps
+// the next tile's loads in flight while it computes the current one.
 // ---------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(256) void int2_split_kernel(SplitParams p) {
-  const int b = blockIdx.z, h = blockIdx.y, sp = blockIdx.x;
-  const int n = p.seq_lens[b];
-  const int w = n < p.window ? n : p.window;
-  const int hist = n - w;
+  constexpr int NRG = (G + 3) / 4;                    // MFMA row groups of 4 heads
+  constexpr int kTileBytes = 4 * NRG * 16 * 128;     // per-wave w-term tiles
+  constexpr int kCombBytes = 4 * G * kD * 4 + 2 * 4 * G * 4;
+  constexpr int kSmem = kTileBytes > kCombBytes ? kTileBytes : kCombBytes;
+
+  const int b = blockIdx.z, h = blockIdx.y / p.gsub, sp = blockIdx.x;
+  const int sub = blockIdx.y % p.gsub;
+  const int hq0 = h * p.gw * p.gsub + sub * p.gw;  // first query head of this workgroup
+  const int n = clamp_len(p.seq_lens[b], p.max_pages);
+  const int hist = n - (n < p.window ? n : p.window);
   const int t_begin = sp * p.split;
   if (t_begin >= hist) return;
   const int t_end = min(t_begin + p.split, hist);
 
-  __shared__ float qs[G][kD];
-  __shared__ float qsum[G];
-  __shared__ float pb[4][16][G];
-  __shared__ float vsz[4][16][2];
-  __shared__ float cm[4][G], cl[4][G];
-  __shared__ float cacc[4][G][kD];
+  __shared__ __align__(16) uint8_t smem[kSmem];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < G * kD; e += 256)
-    qs[e / kD][e % kD] = p.qrot[((int64_t)b * p.hq + h * G) * kD + e];
-  __syncthreads();
-  if (wave == 0) {
-    for (int g = 0; g < G; ++g) {
-      float s = qs[g][lane] + qs[g][lane + 64];
-      for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-      if (lane == 0) qsum[g] = s;
-    }
-  }
-  __syncthreads();
+  const int lg = lane >> 4, lr = lane & 15;
 
-  const int tq = lane & 15, quarter = lane >> 4;
-  float m_run[G], l_run[G], az[G], acc0[G], acc1[G], qsr[G];
+  // score operands prepared once per (sequence, KV head)
+  i32x8 qa[NRG];
+  int qsc[NRG];
+  float qsr[NRG];
+  const int ncb = (p.gw * p.gsub + 3) / 4;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m_run[g] = kNegInf;
-    l_run[g] = 0.f;
-    az[g] = 0.f;
-    acc0[g] = 0.f;
-    acc1[g] = 0.f;
-    qsr[g] = qsum[g];
+  for (int rg = 0; rg < NRG; ++rg) {
+    const int* src = p.qop + ((((int64_t)b * p.hkv + h) * ncb + (sub * p.gw) / 4 + rg) * 64 + lane) * 9;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qa[rg][i] = src[i];
+    qsc[rg] = src[8];
+    qsr[rg] = (4 * rg + lg < p.gw) ? p.qsum[(int64_t)b * p.hq + hq0 + 4 * rg + lg] : 0.f;
   }
-  const int first_page = t_begin >> 4, last_page = (t_end - 1) >> 4;
-  for (int pg = first_page + wave; pg <= last_page; pg += 4) {
-    const int page = p.block_table[(int64_t)b * p.max_pages + pg];
-    if (page < 0 || page >= p.n_pages) continue;
-    const uint8_t* blk = p.pool + ((int64_t)page * p.hkv + h) * kBlock;
-    const int tok = pg * 16 + tq;
-    const bool valid = tok >= t_begin && tok < t_end;
-    // ---- scores ----
-    const uint2 kw = *reinterpret_cast<const uint2*>(blk + kKCodes + 32 * tq + 8 * quarter);
-    float dot[G];
+
+  WaveState<NRG> st;
 #pragma unroll
-    for (int g = 0; g < G; ++g) dot[g] = 0.f;
+  for (int rg = 0; rg < NRG; ++rg) {
+    st.m_run[rg] = kNegInf;
+    st.l_part[rg] = 0.f;
+    st.az_part[rg] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float c0 = (float)((kw.x >> (2 * j)) & 3u), c1 = (float)((kw.y >> (2 * j)) & 3u);
+    for (int nn = 0; nn < 8; ++nn) st.acc[rg][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  uint8_t* wt = smem + wave * (NRG * 2048);
+  const int P0 = t_begin >> 4, P1 = (t_end - 1) >> 4;
+  const int n_tiles = (P1 - P0 + 8) >> 3;
+  const int* btr = p.block_table + (int64_t)b * p.max_pages;
+
+  for (int tile = wave; tile < n_tiles; tile += 4) {
+    Tile ta;
+    load_tile(p, btr, h, P0 + 8 * tile, P1, t_end, lg, lr, ta);
+    compute_tile<G, NRG>(p, ta, P0 + 8 * tile, t_end, lg, lr, qa, qsc, qsr, wt, st);
+  }
+
+  // ---- per-wave partial -> LDS -> workgroup partial ----
+  __syncthreads();  // every wave is done with its w-term tile before smem is reused
+  float* cacc = reinterpret_cast<float*>(smem);  // [4][G][128]
+  float* cm = cacc + 4 * G * kD;                 // [4][G]
+  float* cl = cm + 4 * G;                        // [4][G]
 #pragma unroll
-      for (int g = 0; g < G; ++g)
-        dot[g] = fmaf(qs[g][32 * quarter + j], c0, fmaf(qs[g][32 * quarter + 16 + j], c1, dot[g]));
+  for (int rg = 0; rg < NRG; ++rg) {
+    float l = st.l_part[rg], az = st.az_part[rg];
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      l += __shfl_xor(l, o);
+      az += __shfl_xor(az, o);
     }
-    const float ks = h2f(*reinterpret_cast<const uint16_t*>(blk + kKScale + 2 * tq));
-    const float kz = h2f(*reinterpret_cast<const uint16_t*>(blk + kKZero + 2 * tq));
-    float alpha[G], pv[G];
+    const int head = 4 * rg + lg;
+    if (head < p.gw) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float d = dot[g] + __shfl_xor(dot[g], 16);
-      d += __shfl_xor(d, 32);
-      float lg = valid ? (kz * qsr[g] + ks * d) * p.scale_log2 : kNegInf;
-      float mx = lg;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      const float m_new = fmaxf(m_run[g], mx);
-      alpha[g] = exp2f(m_run[g] - m_new);
-      pv[g] = valid ? exp2f(lg - m_new) : 0.f;
-      float ps = pv[g];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) ps += __shfl_xor(ps, o);
-      l_run[g] = l_run[g] * alpha[g] + ps;
-      m_run[g] = m_new;
-    }
-    if (quarter == 0) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) pb[wave][tq][g] = pv[g];
-      const float vsc = h2f(*reinterpret_cast<const uint16_t*>(blk + kVScale + 2 * tq));
-      const float vzr = h2f(*reinterpret_cast<const uint16_t*>(blk + kVZero + 2 * tq));
-      vsz[wave][tq][0] = valid ? vsc : 0.f;
-      vsz[wave][tq][1] = valid ? fmaf(1.5f, vsc, vzr) : 0.f;  // group midpoint
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- values: this lane owns channels 2*lane, 2*lane+1 ----
-    const uint2 vw = *reinterpret_cast<const uint2*>(blk + kVCodes + 8 * lane);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      acc0[g] *= alpha[g];
-      acc1[g] *= alpha[g];
-      az[g] *= alpha[g];
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const float c0 = (float)((vw.x >> (2 * t)) & 3u) - 1.5f, c1 = (float)((vw.y >> (2 * t)) & 3u) - 1.5f;
-      const float vs = vsz[wave][t][0], vz = vsz[wave][t][1];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float pt = pb[wave][t][g];
-        const float wt = pt * vs;
-        acc0[g] = fmaf(wt, c0, acc0[g]);
-        acc1[g] = fmaf(wt, c1, acc1[g]);
-        az[g] = fmaf(pt, vz, az[g]);
+      for (int nn = 0; nn < 8; ++nn)
+        cacc[(wave * G + head) * kD + 8 * lr + nn] =
+            (st.acc[rg][nn][0] + st.acc[rg][nn][1]) + (st.acc[rg][nn][2] + st.acc[rg][nn][3]) + az;
+      if (lr == 0) {
+        cm[wave * G + head] = st.m_run[rg];
+        cl[wave * G + head] = l;
       }
     }
-    __builtin_amdgcn_wave_barrier();
   }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    cacc[wave][g][2 * lane] = acc0[g] + az[g];
-    cacc[wave][g][2 * lane + 1] = acc1[g] + az[g];
-    if (lane == 0) {
-      cm[wave][g] = m_run[g];
-      cl[wave][g] = l_run[g];
-    }
-  }
-  combine_and_store<G>(p, cm, cl, cacc, b, h, sp);
+  __syncthreads();
+  combine_and_store<G>(p, cm, cl, cacc, b, hq0, sp, p.gw);
 }
 
 // ---------------------------------------------------------------------------
@@ -231,15 +509,15 @@ __global__ __launch_bounds__(256) void int2_split_kernel(SplitParams p) {
 template <int G>
 __global__ __launch_bounds__(256) void bf16_split_kernel(SplitParams p) {
   const int b = blockIdx.z, h = blockIdx.y, sp = blockIdx.x;
-  const int n = p.seq_lens[b];
+  const int n = clamp_len(p.seq_lens[b], p.max_pages);
   const int t_begin = sp * p.split;
   if (t_begin >= n) return;
   const int t_end = min(t_begin + p.split, n);
 
   __shared__ float qs[G][kD];
   __shared__ float pb[4][16][G];
-  __shared__ float cm[4][G], cl[4][G];
-  __shared__ float cacc[4][G][kD];
+  __shared__ float cm[4 * G], cl[4 * G];
+  __shared__ float cacc[4 * G * kD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < G * kD; e += 256)
@@ -327,14 +605,15 @@ __global__ __launch_bounds__(256) void bf16_split_kernel(SplitParams p) {
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    cacc[wave][g][2 * lane] = acc0[g];
-    cacc[wave][g][2 * lane + 1] = acc1[g];
+    cacc[(wave * G + g) * kD + 2 * lane] = acc0[g];
+    cacc[(wave * G + g) * kD + 2 * lane + 1] = acc1[g];
     if (lane == 0) {
-      cm[wave][g] = m_run[g];
-      cl[wave][g] = l_run[g];
+      cm[wave * G + g] = m_run[g];
+      cl[wave * G + g] = l_run[g];
     }
   }
-  combine_and_store<G>(p, cm, cl, cacc, b, h, sp);
+  __syncthreads();
+  combine_and_store<G>(p, cm, cl, cacc, b, h * G, sp);
 }
 
 // ---------------------------------------------------------------------------
@@ -349,70 +628,138 @@ struct MergeParams {
   const uint16_t* win_v;
   const int32_t* seq_lens;
   float* out;
-  int hq, hkv, window, split, n_splits;
+  int hq, hkv, max_pages, window, split, n_splits;
   float scale_log2;
 };
 
 constexpr int kWinChunk = 32;
+constexpr int kSplitChunk = 128;  // splits whose weights are staged in LDS at a time
 
 template <int G>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
+  constexpr int PER = (G * kD + 255) / 256;  // (head, channel) elements per thread
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int n = p.seq_lens[b];
+  const int n = clamp_len(p.seq_lens[b], p.max_pages);
   const bool int2 = p.r_v != nullptr;
   const int w = int2 ? (n < p.window ? n : p.window) : 0;
   const int hist = n - w;
-  const int ns = (hist + p.split - 1) / p.split;
+  const int ns = min((hist + p.split - 1) / p.split, p.n_splits);
 
-  __shared__ float a1[G][kD];   // merged split accumulator (rotated domain for INT2)
-  __shared__ float o2[G][kD];   // window accumulator
+  __shared__ __align__(16) uint16_t rv_s[kD * kD];  // R_V[h], row-major [j][i]
+  __shared__ float a1[G][kD];                        // merged split accumulator
+  __shared__ float o2[G][kD];                        // window accumulator
   __shared__ float qs[G][kD];
+  __shared__ float fsc[G][kSplitChunk];              // per-split weights, one chunk
   __shared__ float M1[G], L1[G], M2[G], L2[G], al[G], mn[G];
   __shared__ uint32_t kw[kWinChunk][65];
   __shared__ uint32_t vw[kWinChunk][65];
   __shared__ float sc[G][kWinChunk];
 
+  if (int2) {  // stage R_V early; consumed after the split merge
+    const uint4* src = reinterpret_cast<const uint4*>(p.r_v + (int64_t)h * kD * kD);
+    uint4* dst = reinterpret_cast<uint4*>(rv_s);
+    for (int i = tid; i < kD * kD / 8; i += 256) dst[i] = src[i];
+  }
   for (int e = tid; e < G * kD; e += 256) {
-    const int g = e / kD, c = e % kD;
-    const float* base = p.part + ((int64_t)b * p.hq + h * G + g) * p.n_splits * kPartStride;
+    qs[e / kD][e % kD] = bf16_to_f32(p.q[((int64_t)b * p.hq + h * G) * kD + e]);
+    o2[e / kD][e % kD] = 0.f;
+  }
+  // M1 per head: one wave per head, strided over splits
+  for (int g0 = 0; g0 < G; g0 += 4) {
+    const int g = g0 + (tid >> 6);
     float M = kNegInf;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, base[s * kPartStride]);
-    float acc = 0.f, L = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float f = exp2f(base[s * kPartStride] - M);
-      acc += f * base[s * kPartStride + 2 + c];
-      L += f * base[s * kPartStride + 1];
+    if (g < G) {
+      const float* base = p.part + ((int64_t)b * p.hq + h * G + g) * p.n_splits * kPartStride;
+      for (int s = tid & 63; s < ns; s += 64) M = fmaxf(M, base[s * kPartStride]);
     }
-    a1[g][c] = acc;
-    o2[g][c] = 0.f;
-    qs[g][c] = bf16_to_f32(p.q[((int64_t)b * p.hq + h * G + g) * kD + c]);
-    if (c == 0) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if (g < G && (tid & 63) == 0) {
       M1[g] = M;
-      L1[g] = L;
       M2[g] = kNegInf;
       L2[g] = 0.f;
     }
   }
   __syncthreads();
+  // a1 = sum_s 2^(m_s - M1) acc_s ; L1 = sum_s 2^(m_s - M1) l_s
+  float accv[PER], lsum[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) accv[k] = lsum[k] = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += kSplitChunk) {
+    const int cnt = min(kSplitChunk, ns - s0);
+    __syncthreads();
+    for (int e = tid; e < G * cnt; e += 256) {
+      const int g = e / cnt, s = e % cnt;
+      const float* ps = p.part + (((int64_t)b * p.hq + h * G + g) * p.n_splits + s0 + s) * kPartStride;
+      fsc[g][s] = exp2f(ps[0] - M1[g]);
+    }
+    __syncthreads();
+    // all loads of a batch of splits issued before the sums (latency bound otherwise)
+    for (int sb = 0; sb < cnt; sb += 16) {
+      const int nb = min(16, cnt - sb);
+      float x[PER][16], xl[PER][16];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int e = tid + 256 * k;
+        const int g = (e < G * kD) ? e / kD : 0, c = e % kD;
+        const float* ps = p.part + (((int64_t)b * p.hq + h * G + g) * p.n_splits + s0 + sb) * kPartStride;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          x[k][s] = (e < G * kD && s < nb) ? ps[s * kPartStride + 2 + c] : 0.f;
+          xl[k][s] = (e < G * kD && s < nb && c == 0) ? ps[s * kPartStride + 1] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int e = tid + 256 * k;
+        const int g = (e < G * kD) ? e / kD : 0;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          const float f = s < nb ? fsc[g][sb + s] : 0.f;
+          accv[k] = fmaf(f, x[k][s], accv[k]);
+          lsum[k] = fmaf(f, xl[k][s], lsum[k]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e = tid + 256 * k;
+    if (e >= G * kD) break;
+    a1[e / kD][e % kD] = accv[k];
+    if (e % kD == 0) L1[e / kD] = lsum[k];
+  }
+  __syncthreads();
 
-  float o1[(G * kD + 255) / 256];
+  float o1[PER];
   if (int2) {
-    const uint16_t* rv = p.r_v + (int64_t)h * kD * kD;
-    int k = 0;
-    for (int e = tid; e < G * kD; e += 256, ++k) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = tid + 256 * k;
+      o1[k] = 0.f;
+      if (e >= G * kD) break;
       const int g = e / kD, i = e % kD;
       float acc = 0.f;
-      for (int j = 0; j < kD; ++j) acc = fmaf(bf16_to_f32(rv[j * kD + i]), a1[g][j], acc);
+#pragma unroll 8
+      for (int j = 0; j < kD; ++j) acc = fmaf(bf16_to_f32(rv_s[j * kD + i]), a1[g][j], acc);
       o1[k] = acc;
     }
     for (int cs = hist; cs < n; cs += kWinChunk) {
       const int nt = min(kWinChunk, n - cs);
       __syncthreads();
-      for (int e = tid; e < nt * 64; e += 256) {
-        const int t = e >> 6, u = e & 63;
+      for (int e = tid; e < nt * 16; e += 256) {
+        const int t = e >> 4, u = e & 15;
         const int64_t row = (((int64_t)b * p.window + (cs + t) % p.window) * p.hkv + h) * kD;
-        kw[t][u] = reinterpret_cast<const uint32_t*>(p.win_k + row)[u];
-        vw[t][u] = reinterpret_cast<const uint32_t*>(p.win_v + row)[u];
+        const uint4 kv4 = reinterpret_cast<const uint4*>(p.win_k + row)[u];
+        const uint4 vv4 = reinterpret_cast<const uint4*>(p.win_v + row)[u];
+        kw[t][4 * u] = kv4.x;
+        kw[t][4 * u + 1] = kv4.y;
+        kw[t][4 * u + 2] = kv4.z;
+        kw[t][4 * u + 3] = kv4.w;
+        vw[t][4 * u] = vv4.x;
+        vw[t][4 * u + 1] = vv4.y;
+        vw[t][4 * u + 2] = vv4.z;
+        vw[t][4 * u + 3] = vv4.w;
       }
       __syncthreads();
       for (int e = tid; e < G * kWinChunk; e += 256) {
@@ -460,8 +807,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
     }
     __syncthreads();
   }
-  int k = 0;
-  for (int e = tid; e < G * kD; e += 256, ++k) {
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e = tid + 256 * k;
+    if (e >= G * kD) break;
     const int g = e / kD, c = e % kD;
     const float v1 = int2 ? o1[k] : a1[g][c];
     const float M = fmaxf(M1[g], M2[g]);
@@ -475,16 +824,23 @@ template <int G>
 int launch_decode(bool int2, const SplitParams& sp, const MergeParams& mp, const uint16_t* r_k,
                   const uint16_t* q, int batch, hipStream_t s) {
   if (int2) {
-    rotate_q_kernel<G><<<dim3(batch, sp.hkv), 128, 0, s>>>(r_k, q, const_cast<float*>(sp.qrot), sp.hq, sp.hkv);
+    prep_q_kernel<G><<<dim3(batch, sp.hkv), 256, 0, s>>>(r_k, q, const_cast<float*>(sp.qsum),
+                                                         const_cast<int*>(sp.qop), sp.hq, sp.hkv);
     if (hipGetLastError() != hipSuccess) return OSCAR_EHIP;
   }
   int slot = -1;
   timing_record_begin(s, int2 ? 1 : 2, &slot);
-  dim3 grid(sp.n_splits, sp.hkv, batch);
-  if (int2)
-    int2_split_kernel<G><<<grid, 256, 0, s>>>(sp);
-  else
-    bf16_split_kernel<G><<<grid, 256, 0, s>>>(sp);
+  if (int2) {
+    // at most 8 query heads per workgroup (register budget of the MFMA tiles)
+    // and the 4-head instantiation for G < 4, masking the missing heads at run time
+    constexpr int GW = G > 8 ? 8 : (G < 4 ? 4 : G);
+    SplitParams p2 = sp;
+    p2.gw = G < GW ? G : GW;
+    p2.gsub = G / p2.gw;
+    int2_split_kernel<GW><<<dim3(sp.n_splits, sp.hkv * p2.gsub, batch), 256, 0, s>>>(p2);
+  } else {
+    bf16_split_kernel<G><<<dim3(sp.n_splits, sp.hkv, batch), 256, 0, s>>>(sp);
+  }
   if (hipGetLastError() != hipSuccess) return OSCAR_EHIP;
   timing_record_end(s, slot);
   merge_kernel<G><<<dim3(batch, sp.hkv), 256, 0, s>>>(mp);
@@ -505,18 +861,20 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   if (!int2 && !kv_pool) return OSCAR_EINVAL;
   if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * kPage) return OSCAR_ENOSPACE;
   const SplitPlan plan = plan_splits(batch, shape->n_kv_heads, max_seq_len);
-  if (workspace_bytes < oscar::workspace_bytes(batch, shape->n_q_heads, plan)) return OSCAR_ENOSPACE;
+  if (workspace_bytes < oscar::workspace_bytes(batch, shape->n_q_heads, shape->n_kv_heads, plan)) return OSCAR_ENOSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return OSCAR_EINVAL;
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   SplitParams sp{};
-  sp.qrot = reinterpret_cast<float*>(ws);
+  sp.qsum = reinterpret_cast<float*>(ws);
+  sp.qop = reinterpret_cast<int*>(ws + qsum_bytes(batch, shape->n_q_heads));
   sp.q = q;
   sp.seq_lens = seq_lens;
   sp.block_table = block_table;
   sp.pool = pool;
   sp.kv_pool = kv_pool;
-  sp.part = reinterpret_cast<float*>(ws + qrot_bytes(batch, shape->n_q_heads));
+  sp.part = reinterpret_cast<float*>(ws + qsum_bytes(batch, shape->n_q_heads) +
+                                     qop_bytes(batch, shape->n_q_heads, shape->n_kv_heads));
   sp.n_pages = n_pages;
   sp.hq = shape->n_q_heads;
   sp.hkv = shape->n_kv_heads;
@@ -524,6 +882,8 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   sp.window = int2 ? shape->window : 0;
   sp.split = plan.split;
   sp.n_splits = plan.n_splits;
+  sp.gsub = 1;
+  sp.gw = shape->n_q_heads / shape->n_kv_heads;
   sp.scale_log2 = kLog2e / sqrtf((float)kD);
   MergeParams mp{};
   mp.part = sp.part;
@@ -535,6 +895,7 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   mp.out = out;
   mp.hq = sp.hq;
   mp.hkv = sp.hkv;
+  mp.max_pages = sp.max_pages;
   mp.window = sp.window;
   mp.split = sp.split;
   mp.n_splits = sp.n_splits;
@@ -580,7 +941,8 @@ __global__ __launch_bounds__(256) void bf16_append_kernel(const uint16_t* __rest
 extern "C" size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int32_t max_seq_len) {
   using namespace oscar;
   if (check_shape(shape) != OSCAR_OK || batch < 1 || max_seq_len < 1) return 0;
-  return workspace_bytes(batch, shape->n_q_heads, plan_splits(batch, shape->n_kv_heads, max_seq_len));
+  return workspace_bytes(batch, shape->n_q_heads, shape->n_kv_heads,
+                         plan_splits(batch, shape->n_kv_heads, max_seq_len));
 }
 
 extern "C" int oscar_decode_attn(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,

@@ -46,14 +46,15 @@ import numpy as np
 # Page-block layout (per page, per KV head, 1152 bytes)
 #   [   0,  512)  K codes: 16 token rows x 32 B; channel c of a row at bit 2c
 #   [ 512, 1024)  V codes: 128 channel words x 4 B; token slot j at bit 2j
-#   [1024, 1056)  K scale fp16[16]     [1056, 1088)  K zero fp16[16]
-#   [1088, 1120)  V scale fp16[16]     [1120, 1152)  V zero fp16[16]
+#   [1024, 1152)  16 token records of 8 bytes: fp16 K scale, K zero, V scale, V zero
 # Pool = uint8 [n_pages][Hkv][1152].  Window ring = bf16 [B][W][Hkv][d], slot pos % W.
 # bf16 comparator pool = bf16 [n_pages][Hkv][2 (K, V)][16][d].
 # ---------------------------------------------------------------------------
 D = 128
 PAGE = 16
-K_CODES, V_CODES, K_SCALE, K_ZERO, V_SCALE, V_ZERO, BLOCK = 0, 512, 1024, 1056, 1088, 1120, 1152
+K_CODES, V_CODES, META, BLOCK = 0, 512, 1024, 1152
+# fields of a token's 8-byte record at META + 8 * slot
+K_SCALE, K_ZERO, V_SCALE, V_ZERO = 0, 2, 4, 6
 
 
 # ---------------------------------------------------------------------------
@@ -251,8 +252,9 @@ def unpack_v_words(words: np.ndarray) -> np.ndarray:
     return ((w >> sh) & 3).astype(np.int64)
 
 
-def _put_fp16(block, off, slot, bits):
-    block[off + 2 * slot: off + 2 * slot + 2] = np.array([bits], dtype=np.uint16).view(np.uint8)
+def _put_fp16(block, field, slot, bits):
+    a = META + 8 * slot + field
+    block[a: a + 2] = np.array([bits], dtype=np.uint16).view(np.uint8)
 
 
 def append_ref(r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,
@@ -304,8 +306,8 @@ def read_history(pool, block_table_row, hist: int, h: int):
     blk = pool[pages, h]                                    # [n_pg][1152]
     kc = unpack_k_rows(blk[:, K_CODES:K_CODES + 512].reshape(n_pg, PAGE, 32))
     vc = unpack_v_words(v_words(blk))                       # [n_pg][16][128]
-    f16 = lambda off: fp16_to_f64(np.ascontiguousarray(blk[:, off:off + 32]).view(np.uint16))
-    ks, kz, vs, vz = f16(K_SCALE), f16(K_ZERO), f16(V_SCALE), f16(V_ZERO)
+    meta = np.ascontiguousarray(blk[:, META:BLOCK]).view(np.uint16).reshape(n_pg, PAGE, 4)
+    ks, kz, vs, vz = (fp16_to_f64(meta[..., f // 2]) for f in (K_SCALE, K_ZERO, V_SCALE, V_ZERO))
     with np.errstate(invalid="ignore", over="ignore"):  # unused slots of the last page
         k = kz[..., None] + kc * ks[..., None]
         v = vz[..., None] + vc * vs[..., None]
@@ -477,9 +479,9 @@ def append_sequence_ref(r_k, r_v, k_bits, v_bits, block_row, pool, win_k, win_v,
         words &= keep
         words |= np.bitwise_or.reduce((vcode[j][m] << (2 * slots[m])[:, None, None].astype(np.uint32)), axis=0)
         blk[:, V_CODES:V_CODES + 512] = words.astype("<u4").view(np.uint8).reshape(hkv, 512)
-        for off, b in bits.items():
-            f = blk[:, off:off + 32].reshape(hkv, PAGE, 2)
-            f[:, m] = np.ascontiguousarray(b[j * PAGE:(j + 1) * PAGE][m].T).view(np.uint8).reshape(hkv, -1, 2)
+        rec = blk[:, META:BLOCK].reshape(hkv, PAGE, 4, 2)                # [h][slot][field][2 bytes]
+        for f, b in bits.items():
+            rec[:, m, f // 2] = np.ascontiguousarray(b[j * PAGE:(j + 1) * PAGE][m].T).view(np.uint8).reshape(hkv, -1, 2)
     if window > 0:
         for p in range(max(0, n - window), n):
             win_k[p % window] = k_bits[p]

@@ -44,7 +44,7 @@ def gpu_group_fields(pool, page, h, slot):
     blk = pool[page, h]
     kc = ref.unpack_k_rows(blk[ref.K_CODES + 32 * slot: ref.K_CODES + 32 * slot + 32])
     vc = ref.unpack_v_words(ref.v_words(blk))[slot]
-    f = lambda off: int(np.ascontiguousarray(blk[off + 2 * slot: off + 2 * slot + 2]).view(np.uint16)[0])
+    f = lambda fld: int(np.ascontiguousarray(blk[ref.META + 8 * slot + fld: ref.META + 8 * slot + fld + 2]).view(np.uint16)[0])
     return kc, vc, f(ref.K_SCALE), f(ref.K_ZERO), f(ref.V_SCALE), f(ref.V_ZERO)
 
 
@@ -53,8 +53,7 @@ def clear_group(pool, page, h, slot):
     blk[ref.K_CODES + 32 * slot: ref.K_CODES + 32 * slot + 32] = 0
     w = ref.v_words(blk).copy() & ~np.uint32(3 << (2 * slot))
     blk[ref.V_CODES:ref.V_CODES + 512] = w.astype("<u4").view(np.uint8)
-    for off in (ref.K_SCALE, ref.K_ZERO, ref.V_SCALE, ref.V_ZERO):
-        blk[off + 2 * slot: off + 2 * slot + 2] = 0
+    blk[ref.META + 8 * slot: ref.META + 8 * slot + 8] = 0
 
 
 def check_group(xr, codes_gpu, s_bits_gpu, z_bits_gpu):

@@ -51,7 +51,7 @@ def test_stray_write_is_caught():
 def test_wrong_scale_is_caught():
     pool0, pool, rk, rv, k, v, si, ps, bt = setup()
     page = bt[0][0]
-    sc = pool[page, 1, ref.V_SCALE:ref.V_SCALE + 2].view(np.uint16)
+    sc = pool[page, 1, ref.META + ref.V_SCALE:ref.META + ref.V_SCALE + 2].view(np.uint16)
     sc[0] ^= 0x0001
     assert P.check_append(pool0, pool, rk, rv, k, v, si, ps, bt)[0] >= 1
 
