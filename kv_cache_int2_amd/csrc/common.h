@@ -16,6 +16,7 @@ constexpr int kBlock = 1152;     // bytes per (page, KV head) block
 constexpr int kKCodes = 0, kVCodes = 512, kMeta = 1024;  // token t's record {Ks, Kz, Vs, Vz} fp16 at kMeta + 8t
 constexpr int kMaxWindow = 1024;
 constexpr int kPartStride = 2 + kD;  // (m, l, acc[128]) per (batch, q head, split)
+constexpr int kMaxSplit = 2048;      // tokens per split at most: 16 tiles of 128, 4 per wave
 
 // Host-side shape check.  Returns OSCAR_OK or an error.
 inline int check_shape(const oscar_shape* s) {
@@ -41,7 +42,7 @@ inline SplitPlan plan_splits(int batch, int n_kv_heads, int max_tokens) {
   // 256 and 2048 tokens so ragged batches neither starve nor over-split.
   long units = (long)batch * n_kv_heads;
   long want = (long)max_tokens * units / 2048;
-  long s = want < 256 ? 256 : (want > 2048 ? 2048 : want);
+  long s = want < 256 ? 256 : (want > kMaxSplit ? kMaxSplit : want);
   s = (s + 63) / 64 * 64;
   int n = max_tokens <= 0 ? 1 : (int)((max_tokens + s - 1) / s);
   return SplitPlan{(int)s, n < 1 ? 1 : n};
@@ -88,6 +89,32 @@ __device__ __forceinline__ uint16_t f2h_bits(float x) {  // round to nearest eve
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Lane permutations inside a 16-lane DPP row (one VALU operand modifier each).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+constexpr int kDppSwap1 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kDppSwap2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within the row
+
+// Max / sum over the 16 lanes of a row, every lane receiving the same result
+// (each step combines two disjoint, already reduced groups of lanes, and
+// a + b == b + a, so all lanes compute bitwise the same value).
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_f32<kDppSwap1>(x));
+  x = fmaxf(x, dpp_f32<kDppSwap2>(x));
+  x = fmaxf(x, dpp_f32<kDppHalfMirror>(x));
+  return fmaxf(x, dpp_f32<kDppMirror>(x));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_f32<kDppSwap1>(x);
+  x += dpp_f32<kDppSwap2>(x);
+  x += dpp_f32<kDppHalfMirror>(x);
+  return x + dpp_f32<kDppMirror>(x);
+}
 
 }  // namespace oscar
 #endif

@@ -229,48 +229,65 @@ __device__ __forceinline__ void combine_and_store(const SplitParams& p, const fl
 // Raw bytes of one 128-token tile (8 pages) as one lane needs them.
 struct Tile {
   uint2 kc[8];    // K row bytes 8lg..8lg+7 of token lr, per page
-  uint2 meta[8];  // token lr's record {Ks, Kz, Vs, Vz}, zero past the history end
+  uint2 meta[8];  // token lr's record {Ks, Kz, Vs, Vz} (any value past the history end)
   uint4 vlo[2], vhi[2];  // V words of channels 8lr..8lr+7, pages 2lg and 2lg+1
   uint32_t page_ok;      // bit pp: page pp of the tile exists in this split and in the pool
 };
 
-// All loads of a tile are issued back to back with no branches: lanes 0..7 read
-// the tile's block-table entries, every page index is broadcast with readlane,
-// and a missing page (past the split or the table, or out of the pool) is read
-// as page 0 and masked, so the memory system sees the whole tile at once.
-__device__ __forceinline__ void load_tile(const SplitParams& p, const int* btr, int h, int pbase, int P1,
-                                          int t_end, int lg, int lr, Tile& t) {
+// Block-table entries of a wave's tiles.  The wave's k-th tile is tile
+// wave + 4k of the split (the waves take tiles round robin); lane 8j + pp holds
+// the page of page pp of the wave's tile k0 + j, or -1 when that page is past
+// the split, past the table or outside the pool.  One load serves 8 tiles, so no
+// tile waits on a block-table read before its own loads can start.
+struct TileTable {
+  int ent;        // this lane's entry
+  uint64_t live;  // ballot of ent >= 0
+};
+
+__device__ __forceinline__ TileTable load_table(const SplitParams& p, const int* btr, int P0, int P1,
+                                                int wave, int k0) {
   const int lane = threadIdx.x & 63;
-  const int pgl = pbase + (lane & 7);
-  int ent = pgl <= P1 ? btr[pgl] : -1;
-  if (ent >= p.n_pages) ent = -1;
-  t.page_ok = (uint32_t)__ballot(ent >= 0) & 0xffu;
+  const int pg = P0 + 8 * (wave + 4 * (k0 + (lane >> 3))) + (lane & 7);
+  int e = pg <= P1 ? btr[pg] : -1;
+  e = (e >= 0 && e < p.n_pages) ? e : -1;
+  return TileTable{e, __ballot(e >= 0)};
+}
+
+// All loads of one tile (j-th of its table chunk) are issued back to back with
+// no branches: every page index is broadcast with readlane (so each page's block
+// address is a scalar and a lane only adds its fixed offset), and a missing
+// page is read as page 0 and masked, so the memory system sees the whole tile
+// at once.
+__device__ __forceinline__ void load_tile(const SplitParams& p, const TileTable& tt, int j, int h, int pbase,
+                                          int t_end, int lg, int lr, Tile& t) {
+  t.page_ok = (uint32_t)(tt.live >> (8 * j)) & 0xffu;
+  const uint32_t off_k = kKCodes + 32 * lr + 8 * lg;
+  const uint32_t off_m = kMeta + 8 * lr;
+  const uint32_t off_v = kVCodes + 32 * lr;
   int pages[8];
 #pragma unroll
   for (int pp = 0; pp < 8; ++pp) {
-    const int e = __builtin_amdgcn_readlane(ent, pp);
+    const int e = __builtin_amdgcn_readlane(tt.ent, 8 * j + pp);
     pages[pp] = e < 0 ? 0 : e;
   }
 #pragma unroll
   for (int pp = 0; pp < 8; ++pp) {
     const uint8_t* blk = p.pool + ((int64_t)pages[pp] * p.hkv + h) * kBlock;
-    t.kc[pp] = *reinterpret_cast<const uint2*>(blk + kKCodes + 32 * lr + 8 * lg);
-    t.meta[pp] = *reinterpret_cast<const uint2*>(blk + kMeta + 8 * lr);
+    t.kc[pp] = *reinterpret_cast<const uint2*>(blk + off_k);
+    t.meta[pp] = *reinterpret_cast<const uint2*>(blk + off_m);
   }
+  // V words: lane group lg takes pages 2lg and 2lg + 1 (entries of lanes
+  // 8j + 2lg + qq, fetched across lanes)
 #pragma unroll
   for (int qq = 0; qq < 2; ++qq) {
-    const int pv = lg == 0 ? pages[qq] : lg == 1 ? pages[2 + qq] : lg == 2 ? pages[4 + qq] : pages[6 + qq];
-    const uint8_t* blk = p.pool + ((int64_t)pv * p.hkv + h) * kBlock + kVCodes + 32 * lr;
+    int pv = __builtin_amdgcn_ds_bpermute(4 * (8 * j + 2 * lg + qq), tt.ent);
+    pv = pv < 0 ? 0 : pv;
+    const uint8_t* blk = p.pool + ((int64_t)pv * p.hkv + h) * kBlock + off_v;
     t.vlo[qq] = *reinterpret_cast<const uint4*>(blk);
     t.vhi[qq] = *reinterpret_cast<const uint4*>(blk + 16);
   }
-  // slots past the history end or on a missing page may hold anything: their
-  // record must not reach the per-tile scale exponent or the sums
-#pragma unroll
-  for (int pp = 0; pp < 8; ++pp) {
-    const bool live = ((t.page_ok >> pp) & 1u) && (pbase + pp) * 16 + lr < t_end;
-    if (!live) t.meta[pp] = make_uint2(0, 0);
-  }
+  // no use of the loaded registers here: the caller computes another tile
+  // while these loads are in flight
 }
 
 // Pins a value at this point of the program.  The matrix instructions read
@@ -311,13 +328,22 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t
     }
   }
   // ---- online softmax, weights, w terms -> LDS ----
+  // slots past the history end or on a missing page may hold anything: their
+  // record must not reach the per-tile scale exponent or the sums
+  uint2 meta[8];
+#pragma unroll
+  for (int pp = 0; pp < 8; ++pp) {
+    const bool live = ((t.page_ok >> pp) & 1u) && (pbase + pp) * 16 + lr < t_end;
+    meta[pp].x = live ? t.meta[pp].x : 0u;
+    meta[pp].y = live ? t.meta[pp].y : 0u;
+  }
   float wsum[NRG];
   float vsmax = 0.f;
 #pragma unroll
-  for (int pp = 0; pp < 8; ++pp) vsmax = fmaxf(vsmax, h2f((uint16_t)(t.meta[pp].y & 0xffffu)));
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) vsmax = fmaxf(vsmax, __shfl_xor(vsmax, o));
+  for (int pp = 0; pp < 8; ++pp) vsmax = fmaxf(vsmax, h2f((uint16_t)(meta[pp].y & 0xffffu)));
+  vsmax = row_max16(vsmax);
   const int wexp = exponent_above(vsmax);  // every w = p vs <= vsmax < 2^wexp
+  const float wmul = ldexpf(1.f, 7 - wexp);  // w * wmul < 128, exact (a power of two)
 #pragma unroll
   for (int rg = 0; rg < NRG; ++rg) {
     const bool hv = 4 * rg + lg < p.gw;
@@ -327,13 +353,14 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t
     for (int pp = 0; pp < 8; ++pp) {
       const int tok = (pbase + pp) * 16 + lr;
       const bool ok = hv && tok < t_end && ((t.page_ok >> pp) & 1u);
-      const float ks = h2f((uint16_t)(t.meta[pp].x & 0xffffu));
-      const float kz = h2f((uint16_t)(t.meta[pp].x >> 16));
-      lgt[pp] = ok ? (kz * qsr[rg] + ks * raw[rg][pp]) * p.scale_log2 : kNegInf;
+      const float ks = h2f((uint16_t)(meta[pp].x & 0xffffu));
+      const float kz = h2f((uint16_t)(meta[pp].x >> 16));
+      // computed on every lane, then masked: a select, not a branch
+      const float v = pin((kz * qsr[rg] + ks * raw[rg][pp]) * p.scale_log2);
+      lgt[pp] = ok ? v : kNegInf;
       mx = fmaxf(mx, lgt[pp]);
     }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    mx = row_max16(mx);
     const float m_new = fmaxf(st.m_run[rg], mx);
     if (__any(m_new > st.m_run[rg])) {
       const float alpha = (m_new == kNegInf) ? 1.f : exp2f(st.m_run[rg] - m_new);
@@ -345,24 +372,23 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t
     }
     float w[8];
     float ws = 0.f;
+    const float m_safe = st.m_run[rg] == kNegInf ? 0.f : st.m_run[rg];  // exp2(-inf - m_safe) = 0
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
-      const float pv = lgt[pp] == kNegInf ? 0.f : exp2f(lgt[pp] - st.m_run[rg]);
-      const float vs = h2f((uint16_t)(t.meta[pp].y & 0xffffu));
-      const float vz = h2f((uint16_t)(t.meta[pp].y >> 16));
+      const float pv = exp2f(lgt[pp] - m_safe);
+      const float vs = h2f((uint16_t)(meta[pp].y & 0xffffu));
+      const float vz = h2f((uint16_t)(meta[pp].y >> 16));
       st.l_part[rg] += pv;
       st.az_part[rg] = fmaf(pv, fmaf(1.5f, vs, vz), st.az_part[rg]);
       w[pp] = pv * vs;
       ws += w[pp];
     }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) ws += __shfl_xor(ws, o);
-    wsum[rg] = ws;
+    wsum[rg] = row_sum16(ws);
     uint8_t* tile_rg = wt + rg * 2048;
 #pragma unroll
     for (int pp = 0; pp < 8; pp += 2) {
       uint32_t tt[4];
-      split4(ldexpf(w[pp], 7 - wexp), ldexpf(w[pp + 1], 7 - wexp), tt);
+      split4(w[pp] * wmul, w[pp + 1] * wmul, tt);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint8_t* row = tile_rg + (4 * lg + j) * 128 + slot_pos;
@@ -419,7 +445,7 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t
 // the next tile's loads in flight while it computes the current one.
 // ---------------------------------------------------------------------------
 template <int G>
-__global__ __launch_bounds__(256) void int2_split_kernel(SplitParams p) {
+__global__ __launch_bounds__(256, G <= 4 ? 2 : 1) void int2_split_kernel(SplitParams p) {
   constexpr int NRG = (G + 3) / 4;                    // MFMA row groups of 4 heads
   constexpr int kTileBytes = 4 * NRG * 16 * 128;     // per-wave w-term tiles
   constexpr int kCombBytes = 4 * G * kD * 4 + 2 * 4 * G * 4;
@@ -436,7 +462,7 @@ __global__ __launch_bounds__(256) void int2_split_kernel(SplitParams p) {
 
   __shared__ __align__(16) uint8_t smem[kSmem];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lr = lane & 15;
 
   // score operands prepared once per (sequence, KV head)
@@ -468,10 +494,32 @@ __global__ __launch_bounds__(256) void int2_split_kernel(SplitParams p) {
   const int n_tiles = (P1 - P0 + 8) >> 3;
   const int* btr = p.block_table + (int64_t)b * p.max_pages;
 
-  for (int tile = wave; tile < n_tiles; tile += 4) {
-    Tile ta;
-    load_tile(p, btr, h, P0 + 8 * tile, P1, t_end, lg, lr, ta);
-    compute_tile<G, NRG>(p, ta, P0 + 8 * tile, t_end, lg, lr, qa, qsc, qsr, wt, st);
+  // The wave's tiles k = 0 .. ntw-1 are tiles wave + 4k of the split (at most
+  // 4: a split holds at most 2048 tokens = 16 tiles).  One block-table load
+  // covers them all.  Two tiles are in flight at a time: the loads of tile k + 1
+  // are issued before tile k is computed.  Those loads are unconditional (a tile
+  // past the wave's last reads page 0 and is never computed), so no branch
+  // makes the compiler wait for them early.  One row group only: with two the
+  // registers of a second tile would cost the occupancy they buy.
+  const int ntw = wave < n_tiles ? (n_tiles - wave + 3) >> 2 : 0;
+  const TileTable tab = load_table(p, btr, P0, P1, wave, 0);
+  auto pbase_of = [&](int k) { return P0 + 8 * (wave + 4 * k); };
+  if constexpr (NRG > 1) {
+    for (int k = 0; k < ntw; ++k) {
+      Tile ta;
+      load_tile(p, tab, k, h, pbase_of(k), t_end, lg, lr, ta);
+      compute_tile<G, NRG>(p, ta, pbase_of(k), t_end, lg, lr, qa, qsc, qsr, wt, st);
+    }
+  } else {
+    Tile ta, tb;
+    load_tile(p, tab, 0, h, pbase_of(0), t_end, lg, lr, ta);
+    for (int k = 0; k < ntw; k += 2) {
+      load_tile(p, tab, k + 1, h, pbase_of(k + 1), t_end, lg, lr, tb);
+      compute_tile<G, NRG>(p, ta, pbase_of(k), t_end, lg, lr, qa, qsc, qsr, wt, st);
+      if (k + 1 >= ntw) break;
+      load_tile(p, tab, k + 2, h, pbase_of(k + 2), t_end, lg, lr, ta);
+      compute_tile<G, NRG>(p, tb, pbase_of(k + 1), t_end, lg, lr, qa, qsc, qsr, wt, st);
+    }
   }
 
   // ---- per-wave partial -> LDS -> workgroup partial ----
@@ -481,12 +529,7 @@ __global__ __launch_bounds__(256) void int2_split_kernel(SplitParams p) {
   float* cl = cm + 4 * G;                        // [4][G]
 #pragma unroll
   for (int rg = 0; rg < NRG; ++rg) {
-    float l = st.l_part[rg], az = st.az_part[rg];
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      l += __shfl_xor(l, o);
-      az += __shfl_xor(az, o);
-    }
+    const float l = row_sum16(st.l_part[rg]), az = row_sum16(st.az_part[rg]);
     const int head = 4 * rg + lg;
     if (head < p.gw) {
 #pragma unroll
