@@ -73,7 +73,7 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
-    ap.add_argument("--cpu-units", type=int, default=3, help="(sequence, KV head) units the oracle times")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="decode time the oracle baseline spends")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -219,7 +219,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int2 codes / fp32 math",
+        "dtype": "f32",
         "data": "synthetic (seeded Gaussian K/V, 4 key outlier channels x20; no dataset exists for this path)",
         "config": {"workload": f"long-context decode step: append 1 token/seq + INT2 decode, B={B}, n={nmax}, "
                                f"{HQ}q/{HKV}kv heads, d=128, group 128, 16-token scattered pages, bf16 window {W}",
@@ -242,14 +242,17 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(s, rk, rv, args.cpu_units, step_bytes_int2)
+        line["cpu_baseline"] = cpu_baseline(s, rk, rv, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(s, rk_bits, rv_bits, units: int, step_bytes: float):
+def cpu_baseline(s, rk_bits, rv_bits, target_s: float, max_units: int = 3):
     """The oracle (numpy fp64, untuned) decoding a bounded sample of the same
-    workload on the host: ``units`` (sequence, KV head) pairs at full context,
-    each from an oracle-built pool, BLAS pinned to one thread."""
+    workload on the host, BLAS pinned to one thread: up to ``max_units``
+    (sequence, KV head) pairs at full context, each with its own oracle-built
+    pool (building it is not timed), decoded round robin until ``target_s``
+    seconds of decode time have been spent.  Throughput is in the bench's unit:
+    algorithmic cache bytes of the decoded units per second."""
     from threadpoolctl import threadpool_limits
 
     import workloads as wl
@@ -257,10 +260,9 @@ def cpu_baseline(s, rk_bits, rv_bits, units: int, step_bytes: float):
 
     rkf, rvf = ref.bf16_to_f64(rk_bits), ref.bf16_to_f64(rv_bits)
     q = wl.decode_queries(s)
-    total_t = 0.0
-    total_bytes = 0.0
+    units = []
     with threadpool_limits(limits=1):
-        for u in range(units):
+        for u in range(max_units):
             b, h = u % s.batch, (3 * u) % s.n_kv_heads
             n = int(s.seq_lens[b])
             k, v = wl.context_kv(s, b)
@@ -272,19 +274,110 @@ def cpu_baseline(s, rk_bits, rv_bits, units: int, step_bytes: float):
             wv = np.zeros_like(wk)
             ref.append_sequence_ref(rkf[h:h + 1], rvf[h:h + 1], k[:, h:h + 1], v[:, h:h + 1], bt[0], pool, wk[0],
                                     wv[0], s.window)
+            units.append((b, h, n, bt, pool, wk, wv))
+            del k, v
+        total_t, total_bytes, calls = 0.0, 0.0, 0
+        while total_t < target_s:
+            b, h, n, bt, pool, wk, wv = units[calls % len(units)]
             qq = q[b:b + 1, h * s.gqa:(h + 1) * s.gqa]
             t = time.perf_counter()
             ref.decode_ref(rkf[h:h + 1], rvf[h:h + 1], qq, np.array([n]), bt, pool, wk, wv, s.window)
             total_t += time.perf_counter() - t
             w = min(n, s.window)
             total_bytes += (n - w) * 72 + w * 512
+            calls += 1
     units_per_step = s.batch * s.n_kv_heads
-    gbs = total_bytes / total_t / 1e9
-    return {"value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{units} of {units_per_step} (sequence, KV head) decode units at n={int(s.seq_lens.max())} "
-                      f"(oracle decode_ref: unpack pool bytes + fp64 attention), {total_t:.1f}s",
-            "decode_tokens_per_s_equiv": s.batch / (total_t / units * units_per_step)}
+    return {"value": total_bytes / total_t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} decode calls (oracle decode_ref: unpack pool bytes + fp64 attention) over "
+                      f"{len(units)} of the {units_per_step} (sequence, KV head) units at n={int(s.seq_lens.max())}, "
+                      f"round robin, {total_t:.1f} s of decode time on 1 thread",
+            "decode_tokens_per_s_equiv": s.batch / (total_t / calls * units_per_step)}
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (text under profiles/): kernel trace statistics and the
+# HBM traffic counters of the INT2 split kernel, scaled by the copy probe.
+# ---------------------------------------------------------------------------
+def _short_kernel(name: str) -> str:
+    n = name.replace("oscar::(anonymous namespace)::", "").replace("void ", "")
+    return n.split("(")[0]
+
+
+def _csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+
+    files = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def summarize_trace(directory: str, command: str) -> str:
+    """Kernel statistics of a `rocprofv3 --kernel-trace --stats --output-format csv` run."""
+    rows = _csv_rows(directory, "kernel_stats.csv")
+    out = ["# rocprofv3 kernel statistics", f"# command: {command}", "#",
+           f"# {'kernel':44s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_%':>8s}"]
+    for r in rows:
+        k = _short_kernel(r["Name"])
+        if k.startswith("at::"):
+            continue
+        out.append(f"  {k:44s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                   f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}")
+    return "\n".join(out) + "\n"
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, command: str) -> str:
+    """HBM bytes per launch of the INT2 split kernel from FETCH_SIZE and WRITE_SIZE
+    runs (KiB per dispatch), each scaled by what the same counter reads for the
+    copy probe of known size (2 GiB read + 2 GiB written per launch)."""
+    def per_kernel(directory, counter):
+        acc = {}
+        for r in _csv_rows(directory, "counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(_short_kernel(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return {k: float(np.mean(v)) for k, v in acc.items()}
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy_bytes = float(2 << 30)
+    f_copy = fetch["copy_kernel"] * 1024.0
+    w_copy = write["copy_kernel"] * 1024.0
+    f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
+    split = [k for k in fetch if k.startswith("int2_split_kernel")][0]
+    fb = fetch[split] * 1024.0 * f_scale
+    wb = write[split] * 1024.0 * w_scale
+    lines = ["# HBM traffic of the INT2 split kernel (rocprofv3 --pmc), long-context decode B=8 n=100000",
+             f"# command: {command}",
+             "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by copy_bytes / (counter of the",
+             "# copy probe), the probe moving 2 GiB each way per launch.",
+             f"decode_source_sha: {source_sha()}",
+             f"split_kernel: {split}",
+             f"fetch_kib_raw: {fetch[split]:.1f}",
+             f"write_kib_raw: {write[split]:.1f}",
+             f"copy_fetch_kib_raw: {fetch['copy_kernel']:.1f}",
+             f"copy_write_kib_raw: {write['copy_kernel']:.1f}",
+             f"fetch_scale: {f_scale:.4f}",
+             f"write_scale: {w_scale:.4f}",
+             f"fetch_bytes_per_launch: {fb:.0f}",
+             f"write_bytes_per_launch: {wb:.0f}"]
+    for k in sorted(fetch):
+        if k.startswith("at::"):
+            continue
+        lines.append(f"# {k:40s} FETCH_SIZE {fetch[k]:12.1f} KiB  WRITE_SIZE {write.get(k, float('nan')):12.1f} KiB (raw)")
+    return "\n".join(lines) + "\n"
 
 
 if __name__ == "__main__":
-    main()
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
+        # bench.py --summarize-trace DIR "COMMAND"
+        sys.stdout.write(summarize_trace(sys.argv[2], sys.argv[3]))
+    elif len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
+        # bench.py --summarize-pmc FETCH_DIR WRITE_DIR "COMMAND"
+        sys.stdout.write(summarize_pmc(sys.argv[2], sys.argv[3], sys.argv[4]))
+    else:
+        main()
