@@ -73,6 +73,7 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-append", action="store_true", help="skip the prefill-ingest (append) leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="decode time the oracle baseline spends")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -206,6 +207,8 @@ def main():
         }
     assert torch.isfinite(out).all()
 
+    res_append = None if args.no_append else append_leg(K, torch, dev, shape, rkd, rvd, args)
+
     achieved = b_hist / split_s / 1e9 if split_s else None
     traffic = load_traffic(b_hist)
     line = {
@@ -228,6 +231,7 @@ def main():
         "bf16_kv": res_bf16,
         "speedup_vs_bf16": (res_bf16["ms_per_step"] / (dt * 1e3)) if res_bf16 else None,
         "hbm_probe_copy_gbs": probe_gbs,
+        "append": res_append,
         "roofline": {
             "kernel": "int2_split_kernel",
             "bound": "hbm",
@@ -244,6 +248,49 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(s, rk, rv, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def append_leg(K, torch, dev, shape, rkd, rvd, args):
+    """Prefill ingest: oscar_quantize_append of 65536 new tokens x 8 KV heads into
+    empty pages of one sequence (bf16 Gaussian K/V with outlier channels), timed
+    on the append kernel's own events.  Algorithmic bytes per call: bf16 K and V
+    read (512 B per token and KV head), codes + scale/zero written (72 B), the
+    last 128 tokens written to the bf16 window (512 B), both rotations read."""
+    import workloads as wl
+
+    s4 = wl.spec(4)
+    n, hkv, w = int(s4.seq_lens[0]), s4.n_kv_heads, s4.window
+    k, v, si, ps = wl.prefill_tokens(s4, 0)
+    bt, n_pages = wl.page_table(s4)
+
+    def T(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    kd, vd, sid, psd, btd = T(k), T(v), T(si), T(ps), T(bt)
+    lens = T(np.array([n], np.int32))
+    pool = torch.zeros((n_pages, hkv, K.BLOCK_BYTES), dtype=torch.uint8, device=dev)
+    wk = torch.zeros((1, w, hkv, 128), dtype=torch.int16, device=dev)
+    wv = torch.zeros_like(wk)
+    for _ in range(2):
+        K.oscar_quantize_append(shape, rkd, rvd, kd, vd, sid, psd, btd, lens, pool, wk, wv)
+    torch.cuda.synchronize()
+    reps = 10
+    K.oscar_timing_begin(4 * reps + 8)
+    for _ in range(reps):
+        K.oscar_quantize_append(shape, rkd, rvd, kd, vd, sid, psd, btd, lens, pool, wk, wv)
+    torch.cuda.synchronize()
+    ms, kinds = K.oscar_timing_end(4 * reps + 8)
+    t = float(np.mean([m for m, kk in zip(ms, kinds) if kk == 3])) / 1e3
+    byts = n * hkv * (512 + 72) + min(n, w) * hkv * 512 + 2 * hkv * 128 * 128 * 2
+    flops = 2 * 2 * n * hkv * 128 * 128
+    log(f"append 65536 tokens: {t * 1e6:.1f} us, {byts / t / 1e9:.0f} GB/s, rotation {flops / t / 1e12:.1f} TFLOP/s")
+    return {"workload": "prefill ingest: 65536 bf16 K/V tokens x 8 KV heads into empty pages (one sequence)",
+            "avg_launch_ms": t * 1e3, "algorithmic_bytes": byts, "achieved_gbs": byts / t / 1e9,
+            "frac_hbm": byts / t / 1e9 / PEAK_HBM_GBS, "rotation_tflops": flops / t / 1e12,
+            "mfma_frac_bf16": flops / t / 1e12 / 2500.0}
 
 
 def cpu_baseline(s, rk_bits, rv_bits, target_s: float, max_units: int = 3):
