@@ -49,18 +49,23 @@ inline SplitPlan plan_splits(int batch, int n_kv_heads, int max_tokens) {
 }
 
 // Workspace layout (bytes, each region 256-aligned):
-//   qsum  float [B][Hq]                          sum of the rotated query's channels
-//   qop   int   [B][Hkv][ceil(G/4)][64][9]       per-lane fp8 score operand (8 dwords) + E8M0 scale
-//   part  float [B][Hq][n_splits][130]           split partials (m, l, acc[128])
+//   qsum      float [B][Hq]                      sum of the rotated query's channels
+//   qop       int   [B][Hkv][ceil(G/4)][64][9]   per-lane fp8 score operand (8 dwords) + E8M0 scale
+//   part      float [B][Hq][n_splits][130]       split partials (m, l, acc[128])
+//   wpart     float [B][Hq][130]                 window partials (m, l, acc[128])
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-inline size_t qsum_bytes(int batch, int n_q_heads) { return align256((size_t)batch * n_q_heads * sizeof(float)); }
-inline int q_combos(int n_q_heads, int n_kv_heads) { return (n_q_heads / n_kv_heads + 3) / 4; }
-inline size_t qop_bytes(int batch, int n_q_heads, int n_kv_heads) {
-  return align256((size_t)batch * n_kv_heads * q_combos(n_q_heads, n_kv_heads) * 64 * 9 * sizeof(int));
-}
-inline size_t workspace_bytes(int batch, int n_q_heads, int n_kv_heads, const SplitPlan& p) {
-  size_t parts = (size_t)batch * n_q_heads * p.n_splits * kPartStride * sizeof(float);
-  return qsum_bytes(batch, n_q_heads) + qop_bytes(batch, n_q_heads, n_kv_heads) + parts;
+struct WorkspaceLayout {
+  size_t qsum, qop, part, wpart, total;
+};
+inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, const SplitPlan& p) {
+  const size_t g4 = (size_t)((n_q_heads / n_kv_heads + 3) / 4);
+  WorkspaceLayout w{};
+  w.qsum = 0;
+  w.qop = w.qsum + align256((size_t)batch * n_q_heads * sizeof(float));
+  w.part = w.qop + align256((size_t)batch * n_kv_heads * g4 * 64 * 9 * sizeof(int));
+  w.wpart = w.part + align256((size_t)batch * n_q_heads * p.n_splits * kPartStride * sizeof(float));
+  w.total = w.wpart + align256((size_t)batch * n_q_heads * kPartStride * sizeof(float));
+  return w;
 }
 
 // Event-pair recording around main kernels (measurement only).

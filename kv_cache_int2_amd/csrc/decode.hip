@@ -187,18 +187,29 @@ __global__ __launch_bounds__(256) void prep_q_kernel(const uint16_t* __restrict_
 struct SplitParams {
   const float* qsum;          // [B][Hq]      (INT2 path)
   const int* qop;             // [B][Hkv][ceil(G/4)][64][9] (INT2 path)
-  const uint16_t* q;          // [B][Hq][128] bf16 queries (bf16 comparator)
+  const uint16_t* q;          // [B][Hq][128] bf16 queries
   const int32_t* seq_lens;
   const int32_t* block_table;
   const uint8_t* pool;        // INT2 pool
   const uint16_t* kv_pool;    // bf16 pool
-  float* part;                // [B][Hq][n_splits][130]
+  const uint16_t* r_v;        // INT2: value rotations [Hkv][128][128] (un-rotation in the merge)
+  const uint16_t* win_k;      // INT2: bf16 window rings [B][W][Hkv][128]
+  const uint16_t* win_v;
+  float* part;                // [B][Hq][n_splits][130] split partials
+  float* wpart;               // INT2: [B][Hq][130] window partials (unrotated domain)
+  float* out;                 // [B][Hq][128]
   int64_t n_pages;
-  int hq, hkv, max_pages, window, split, n_splits;
-  int gsub;                   // workgroups per KV head, each taking G of its query heads
+  int batch, hq, hkv, max_pages, max_len, window, split, n_splits;
+  int gsub;                   // workgroups per KV head, each taking gw of its query heads
   int gw;                     // query heads a workgroup really has (<= G of its instantiation)
   float scale_log2;           // log2(e) / sqrt(d)
 };
+
+// Sequence length as the kernels see it: clamped to [0, max_len].
+__device__ __forceinline__ int seq_len_of(const SplitParams& p, int b) {
+  const int n = p.seq_lens[b];
+  return n < 0 ? 0 : (n > p.max_len ? p.max_len : n);
+}
 
 // Combine the 4 waves' (m, l, acc) partials (LDS) into the workgroup partial.
 template <int G>
@@ -435,6 +446,135 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t
   __builtin_amdgcn_wave_barrier();
 }
 
+__device__ __forceinline__ float wave_max64(float x) {
+  x = row_max16(x);
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+
+constexpr int kWinPass = 128;  // window tokens per pass (one per thread pair)
+
+template <int GW>
+constexpr int window_smem_bytes() { return (2 * GW * kD + kWinPass * 65 + 12 * GW) * 4; }
+
+// bf16 window of one merge unit: positions [n - w, n) at ring slots pos % W,
+// unrotated, for query heads hq0 .. hq0 + gw - 1; writes (m, l, acc[128]) per
+// head to the window partials.  A pass takes up to 128 tokens with every load
+// issued up front: thread pair (t, half) holds 64 dims of token t's key (for
+// the scores) and stages the same dims of its value in LDS (for P V).
+template <int GW>
+__device__ void window_unit(const SplitParams& p, int b, int h, int hq0, int n, int w, float* sm) {
+  constexpr int PER = (GW * kD + 255) / 256;
+  const int tid = threadIdx.x, gw = p.gw, wave = tid >> 6;
+  float* qs = sm;                                            // [GW][128]
+  uint32_t* vw = reinterpret_cast<uint32_t*>(qs + GW * kD);  // [kWinPass][65] bf16 pairs
+  float* ps = reinterpret_cast<float*>(vw + kWinPass * 65);  // [GW][kWinPass]
+  float* red = ps + GW * kWinPass;                           // [4][GW]
+  float* red2 = red + 4 * GW;                                // [4][GW]
+  float* Mrun = red2 + 4 * GW;                               // [GW]
+  float* Lrun = Mrun + GW;                                   // [GW]
+  float* Mnew = Lrun + GW;                                   // [GW]
+  float* Alph = Mnew + GW;                                   // [GW]
+  for (int e = tid; e < GW * kD; e += 256)
+    qs[e] = e < gw * kD ? bf16_to_f32(p.q[((int64_t)b * p.hq + hq0) * kD + e]) : 0.f;
+  if (tid < GW) {
+    Mrun[tid] = kNegInf;
+    Lrun[tid] = 0.f;
+  }
+  float o2[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) o2[k] = 0.f;
+  const int t = tid >> 1, hf = tid & 1;
+  for (int cs = n - w; cs < n; cs += kWinPass) {
+    const int nt = min(kWinPass, n - cs);
+    const bool valid = t < nt;
+    uint4 kk[8], vv[8];
+    if (valid) {
+      const int64_t row = (((int64_t)b * p.window + (cs + t) % p.window) * p.hkv + h) * kD + 64 * hf;
+      const uint4* kr = reinterpret_cast<const uint4*>(p.win_k + row);
+      const uint4* vr = reinterpret_cast<const uint4*>(p.win_v + row);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        kk[i] = kr[i];
+        vv[i] = vr[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kk[i] = vv[i] = make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();  // qs, Mrun ready; the previous pass is done with vw and ps
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t* dst = vw + t * 65 + 32 * hf + 4 * i;
+      dst[0] = vv[i].x; dst[1] = vv[i].y; dst[2] = vv[i].z; dst[3] = vv[i].w;
+    }
+    float sc[GW];
+#pragma unroll
+    for (int g = 0; g < GW; ++g) {
+      const float* qg = qs + g * kD + 64 * hf;
+      float d = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t u[4] = {kk[i].x, kk[i].y, kk[i].z, kk[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          d = fmaf(bf16lo(u[j]), qg[8 * i + 2 * j], fmaf(bf16hi(u[j]), qg[8 * i + 2 * j + 1], d));
+      }
+      d += dpp_f32<kDppSwap1>(d);  // the pair's two halves
+      sc[g] = (valid && g < gw) ? d * p.scale_log2 : kNegInf;
+      const float m = wave_max64(sc[g]);
+      if ((tid & 63) == 0) red[wave * GW + g] = m;
+    }
+    __syncthreads();
+    if (tid < GW) {
+      const float mc = fmaxf(fmaxf(red[tid], red[GW + tid]), fmaxf(red[2 * GW + tid], red[3 * GW + tid]));
+      const float mn = fmaxf(Mrun[tid], mc);
+      Mnew[tid] = mn;
+      Alph[tid] = mn == kNegInf ? 1.f : exp2f(Mrun[tid] - mn);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < GW; ++g) {
+      const float mn = Mnew[g];
+      const float pv = sc[g] == kNegInf ? 0.f : exp2f(sc[g] - mn);
+      if (hf == 0) ps[g * kWinPass + t] = pv;
+    }
+    __syncthreads();
+    if (tid < GW) {
+      float su = 0.f;
+      for (int tt = 0; tt < nt; ++tt) su += ps[tid * kWinPass + tt];
+      Lrun[tid] = Lrun[tid] * Alph[tid] + su;
+      Mrun[tid] = Mnew[tid];
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = tid + 256 * k;
+      const int g = e / kD, c = e % kD;
+      float acc = o2[k] * Alph[g];
+      const float* pg = ps + g * kWinPass;
+      for (int tt = 0; tt < nt; ++tt) {
+        const uint32_t x = vw[tt * 65 + (c >> 1)];
+        acc = fmaf(pg[tt], (c & 1) ? bf16hi(x) : bf16lo(x), acc);
+      }
+      o2[k] = acc;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e = tid + 256 * k;
+    if (e >= gw * kD) break;
+    const int g = e / kD, c = e % kD;
+    float* dst = p.wpart + ((int64_t)b * p.hq + hq0 + g) * kPartStride;
+    dst[2 + c] = o2[k];
+    if (c == 0) {
+      dst[0] = Mrun[g];
+      dst[1] = Lrun[g];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // INT2 history split on the matrix cores.  Lane l = 16 lg + lr.
 //   score MFMA output: head 4 rg + lg, token lr of the page;
@@ -449,18 +589,31 @@ __global__ __launch_bounds__(256, G <= 4 ? 2 : 1) void int2_split_kernel(SplitPa
   constexpr int NRG = (G + 3) / 4;                    // MFMA row groups of 4 heads
   constexpr int kTileBytes = 4 * NRG * 16 * 128;     // per-wave w-term tiles
   constexpr int kCombBytes = 4 * G * kD * 4 + 2 * 4 * G * 4;
-  constexpr int kSmem = kTileBytes > kCombBytes ? kTileBytes : kCombBytes;
+  constexpr int kS1 = kTileBytes > kCombBytes ? kTileBytes : kCombBytes;
+  constexpr int kSmem = kS1 > window_smem_bytes<G>() ? kS1 : window_smem_bytes<G>();
 
-  const int b = blockIdx.z, h = blockIdx.y / p.gsub, sp = blockIdx.x;
+  // z = 0: the bf16 windows (x = sequence); they are dispatched before every
+  // history split so that they overlap the history stream instead of trailing
+  // it.  z = 1 + b: history split x of sequence b.
+  const bool win_wg = blockIdx.z == 0;
+  if (win_wg && (int)blockIdx.x >= p.batch) return;
+  const int b = win_wg ? (int)blockIdx.x : (int)blockIdx.z - 1, h = blockIdx.y / p.gsub;
+  const int sp = win_wg ? -1 : (int)blockIdx.x;
   const int sub = blockIdx.y % p.gsub;
   const int hq0 = h * p.gw * p.gsub + sub * p.gw;  // first query head of this workgroup
-  const int n = clamp_len(p.seq_lens[b], p.max_pages);
-  const int hist = n - (n < p.window ? n : p.window);
+  const int n = seq_len_of(p, b);
+  const int w = n < p.window ? n : p.window;
+  const int hist = n - w;
+
+  __shared__ __align__(16) uint8_t smem[kSmem];
+
+  if (sp < 0) {  // the bf16 window of these heads, beside their history splits
+    window_unit<G>(p, b, h, hq0, n, w, reinterpret_cast<float*>(smem));
+    return;
+  }
   const int t_begin = sp * p.split;
   if (t_begin >= hist) return;
   const int t_end = min(t_begin + p.split, hist);
-
-  __shared__ __align__(16) uint8_t smem[kSmem];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lr = lane & 15;
@@ -552,7 +705,7 @@ __global__ __launch_bounds__(256, G <= 4 ? 2 : 1) void int2_split_kernel(SplitPa
 template <int G>
 __global__ __launch_bounds__(256) void bf16_split_kernel(SplitParams p) {
   const int b = blockIdx.z, h = blockIdx.y, sp = blockIdx.x;
-  const int n = clamp_len(p.seq_lens[b], p.max_pages);
+  const int n = seq_len_of(p, b);
   const int t_begin = sp * p.split;
   if (t_begin >= n) return;
   const int t_end = min(t_begin + p.split, n);
@@ -660,233 +813,139 @@ __global__ __launch_bounds__(256) void bf16_split_kernel(SplitParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// merge: LSE over splits; for the INT2 path also un-rotate with R_V^T and fold
-// in the bf16 window (positions [n - w, n) at ring slots pos % W).
+// merge: one workgroup per (sequence, q head).  Log-sum-exp merge of the split
+// partials; for the INT2 path the un-rotation by R_V^T and the bf16 window's
+// partial, then the normalisation.  Every load the workgroup needs (the split
+// partials, its 128 x 128 R_V tile, the window partial) is issued up front, so
+// the kernel costs about one memory round trip.  A head with no position at
+// all gets zeros.
 // ---------------------------------------------------------------------------
-struct MergeParams {
-  const float* part;
-  const uint16_t* r_v;       // nullptr: no un-rotation, no window (bf16 comparator)
-  const uint16_t* q;         // bf16 [B][Hq][128] (window scores)
-  const uint16_t* win_k;
-  const uint16_t* win_v;
-  const int32_t* seq_lens;
-  float* out;
-  int hq, hkv, max_pages, window, split, n_splits;
-  float scale_log2;
-};
+constexpr int kMergeSplits = 64;  // splits whose accumulators a thread pair holds in registers per pass
 
-constexpr int kWinChunk = 32;
-constexpr int kSplitChunk = 128;  // splits whose weights are staged in LDS at a time
-
-template <int G>
-__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  constexpr int PER = (G * kD + 255) / 256;  // (head, channel) elements per thread
-  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int n = clamp_len(p.seq_lens[b], p.max_pages);
+__global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
+  const int b = blockIdx.y, hq = blockIdx.x, h = hq / gq, tid = threadIdx.x;
   const bool int2 = p.r_v != nullptr;
+  const int n = seq_len_of(p, b);
   const int w = int2 ? (n < p.window ? n : p.window) : 0;
   const int hist = n - w;
-  const int ns = min((hist + p.split - 1) / p.split, p.n_splits);
+  const int ns = (hist + p.split - 1) / p.split;
 
-  __shared__ __align__(16) uint16_t rv_s[kD * kD];  // R_V[h], row-major [j][i]
-  __shared__ float a1[G][kD];                        // merged split accumulator
-  __shared__ float o2[G][kD];                        // window accumulator
-  __shared__ float qs[G][kD];
-  __shared__ float fsc[G][kSplitChunk];              // per-split weights, one chunk
-  __shared__ float M1[G], L1[G], M2[G], L2[G], al[G], mn[G];
-  __shared__ uint32_t kw[kWinChunk][65];
-  __shared__ uint32_t vw[kWinChunk][65];
-  __shared__ float sc[G][kWinChunk];
+  __shared__ float fs[kMergeSplits * 2];      // 2^(m_s - M), l_s of the current pass
+  __shared__ float red[256];
+  __shared__ float a1s[kD];
+  __shared__ float o1p[16][kD + 4];
+  __shared__ float Ms, Ls;
 
-  if (int2) {  // stage R_V early; consumed after the split merge
-    const uint4* src = reinterpret_cast<const uint4*>(p.r_v + (int64_t)h * kD * kD);
-    uint4* dst = reinterpret_cast<uint4*>(rv_s);
-    for (int i = tid; i < kD * kD / 8; i += 256) dst[i] = src[i];
-  }
-  for (int e = tid; e < G * kD; e += 256) {
-    qs[e / kD][e % kD] = bf16_to_f32(p.q[((int64_t)b * p.hq + h * G) * kD + e]);
-    o2[e / kD][e % kD] = 0.f;
-  }
-  // M1 per head: one wave per head, strided over splits
-  for (int g0 = 0; g0 < G; g0 += 4) {
-    const int g = g0 + (tid >> 6);
-    float M = kNegInf;
-    if (g < G) {
-      const float* base = p.part + ((int64_t)b * p.hq + h * G + g) * p.n_splits * kPartStride;
-      for (int s = tid & 63; s < ns; s += 64) M = fmaxf(M, base[s * kPartStride]);
-    }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-    if (g < G && (tid & 63) == 0) {
-      M1[g] = M;
-      M2[g] = kNegInf;
-      L2[g] = 0.f;
-    }
-  }
-  __syncthreads();
-  // a1 = sum_s 2^(m_s - M1) acc_s ; L1 = sum_s 2^(m_s - M1) l_s
-  float accv[PER], lsum[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) accv[k] = lsum[k] = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += kSplitChunk) {
-    const int cnt = min(kSplitChunk, ns - s0);
-    __syncthreads();
-    for (int e = tid; e < G * cnt; e += 256) {
-      const int g = e / cnt, s = e % cnt;
-      const float* ps = p.part + (((int64_t)b * p.hq + h * G + g) * p.n_splits + s0 + s) * kPartStride;
-      fsc[g][s] = exp2f(ps[0] - M1[g]);
-    }
-    __syncthreads();
-    // all loads of a batch of splits issued before the sums (latency bound otherwise)
-    for (int sb = 0; sb < cnt; sb += 16) {
-      const int nb = min(16, cnt - sb);
-      float x[PER][16], xl[PER][16];
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int e = tid + 256 * k;
-        const int g = (e < G * kD) ? e / kD : 0, c = e % kD;
-        const float* ps = p.part + (((int64_t)b * p.hq + h * G + g) * p.n_splits + s0 + sb) * kPartStride;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) {
-          x[k][s] = (e < G * kD && s < nb) ? ps[s * kPartStride + 2 + c] : 0.f;
-          xl[k][s] = (e < G * kD && s < nb && c == 0) ? ps[s * kPartStride + 1] : 0.f;
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int e = tid + 256 * k;
-        const int g = (e < G * kD) ? e / kD : 0;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) {
-          const float f = s < nb ? fsc[g][sb + s] : 0.f;
-          accv[k] = fmaf(f, x[k][s], accv[k]);
-          lsum[k] = fmaf(f, xl[k][s], lsum[k]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int e = tid + 256 * k;
-    if (e >= G * kD) break;
-    a1[e / kD][e % kD] = accv[k];
-    if (e % kD == 0) L1[e / kD] = lsum[k];
-  }
-  __syncthreads();
-
-  float o1[PER];
+  // R_V tile loads first (INT2): thread (cg, jg) takes channels 8cg..8cg+7 of rows 8jg..8jg+7
+  const int cg = tid & 15, jg = tid >> 4;
+  uint4 rv[8];
   if (int2) {
+    const uint16_t* r = p.r_v + ((int64_t)h * kD + 8 * jg) * kD + 8 * cg;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int e = tid + 256 * k;
-      o1[k] = 0.f;
-      if (e >= G * kD) break;
-      const int g = e / kD, i = e % kD;
-      float acc = 0.f;
-#pragma unroll 8
-      for (int j = 0; j < kD; ++j) acc = fmaf(bf16_to_f32(rv_s[j * kD + i]), a1[g][j], acc);
-      o1[k] = acc;
-    }
-    for (int cs = hist; cs < n; cs += kWinChunk) {
-      const int nt = min(kWinChunk, n - cs);
-      __syncthreads();
-      for (int e = tid; e < nt * 16; e += 256) {
-        const int t = e >> 4, u = e & 15;
-        const int64_t row = (((int64_t)b * p.window + (cs + t) % p.window) * p.hkv + h) * kD;
-        const uint4 kv4 = reinterpret_cast<const uint4*>(p.win_k + row)[u];
-        const uint4 vv4 = reinterpret_cast<const uint4*>(p.win_v + row)[u];
-        kw[t][4 * u] = kv4.x;
-        kw[t][4 * u + 1] = kv4.y;
-        kw[t][4 * u + 2] = kv4.z;
-        kw[t][4 * u + 3] = kv4.w;
-        vw[t][4 * u] = vv4.x;
-        vw[t][4 * u + 1] = vv4.y;
-        vw[t][4 * u + 2] = vv4.z;
-        vw[t][4 * u + 3] = vv4.w;
-      }
-      __syncthreads();
-      for (int e = tid; e < G * kWinChunk; e += 256) {
-        const int g = e / kWinChunk, t = e % kWinChunk;
-        float s = kNegInf;
-        if (t < nt) {
-          s = 0.f;
-          for (int u = 0; u < 64; ++u) {
-            const uint32_t x = kw[t][u];
-            s = fmaf(bf16lo(x), qs[g][2 * u], fmaf(bf16hi(x), qs[g][2 * u + 1], s));
-          }
-          s *= p.scale_log2;
-        }
-        sc[g][t] = s;
-      }
-      __syncthreads();
-      if (tid < G) {
-        float cmx = kNegInf;
-        for (int t = 0; t < nt; ++t) cmx = fmaxf(cmx, sc[tid][t]);
-        const float m_new = fmaxf(M2[tid], cmx);
-        al[tid] = exp2f(M2[tid] - m_new);
-        mn[tid] = m_new;
-      }
-      __syncthreads();
-      for (int e = tid; e < G * kWinChunk; e += 256) {
-        const int g = e / kWinChunk, t = e % kWinChunk;
-        sc[g][t] = t < nt ? exp2f(sc[g][t] - mn[g]) : 0.f;
-      }
-      __syncthreads();
-      if (tid < G) {
-        float s = 0.f;
-        for (int t = 0; t < nt; ++t) s += sc[tid][t];
-        L2[tid] = L2[tid] * al[tid] + s;
-        M2[tid] = mn[tid];
-      }
-      for (int e = tid; e < G * kD; e += 256) {
-        const int g = e / kD, c = e % kD;
-        float acc = o2[g][c] * al[g];
-        for (int t = 0; t < nt; ++t) {
-          const uint32_t x = vw[t][c >> 1];
-          acc = fmaf(sc[g][t], (c & 1) ? bf16hi(x) : bf16lo(x), acc);
-        }
-        o2[g][c] = acc;
-      }
+    for (int j = 0; j < 8; ++j) rv[j] = *reinterpret_cast<const uint4*>(r + j * kD);
+  }
+  // split partials: thread (c, half) sums channel c over the splits s = half, half + 2, ...
+  const int c = tid & 127, half = tid >> 7;
+  const float* base = p.part + ((int64_t)b * p.hq + hq) * p.n_splits * kPartStride;
+  float M = kNegInf;
+  for (int s = tid; s < ns; s += 256) M = fmaxf(M, base[s * kPartStride]);
+  M = wave_max64(M);
+  if ((tid & 63) == 0) red[tid >> 6] = M;
+  __syncthreads();
+  if (tid == 0) Ms = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  M = Ms;
+  float acc = 0.f, lsum = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += kMergeSplits) {
+    const int cnt = min(kMergeSplits, ns - s0);
+    __syncthreads();
+    if (tid < cnt) {
+      const float* ps = base + (s0 + tid) * kPartStride;
+      const float m = ps[0];
+      fs[tid] = m == kNegInf ? 0.f : exp2f(m - M);
+      fs[kMergeSplits + tid] = ps[1];
     }
     __syncthreads();
-  }
+    float x[kMergeSplits / 2];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int e = tid + 256 * k;
-    if (e >= G * kD) break;
-    const int g = e / kD, c = e % kD;
-    const float v1 = int2 ? o1[k] : a1[g][c];
-    const float M = fmaxf(M1[g], M2[g]);
-    const float f1 = M1[g] == kNegInf ? 0.f : exp2f(M1[g] - M);
-    const float f2 = M2[g] == kNegInf ? 0.f : exp2f(M2[g] - M);
-    p.out[((int64_t)b * p.hq + h * G + g) * kD + c] = (f1 * v1 + f2 * o2[g][c]) / (f1 * L1[g] + f2 * L2[g]);
+    for (int k = 0; k < kMergeSplits / 2; ++k) {
+      const int s = 2 * k + half;
+      x[k] = s < cnt ? base[(s0 + s) * kPartStride + 2 + c] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeSplits / 2; ++k) {
+      const int s = 2 * k + half;
+      if (s < cnt) {
+        acc = fmaf(fs[s], x[k], acc);
+        if (c == 0) lsum = fmaf(fs[s], fs[kMergeSplits + s], lsum);
+      }
+    }
+  }
+  red[tid] = acc;
+  if (c == 0) o1p[0][half] = lsum;
+  __syncthreads();
+  if (tid < kD) a1s[tid] = red[tid] + red[tid + 128];
+  if (tid == 0) Ls = o1p[0][0] + o1p[0][1];
+  __syncthreads();
+  float* dst = p.out + ((int64_t)b * p.hq + hq) * kD;
+  if (!int2) {
+    if (tid < kD) dst[tid] = Ls > 0.f ? a1s[tid] / Ls : 0.f;
+    return;
+  }
+  // o1 = R_V^T a1 from the register tile, partial sums over 8 rows per thread
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float aj = a1s[8 * jg + j];
+    const uint32_t u[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = fmaf(bf16lo(u[i]), aj, o[2 * i]);
+      o[2 * i + 1] = fmaf(bf16hi(u[i]), aj, o[2 * i + 1]);
+    }
+  }
+  __syncthreads();  // o1p[0][0..1] (the l sums) were read
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o1p[jg][8 * cg + i] = o[i];
+  __syncthreads();
+  if (tid < kD) {
+    float o1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) o1 += o1p[k][tid];
+    const float* wp = p.wpart + ((int64_t)b * p.hq + hq) * kPartStride;
+    const float m1 = M, m2 = wp[0];
+    const float Mx = fmaxf(m1, m2);
+    const float f1 = m1 == kNegInf ? 0.f : exp2f(m1 - Mx);
+    const float f2 = m2 == kNegInf ? 0.f : exp2f(m2 - Mx);
+    const float den = f1 * Ls + f2 * wp[1];
+    dst[tid] = den > 0.f ? (f1 * o1 + f2 * wp[2 + tid]) / den : 0.f;
   }
 }
 
 template <int G>
-int launch_decode(bool int2, const SplitParams& sp, const MergeParams& mp, const uint16_t* r_k,
-                  const uint16_t* q, int batch, hipStream_t s) {
+int launch_decode(bool int2, const SplitParams& sp, const uint16_t* r_k, int batch, hipStream_t s) {
+  // INT2: at most 8 query heads per workgroup (register budget of the MFMA
+  // tiles), and the 4-head instantiation for G < 4 masking the missing heads
+  constexpr int GW = G > 8 ? 8 : (G < 4 ? 4 : G);
+  SplitParams p2 = sp;
   if (int2) {
-    prep_q_kernel<G><<<dim3(batch, sp.hkv), 256, 0, s>>>(r_k, q, const_cast<float*>(sp.qsum),
+    p2.gw = G < GW ? G : GW;
+    p2.gsub = G / p2.gw;
+    prep_q_kernel<G><<<dim3(batch, sp.hkv), 256, 0, s>>>(r_k, sp.q, const_cast<float*>(sp.qsum),
                                                          const_cast<int*>(sp.qop), sp.hq, sp.hkv);
     if (hipGetLastError() != hipSuccess) return OSCAR_EHIP;
   }
   int slot = -1;
   timing_record_begin(s, int2 ? 1 : 2, &slot);
-  if (int2) {
-    // at most 8 query heads per workgroup (register budget of the MFMA tiles)
-    // and the 4-head instantiation for G < 4, masking the missing heads at run time
-    constexpr int GW = G > 8 ? 8 : (G < 4 ? 4 : G);
-    SplitParams p2 = sp;
-    p2.gw = G < GW ? G : GW;
-    p2.gsub = G / p2.gw;
-    int2_split_kernel<GW><<<dim3(sp.n_splits, sp.hkv * p2.gsub, batch), 256, 0, s>>>(p2);
-  } else {
+  if (int2)  // a leading z slab: one workgroup per (sequence, KV head, head subset) takes the bf16 window
+    int2_split_kernel<GW><<<dim3(sp.n_splits > batch ? sp.n_splits : batch, sp.hkv * p2.gsub, batch + 1), 256, 0, s>>>(p2);
+  else
     bf16_split_kernel<G><<<dim3(sp.n_splits, sp.hkv, batch), 256, 0, s>>>(sp);
-  }
   if (hipGetLastError() != hipSuccess) return OSCAR_EHIP;
   timing_record_end(s, slot);
-  merge_kernel<G><<<dim3(batch, sp.hkv), 256, 0, s>>>(mp);
+  merge_kernel<<<dim3(sp.hq, batch), 256, 0, s>>>(sp, G);
   return hipGetLastError() == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
 }
 
@@ -904,52 +963,44 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   if (!int2 && !kv_pool) return OSCAR_EINVAL;
   if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * kPage) return OSCAR_ENOSPACE;
   const SplitPlan plan = plan_splits(batch, shape->n_kv_heads, max_seq_len);
-  if (workspace_bytes < oscar::workspace_bytes(batch, shape->n_q_heads, shape->n_kv_heads, plan)) return OSCAR_ENOSPACE;
+  const WorkspaceLayout wl = workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads, plan);
+  if (workspace_bytes < wl.total) return OSCAR_ENOSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return OSCAR_EINVAL;
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   SplitParams sp{};
-  sp.qsum = reinterpret_cast<float*>(ws);
-  sp.qop = reinterpret_cast<int*>(ws + qsum_bytes(batch, shape->n_q_heads));
+  sp.qsum = reinterpret_cast<float*>(ws + wl.qsum);
+  sp.qop = reinterpret_cast<int*>(ws + wl.qop);
   sp.q = q;
   sp.seq_lens = seq_lens;
   sp.block_table = block_table;
   sp.pool = pool;
   sp.kv_pool = kv_pool;
-  sp.part = reinterpret_cast<float*>(ws + qsum_bytes(batch, shape->n_q_heads) +
-                                     qop_bytes(batch, shape->n_q_heads, shape->n_kv_heads));
+  sp.r_v = int2 ? r_v : nullptr;
+  sp.win_k = win_k;
+  sp.win_v = win_v;
+  sp.part = reinterpret_cast<float*>(ws + wl.part);
+  sp.wpart = reinterpret_cast<float*>(ws + wl.wpart);
+  sp.out = out;
   sp.n_pages = n_pages;
+  sp.batch = batch;
   sp.hq = shape->n_q_heads;
   sp.hkv = shape->n_kv_heads;
   sp.max_pages = max_pages_per_seq;
+  sp.max_len = max_seq_len;
   sp.window = int2 ? shape->window : 0;
   sp.split = plan.split;
   sp.n_splits = plan.n_splits;
   sp.gsub = 1;
   sp.gw = shape->n_q_heads / shape->n_kv_heads;
   sp.scale_log2 = kLog2e / sqrtf((float)kD);
-  MergeParams mp{};
-  mp.part = sp.part;
-  mp.r_v = int2 ? r_v : nullptr;
-  mp.q = q;
-  mp.win_k = win_k;
-  mp.win_v = win_v;
-  mp.seq_lens = seq_lens;
-  mp.out = out;
-  mp.hq = sp.hq;
-  mp.hkv = sp.hkv;
-  mp.max_pages = sp.max_pages;
-  mp.window = sp.window;
-  mp.split = sp.split;
-  mp.n_splits = sp.n_splits;
-  mp.scale_log2 = sp.scale_log2;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (shape->n_q_heads / shape->n_kv_heads) {
-    case 1: return launch_decode<1>(int2, sp, mp, r_k, q, batch, s);
-    case 2: return launch_decode<2>(int2, sp, mp, r_k, q, batch, s);
-    case 4: return launch_decode<4>(int2, sp, mp, r_k, q, batch, s);
-    case 8: return launch_decode<8>(int2, sp, mp, r_k, q, batch, s);
-    case 16: return launch_decode<16>(int2, sp, mp, r_k, q, batch, s);
+    case 1: return launch_decode<1>(int2, sp, r_k, batch, s);
+    case 2: return launch_decode<2>(int2, sp, r_k, batch, s);
+    case 4: return launch_decode<4>(int2, sp, r_k, batch, s);
+    case 8: return launch_decode<8>(int2, sp, r_k, batch, s);
+    case 16: return launch_decode<16>(int2, sp, r_k, batch, s);
   }
   return OSCAR_EUNSUPPORTED;
 }
@@ -984,8 +1035,8 @@ __global__ __launch_bounds__(256) void bf16_append_kernel(const uint16_t* __rest
 extern "C" size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int32_t max_seq_len) {
   using namespace oscar;
   if (check_shape(shape) != OSCAR_OK || batch < 1 || max_seq_len < 1) return 0;
-  return workspace_bytes(batch, shape->n_q_heads, shape->n_kv_heads,
-                         plan_splits(batch, shape->n_kv_heads, max_seq_len));
+  return workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads,
+                          plan_splits(batch, shape->n_kv_heads, max_seq_len)).total;
 }
 
 extern "C" int oscar_decode_attn(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
