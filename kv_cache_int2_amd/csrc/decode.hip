@@ -585,7 +585,7 @@ __device__ void window_unit(const SplitParams& p, int b, int h, int hq0, int n, 
 // the next tile's loads in flight while it computes the current one.
 // ---------------------------------------------------------------------------
 template <int G>
-__global__ __launch_bounds__(256, G <= 4 ? 2 : 1) void int2_split_kernel(SplitParams p) {
+__global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void int2_split_kernel(SplitParams p) {
   constexpr int NRG = (G + 3) / 4;                    // MFMA row groups of 4 heads
   constexpr int kTileBytes = 4 * NRG * 16 * 128;     // per-wave w-term tiles
   constexpr int kCombBytes = 4 * G * kD * 4 + 2 * 4 * G * 4;
@@ -649,30 +649,17 @@ __global__ __launch_bounds__(256, G <= 4 ? 2 : 1) void int2_split_kernel(SplitPa
 
   // The wave's tiles k = 0 .. ntw-1 are tiles wave + 4k of the split (at most
   // 4: a split holds at most 2048 tokens = 16 tiles).  One block-table load
-  // covers them all.  Two tiles are in flight at a time: the loads of tile k + 1
-  // are issued before tile k is computed.  Those loads are unconditional (a tile
-  // past the wave's last reads page 0 and is never computed), so no branch
-  // makes the compiler wait for them early.  One row group only: with two the
-  // registers of a second tile would cost the occupancy they buy.
+  // covers them all, so a tile's loads never wait on a table read.  A wave keeps
+  // one tile in registers: at ~122 VGPRs four waves share each SIMD, and the
+  // other waves' work hides a wave's load latency (measured faster than keeping
+  // two tiles per wave in flight at two waves per SIMD).
   const int ntw = wave < n_tiles ? (n_tiles - wave + 3) >> 2 : 0;
   const TileTable tab = load_table(p, btr, P0, P1, wave, 0);
-  auto pbase_of = [&](int k) { return P0 + 8 * (wave + 4 * k); };
-  if constexpr (NRG > 1) {
-    for (int k = 0; k < ntw; ++k) {
-      Tile ta;
-      load_tile(p, tab, k, h, pbase_of(k), t_end, lg, lr, ta);
-      compute_tile<G, NRG>(p, ta, pbase_of(k), t_end, lg, lr, qa, qsc, qsr, wt, st);
-    }
-  } else {
-    Tile ta, tb;
-    load_tile(p, tab, 0, h, pbase_of(0), t_end, lg, lr, ta);
-    for (int k = 0; k < ntw; k += 2) {
-      load_tile(p, tab, k + 1, h, pbase_of(k + 1), t_end, lg, lr, tb);
-      compute_tile<G, NRG>(p, ta, pbase_of(k), t_end, lg, lr, qa, qsc, qsr, wt, st);
-      if (k + 1 >= ntw) break;
-      load_tile(p, tab, k + 2, h, pbase_of(k + 2), t_end, lg, lr, ta);
-      compute_tile<G, NRG>(p, tb, pbase_of(k + 1), t_end, lg, lr, qa, qsc, qsr, wt, st);
-    }
+  for (int k = 0; k < ntw; ++k) {
+    const int pbase = P0 + 8 * (wave + 4 * k);
+    Tile ta;
+    load_tile(p, tab, k, h, pbase, t_end, lg, lr, ta);
+    compute_tile<G, NRG>(p, ta, pbase, t_end, lg, lr, qa, qsc, qsr, wt, st);
   }
 
   // ---- per-wave partial -> LDS -> workgroup partial ----
@@ -962,7 +949,8 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   if (int2 && shape->window > 0 && (!win_k || !win_v)) return OSCAR_EINVAL;
   if (!int2 && !kv_pool) return OSCAR_EINVAL;
   if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * kPage) return OSCAR_ENOSPACE;
-  const SplitPlan plan = plan_splits(batch, shape->n_kv_heads, max_seq_len);
+  const SplitPlan plan = plan_splits(batch, shape->n_kv_heads, shape->n_q_heads / shape->n_kv_heads, max_seq_len,
+                                     device_cu_count());
   const WorkspaceLayout wl = workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads, plan);
   if (workspace_bytes < wl.total) return OSCAR_ENOSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return OSCAR_EINVAL;
@@ -1036,7 +1024,8 @@ extern "C" size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t
   using namespace oscar;
   if (check_shape(shape) != OSCAR_OK || batch < 1 || max_seq_len < 1) return 0;
   return workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads,
-                          plan_splits(batch, shape->n_kv_heads, max_seq_len)).total;
+                          plan_splits(batch, shape->n_kv_heads, shape->n_q_heads / shape->n_kv_heads, max_seq_len,
+                                      device_cu_count())).total;
 }
 
 extern "C" int oscar_decode_attn(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,

@@ -1,6 +1,7 @@
-// Measurement helpers and status strings: a streaming copy kernel (HBM probe
-// and the known-size reference for HBM traffic counters) and opt-in event-pair
-// recording around the main kernel of each append / decode call.
+// Measurement helpers, the device's compute-unit count and status strings: a
+// streaming copy kernel (HBM probe and the known-size reference for HBM traffic
+// counters) and opt-in event-pair recording around the main kernel of each
+// append / decode call.
 #include <vector>
 
 #include "common.h"
@@ -23,6 +24,19 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src
 }
 
 }  // namespace
+
+int device_cu_count() {
+  // cached per device: an attribute query per decode call would be a needless
+  // runtime round trip
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
 
 void timing_record_begin(hipStream_t st, int kind, int* slot) {
   *slot = -1;
