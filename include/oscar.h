@@ -39,7 +39,8 @@
  *
  * Page block (one per page and KV head, 1152 bytes, 128-byte aligned within a
  * 128-byte aligned pool; pool = uint8 [n_pages][n_kv_heads][1152]):
- *   [   0,  512)  K codes: 16 token rows x 32 B; channel c at bit 2c of the row
+ *   [   0,  512)  K codes: 16 token rows x 32 B; channel c in row byte
+ *                 8 ((c >> 2) & 3) + (c >> 4), bits 2 (c & 3)
  *   [ 512, 1024)  V codes: 128 channel words (uint32, little endian); token slot
  *                 j of the page at bits 2j..2j+1
  *   [1024, 1152)  16 token records of 8 bytes, slot j at 1024 + 8j:

@@ -5,17 +5,24 @@
 // (recent tokens kept in bf16, history in INT2, paged storage).
 //
 // One workgroup = 4 waves = 64 tokens per iteration of one (KV head, K|V).
-// R (128 x 128 bf16) is staged once per workgroup in LDS.  Each wave rotates 16
-// tokens with v_mfma_f32_16x16x32_bf16: 8 output tiles x 4 k-steps.
-//  - keys use A = R, B = X^T: a lane ends with 32 channels of ONE token, so the
-//    per-token min/max needs 2 shuffles and the token-major K row is assembled
-//    from 4 lanes' bytes;
+// R (128 x 128 bf16) is staged once per workgroup in LDS.  Each wave rotates its
+// 16-token tile(s) with v_mfma_f32_16x16x32_bf16; every R tile read from LDS
+// feeds every token tile of the wave.  One tile per wave by default: at ~114
+// VGPRs four waves share each SIMD, which measured faster than two tiles per
+// wave (fewer LDS reads of R) at two waves per SIMD.
+//  - keys use A = R, B = X^T: a lane ends with channels 16m + 4g + i (m = 0..7,
+//    i = 0..3) of ONE token, exactly the 8-byte segment g of the token's K row,
+//    so it writes that segment itself;
 //  - values use A = X, B = R^T: a lane ends with 4 tokens x 8 channels, so the
-//    channel-major V words (16 slots x 2 bits) are assembled from 4 lanes and a
-//    whole aligned page is written with plain stores; a partial page falls back
-//    to per-token atomic and/or on the channel words.
+//    channel-major V words (16 slots x 2 bits) are OR-ed over the 4 lane groups
+//    with permlane swaps and a whole aligned page is written with plain stores;
+//    a partial page falls back to per-token atomic and/or on the channel words.
 // The k-slot -> input channel map (lane group g, step s, slot j -> 32g + 8s + j)
 // is the same for both operands, so the hardware's internal k order is moot.
+// Codes: t = (x' - z) / s is evaluated as x' * (1/s) - z * (1/s) (one FMA; the
+// reciprocal once per token); it differs from the quotient by a few ulp, so a
+// code can only differ next to a rounding boundary.  The scale itself is the
+// correctly rounded fp32 (max - min) / 3, as the definition has it.
 #include "common.h"
 
 namespace oscar {
@@ -39,17 +46,75 @@ struct AppendParams {
 };
 
 constexpr int kRowU4 = 17;  // LDS row stride of R in uint4 (16 + 1 pad: 272 B)
+#ifndef OSCAR_APPEND_TILES
+#define OSCAR_APPEND_TILES 1
+#endif
+constexpr int kAppendTiles = OSCAR_APPEND_TILES;  // 16-token tiles per wave and iteration
+constexpr int kAppendTokens = 4 * 16 * kAppendTiles;  // tokens per workgroup and iteration
 
 __device__ __forceinline__ f32x4 mfma(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t encode(float v, float z, float s) {
-  if (s == 0.f) return 0u;
-  float t = rintf((v - z) / s);
-  t = fminf(fmaxf(t, 0.f), 3.f);
-  return (uint32_t)t;
+// code = clamp(rint(t), 0, 3) with t = x * inv - zi
+__device__ __forceinline__ uint32_t encode(float v, float inv, float zi) {
+  const float t = __builtin_amdgcn_fmed3f(fmaf(v, inv, -zi), 0.f, 3.f);
+  return (uint32_t)__builtin_rintf(t);
+}
+
+// OR over the 4 lane groups (rows of 16 lanes) of a wave: every lane receives
+// the OR of its own and the 3 partner lanes 16, 32, 48 apart.
+__device__ __forceinline__ uint32_t or_rows(uint32_t d) {
+  auto a = __builtin_amdgcn_permlane16_swap(d, d, false, false);
+  d = a[0] | a[1];
+  auto b = __builtin_amdgcn_permlane32_swap(d, d, false, false);
+  return b[0] | b[1];
+}
+__device__ __forceinline__ float min_rows(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float max_rows(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row_min16(float x) {
+  x = fminf(x, dpp_f32<kDppSwap1>(x));
+  x = fminf(x, dpp_f32<kDppSwap2>(x));
+  x = fminf(x, dpp_f32<kDppHalfMirror>(x));
+  return fminf(x, dpp_f32<kDppMirror>(x));
+}
+
+// Scale and zero of a group from its min and max: s16 = fp16((max - min) / 3),
+// z16 = fp16(min); codes are taken against the stored (fp16) values.  The
+// division by 3 is q0 = d * fl(1/3) corrected once with the exact remainder
+// d - 3 q0 (an FMA), which gives the correctly rounded quotient; 1/s is the
+// hardware reciprocal (a code can only move next to a rounding boundary).
+struct Quant {
+  uint32_t sz;  // s16 | z16 << 16
+  float inv, zi;
+};
+__device__ __forceinline__ Quant quant_params(float mn, float mx) {
+  const float d = mx - mn;
+  const float q0 = d * 0.333333343f;
+  const float sigma = fmaf(fmaf(-3.0f, q0, d), 0.333333343f, q0);
+  const uint16_t sb = f2h_bits(sigma), zb = f2h_bits(mn);
+  const float sc = h2f(sb), z = h2f(zb);
+  Quant q;
+  q.sz = (uint32_t)sb | ((uint32_t)zb << 16);
+  q.inv = sc > 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;  // a zero scale codes every channel 0
+  q.zi = z * q.inv;
+  return q;
+}
+
+template <int LANE>  // value of lane LANE of each quad, on all 4 lanes of the quad
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, LANE * 0x55, 0xf, 0xf, true);
 }
 
 // Resolve token `tok`: returns its block base (or nullptr if it must be skipped)
@@ -78,152 +143,148 @@ __device__ __forceinline__ TokInfo resolve(const AppendParams& p, int64_t tok, i
 }
 
 template <int KIND>
-__device__ __forceinline__ void process_tile(const AppendParams& p, const uint4* r_lds, int64_t t0,
-                                             int h, int lane) {
+__device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4* r_lds, int64_t t0, int h,
+                                              int lane) {
+  constexpr int NT = kAppendTiles;
   const int g = lane >> 4, r = lane & 15;
-  const int64_t tok = t0 + r;
-  TokInfo ti = resolve(p, tok, h);
-  const bool valid = tok < p.n_tokens;
 
-  // X operand: token t0 + r, input channels 32g .. 32g + 31
-  uint4 xv[4];
-  const uint4* xp = reinterpret_cast<const uint4*>(p.x[KIND] + ((valid ? tok : 0) * p.hkv + h) * kD + 32 * g);
+  // X operand of tile j: token t0 + 16 j + r, input channels 32g .. 32g + 31
+  uint4 xv[NT][4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) xv[s] = valid ? xp[s] : make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < NT; ++j) {
+    const int64_t tok = t0 + 16 * j + r;
+    const bool valid = tok < p.n_tokens;
+    const uint4* xp = reinterpret_cast<const uint4*>(p.x[KIND] + ((valid ? tok : 0) * p.hkv + h) * kD + 32 * g);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) xv[j][s] = valid ? xp[s] : make_uint4(0, 0, 0, 0);
+  }
 
-  f32x4 acc[8];
+  f32x4 acc[NT][8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
-    acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[j][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      uint4 rv = r_lds[(16 * m + r) * kRowU4 + 4 * g + s];
-      acc[m] = KIND == 0 ? mfma(rv, xv[s], acc[m]) : mfma(xv[s], rv, acc[m]);
+      const uint4 rv = r_lds[(16 * m + r) * kRowU4 + 4 * g + s];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j][m] = KIND == 0 ? mfma(rv, xv[j][s], acc[j][m]) : mfma(xv[j][s], rv, acc[j][m]);
     }
   }
 
-  // raw bf16 copy into the window ring (same for K and V)
-  if (ti.blk && ti.in_win) {
-    uint4* wp = reinterpret_cast<uint4*>(p.win[KIND] + (((int64_t)ti.b * p.window + ti.pos % p.window) * p.hkv + h) * kD + 32 * g);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) wp[s] = xv[s];
-  }
+  for (int j = 0; j < NT; ++j) {
+    const int64_t tj = t0 + 16 * j;
+    if (tj >= p.n_tokens) break;  // uniform: the wave's tokens are contiguous
+    TokInfo ti = resolve(p, tj + r, h);
 
-  if (KIND == 0) {
-    // acc[m][i] = x'[token t0 + r][channel 16m + 4g + i]
-    float mn = acc[0][0], mx = acc[0][0];
+    // raw bf16 copy into the window ring (same for K and V)
+    if (ti.blk && ti.in_win) {
+      uint4* wp = reinterpret_cast<uint4*>(p.win[KIND] + (((int64_t)ti.b * p.window + ti.pos % p.window) * p.hkv + h) * kD + 32 * g);
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        mn = fminf(mn, acc[m][i]);
-        mx = fmaxf(mx, acc[m][i]);
-      }
-    mn = fminf(mn, __shfl_xor(mn, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mn = fminf(mn, __shfl_xor(mn, 32));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float sigma = (mx - mn) / 3.0f;
-    const uint16_t sb = f2h_bits(sigma), zb = f2h_bits(mn);
-    const float sc = h2f(sb), z = h2f(zb);
-    uint32_t dw[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      uint32_t byte = encode(acc[m][0], z, sc) | (encode(acc[m][1], z, sc) << 2) |
-                      (encode(acc[m][2], z, sc) << 4) | (encode(acc[m][3], z, sc) << 6);
-      uint32_t d = byte << (8 * g);
-      d |= __shfl_xor(d, 16);
-      d |= __shfl_xor(d, 32);
-      dw[m] = d;
+      for (int s = 0; s < 4; ++s) wp[s] = xv[j][s];
     }
-    if (ti.blk) {
-      uint2 out = make_uint2(dw[0], dw[1]);
-      if (g == 1) out = make_uint2(dw[2], dw[3]);
-      if (g == 2) out = make_uint2(dw[4], dw[5]);
-      if (g == 3) out = make_uint2(dw[6], dw[7]);
-      *reinterpret_cast<uint2*>(ti.blk + kKCodes + 32 * ti.slot + 8 * g) = out;
-      if (g == 0) *reinterpret_cast<uint32_t*>(ti.blk + kMeta + 8 * ti.slot) = (uint32_t)sb | ((uint32_t)zb << 16);
-    }
-  } else {
-    // acc[m][i] = x'[token t0 + 4g + i][channel 16m + r]
-    float sc[4], z[4];
-    uint16_t sbits[4], zbits[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mn = acc[0][i], mx = acc[0][i];
-#pragma unroll
-      for (int m = 1; m < 8; ++m) {
-        mn = fminf(mn, acc[m][i]);
-        mx = fmaxf(mx, acc[m][i]);
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        mn = fminf(mn, __shfl_xor(mn, o));
-        mx = fmaxf(mx, __shfl_xor(mx, o));
-      }
-      const float sigma = (mx - mn) / 3.0f;
-      sbits[i] = f2h_bits(sigma);
-      zbits[i] = f2h_bits(mn);
-      sc[i] = h2f(sbits[i]);
-      z[i] = h2f(zbits[i]);
-    }
-    uint32_t code[8][4];
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) code[m][i] = encode(acc[m][i], z[i], sc[i]);
 
-    // fast path: the wave's 16 tokens are slots 0..15 of one page, in order
-    const int b0 = __shfl(ti.b, 0), pos0 = __shfl(ti.pos, 0);
-    uint8_t* blk0 = reinterpret_cast<uint8_t*>(__shfl(reinterpret_cast<uintptr_t>(ti.blk), 0));
-    const bool mine = ti.blk != nullptr && ti.b == b0 && ti.pos == pos0 + r && (pos0 & 15) == 0;
-    const bool full = __all(mine);
-    // per-token info of the 4 tokens this lane holds codes for
-    uint8_t* tblk[4];
-    int tslot[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tblk[i] = reinterpret_cast<uint8_t*>(__shfl(reinterpret_cast<uintptr_t>(ti.blk), 4 * g + i));
-      tslot[i] = __shfl(ti.slot, 4 * g + i);
-    }
-    if (full) {
-      uint32_t w[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        uint32_t d = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) d |= code[m][i] << (2 * (4 * g + i));
-        d |= __shfl_xor(d, 16);
-        d |= __shfl_xor(d, 32);
-        w[m] = d;
-      }
-      uint32_t* vw = reinterpret_cast<uint32_t*>(blk0 + kVCodes);
+    if (KIND == 0) {
+      // acc[j][m][i] = x'[token tj + r][channel 16m + 4g + i]: row segment g
+      float mn = acc[j][0][0], mx = acc[j][0][0];
 #pragma unroll
       for (int m = 0; m < 8; ++m)
-        if ((m >> 1) == g) vw[16 * m + r] = w[m];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          mn = fminf(mn, acc[j][m][i]);
+          mx = fmaxf(mx, acc[j][m][i]);
+        }
+      const Quant q = quant_params(min_rows(mn), max_rows(mx));
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[m >> 2] |= encode(acc[j][m][i], q.inv, q.zi) << (8 * (m & 3) + 2 * i);
+      if (ti.blk) {
+        *reinterpret_cast<uint2*>(ti.blk + kKCodes + 32 * ti.slot + 8 * g) = make_uint2(w[0], w[1]);
+        if (g == 0) *reinterpret_cast<uint32_t*>(ti.blk + kMeta + 8 * ti.slot) = q.sz;
+      }
     } else {
+      // acc[j][m][i] = x'[token tj + 4g + i][channel 16m + r]
+      float mn[4], mx[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (!tblk[i]) continue;
-        uint32_t* vw = reinterpret_cast<uint32_t*>(tblk[i] + kVCodes);
-        const uint32_t clr = ~(3u << (2 * tslot[i]));
+        mn[i] = acc[j][0][i];
+        mx[i] = acc[j][0][i];
+#pragma unroll
+        for (int m = 1; m < 8; ++m) {
+          mn[i] = fminf(mn[i], acc[j][m][i]);
+          mx[i] = fmaxf(mx[i], acc[j][m][i]);
+        }
+        mn[i] = row_min16(mn[i]);
+        mx[i] = row_max16(mx[i]);
+      }
+      // lane r of each quad takes token 4g + (r & 3); the quad then shares them
+      const int mi = r & 3;
+      const float mn_l = mi == 0 ? mn[0] : mi == 1 ? mn[1] : mi == 2 ? mn[2] : mn[3];
+      const float mx_l = mi == 0 ? mx[0] : mi == 1 ? mx[1] : mi == 2 ? mx[2] : mx[3];
+      const Quant ql = quant_params(mn_l, mx_l);
+      Quant q[4];
+      q[0] = Quant{quad_bcast<0>(ql.sz), __uint_as_float(quad_bcast<0>(__float_as_uint(ql.inv))),
+                   __uint_as_float(quad_bcast<0>(__float_as_uint(ql.zi)))};
+      q[1] = Quant{quad_bcast<1>(ql.sz), __uint_as_float(quad_bcast<1>(__float_as_uint(ql.inv))),
+                   __uint_as_float(quad_bcast<1>(__float_as_uint(ql.zi)))};
+      q[2] = Quant{quad_bcast<2>(ql.sz), __uint_as_float(quad_bcast<2>(__float_as_uint(ql.inv))),
+                   __uint_as_float(quad_bcast<2>(__float_as_uint(ql.zi)))};
+      q[3] = Quant{quad_bcast<3>(ql.sz), __uint_as_float(quad_bcast<3>(__float_as_uint(ql.inv))),
+                   __uint_as_float(quad_bcast<3>(__float_as_uint(ql.zi)))};
+      // fast path: the tile's 16 tokens are slots 0..15 of one page, in order
+      const int b0 = __builtin_amdgcn_readfirstlane(ti.b), pos0 = __builtin_amdgcn_readfirstlane(ti.pos);
+      const uintptr_t bp = reinterpret_cast<uintptr_t>(ti.blk);
+      uint8_t* blk0 = reinterpret_cast<uint8_t*>(
+          ((uintptr_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(bp >> 32)) << 32) |
+          (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bp));
+      const bool mine = ti.blk != nullptr && ti.b == b0 && ti.pos == pos0 + r && (pos0 & 15) == 0;
+      if (__all(mine)) {
+        uint32_t w[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          atomicAnd(&vw[16 * m + r], clr);
-          atomicOr(&vw[16 * m + r], code[m][i] << (2 * tslot[i]));
+          uint32_t d = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d |= encode(acc[j][m][i], q[i].inv, q[i].zi) << (2 * (4 * g + i));
+          w[m] = or_rows(d);
+        }
+        uint32_t* vw = reinterpret_cast<uint32_t*>(blk0 + kVCodes);
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+          if ((m >> 1) == g) vw[16 * m + r] = w[m];
+        // token 4g + i is slot 4g + i; lane r == i stores its scale / zero
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (r == i) *reinterpret_cast<uint32_t*>(blk0 + kMeta + 8 * (4 * g + i) + 4) = q[i].sz;
+      } else {
+        // per-token info of the 4 tokens this lane holds codes for
+        uint8_t* tblk[4];
+        int tslot[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          tblk[i] = reinterpret_cast<uint8_t*>(__shfl(bp, 4 * g + i));
+          tslot[i] = __shfl(ti.slot, 4 * g + i);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (!tblk[i]) continue;
+          uint32_t* vw = reinterpret_cast<uint32_t*>(tblk[i] + kVCodes);
+          const uint32_t clr = ~(3u << (2 * tslot[i]));
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            atomicAnd(&vw[16 * m + r], clr);
+            atomicOr(&vw[16 * m + r], encode(acc[j][m][i], q[i].inv, q[i].zi) << (2 * tslot[i]));
+          }
+          if (r == i) *reinterpret_cast<uint32_t*>(tblk[i] + kMeta + 8 * tslot[i] + 4) = q[i].sz;
         }
       }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (!tblk[i]) continue;
-      if (r == i)
-        *reinterpret_cast<uint32_t*>(tblk[i] + kMeta + 8 * tslot[i] + 4) = (uint32_t)sbits[i] | ((uint32_t)zbits[i] << 16);
     }
   }
 }
 
-__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+__global__ __launch_bounds__(256, 4) void append_kernel(AppendParams p) {
   __shared__ uint4 r_lds[128 * kRowU4];
   const int h = blockIdx.y;
   const int kind = blockIdx.z;
@@ -232,12 +293,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int it = 0; it < p.tiles_per_wg; ++it) {
-    const int64_t t0 = ((int64_t)blockIdx.x * p.tiles_per_wg + it) * 64 + wave * 16;
+    const int64_t t0 = ((int64_t)blockIdx.x * p.tiles_per_wg + it) * kAppendTokens + wave * 16 * kAppendTiles;
     if (t0 >= p.n_tokens) break;
     if (kind == 0)
-      process_tile<0>(p, r_lds, t0, h, lane);
+      process_tiles<0>(p, r_lds, t0, h, lane);
     else
-      process_tile<1>(p, r_lds, t0, h, lane);
+      process_tiles<1>(p, r_lds, t0, h, lane);
   }
 }
 
@@ -281,8 +342,8 @@ extern "C" int oscar_quantize_append(const oscar_shape* shape, const uint16_t* r
   p.max_pages = max_pages_per_seq;
   p.hkv = shape->n_kv_heads;
   p.window = shape->window;
-  const int64_t tiles = (n_tokens + 63) / 64;
-  p.tiles_per_wg = tiles >= 1024 ? 8 : (tiles >= 256 ? 4 : 1);
+  const int64_t tiles = (n_tokens + kAppendTokens - 1) / kAppendTokens;  // workgroup iterations
+  p.tiles_per_wg = tiles >= 512 ? 4 : (tiles >= 128 ? 2 : 1);
   dim3 grid((unsigned)((tiles + p.tiles_per_wg - 1) / p.tiles_per_wg), (unsigned)p.hkv, 2);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int slot = -1;

@@ -62,11 +62,14 @@ __device__ __forceinline__ f32x4 mfma_f8_f4(const i32x8& a, const i32x8& b, f32x
 // k index of byte e (0..31) of an 8-bit operand lane in lane group g
 __device__ __forceinline__ int k_of_fp8(int g, int e) { return e < 16 ? 16 * g + e : 48 + 16 * g + e; }
 
-// channel of element k of the K-code operand: lane group g = k / 32 holds the
-// row bytes 8g .. 8g + 7 as dwords w0, w1 and presents lo(w0), hi(w0), lo(w1), hi(w1)
+// channel of element k of the K-code operand.  Lane group g = k / 32 holds the
+// row bytes 8g .. 8g + 7 (row segment g: byte m holds channels 16m + 4g + i at
+// bits 2i) as dwords w0, w1 and presents lo(w0), hi(w0), lo(w1), hi(w1), where
+// lo keeps bits 2i of each nibble (i even) and hi the bits above (i odd).
 __device__ __forceinline__ int k_channel(int k) {
-  const int g = k >> 5, e = k & 31, d = e >> 3, m = e & 7;
-  return 32 * g + 16 * (d >> 1) + 2 * m + (d & 1);
+  const int g = k >> 5, e = k & 31, d = e >> 3, nib = e & 7;
+  const int m = 4 * (d >> 1) + (nib >> 1), i = 2 * (nib & 1) + (d & 1);
+  return 16 * m + 4 * g + i;
 }
 
 // A sequence length is clamped to what its block-table row can hold.

@@ -44,7 +44,8 @@ import numpy as np
 
 # ---------------------------------------------------------------------------
 # Page-block layout (per page, per KV head, 1152 bytes)
-#   [   0,  512)  K codes: 16 token rows x 32 B; channel c of a row at bit 2c
+#   [   0,  512)  K codes: 16 token rows x 32 B; channel c of a row in byte
+#                 8 ((c >> 2) & 3) + (c >> 4), bits 2 (c & 3) (see k_row_byte)
 #   [ 512, 1024)  V codes: 128 channel words x 4 B; token slot j at bit 2j
 #   [1024, 1152)  16 token records of 8 bytes: fp16 K scale, K zero, V scale, V zero
 # Pool = uint8 [n_pages][Hkv][1152].  Window ring = bf16 [B][W][Hkv][d], slot pos % W.
@@ -228,16 +229,29 @@ def quantize(xr: np.ndarray):
     return c, s, z, dict(sigma=sigma, m=m, t=t)
 
 
+def k_row_byte(c):
+    """Byte of a K row holding channel c (its bits: 2 (c mod 4) .. +1).  The row is
+    four 8-byte segments; segment s holds channels 16 m + 4 s + i (m = 0..7 is the
+    byte within the segment, i = 0..3 the 2-bit field within the byte)."""
+    c = np.asarray(c)
+    return 8 * ((c >> 2) & 3) + (c >> 4)
+
+
 def pack_k_row(codes: np.ndarray) -> np.ndarray:
-    """[..., 128] codes -> [..., 32] bytes; channel c at bit 2c of the row."""
-    c = np.asarray(codes, dtype=np.uint8).reshape(*np.shape(codes)[:-1], 32, 4)
-    return (c[..., 0] | (c[..., 1] << 2) | (c[..., 2] << 4) | (c[..., 3] << 6)).astype(np.uint8)
+    """[..., 128] codes -> [..., 32] bytes in the K-row layout of ``k_row_byte``."""
+    c = np.asarray(codes, dtype=np.uint8)
+    lead = c.shape[:-1]
+    out = np.zeros(lead + (32,), dtype=np.uint8)
+    for ch in range(128):
+        out[..., k_row_byte(ch)] |= (c[..., ch] << (2 * (ch & 3))).astype(np.uint8)
+    return out
 
 
 def unpack_k_rows(rows: np.ndarray) -> np.ndarray:
-    """[..., 32] bytes -> [..., 128] codes."""
-    r = np.asarray(rows, dtype=np.uint8)[..., None]
-    return ((r >> (2 * np.arange(4, dtype=np.uint8))) & 3).reshape(*r.shape[:-2], 128).astype(np.int64)
+    """[..., 32] bytes -> [..., 128] codes (inverse of ``pack_k_row``)."""
+    r = np.asarray(rows, dtype=np.uint8)
+    ch = np.arange(128)
+    return ((r[..., k_row_byte(ch)] >> (2 * (ch & 3)).astype(np.uint8)) & 3).astype(np.int64)
 
 
 def v_words(block: np.ndarray) -> np.ndarray:

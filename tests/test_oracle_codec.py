@@ -98,10 +98,11 @@ def test_bitrev_only_permutes_codes_at_full_group(rng):
 
 def test_pack_bit_positions_by_hand():
     c = np.zeros(128, dtype=np.int64)
-    c[5] = 3                      # byte 1, bits 2-3
-    c[127] = 2                    # byte 31, bits 6-7
+    c[5] = 3                      # segment 1 (channels 4..7 of each 16), byte 0 -> row byte 8, bits 2-3
+    c[127] = 2                    # segment 3, byte 7 -> row byte 31, bits 6-7
+    c[16] = 1                     # segment 0, byte 1 -> row byte 1, bits 0-1
     row = ref.pack_k_row(c)
-    assert row[1] == 0x0C and row[31] == 0x80 and row.sum() == 0x0C + 0x80
+    assert row[8] == 0x0C and row[31] == 0x80 and row[1] == 0x01 and row.sum() == 0x0C + 0x80 + 0x01
     blk = np.zeros(1152, dtype=np.uint8)
     words = np.zeros(128, dtype="<u4")
     words[7] = 2 << 6             # channel 7, slot 3, code 2
