@@ -113,7 +113,7 @@ def main():
     pools = [torch.zeros((n_pages, HKV, K.BLOCK_BYTES), dtype=torch.uint8, device=dev) for _ in range(L)]
     wks = [torch.zeros((B, W, HKV, 128), dtype=torch.int16, device=dev) for _ in range(L)]
     wvs = [torch.zeros((B, W, HKV, 128), dtype=torch.int16, device=dev) for _ in range(L)]
-    kvp = [] if args.no_bf16 else [torch.zeros((n_pages, HKV, 2, 16, 128), dtype=torch.int16, device=dev)
+    kvp = [] if args.no_bf16 else [torch.zeros((n_pages, HKV, K.BF16_BLOCK_ELEMS), dtype=torch.int16, device=dev)
                                    for _ in range(L)]
     cur_k = np.empty((B, HKV, 128), np.uint16)
     cur_v = np.empty((B, HKV, 128), np.uint16)

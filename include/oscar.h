@@ -168,7 +168,9 @@ int oscar_decode_attn(const oscar_shape* shape, const uint16_t* r_k, const uint1
  * bf16-KV comparator (not part of the method; the baseline the INT2 decode is
  * measured against, P2 «OSCAR има значение…» and P3 «Resultados e Métricas de
  * Desempenho» quote decode speed against a BF16 cache).  Paged bf16 pool:
- * uint16 [n_pages][n_kv_heads][2 (K, V)][16][128], same block table semantics.
+ * uint16 [n_pages][n_kv_heads][4096] (8 KiB per page and KV head): the K rows
+ * [16 slots][128] followed by V transposed [128][16 slots] (V of slot j,
+ * channel c at element 2048 + 16 c + j), same block table semantics.
  * oscar_bf16_append scatters k_new/v_new [n_tokens][n_kv_heads][128] into it;
  * oscar_bf16_decode_attn is plain softmax attention over all seq_lens[b]
  * positions, fp32 output [batch][n_q_heads][128], same workspace rule.

@@ -19,10 +19,11 @@ __all__ = [
     "OscarError", "OscarShape", "make_shape", "oscar_calibrate", "oscar_quantize_append",
     "oscar_decode_workspace_bytes", "oscar_decode_attn", "oscar_bf16_append",
     "oscar_bf16_decode_attn", "oscar_hbm_copy", "oscar_timing_begin", "oscar_timing_end",
-    "oscar_strerror", "BLOCK_BYTES", "PAGE_SIZE", "HEAD_DIM",
+    "oscar_strerror", "BLOCK_BYTES", "BF16_BLOCK_ELEMS", "PAGE_SIZE", "HEAD_DIM",
 ]
 
 BLOCK_BYTES = 1152
+BF16_BLOCK_ELEMS = 4096  # bf16 comparator pool: K [16][128] then V^T [128][16] per (page, KV head)
 PAGE_SIZE = 16
 HEAD_DIM = 128
 

@@ -28,7 +28,6 @@
 namespace oscar {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct AppendParams {
@@ -61,33 +60,6 @@ __device__ __forceinline__ f32x4 mfma(uint4 a, uint4 b, f32x4 c) {
 __device__ __forceinline__ uint32_t encode(float v, float inv, float zi) {
   const float t = __builtin_amdgcn_fmed3f(fmaf(v, inv, -zi), 0.f, 3.f);
   return (uint32_t)__builtin_rintf(t);
-}
-
-// OR over the 4 lane groups (rows of 16 lanes) of a wave: every lane receives
-// the OR of its own and the 3 partner lanes 16, 32, 48 apart.
-__device__ __forceinline__ uint32_t or_rows(uint32_t d) {
-  auto a = __builtin_amdgcn_permlane16_swap(d, d, false, false);
-  d = a[0] | a[1];
-  auto b = __builtin_amdgcn_permlane32_swap(d, d, false, false);
-  return b[0] | b[1];
-}
-__device__ __forceinline__ float min_rows(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float max_rows(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float row_min16(float x) {
-  x = fminf(x, dpp_f32<kDppSwap1>(x));
-  x = fminf(x, dpp_f32<kDppSwap2>(x));
-  x = fminf(x, dpp_f32<kDppHalfMirror>(x));
-  return fminf(x, dpp_f32<kDppMirror>(x));
 }
 
 // Scale and zero of a group from its min and max: s16 = fp16((max - min) / 3),

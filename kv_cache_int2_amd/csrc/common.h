@@ -99,6 +99,10 @@ namespace oscar {
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {  // finite x: round to nearest even
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
 
 __device__ __forceinline__ float h2f(uint16_t b) {
   _Float16 h = __builtin_bit_cast(_Float16, b);
@@ -136,6 +140,36 @@ __device__ __forceinline__ float row_sum16(float x) {
   x += dpp_f32<kDppHalfMirror>(x);
   return x + dpp_f32<kDppMirror>(x);
 }
+
+// OR / min / max over the 4 rows of 16 lanes of a wave (v_permlane16_swap and
+// v_permlane32_swap exchange whole rows): every lane receives the combination
+// of its own and the 3 partner lanes 16, 32 and 48 apart.
+__device__ __forceinline__ uint32_t or_rows(uint32_t d) {
+  auto a = __builtin_amdgcn_permlane16_swap(d, d, false, false);
+  d = a[0] | a[1];
+  auto b = __builtin_amdgcn_permlane32_swap(d, d, false, false);
+  return b[0] | b[1];
+}
+__device__ __forceinline__ float min_rows(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float max_rows(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row_min16(float x) {
+  x = fminf(x, dpp_f32<kDppSwap1>(x));
+  x = fminf(x, dpp_f32<kDppSwap2>(x));
+  x = fminf(x, dpp_f32<kDppHalfMirror>(x));
+  return fminf(x, dpp_f32<kDppMirror>(x));
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 }  // namespace oscar
 #endif

@@ -690,114 +690,177 @@ __global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void int2_split_kernel(SplitPa
 }
 
 // ---------------------------------------------------------------------------
-// bf16 comparator split: plain attention over bf16 pages, all n positions.
+// bf16 comparator split: plain attention over bf16 pages, all n positions, on
+// the matrix cores (v_mfma_f32_16x16x32_bf16).  Pool block per (page, KV head):
+// K rows [16][128], then V transposed [128][16].  A tile is 32 tokens (2 pages).
+//   scores: A = K (rows = 16 tokens), B = q^T (columns = query heads) -> lane
+//           (g, r) holds tokens 4g .. 4g + 3 of head r;
+//   P V:    A = p^T (rows = (head, hi|lo), k = 32 tokens), B = V (k = tokens,
+//           columns = 16 channels) -> lane (g, r) holds channel 16c + r of rows
+//           4g .. 4g + 3.
+// The softmax weights go through a per-wave LDS tile as two bf16 rows each
+// (p = hi + lo, about 16 significant bits); q is bf16 already, so the scores
+// are exact products accumulated in fp32.
 // ---------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(256) void bf16_split_kernel(SplitParams p) {
+  constexpr int NRG = (2 * G + 15) / 16;  // P V row groups: 8 heads x (hi, lo) rows each
   const int b = blockIdx.z, h = blockIdx.y, sp = blockIdx.x;
   const int n = seq_len_of(p, b);
   const int t_begin = sp * p.split;
   if (t_begin >= n) return;
   const int t_end = min(t_begin + p.split, n);
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r = lane & 15;
 
-  __shared__ float qs[G][kD];
-  __shared__ float pb[4][16][G];
+  __shared__ __align__(16) uint16_t pt[4][NRG][16][40];  // per wave: p^T rows x 32 tokens (bf16), padded rows
+  __shared__ float alph[4][16];
   __shared__ float cm[4 * G], cl[4 * G];
   __shared__ float cacc[4 * G * kD];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < G * kD; e += 256)
-    qs[e / kD][e % kD] = bf16_to_f32(p.q[((int64_t)b * p.hq + h * G) * kD + e]);
-  __syncthreads();
+  for (int e = tid; e < 4 * NRG * 16 * 40; e += 256) (&pt[0][0][0][0])[e] = 0;  // rows of absent heads stay 0
+  if (tid < 64) (&alph[0][0])[tid] = 1.f;
 
-  const int tq = lane & 15, quarter = lane >> 4;
-  float m_run[G], l_run[G], acc0[G], acc1[G];
+  // B operand of the scores: column r = query head r, k-slots 8g .. 8g + 7 of each 32-dim chunk
+  uint4 qb[4];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m_run[g] = kNegInf;
-    l_run[g] = 0.f;
-    acc0[g] = 0.f;
-    acc1[g] = 0.f;
+  for (int s = 0; s < 4; ++s)
+    qb[s] = r < G ? *reinterpret_cast<const uint4*>(p.q + ((int64_t)b * p.hq + h * G + r) * kD + 32 * s + 8 * g)
+                  : make_uint4(0, 0, 0, 0);
+
+  float m_run = kNegInf, l_part = 0.f;  // head r
+  f32x4 acc[NRG][8];
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[rg][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // block-table entries of the wave's tiles (tile k of the wave = tile wave + 4k,
+  // pages P0 + 2 (wave + 4k) + {0, 1}): lane 2k + pp, at most 32 tiles (2048 tokens / 4 waves)
+  const int P0 = t_begin >> 4, P1 = (t_end - 1) >> 4;
+  const int n_tiles = (P1 - P0 + 2) >> 1;
+  const int ntw = wave < n_tiles ? (n_tiles - wave + 3) >> 2 : 0;
+  const int* btr = p.block_table + (int64_t)b * p.max_pages;
+  int ent;
+  {
+    const int pg = P0 + 2 * (wave + 4 * (lane >> 1)) + (lane & 1);
+    ent = pg <= P1 ? btr[pg] : -1;
+    ent = (ent >= 0 && ent < p.n_pages) ? ent : -1;
   }
-  const int first_page = t_begin >> 4, last_page = (t_end - 1) >> 4;
-  for (int pg = first_page + wave; pg <= last_page; pg += 4) {
-    const int page = p.block_table[(int64_t)b * p.max_pages + pg];
-    if (page < 0 || page >= p.n_pages) continue;
-    const uint16_t* kb = p.kv_pool + ((int64_t)page * p.hkv + h) * (2 * kPage * kD);
-    const uint16_t* vb = kb + kPage * kD;
-    const int tok = pg * 16 + tq;
-    const bool valid = tok >= t_begin && tok < t_end;
-    const uint4* kr = reinterpret_cast<const uint4*>(kb + tq * kD + 32 * quarter);
-    uint4 k4[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) k4[s] = kr[s];
-    float dot[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) dot[g] = 0.f;
+  const uint64_t live = __ballot(ent >= 0);
+  __syncthreads();  // pt, alph initialised
+
+  for (int k = 0; k < ntw; ++k) {
+    const int pbase = P0 + 2 * (wave + 4 * k);
+    const int ea = __builtin_amdgcn_readlane(ent, 2 * k), eb = __builtin_amdgcn_readlane(ent, 2 * k + 1);
+    const int pg0 = ea < 0 ? 0 : ea, pg1 = eb < 0 ? 0 : eb;
+    const uint32_t ok = (uint32_t)(live >> (2 * k)) & 3u;
+    const uint16_t* blk0 = p.kv_pool + ((int64_t)pg0 * p.hkv + h) * (2 * kPage * kD);
+    const uint16_t* blk1 = p.kv_pool + ((int64_t)pg1 * p.hkv + h) * (2 * kPage * kD);
+    uint4 kk[2][4], vv[8];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint32_t wv[4] = {k4[s].x, k4[s].y, k4[s].z, k4[s].w};
+      kk[0][s] = *reinterpret_cast<const uint4*>(blk0 + r * kD + 32 * s + 8 * g);
+      kk[1][s] = *reinterpret_cast<const uint4*>(blk1 + r * kD + 32 * s + 8 * g);
+    }
+    const uint16_t* vblk = (g >> 1) ? blk1 : blk0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float lo = bf16lo(wv[u]), hi = bf16hi(wv[u]);
-        const int c = 32 * quarter + 8 * s + 2 * u;
+    for (int c = 0; c < 8; ++c)
+      vv[c] = *reinterpret_cast<const uint4*>(vblk + kPage * kD + (16 * c + r) * kPage + 8 * (g & 1));
+
+    // ---- scores and online softmax of head r ----
+    float lg[2][4];
+    float mx = kNegInf;
 #pragma unroll
-        for (int g = 0; g < G; ++g) dot[g] = fmaf(lo, qs[g][c], fmaf(hi, qs[g][c + 1], dot[g]));
+    for (int pp = 0; pp < 2; ++pp) {
+      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk[pp][s]),
+                                                     __builtin_bit_cast(bf16x8, qb[s]), sc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = (pbase + pp) * 16 + 4 * g + i;
+        const bool valid = r < G && ((ok >> pp) & 1u) && tok < t_end;
+        const float v = pin(sc[i] * p.scale_log2);
+        lg[pp][i] = valid ? v : kNegInf;
+        mx = fmaxf(mx, lg[pp][i]);
       }
     }
-    float alpha[G], pv[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float d = dot[g] + __shfl_xor(dot[g], 16);
-      d += __shfl_xor(d, 32);
-      float lg = valid ? d * p.scale_log2 : kNegInf;
-      float mx = lg;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      const float m_new = fmaxf(m_run[g], mx);
-      alpha[g] = exp2f(m_run[g] - m_new);
-      pv[g] = valid ? exp2f(lg - m_new) : 0.f;
-      float ps = pv[g];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) ps += __shfl_xor(ps, o);
-      l_run[g] = l_run[g] * alpha[g] + ps;
-      m_run[g] = m_new;
+    mx = max_rows(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const bool grow = __any(m_new > m_run);
+    if (grow) {
+      const float alpha = m_new == kNegInf ? 1.f : exp2f(m_run - m_new);
+      l_part *= alpha;
+      if (g == 0) alph[wave][r] = alpha;
+      m_run = m_new;
     }
-    if (quarter == 0) {
+    const float m_safe = m_run == kNegInf ? 0.f : m_run;
 #pragma unroll
-      for (int g = 0; g < G; ++g) pb[wave][tq][g] = pv[g];
+    for (int pp = 0; pp < 2; ++pp) {
+      uint32_t hw[2], lw[2];
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const float p0 = exp2f(lg[pp][i] - m_safe), p1 = exp2f(lg[pp][i + 1] - m_safe);
+        l_part += p0 + p1;
+        const uint32_t h0 = bf16_rne_bits(p0), h1 = bf16_rne_bits(p1);
+        const uint32_t l0 = bf16_rne_bits(p0 - bf16_to_f32(h0)), l1 = bf16_rne_bits(p1 - bf16_to_f32(h1));
+        hw[i >> 1] = h0 | (h1 << 16);
+        lw[i >> 1] = l0 | (l1 << 16);
+      }
+      if (r < G) {
+        uint16_t* row = &pt[wave][r >> 3][2 * (r & 7)][16 * pp + 4 * g];
+        *reinterpret_cast<uint2*>(row) = make_uint2(hw[0], hw[1]);
+        *reinterpret_cast<uint2*>(row + 40) = make_uint2(lw[0], lw[1]);
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- P V ----
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      acc0[g] *= alpha[g];
-      acc1[g] *= alpha[g];
-    }
-    const int tcount = min(16, t_end - pg * 16);
-    for (int t = 0; t < tcount; ++t) {
-      if (pg * 16 + t < t_begin) continue;
-      const uint32_t v2 = reinterpret_cast<const uint32_t*>(vb + t * kD)[lane];
-      const float v0 = bf16lo(v2), v1 = bf16hi(v2);
+    for (int rg = 0; rg < NRG; ++rg) {
+      if (grow) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float pt = pb[wave][t][g];
-        acc0[g] = fmaf(pt, v0, acc0[g]);
-        acc1[g] = fmaf(pt, v1, acc1[g]);
+        for (int i = 0; i < 4; ++i) {
+          const float a = alph[wave][(8 * rg + 2 * g + (i >> 1)) & 15];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[rg][c][i] *= a;
+        }
       }
+      const uint4 pa = *reinterpret_cast<const uint4*>(&pt[wave][rg][r][8 * g]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        acc[rg][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                             __builtin_bit_cast(bf16x8, vv[c]), acc[rg][c], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
   }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    cacc[(wave * G + g) * kD + 2 * lane] = acc0[g];
-    cacc[(wave * G + g) * kD + 2 * lane + 1] = acc1[g];
-    if (lane == 0) {
-      cm[wave * G + g] = m_run[g];
-      cl[wave * G + g] = l_run[g];
-    }
+
+  // ---- per-wave partial -> LDS -> workgroup partial ----
+  float l = l_part;
+  {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+    l = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto c2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+    l = __uint_as_float(c2[0]) + __uint_as_float(c2[1]);
   }
+  if (g == 0 && r < G) {
+    cm[wave * G + r] = m_run;
+    cl[wave * G + r] = l;
+  }
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int head = 8 * rg + 2 * g + j;
+      if (head < G) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) cacc[(wave * G + head) * kD + 16 * c + r] = acc[rg][c][2 * j] + acc[rg][c][2 * j + 1];
+      }
+    }
   __syncthreads();
   combine_and_store<G>(p, cm, cl, cacc, b, h * G, sp);
 }
@@ -996,13 +1059,14 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   return OSCAR_EUNSUPPORTED;
 }
 
-// bf16 comparator append: scatter rows into [page][Hkv][2][16][128]
+// bf16 comparator append: K rows into [page][Hkv] elements [16 slot][128],
+// V into the transposed part, element 2048 + 16 c + slot.
 __global__ __launch_bounds__(256) void bf16_append_kernel(const uint16_t* __restrict__ k_new,
                                                           const uint16_t* __restrict__ v_new, int64_t n_tokens,
                                                           const int32_t* seq_idx, const int32_t* pos, int batch,
                                                           const int32_t* block_table, int max_pages,
                                                           uint16_t* kv_pool, int64_t n_pages, int hkv) {
-  // one thread per (token, head, 16-byte chunk of K or V row)
+  // one thread per (token, head, 8-channel chunk of K or V)
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = n_tokens * hkv * 2 * 16;
   if (i >= total) return;
@@ -1015,9 +1079,20 @@ __global__ __launch_bounds__(256) void bf16_append_kernel(const uint16_t* __rest
   if (b < 0 || b >= batch || ps < 0 || (ps >> 4) >= max_pages) return;
   const int page = block_table[(int64_t)b * max_pages + (ps >> 4)];
   if (page < 0 || page >= n_pages) return;
-  const uint4* src = reinterpret_cast<const uint4*>((kv ? v_new : k_new) + (t * hkv + h) * kD);
-  uint4* dst = reinterpret_cast<uint4*>(kv_pool + ((((int64_t)page * hkv + h) * 2 + kv) * kPage + (ps & 15)) * kD);
-  dst[chunk] = src[chunk];
+  const uint4 src = reinterpret_cast<const uint4*>((kv ? v_new : k_new) + (t * hkv + h) * kD)[chunk];
+  uint16_t* blk = kv_pool + ((int64_t)page * hkv + h) * (2 * kPage * kD);
+  const int slot = ps & 15;
+  if (kv == 0) {
+    reinterpret_cast<uint4*>(blk + slot * kD)[chunk] = src;
+  } else {
+    const uint32_t w[4] = {src.x, src.y, src.z, src.w};
+    uint16_t* vt = blk + kPage * kD + (8 * chunk) * kPage + slot;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vt[(2 * e) * kPage] = (uint16_t)(w[e] & 0xffffu);
+      vt[(2 * e + 1) * kPage] = (uint16_t)(w[e] >> 16);
+    }
+  }
 }
 
 }  // namespace

@@ -49,7 +49,8 @@ import numpy as np
 #   [ 512, 1024)  V codes: 128 channel words x 4 B; token slot j at bit 2j
 #   [1024, 1152)  16 token records of 8 bytes: fp16 K scale, K zero, V scale, V zero
 # Pool = uint8 [n_pages][Hkv][1152].  Window ring = bf16 [B][W][Hkv][d], slot pos % W.
-# bf16 comparator pool = bf16 [n_pages][Hkv][2 (K, V)][16][d].
+# bf16 comparator pool = bf16 [n_pages][Hkv][4096]: K rows [16 slots][d], then V
+# transposed [d][16 slots] (see append_bf16_ref).
 # ---------------------------------------------------------------------------
 D = 128
 PAGE = 16
@@ -370,14 +371,29 @@ def decode_ref(r_k, r_v, q_bits, seq_lens, block_table, pool, win_k, win_v,
     return out
 
 
+BF16_BLOCK = 2 * PAGE * D  # elements of one (page, KV head) block of the bf16 comparator pool
+
+
 def append_bf16_ref(k_new, v_new, seq_idx, pos, block_table, kv_pool):
-    """Scatter bf16 k/v [T][Hkv][d] into the comparator pool [n_pages][Hkv][2][16][d]."""
+    """Scatter bf16 k/v [T][Hkv][d] into the comparator pool [n_pages][Hkv][4096]:
+    K rows [16 slots][d], then V transposed [d][16 slots]."""
+    ch = np.arange(D)
     for i in range(np.shape(k_new)[0]):
         b, p = int(seq_idx[i]), int(pos[i])
         page = int(block_table[b][p // PAGE])
         assert page >= 0
-        kv_pool[page, :, 0, p % PAGE] = k_new[i]
-        kv_pool[page, :, 1, p % PAGE] = v_new[i]
+        slot = p % PAGE
+        blk = kv_pool[page]                      # [Hkv][4096] view
+        blk[:, slot * D:(slot + 1) * D] = k_new[i]
+        blk[:, PAGE * D + ch * PAGE + slot] = v_new[i]
+
+
+def bf16_pages_kv(kv_pool, pages, h):
+    """K, V bits [len(pages) * 16][d] of KV head h from comparator pool blocks."""
+    blk = np.asarray(kv_pool)[pages, h]                                  # [n_pg][4096]
+    k = blk[:, :PAGE * D].reshape(-1, PAGE, D)
+    v = blk[:, PAGE * D:].reshape(-1, D, PAGE).transpose(0, 2, 1)
+    return k.reshape(-1, D), v.reshape(-1, D)
 
 
 def decode_bf16_ref(q_bits, seq_lens, block_table, kv_pool, n_kv_heads: int, pairs=None):
@@ -393,8 +409,9 @@ def decode_bf16_ref(q_bits, seq_lens, block_table, kv_pool, n_kv_heads: int, pai
         n_pg = -(-n // PAGE)
         pages = np.asarray(block_table[b][:n_pg], dtype=np.int64)
         assert np.all(pages >= 0)
-        k = bf16_to_f64(kv_pool[pages, h, 0]).reshape(-1, d)[:n]
-        v = bf16_to_f64(kv_pool[pages, h, 1]).reshape(-1, d)[:n]
+        kb, vb = bf16_pages_kv(kv_pool, pages, h)
+        k = bf16_to_f64(kb)[:n]
+        v = bf16_to_f64(vb)[:n]
         for j in range(g):
             s = k @ q[b, h * g + j] / math.sqrt(d)
             p = np.exp(s - s.max())

@@ -236,12 +236,12 @@ def test_decode_max_len_above_actual(K):
 def test_bf16_comparator_small(K):
     s = make_spec(1, [1000, 77])
     bt, n_pages = wl.page_table(s)
-    kv = np.zeros((n_pages, 8, 2, 16, 128), np.uint16)
+    kv = np.zeros((n_pages, 8, ref.BF16_BLOCK), np.uint16)
     k, v, si, ps = token_list(s)
     ref.append_bf16_ref(k, v, si, ps, bt, kv)
     q = wl.decode_queries(s)
     shape = K.make_shape(32, 8, 128)
-    kvd = torch.zeros((n_pages, 8, 2, 16, 128), dtype=torch.int16, device=DEV)
+    kvd = torch.zeros((n_pages, 8, ref.BF16_BLOCK), dtype=torch.int16, device=DEV)
     K.oscar_bf16_append(shape, D(k), D(v), D(si), D(ps), D(bt), kvd)
     torch.cuda.synchronize()
     assert np.array_equal(H(kvd, np.uint16), kv)
@@ -437,7 +437,7 @@ def test_full_config3_bf16_comparator(K):
     shape = K.make_shape(32, 8, 128)
     bt, n_pages = wl.page_table(s)
     btd = D(bt)
-    kv = torch.zeros((n_pages, 8, 2, 16, 128), dtype=torch.int16, device=DEV)
+    kv = torch.zeros((n_pages, 8, K.BF16_BLOCK_ELEMS), dtype=torch.int16, device=DEV)
     kept = {}
     for b in range(s.batch):
         k, v, si, ps = wl.prefill_tokens(s, b)

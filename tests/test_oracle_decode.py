@@ -143,7 +143,7 @@ def test_bf16_comparator_is_sdpa(rng):
     s = wl.spec(1, batch=2)
     s.seq_lens = np.array([45, 17], np.int32)
     bt, n_pages = wl.page_table(s)
-    pool = np.zeros((n_pages, 8, 2, 16, 128), np.uint16)
+    pool = np.zeros((n_pages, 8, ref.BF16_BLOCK), np.uint16)
     q = wl.decode_queries(s)
     for b in range(2):
         k, v, si, pos = wl.prefill_tokens(s, b)
@@ -154,6 +154,22 @@ def test_bf16_comparator_is_sdpa(rng):
         qq = torch.from_numpy(ref.bf16_to_f64(q[b])).view(8, 4, 1, 128)
         o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv).reshape(32, 128).numpy()
         assert np.allclose(got[b], o, rtol=1e-12, atol=1e-13)
+
+
+def test_bf16_comparator_layout_by_hand():
+    """K row j of a page at elements [128 j, 128 j + 128); V of slot j, channel c at
+    element 2048 + 16 c + j; round trip through bf16_pages_kv."""
+    bt = np.array([[1, 0]], np.int32)
+    pool = np.zeros((2, 1, ref.BF16_BLOCK), np.uint16)
+    k = np.zeros((1, 1, 128), np.uint16)
+    v = np.zeros((1, 1, 128), np.uint16)
+    k[0, 0, 5] = 0x3F80                     # 1.0 at channel 5
+    v[0, 0, 9] = 0x4000                     # 2.0 at channel 9
+    ref.append_bf16_ref(k, v, np.array([0]), np.array([3]), bt, pool)   # position 3: page 1, slot 3
+    assert pool[1, 0, 3 * 128 + 5] == 0x3F80 and pool[1, 0, 2048 + 16 * 9 + 3] == 0x4000
+    assert np.count_nonzero(pool) == 2
+    kk, vv = ref.bf16_pages_kv(pool, np.array([1]), 0)
+    assert kk[3, 5] == 0x3F80 and vv[3, 9] == 0x4000 and np.count_nonzero(kk) == 1 and np.count_nonzero(vv) == 1
 
 
 def test_direct_decode_equals_paged_decode(rng):
