@@ -15,6 +15,7 @@ constexpr int kPage = 16;        // tokens per page
 constexpr int kBlock = 1152;     // bytes per (page, KV head) block
 constexpr int kKCodes = 0, kVCodes = 512, kMeta = 1024;  // token t's record {Ks, Kz, Vs, Vz} fp16 at kMeta + 8t
 constexpr int kMaxWindow = 1024;
+constexpr int kWinChunk = 32;  // window tokens per decode workgroup (one window partial each)
 constexpr int kPartStride = 2 + kD;  // (m, l, acc[128]) per (batch, q head, split)
 constexpr int kMaxSplit = 2048;      // tokens per split at most: 16 tiles of 128, 4 per wave
 
@@ -37,9 +38,9 @@ struct SplitPlan {
   int n_splits;  // splits for the longest sequence
 };
 
-// Workgroups of the INT2 split kernel resident per compute unit (its register
-// and LDS budget: four 4-wave workgroups at G <= 4, two at G = 8, 16).
-inline int split_wgs_per_cu(int gqa) { return gqa <= 4 ? 4 : 2; }
+// Workgroups of the INT2 split kernel resident per compute unit: two 4-wave
+// workgroups (its register budget, two tiles in flight per wave at G <= 4).
+inline int split_wgs_per_cu(int /*gqa*/) { return 2; }
 
 // The longest split (multiple of 64 in [256, 2048]) that still gives every
 // resident workgroup slot of the device a range of the longest sequence.  A
@@ -64,23 +65,43 @@ inline SplitPlan plan_splits(int batch, int n_kv_heads, int gqa, int max_tokens,
 // Compute units of the current device (the split plan depends on it).
 int device_cu_count();
 
+// KV heads a workgroup of the INT2 split kernel reads side by side (its 4
+// waves take one head each, or share one head round robin): adjacent heads'
+// blocks of a page are adjacent in the pool, so 4 of them make one 4.6 KB read.
+inline int split_heads_per_wg(int n_kv_heads) { return n_kv_heads % 4 == 0 ? 4 : (n_kv_heads % 2 == 0 ? 2 : 1); }
+
+// Resident workgroups of the persistent INT2 split kernel.
+inline int split_wg_count(int gqa, int n_cu) { return (n_cu > 0 ? n_cu : 256) * split_wgs_per_cu(gqa); }
+
 // Workspace layout (bytes, each region 256-aligned):
-//   qsum      float [B][Hq]                      sum of the rotated query's channels
-//   qop       int   [B][Hkv][ceil(G/4)][64][9]   per-lane fp8 score operand (8 dwords) + E8M0 scale
-//   part      float [B][Hq][n_splits][130]       split partials (m, l, acc[128])
-//   wpart     float [B][Hq][130]                 window partials (m, l, acc[128])
+//   qsum         float [B][Hq]                      sum of the rotated query's channels
+//   qop          int   [B][Hkv][ceil(G/4)][64][9]   per-lane fp8 score operand (8 dwords) + E8M0 scale
+//   part         float  bf16 comparator: [B][Hq][n_splits][130] split partials (m, l, acc[128]);
+//                       INT2: [n_wg + units][hw][gw][130] partials of the persistent workgroups
+//                       (units = B Hkv / hw x Hq / (Hkv gw); hw KV heads per workgroup)
+//   wpart        float [B][Hq][ceil(W/32)][130]     window chunk partials (m, l, acc[128])
+//   tile_prefix  int   [units + 1]                  first history tile of each merge unit
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct WorkspaceLayout {
-  size_t qsum, qop, part, wpart, total;
+  size_t qsum, qop, part, wpart, tile_prefix, total;
 };
-inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, const SplitPlan& p) {
-  const size_t g4 = (size_t)((n_q_heads / n_kv_heads + 3) / 4);
+inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int window, const SplitPlan& p,
+                                        int n_cu) {
+  const int gqa = n_q_heads / n_kv_heads;
+  const size_t g4 = (size_t)((gqa + 3) / 4);
+  const size_t gw = (size_t)(gqa > 8 ? 8 : gqa);
+  const size_t units = (size_t)batch * n_q_heads / (gw * (size_t)split_heads_per_wg(n_kv_heads));
+  const size_t hw = (size_t)split_heads_per_wg(n_kv_heads);
+  const size_t part_bf16 = (size_t)batch * n_q_heads * p.n_splits * kPartStride;
+  const size_t part_int2 = ((size_t)split_wg_count(gqa, n_cu) * hw * gw + (size_t)batch * n_q_heads) * kPartStride;
   WorkspaceLayout w{};
   w.qsum = 0;
   w.qop = w.qsum + align256((size_t)batch * n_q_heads * sizeof(float));
   w.part = w.qop + align256((size_t)batch * n_kv_heads * g4 * 64 * 9 * sizeof(int));
-  w.wpart = w.part + align256((size_t)batch * n_q_heads * p.n_splits * kPartStride * sizeof(float));
-  w.total = w.wpart + align256((size_t)batch * n_q_heads * kPartStride * sizeof(float));
+  w.wpart = w.part + align256((part_bf16 > part_int2 ? part_bf16 : part_int2) * sizeof(float));
+  const size_t n_wchunks = (size_t)((window + kWinChunk - 1) / kWinChunk);
+  w.tile_prefix = w.wpart + align256((size_t)batch * n_q_heads * n_wchunks * kPartStride * sizeof(float));
+  w.total = w.tile_prefix + align256((units + 1) * sizeof(int));
   return w;
 }
 
@@ -167,6 +188,12 @@ __device__ __forceinline__ float row_min16(float x) {
   x = fminf(x, dpp_f32<kDppSwap2>(x));
   x = fminf(x, dpp_f32<kDppHalfMirror>(x));
   return fminf(x, dpp_f32<kDppMirror>(x));
+}
+
+// max over the 64 lanes of a wave
+__device__ __forceinline__ float wave_max64(float x) {
+  x = row_max16(x);
+  return max_rows(x);
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -19,11 +19,12 @@
 // matrix cores as v_mfma_scale_f32_16x16x128_f8f6f4 with the packed 2-bit codes
 // as the fp4 (e2m1) operand: a code c zero-extended to a nibble is exactly the
 // e2m1 value c/2, so (w & 0x33333333) and ((w >> 2) & 0x33333333) turn 16 packed
-// codes into two ready operand dwords.  The other operand (q' for the scores,
-// softmax weights for the values) is carried as four fp8 (e4m3) terms
-// x = t0 + t1/16 + t2/256 + t3/4096 (each the RNE of the remaining residual),
-// one term per MFMA row, with the power-of-two factors in the E8M0 operand
-// scales: about 16 significant bits.  Rows are (head, term): 4 heads per MFMA.
+// codes into two ready operand dwords.  The other operand is carried as fp8
+// (e4m3) terms x = t0 + t1/16 + t2/256 (+ t3/4096), each the RNE of the
+// remaining residual, one term per MFMA row, with the power-of-two factors in
+// the E8M0 operand scales: four terms (~16 significant bits) for q' in the
+// scores, three (~12 bits; their rounding is random across tokens) for the
+// softmax weights in the values.  Rows are (head, term): 4 heads per MFMA.
 //   scores: A = q' terms [(head, term) x 128 channels], B = K codes [128 x 16 tokens]
 //   values: A = w terms  [(head, term) x 128 tokens],  B = V codes [128 x 16 channels]
 // The score output leaves one (head, token) per lane after an in-lane sum of
@@ -79,24 +80,158 @@ __device__ __forceinline__ int clamp_len(int n, int max_pages) {
 
 __device__ __forceinline__ int clamp_scale(int s) { return s < 1 ? 1 : (s > 254 ? 254 : s); }
 
-// Four e4m3 terms of a pair of values (|x| < 128): term j of a in byte 0 and of
-// b in byte 1 of out[j].
-__device__ __forceinline__ void split4(float a, float b, uint32_t out[4]) {
+// NT e4m3 terms of a pair of values (|x| < 128): term j of a in byte 0 and of
+// b in byte 1 of out[j]; each term is the RNE of the remaining residual x 16^j.
+template <int NT>
+__device__ __forceinline__ void split_terms(float a, float b, uint32_t out[NT]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NT; ++j) {
     const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     out[j] = (uint32_t)pk & 0xffffu;
-    if (j < 3) {
+    if (j < NT - 1) {
       a = (a - __builtin_amdgcn_cvt_f32_fp8(pk, 0)) * 16.f;
       b = (b - __builtin_amdgcn_cvt_f32_fp8(pk, 1)) * 16.f;
     }
   }
 }
+__device__ __forceinline__ void split4(float a, float b, uint32_t out[4]) { split_terms<4>(a, b, out); }
+
+// Terms of the softmax-weight operand of the value MFMA: 3 terms (~12
+// significant bits; their rounding is random across tokens, so the output's
+// relative error stays near 2^-12).  The fourth row of each head stays zero.
+constexpr int kWTerms = 3;
 
 __device__ __forceinline__ int exponent_above(float x) {  // E with |x| < 2^E (0 for x == 0)
   int e = 0;
   frexpf(x, &e);
   return e;
+}
+
+struct SplitParams {
+  const float* qsum;          // [B][Hq]      (INT2 path)
+  const int* qop;             // [B][Hkv][ceil(G/4)][64][9] (INT2 path)
+  const uint16_t* q;          // [B][Hq][128] bf16 queries
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  const uint8_t* pool;        // INT2 pool
+  const uint16_t* kv_pool;    // bf16 pool
+  const uint16_t* r_v;        // INT2: value rotations [Hkv][128][128] (un-rotation in the merge)
+  const uint16_t* win_k;      // INT2: bf16 window rings [B][W][Hkv][128]
+  const uint16_t* win_v;
+  float* part;                // bf16: [B][Hq][n_splits][130]; INT2: [n_wg + units][gw][130] slot partials
+  float* wpart;               // INT2: [B][Hq][n_wchunks][130] window chunk partials (unrotated domain)
+  int* tile_prefix;           // INT2: [units + 1] first history tile of each unit in the flattened order
+  float* out;                 // [B][Hq][128]
+  int64_t n_pages;
+  int batch, hq, hkv, max_pages, max_len, window, split, n_splits;
+  int n_wchunks;              // INT2: 32-token chunks of the window, ceil(W / 32)
+  int gsub;                   // INT2 merge units per KV head, each taking gw of its query heads
+  int gw;                     // query heads a unit really has (<= G of the kernel's instantiation)
+  int n_wg;                   // INT2: persistent workgroups of the split kernel
+  int hw;                     // INT2: KV heads a split workgroup reads side by side (1, 2 or 4)
+  float scale_log2;           // log2(e) / sqrt(d)
+};
+
+// Sequence length as the kernels see it: clamped to [0, max_len].
+__device__ __forceinline__ int seq_len_of(const SplitParams& p, int b) {
+  const int n = p.seq_lens[b];
+  return n < 0 ? 0 : (n > p.max_len ? p.max_len : n);
+}
+
+// History tiles (128 tokens) of sequence b.
+__device__ __forceinline__ int hist_tiles(const SplitParams& p, int b) {
+  const int n = seq_len_of(p, b);
+  const int hist = n - (n < p.window ? n : p.window);
+  return (hist + 127) >> 7;
+}
+
+template <int G>
+constexpr int window_smem_bytes() { return (G * kD + kWinChunk * 65 + G * kWinChunk + 4 * G) * 4; }
+
+// One 32-token chunk of the bf16 window of (sequence b, KV head h): positions
+// n - w + 32 c .. at ring slots pos % W, unrotated, for the G query heads of h.
+// Thread (t, part) = (tid / 8, tid % 8) loads dims 16 part .. 16 part + 15 of
+// token t's key and value (all loads issued first); the 8 parts of a score are
+// summed across lanes, V goes through LDS for P V.  Writes (m, l, acc[128]) of
+// the chunk per head; an empty chunk writes m = -inf, l = 0, acc = 0.
+template <int G>
+__device__ void window_chunk(const SplitParams& p, int b, int h, int c, float* sm) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int n = seq_len_of(p, b);
+  const int w = n < p.window ? n : p.window;
+  const int cs = n - w + kWinChunk * c;
+  const int nt = min(kWinChunk, n - cs);  // <= 0: empty chunk
+  const int hq0 = h * G;
+  float* dst0 = p.wpart + (((int64_t)b * p.hq + hq0) * p.n_wchunks + c) * kPartStride;
+  const int64_t head_stride = (int64_t)p.n_wchunks * kPartStride;
+  if (nt <= 0) {
+    for (int e = tid; e < G * kPartStride; e += 256) {
+      const int g = e / kPartStride, i = e % kPartStride;
+      dst0[g * head_stride + i] = i == 0 ? kNegInf : 0.f;
+    }
+    return;
+  }
+  float* qs = sm;                                            // [G][128]
+  uint32_t* vs = reinterpret_cast<uint32_t*>(qs + G * kD);   // [32][65] bf16 pairs
+  float* ps = reinterpret_cast<float*>(vs + kWinChunk * 65);  // [G][32]
+  float* red = ps + G * kWinChunk;                            // [4][G]
+  const int t = tid >> 3, part = tid & 7;
+  const bool valid = t < nt;
+  uint4 kk[2], vv[2];
+  {
+    const int slot = valid ? (cs + t) % p.window : 0;
+    const int64_t row = (((int64_t)b * p.window + slot) * p.hkv + h) * kD + 16 * part;
+    const uint4* kr = reinterpret_cast<const uint4*>(p.win_k + row);
+    const uint4* vr = reinterpret_cast<const uint4*>(p.win_v + row);
+    kk[0] = kr[0]; kk[1] = kr[1];
+    vv[0] = vr[0]; vv[1] = vr[1];
+  }
+  for (int e = tid; e < G * kD; e += 256) qs[e] = bf16_to_f32(p.q[((int64_t)b * p.hq + hq0) * kD + e]);
+  {
+    uint32_t* d = vs + t * 65 + 8 * part;
+    const uint32_t u[8] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w, vv[1].x, vv[1].y, vv[1].z, vv[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d[i] = valid ? u[i] : 0u;
+  }
+  __syncthreads();
+  const uint32_t ku[8] = {kk[0].x, kk[0].y, kk[0].z, kk[0].w, kk[1].x, kk[1].y, kk[1].z, kk[1].w};
+  float sc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float* qg = qs + g * kD + 16 * part;
+    float d = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d = fmaf(bf16lo(ku[i]), qg[2 * i], fmaf(bf16hi(ku[i]), qg[2 * i + 1], d));
+    d += dpp_f32<kDppSwap1>(d);
+    d += dpp_f32<kDppSwap2>(d);
+    d += dpp_f32<kDppHalfMirror>(d);  // the 8 parts of token t
+    sc[g] = valid ? d * p.scale_log2 : kNegInf;
+    const float m = wave_max64(sc[g]);
+    if ((tid & 63) == 0) red[wave * G + g] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float m = fmaxf(fmaxf(red[g], red[G + g]), fmaxf(red[2 * G + g], red[3 * G + g]));
+    if (part == 0) ps[g * kWinChunk + t] = valid ? exp2f(sc[g] - m) : 0.f;
+  }
+  __syncthreads();
+  for (int e = tid; e < G * kD; e += 256) {
+    const int g = e >> 7, ch = e & (kD - 1);
+    const float* pg = ps + g * kWinChunk;
+    float acc = 0.f, l = 0.f;
+    for (int tt = 0; tt < nt; ++tt) {
+      const uint32_t x = vs[tt * 65 + (ch >> 1)];
+      acc = fmaf(pg[tt], (ch & 1) ? bf16hi(x) : bf16lo(x), acc);
+      l += pg[tt];
+    }
+    float* dst = dst0 + g * head_stride;
+    dst[2 + ch] = acc;
+    if (ch == 0) {
+      dst[0] = fmaxf(fmaxf(red[g], red[G + g]), fmaxf(red[2 * G + g], red[3 * G + g]));
+      dst[1] = l;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -110,20 +245,41 @@ __device__ __forceinline__ int exponent_above(float x) {  // E with |x| < 2^E (0
 //   consumes it.
 // ---------------------------------------------------------------------------
 template <int G>
-__global__ __launch_bounds__(256) void prep_q_kernel(const uint16_t* __restrict__ r_k,
-                                                     const uint16_t* __restrict__ q, float* __restrict__ qsum_out,
-                                                     int* __restrict__ qop, int hq, int hkv) {
+__global__ __launch_bounds__(256) void prep_kernel(SplitParams p, const uint16_t* __restrict__ r_k) {
   constexpr int NCB = (G + 3) / 4;  // 4-head operand groups
-  __shared__ float qs[G][kD];
-  __shared__ int qexp[G];
+  constexpr int kQBytes = 2 * G * kD * 4 + G * 4;
+  constexpr int kSmem = kQBytes > window_smem_bytes<G>() ? kQBytes : window_smem_bytes<G>();
+  __shared__ __align__(16) float smem_f[kSmem / 4];
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int hq = p.hq, hkv = p.hkv;
+  if (blockIdx.z > 0) {  // chunk z - 1 of the bf16 window of this (sequence, KV head)
+    window_chunk<G>(p, b, h, blockIdx.z - 1, smem_f);
+    return;
+  }
+  // first history tile of the units (b, head group, sub) in the flattened order
+  // (sequence-major, then KV head group, then head subset), written by the first
+  // head of each group; the last group also closes the array
+  if (tid == 0 && h % p.hw == 0) {
+    int pb = 0;
+    for (int bb = 0; bb < b; ++bb) pb += hist_tiles(p, bb);
+    const int tb = hist_tiles(p, b);
+    const int hgp = h / p.hw, per_seq = (hkv / p.hw) * p.gsub;
+    for (int sub = 0; sub < p.gsub; ++sub)
+      p.tile_prefix[(int64_t)b * per_seq + hgp * p.gsub + sub] = per_seq * pb + (hgp * p.gsub + sub) * tb;
+    if (b == p.batch - 1 && h == hkv - p.hw) p.tile_prefix[(int64_t)p.batch * per_seq] = per_seq * (pb + tb);
+  }
+  float (*qs)[kD] = reinterpret_cast<float (*)[kD]>(smem_f);
+  float (*qraw)[kD] = reinterpret_cast<float (*)[kD]>(smem_f + G * kD);
+  int* qexp = reinterpret_cast<int*>(smem_f + 2 * G * kD);
+  const uint16_t* q = p.q;
+  float* qsum_out = const_cast<float*>(p.qsum);
+  int* qop = const_cast<int*>(p.qop);
   {
     const int c = tid >> 1, half = tid & 1;
     const uint4* rrow = reinterpret_cast<const uint4*>(r_k + ((int64_t)h * kD + c) * kD + 64 * half);
     uint4 rv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) rv[i] = rrow[i];
-    __shared__ float qraw[G][kD];
     for (int e = tid; e < G * kD; e += 256) qraw[e / kD][e % kD] = bf16_to_f32(q[((int64_t)b * hq + h * G) * kD + e]);
     __syncthreads();
 #pragma unroll 1
@@ -187,37 +343,11 @@ __global__ __launch_bounds__(256) void prep_q_kernel(const uint16_t* __restrict_
   }
 }
 
-struct SplitParams {
-  const float* qsum;          // [B][Hq]      (INT2 path)
-  const int* qop;             // [B][Hkv][ceil(G/4)][64][9] (INT2 path)
-  const uint16_t* q;          // [B][Hq][128] bf16 queries
-  const int32_t* seq_lens;
-  const int32_t* block_table;
-  const uint8_t* pool;        // INT2 pool
-  const uint16_t* kv_pool;    // bf16 pool
-  const uint16_t* r_v;        // INT2: value rotations [Hkv][128][128] (un-rotation in the merge)
-  const uint16_t* win_k;      // INT2: bf16 window rings [B][W][Hkv][128]
-  const uint16_t* win_v;
-  float* part;                // [B][Hq][n_splits][130] split partials
-  float* wpart;               // INT2: [B][Hq][130] window partials (unrotated domain)
-  float* out;                 // [B][Hq][128]
-  int64_t n_pages;
-  int batch, hq, hkv, max_pages, max_len, window, split, n_splits;
-  int gsub;                   // workgroups per KV head, each taking gw of its query heads
-  int gw;                     // query heads a workgroup really has (<= G of its instantiation)
-  float scale_log2;           // log2(e) / sqrt(d)
-};
-
-// Sequence length as the kernels see it: clamped to [0, max_len].
-__device__ __forceinline__ int seq_len_of(const SplitParams& p, int b) {
-  const int n = p.seq_lens[b];
-  return n < 0 ? 0 : (n > p.max_len ? p.max_len : n);
-}
-
-// Combine the 4 waves' (m, l, acc) partials (LDS) into the workgroup partial.
+// Combine the 4 waves' (m, l, acc) partials (LDS) into the workgroup partial
+// (m, l, acc[128]) of each of the gw heads, written to dst0 + g * head_stride.
 template <int G>
-__device__ __forceinline__ void combine_and_store(const SplitParams& p, const float* cm, const float* cl,
-                                                  const float* cacc, int b, int hq0, int sp, int gw = G) {
+__device__ __forceinline__ void combine_and_store(const float* cm, const float* cl, const float* cacc, float* dst0,
+                                                  int64_t head_stride, int gw) {
   const int tid = threadIdx.x;
   for (int e = tid; e < gw * kD; e += 256) {
     const int g = e / kD, c = e % kD;
@@ -231,7 +361,7 @@ __device__ __forceinline__ void combine_and_store(const SplitParams& p, const fl
       acc += f * cacc[(w * G + g) * kD + c];
       L += f * cl[w * G + g];
     }
-    float* dst = p.part + (((int64_t)b * p.hq + hq0 + g) * p.n_splits + sp) * kPartStride;
+    float* dst = dst0 + g * head_stride;
     dst[2 + c] = acc;
     if (c == 0) {
       dst[0] = M;
@@ -248,26 +378,39 @@ struct Tile {
   uint32_t page_ok;      // bit pp: page pp of the tile exists in this split and in the pool
 };
 
-// Block-table entries of a wave's tiles.  The wave's k-th tile is tile
-// wave + 4k of the split (the waves take tiles round robin); lane 8j + pp holds
-// the page of page pp of the wave's tile k0 + j, or -1 when that page is past
-// the split, past the table or outside the pool.  One load serves 8 tiles, so no
-// tile waits on a block-table read before its own loads can start.
+// Block-table entries of two consecutive tiles of a wave.  The wave's k-th
+// tile is tile ph + ts k of the range (ph = the wave's phase, ts = the waves
+// sharing its KV head, which take its tiles round robin);
+// lane 8j + pp (j < 2) holds the page of page pp of the wave's tile k0 + j, or
+// -1 when that page is past the history, the tile past the wave's range, or
+// the entry outside the pool.  The entries are loaded one loop iteration ahead
+// of their use (table_load, no branch: the index is clamped) and validated
+// only when the iteration that uses them starts (table_ready), so no wait on
+// the block table ever drains the tile loads in flight behind it.
 struct TileTable {
   int ent;        // this lane's entry
   uint64_t live;  // ballot of ent >= 0
 };
 
-__device__ __forceinline__ TileTable load_table(const SplitParams& p, const int* btr, int P0, int P1,
-                                                int wave, int k0) {
+__device__ __forceinline__ int table_page(int P0, int ph, int ts, int k0) {
   const int lane = threadIdx.x & 63;
-  const int pg = P0 + 8 * (wave + 4 * (k0 + (lane >> 3))) + (lane & 7);
-  int e = pg <= P1 ? btr[pg] : -1;
-  e = (e >= 0 && e < p.n_pages) ? e : -1;
-  return TileTable{e, __ballot(e >= 0)};
+  return P0 + 8 * (ph + ts * (k0 + ((lane >> 3) & 1))) + (lane & 7);
 }
 
-// All loads of one tile (j-th of its table chunk) are issued back to back with
+__device__ __forceinline__ int table_load(const int* btr, int P0, int P1, int ph, int ts, int k0) {
+  const int pg = table_page(P0, ph, ts, k0);
+  return btr[pg < P1 ? pg : P1];
+}
+
+__device__ __forceinline__ TileTable table_ready(const SplitParams& p, int raw, int P0, int P1, int ph, int ts,
+                                                 int k0, int ntw) {
+  const int lane = threadIdx.x & 63;
+  const int pg = table_page(P0, ph, ts, k0);
+  const bool ok = lane < 16 && pg <= P1 && k0 + (lane >> 3) < ntw && raw >= 0 && raw < p.n_pages;
+  return TileTable{ok ? raw : -1, __ballot(ok)};
+}
+
+// All loads of one tile (j-th of its table pair) are issued back to back with
 // no branches: every page index is broadcast with readlane (so each page's block
 // address is a scalar and a lane only adds its fixed offset), and a missing
 // page is read as page 0 and masked, so the memory system sees the whole tile
@@ -320,7 +463,7 @@ struct WaveState {
   float m_run[NRG], l_part[NRG], az_part[NRG];
 };
 
-template <int G, int NRG>
+template <int G, int NRG, bool FULL>  // FULL: all 8 pages exist and every token is below t_end
 __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t, int pbase, int t_end, int lg,
                                              int lr, const i32x8* qa, const int* qsc, const float* qsr,
                                              uint8_t* wt, WaveState<NRG>& st) {
@@ -347,7 +490,7 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t
   uint2 meta[8];
 #pragma unroll
   for (int pp = 0; pp < 8; ++pp) {
-    const bool live = ((t.page_ok >> pp) & 1u) && (pbase + pp) * 16 + lr < t_end;
+    const bool live = FULL || (((t.page_ok >> pp) & 1u) && (pbase + pp) * 16 + lr < t_end);
     meta[pp].x = live ? t.meta[pp].x : 0u;
     meta[pp].y = live ? t.meta[pp].y : 0u;
   }
@@ -366,7 +509,7 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
       const int tok = (pbase + pp) * 16 + lr;
-      const bool ok = hv && tok < t_end && ((t.page_ok >> pp) & 1u);
+      const bool ok = hv && (FULL || (tok < t_end && ((t.page_ok >> pp) & 1u)));
       const float ks = h2f((uint16_t)(meta[pp].x & 0xffffu));
       const float kz = h2f((uint16_t)(meta[pp].x >> 16));
       // computed on every lane, then masked: a select, not a branch
@@ -401,10 +544,10 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t
     uint8_t* tile_rg = wt + rg * 2048;
 #pragma unroll
     for (int pp = 0; pp < 8; pp += 2) {
-      uint32_t tt[4];
-      split4(w[pp] * wmul, w[pp + 1] * wmul, tt);
+      uint32_t tt[kWTerms];
+      split_terms<kWTerms>(w[pp] * wmul, w[pp + 1] * wmul, tt);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < kWTerms; ++j) {
         uint8_t* row = tile_rg + (4 * lg + j) * 128 + slot_pos;
         row[16 * pp] = (uint8_t)(tt[j] & 0xffu);
         row[16 * (pp + 1)] = (uint8_t)(tt[j] >> 8);
@@ -449,244 +592,171 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t
   __builtin_amdgcn_wave_barrier();
 }
 
-__device__ __forceinline__ float wave_max64(float x) {
-  x = row_max16(x);
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
-}
 
-
-constexpr int kWinPass = 128;  // window tokens per pass (one per thread pair)
-
-template <int GW>
-constexpr int window_smem_bytes() { return (2 * GW * kD + kWinPass * 65 + 12 * GW) * 4; }
-
-// bf16 window of one merge unit: positions [n - w, n) at ring slots pos % W,
-// unrotated, for query heads hq0 .. hq0 + gw - 1; writes (m, l, acc[128]) per
-// head to the window partials.  A pass takes up to 128 tokens with every load
-// issued up front: thread pair (t, half) holds 64 dims of token t's key (for
-// the scores) and stages the same dims of its value in LDS (for P V).
-template <int GW>
-__device__ void window_unit(const SplitParams& p, int b, int h, int hq0, int n, int w, float* sm) {
-  constexpr int PER = (GW * kD + 255) / 256;
-  const int tid = threadIdx.x, gw = p.gw, wave = tid >> 6;
-  float* qs = sm;                                            // [GW][128]
-  uint32_t* vw = reinterpret_cast<uint32_t*>(qs + GW * kD);  // [kWinPass][65] bf16 pairs
-  float* ps = reinterpret_cast<float*>(vw + kWinPass * 65);  // [GW][kWinPass]
-  float* red = ps + GW * kWinPass;                           // [4][GW]
-  float* red2 = red + 4 * GW;                                // [4][GW]
-  float* Mrun = red2 + 4 * GW;                               // [GW]
-  float* Lrun = Mrun + GW;                                   // [GW]
-  float* Mnew = Lrun + GW;                                   // [GW]
-  float* Alph = Mnew + GW;                                   // [GW]
-  for (int e = tid; e < GW * kD; e += 256)
-    qs[e] = e < gw * kD ? bf16_to_f32(p.q[((int64_t)b * p.hq + hq0) * kD + e]) : 0.f;
-  if (tid < GW) {
-    Mrun[tid] = kNegInf;
-    Lrun[tid] = 0.f;
-  }
-  float o2[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) o2[k] = 0.f;
-  const int t = tid >> 1, hf = tid & 1;
-  for (int cs = n - w; cs < n; cs += kWinPass) {
-    const int nt = min(kWinPass, n - cs);
-    const bool valid = t < nt;
-    uint4 kk[8], vv[8];
-    if (valid) {
-      const int64_t row = (((int64_t)b * p.window + (cs + t) % p.window) * p.hkv + h) * kD + 64 * hf;
-      const uint4* kr = reinterpret_cast<const uint4*>(p.win_k + row);
-      const uint4* vr = reinterpret_cast<const uint4*>(p.win_v + row);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        kk[i] = kr[i];
-        vv[i] = vr[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) kk[i] = vv[i] = make_uint4(0, 0, 0, 0);
-    }
-    __syncthreads();  // qs, Mrun ready; the previous pass is done with vw and ps
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t* dst = vw + t * 65 + 32 * hf + 4 * i;
-      dst[0] = vv[i].x; dst[1] = vv[i].y; dst[2] = vv[i].z; dst[3] = vv[i].w;
-    }
-    float sc[GW];
-#pragma unroll
-    for (int g = 0; g < GW; ++g) {
-      const float* qg = qs + g * kD + 64 * hf;
-      float d = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t u[4] = {kk[i].x, kk[i].y, kk[i].z, kk[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          d = fmaf(bf16lo(u[j]), qg[8 * i + 2 * j], fmaf(bf16hi(u[j]), qg[8 * i + 2 * j + 1], d));
-      }
-      d += dpp_f32<kDppSwap1>(d);  // the pair's two halves
-      sc[g] = (valid && g < gw) ? d * p.scale_log2 : kNegInf;
-      const float m = wave_max64(sc[g]);
-      if ((tid & 63) == 0) red[wave * GW + g] = m;
-    }
-    __syncthreads();
-    if (tid < GW) {
-      const float mc = fmaxf(fmaxf(red[tid], red[GW + tid]), fmaxf(red[2 * GW + tid], red[3 * GW + tid]));
-      const float mn = fmaxf(Mrun[tid], mc);
-      Mnew[tid] = mn;
-      Alph[tid] = mn == kNegInf ? 1.f : exp2f(Mrun[tid] - mn);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < GW; ++g) {
-      const float mn = Mnew[g];
-      const float pv = sc[g] == kNegInf ? 0.f : exp2f(sc[g] - mn);
-      if (hf == 0) ps[g * kWinPass + t] = pv;
-    }
-    __syncthreads();
-    if (tid < GW) {
-      float su = 0.f;
-      for (int tt = 0; tt < nt; ++tt) su += ps[tid * kWinPass + tt];
-      Lrun[tid] = Lrun[tid] * Alph[tid] + su;
-      Mrun[tid] = Mnew[tid];
-    }
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int e = tid + 256 * k;
-      const int g = e / kD, c = e % kD;
-      float acc = o2[k] * Alph[g];
-      const float* pg = ps + g * kWinPass;
-      for (int tt = 0; tt < nt; ++tt) {
-        const uint32_t x = vw[tt * 65 + (c >> 1)];
-        acc = fmaf(pg[tt], (c & 1) ? bf16hi(x) : bf16lo(x), acc);
-      }
-      o2[k] = acc;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int e = tid + 256 * k;
-    if (e >= gw * kD) break;
-    const int g = e / kD, c = e % kD;
-    float* dst = p.wpart + ((int64_t)b * p.hq + hq0 + g) * kPartStride;
-    dst[2 + c] = o2[k];
-    if (c == 0) {
-      dst[0] = Mrun[g];
-      dst[1] = Lrun[g];
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
-// INT2 history split on the matrix cores.  Lane l = 16 lg + lr.
+// INT2 history attention on the matrix cores, persistent and balanced.
+// The history tiles (128 tokens) of every merge unit (sequence, KV head, head
+// subset) form one flattened sequence, unit after unit.  Workgroup w of the
+// n_wg resident workgroups takes tiles [w T / n_wg, (w + 1) T / n_wg): every
+// workgroup the same amount of work and one prologue, whatever the lengths.  For
+// each unit its range touches it writes one partial, slot w + u of the unit's
+// heads (unique: consecutive units share at most one workgroup).
+// Lane l = 16 lg + lr:
 //   score MFMA output: head 4 rg + lg, token lr of the page;
 //   value accumulators: head 4 rg + lg, channels 8 lr + n (n = 0..7);
 //   loads per tile: K row bytes 8lg..8lg+7 of token lr and its metadata record
 //   for each of the 8 pages; V words of channels 8lr..8lr+7 for pages 2lg, 2lg+1.
-// The waves of a workgroup take the split's tiles round robin; each wave keeps
-// the next tile's loads in flight while it computes the current one.
+// A merge unit is (sequence, group of hw adjacent KV heads, head subset): wave
+// v takes KV head hw g + v % hw and, of the range's tiles, those congruent to
+// v / hw modulo 4 / hw.  With hw = 4 the 4 waves read the same pages' 4 adjacent
+// head blocks (one 4.6 KB span per page) instead of 4 scattered 1152-byte blocks.
+// Each wave keeps two tiles in flight (the loads of its next tile go out before
+// the current one is computed); two workgroups per CU.
 // ---------------------------------------------------------------------------
 template <int G>
-__global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void int2_split_kernel(SplitParams p) {
+__global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
   constexpr int NRG = (G + 3) / 4;                    // MFMA row groups of 4 heads
   constexpr int kTileBytes = 4 * NRG * 16 * 128;     // per-wave w-term tiles
   constexpr int kCombBytes = 4 * G * kD * 4 + 2 * 4 * G * 4;
-  constexpr int kS1 = kTileBytes > kCombBytes ? kTileBytes : kCombBytes;
-  constexpr int kSmem = kS1 > window_smem_bytes<G>() ? kS1 : window_smem_bytes<G>();
-
-  // z = 0: the bf16 windows (x = sequence); they are dispatched before every
-  // history split so that they overlap the history stream instead of trailing
-  // it.  z = 1 + b: history split x of sequence b.
-  const bool win_wg = blockIdx.z == 0;
-  if (win_wg && (int)blockIdx.x >= p.batch) return;
-  const int b = win_wg ? (int)blockIdx.x : (int)blockIdx.z - 1, h = blockIdx.y / p.gsub;
-  const int sp = win_wg ? -1 : (int)blockIdx.x;
-  const int sub = blockIdx.y % p.gsub;
-  const int hq0 = h * p.gw * p.gsub + sub * p.gw;  // first query head of this workgroup
-  const int n = seq_len_of(p, b);
-  const int w = n < p.window ? n : p.window;
-  const int hist = n - w;
-
+  constexpr int kSmem = kTileBytes > kCombBytes ? kTileBytes : kCombBytes;
   __shared__ __align__(16) uint8_t smem[kSmem];
 
-  if (sp < 0) {  // the bf16 window of these heads, beside their history splits
-    window_unit<G>(p, b, h, hq0, n, w, reinterpret_cast<float*>(smem));
-    return;
+  const int hg_per_seq = p.hkv / p.hw;  // KV head groups per sequence
+  const int per_seq = hg_per_seq * p.gsub;
+  const int units = p.batch * per_seq;
+  const int64_t T = p.tile_prefix[units];
+  const int64_t nw = T < p.n_wg ? T : p.n_wg;  // at least one tile per workgroup
+  if ((int64_t)blockIdx.x >= nw) return;
+  const int64_t lo = T * blockIdx.x / nw, hi = T * (blockIdx.x + 1) / nw;
+  // first unit of the range: the last u with tile_prefix[u] <= lo
+  int u = 0;
+  {
+    int a = 0, c = units;  // tile_prefix[a] <= lo < tile_prefix[c]
+    while (c - a > 1) {
+      const int mid = (a + c) >> 1;
+      if (p.tile_prefix[mid] <= lo) a = mid; else c = mid;
+    }
+    u = a;
   }
-  const int t_begin = sp * p.split;
-  if (t_begin >= hist) return;
-  const int t_end = min(t_begin + p.split, hist);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lr = lane & 15;
-
-  // score operands prepared once per (sequence, KV head)
-  i32x8 qa[NRG];
-  int qsc[NRG];
-  float qsr[NRG];
-  const int ncb = (p.gw * p.gsub + 3) / 4;
-#pragma unroll
-  for (int rg = 0; rg < NRG; ++rg) {
-    const int* src = p.qop + ((((int64_t)b * p.hkv + h) * ncb + (sub * p.gw) / 4 + rg) * 64 + lane) * 9;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qa[rg][i] = src[i];
-    qsc[rg] = src[8];
-    qsr[rg] = (4 * rg + lg < p.gw) ? p.qsum[(int64_t)b * p.hq + hq0 + 4 * rg + lg] : 0.f;
-  }
-
-  WaveState<NRG> st;
-#pragma unroll
-  for (int rg = 0; rg < NRG; ++rg) {
-    st.m_run[rg] = kNegInf;
-    st.l_part[rg] = 0.f;
-    st.az_part[rg] = 0.f;
-#pragma unroll
-    for (int nn = 0; nn < 8; ++nn) st.acc[rg][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
+  const int hv = wave % p.hw, ts = 4 / p.hw, ph = wave / p.hw;  // head in group, tile stride, phase
   uint8_t* wt = smem + wave * (NRG * 2048);
-  const int P0 = t_begin >> 4, P1 = (t_end - 1) >> 4;
-  const int n_tiles = (P1 - P0 + 8) >> 3;
-  const int* btr = p.block_table + (int64_t)b * p.max_pages;
+  const int ncb = (p.gw * p.gsub + 3) / 4;
 
-  // The wave's tiles k = 0 .. ntw-1 are tiles wave + 4k of the split (at most
-  // 4: a split holds at most 2048 tokens = 16 tiles).  One block-table load
-  // covers them all, so a tile's loads never wait on a table read.  A wave keeps
-  // one tile in registers: at ~122 VGPRs four waves share each SIMD, and the
-  // other waves' work hides a wave's load latency (measured faster than keeping
-  // two tiles per wave in flight at two waves per SIMD).
-  const int ntw = wave < n_tiles ? (n_tiles - wave + 3) >> 2 : 0;
-  const TileTable tab = load_table(p, btr, P0, P1, wave, 0);
-  for (int k = 0; k < ntw; ++k) {
-    const int pbase = P0 + 8 * (wave + 4 * k);
-    Tile ta;
-    load_tile(p, tab, k, h, pbase, t_end, lg, lr, ta);
-    compute_tile<G, NRG>(p, ta, pbase, t_end, lg, lr, qa, qsc, qsr, wt, st);
-  }
+  for (; u < units; ++u) {
+    const int64_t su = p.tile_prefix[u], su1 = p.tile_prefix[u + 1];
+    if (su >= hi) break;
+    const int j0 = (int)((lo > su ? lo : su) - su), j1 = (int)((hi < su1 ? hi : su1) - su);
+    if (j1 <= j0) continue;
+    const int b = u / per_seq, hs = u % per_seq, hgp = hs / p.gsub, sub = hs % p.gsub;
+    const int h = hgp * p.hw + hv;                   // this wave's KV head
+    const int hq0 = h * p.gw * p.gsub + sub * p.gw;  // first query head of the unit for this wave
+    const int n = seq_len_of(p, b);
+    const int t_end = n - (n < p.window ? n : p.window);  // history tokens
 
-  // ---- per-wave partial -> LDS -> workgroup partial ----
-  __syncthreads();  // every wave is done with its w-term tile before smem is reused
-  float* cacc = reinterpret_cast<float*>(smem);  // [4][G][128]
-  float* cm = cacc + 4 * G * kD;                 // [4][G]
-  float* cl = cm + 4 * G;                        // [4][G]
+    // score operands prepared once per (sequence, KV head)
+    i32x8 qa[NRG];
+    int qsc[NRG];
+    float qsr[NRG];
 #pragma unroll
-  for (int rg = 0; rg < NRG; ++rg) {
-    const float l = row_sum16(st.l_part[rg]), az = row_sum16(st.az_part[rg]);
-    const int head = 4 * rg + lg;
-    if (head < p.gw) {
+    for (int rg = 0; rg < NRG; ++rg) {
+      const int* src = p.qop + ((((int64_t)b * p.hkv + h) * ncb + (sub * p.gw) / 4 + rg) * 64 + lane) * 9;
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn)
-        cacc[(wave * G + head) * kD + 8 * lr + nn] =
-            (st.acc[rg][nn][0] + st.acc[rg][nn][1]) + (st.acc[rg][nn][2] + st.acc[rg][nn][3]) + az;
-      if (lr == 0) {
-        cm[wave * G + head] = st.m_run[rg];
-        cl[wave * G + head] = l;
+      for (int i = 0; i < 8; ++i) qa[rg][i] = src[i];
+      qsc[rg] = src[8];
+      qsr[rg] = (4 * rg + lg < p.gw) ? p.qsum[(int64_t)b * p.hq + hq0 + 4 * rg + lg] : 0.f;
+    }
+    WaveState<NRG> st;
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg) {
+      st.m_run[rg] = kNegInf;
+      st.l_part[rg] = 0.f;
+      st.az_part[rg] = 0.f;
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn) st.acc[rg][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // the w-term tile: rows of an unused term (the 4th) must read 0
+    for (int e = lane; e < NRG * 2048 / 16; e += 64) reinterpret_cast<uint4*>(wt)[e] = make_uint4(0, 0, 0, 0);
+
+    // tiles j0 + ph + ts k of the unit, two per iteration
+    const int P0 = 8 * j0, P1 = (t_end - 1) >> 4;
+    const int ntw = (j1 - j0 - ph + ts - 1) / ts;
+    const int* btr = p.block_table + (int64_t)b * p.max_pages;
+    auto pbase_of = [&](int k) { return P0 + 8 * (ph + ts * k); };
+    TileTable tab = table_ready(p, table_load(btr, P0, P1, ph, ts, 0), P0, P1, ph, ts, 0, ntw);
+    int raw_next = table_load(btr, P0, P1, ph, ts, 2);
+    if constexpr (NRG > 1) {  // one tile in flight per wave (registers)
+      for (int k = 0; k < ntw; k += 2) {
+        Tile t;
+        load_tile(p, tab, 0, h, pbase_of(k), t_end, lg, lr, t);
+        compute_tile<G, NRG, false>(p, t, pbase_of(k), t_end, lg, lr, qa, qsc, qsr, wt, st);
+        if (k + 1 >= ntw) break;
+        load_tile(p, tab, 1, h, pbase_of(k + 1), t_end, lg, lr, t);
+        compute_tile<G, NRG, false>(p, t, pbase_of(k + 1), t_end, lg, lr, qa, qsc, qsr, wt, st);
+        tab = table_ready(p, raw_next, P0, P1, ph, ts, k + 2, ntw);
+        raw_next = table_load(btr, P0, P1, ph, ts, k + 4);
+      }
+    } else {  // two tiles in flight per wave: tile k + 1's loads go out before tile k is computed
+      Tile ta, tb;
+      load_tile(p, tab, 0, h, pbase_of(0), t_end, lg, lr, ta);
+      for (int k = 0; k < ntw; k += 2) {
+        // past the range (k + 1 == ntw) the tile's entries are empty: it re-reads
+        // page 0's block (cache resident) and is never computed
+        load_tile(p, tab, 1, h, pbase_of(k + 1), t_end, lg, lr, tb);
+        compute_tile<G, NRG, false>(p, ta, pbase_of(k), t_end, lg, lr, qa, qsc, qsr, wt, st);
+        if (k + 1 >= ntw) break;
+        tab = table_ready(p, raw_next, P0, P1, ph, ts, k + 2, ntw);
+        raw_next = table_load(btr, P0, P1, ph, ts, k + 4);
+        load_tile(p, tab, 0, h, pbase_of(k + 2), t_end, lg, lr, ta);
+        compute_tile<G, NRG, false>(p, tb, pbase_of(k + 1), t_end, lg, lr, qa, qsc, qsr, wt, st);
       }
     }
+
+    // ---- per-wave partial -> LDS -> the unit's slot partials ----
+    __syncthreads();  // every wave is done with its w-term tile before smem is reused
+    float* cacc = reinterpret_cast<float*>(smem);  // [4][G][128]
+    float* cm = cacc + 4 * G * kD;                 // [4][G]
+    float* cl = cm + 4 * G;                        // [4][G]
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg) {
+      const float l = row_sum16(st.l_part[rg]), az = row_sum16(st.az_part[rg]);
+      const int head = 4 * rg + lg;
+      if (head < p.gw) {
+#pragma unroll
+        for (int nn = 0; nn < 8; ++nn)
+          cacc[(wave * G + head) * kD + 8 * lr + nn] =
+              (st.acc[rg][nn][0] + st.acc[rg][nn][1]) + (st.acc[rg][nn][2] + st.acc[rg][nn][3]) + az;
+        if (lr == 0) {
+          cm[wave * G + head] = st.m_run[rg];
+          cl[wave * G + head] = l;
+        }
+      }
+    }
+    __syncthreads();
+    // slot partial (hv, g): the waves v = hv + hw i, i < ts
+    float* dst0 = p.part + (int64_t)(blockIdx.x + u) * p.hw * p.gw * kPartStride;
+    for (int e = tid; e < p.hw * p.gw * kD; e += 256) {
+      const int c = e % kD, hg = e / kD, g = hg % p.gw, v0 = hg / p.gw;
+      float M = kNegInf;
+      for (int v = v0; v < 4; v += p.hw) M = fmaxf(M, cm[v * G + g]);
+      float acc = 0.f, L = 0.f;
+      for (int v = v0; v < 4; v += p.hw) {
+        const float f = cm[v * G + g] == kNegInf ? 0.f : exp2f(cm[v * G + g] - M);
+        acc = fmaf(f, cacc[(v * G + g) * kD + c], acc);
+        L = fmaf(f, cl[v * G + g], L);
+      }
+      float* dst = dst0 + (int64_t)hg * kPartStride;
+      dst[2 + c] = acc;
+      if (c == 0) {
+        dst[0] = M;
+        dst[1] = L;
+      }
+    }
+    __syncthreads();  // smem is the next unit's w-term tiles
   }
-  __syncthreads();
-  combine_and_store<G>(p, cm, cl, cacc, b, hq0, sp, p.gw);
 }
 
 // ---------------------------------------------------------------------------
@@ -862,7 +932,8 @@ __global__ __launch_bounds__(256) void bf16_split_kernel(SplitParams p) {
       }
     }
   __syncthreads();
-  combine_and_store<G>(p, cm, cl, cacc, b, h * G, sp);
+  combine_and_store<G>(cm, cl, cacc, p.part + (((int64_t)b * p.hq + h * G) * p.n_splits + sp) * kPartStride,
+                       (int64_t)p.n_splits * kPartStride, G);
 }
 
 // ---------------------------------------------------------------------------
@@ -878,10 +949,32 @@ constexpr int kMergeSplits = 64;  // splits whose accumulators a thread pair hol
 __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
   const int b = blockIdx.y, hq = blockIdx.x, h = hq / gq, tid = threadIdx.x;
   const bool int2 = p.r_v != nullptr;
-  const int n = seq_len_of(p, b);
-  const int w = int2 ? (n < p.window ? n : p.window) : 0;
-  const int hist = n - w;
-  const int ns = (hist + p.split - 1) / p.split;
+  // partials of this head: INT2 - the slots w + u of the workgroups whose tile
+  // range touches unit u; bf16 - the splits of the sequence
+  const float* base;
+  int ns;
+  int64_t stride;
+  if (int2) {
+    const int jq = hq % gq, sub = jq / p.gw, g = jq % p.gw;
+    const int per_seq = (p.hkv / p.hw) * p.gsub;
+    const int u = b * per_seq + (h / p.hw) * p.gsub + sub;
+    const int64_t T = p.tile_prefix[p.batch * per_seq];
+    const int64_t nw = T < p.n_wg ? T : p.n_wg;
+    const int64_t su = p.tile_prefix[u], su1 = p.tile_prefix[u + 1];
+    int w_lo = 0;
+    ns = 0;
+    if (su1 > su) {  // workgroup of tile t: ((t + 1) nw - 1) / T
+      w_lo = (int)(((su + 1) * nw - 1) / T);
+      ns = (int)((su1 * nw - 1) / T) - w_lo + 1;
+    }
+    base = p.part + (((int64_t)(w_lo + u) * p.hw + h % p.hw) * p.gw + g) * kPartStride;
+    stride = (int64_t)p.hw * p.gw * kPartStride;
+  } else {
+    const int n = seq_len_of(p, b);
+    ns = (n + p.split - 1) / p.split;
+    base = p.part + ((int64_t)b * p.hq + hq) * p.n_splits * kPartStride;
+    stride = kPartStride;
+  }
 
   __shared__ float fs[kMergeSplits * 2];      // 2^(m_s - M), l_s of the current pass
   __shared__ float red[256];
@@ -897,11 +990,10 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) rv[j] = *reinterpret_cast<const uint4*>(r + j * kD);
   }
-  // split partials: thread (c, half) sums channel c over the splits s = half, half + 2, ...
+  // split partials: thread (c, half) sums channel c over the partials s = half, half + 2, ...
   const int c = tid & 127, half = tid >> 7;
-  const float* base = p.part + ((int64_t)b * p.hq + hq) * p.n_splits * kPartStride;
   float M = kNegInf;
-  for (int s = tid; s < ns; s += 256) M = fmaxf(M, base[s * kPartStride]);
+  for (int s = tid; s < ns; s += 256) M = fmaxf(M, base[s * stride]);
   M = wave_max64(M);
   if ((tid & 63) == 0) red[tid >> 6] = M;
   __syncthreads();
@@ -913,7 +1005,7 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
     const int cnt = min(kMergeSplits, ns - s0);
     __syncthreads();
     if (tid < cnt) {
-      const float* ps = base + (s0 + tid) * kPartStride;
+      const float* ps = base + (s0 + tid) * stride;
       const float m = ps[0];
       fs[tid] = m == kNegInf ? 0.f : exp2f(m - M);
       fs[kMergeSplits + tid] = ps[1];
@@ -923,7 +1015,7 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
 #pragma unroll
     for (int k = 0; k < kMergeSplits / 2; ++k) {
       const int s = 2 * k + half;
-      x[k] = s < cnt ? base[(s0 + s) * kPartStride + 2 + c] : 0.f;
+      x[k] = s < cnt ? base[(s0 + s) * stride + 2 + c] : 0.f;
     }
 #pragma unroll
     for (int k = 0; k < kMergeSplits / 2; ++k) {
@@ -967,35 +1059,37 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
     float o1 = 0.f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) o1 += o1p[k][tid];
-    const float* wp = p.wpart + ((int64_t)b * p.hq + hq) * kPartStride;
-    const float m1 = M, m2 = wp[0];
-    const float Mx = fmaxf(m1, m2);
-    const float f1 = m1 == kNegInf ? 0.f : exp2f(m1 - Mx);
-    const float f2 = m2 == kNegInf ? 0.f : exp2f(m2 - Mx);
-    const float den = f1 * Ls + f2 * wp[1];
-    dst[tid] = den > 0.f ? (f1 * o1 + f2 * wp[2 + tid]) / den : 0.f;
+    const float* wp = p.wpart + ((int64_t)b * p.hq + hq) * p.n_wchunks * kPartStride;
+    float Mx = M;
+    for (int cc = 0; cc < p.n_wchunks; ++cc) Mx = fmaxf(Mx, wp[cc * kPartStride]);
+    const float f1 = M == kNegInf ? 0.f : exp2f(M - Mx);
+    float den = f1 * Ls, num = f1 * o1;
+    for (int cc = 0; cc < p.n_wchunks; ++cc) {
+      const float* wc = wp + cc * kPartStride;
+      const float m2 = wc[0];
+      const float f2 = m2 == kNegInf ? 0.f : exp2f(m2 - Mx);
+      den = fmaf(f2, wc[1], den);
+      num = fmaf(f2, wc[2 + tid], num);
+    }
+    dst[tid] = den > 0.f ? num / den : 0.f;
   }
 }
 
 template <int G>
 int launch_decode(bool int2, const SplitParams& sp, const uint16_t* r_k, int batch, hipStream_t s) {
-  // INT2: at most 8 query heads per workgroup (register budget of the MFMA
-  // tiles), and the 4-head instantiation for G < 4 masking the missing heads
-  constexpr int GW = G > 8 ? 8 : (G < 4 ? 4 : G);
-  SplitParams p2 = sp;
   if (int2) {
-    p2.gw = G < GW ? G : GW;
-    p2.gsub = G / p2.gw;
-    prep_q_kernel<G><<<dim3(batch, sp.hkv), 256, 0, s>>>(r_k, sp.q, const_cast<float*>(sp.qsum),
-                                                         const_cast<int*>(sp.qop), sp.hq, sp.hkv);
+    // z = 0: rotated query and its MFMA operands, the tile prefix; z > 0: the bf16 window chunks
+    prep_kernel<G><<<dim3(batch, sp.hkv, 1 + sp.n_wchunks), 256, 0, s>>>(sp, r_k);
     if (hipGetLastError() != hipSuccess) return OSCAR_EHIP;
   }
   int slot = -1;
   timing_record_begin(s, int2 ? 1 : 2, &slot);
-  if (int2)  // a leading z slab: one workgroup per (sequence, KV head, head subset) takes the bf16 window
-    int2_split_kernel<GW><<<dim3(sp.n_splits > batch ? sp.n_splits : batch, sp.hkv * p2.gsub, batch + 1), 256, 0, s>>>(p2);
-  else
+  if (int2) {
+    constexpr int GW = G > 8 ? 8 : (G < 4 ? 4 : G);
+    int2_split_kernel<GW><<<sp.n_wg, 256, 0, s>>>(sp);
+  } else {
     bf16_split_kernel<G><<<dim3(sp.n_splits, sp.hkv, batch), 256, 0, s>>>(sp);
+  }
   if (hipGetLastError() != hipSuccess) return OSCAR_EHIP;
   timing_record_end(s, slot);
   merge_kernel<<<dim3(sp.hq, batch), 256, 0, s>>>(sp, G);
@@ -1015,9 +1109,10 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   if (int2 && shape->window > 0 && (!win_k || !win_v)) return OSCAR_EINVAL;
   if (!int2 && !kv_pool) return OSCAR_EINVAL;
   if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * kPage) return OSCAR_ENOSPACE;
-  const SplitPlan plan = plan_splits(batch, shape->n_kv_heads, shape->n_q_heads / shape->n_kv_heads, max_seq_len,
-                                     device_cu_count());
-  const WorkspaceLayout wl = workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads, plan);
+  const int gqa = shape->n_q_heads / shape->n_kv_heads;
+  const int n_cu = device_cu_count();
+  const SplitPlan plan = plan_splits(batch, shape->n_kv_heads, gqa, max_seq_len, n_cu);
+  const WorkspaceLayout wl = workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads, shape->window, plan, n_cu);
   if (workspace_bytes < wl.total) return OSCAR_ENOSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return OSCAR_EINVAL;
 
@@ -1035,6 +1130,7 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   sp.win_v = win_v;
   sp.part = reinterpret_cast<float*>(ws + wl.part);
   sp.wpart = reinterpret_cast<float*>(ws + wl.wpart);
+  sp.tile_prefix = reinterpret_cast<int*>(ws + wl.tile_prefix);
   sp.out = out;
   sp.n_pages = n_pages;
   sp.batch = batch;
@@ -1043,10 +1139,15 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   sp.max_pages = max_pages_per_seq;
   sp.max_len = max_seq_len;
   sp.window = int2 ? shape->window : 0;
+  sp.n_wchunks = (sp.window + kWinChunk - 1) / kWinChunk;
   sp.split = plan.split;
   sp.n_splits = plan.n_splits;
-  sp.gsub = 1;
-  sp.gw = shape->n_q_heads / shape->n_kv_heads;
+  // INT2: at most 8 query heads per merge unit (register budget of the MFMA
+  // tiles); G < 4 runs the 4-head instantiation masking the missing heads
+  sp.gw = int2 ? (gqa > 8 ? 8 : gqa) : gqa;
+  sp.gsub = gqa / sp.gw;
+  sp.n_wg = int2 ? split_wg_count(gqa, n_cu) : 0;
+  sp.hw = split_heads_per_wg(shape->n_kv_heads);
   sp.scale_log2 = kLog2e / sqrtf((float)kD);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (shape->n_q_heads / shape->n_kv_heads) {
@@ -1101,9 +1202,12 @@ __global__ __launch_bounds__(256) void bf16_append_kernel(const uint16_t* __rest
 extern "C" size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int32_t max_seq_len) {
   using namespace oscar;
   if (check_shape(shape) != OSCAR_OK || batch < 1 || max_seq_len < 1) return 0;
-  return workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads,
+  const int n_cu = device_cu_count();
+  return workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads, shape->window,
                           plan_splits(batch, shape->n_kv_heads, shape->n_q_heads / shape->n_kv_heads, max_seq_len,
-                                      device_cu_count())).total;
+                                      n_cu),
+                          n_cu)
+      .total;
 }
 
 extern "C" int oscar_decode_attn(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,

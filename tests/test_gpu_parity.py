@@ -210,6 +210,7 @@ def run_decode(K, s, rk, rv, q, bt, pool, wk, wv, max_len=None):
     (1, [515], 128, 16),               # G = 2
     (1, [260, 1030], 128, 128),        # G = 16
     (1, [4100, 2500, 16], 128, 32),    # longer, splits of 256+ tokens
+    (1, [1500, 200, 333], 300, 32),    # window of 10 chunks, the last one partial; n < W
 ])
 def test_decode_small(K, cfg, lens, window, hq):
     s = make_spec(cfg, lens, window, hq)
@@ -218,6 +219,19 @@ def test_decode_small(K, cfg, lens, window, hq):
     want = ref.decode_ref(rkf, rvf, q, s.seq_lens, bt, pool, wk, wv, window)
     err = P.attn_rel_err(got, want)
     log(f"decode lens={lens} W={window} Hq={hq}: max rel err {err.max():.3e}")
+    assert np.isfinite(got).all()
+    assert err.max() <= P.ATTN_TOL
+
+
+@pytest.mark.parametrize("hkv,hq", [(1, 4), (2, 8), (4, 16), (6, 24), (2, 2)])
+def test_decode_kv_head_counts(K, hkv, hq):
+    """KV head counts that give 1, 2 or 4 heads per split workgroup, and their groups."""
+    s = make_spec(1, [1400, 531], 128, hq, hkv=hkv)
+    rk, rv, rkf, rvf, bt, pool, wk, wv, q = oracle_cache(s)
+    got = run_decode(K, s, rk, rv, q, bt, pool, wk, wv)
+    want = ref.decode_ref(rkf, rvf, q, s.seq_lens, bt, pool, wk, wv, 128)
+    err = P.attn_rel_err(got, want)
+    log(f"decode Hkv={hkv} Hq={hq}: max rel err {err.max():.3e}")
     assert np.isfinite(got).all()
     assert err.max() <= P.ATTN_TOL
 
