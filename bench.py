@@ -148,17 +148,21 @@ def main():
         K.oscar_bf16_decode_attn(shape, q, lensd, nmax, btd, kvp[l], out, ws)
 
     def timed(step, kind):
+        """Wall time per step over the timed steps (no instrumentation), then the
+        same steps again with HIP events around the split kernel for its duration."""
         for i in range(args.warmup):
             step(i)
-        torch.cuda.synchronize()
-        cap = 4 * args.steps + 8
-        K.oscar_timing_begin(cap)
         torch.cuda.synchronize()
         t = time.perf_counter()
         for i in range(args.steps):
             step(args.warmup + i)
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t) / args.steps
+        cap = 4 * args.steps + 8
+        K.oscar_timing_begin(cap)
+        for i in range(args.steps):
+            step(args.warmup + i)
+        torch.cuda.synchronize()
         ms, kinds = K.oscar_timing_end(cap)
         kern = [m for m, k in zip(ms, kinds) if k == kind]
         return dt, float(np.mean(kern)) / 1e3 if kern else None, kern

@@ -81,9 +81,10 @@ inline int split_wg_count(int gqa, int n_cu) { return (n_cu > 0 ? n_cu : 256) * 
 //                       (units = B Hkv / hw x Hq / (Hkv gw); hw KV heads per workgroup)
 //   wpart        float [B][Hq][ceil(W/32)][130]     window chunk partials (m, l, acc[128])
 //   tile_prefix  int   [units + 1]                  first history tile of each merge unit
+//   counter      int   [1]                          window chunks claimed (zeroed by the prep kernel)
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct WorkspaceLayout {
-  size_t qsum, qop, part, wpart, tile_prefix, total;
+  size_t qsum, qop, part, wpart, tile_prefix, counter, total;
 };
 inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int window, const SplitPlan& p,
                                         int n_cu) {
@@ -101,7 +102,8 @@ inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads
   w.wpart = w.part + align256((part_bf16 > part_int2 ? part_bf16 : part_int2) * sizeof(float));
   const size_t n_wchunks = (size_t)((window + kWinChunk - 1) / kWinChunk);
   w.tile_prefix = w.wpart + align256((size_t)batch * n_q_heads * n_wchunks * kPartStride * sizeof(float));
-  w.total = w.tile_prefix + align256((units + 1) * sizeof(int));
+  w.counter = w.tile_prefix + align256((units + 1) * sizeof(int));
+  w.total = w.counter + 256;
   return w;
 }
 
@@ -190,11 +192,19 @@ __device__ __forceinline__ float row_min16(float x) {
   return fminf(x, dpp_f32<kDppMirror>(x));
 }
 
-// max over the 64 lanes of a wave
+__device__ __forceinline__ float sum_rows(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// max / sum over the 64 lanes of a wave (the same bits on every lane)
 __device__ __forceinline__ float wave_max64(float x) {
   x = row_max16(x);
   return max_rows(x);
 }
+__device__ __forceinline__ float wave_sum64(float x) { return sum_rows(row_sum16(x)); }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 

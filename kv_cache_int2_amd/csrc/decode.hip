@@ -121,6 +121,7 @@ struct SplitParams {
   float* part;                // bf16: [B][Hq][n_splits][130]; INT2: [n_wg + units][gw][130] slot partials
   float* wpart;               // INT2: [B][Hq][n_wchunks][130] window chunk partials (unrotated domain)
   int* tile_prefix;           // INT2: [units + 1] first history tile of each unit in the flattened order
+  int* counter;               // INT2: window chunks claimed so far (zeroed by the prep kernel)
   float* out;                 // [B][Hq][128]
   int64_t n_pages;
   int batch, hq, hkv, max_pages, max_len, window, split, n_splits;
@@ -145,17 +146,18 @@ __device__ __forceinline__ int hist_tiles(const SplitParams& p, int b) {
   return (hist + 127) >> 7;
 }
 
-template <int G>
-constexpr int window_smem_bytes() { return (G * kD + kWinChunk * 65 + G * kWinChunk + 4 * G) * 4; }
+template <int GMAX>
+constexpr int window_smem_bytes() { return (GMAX * kD + kWinChunk * 65 + GMAX * kWinChunk + 4 * GMAX) * 4; }
 
 // One 32-token chunk of the bf16 window of (sequence b, KV head h): positions
-// n - w + 32 c .. at ring slots pos % W, unrotated, for the G query heads of h.
+// n - w + 32 c .. at ring slots pos % W, unrotated, for the G <= GMAX query
+// heads of h.
 // Thread (t, part) = (tid / 8, tid % 8) loads dims 16 part .. 16 part + 15 of
 // token t's key and value (all loads issued first); the 8 parts of a score are
 // summed across lanes, V goes through LDS for P V.  Writes (m, l, acc[128]) of
 // the chunk per head; an empty chunk writes m = -inf, l = 0, acc = 0.
-template <int G>
-__device__ void window_chunk(const SplitParams& p, int b, int h, int c, float* sm) {
+template <int GMAX>
+__device__ void window_chunk(const SplitParams& p, int b, int h, int c, int G, float* sm) {
   const int tid = threadIdx.x, wave = tid >> 6;
   const int n = seq_len_of(p, b);
   const int w = n < p.window ? n : p.window;
@@ -173,8 +175,8 @@ __device__ void window_chunk(const SplitParams& p, int b, int h, int c, float* s
   }
   float* qs = sm;                                            // [G][128]
   uint32_t* vs = reinterpret_cast<uint32_t*>(qs + G * kD);   // [32][65] bf16 pairs
-  float* ps = reinterpret_cast<float*>(vs + kWinChunk * 65);  // [G][32]
-  float* red = ps + G * kWinChunk;                            // [4][G]
+  float* ps = reinterpret_cast<float*>(vs + kWinChunk * 65);  // [GMAX][32]
+  float* red = ps + GMAX * kWinChunk;                         // [4][GMAX]
   const int t = tid >> 3, part = tid & 7;
   const bool valid = t < nt;
   uint4 kk[2], vv[2];
@@ -195,9 +197,10 @@ __device__ void window_chunk(const SplitParams& p, int b, int h, int c, float* s
   }
   __syncthreads();
   const uint32_t ku[8] = {kk[0].x, kk[0].y, kk[0].z, kk[0].w, kk[1].x, kk[1].y, kk[1].z, kk[1].w};
-  float sc[G];
+  float sc[GMAX];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+  for (int g = 0; g < GMAX; ++g) {
+    if (g >= G) break;  // uniform
     const float* qg = qs + g * kD + 16 * part;
     float d = 0.f;
 #pragma unroll
@@ -207,12 +210,13 @@ __device__ void window_chunk(const SplitParams& p, int b, int h, int c, float* s
     d += dpp_f32<kDppHalfMirror>(d);  // the 8 parts of token t
     sc[g] = valid ? d * p.scale_log2 : kNegInf;
     const float m = wave_max64(sc[g]);
-    if ((tid & 63) == 0) red[wave * G + g] = m;
+    if ((tid & 63) == 0) red[wave * GMAX + g] = m;
   }
   __syncthreads();
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float m = fmaxf(fmaxf(red[g], red[G + g]), fmaxf(red[2 * G + g], red[3 * G + g]));
+  for (int g = 0; g < GMAX; ++g) {
+    if (g >= G) break;
+    const float m = fmaxf(fmaxf(red[g], red[GMAX + g]), fmaxf(red[2 * GMAX + g], red[3 * GMAX + g]));
     if (part == 0) ps[g * kWinChunk + t] = valid ? exp2f(sc[g] - m) : 0.f;
   }
   __syncthreads();
@@ -228,7 +232,7 @@ __device__ void window_chunk(const SplitParams& p, int b, int h, int c, float* s
     float* dst = dst0 + g * head_stride;
     dst[2 + ch] = acc;
     if (ch == 0) {
-      dst[0] = fmaxf(fmaxf(red[g], red[G + g]), fmaxf(red[2 * G + g], red[3 * G + g]));
+      dst[0] = fmaxf(fmaxf(red[g], red[GMAX + g]), fmaxf(red[2 * GMAX + g], red[3 * GMAX + g]));
       dst[1] = l;
     }
   }
@@ -248,25 +252,24 @@ template <int G>
 __global__ __launch_bounds__(256) void prep_kernel(SplitParams p, const uint16_t* __restrict__ r_k) {
   constexpr int NCB = (G + 3) / 4;  // 4-head operand groups
   constexpr int kQBytes = 2 * G * kD * 4 + G * 4;
-  constexpr int kSmem = kQBytes > window_smem_bytes<G>() ? kQBytes : window_smem_bytes<G>();
-  __shared__ __align__(16) float smem_f[kSmem / 4];
+  __shared__ __align__(16) float smem_f[kQBytes / 4];
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int hq = p.hq, hkv = p.hkv;
-  if (blockIdx.z > 0) {  // chunk z - 1 of the bf16 window of this (sequence, KV head)
-    window_chunk<G>(p, b, h, blockIdx.z - 1, smem_f);
-    return;
-  }
   // first history tile of the units (b, head group, sub) in the flattened order
   // (sequence-major, then KV head group, then head subset), written by the first
   // head of each group; the last group also closes the array
-  if (tid == 0 && h % p.hw == 0) {
+  if (tid == 0 && b == 0 && h == 0) *p.counter = 0;  // the split kernel's window chunk counter
+  if (tid < 64 && h % p.hw == 0) {  // wave 0: tiles of the sequences before b, summed across lanes
     int pb = 0;
-    for (int bb = 0; bb < b; ++bb) pb += hist_tiles(p, bb);
+    for (int bb = tid; bb < b; bb += 64) pb += hist_tiles(p, bb);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) pb += __shfl_xor(pb, o);
     const int tb = hist_tiles(p, b);
     const int hgp = h / p.hw, per_seq = (hkv / p.hw) * p.gsub;
-    for (int sub = 0; sub < p.gsub; ++sub)
+    for (int sub = tid; sub < p.gsub; sub += 64)
       p.tile_prefix[(int64_t)b * per_seq + hgp * p.gsub + sub] = per_seq * pb + (hgp * p.gsub + sub) * tb;
-    if (b == p.batch - 1 && h == hkv - p.hw) p.tile_prefix[(int64_t)p.batch * per_seq] = per_seq * (pb + tb);
+    if (tid == 0 && b == p.batch - 1 && h == hkv - p.hw)
+      p.tile_prefix[(int64_t)p.batch * per_seq] = per_seq * (pb + tb);
   }
   float (*qs)[kD] = reinterpret_cast<float (*)[kD]>(smem_f);
   float (*qraw)[kD] = reinterpret_cast<float (*)[kD]>(smem_f + G * kD);
@@ -319,27 +322,28 @@ __global__ __launch_bounds__(256) void prep_kernel(SplitParams p, const uint16_t
   }
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
-  for (int cb = wave; cb < NCB; cb += 4) {
+  // item (cb, q4): dwords 2 q4 and 2 q4 + 1 of the operand (k-slots 8 q4 .. 8 q4 + 7)
+  for (int it = wave; it < NCB * 4; it += 4) {
+    const int cb = it >> 2, q4 = it & 3;
     const int head = 4 * cb + (lr >> 2), term = lr & 3;
-    int op[9];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) op[i] = 0;
-    op[8] = kScaleOne;
+    int op[2] = {0, 0};
+    int sc = kScaleOne;
     if (head < G) {
       const int E = qexp[head];
-      op[8] = clamp_scale(kScaleOne + E - 7 - 4 * term);
+      sc = clamp_scale(kScaleOne + E - 7 - 4 * term);
 #pragma unroll
-      for (int e = 0; e < 32; e += 2) {
-        const float a = ldexpf(qs[head][k_channel(k_of_fp8(lg, e))], 7 - E);
-        const float c = ldexpf(qs[head][k_channel(k_of_fp8(lg, e + 1))], 7 - E);
+      for (int e = 0; e < 8; e += 2) {
+        const float a = ldexpf(qs[head][k_channel(k_of_fp8(lg, 8 * q4 + e))], 7 - E);
+        const float c = ldexpf(qs[head][k_channel(k_of_fp8(lg, 8 * q4 + e + 1))], 7 - E);
         uint32_t t[4];
         split4(a, c, t);
         op[e >> 2] |= (int)(t[term] << (8 * (e & 3)));
       }
     }
     int* dst = qop + ((((int64_t)b * hkv + h) * NCB + cb) * 64 + lane) * 9;
-#pragma unroll
-    for (int i = 0; i < 9; ++i) dst[i] = op[i];
+    dst[2 * q4] = op[0];
+    dst[2 * q4 + 1] = op[1];
+    if (q4 == 0) dst[8] = sc;
   }
 }
 
@@ -614,37 +618,48 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t
 // Each wave keeps two tiles in flight (the loads of its next tile go out before
 // the current one is computed); two workgroups per CU.
 // ---------------------------------------------------------------------------
+// The last unit u < units with tp[u] <= t (tp[0] = 0 <= t): a 64-way search,
+// one round of loads per factor of 64 in the unit count.
+__device__ __forceinline__ int find_unit(const int* tp, int units, int64_t t) {
+  const int lane = threadIdx.x & 63;
+  int a = 0, n = units;  // the answer lies in [a, a + n)
+  while (n > 1) {
+    const int step = (n + 63) >> 6;
+    const bool ok = lane * step < n && tp[a + lane * step] <= t;
+    const uint64_t m = __ballot(ok);  // lane 0 always set
+    const int last = 63 - __builtin_clzll(m);
+    a += last * step;
+    n = min(step, n - last * step);
+  }
+  return a;
+}
+
 template <int G>
 __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
   constexpr int NRG = (G + 3) / 4;                    // MFMA row groups of 4 heads
   constexpr int kTileBytes = 4 * NRG * 16 * 128;     // per-wave w-term tiles
   constexpr int kCombBytes = 4 * G * kD * 4 + 2 * 4 * G * 4;
-  constexpr int kSmem = kTileBytes > kCombBytes ? kTileBytes : kCombBytes;
+  constexpr int kWinBytes = window_smem_bytes<G == 8 ? 16 : 4>();
+  constexpr int kSmem0 = kTileBytes > kCombBytes ? kTileBytes : kCombBytes;
+  constexpr int kSmem = kSmem0 > kWinBytes ? kSmem0 : kWinBytes;
   __shared__ __align__(16) uint8_t smem[kSmem];
 
+  __shared__ int s_chunk;
   const int hg_per_seq = p.hkv / p.hw;  // KV head groups per sequence
   const int per_seq = hg_per_seq * p.gsub;
   const int units = p.batch * per_seq;
-  const int64_t T = p.tile_prefix[units];
-  const int64_t nw = T < p.n_wg ? T : p.n_wg;  // at least one tile per workgroup
-  if ((int64_t)blockIdx.x >= nw) return;
-  const int64_t lo = T * blockIdx.x / nw, hi = T * (blockIdx.x + 1) / nw;
-  // first unit of the range: the last u with tile_prefix[u] <= lo
-  int u = 0;
-  {
-    int a = 0, c = units;  // tile_prefix[a] <= lo < tile_prefix[c]
-    while (c - a > 1) {
-      const int mid = (a + c) >> 1;
-      if (p.tile_prefix[mid] <= lo) a = mid; else c = mid;
-    }
-    u = a;
-  }
-
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lr = lane & 15;
   const int hv = wave % p.hw, ts = 4 / p.hw, ph = wave / p.hw;  // head in group, tile stride, phase
   uint8_t* wt = smem + wave * (NRG * 2048);
   const int ncb = (p.gw * p.gsub + 3) / 4;
+  // equal shares [T w / nw, T (w + 1) / nw) of the T flattened tiles
+  const int64_t T = p.tile_prefix[units];
+  const int64_t nw = T < p.n_wg ? T : p.n_wg;  // at least one tile per share
+
+  // Tiles [lo, hi) of the flattened order: one partial per unit touched, at slot slot0 + u.
+  auto run_range = [&](int64_t lo, int64_t hi, int64_t slot0) {
+  int u = find_unit(p.tile_prefix, units, lo);
 
   for (; u < units; ++u) {
     const int64_t su = p.tile_prefix[u], su1 = p.tile_prefix[u + 1];
@@ -737,7 +752,7 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
     }
     __syncthreads();
     // slot partial (hv, g): the waves v = hv + hw i, i < ts
-    float* dst0 = p.part + (int64_t)(blockIdx.x + u) * p.hw * p.gw * kPartStride;
+    float* dst0 = p.part + (slot0 + u) * p.hw * p.gw * kPartStride;
     for (int e = tid; e < p.hw * p.gw * kD; e += 256) {
       const int c = e % kD, hg = e / kD, g = hg % p.gw, v0 = hg / p.gw;
       float M = kNegInf;
@@ -756,6 +771,24 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
       }
     }
     __syncthreads();  // smem is the next unit's w-term tiles
+  }
+  };
+
+  if ((int64_t)blockIdx.x < nw) run_range(T * blockIdx.x / nw, T * (blockIdx.x + 1) / nw, blockIdx.x);
+
+  // The bf16 window: its 32-token chunks are claimed one at a time by the
+  // workgroups that are done with their share, so the chunks fill the time the
+  // slower workgroups still need for their tiles.
+  const int n_items = p.batch * p.hkv * p.n_wchunks;
+  for (;;) {
+    __syncthreads();  // smem and s_chunk are free
+    if (tid == 0) s_chunk = atomicAdd(p.counter, 1);
+    __syncthreads();
+    const int c = s_chunk;
+    if (c >= n_items) break;
+    const int bh = c / p.n_wchunks;
+    window_chunk<G == 8 ? 16 : 4>(p, bh / p.hkv, bh % p.hkv, c % p.n_wchunks, p.gw * p.gsub,
+                                   reinterpret_cast<float*>(smem));
   }
 }
 
@@ -939,18 +972,22 @@ __global__ __launch_bounds__(256) void bf16_split_kernel(SplitParams p) {
 // ---------------------------------------------------------------------------
 // merge: one workgroup per (sequence, q head).  Log-sum-exp merge of the split
 // partials; for the INT2 path the un-rotation by R_V^T and the bf16 window's
-// partial, then the normalisation.  Every load the workgroup needs (the split
-// partials, its 128 x 128 R_V tile, the window partial) is issued up front, so
-// the kernel costs about one memory round trip.  A head with no position at
-// all gets zeros.
+// chunk partials, then the normalisation.  All loads of a pass (up to 64
+// partials: lane s of every wave reads partial s's (m, l), thread (c, half)
+// its accumulators of channel c), the R_V tile and the window partials are
+// issued before any of them is used, so a head costs about one memory round
+// trip.  Every wave reduces the (m, l) values itself, so the waves need no
+// exchange until the two halves of the channel sums are added.  A head with
+// no position at all gets zeros.
 // ---------------------------------------------------------------------------
-constexpr int kMergeSplits = 64;  // splits whose accumulators a thread pair holds in registers per pass
+constexpr int kMergePass = 64;  // partials per pass
+constexpr int kMergeWin = 8;    // window chunk partials held in registers
 
 __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
-  const int b = blockIdx.y, hq = blockIdx.x, h = hq / gq, tid = threadIdx.x;
+  const int b = blockIdx.y, hq = blockIdx.x, h = hq / gq, tid = threadIdx.x, lane = tid & 63;
   const bool int2 = p.r_v != nullptr;
-  // partials of this head: INT2 - the slots w + u of the workgroups whose tile
-  // range touches unit u; bf16 - the splits of the sequence
+  // partials of this head, at base + s stride: INT2 - the slots w + u of the
+  // workgroups whose tile range touches unit u; bf16 - the splits of the sequence
   const float* base;
   int ns;
   int64_t stride;
@@ -961,13 +998,13 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
     const int64_t T = p.tile_prefix[p.batch * per_seq];
     const int64_t nw = T < p.n_wg ? T : p.n_wg;
     const int64_t su = p.tile_prefix[u], su1 = p.tile_prefix[u + 1];
-    int w_lo = 0;
+    int64_t w_lo = 0;
     ns = 0;
     if (su1 > su) {  // workgroup of tile t: ((t + 1) nw - 1) / T
-      w_lo = (int)(((su + 1) * nw - 1) / T);
-      ns = (int)((su1 * nw - 1) / T) - w_lo + 1;
+      w_lo = ((su + 1) * nw - 1) / T;
+      ns = (int)((su1 * nw - 1) / T - w_lo + 1);
     }
-    base = p.part + (((int64_t)(w_lo + u) * p.hw + h % p.hw) * p.gw + g) * kPartStride;
+    base = p.part + (((w_lo + u) * p.hw + h % p.hw) * p.gw + g) * kPartStride;
     stride = (int64_t)p.hw * p.gw * kPartStride;
   } else {
     const int n = seq_len_of(p, b);
@@ -976,13 +1013,10 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
     stride = kPartStride;
   }
 
-  __shared__ float fs[kMergeSplits * 2];      // 2^(m_s - M), l_s of the current pass
-  __shared__ float red[256];
-  __shared__ float a1s[kD];
+  __shared__ float red[2][kD];
   __shared__ float o1p[16][kD + 4];
-  __shared__ float Ms, Ls;
 
-  // R_V tile loads first (INT2): thread (cg, jg) takes channels 8cg..8cg+7 of rows 8jg..8jg+7
+  // R_V tile (INT2): thread (cg, jg) takes channels 8cg..8cg+7 of rows 8jg..8jg+7
   const int cg = tid & 15, jg = tid >> 4;
   uint4 rv[8];
   if (int2) {
@@ -990,51 +1024,54 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) rv[j] = *reinterpret_cast<const uint4*>(r + j * kD);
   }
-  // split partials: thread (c, half) sums channel c over the partials s = half, half + 2, ...
-  const int c = tid & 127, half = tid >> 7;
-  float M = kNegInf;
-  for (int s = tid; s < ns; s += 256) M = fmaxf(M, base[s * stride]);
-  M = wave_max64(M);
-  if ((tid & 63) == 0) red[tid >> 6] = M;
-  __syncthreads();
-  if (tid == 0) Ms = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  M = Ms;
-  float acc = 0.f, lsum = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += kMergeSplits) {
-    const int cnt = min(kMergeSplits, ns - s0);
-    __syncthreads();
-    if (tid < cnt) {
-      const float* ps = base + (s0 + tid) * stride;
-      const float m = ps[0];
-      fs[tid] = m == kNegInf ? 0.f : exp2f(m - M);
-      fs[kMergeSplits + tid] = ps[1];
-    }
-    __syncthreads();
-    float x[kMergeSplits / 2];
+  // window chunk partials (INT2): thread c < 128 takes channel c of the first kMergeWin chunks
+  const float* wp = p.wpart + ((int64_t)b * p.hq + hq) * p.n_wchunks * kPartStride;
+  const int nwc = int2 ? p.n_wchunks : 0;
+  float wv[kMergeWin], wm[kMergeWin], wl[kMergeWin];
 #pragma unroll
-    for (int k = 0; k < kMergeSplits / 2; ++k) {
-      const int s = 2 * k + half;
-      x[k] = s < cnt ? base[(s0 + s) * stride + 2 + c] : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < kMergeSplits / 2; ++k) {
-      const int s = 2 * k + half;
-      if (s < cnt) {
-        acc = fmaf(fs[s], x[k], acc);
-        if (c == 0) lsum = fmaf(fs[s], fs[kMergeSplits + s], lsum);
-      }
-    }
+  for (int cc = 0; cc < kMergeWin; ++cc) {
+    const bool ok = cc < nwc;
+    const float* wc = wp + (ok ? cc : 0) * kPartStride;  // in the workspace even when unused
+    const float v = wc[2 + (tid & (kD - 1))], m = wc[0], l = wc[1];
+    wv[cc] = ok ? v : 0.f;
+    wm[cc] = ok ? m : kNegInf;
+    wl[cc] = ok ? l : 0.f;
   }
-  red[tid] = acc;
-  if (c == 0) o1p[0][half] = lsum;
+
+  // split partials: thread (c, half) sums channel c over the partials s = half, half + 2, ...
+  const int c = tid & (kD - 1), half = __builtin_amdgcn_readfirstlane(tid >> 7);
+  float M = kNegInf, acc = 0.f, lsum = 0.f;  // running max and sums (M, lsum the same on every lane)
+  for (int s0 = 0; s0 < ns; s0 += kMergePass) {
+    const int cnt = min(kMergePass, ns - s0);
+    // loads first, at clamped indices (no branch around a load)
+    const float* pl = base + (s0 + min(lane, cnt - 1)) * stride;
+    const float ml_raw = pl[0], ll_raw = pl[1];
+    float x[kMergePass / 2];
+#pragma unroll
+    for (int k = 0; k < kMergePass / 2; ++k) x[k] = base[(s0 + min(2 * k + half, cnt - 1)) * stride + 2 + c];
+    const float ml = lane < cnt ? ml_raw : kNegInf;
+    const float ll = lane < cnt ? ll_raw : 0.f;
+    const float Mn = fmaxf(M, wave_max64(ml));
+    const float alpha = M == kNegInf ? 0.f : exp2f(M - Mn);
+    const float f = ml == kNegInf ? 0.f : exp2f(ml - Mn);  // weight of partial s0 + lane
+    acc *= alpha;
+    lsum = lsum * alpha + wave_sum64(f * ll);
+#pragma unroll
+    for (int k = 0; k < kMergePass / 2; ++k) {
+      const int s = 2 * k + half;
+      // unconditional (weight 0 past cnt, x finite): a guarded FMA would let the
+      // compiler sink the load of x[k] into the guard
+      const float fs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(f), s));
+      acc = fmaf(s < cnt ? fs : 0.f, x[k], acc);
+    }
+    M = Mn;
+  }
+  red[half][c] = acc;
   __syncthreads();
-  if (tid < kD) a1s[tid] = red[tid] + red[tid + 128];
-  if (tid == 0) Ls = o1p[0][0] + o1p[0][1];
-  __syncthreads();
+  const float a1 = red[0][c] + red[1][c];  // channel c (threads c and c + 128 alike)
   float* dst = p.out + ((int64_t)b * p.hq + hq) * kD;
   if (!int2) {
-    if (tid < kD) dst[tid] = Ls > 0.f ? a1s[tid] / Ls : 0.f;
+    if (tid < kD) dst[tid] = lsum > 0.f ? a1 / lsum : 0.f;
     return;
   }
   // o1 = R_V^T a1 from the register tile, partial sums over 8 rows per thread
@@ -1043,7 +1080,7 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
   for (int i = 0; i < 8; ++i) o[i] = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float aj = a1s[8 * jg + j];
+    const float aj = red[0][8 * jg + j] + red[1][8 * jg + j];
     const uint32_t u[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1051,7 +1088,6 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
       o[2 * i + 1] = fmaf(bf16hi(u[i]), aj, o[2 * i + 1]);
     }
   }
-  __syncthreads();  // o1p[0][0..1] (the l sums) were read
 #pragma unroll
   for (int i = 0; i < 8; ++i) o1p[jg][8 * cg + i] = o[i];
   __syncthreads();
@@ -1059,12 +1095,19 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
     float o1 = 0.f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) o1 += o1p[k][tid];
-    const float* wp = p.wpart + ((int64_t)b * p.hq + hq) * p.n_wchunks * kPartStride;
     float Mx = M;
-    for (int cc = 0; cc < p.n_wchunks; ++cc) Mx = fmaxf(Mx, wp[cc * kPartStride]);
+#pragma unroll
+    for (int cc = 0; cc < kMergeWin; ++cc) Mx = fmaxf(Mx, wm[cc]);
+    for (int cc = kMergeWin; cc < nwc; ++cc) Mx = fmaxf(Mx, wp[cc * kPartStride]);
     const float f1 = M == kNegInf ? 0.f : exp2f(M - Mx);
-    float den = f1 * Ls, num = f1 * o1;
-    for (int cc = 0; cc < p.n_wchunks; ++cc) {
+    float den = f1 * lsum, num = f1 * o1;
+#pragma unroll
+    for (int cc = 0; cc < kMergeWin; ++cc) {
+      const float f2 = wm[cc] == kNegInf ? 0.f : exp2f(wm[cc] - Mx);
+      den = fmaf(f2, wl[cc], den);
+      num = fmaf(f2, wv[cc], num);
+    }
+    for (int cc = kMergeWin; cc < nwc; ++cc) {
       const float* wc = wp + cc * kPartStride;
       const float m2 = wc[0];
       const float f2 = m2 == kNegInf ? 0.f : exp2f(m2 - Mx);
@@ -1078,8 +1121,8 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
 template <int G>
 int launch_decode(bool int2, const SplitParams& sp, const uint16_t* r_k, int batch, hipStream_t s) {
   if (int2) {
-    // z = 0: rotated query and its MFMA operands, the tile prefix; z > 0: the bf16 window chunks
-    prep_kernel<G><<<dim3(batch, sp.hkv, 1 + sp.n_wchunks), 256, 0, s>>>(sp, r_k);
+    // rotated query and its MFMA operands, the tile prefix, the window chunk counter
+    prep_kernel<G><<<dim3(batch, sp.hkv), 256, 0, s>>>(sp, r_k);
     if (hipGetLastError() != hipSuccess) return OSCAR_EHIP;
   }
   int slot = -1;
@@ -1131,6 +1174,7 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   sp.part = reinterpret_cast<float*>(ws + wl.part);
   sp.wpart = reinterpret_cast<float*>(ws + wl.wpart);
   sp.tile_prefix = reinterpret_cast<int*>(ws + wl.tile_prefix);
+  sp.counter = reinterpret_cast<int*>(ws + wl.counter);
   sp.out = out;
   sp.n_pages = n_pages;
   sp.batch = batch;
