@@ -77,14 +77,13 @@ inline int split_wg_count(int gqa, int n_cu) { return (n_cu > 0 ? n_cu : 256) * 
 //   qsum         float [B][Hq]                      sum of the rotated query's channels
 //   qop          int   [B][Hkv][ceil(G/4)][64][9]   per-lane fp8 score operand (8 dwords) + E8M0 scale
 //   part         float  bf16 comparator: [B][Hq][n_splits][130] split partials (m, l, acc[128]);
-//                       INT2: [n_wg + units][hw][gw][130] partials of the persistent workgroups
-//                       (units = B Hkv / hw x Hq / (Hkv gw); hw KV heads per workgroup)
+//                       INT2: [n_wg + units][4][gw][130] partials of the persistent workgroups'
+//                       waves (units = B Hkv / hw x Hq / (Hkv gw); hw KV heads per workgroup)
 //   wpart        float [B][Hq][ceil(W/32)][130]     window chunk partials (m, l, acc[128])
 //   tile_prefix  int   [units + 1]                  first history tile of each merge unit
-//   counter      int   [1]                          window chunks claimed (zeroed by the prep kernel)
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct WorkspaceLayout {
-  size_t qsum, qop, part, wpart, tile_prefix, counter, total;
+  size_t qsum, qop, part, wpart, tile_prefix, total;
 };
 inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int window, const SplitPlan& p,
                                         int n_cu) {
@@ -92,9 +91,9 @@ inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads
   const size_t g4 = (size_t)((gqa + 3) / 4);
   const size_t gw = (size_t)(gqa > 8 ? 8 : gqa);
   const size_t units = (size_t)batch * n_q_heads / (gw * (size_t)split_heads_per_wg(n_kv_heads));
-  const size_t hw = (size_t)split_heads_per_wg(n_kv_heads);
   const size_t part_bf16 = (size_t)batch * n_q_heads * p.n_splits * kPartStride;
-  const size_t part_int2 = ((size_t)split_wg_count(gqa, n_cu) * hw * gw + (size_t)batch * n_q_heads) * kPartStride;
+  const size_t n_wg = (size_t)split_wg_count(gqa, n_cu);
+  const size_t part_int2 = (n_wg + units) * 4 * gw * kPartStride;
   WorkspaceLayout w{};
   w.qsum = 0;
   w.qop = w.qsum + align256((size_t)batch * n_q_heads * sizeof(float));
@@ -102,8 +101,7 @@ inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads
   w.wpart = w.part + align256((part_bf16 > part_int2 ? part_bf16 : part_int2) * sizeof(float));
   const size_t n_wchunks = (size_t)((window + kWinChunk - 1) / kWinChunk);
   w.tile_prefix = w.wpart + align256((size_t)batch * n_q_heads * n_wchunks * kPartStride * sizeof(float));
-  w.counter = w.tile_prefix + align256((units + 1) * sizeof(int));
-  w.total = w.counter + 256;
+  w.total = w.tile_prefix + align256((units + 1) * sizeof(int));
   return w;
 }
 

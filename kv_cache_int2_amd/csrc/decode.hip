@@ -121,7 +121,6 @@ struct SplitParams {
   float* part;                // bf16: [B][Hq][n_splits][130]; INT2: [n_wg + units][gw][130] slot partials
   float* wpart;               // INT2: [B][Hq][n_wchunks][130] window chunk partials (unrotated domain)
   int* tile_prefix;           // INT2: [units + 1] first history tile of each unit in the flattened order
-  int* counter;               // INT2: window chunks claimed so far (zeroed by the prep kernel)
   float* out;                 // [B][Hq][128]
   int64_t n_pages;
   int batch, hq, hkv, max_pages, max_len, window, split, n_splits;
@@ -252,13 +251,17 @@ template <int G>
 __global__ __launch_bounds__(256) void prep_kernel(SplitParams p, const uint16_t* __restrict__ r_k) {
   constexpr int NCB = (G + 3) / 4;  // 4-head operand groups
   constexpr int kQBytes = 2 * G * kD * 4 + G * 4;
-  __shared__ __align__(16) float smem_f[kQBytes / 4];
+  constexpr int kSmem = kQBytes > window_smem_bytes<G>() ? kQBytes : window_smem_bytes<G>();
+  __shared__ __align__(16) float smem_f[kSmem / 4];
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int hq = p.hq, hkv = p.hkv;
+  if (blockIdx.z > 0) {  // chunk z - 1 of the bf16 window of this (sequence, KV head)
+    window_chunk<G>(p, b, h, blockIdx.z - 1, G, smem_f);
+    return;
+  }
   // first history tile of the units (b, head group, sub) in the flattened order
   // (sequence-major, then KV head group, then head subset), written by the first
   // head of each group; the last group also closes the array
-  if (tid == 0 && b == 0 && h == 0) *p.counter = 0;  // the split kernel's window chunk counter
   if (tid < 64 && h % p.hw == 0) {  // wave 0: tiles of the sequences before b, summed across lanes
     int pb = 0;
     for (int bb = tid; bb < b; bb += 64) pb += hist_tiles(p, bb);
@@ -599,22 +602,24 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t
 
 
 // ---------------------------------------------------------------------------
-// INT2 history attention on the matrix cores, persistent and balanced.
-// The history tiles (128 tokens) of every merge unit (sequence, KV head, head
-// subset) form one flattened sequence, unit after unit.  Workgroup w of the
-// n_wg resident workgroups takes tiles [w T / n_wg, (w + 1) T / n_wg): every
-// workgroup the same amount of work and one prologue, whatever the lengths.  For
-// each unit its range touches it writes one partial, slot w + u of the unit's
-// heads (unique: consecutive units share at most one workgroup).
+// INT2 history attention on the matrix cores, persistent.
+// The history tiles (128 tokens) of every merge unit (sequence, group of hw
+// adjacent KV heads, head subset) form one flattened sequence, unit after
+// unit.  Workgroup w of the nw resident workgroups takes tiles
+// [w T / nw, (w + 1) T / nw): every workgroup the same amount of work, whatever
+// the lengths.  Each wave works alone (no barrier in the kernel): wave v takes
+// KV head hw g + v % hw of group g and, of the range's tiles of a unit, those
+// congruent to v / hw modulo 4 / hw, and writes one partial per unit its range
+// touches, at (slot w + u, v) - unique, as consecutive ranges share at most one
+// unit.  At 100K context the workgroups' finish times spread over ~25 % of the
+// kernel (CUs stream at different rates); handing steps out dynamically through
+// device-scope atomics (a shared chunk counter, or per-wave claim words with
+// stealing) measured slower than this static split on this part.
 // Lane l = 16 lg + lr:
 //   score MFMA output: head 4 rg + lg, token lr of the page;
 //   value accumulators: head 4 rg + lg, channels 8 lr + n (n = 0..7);
 //   loads per tile: K row bytes 8lg..8lg+7 of token lr and its metadata record
 //   for each of the 8 pages; V words of channels 8lr..8lr+7 for pages 2lg, 2lg+1.
-// A merge unit is (sequence, group of hw adjacent KV heads, head subset): wave
-// v takes KV head hw g + v % hw and, of the range's tiles, those congruent to
-// v / hw modulo 4 / hw.  With hw = 4 the 4 waves read the same pages' 4 adjacent
-// head blocks (one 4.6 KB span per page) instead of 4 scattered 1152-byte blocks.
 // Each wave keeps two tiles in flight (the loads of its next tile go out before
 // the current one is computed); two workgroups per CU.
 // ---------------------------------------------------------------------------
@@ -636,39 +641,45 @@ __device__ __forceinline__ int find_unit(const int* tp, int units, int64_t t) {
 
 template <int G>
 __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
-  constexpr int NRG = (G + 3) / 4;                    // MFMA row groups of 4 heads
-  constexpr int kTileBytes = 4 * NRG * 16 * 128;     // per-wave w-term tiles
-  constexpr int kCombBytes = 4 * G * kD * 4 + 2 * 4 * G * 4;
-  constexpr int kWinBytes = window_smem_bytes<G == 8 ? 16 : 4>();
-  constexpr int kSmem0 = kTileBytes > kCombBytes ? kTileBytes : kCombBytes;
-  constexpr int kSmem = kSmem0 > kWinBytes ? kSmem0 : kWinBytes;
-  __shared__ __align__(16) uint8_t smem[kSmem];
+  constexpr int NRG = (G + 3) / 4;  // MFMA row groups of 4 heads
+  __shared__ __align__(16) uint8_t smem[4 * NRG * 2048];  // per-wave w-term tiles
 
-  __shared__ int s_chunk;
   const int hg_per_seq = p.hkv / p.hw;  // KV head groups per sequence
   const int per_seq = hg_per_seq * p.gsub;
   const int units = p.batch * per_seq;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lr = lane & 15;
-  const int hv = wave % p.hw, ts = 4 / p.hw, ph = wave / p.hw;  // head in group, tile stride, phase
+  const int ts = 4 / p.hw;  // waves sharing a head (tile stride)
   uint8_t* wt = smem + wave * (NRG * 2048);
   const int ncb = (p.gw * p.gsub + 3) / 4;
+  const int64_t wave_part = (int64_t)p.gw * kPartStride;  // floats of one wave's partial
   // equal shares [T w / nw, T (w + 1) / nw) of the T flattened tiles
   const int64_t T = p.tile_prefix[units];
-  const int64_t nw = T < p.n_wg ? T : p.n_wg;  // at least one tile per share
+  const int nw = (int)(T < p.n_wg ? T : p.n_wg);  // at least one tile per share
+  const int w = blockIdx.x;
 
-  // Tiles [lo, hi) of the flattened order: one partial per unit touched, at slot slot0 + u.
-  auto run_range = [&](int64_t lo, int64_t hi, int64_t slot0) {
-  int u = find_unit(p.tile_prefix, units, lo);
-
-  for (; u < units; ++u) {
+  // unit part [a, e) of the tiles [lo, hi) of the flattened order; false past the range
+  auto segment = [&](int u, int64_t lo, int64_t hi, int& a, int& e) {
     const int64_t su = p.tile_prefix[u], su1 = p.tile_prefix[u + 1];
-    if (su >= hi) break;
-    const int j0 = (int)((lo > su ? lo : su) - su), j1 = (int)((hi < su1 ? hi : su1) - su);
-    if (j1 <= j0) continue;
+    if (su >= hi) return false;
+    a = (int)((lo > su ? lo : su) - su);
+    e = (int)((hi < su1 ? hi : su1) - su);
+    return true;
+  };
+  // steps of phase ph in a unit part of tiles [a, e)
+  auto steps_of = [&](int a, int e, int ph) { return ((e - a - ph + ts - 1) / ts + 1) >> 1; };
+
+  // Empty partial (m = -inf, l = 0, acc = 0) of one wave.
+  auto write_empty = [&](float* dst) {
+    for (int i = lane; i < p.gw * kPartStride; i += 64) dst[i] = (i % kPartStride) == 0 ? kNegInf : 0.f;
+  };
+
+  // Steps [0, ns) of phase ph, KV head hv of the group, in tiles [a, e) of
+  // unit u (indices within the unit); the wave's partial to dst.
+  auto run_steps = [&](int u, int a, int e, int ph, int hv, int ns, float* dst) {
     const int b = u / per_seq, hs = u % per_seq, hgp = hs / p.gsub, sub = hs % p.gsub;
-    const int h = hgp * p.hw + hv;                   // this wave's KV head
-    const int hq0 = h * p.gw * p.gsub + sub * p.gw;  // first query head of the unit for this wave
+    const int h = hgp * p.hw + hv;                   // the KV head
+    const int hq0 = h * p.gw * p.gsub + sub * p.gw;  // first query head of the unit
     const int n = seq_len_of(p, b);
     const int t_end = n - (n < p.window ? n : p.window);  // history tokens
 
@@ -694,101 +705,86 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
       for (int nn = 0; nn < 8; ++nn) st.acc[rg][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     // the w-term tile: rows of an unused term (the 4th) must read 0
-    for (int e = lane; e < NRG * 2048 / 16; e += 64) reinterpret_cast<uint4*>(wt)[e] = make_uint4(0, 0, 0, 0);
+    for (int i = lane; i < NRG * 2048 / 16; i += 64) reinterpret_cast<uint4*>(wt)[i] = make_uint4(0, 0, 0, 0);
 
-    // tiles j0 + ph + ts k of the unit, two per iteration
-    const int P0 = 8 * j0, P1 = (t_end - 1) >> 4;
-    const int ntw = (j1 - j0 - ph + ts - 1) / ts;
+    // step s: the wave's tiles 2s and 2s + 1, i.e. tiles a + ph + ts k of the
+    // unit; a step with one tile computes an empty (all-masked) second one
+    const int P0 = 8 * a, P1 = (t_end - 1) >> 4;
+    const int ntw = (e - a - ph + ts - 1) / ts;
     const int* btr = p.block_table + (int64_t)b * p.max_pages;
     auto pbase_of = [&](int k) { return P0 + 8 * (ph + ts * k); };
     TileTable tab = table_ready(p, table_load(btr, P0, P1, ph, ts, 0), P0, P1, ph, ts, 0, ntw);
     int raw_next = table_load(btr, P0, P1, ph, ts, 2);
     if constexpr (NRG > 1) {  // one tile in flight per wave (registers)
-      for (int k = 0; k < ntw; k += 2) {
+      for (int s = 0;; ++s) {
+        const int k = 2 * s;
         Tile t;
         load_tile(p, tab, 0, h, pbase_of(k), t_end, lg, lr, t);
         compute_tile<G, NRG, false>(p, t, pbase_of(k), t_end, lg, lr, qa, qsc, qsr, wt, st);
-        if (k + 1 >= ntw) break;
         load_tile(p, tab, 1, h, pbase_of(k + 1), t_end, lg, lr, t);
         compute_tile<G, NRG, false>(p, t, pbase_of(k + 1), t_end, lg, lr, qa, qsc, qsr, wt, st);
+        if (s + 1 >= ns) break;
         tab = table_ready(p, raw_next, P0, P1, ph, ts, k + 2, ntw);
         raw_next = table_load(btr, P0, P1, ph, ts, k + 4);
       }
     } else {  // two tiles in flight per wave: tile k + 1's loads go out before tile k is computed
       Tile ta, tb;
       load_tile(p, tab, 0, h, pbase_of(0), t_end, lg, lr, ta);
-      for (int k = 0; k < ntw; k += 2) {
-        // past the range (k + 1 == ntw) the tile's entries are empty: it re-reads
-        // page 0's block (cache resident) and is never computed
+      for (int s = 0;; ++s) {
+        const int k = 2 * s;
         load_tile(p, tab, 1, h, pbase_of(k + 1), t_end, lg, lr, tb);
         compute_tile<G, NRG, false>(p, ta, pbase_of(k), t_end, lg, lr, qa, qsc, qsr, wt, st);
-        if (k + 1 >= ntw) break;
-        tab = table_ready(p, raw_next, P0, P1, ph, ts, k + 2, ntw);
+        const bool more = s + 1 < ns;
+        // past the last step the table is empty: tile k + 2 re-reads page 0's
+        // block (cache resident) and is never computed
+        tab = table_ready(p, raw_next, P0, P1, ph, ts, k + 2, more ? ntw : 0);
         raw_next = table_load(btr, P0, P1, ph, ts, k + 4);
         load_tile(p, tab, 0, h, pbase_of(k + 2), t_end, lg, lr, ta);
         compute_tile<G, NRG, false>(p, tb, pbase_of(k + 1), t_end, lg, lr, qa, qsc, qsr, wt, st);
+        if (!more) break;
       }
     }
 
-    // ---- per-wave partial -> LDS -> the unit's slot partials ----
-    __syncthreads();  // every wave is done with its w-term tile before smem is reused
-    float* cacc = reinterpret_cast<float*>(smem);  // [4][G][128]
-    float* cm = cacc + 4 * G * kD;                 // [4][G]
-    float* cl = cm + 4 * G;                        // [4][G]
+    // ---- the wave's partial: lane (lg, lr) holds channels 8 lr .. 8 lr + 7 of head 4 rg + lg ----
+    // (the accumulators are pinned here, with every lane active: otherwise the
+    // last tile's value MFMAs could be sunk into the per-lane store branch)
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.acc[rg][nn][i] = pin(st.acc[rg][nn][i]);
 #pragma unroll
     for (int rg = 0; rg < NRG; ++rg) {
       const float l = row_sum16(st.l_part[rg]), az = row_sum16(st.az_part[rg]);
       const int head = 4 * rg + lg;
       if (head < p.gw) {
+        float* d = dst + head * kPartStride;
 #pragma unroll
-        for (int nn = 0; nn < 8; ++nn)
-          cacc[(wave * G + head) * kD + 8 * lr + nn] =
-              (st.acc[rg][nn][0] + st.acc[rg][nn][1]) + (st.acc[rg][nn][2] + st.acc[rg][nn][3]) + az;
-        if (lr == 0) {
-          cm[wave * G + head] = st.m_run[rg];
-          cl[wave * G + head] = l;
+        for (int nn = 0; nn < 8; nn += 2) {
+          const float x0 = (st.acc[rg][nn][0] + st.acc[rg][nn][1]) + (st.acc[rg][nn][2] + st.acc[rg][nn][3]) + az;
+          const float x1 =
+              (st.acc[rg][nn + 1][0] + st.acc[rg][nn + 1][1]) + (st.acc[rg][nn + 1][2] + st.acc[rg][nn + 1][3]) + az;
+          *reinterpret_cast<float2*>(d + 2 + 8 * lr + nn) = make_float2(x0, x1);
         }
+        if (lr == 0) *reinterpret_cast<float2*>(d) = make_float2(st.m_run[rg], l);
       }
     }
-    __syncthreads();
-    // slot partial (hv, g): the waves v = hv + hw i, i < ts
-    float* dst0 = p.part + (slot0 + u) * p.hw * p.gw * kPartStride;
-    for (int e = tid; e < p.hw * p.gw * kD; e += 256) {
-      const int c = e % kD, hg = e / kD, g = hg % p.gw, v0 = hg / p.gw;
-      float M = kNegInf;
-      for (int v = v0; v < 4; v += p.hw) M = fmaxf(M, cm[v * G + g]);
-      float acc = 0.f, L = 0.f;
-      for (int v = v0; v < 4; v += p.hw) {
-        const float f = cm[v * G + g] == kNegInf ? 0.f : exp2f(cm[v * G + g] - M);
-        acc = fmaf(f, cacc[(v * G + g) * kD + c], acc);
-        L = fmaf(f, cl[v * G + g], L);
-      }
-      float* dst = dst0 + (int64_t)hg * kPartStride;
-      dst[2 + c] = acc;
-      if (c == 0) {
-        dst[0] = M;
-        dst[1] = L;
-      }
-    }
-    __syncthreads();  // smem is the next unit's w-term tiles
-  }
+    __builtin_amdgcn_wave_barrier();
   };
 
-  if ((int64_t)blockIdx.x < nw) run_range(T * blockIdx.x / nw, T * (blockIdx.x + 1) / nw, blockIdx.x);
-
-  // The bf16 window: its 32-token chunks are claimed one at a time by the
-  // workgroups that are done with their share, so the chunks fill the time the
-  // slower workgroups still need for their tiles.
-  const int n_items = p.batch * p.hkv * p.n_wchunks;
-  for (;;) {
-    __syncthreads();  // smem and s_chunk are free
-    if (tid == 0) s_chunk = atomicAdd(p.counter, 1);
-    __syncthreads();
-    const int c = s_chunk;
-    if (c >= n_items) break;
-    const int bh = c / p.n_wchunks;
-    window_chunk<G == 8 ? 16 : 4>(p, bh / p.hkv, bh % p.hkv, c % p.n_wchunks, p.gw * p.gsub,
-                                   reinterpret_cast<float*>(smem));
+  // ---- the workgroup's range: one wave partial per unit it touches, at (w + u, wave) ----
+  if (w < nw) {
+    const int64_t lo = T * w / nw, hi = T * (w + 1) / nw;
+    const int ph = wave / p.hw, hv = wave % p.hw;
+    int a, e;
+    for (int u = find_unit(p.tile_prefix, units, lo); u < units && segment(u, lo, hi, a, e); ++u) {
+      if (e <= a) continue;
+      float* dst = p.part + ((int64_t)(w + u) * 4 + wave) * wave_part;
+      const int nst = steps_of(a, e, ph);
+      if (nst > 0) run_steps(u, a, e, ph, hv, nst, dst);
+      else write_empty(dst);
+    }
   }
 }
 
@@ -986,11 +982,15 @@ constexpr int kMergeWin = 8;    // window chunk partials held in registers
 __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
   const int b = blockIdx.y, hq = blockIdx.x, h = hq / gq, tid = threadIdx.x, lane = tid & 63;
   const bool int2 = p.r_v != nullptr;
-  // partials of this head, at base + s stride: INT2 - the slots w + u of the
-  // workgroups whose tile range touches unit u; bf16 - the splits of the sequence
+  // partials of this head: INT2 - the wave partials (w + u, v) of the ts waves
+  // v of this head in each workgroup w whose tile range touches unit u, at
+  // p.part + ((4 (w + u) + v) gw + g) 130 (partial s: workgroup w_lo + s / ts,
+  // wave hv + hw (s % ts)); bf16 - the splits of the sequence (partial s at
+  // base + s 130)
   const float* base;
   int ns;
   int64_t stride;
+  int ts = 1, hw = 1, w0 = 0;
   if (int2) {
     const int jq = hq % gq, sub = jq / p.gw, g = jq % p.gw;
     const int per_seq = (p.hkv / p.hw) * p.gsub;
@@ -1004,8 +1004,12 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
       w_lo = ((su + 1) * nw - 1) / T;
       ns = (int)((su1 * nw - 1) / T - w_lo + 1);
     }
-    base = p.part + (((w_lo + u) * p.hw + h % p.hw) * p.gw + g) * kPartStride;
-    stride = (int64_t)p.hw * p.gw * kPartStride;
+    hw = p.hw;
+    ts = 4 / hw;
+    w0 = (int)(w_lo + u);
+    base = p.part + ((int64_t)h % hw * p.gw + g) * kPartStride;
+    stride = (int64_t)p.gw * kPartStride;
+    ns *= ts;
   } else {
     const int n = seq_len_of(p, b);
     ns = (n + p.split - 1) / p.split;
@@ -1044,11 +1048,12 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
   for (int s0 = 0; s0 < ns; s0 += kMergePass) {
     const int cnt = min(kMergePass, ns - s0);
     // loads first, at clamped indices (no branch around a load)
-    const float* pl = base + (s0 + min(lane, cnt - 1)) * stride;
+    auto part_at = [&](int s) { return base + (int64_t)(int2 ? 4 * (w0 + s / ts) + hw * (s % ts) : s) * stride; };
+    const float* pl = part_at(s0 + min(lane, cnt - 1));
     const float ml_raw = pl[0], ll_raw = pl[1];
     float x[kMergePass / 2];
 #pragma unroll
-    for (int k = 0; k < kMergePass / 2; ++k) x[k] = base[(s0 + min(2 * k + half, cnt - 1)) * stride + 2 + c];
+    for (int k = 0; k < kMergePass / 2; ++k) x[k] = part_at(s0 + min(2 * k + half, cnt - 1))[2 + c];
     const float ml = lane < cnt ? ml_raw : kNegInf;
     const float ll = lane < cnt ? ll_raw : 0.f;
     const float Mn = fmaxf(M, wave_max64(ml));
@@ -1121,8 +1126,8 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
 template <int G>
 int launch_decode(bool int2, const SplitParams& sp, const uint16_t* r_k, int batch, hipStream_t s) {
   if (int2) {
-    // rotated query and its MFMA operands, the tile prefix, the window chunk counter
-    prep_kernel<G><<<dim3(batch, sp.hkv), 256, 0, s>>>(sp, r_k);
+    // z = 0: rotated query and its MFMA operands, the tile prefix; z > 0: the bf16 window chunks
+    prep_kernel<G><<<dim3(batch, sp.hkv, 1 + sp.n_wchunks), 256, 0, s>>>(sp, r_k);
     if (hipGetLastError() != hipSuccess) return OSCAR_EHIP;
   }
   int slot = -1;
@@ -1174,7 +1179,6 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   sp.part = reinterpret_cast<float*>(ws + wl.part);
   sp.wpart = reinterpret_cast<float*>(ws + wl.wpart);
   sp.tile_prefix = reinterpret_cast<int*>(ws + wl.tile_prefix);
-  sp.counter = reinterpret_cast<int*>(ws + wl.counter);
   sp.out = out;
   sp.n_pages = n_pages;
   sp.batch = batch;
