@@ -159,10 +159,17 @@ def main():
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t) / args.steps
         cap = 4 * args.steps + 8
+        # ~3 ms of copies queued first: the host has enqueued every step before
+        # the GPU reaches them, so no launch gap of the host falls between an
+        # event and the kernel it brackets
+        busy = torch.empty(2, 512 << 20, dtype=torch.uint8, device=dev)
+        for _ in range(12):
+            K.oscar_hbm_copy(busy[0], busy[1])
         K.oscar_timing_begin(cap)
         for i in range(args.steps):
             step(args.warmup + i)
         torch.cuda.synchronize()
+        del busy
         ms, kinds = K.oscar_timing_end(cap)
         kern = [m for m, k in zip(ms, kinds) if k == kind]
         return dt, float(np.mean(kern)) / 1e3 if kern else None, kern
