@@ -151,7 +151,8 @@ size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int
  *   p = exp(s - max s); query head j uses KV head j / G.
  * Arguments (device memory):
  *   r_k, r_v bf16 [n_kv_heads][128][128]; q bf16 [batch][n_q_heads][128]
- *   seq_lens int32 [batch], each in [1, max_seq_len] (host max_seq_len)
+ *   seq_lens int32 [batch], each in [0, max_seq_len] (host max_seq_len >= 0);
+ *     a sequence of length 0 has no position to attend and gets out = 0
  *   block_table, pool, win_k, win_v as for oscar_quantize_append
  *   out float [batch][n_q_heads][128]
  *   workspace >= oscar_decode_workspace_bytes(shape, batch, max_seq_len) bytes

@@ -1151,7 +1151,7 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
                   float* out, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_shape(shape);
   if (st != OSCAR_OK) return st;
-  if (batch < 1 || max_seq_len < 1 || max_pages_per_seq < 1 || n_pages < 1) return OSCAR_EINVAL;
+  if (batch < 1 || max_seq_len < 0 || max_pages_per_seq < 1 || n_pages < 1) return OSCAR_EINVAL;
   if (!q || !seq_lens || !block_table || !out || !workspace) return OSCAR_EINVAL;
   if (int2 && (!r_k || !r_v || !pool)) return OSCAR_EINVAL;
   if (int2 && shape->window > 0 && (!win_k || !win_v)) return OSCAR_EINVAL;
@@ -1249,7 +1249,7 @@ __global__ __launch_bounds__(256) void bf16_append_kernel(const uint16_t* __rest
 
 extern "C" size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int32_t max_seq_len) {
   using namespace oscar;
-  if (check_shape(shape) != OSCAR_OK || batch < 1 || max_seq_len < 1) return 0;
+  if (check_shape(shape) != OSCAR_OK || batch < 1 || max_seq_len < 0) return 0;
   const int n_cu = device_cu_count();
   return workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads, shape->window,
                           plan_splits(batch, shape->n_kv_heads, shape->n_q_heads / shape->n_kv_heads, max_seq_len,

@@ -354,6 +354,9 @@ def decode_ref(r_k, r_v, q_bits, seq_lens, block_table, pool, win_k, win_v,
         pairs = [(b, h) for b in range(bsz) for h in range(hkv)]
     for b, h in pairs:
         n = int(seq_lens[b])
+        if n == 0:  # no position to attend: the output is zero (a reading; softmax over nothing is undefined)
+            out[b, h * g:(h + 1) * g] = 0.0
+            continue
         w = min(n, window)
         hist = n - w
         kh, vh = read_history(pool, block_table[b], hist, h) if hist > 0 else (np.zeros((0, d)), np.zeros((0, d)))

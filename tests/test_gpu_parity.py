@@ -211,6 +211,9 @@ def run_decode(K, s, rk, rv, q, bt, pool, wk, wv, max_len=None):
     (1, [260, 1030], 128, 128),        # G = 16
     (1, [4100, 2500, 16], 128, 32),    # longer, splits of 256+ tokens
     (1, [1500, 200, 333], 300, 32),    # window of 10 chunks, the last one partial; n < W
+    (1, [0, 700], 128, 32),            # an empty sequence in the batch
+    (1, [2000, 1030, 1024, 5], 1024, 32),  # the largest window
+    (1, [1280], 128, 32),              # history of exactly 9 tiles
 ])
 def test_decode_small(K, cfg, lens, window, hq):
     s = make_spec(cfg, lens, window, hq)
@@ -234,6 +237,17 @@ def test_decode_kv_head_counts(K, hkv, hq):
     log(f"decode Hkv={hkv} Hq={hq}: max rel err {err.max():.3e}")
     assert np.isfinite(got).all()
     assert err.max() <= P.ATTN_TOL
+
+
+def test_decode_every_sequence_empty(K):
+    """seq_lens all 0 (and max_seq_len 0) over an existing cache: zeros."""
+    s = make_spec(1, [40, 300])
+    rk, rv, rkf, rvf, bt, pool, wk, wv, q = oracle_cache(s)
+    s.seq_lens = np.zeros(2, np.int32)
+    got = run_decode(K, s, rk, rv, q, bt, pool, wk, wv, max_len=0)
+    want = ref.decode_ref(rkf, rvf, q, s.seq_lens, bt, pool, wk, wv, 128)
+    assert np.array_equal(want, np.zeros_like(want))
+    assert np.array_equal(got, np.zeros_like(got))
 
 
 def test_decode_max_len_above_actual(K):

@@ -110,6 +110,17 @@ def test_decode_single_int2_token(rng):
             assert np.allclose(got[0, h * 4 + j], rv[h].T @ vh[0], atol=1e-13)
 
 
+def test_decode_empty_sequence_is_zero_and_leaves_others_alone(rng):
+    """A sequence of length 0 has no position to attend: its output is zero
+    (reading S19), and the other sequences of the batch are unaffected."""
+    s, bt, pool, wk, wv, rk, rv, kv, q = build(rng, (30, 1), 8)
+    full = ref.decode_ref(rk, rv, q, s.seq_lens, bt, pool, wk, wv, 8)
+    lens0 = np.array([30, 0], np.int32)
+    got = ref.decode_ref(rk, rv, q, lens0, bt, pool, wk, wv, 8)
+    assert np.array_equal(got[1], np.zeros_like(got[1]))
+    assert np.array_equal(got[0], full[0])
+
+
 def test_decode_identical_keys_average_values(rng):
     s = wl.spec(1, batch=1)
     s.seq_lens = np.array([50], np.int32)
