@@ -75,6 +75,9 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the prefill-ingest (append) leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="decode time the oracle baseline spends")
+    ap.add_argument("--quality", action="store_true",
+                    help="instead of the benchmark: cache quality of the OSCAR, Hadamard-only and identity "
+                         "rotations through the same kernels (one JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -87,6 +90,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.quality:
+        quality_leg(K, wl, torch)
+        return
     s = wl.spec(args.config)
     B, HQ, HKV, W = s.batch, s.n_q_heads, s.n_kv_heads, s.window
     lens = s.seq_lens.astype(np.int64)
@@ -304,6 +310,23 @@ def append_leg(K, torch, dev, shape, rkd, rvd, args):
             "avg_launch_ms": t * 1e3, "algorithmic_bytes": byts, "achieved_gbs": byts / t / 1e9,
             "frac_hbm": byts / t / 1e9 / PEAK_HBM_GBS, "rotation_tflops": flops / t / 1e12,
             "mfma_frac_bf16": flops / t / 1e12 / 2500.0}
+
+
+def quality_leg(K, wl, torch):
+    """Quality of the three rotations on the 2048-token workload and on a
+    shrunk copy of the 32K-context one (same distributions)."""
+    from kv_cache_int2_amd import quality
+
+    res = {}
+    for label, s in (("B1_n2048", wl.spec(1)), ("B2_n8192", wl.spec(2, batch=2, seq_len=8192))):
+        shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window)
+        q_cal, k_cal, v_cal = wl.calibration_set(s)
+        rot = quality.rotations(shape, q_cal, k_cal, v_cal, K.oscar_calibrate)
+        t = time.perf_counter()
+        res[label] = quality.measure(K, s, rot, wl, torch)
+        log(f"quality {label}: {time.perf_counter() - t:.1f}s " +
+            " | ".join(f"{k}: " + ", ".join(f"{m} {v:.3g}" for m, v in r.items()) for k, r in res[label].items()))
+    print(json.dumps({"quality": res, "data": "synthetic (seeded Gaussian K/V, 4 key outlier channels x20)"}))
 
 
 def cpu_baseline(s, rk_bits, rv_bits, target_s: float, max_units: int = 3):
