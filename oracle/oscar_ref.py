@@ -273,15 +273,17 @@ def _put_fp16(block, field, slot, bits):
 
 
 def append_ref(r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,
-               pool, win_k, win_v, window: int):
-    """Write each token into the paged INT2 cache and, if recent, the bf16 window.
+               pool, win_k, win_v, window: int, n_sink: int = 0):
+    """Write each token into the paged INT2 cache and, if recent or a sink, the
+    bf16 ring.
 
     r_k, r_v: fp64 [Hkv][d][d] (bf16 values as data); k_new, v_new: bf16 bits
-    [T][Hkv][d]; pool uint8 [n_pages][Hkv][1152] and windows bf16 bits
-    [B][W][Hkv][d] are updated in place.  Token i lands in page
-    block_table[b][pos // 16], slot pos % 16; its raw bf16 k/v also go to window
-    slot pos % W when pos >= seq_len_after[b] - W  [P2 «OSCAR има значение…»,
-    P4 «OSCAR: figyelem-tudatos…»: recent tokens stay bf16, history is INT2]."""
+    [T][Hkv][d]; pool uint8 [n_pages][Hkv][1152] and rings bf16 bits
+    [B][W + n_sink][Hkv][d] are updated in place.  Token i lands in page
+    block_table[b][pos // 16], slot pos % 16; its raw bf16 k/v also go to ring
+    row pos % W when pos >= seq_len_after[b] - W, and to ring row W + pos when
+    pos < n_sink  [P2 «OSCAR има значение…», P4 «OSCAR: figyelem-tudatos…»:
+    sink and recent tokens stay bf16, history is INT2]."""
     k_new = np.asarray(k_new)
     hkv = k_new.shape[1]
     # x'[t, h] = R[h] x[t, h]
@@ -310,6 +312,9 @@ def append_ref(r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,
         if window > 0 and p >= int(seq_len_after[b]) - window:
             win_k[b, p % window] = k_new[i]
             win_v[b, p % window] = v_new[i]
+        if p < n_sink:
+            win_k[b, window + p] = k_new[i]
+            win_v[b, window + p] = v_new[i]
 
 
 def read_history(pool, block_table_row, hist: int, h: int):
@@ -338,13 +343,14 @@ def read_history(pool, block_table_row, hist: int, h: int):
 # ---------------------------------------------------------------------------
 
 def decode_ref(r_k, r_v, q_bits, seq_lens, block_table, pool, win_k, win_v,
-               window: int, pairs=None):
+               window: int, pairs=None, n_sink: int = 0):
     """Softmax attention of one query token per (sequence, q head) over the
-    dequantised cache, fp64.  Positions [0, n - w) come from the INT2 pages
-    (rotated domain: scores q'.k'/sqrt d with q' = R_K q; values un-rotated by
-    R_V^T), positions [n - w, n), w = min(n, W), from the bf16 window (plain
-    domain).  ``pairs``: iterable of (b, kv_head) to compute (default all);
-    other outputs are NaN."""
+    dequantised cache, fp64.  With w = min(n, W) and s = min(n_sink, n - w):
+    positions [0, s) come from the bf16 sink rows W + pos of the ring, [s, n - w)
+    from the INT2 pages (rotated domain: scores q'.k'/sqrt d with q' = R_K q;
+    values un-rotated by R_V^T), [n - w, n) from the bf16 window rows pos % W
+    (sink and window in the plain domain).  ``pairs``: iterable of (b, kv_head)
+    to compute (default all); other outputs are NaN."""
     q = bf16_to_f64(q_bits)
     bsz, hq, d = q.shape
     hkv = np.shape(r_k)[0]
@@ -359,17 +365,21 @@ def decode_ref(r_k, r_v, q_bits, seq_lens, block_table, pool, win_k, win_v,
             continue
         w = min(n, window)
         hist = n - w
+        ns = min(n_sink, hist)
         kh, vh = read_history(pool, block_table[b], hist, h) if hist > 0 else (np.zeros((0, d)), np.zeros((0, d)))
-        wpos = np.arange(hist, n) % window if w > 0 else np.zeros(0, dtype=np.int64)
-        kw = bf16_to_f64(win_k[b, wpos, h]) if w > 0 else np.zeros((0, d))
-        vw = bf16_to_f64(win_v[b, wpos, h]) if w > 0 else np.zeros((0, d))
+        kh, vh = kh[ns:], vh[ns:]
+        # plain-domain rows: sinks (rows W + pos), then the window (rows pos % W)
+        rows = np.concatenate([window + np.arange(ns), np.arange(hist, n) % max(window, 1)]).astype(np.int64)
+        kw = bf16_to_f64(win_k[b, rows, h]) if rows.size else np.zeros((0, d))
+        vw = bf16_to_f64(win_v[b, rows, h]) if rows.size else np.zeros((0, d))
+        nh = hist - ns
         for j in range(g):
             qq = q[b, h * g + j]
             qr = np.asarray(r_k[h], np.float64) @ qq
             s = np.concatenate([kh @ qr, kw @ qq]) / math.sqrt(d)
             p = np.exp(s - s.max())
-            o_rot = p[:hist] @ vh
-            o = np.asarray(r_v[h], np.float64).T @ o_rot + p[hist:] @ vw
+            o_rot = p[:nh] @ vh
+            o = np.asarray(r_v[h], np.float64).T @ o_rot + p[nh:] @ vw
             out[b, h * g + j] = o / p.sum()
     return out
 
@@ -448,39 +458,44 @@ def bf16_kv_bytes_per_token(n_layers: int, n_kv_heads: int, d: int) -> int:
     return 2 * n_layers * n_kv_heads * d * 2
 
 
-def decode_direct_ref(r_k, r_v, q_bits, k_bits, v_bits, n: int, window: int, kv_head: int):
+def decode_direct_ref(r_k, r_v, q_bits, k_bits, v_bits, n: int, window: int, kv_head: int,
+                      n_sink: int = 0):
     """Decode of one (sequence, KV head) straight from its token sequence, with
-    no pool or ring: the history positions [0, n - w) are encoded with
-    ``quantize`` (the cache's content by definition), the last w = min(n, W)
-    positions are the raw bf16 tokens.  Same attention as ``decode_ref``.
-    q_bits [G][d] (the G query heads of this KV head); k_bits, v_bits [>= n][d].
-    Returns fp64 [G][d]."""
+    no pool or ring: with w = min(n, W) and s = min(n_sink, n - w), positions
+    [s, n - w) are encoded with ``quantize`` (the cache's content by definition),
+    positions [0, s) and the last w are the raw bf16 tokens.  Same attention as
+    ``decode_ref``.  q_bits [G][d] (the G query heads of this KV head); k_bits,
+    v_bits [>= n][d].  Returns fp64 [G][d]."""
     d = D
     w = min(n, window)
     hist = n - w
+    ns = min(n_sink, hist)
     rk = np.asarray(r_k[kv_head], np.float64)
     rv = np.asarray(r_v[kv_head], np.float64)
     kx = bf16_to_f64(np.asarray(k_bits)[:n])
     vx = bf16_to_f64(np.asarray(v_bits)[:n])
-    ck, sk, zk, _ = quantize(rotate(rk, kx[:hist]))
-    cv, sv, zv, _ = quantize(rotate(rv, vx[:hist]))
+    ck, sk, zk, _ = quantize(rotate(rk, kx[ns:hist]))
+    cv, sv, zv, _ = quantize(rotate(rv, vx[ns:hist]))
     kh = zk[:, None] + ck * sk[:, None]
     vh = zv[:, None] + cv * sv[:, None]
+    plain = np.r_[0:ns, hist:n]
     q = bf16_to_f64(q_bits)
     out = np.empty((q.shape[0], d))
     for j in range(q.shape[0]):
-        s = np.concatenate([kh @ (rk @ q[j]), kx[hist:] @ q[j]]) / math.sqrt(d)
+        s = np.concatenate([kh @ (rk @ q[j]), kx[plain] @ q[j]]) / math.sqrt(d)
         p = np.exp(s - s.max())
-        out[j] = (rv.T @ (p[:hist] @ vh) + p[hist:] @ vx[hist:]) / p.sum()
+        nh = hist - ns
+        out[j] = (rv.T @ (p[:nh] @ vh) + p[nh:] @ vx[plain]) / p.sum()
     return out
 
 
-def append_sequence_ref(r_k, r_v, k_bits, v_bits, block_row, pool, win_k, win_v, window: int):
+def append_sequence_ref(r_k, r_v, k_bits, v_bits, block_row, pool, win_k, win_v, window: int,
+                        n_sink: int = 0):
     """Bulk form of ``append_ref`` for positions 0..n-1 of one sequence appended
     in order (seq_len_after = n): whole pages are packed at once.  Produces the
     same bytes as ``append_ref`` (pinned by a test).  k_bits, v_bits [n][Hkv][d];
     block_row int32 [max_pages]; pool [n_pages][Hkv][1152]; win_k, win_v
-    [W][Hkv][d] (this sequence's ring)."""
+    [W + n_sink][Hkv][d] (this sequence's ring)."""
     k_bits = np.asarray(k_bits)
     n, hkv, _ = k_bits.shape
     kr = np.empty((n, hkv, D))
@@ -520,3 +535,6 @@ def append_sequence_ref(r_k, r_v, k_bits, v_bits, block_row, pool, win_k, win_v,
         for p in range(max(0, n - window), n):
             win_k[p % window] = k_bits[p]
             win_v[p % window] = v_bits[p]
+    for p in range(min(n_sink, n)):
+        win_k[window + p] = k_bits[p]
+        win_v[window + p] = v_bits[p]

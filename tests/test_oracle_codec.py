@@ -112,13 +112,13 @@ def test_pack_bit_positions_by_hand():
     assert blk[ref.V_CODES + 28] == 0x80  # little-endian word 7, low byte
 
 
-def small_cache(cfg=1, batch=2, lens=(40, 23), window=16, seed=0):
+def small_cache(cfg=1, batch=2, lens=(40, 23), window=16, seed=0, n_sink=0):
     s = wl.spec(cfg, seed=seed, batch=batch)
     s.seq_lens = np.asarray(lens, dtype=np.int32)
     s.window = window
     bt, n_pages = wl.page_table(s)
     pool = np.zeros((n_pages, s.n_kv_heads, ref.BLOCK), dtype=np.uint8)
-    win_k = np.zeros((batch, max(window, 1), s.n_kv_heads, 128), dtype=np.uint16)
+    win_k = np.zeros((batch, max(window + n_sink, 1), s.n_kv_heads, 128), dtype=np.uint16)
     win_v = np.zeros_like(win_k)
     return s, bt, pool, win_k, win_v
 
@@ -176,23 +176,23 @@ def test_append_ref_keeps_other_slots_and_skips_old_window_positions(rng):
 
 def test_bulk_sequence_append_equals_per_token_append(rng):
     """append_sequence_ref is byte-identical to append_ref for an in-order prefill."""
-    for n, window in ((37, 16), (64, 128), (1, 4)):
-        s, bt, pool, win_k, win_v = small_cache(batch=1, lens=(n,), window=window)
+    for n, window, n_sink in ((37, 16, 0), (64, 128, 0), (1, 4, 0), (37, 16, 5), (20, 0, 40)):
+        s, bt, pool, win_k, win_v = small_cache(batch=1, lens=(n,), window=window, n_sink=n_sink)
         rk, rv = random_rotations(rng, s.n_kv_heads)
         k, v, si, pos = wl.prefill_tokens(s, 0)
         pool_a, wk_a, wv_a = pool.copy(), win_k.copy(), win_v.copy()
-        ref.append_ref(rk, rv, k, v, si, pos, bt, s.seq_lens, pool_a, wk_a, wv_a, window)
+        ref.append_ref(rk, rv, k, v, si, pos, bt, s.seq_lens, pool_a, wk_a, wv_a, window, n_sink)
         pool_b = rng.integers(0, 256, pool.shape, dtype=np.uint8)
         used = np.zeros(pool.shape[0], bool)
         used[bt[0][bt[0] >= 0]] = True
         pool_b0 = pool_b.copy()
         wk_b, wv_b = win_k.copy(), win_v.copy()
-        ref.append_sequence_ref(rk, rv, k, v, bt[0], pool_b, wk_b[0], wv_b[0], window)
+        ref.append_sequence_ref(rk, rv, k, v, bt[0], pool_b, wk_b[0], wv_b[0], window, n_sink)
         # written slots equal; unwritten bytes of the last page keep their old values
         kh_a, vh_a = ref.read_history(pool_a, bt[0], n, 2)
         kh_b, vh_b = ref.read_history(pool_b, bt[0], n, 2)
         assert np.array_equal(kh_a, kh_b) and np.array_equal(vh_a, vh_b)
         pool_c = pool_b0.copy()
-        ref.append_ref(rk, rv, k, v, si, pos, bt, s.seq_lens, pool_c, win_k.copy(), win_v.copy(), window)
+        ref.append_ref(rk, rv, k, v, si, pos, bt, s.seq_lens, pool_c, win_k.copy(), win_v.copy(), window, n_sink)
         assert np.array_equal(pool_b, pool_c)
         assert np.array_equal(wk_b, wk_a) and np.array_equal(wv_b, wv_a)

@@ -23,14 +23,14 @@ def orthogonal(rng, hkv):
     return np.stack([np.linalg.qr(rng.standard_normal((128, 128)))[0] for _ in range(hkv)])
 
 
-def build(rng, lens, window, hq=8, hkv=2, cfg=1, rot=None):
+def build(rng, lens, window, hq=8, hkv=2, cfg=1, rot=None, n_sink=0):
     s = wl.spec(cfg, batch=len(lens))
     s.seq_lens = np.asarray(lens, dtype=np.int32)
     s.window = window
     s.n_q_heads, s.n_kv_heads = hq, hkv
     bt, n_pages = wl.page_table(s)
     pool = np.zeros((n_pages, hkv, ref.BLOCK), dtype=np.uint8)
-    win_k = np.zeros((len(lens), max(window, 1), hkv, 128), dtype=np.uint16)
+    win_k = np.zeros((len(lens), max(window + n_sink, 1), hkv, 128), dtype=np.uint16)
     win_v = np.zeros_like(win_k)
     rk, rv = rot if rot is not None else (orthogonal(rng, hkv), orthogonal(rng, hkv))
     kv = {}
@@ -39,14 +39,16 @@ def build(rng, lens, window, hq=8, hkv=2, cfg=1, rot=None):
         k, v = k[:, :hkv], v[:, :hkv]
         n = k.shape[0]
         ref.append_ref(rk, rv, k, v, np.full(n, b, np.int32), np.arange(n, dtype=np.int32),
-                       bt, s.seq_lens, pool, win_k, win_v, window)
+                       bt, s.seq_lens, pool, win_k, win_v, window, n_sink)
         kv[b] = (k, v)
     q = wl.decode_queries(s)[:, :hq]
     return s, bt, pool, win_k, win_v, rk, rv, kv, q
 
 
-def brute_force(q_bits, kv, lens, window, rk, rv, hkv):
-    """Pure-Python textbook attention over the dequantised, un-rotated cache."""
+def brute_force(q_bits, kv, lens, window, rk, rv, hkv, n_sink=0):
+    """Pure-Python textbook attention over the dequantised, un-rotated cache
+    (positions below min(n_sink, n - w) and the last w = min(n, W) are the raw
+    bf16 tokens)."""
     bsz, hq, d = q_bits.shape
     g = hq // hkv
     out = np.zeros((bsz, hq, d))
@@ -54,6 +56,7 @@ def brute_force(q_bits, kv, lens, window, rk, rv, hkv):
         k_bits, v_bits = kv[b]
         n = int(lens[b])
         hist = n - min(n, window)
+        ns = min(n_sink, hist)
         for j in range(hq):
             h = j // g
             kx = ref.bf16_to_f64(k_bits[:, h])
@@ -62,7 +65,7 @@ def brute_force(q_bits, kv, lens, window, rk, rv, hkv):
             cv, sv, zv, _ = ref.quantize(ref.rotate(rv[h], vx))
             keys, vals = [], []
             for t in range(n):
-                if t < hist:
+                if ns <= t < hist:
                     kr = zk[t] + ck[t] * sk[t]
                     vr = zv[t] + cv[t] * sv[t]
                     keys.append(rk[h].T @ kr)
@@ -86,6 +89,40 @@ def test_decode_matches_brute_force(rng):
     got = ref.decode_ref(rk, rv, q, s.seq_lens, bt, pool, wk, wv, window)
     want = brute_force(q, kv, lens, window, rk, rv, 2)
     assert np.abs(got - want).max() <= 1e-11 * np.abs(want).max()
+
+
+def test_decode_with_sinks_matches_brute_force(rng):
+    lens, window, n_sink = (37, 5, 20, 30), 8, 6   # sinks inside the history, n < W, sinks past the history
+    s, bt, pool, wk, wv, rk, rv, kv, q = build(rng, lens, window, n_sink=n_sink)
+    got = ref.decode_ref(rk, rv, q, s.seq_lens, bt, pool, wk, wv, window, n_sink=n_sink)
+    want = brute_force(q, kv, lens, window, rk, rv, 2, n_sink=n_sink)
+    assert np.abs(got - want).max() <= 1e-11 * np.abs(want).max()
+
+
+def test_decode_sinks_covering_the_history_is_sdpa(rng):
+    """n_sink >= n - w: every position is a raw bf16 token, so decode is plain
+    softmax attention (torch SDPA in fp64)."""
+    lens, window, n_sink = (40, 25), 16, 24
+    s, bt, pool, wk, wv, rk, rv, kv, q = build(rng, lens, window, n_sink=n_sink)
+    got = ref.decode_ref(rk, rv, q, s.seq_lens, bt, pool, wk, wv, window, n_sink=n_sink)
+    for b in range(2):
+        k, v = kv[b]
+        kk = torch.from_numpy(ref.bf16_to_f64(k)).permute(1, 0, 2)
+        vv = torch.from_numpy(ref.bf16_to_f64(v)).permute(1, 0, 2)
+        qq = torch.from_numpy(ref.bf16_to_f64(q[b])).view(2, 4, 1, 128)
+        o = torch.nn.functional.scaled_dot_product_attention(qq, kk[:, None], vv[:, None])
+        assert np.allclose(got[b], o.reshape(8, 128).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_append_ref_sink_rows(rng):
+    """Position p < n_sink is also stored raw in ring row W + p; other rows of
+    that block of the ring stay untouched."""
+    lens, window, n_sink = (50,), 8, 5
+    s, bt, pool, wk, wv, rk, rv, kv, q = build(rng, lens, window, n_sink=n_sink)
+    k, v = kv[0]
+    assert np.array_equal(wk[0, window:window + n_sink], k[:n_sink])
+    assert np.array_equal(wv[0, window:window + n_sink], v[:n_sink])
+    assert np.array_equal(wk[0, :window], k[np.arange(42, 50)][np.argsort(np.arange(42, 50) % window)])
 
 
 def test_decode_pure_window_is_sdpa(rng):
@@ -183,13 +220,15 @@ def test_bf16_comparator_layout_by_hand():
     assert kk[3, 5] == 0x3F80 and vv[3, 9] == 0x4000 and np.count_nonzero(kk) == 1 and np.count_nonzero(vv) == 1
 
 
-def test_direct_decode_equals_paged_decode(rng):
+@pytest.mark.parametrize("n_sink", [0, 4, 200])
+def test_direct_decode_equals_paged_decode(rng, n_sink):
     lens, window = (300, 20, 129), 128
-    s, bt, pool, wk, wv, rk, rv, kv, q = build(rng, lens, window)
-    full = ref.decode_ref(rk, rv, q, s.seq_lens, bt, pool, wk, wv, window)
+    s, bt, pool, wk, wv, rk, rv, kv, q = build(rng, lens, window, n_sink=n_sink)
+    full = ref.decode_ref(rk, rv, q, s.seq_lens, bt, pool, wk, wv, window, n_sink=n_sink)
     for b in range(3):
         k, v = kv[b]
         for h in range(2):
-            got = ref.decode_direct_ref(rk, rv, q[b, 4 * h:4 * h + 4], k[:, h], v[:, h], lens[b], window, h)
+            got = ref.decode_direct_ref(rk, rv, q[b, 4 * h:4 * h + 4], k[:, h], v[:, h], lens[b], window, h,
+                                        n_sink=n_sink)
             assert np.array_equal(got, full[b, 4 * h:4 * h + 4]) or np.allclose(got, full[b, 4 * h:4 * h + 4],
                                                                               rtol=1e-13, atol=1e-15)

@@ -73,6 +73,7 @@ class Spec:
     group_size: int = GROUP
     page_size: int = PAGE
     window: int = WINDOW
+    n_sink: int = 0        # leading positions also kept in bf16 (attention sinks)
     decode_steps: int = 1  # >1: one appended token per sequence between steps
     seed: int = 0
 
