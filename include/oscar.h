@@ -35,7 +35,8 @@
  *
  * Supported shape (anything else returns OSCAR_EUNSUPPORTED): head_dim 128,
  * group_size 128 (one INT2 group per token vector), page_size 16,
- * n_q_heads = G * n_kv_heads with G in {1, 2, 4, 8, 16}, 0 <= window <= 1024.
+ * n_q_heads = G * n_kv_heads with G in {1, 2, 4, 8, 16}, 0 <= window <= 1024,
+ * 0 <= n_sink <= 1024.
  *
  * Page block (one per page and KV head, 1152 bytes, 128-byte aligned within a
  * 128-byte aligned pool; pool = uint8 [n_pages][n_kv_heads][1152]):
@@ -47,7 +48,8 @@
  *                 fp16 K scale, K zero, V scale, V zero
  * A token at position pos of sequence b lives in page block_table[b][pos / 16],
  * slot pos % 16.  Dequantised rotated value of channel c: zero + code * scale.
- * bf16 window ring: [batch][window][n_kv_heads][128], position pos in slot pos % window.
+ * bf16 ring: [batch][window + n_sink][n_kv_heads][128]: recent position pos in row
+ * pos % window, sink position pos < n_sink in row window + pos.
  */
 #ifndef OSCAR_H
 #define OSCAR_H
@@ -74,6 +76,7 @@ typedef struct oscar_shape {
   int32_t group_size;  /* channels per INT2 group; must be 128 */
   int32_t page_size;   /* tokens per page; must be 16 */
   int32_t window;      /* most recent tokens also kept in bf16 (0 = none) */
+  int32_t n_sink;      /* first tokens of a sequence also kept in bf16 (attention sinks; 0 = none) */
 } oscar_shape;
 
 #define OSCAR_HEAD_DIM 128
@@ -114,8 +117,9 @@ int oscar_calibrate(const oscar_shape* shape, const float* q_cal, int64_t n_q,
  *   m = min x', M = max x'; scale = fp16_rne((M - m) / 3); zero = fp16_rne(m);
  *   code_c = clamp(rint((x'_c - zero) / scale), 0, 3) (all 0 if scale == 0);
  *   written to page block_table[b][p / 16], slot p % 16, in the layout above.
- *   If p >= seq_len_after[b] - window, the raw bf16 k/v also go to window slot
- *   p % window.
+ *   If p >= seq_len_after[b] - window, the raw bf16 k/v also go to ring row
+ *   p % window; if p < n_sink, also to ring row window + p (sink and recent
+ *   tokens stay bf16: P2 «OSCAR има значение…»).
  * Arguments (device memory unless noted):
  *   r_k, r_v     bf16 [n_kv_heads][128][128]
  *   k_new, v_new bf16 [n_tokens][n_kv_heads][128]
@@ -123,7 +127,8 @@ int oscar_calibrate(const oscar_shape* shape, const float* q_cal, int64_t n_q,
  *   block_table  int32 [batch][max_pages_per_seq]
  *   seq_len_after int32 [batch]: sequence length once this call's tokens are in
  *   pool         uint8 [n_pages][n_kv_heads][1152], updated in place (other slots kept)
- *   win_k, win_v bf16 [batch][window][n_kv_heads][128] (may be NULL if window == 0)
+ *   win_k, win_v bf16 [batch][window + n_sink][n_kv_heads][128] (may be NULL if
+ *                window + n_sink == 0)
  * n_tokens == 0 is a no-op.  Errors: OSCAR_EINVAL, OSCAR_EUNSUPPORTED, OSCAR_EHIP.
  */
 int oscar_quantize_append(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
@@ -144,10 +149,11 @@ size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int
  * Decode attention for one query token per sequence over the mixed-precision
  * cache (P1 «Что придумали в Together AI»: q is rotated by the key transform and
  * the output un-rotated by the value transform; P2 «OSCAR има значение…»: bf16
- * recent window + INT2 history).  With n = seq_lens[b], w = min(n, window):
- *   history t < n - w: s_t = (R_K q) . (zero + code * scale)_t / sqrt(d)  (INT2 K)
- *   window  t >= n - w: s_t = q . k_t / sqrt(d)                           (bf16 K)
- *   out = (R_V^T sum_hist p_t v'_t + sum_win p_t v_t) / sum_all p_t,
+ * sink and recent tokens + INT2 history).  With n = seq_lens[b],
+ * w = min(n, window) and s = min(n_sink, n - w):
+ *   history s <= t < n - w: s_t = (R_K q) . (zero + code * scale)_t / sqrt(d) (INT2 K)
+ *   sinks t < s and window t >= n - w: s_t = q . k_t / sqrt(d)               (bf16 K)
+ *   out = (R_V^T sum_hist p_t v'_t + sum_sink,win p_t v_t) / sum_all p_t,
  *   p = exp(s - max s); query head j uses KV head j / G.
  * Arguments (device memory):
  *   r_k, r_v bf16 [n_kv_heads][128][128]; q bf16 [batch][n_q_heads][128]

@@ -35,8 +35,8 @@ class OscarError(RuntimeError):
 
 
 def make_shape(n_q_heads: int, n_kv_heads: int, window: int = 128, head_dim: int = 128,
-               group_size: int = 128, page_size: int = 16) -> OscarShape:
-    return OscarShape(n_q_heads, n_kv_heads, head_dim, group_size, page_size, window)
+               group_size: int = 128, page_size: int = 16, n_sink: int = 0) -> OscarShape:
+    return OscarShape(n_q_heads, n_kv_heads, head_dim, group_size, page_size, window, n_sink)
 
 
 def _check(fn: str, status: int) -> None:

@@ -14,7 +14,8 @@ LIB_PATH = os.path.join(HERE, "libkv_cache_int2_amd.so")
 
 class OscarShape(C.Structure):
     _fields_ = [("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
-                ("group_size", C.c_int32), ("page_size", C.c_int32), ("window", C.c_int32)]
+                ("group_size", C.c_int32), ("page_size", C.c_int32), ("window", C.c_int32),
+                ("n_sink", C.c_int32)]
 
 
 P = C.c_void_p

@@ -33,7 +33,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 struct AppendParams {
   const uint16_t* r[2];  // K, V rotations [Hkv][128][128]
   const uint16_t* x[2];  // k_new, v_new [T][Hkv][128]
-  uint16_t* win[2];      // window rings [B][W][Hkv][128]
+  uint16_t* win[2];      // bf16 rings [B][W + n_sink][Hkv][128]
   const int32_t* seq_idx;
   const int32_t* pos;
   const int32_t* block_table;
@@ -42,6 +42,8 @@ struct AppendParams {
   int64_t n_tokens;
   int64_t n_pages;
   int batch, max_pages, hkv, window, tiles_per_wg;
+  int n_sink;  // leading positions also kept in bf16 (ring rows window + pos)
+  int ring;    // ring rows per sequence: window + n_sink
 };
 
 constexpr int kRowU4 = 17;  // LDS row stride of R in uint4 (16 + 1 pad: 272 B)
@@ -96,11 +98,12 @@ struct TokInfo {
   int slot;
   int b;
   int pos;
-  bool in_win;
+  bool in_win;   // recent: ring row pos % window
+  bool in_sink;  // sink: ring row window + pos
 };
 
 __device__ __forceinline__ TokInfo resolve(const AppendParams& p, int64_t tok, int h) {
-  TokInfo ti{nullptr, 0, 0, 0, false};
+  TokInfo ti{nullptr, 0, 0, 0, false, false};
   if (tok >= p.n_tokens) return ti;
   int b = p.seq_idx[tok], ps = p.pos[tok];
   if (b < 0 || b >= p.batch || ps < 0 || (ps >> 4) >= p.max_pages) return ti;
@@ -111,6 +114,7 @@ __device__ __forceinline__ TokInfo resolve(const AppendParams& p, int64_t tok, i
   ti.b = b;
   ti.pos = ps;
   ti.in_win = p.window > 0 && ps >= p.len_after[b] - p.window;
+  ti.in_sink = ps < p.n_sink;
   return ti;
 }
 
@@ -150,9 +154,14 @@ __device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4
     if (tj >= p.n_tokens) break;  // uniform: the wave's tokens are contiguous
     TokInfo ti = resolve(p, tj + r, h);
 
-    // raw bf16 copy into the window ring (same for K and V)
+    // raw bf16 copies into the ring (same for K and V): recent tokens, sinks
     if (ti.blk && ti.in_win) {
-      uint4* wp = reinterpret_cast<uint4*>(p.win[KIND] + (((int64_t)ti.b * p.window + ti.pos % p.window) * p.hkv + h) * kD + 32 * g);
+      uint4* wp = reinterpret_cast<uint4*>(p.win[KIND] + (((int64_t)ti.b * p.ring + ti.pos % p.window) * p.hkv + h) * kD + 32 * g);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) wp[s] = xv[j][s];
+    }
+    if (ti.blk && ti.in_sink) {
+      uint4* wp = reinterpret_cast<uint4*>(p.win[KIND] + (((int64_t)ti.b * p.ring + p.window + ti.pos) * p.hkv + h) * kD + 32 * g);
 #pragma unroll
       for (int s = 0; s < 4; ++s) wp[s] = xv[j][s];
     }
@@ -290,7 +299,7 @@ extern "C" int oscar_quantize_append(const oscar_shape* shape, const uint16_t* r
   if (n_tokens == 0) return OSCAR_OK;
   if (!r_k || !r_v || !k_new || !v_new || !seq_idx || !pos || !block_table || !seq_len_after || !pool)
     return OSCAR_EINVAL;
-  if (shape->window > 0 && (!win_k || !win_v)) return OSCAR_EINVAL;
+  if (shape->window + shape->n_sink > 0 && (!win_k || !win_v)) return OSCAR_EINVAL;
   if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
        reinterpret_cast<uintptr_t>(r_k) | reinterpret_cast<uintptr_t>(r_v) |
        reinterpret_cast<uintptr_t>(pool) | reinterpret_cast<uintptr_t>(win_k) |
@@ -314,6 +323,8 @@ extern "C" int oscar_quantize_append(const oscar_shape* shape, const uint16_t* r
   p.max_pages = max_pages_per_seq;
   p.hkv = shape->n_kv_heads;
   p.window = shape->window;
+  p.n_sink = shape->n_sink;
+  p.ring = shape->window + shape->n_sink;
   const int64_t tiles = (n_tokens + kAppendTokens - 1) / kAppendTokens;  // workgroup iterations
   p.tiles_per_wg = tiles >= 512 ? 4 : (tiles >= 128 ? 2 : 1);
   dim3 grid((unsigned)((tiles + p.tiles_per_wg - 1) / p.tiles_per_wg), (unsigned)p.hkv, 2);

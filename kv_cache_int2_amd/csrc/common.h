@@ -27,7 +27,8 @@ inline int check_shape(const oscar_shape* s) {
   if (s->n_q_heads % s->n_kv_heads) return OSCAR_EINVAL;
   int g = s->n_q_heads / s->n_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return OSCAR_EUNSUPPORTED;
-  if (s->window > kMaxWindow) return OSCAR_EUNSUPPORTED;
+  if (s->n_sink < 0) return OSCAR_EINVAL;
+  if (s->window > kMaxWindow || s->n_sink > kMaxWindow) return OSCAR_EUNSUPPORTED;
   return OSCAR_OK;
 }
 
@@ -79,14 +80,14 @@ inline int split_wg_count(int gqa, int n_cu) { return (n_cu > 0 ? n_cu : 256) * 
 //   part         float  bf16 comparator: [B][Hq][n_splits][130] split partials (m, l, acc[128]);
 //                       INT2: [n_wg + units][4][gw][130] partials of the persistent workgroups'
 //                       waves (units = B Hkv / hw x Hq / (Hkv gw); hw KV heads per workgroup)
-//   wpart        float [B][Hq][ceil(W/32)][130]     window chunk partials (m, l, acc[128])
+//   wpart        float [B][Hq][ceil(W/32) + ceil(n_sink/32)][130]  window, then sink chunk partials
 //   tile_prefix  int   [units + 1]                  first history tile of each merge unit
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct WorkspaceLayout {
   size_t qsum, qop, part, wpart, tile_prefix, total;
 };
-inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int window, const SplitPlan& p,
-                                        int n_cu) {
+inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int window, int n_sink,
+                                        const SplitPlan& p, int n_cu) {
   const int gqa = n_q_heads / n_kv_heads;
   const size_t g4 = (size_t)((gqa + 3) / 4);
   const size_t gw = (size_t)(gqa > 8 ? 8 : gqa);
@@ -99,7 +100,7 @@ inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads
   w.qop = w.qsum + align256((size_t)batch * n_q_heads * sizeof(float));
   w.part = w.qop + align256((size_t)batch * n_kv_heads * g4 * 64 * 9 * sizeof(int));
   w.wpart = w.part + align256((part_bf16 > part_int2 ? part_bf16 : part_int2) * sizeof(float));
-  const size_t n_wchunks = (size_t)((window + kWinChunk - 1) / kWinChunk);
+  const size_t n_wchunks = (size_t)((window + kWinChunk - 1) / kWinChunk + (n_sink + kWinChunk - 1) / kWinChunk);
   w.tile_prefix = w.wpart + align256((size_t)batch * n_q_heads * n_wchunks * kPartStride * sizeof(float));
   w.total = w.tile_prefix + align256((units + 1) * sizeof(int));
   return w;

@@ -119,12 +119,15 @@ struct SplitParams {
   const uint16_t* win_k;      // INT2: bf16 window rings [B][W][Hkv][128]
   const uint16_t* win_v;
   float* part;                // bf16: [B][Hq][n_splits][130]; INT2: [n_wg + units][gw][130] slot partials
-  float* wpart;               // INT2: [B][Hq][n_wchunks][130] window chunk partials (unrotated domain)
+  float* wpart;               // INT2: [B][Hq][n_wchunks][130] window, then sink chunk partials (plain domain)
   int* tile_prefix;           // INT2: [units + 1] first history tile of each unit in the flattened order
   float* out;                 // [B][Hq][128]
   int64_t n_pages;
   int batch, hq, hkv, max_pages, max_len, window, split, n_splits;
-  int n_wchunks;              // INT2: 32-token chunks of the window, ceil(W / 32)
+  int n_wchunks;              // INT2: 32-token chunks of the ring, ceil(W / 32) + ceil(n_sink / 32)
+  int n_wwin;                 // INT2: the first ceil(W / 32) of them cover the window, the rest the sinks
+  int n_sink;                 // INT2: leading positions kept in bf16 (ring rows W + pos)
+  int ring;                   // INT2: ring rows per sequence, W + n_sink
   int gsub;                   // INT2 merge units per KV head, each taking gw of its query heads
   int gw;                     // query heads a unit really has (<= G of the kernel's instantiation)
   int n_wg;                   // INT2: persistent workgroups of the split kernel
@@ -148,9 +151,10 @@ __device__ __forceinline__ int hist_tiles(const SplitParams& p, int b) {
 template <int GMAX>
 constexpr int window_smem_bytes() { return (GMAX * kD + kWinChunk * 65 + GMAX * kWinChunk + 4 * GMAX) * 4; }
 
-// One 32-token chunk of the bf16 window of (sequence b, KV head h): positions
-// n - w + 32 c .. at ring slots pos % W, unrotated, for the G <= GMAX query
-// heads of h.
+// One 32-token chunk of the bf16 ring of (sequence b, KV head h), unrotated,
+// for the G <= GMAX query heads of h: chunk c < n_wwin covers window positions
+// n - w + 32 c .. (ring rows pos % W), chunk n_wwin + c' the sink positions
+// 32 c' .. below s = min(n_sink, n - w) (ring rows W + pos).
 // Thread (t, part) = (tid / 8, tid % 8) loads dims 16 part .. 16 part + 15 of
 // token t's key and value (all loads issued first); the 8 parts of a score are
 // summed across lanes, V goes through LDS for P V.  Writes (m, l, acc[128]) of
@@ -160,8 +164,10 @@ __device__ void window_chunk(const SplitParams& p, int b, int h, int c, int G, f
   const int tid = threadIdx.x, wave = tid >> 6;
   const int n = seq_len_of(p, b);
   const int w = n < p.window ? n : p.window;
-  const int cs = n - w + kWinChunk * c;
-  const int nt = min(kWinChunk, n - cs);  // <= 0: empty chunk
+  const bool sink = c >= p.n_wwin;
+  const int s_end = min(p.n_sink, n - w);  // sink positions [0, s_end)
+  const int cs = sink ? kWinChunk * (c - p.n_wwin) : n - w + kWinChunk * c;
+  const int nt = min(kWinChunk, (sink ? s_end : n) - cs);  // <= 0: empty chunk
   const int hq0 = h * G;
   float* dst0 = p.wpart + (((int64_t)b * p.hq + hq0) * p.n_wchunks + c) * kPartStride;
   const int64_t head_stride = (int64_t)p.n_wchunks * kPartStride;
@@ -180,8 +186,8 @@ __device__ void window_chunk(const SplitParams& p, int b, int h, int c, int G, f
   const bool valid = t < nt;
   uint4 kk[2], vv[2];
   {
-    const int slot = valid ? (cs + t) % p.window : 0;
-    const int64_t row = (((int64_t)b * p.window + slot) * p.hkv + h) * kD + 16 * part;
+    const int slot = !valid ? 0 : sink ? p.window + cs + t : (cs + t) % p.window;
+    const int64_t row = (((int64_t)b * p.ring + slot) * p.hkv + h) * kD + 16 * part;
     const uint4* kr = reinterpret_cast<const uint4*>(p.win_k + row);
     const uint4* vr = reinterpret_cast<const uint4*>(p.win_v + row);
     kk[0] = kr[0]; kk[1] = kr[1];
@@ -471,8 +477,8 @@ struct WaveState {
 };
 
 template <int G, int NRG, bool FULL>  // FULL: all 8 pages exist and every token is below t_end
-__device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t, int pbase, int t_end, int lg,
-                                             int lr, const i32x8* qa, const int* qsc, const float* qsr,
+__device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t, int pbase, int t_beg, int t_end,
+                                             int lg, int lr, const i32x8* qa, const int* qsc, const float* qsr,
                                              uint8_t* wt, WaveState<NRG>& st) {
   const int slot_pos = 8 * (lr & 1) + (lr >> 1);  // k position of token lr within its page's 16
   // ---- scores: raw[rg][pp] = q'_(4rg+lg) . code(token lr of page pp) ----
@@ -497,7 +503,8 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t
   uint2 meta[8];
 #pragma unroll
   for (int pp = 0; pp < 8; ++pp) {
-    const bool live = FULL || (((t.page_ok >> pp) & 1u) && (pbase + pp) * 16 + lr < t_end);
+    const int tok = (pbase + pp) * 16 + lr;
+    const bool live = FULL || (((t.page_ok >> pp) & 1u) && tok >= t_beg && tok < t_end);
     meta[pp].x = live ? t.meta[pp].x : 0u;
     meta[pp].y = live ? t.meta[pp].y : 0u;
   }
@@ -516,7 +523,7 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
       const int tok = (pbase + pp) * 16 + lr;
-      const bool ok = hv && (FULL || (tok < t_end && ((t.page_ok >> pp) & 1u)));
+      const bool ok = hv && (FULL || (tok >= t_beg && tok < t_end && ((t.page_ok >> pp) & 1u)));
       const float ks = h2f((uint16_t)(meta[pp].x & 0xffffu));
       const float kz = h2f((uint16_t)(meta[pp].x >> 16));
       // computed on every lane, then masked: a select, not a branch
@@ -682,6 +689,7 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
     const int hq0 = h * p.gw * p.gsub + sub * p.gw;  // first query head of the unit
     const int n = seq_len_of(p, b);
     const int t_end = n - (n < p.window ? n : p.window);  // history tokens
+    const int t_beg = min(p.n_sink, t_end);               // the sinks before it are bf16
 
     // score operands prepared once per (sequence, KV head)
     i32x8 qa[NRG];
@@ -720,9 +728,9 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
         const int k = 2 * s;
         Tile t;
         load_tile(p, tab, 0, h, pbase_of(k), t_end, lg, lr, t);
-        compute_tile<G, NRG, false>(p, t, pbase_of(k), t_end, lg, lr, qa, qsc, qsr, wt, st);
+        compute_tile<G, NRG, false>(p, t, pbase_of(k), t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
         load_tile(p, tab, 1, h, pbase_of(k + 1), t_end, lg, lr, t);
-        compute_tile<G, NRG, false>(p, t, pbase_of(k + 1), t_end, lg, lr, qa, qsc, qsr, wt, st);
+        compute_tile<G, NRG, false>(p, t, pbase_of(k + 1), t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
         if (s + 1 >= ns) break;
         tab = table_ready(p, raw_next, P0, P1, ph, ts, k + 2, ntw);
         raw_next = table_load(btr, P0, P1, ph, ts, k + 4);
@@ -733,14 +741,14 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
       for (int s = 0;; ++s) {
         const int k = 2 * s;
         load_tile(p, tab, 1, h, pbase_of(k + 1), t_end, lg, lr, tb);
-        compute_tile<G, NRG, false>(p, ta, pbase_of(k), t_end, lg, lr, qa, qsc, qsr, wt, st);
+        compute_tile<G, NRG, false>(p, ta, pbase_of(k), t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
         const bool more = s + 1 < ns;
         // past the last step the table is empty: tile k + 2 re-reads page 0's
         // block (cache resident) and is never computed
         tab = table_ready(p, raw_next, P0, P1, ph, ts, k + 2, more ? ntw : 0);
         raw_next = table_load(btr, P0, P1, ph, ts, k + 4);
         load_tile(p, tab, 0, h, pbase_of(k + 2), t_end, lg, lr, ta);
-        compute_tile<G, NRG, false>(p, tb, pbase_of(k + 1), t_end, lg, lr, qa, qsc, qsr, wt, st);
+        compute_tile<G, NRG, false>(p, tb, pbase_of(k + 1), t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
         if (!more) break;
       }
     }
@@ -1154,13 +1162,14 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   if (batch < 1 || max_seq_len < 0 || max_pages_per_seq < 1 || n_pages < 1) return OSCAR_EINVAL;
   if (!q || !seq_lens || !block_table || !out || !workspace) return OSCAR_EINVAL;
   if (int2 && (!r_k || !r_v || !pool)) return OSCAR_EINVAL;
-  if (int2 && shape->window > 0 && (!win_k || !win_v)) return OSCAR_EINVAL;
+  if (int2 && shape->window + shape->n_sink > 0 && (!win_k || !win_v)) return OSCAR_EINVAL;
   if (!int2 && !kv_pool) return OSCAR_EINVAL;
   if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * kPage) return OSCAR_ENOSPACE;
   const int gqa = shape->n_q_heads / shape->n_kv_heads;
   const int n_cu = device_cu_count();
   const SplitPlan plan = plan_splits(batch, shape->n_kv_heads, gqa, max_seq_len, n_cu);
-  const WorkspaceLayout wl = workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads, shape->window, plan, n_cu);
+  const WorkspaceLayout wl = workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads, shape->window, shape->n_sink,
+                                              plan, n_cu);
   if (workspace_bytes < wl.total) return OSCAR_ENOSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return OSCAR_EINVAL;
 
@@ -1187,7 +1196,10 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   sp.max_pages = max_pages_per_seq;
   sp.max_len = max_seq_len;
   sp.window = int2 ? shape->window : 0;
-  sp.n_wchunks = (sp.window + kWinChunk - 1) / kWinChunk;
+  sp.n_sink = int2 ? shape->n_sink : 0;
+  sp.ring = sp.window + sp.n_sink;
+  sp.n_wwin = (sp.window + kWinChunk - 1) / kWinChunk;
+  sp.n_wchunks = sp.n_wwin + (sp.n_sink + kWinChunk - 1) / kWinChunk;
   sp.split = plan.split;
   sp.n_splits = plan.n_splits;
   // INT2: at most 8 query heads per merge unit (register budget of the MFMA
@@ -1251,7 +1263,7 @@ extern "C" size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t
   using namespace oscar;
   if (check_shape(shape) != OSCAR_OK || batch < 1 || max_seq_len < 0) return 0;
   const int n_cu = device_cu_count();
-  return workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads, shape->window,
+  return workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads, shape->window, shape->n_sink,
                           plan_splits(batch, shape->n_kv_heads, shape->n_q_heads / shape->n_kv_heads, max_seq_len,
                                       n_cu),
                           n_cu)

@@ -57,10 +57,11 @@ def rotations(cfg, hkv=8):
     return ref.bf16_bits(rk), ref.bf16_bits(rv)
 
 
-def make_spec(cfg, lens, window=128, hq=None, hkv=8):
+def make_spec(cfg, lens, window=128, hq=None, hkv=8, n_sink=0):
     s = wl.spec(cfg, batch=len(lens))
     s.seq_lens = np.asarray(lens, np.int32)
     s.window = window
+    s.n_sink = n_sink
     if hq is not None:
         s.n_q_heads = hq
     s.n_kv_heads = hkv
@@ -82,11 +83,15 @@ def token_list(s, order="inorder", rng=None):
     return np.ascontiguousarray(k), np.ascontiguousarray(v), si, ps
 
 
+def ring_rows(s):
+    return max(s.window + s.n_sink, 1)
+
+
 def run_append(K, s, rk, rv, k, v, si, ps, bt, pool0, wk0, wv0, lens_after):
-    shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window)
+    shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window, n_sink=s.n_sink)
     pool = D(pool0)
-    wk = D(wk0) if s.window > 0 else None
-    wv = D(wv0) if s.window > 0 else None
+    wk = D(wk0) if s.window + s.n_sink > 0 else None
+    wv = D(wv0) if s.window + s.n_sink > 0 else None
     K.oscar_quantize_append(shape, D(rk), D(rv), D(k), D(v), D(si), D(ps), D(bt), D(lens_after),
                             pool, wk, wv)
     torch.cuda.synchronize()
@@ -99,7 +104,7 @@ def append_case(K, s, order="inorder", split_at=None, seed=0):
     rkf, rvf = ref.bf16_to_f64(rk), ref.bf16_to_f64(rv)
     bt, n_pages = wl.page_table(s)
     pool0 = rng.integers(0, 256, (n_pages, s.n_kv_heads, ref.BLOCK), dtype=np.uint8)
-    wsh = (s.batch, max(s.window, 1), s.n_kv_heads, 128)
+    wsh = (s.batch, ring_rows(s), s.n_kv_heads, 128)
     wk0 = rng.integers(0, 65536, wsh, dtype=np.uint16)
     wv0 = rng.integers(0, 65536, wsh, dtype=np.uint16)
     k, v, si, ps = token_list(s, order, rng)
@@ -109,14 +114,15 @@ def append_case(K, s, order="inorder", split_at=None, seed=0):
     for a, b in chunks:
         pool_g, wk_g2, wv_g2 = run_append(K, s, rk, rv, k[a:b], v[a:b], si[a:b], ps[a:b], bt, pool_g, wk_g, wv_g,
                                           s.seq_lens)
-        if s.window > 0:
+        if s.window + s.n_sink > 0:
             wk_g, wv_g = wk_g2, wv_g2
         ref.append_ref(rkf, rvf, k[a:b], v[a:b], si[a:b], ps[a:b], bt, s.seq_lens, pool_ref, wk_ref, wv_ref,
-                       s.window)
+                       s.window, s.n_sink)
     mism, excl, stray = P.check_append(pool0, pool_g, rkf, rvf, k, v, si, ps, bt)
-    log(f"append {s.cfg} lens={list(s.seq_lens)} W={s.window} {order}: mismatches={mism} excluded={excl} stray={stray}")
+    log(f"append {s.cfg} lens={list(s.seq_lens)} W={s.window} sinks={s.n_sink} {order}: "
+        f"mismatches={mism} excluded={excl} stray={stray}")
     assert mism == 0 and stray == 0
-    if s.window > 0:
+    if s.window + s.n_sink > 0:
         assert np.array_equal(wk_g, wk_ref) and np.array_equal(wv_g, wv_ref)
     return excl
 
@@ -135,6 +141,14 @@ def test_append_continuation_mid_page(K):
 
 def test_append_no_window(K):
     append_case(K, make_spec(1, [77, 200], window=0), seed=3)
+
+
+def test_append_with_sinks(K):
+    append_case(K, make_spec(1, [300, 37, 129], window=100, n_sink=40), order="shuffled", seed=5)
+
+
+def test_append_sinks_no_window(K):
+    append_case(K, make_spec(1, [77, 20], window=0, n_sink=64), split_at=30, seed=6)
 
 
 def test_append_single_tokens(K):
@@ -182,21 +196,22 @@ def oracle_cache(s, seed=0):
     rng = np.random.default_rng(seed)
     # unused slots hold random bytes (the decode must never read them)
     pool = rng.integers(0, 256, (n_pages, s.n_kv_heads, ref.BLOCK), dtype=np.uint8)
-    wk = np.zeros((s.batch, max(s.window, 1), s.n_kv_heads, 128), np.uint16)
+    wk = np.zeros((s.batch, ring_rows(s), s.n_kv_heads, 128), np.uint16)
     wv = np.zeros_like(wk)
     k, v, si, ps = token_list(s)
-    ref.append_ref(rkf, rvf, k, v, si, ps, bt, s.seq_lens, pool, wk, wv, s.window)
+    ref.append_ref(rkf, rvf, k, v, si, ps, bt, s.seq_lens, pool, wk, wv, s.window, s.n_sink)
     q = wl.decode_queries(s)[:, :s.n_q_heads]
     return rk, rv, rkf, rvf, bt, pool, wk, wv, q
 
 
 def run_decode(K, s, rk, rv, q, bt, pool, wk, wv, max_len=None):
-    shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window)
+    shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window, n_sink=s.n_sink)
     max_len = int(s.seq_lens.max()) if max_len is None else max_len
     ws = torch.empty(K.oscar_decode_workspace_bytes(shape, s.batch, max_len), dtype=torch.uint8, device=DEV)
     out = torch.full((s.batch, s.n_q_heads, 128), float("nan"), dtype=torch.float32, device=DEV)
     K.oscar_decode_attn(shape, D(rk), D(rv), D(q), D(s.seq_lens), max_len, D(bt), D(pool),
-                        D(wk) if s.window > 0 else None, D(wv) if s.window > 0 else None, out, ws)
+                        D(wk) if s.window + s.n_sink > 0 else None, D(wv) if s.window + s.n_sink > 0 else None,
+                        out, ws)
     torch.cuda.synchronize()
     return H(out)
 
@@ -222,6 +237,24 @@ def test_decode_small(K, cfg, lens, window, hq):
     want = ref.decode_ref(rkf, rvf, q, s.seq_lens, bt, pool, wk, wv, window)
     err = P.attn_rel_err(got, want)
     log(f"decode lens={lens} W={window} Hq={hq}: max rel err {err.max():.3e}")
+    assert np.isfinite(got).all()
+    assert err.max() <= P.ATTN_TOL
+
+
+@pytest.mark.parametrize("lens,window,n_sink,hq", [
+    ([700, 333], 128, 4, 32),          # a few sinks
+    ([1500, 200], 256, 64, 32),        # W + sinks = 320 bf16 tokens (0.24 % of 128K)
+    ([300, 90], 0, 100, 32),           # sinks and no window; n < n_sink
+    ([5000, 129], 128, 300, 64),       # sinks over two tiles (masked in the INT2 tiles); G = 8
+    ([2000, 1100], 1024, 1024, 32),    # the largest ring: sinks reach into the window
+])
+def test_decode_with_sinks(K, lens, window, n_sink, hq):
+    s = make_spec(1, lens, window, hq, n_sink=n_sink)
+    rk, rv, rkf, rvf, bt, pool, wk, wv, q = oracle_cache(s)
+    got = run_decode(K, s, rk, rv, q, bt, pool, wk, wv)
+    want = ref.decode_ref(rkf, rvf, q, s.seq_lens, bt, pool, wk, wv, window, n_sink=n_sink)
+    err = P.attn_rel_err(got, want)
+    log(f"decode sinks lens={lens} W={window} n_sink={n_sink} Hq={hq}: max rel err {err.max():.3e}")
     assert np.isfinite(got).all()
     assert err.max() <= P.ATTN_TOL
 
