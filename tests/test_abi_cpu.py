@@ -43,7 +43,8 @@ def test_strerror():
 
 def bad_shapes():
     return [K.make_shape(32, 8, head_dim=64), K.make_shape(32, 8, group_size=32),
-            K.make_shape(32, 8, page_size=32), K.make_shape(24, 8), K.make_shape(32, 8, window=4096)]
+            K.make_shape(32, 8, page_size=32), K.make_shape(24, 8), K.make_shape(32, 8, window=4096),
+            K.make_shape(32, 8, n_sink=-1), K.make_shape(32, 8, n_sink=2048)]
 
 
 def test_host_validation_before_launch():
@@ -73,6 +74,14 @@ def test_host_validation_before_launch():
     assert lib.oscar_decode_attn(*args, ws, None) == ENOSPACE
     assert lib.oscar_decode_attn(C.byref(good), None, None, None, 8, None, 10, None, 1, None, 1, None, None,
                                  None, None, 0, None) == EINVAL
+    # sinks without a window still need the ring
+    sink_only = K.make_shape(32, 8, window=0, n_sink=4)
+    assert lib.oscar_decode_attn(C.byref(sink_only), fake, fake, fake, 8, fake, 10, fake, 1, fake, 1, None, None,
+                                 fake, fake, 1 << 30, None) == EINVAL
+    assert lib.oscar_quantize_append(C.byref(sink_only), fake, fake, fake, fake, 1, fake, fake, 1, fake, 1, fake,
+                                     fake, 1, None, None, None) == EINVAL
+    # the sink chunks enlarge the workspace
+    assert lib.oscar_decode_workspace_bytes(C.byref(K.make_shape(32, 8, n_sink=64)), 8, 100000) > ws
     assert lib.oscar_hbm_copy(fake, fake, 17, None) == EINVAL
     assert lib.oscar_timing_end(None, None, 0, None) == EINVAL
 
