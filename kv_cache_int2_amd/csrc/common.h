@@ -101,7 +101,9 @@ inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads
   w.part = w.qop + align256((size_t)batch * n_kv_heads * g4 * 64 * 9 * sizeof(int));
   w.wpart = w.part + align256((part_bf16 > part_int2 ? part_bf16 : part_int2) * sizeof(float));
   const size_t n_wchunks = (size_t)((window + kWinChunk - 1) / kWinChunk + (n_sink + kWinChunk - 1) / kWinChunk);
-  w.tile_prefix = w.wpart + align256((size_t)batch * n_q_heads * n_wchunks * kPartStride * sizeof(float));
+  // at least one partial: the merge reads chunk 0 of its head unconditionally
+  const size_t n_wparts = (size_t)batch * n_q_heads * n_wchunks;
+  w.tile_prefix = w.wpart + align256((n_wparts > 0 ? n_wparts : 1) * kPartStride * sizeof(float));
   w.total = w.tile_prefix + align256((units + 1) * sizeof(int));
   return w;
 }

@@ -228,14 +228,19 @@ __device__ void window_chunk(const SplitParams& p, int b, int h, int c, int G, f
   for (int e = tid; e < G * kD; e += 256) {
     const int g = e >> 7, ch = e & (kD - 1);
     const float* pg = ps + g * kWinChunk;
-    float acc = 0.f, l = 0.f;
-    for (int tt = 0; tt < nt; ++tt) {
-      const uint32_t x = vs[tt * 65 + (ch >> 1)];
-      acc = fmaf(pg[tt], (ch & 1) ? bf16hi(x) : bf16lo(x), acc);
-      l += pg[tt];
+    // all 32 rows with a fixed trip count (a token past nt has p = 0 and a zero
+    // row), so the LDS reads are issued together rather than one per iteration
+    float acc0 = 0.f, acc1 = 0.f, l = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < kWinChunk; tt += 2) {
+      const uint32_t x0 = vs[tt * 65 + (ch >> 1)], x1 = vs[(tt + 1) * 65 + (ch >> 1)];
+      const float2 pp = *reinterpret_cast<const float2*>(pg + tt);
+      acc0 = fmaf(pp.x, (ch & 1) ? bf16hi(x0) : bf16lo(x0), acc0);
+      acc1 = fmaf(pp.y, (ch & 1) ? bf16hi(x1) : bf16lo(x1), acc1);
+      l += pp.x + pp.y;
     }
     float* dst = dst0 + g * head_stride;
-    dst[2 + ch] = acc;
+    dst[2 + ch] = acc0 + acc1;
     if (ch == 0) {
       dst[0] = fmaxf(fmaxf(red[g], red[GMAX + g]), fmaxf(red[2 * GMAX + g], red[3 * GMAX + g]));
       dst[1] = l;
@@ -974,25 +979,29 @@ __global__ __launch_bounds__(256) void bf16_split_kernel(SplitParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// merge: one workgroup per (sequence, q head).  Log-sum-exp merge of the split
-// partials; for the INT2 path the un-rotation by R_V^T and the bf16 window's
-// chunk partials, then the normalisation.  All loads of a pass (up to 64
-// partials: lane s of every wave reads partial s's (m, l), thread (c, half)
-// its accumulators of channel c), the R_V tile and the window partials are
-// issued before any of them is used, so a head costs about one memory round
-// trip.  Every wave reduces the (m, l) values itself, so the waves need no
-// exchange until the two halves of the channel sums are added.  A head with
-// no position at all gets zeros.
+// merge: one workgroup per (sequence, group of mh q heads of one KV head),
+// wave v < mh taking head mh x + v; mh (1, 2 or 4, dividing G) is chosen on the
+// host so that the grid still has about two workgroups per CU.  Each wave merges its head's partials
+// (log-sum-exp): every load of a pass (the (m, l) of up to 32 partials on its
+// lanes, the accumulators of channels lane and lane + 64) is issued before any
+// is used, the passes keep a running max, and the wave reduces the (m, l)
+// values itself.  INT2: the workgroup's R_V tile (loaded once for its MH
+// heads) un-rotates every head, then each wave merges its head's window and
+// sink chunk partials and normalises.  A head with no position at all gets
+// zeros.
 // ---------------------------------------------------------------------------
-constexpr int kMergePass = 64;  // partials per pass
-constexpr int kMergeWin = 8;    // window chunk partials held in registers
+constexpr int kMergePass = 32;  // partials per pass
+constexpr int kMergeWin = 8;    // window / sink chunk partials held in registers
+constexpr int kMergeHeads = 4;  // q heads per workgroup at most (one per wave)
 
-__global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
-  const int b = blockIdx.y, hq = blockIdx.x, h = hq / gq, tid = threadIdx.x, lane = tid & 63;
+__global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq, int mh) {
+  const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool active = wave < mh;
+  const int hq = blockIdx.x * mh + (active ? wave : 0), h = hq / gq;
   const bool int2 = p.r_v != nullptr;
-  // partials of this head: INT2 - the wave partials (w + u, v) of the ts waves
-  // v of this head in each workgroup w whose tile range touches unit u, at
-  // p.part + ((4 (w + u) + v) gw + g) 130 (partial s: workgroup w_lo + s / ts,
+  // partials of this wave's head: INT2 - the wave partials (w + u, v) of the ts
+  // waves v of this head in each workgroup w whose tile range touches unit u,
+  // at p.part + ((4 (w + u) + v) gw + g) 130 (partial s: workgroup w_lo + s / ts,
   // wave hv + hw (s % ts)); bf16 - the splits of the sequence (partial s at
   // base + s 130)
   const float* base;
@@ -1024,9 +1033,14 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
     base = p.part + ((int64_t)b * p.hq + hq) * p.n_splits * kPartStride;
     stride = kPartStride;
   }
+  if (!active) ns = 0;
+  const int tsh = ts == 4 ? 2 : ts == 2 ? 1 : 0;  // ts = 4 / hw: 1, 2 or 4
+  auto part_at = [&](int s) {
+    return base + (int64_t)(int2 ? 4 * (w0 + (s >> tsh)) + hw * (s & (ts - 1)) : s) * stride;
+  };
 
-  __shared__ float red[2][kD];
-  __shared__ float o1p[16][kD + 4];
+  __shared__ float a1s[kMergeHeads][kD];
+  __shared__ float o1p[kMergeHeads][16][kD + 4];
 
   // R_V tile (INT2): thread (cg, jg) takes channels 8cg..8cg+7 of rows 8jg..8jg+7
   const int cg = tid & 15, jg = tid >> 4;
@@ -1036,99 +1050,114 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) rv[j] = *reinterpret_cast<const uint4*>(r + j * kD);
   }
-  // window chunk partials (INT2): thread c < 128 takes channel c of the first kMergeWin chunks
+  // window / sink chunk partials (INT2): channels lane and lane + 64 of the first kMergeWin chunks
   const float* wp = p.wpart + ((int64_t)b * p.hq + hq) * p.n_wchunks * kPartStride;
-  const int nwc = int2 ? p.n_wchunks : 0;
-  float wv[kMergeWin], wm[kMergeWin], wl[kMergeWin];
+  const int nwc = int2 && active ? p.n_wchunks : 0;
+  float wv0[kMergeWin], wv1[kMergeWin], wm[kMergeWin], wl[kMergeWin];
 #pragma unroll
   for (int cc = 0; cc < kMergeWin; ++cc) {
     const bool ok = cc < nwc;
     const float* wc = wp + (ok ? cc : 0) * kPartStride;  // in the workspace even when unused
-    const float v = wc[2 + (tid & (kD - 1))], m = wc[0], l = wc[1];
-    wv[cc] = ok ? v : 0.f;
+    const float v0 = wc[2 + lane], v1 = wc[2 + 64 + lane], m = wc[0], l = wc[1];
+    wv0[cc] = ok ? v0 : 0.f;
+    wv1[cc] = ok ? v1 : 0.f;
     wm[cc] = ok ? m : kNegInf;
     wl[cc] = ok ? l : 0.f;
   }
 
-  // split partials: thread (c, half) sums channel c over the partials s = half, half + 2, ...
-  const int c = tid & (kD - 1), half = __builtin_amdgcn_readfirstlane(tid >> 7);
-  float M = kNegInf, acc = 0.f, lsum = 0.f;  // running max and sums (M, lsum the same on every lane)
+  // the head's partials: lane s of a pass holds partial s0 + s's (m, l)
+  float M = kNegInf, acc0 = 0.f, acc1 = 0.f, lsum = 0.f;  // M, lsum: the same on every lane
   for (int s0 = 0; s0 < ns; s0 += kMergePass) {
     const int cnt = min(kMergePass, ns - s0);
     // loads first, at clamped indices (no branch around a load)
-    auto part_at = [&](int s) { return base + (int64_t)(int2 ? 4 * (w0 + s / ts) + hw * (s % ts) : s) * stride; };
     const float* pl = part_at(s0 + min(lane, cnt - 1));
     const float ml_raw = pl[0], ll_raw = pl[1];
-    float x[kMergePass / 2];
+    float x0[kMergePass], x1[kMergePass];
 #pragma unroll
-    for (int k = 0; k < kMergePass / 2; ++k) x[k] = part_at(s0 + min(2 * k + half, cnt - 1))[2 + c];
+    for (int k = 0; k < kMergePass; ++k) {
+      const float* pk = part_at(s0 + min(k, cnt - 1));
+      x0[k] = pk[2 + lane];
+      x1[k] = pk[2 + 64 + lane];
+    }
     const float ml = lane < cnt ? ml_raw : kNegInf;
     const float ll = lane < cnt ? ll_raw : 0.f;
     const float Mn = fmaxf(M, wave_max64(ml));
     const float alpha = M == kNegInf ? 0.f : exp2f(M - Mn);
     const float f = ml == kNegInf ? 0.f : exp2f(ml - Mn);  // weight of partial s0 + lane
-    acc *= alpha;
+    acc0 *= alpha;
+    acc1 *= alpha;
     lsum = lsum * alpha + wave_sum64(f * ll);
 #pragma unroll
-    for (int k = 0; k < kMergePass / 2; ++k) {
-      const int s = 2 * k + half;
+    for (int k = 0; k < kMergePass; ++k) {
       // unconditional (weight 0 past cnt, x finite): a guarded FMA would let the
-      // compiler sink the load of x[k] into the guard
-      const float fs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(f), s));
-      acc = fmaf(s < cnt ? fs : 0.f, x[k], acc);
+      // compiler sink the loads of x into the guard
+      const float fs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(f), k));
+      const float wk = k < cnt ? fs : 0.f;
+      acc0 = fmaf(wk, x0[k], acc0);
+      acc1 = fmaf(wk, x1[k], acc1);
     }
     M = Mn;
   }
-  red[half][c] = acc;
-  __syncthreads();
-  const float a1 = red[0][c] + red[1][c];  // channel c (threads c and c + 128 alike)
   float* dst = p.out + ((int64_t)b * p.hq + hq) * kD;
   if (!int2) {
-    if (tid < kD) dst[tid] = lsum > 0.f ? a1 / lsum : 0.f;
+    if (active) {
+      dst[lane] = lsum > 0.f ? acc0 / lsum : 0.f;
+      dst[lane + 64] = lsum > 0.f ? acc1 / lsum : 0.f;
+    }
     return;
   }
-  // o1 = R_V^T a1 from the register tile, partial sums over 8 rows per thread
-  float o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float aj = red[0][8 * jg + j] + red[1][8 * jg + j];
-    const uint32_t u[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[2 * i] = fmaf(bf16lo(u[i]), aj, o[2 * i]);
-      o[2 * i + 1] = fmaf(bf16hi(u[i]), aj, o[2 * i + 1]);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o1p[jg][8 * cg + i] = o[i];
+  a1s[wave][lane] = acc0;
+  a1s[wave][lane + 64] = acc1;
   __syncthreads();
-  if (tid < kD) {
-    float o1 = 0.f;
+  // o1 = R_V^T a1 of every head from the register tile, partial sums over 8 rows per thread
+  for (int m = 0; m < mh; ++m) {
+    float o[8];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) o1 += o1p[k][tid];
-    float Mx = M;
+    for (int i = 0; i < 8; ++i) o[i] = 0.f;
 #pragma unroll
-    for (int cc = 0; cc < kMergeWin; ++cc) Mx = fmaxf(Mx, wm[cc]);
-    for (int cc = kMergeWin; cc < nwc; ++cc) Mx = fmaxf(Mx, wp[cc * kPartStride]);
-    const float f1 = M == kNegInf ? 0.f : exp2f(M - Mx);
-    float den = f1 * lsum, num = f1 * o1;
+    for (int j = 0; j < 8; ++j) {
+      const float aj = a1s[m][8 * jg + j];
+      const uint32_t u[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
 #pragma unroll
-    for (int cc = 0; cc < kMergeWin; ++cc) {
-      const float f2 = wm[cc] == kNegInf ? 0.f : exp2f(wm[cc] - Mx);
-      den = fmaf(f2, wl[cc], den);
-      num = fmaf(f2, wv[cc], num);
+      for (int i = 0; i < 4; ++i) {
+        o[2 * i] = fmaf(bf16lo(u[i]), aj, o[2 * i]);
+        o[2 * i + 1] = fmaf(bf16hi(u[i]), aj, o[2 * i + 1]);
+      }
     }
-    for (int cc = kMergeWin; cc < nwc; ++cc) {
-      const float* wc = wp + cc * kPartStride;
-      const float m2 = wc[0];
-      const float f2 = m2 == kNegInf ? 0.f : exp2f(m2 - Mx);
-      den = fmaf(f2, wc[1], den);
-      num = fmaf(f2, wc[2 + tid], num);
-    }
-    dst[tid] = den > 0.f ? num / den : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o1p[m][jg][8 * cg + i] = o[i];
   }
+  __syncthreads();
+  if (!active) return;
+  float o1[2] = {0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    o1[0] += o1p[wave][k][lane];
+    o1[1] += o1p[wave][k][lane + 64];
+  }
+  float Mx = M;
+#pragma unroll
+  for (int cc = 0; cc < kMergeWin; ++cc) Mx = fmaxf(Mx, wm[cc]);
+  for (int cc = kMergeWin; cc < nwc; ++cc) Mx = fmaxf(Mx, wp[cc * kPartStride]);
+  const float f1 = M == kNegInf ? 0.f : exp2f(M - Mx);
+  float den = f1 * lsum, num0 = f1 * o1[0], num1 = f1 * o1[1];
+#pragma unroll
+  for (int cc = 0; cc < kMergeWin; ++cc) {
+    const float f2 = wm[cc] == kNegInf ? 0.f : exp2f(wm[cc] - Mx);
+    den = fmaf(f2, wl[cc], den);
+    num0 = fmaf(f2, wv0[cc], num0);
+    num1 = fmaf(f2, wv1[cc], num1);
+  }
+  for (int cc = kMergeWin; cc < nwc; ++cc) {
+    const float* wc = wp + cc * kPartStride;
+    const float m2 = wc[0];
+    const float f2 = m2 == kNegInf ? 0.f : exp2f(m2 - Mx);
+    den = fmaf(f2, wc[1], den);
+    num0 = fmaf(f2, wc[2 + lane], num0);
+    num1 = fmaf(f2, wc[2 + 64 + lane], num1);
+  }
+  dst[lane] = den > 0.f ? num0 / den : 0.f;
+  dst[lane + 64] = den > 0.f ? num1 / den : 0.f;
 }
 
 template <int G>
@@ -1148,7 +1177,12 @@ int launch_decode(bool int2, const SplitParams& sp, const uint16_t* r_k, int bat
   }
   if (hipGetLastError() != hipSuccess) return OSCAR_EHIP;
   timing_record_end(s, slot);
-  merge_kernel<<<dim3(sp.hq, batch), 256, 0, s>>>(sp, G);
+  // heads per merge workgroup: the R_V tile is loaded once for all of them,
+  // as long as about two workgroups per CU remain
+  int mh = 1;
+  while (2 * mh <= kMergeHeads && 2 * mh <= G && (int64_t)batch * sp.hq / (2 * mh) >= 2 * (int64_t)device_cu_count())
+    mh *= 2;
+  merge_kernel<<<dim3(sp.hq / mh, batch), 256, 0, s>>>(sp, G, mh);
   return hipGetLastError() == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
 }
 
