@@ -23,7 +23,8 @@ uncentred second moments; eigenvectors as columns, sorted by descending
 eigenvalue, sign fixed so the largest-magnitude entry of each is positive;
 value weights = total softmax mass each calibration token receives; Sylvester
 Hadamard scaled by 1/sqrt(d); R = P_br . (H/sqrt d) . U^T acting on column
-vectors; one quantisation group = the 128 rotated channels of one token; float
+vectors; one quantisation group = g consecutive rotated channels of one token
+(g = 128, the whole token, by default; 64 or 32 for the finer variant); float
 zero point = group minimum; fp16 RNE for scale and zero; codes rounded half to
 even from the stored fp16 scale/zero, clamped to [0, 3].
 
@@ -43,20 +44,31 @@ import math
 import numpy as np
 
 # ---------------------------------------------------------------------------
-# Page-block layout (per page, per KV head, 1152 bytes)
+# Page-block layout (per page, per KV head, 1152 bytes at group size 128)
 #   [   0,  512)  K codes: 16 token rows x 32 B; channel c of a row in byte
 #                 8 ((c >> 2) & 3) + (c >> 4), bits 2 (c & 3) (see k_row_byte)
 #   [ 512, 1024)  V codes: 128 channel words x 4 B; token slot j at bit 2j
 #   [1024, 1152)  16 token records of 8 bytes: fp16 K scale, K zero, V scale, V zero
-# Pool = uint8 [n_pages][Hkv][1152].  Window ring = bf16 [B][W][Hkv][d], slot pos % W.
+# With groups of g < 128 channels (ng = 128 / g per token) the records grow to
+# 16 x ng: the record of group j of slot t sits at 1024 + 8 (ng t + j), and the
+# block is 1024 + 128 ng bytes (block_bytes).
+# Pool = uint8 [n_pages][Hkv][block bytes].  Window ring = bf16 [B][W][Hkv][d], slot pos % W.
 # bf16 comparator pool = bf16 [n_pages][Hkv][4096]: K rows [16 slots][d], then V
 # transposed [d][16 slots] (see append_bf16_ref).
 # ---------------------------------------------------------------------------
 D = 128
 PAGE = 16
 K_CODES, V_CODES, META, BLOCK = 0, 512, 1024, 1152
-# fields of a token's 8-byte record at META + 8 * slot
+# fields of a token's 8-byte record at META + 8 * slot (per group: META + 8 (ng slot + j))
 K_SCALE, K_ZERO, V_SCALE, V_ZERO = 0, 2, 4, 6
+GROUP_SIZES = (32, 64, 128)
+
+
+def block_bytes(group: int = D) -> int:
+    """Bytes of one (page, KV head) block: 1024 of K and V codes plus one 8-byte
+    record per token and group."""
+    assert group in GROUP_SIZES
+    return META + 8 * PAGE * (D // group)
 
 
 # ---------------------------------------------------------------------------
@@ -230,6 +242,17 @@ def quantize(xr: np.ndarray):
     return c, s, z, dict(sigma=sigma, m=m, t=t)
 
 
+def quantize_groups(xr: np.ndarray, group: int = D):
+    """``quantize`` applied to each run of ``group`` consecutive rotated channels
+    [P1 «Что придумали в Together AI»: per-token asymmetric 2-bit groups; a group
+    shorter than the token is the finer variant with more scale/zero metadata].
+    Returns codes int64 [..., d] and s, z fp64 [..., d / group]."""
+    xr = np.asarray(xr, dtype=np.float64)
+    ng = D // group
+    c, s, z, _ = quantize(xr.reshape(xr.shape[:-1] + (ng, group)))
+    return c.reshape(xr.shape), s, z
+
+
 def k_row_byte(c):
     """Byte of a K row holding channel c (its bits: 2 (c mod 4) .. +1).  The row is
     four 8-byte segments; segment s holds channels 16 m + 4 s + i (m = 0..7 is the
@@ -267,18 +290,18 @@ def unpack_v_words(words: np.ndarray) -> np.ndarray:
     return ((w >> sh) & 3).astype(np.int64)
 
 
-def _put_fp16(block, field, slot, bits):
-    a = META + 8 * slot + field
+def _put_fp16(block, field, slot, bits, grp: int = 0, ng: int = 1):
+    a = META + 8 * (ng * slot + grp) + field
     block[a: a + 2] = np.array([bits], dtype=np.uint16).view(np.uint8)
 
 
 def append_ref(r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,
-               pool, win_k, win_v, window: int, n_sink: int = 0):
+               pool, win_k, win_v, window: int, n_sink: int = 0, group: int = D):
     """Write each token into the paged INT2 cache and, if recent or a sink, the
     bf16 ring.
 
     r_k, r_v: fp64 [Hkv][d][d] (bf16 values as data); k_new, v_new: bf16 bits
-    [T][Hkv][d]; pool uint8 [n_pages][Hkv][1152] and rings bf16 bits
+    [T][Hkv][d]; pool uint8 [n_pages][Hkv][block_bytes(group)] and rings bf16 bits
     [B][W + n_sink][Hkv][d] are updated in place.  Token i lands in page
     block_table[b][pos // 16], slot pos % 16; its raw bf16 k/v also go to ring
     row pos % W when pos >= seq_len_after[b] - W, and to ring row W + pos when
@@ -289,8 +312,9 @@ def append_ref(r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,
     # x'[t, h] = R[h] x[t, h]
     kr = np.einsum("hij,thj->thi", np.asarray(r_k, np.float64), bf16_to_f64(k_new))
     vr = np.einsum("hij,thj->thi", np.asarray(r_v, np.float64), bf16_to_f64(v_new))
-    kc, ks, kz, _ = quantize(kr)
-    vc, vs, vz, _ = quantize(vr)
+    ng = D // group
+    kc, ks, kz = quantize_groups(kr, group)                 # s, z: [T][Hkv][ng]
+    vc, vs, vz = quantize_groups(vr, group)
     ksb, kzb, vsb, vzb = fp16_bits(ks), fp16_bits(kz), fp16_bits(vs), fp16_bits(vz)
     krow = pack_k_row(kc)                                   # [T][Hkv][32]
     for i in range(k_new.shape[0]):
@@ -305,10 +329,11 @@ def append_ref(r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,
             words &= ~np.uint32(3 << (2 * slot))
             words |= (vc[i, h].astype(np.uint32) << np.uint32(2 * slot))
             blk[V_CODES:V_CODES + 512] = words.astype("<u4").view(np.uint8)
-            _put_fp16(blk, K_SCALE, slot, ksb[i, h])
-            _put_fp16(blk, K_ZERO, slot, kzb[i, h])
-            _put_fp16(blk, V_SCALE, slot, vsb[i, h])
-            _put_fp16(blk, V_ZERO, slot, vzb[i, h])
+            for j in range(ng):
+                _put_fp16(blk, K_SCALE, slot, ksb[i, h, j], j, ng)
+                _put_fp16(blk, K_ZERO, slot, kzb[i, h, j], j, ng)
+                _put_fp16(blk, V_SCALE, slot, vsb[i, h, j], j, ng)
+                _put_fp16(blk, V_ZERO, slot, vzb[i, h, j], j, ng)
         if window > 0 and p >= int(seq_len_after[b]) - window:
             win_k[b, p % window] = k_new[i]
             win_v[b, p % window] = v_new[i]
@@ -317,20 +342,24 @@ def append_ref(r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,
             win_v[b, window + p] = v_new[i]
 
 
-def read_history(pool, block_table_row, hist: int, h: int):
+def read_history(pool, block_table_row, hist: int, h: int, group: int = D):
     """Dequantised rotated history of one (sequence, KV head): (k', v') fp64 [hist][d].
-    x' = z + c s with the stored fp16 z, s."""
+    x'_c = z + code_c s with the stored fp16 z, s of channel c's group."""
     n_pg = -(-hist // PAGE)
+    ng = D // group
     pages = np.asarray(block_table_row[:n_pg], dtype=np.int64)
     assert np.all(pages >= 0)
-    blk = pool[pages, h]                                    # [n_pg][1152]
+    blk = pool[pages, h]                                    # [n_pg][block bytes]
+    assert blk.shape[-1] == block_bytes(group)
     kc = unpack_k_rows(blk[:, K_CODES:K_CODES + 512].reshape(n_pg, PAGE, 32))
     vc = unpack_v_words(v_words(blk))                       # [n_pg][16][128]
-    meta = np.ascontiguousarray(blk[:, META:BLOCK]).view(np.uint16).reshape(n_pg, PAGE, 4)
-    ks, kz, vs, vz = (fp16_to_f64(meta[..., f // 2]) for f in (K_SCALE, K_ZERO, V_SCALE, V_ZERO))
+    meta = np.ascontiguousarray(blk[:, META:]).view(np.uint16).reshape(n_pg, PAGE, ng, 4)
+    # each group's value spread over its channels: [n_pg][16][128]
+    ks, kz, vs, vz = (np.repeat(fp16_to_f64(meta[..., f // 2]), group, axis=-1)
+                      for f in (K_SCALE, K_ZERO, V_SCALE, V_ZERO))
     with np.errstate(invalid="ignore", over="ignore"):  # unused slots of the last page
-        k = kz[..., None] + kc * ks[..., None]
-        v = vz[..., None] + vc * vs[..., None]
+        k = kz + kc * ks
+        v = vz + vc * vs
     return k.reshape(-1, D)[:hist], v.reshape(-1, D)[:hist]
 
 
@@ -343,7 +372,7 @@ def read_history(pool, block_table_row, hist: int, h: int):
 # ---------------------------------------------------------------------------
 
 def decode_ref(r_k, r_v, q_bits, seq_lens, block_table, pool, win_k, win_v,
-               window: int, pairs=None, n_sink: int = 0):
+               window: int, pairs=None, n_sink: int = 0, group: int = D):
     """Softmax attention of one query token per (sequence, q head) over the
     dequantised cache, fp64.  With w = min(n, W) and s = min(n_sink, n - w):
     positions [0, s) come from the bf16 sink rows W + pos of the ring, [s, n - w)
@@ -366,7 +395,7 @@ def decode_ref(r_k, r_v, q_bits, seq_lens, block_table, pool, win_k, win_v,
         w = min(n, window)
         hist = n - w
         ns = min(n_sink, hist)
-        kh, vh = read_history(pool, block_table[b], hist, h) if hist > 0 else (np.zeros((0, d)), np.zeros((0, d)))
+        kh, vh = read_history(pool, block_table[b], hist, h, group) if hist > 0 else (np.zeros((0, d)), np.zeros((0, d)))
         kh, vh = kh[ns:], vh[ns:]
         # plain-domain rows: sinks (rows W + pos), then the window (rows pos % W)
         rows = np.concatenate([window + np.arange(ns), np.arange(hist, n) % max(window, 1)]).astype(np.int64)
@@ -459,10 +488,10 @@ def bf16_kv_bytes_per_token(n_layers: int, n_kv_heads: int, d: int) -> int:
 
 
 def decode_direct_ref(r_k, r_v, q_bits, k_bits, v_bits, n: int, window: int, kv_head: int,
-                      n_sink: int = 0):
+                      n_sink: int = 0, group: int = D):
     """Decode of one (sequence, KV head) straight from its token sequence, with
     no pool or ring: with w = min(n, W) and s = min(n_sink, n - w), positions
-    [s, n - w) are encoded with ``quantize`` (the cache's content by definition),
+    [s, n - w) are encoded with ``quantize_groups`` (the cache's content by definition),
     positions [0, s) and the last w are the raw bf16 tokens.  Same attention as
     ``decode_ref``.  q_bits [G][d] (the G query heads of this KV head); k_bits,
     v_bits [>= n][d].  Returns fp64 [G][d]."""
@@ -474,10 +503,11 @@ def decode_direct_ref(r_k, r_v, q_bits, k_bits, v_bits, n: int, window: int, kv_
     rv = np.asarray(r_v[kv_head], np.float64)
     kx = bf16_to_f64(np.asarray(k_bits)[:n])
     vx = bf16_to_f64(np.asarray(v_bits)[:n])
-    ck, sk, zk, _ = quantize(rotate(rk, kx[ns:hist]))
-    cv, sv, zv, _ = quantize(rotate(rv, vx[ns:hist]))
-    kh = zk[:, None] + ck * sk[:, None]
-    vh = zv[:, None] + cv * sv[:, None]
+    ck, sk, zk = quantize_groups(rotate(rk, kx[ns:hist]), group)
+    cv, sv, zv = quantize_groups(rotate(rv, vx[ns:hist]), group)
+    grp = np.arange(D) // group                     # group of each channel
+    kh = zk[:, grp] + ck * sk[:, grp]
+    vh = zv[:, grp] + cv * sv[:, grp]
     plain = np.r_[0:ns, hist:n]
     q = bf16_to_f64(q_bits)
     out = np.empty((q.shape[0], d))
@@ -490,11 +520,11 @@ def decode_direct_ref(r_k, r_v, q_bits, k_bits, v_bits, n: int, window: int, kv_
 
 
 def append_sequence_ref(r_k, r_v, k_bits, v_bits, block_row, pool, win_k, win_v, window: int,
-                        n_sink: int = 0):
+                        n_sink: int = 0, group: int = D):
     """Bulk form of ``append_ref`` for positions 0..n-1 of one sequence appended
     in order (seq_len_after = n): whole pages are packed at once.  Produces the
     same bytes as ``append_ref`` (pinned by a test).  k_bits, v_bits [n][Hkv][d];
-    block_row int32 [max_pages]; pool [n_pages][Hkv][1152]; win_k, win_v
+    block_row int32 [max_pages]; pool [n_pages][Hkv][block_bytes(group)]; win_k, win_v
     [W + n_sink][Hkv][d] (this sequence's ring)."""
     k_bits = np.asarray(k_bits)
     n, hkv, _ = k_bits.shape
@@ -503,8 +533,9 @@ def append_sequence_ref(r_k, r_v, k_bits, v_bits, block_row, pool, win_k, win_v,
     for h in range(hkv):   # x' = R x for every token (library matmul per head)
         kr[:, h] = bf16_to_f64(k_bits[:, h]) @ np.asarray(r_k[h], np.float64).T
         vr[:, h] = bf16_to_f64(np.asarray(v_bits)[:, h]) @ np.asarray(r_v[h], np.float64).T
-    kc, ks, kz, _ = quantize(kr)
-    vc, vs, vz, _ = quantize(vr)
+    ng = D // group
+    kc, ks, kz = quantize_groups(kr, group)                        # s, z: [n][Hkv][ng]
+    vc, vs, vz = quantize_groups(vr, group)
     del kr, vr
     n_pg = -(-n // PAGE)
     pad = n_pg * PAGE - n
@@ -520,7 +551,7 @@ def append_sequence_ref(r_k, r_v, k_bits, v_bits, block_row, pool, win_k, win_v,
     nslot[-1] = PAGE - pad
     for j, pg in enumerate(pages):
         m = slots < nslot[j]
-        blk = pool[pg]                                              # [Hkv][1152]
+        blk = pool[pg]                                              # [Hkv][block bytes]
         kb = blk[:, K_CODES:K_CODES + 512].reshape(hkv, PAGE, 32)
         kb[:, m] = krow[j][m].transpose(1, 0, 2)
         words = np.ascontiguousarray(blk[:, V_CODES:V_CODES + 512]).view("<u4").copy()  # [Hkv][128]
@@ -528,9 +559,12 @@ def append_sequence_ref(r_k, r_v, k_bits, v_bits, block_row, pool, win_k, win_v,
         words &= keep
         words |= np.bitwise_or.reduce((vcode[j][m] << (2 * slots[m])[:, None, None].astype(np.uint32)), axis=0)
         blk[:, V_CODES:V_CODES + 512] = words.astype("<u4").view(np.uint8).reshape(hkv, 512)
-        rec = blk[:, META:BLOCK].reshape(hkv, PAGE, 4, 2)                # [h][slot][field][2 bytes]
+        rec = blk[:, META:].reshape(hkv, PAGE, ng, 4, 2)           # [h][slot][group][field][2 bytes]
         for f, b in bits.items():
-            rec[:, m, f // 2] = np.ascontiguousarray(b[j * PAGE:(j + 1) * PAGE][m].T).view(np.uint8).reshape(hkv, -1, 2)
+            # b: [n][Hkv][ng] -> this page's live slots as [h][slot][group]
+            src = np.ascontiguousarray(b[j * PAGE:(j + 1) * PAGE][m].transpose(1, 0, 2))
+            field = rec[:, :, :, f // 2]                           # view [h][slot][group][2 bytes]
+            field[:, m] = src.view(np.uint8).reshape(hkv, -1, ng, 2)
     if window > 0:
         for p in range(max(0, n - window), n):
             win_k[p % window] = k_bits[p]

@@ -23,13 +23,13 @@ def orthogonal(rng, hkv):
     return np.stack([np.linalg.qr(rng.standard_normal((128, 128)))[0] for _ in range(hkv)])
 
 
-def build(rng, lens, window, hq=8, hkv=2, cfg=1, rot=None, n_sink=0):
+def build(rng, lens, window, hq=8, hkv=2, cfg=1, rot=None, n_sink=0, group=128):
     s = wl.spec(cfg, batch=len(lens))
     s.seq_lens = np.asarray(lens, dtype=np.int32)
     s.window = window
     s.n_q_heads, s.n_kv_heads = hq, hkv
     bt, n_pages = wl.page_table(s)
-    pool = np.zeros((n_pages, hkv, ref.BLOCK), dtype=np.uint8)
+    pool = np.zeros((n_pages, hkv, ref.block_bytes(group)), dtype=np.uint8)
     win_k = np.zeros((len(lens), max(window + n_sink, 1), hkv, 128), dtype=np.uint16)
     win_v = np.zeros_like(win_k)
     rk, rv = rot if rot is not None else (orthogonal(rng, hkv), orthogonal(rng, hkv))
@@ -39,16 +39,17 @@ def build(rng, lens, window, hq=8, hkv=2, cfg=1, rot=None, n_sink=0):
         k, v = k[:, :hkv], v[:, :hkv]
         n = k.shape[0]
         ref.append_ref(rk, rv, k, v, np.full(n, b, np.int32), np.arange(n, dtype=np.int32),
-                       bt, s.seq_lens, pool, win_k, win_v, window, n_sink)
+                       bt, s.seq_lens, pool, win_k, win_v, window, n_sink, group)
         kv[b] = (k, v)
     q = wl.decode_queries(s)[:, :hq]
     return s, bt, pool, win_k, win_v, rk, rv, kv, q
 
 
-def brute_force(q_bits, kv, lens, window, rk, rv, hkv, n_sink=0):
+def brute_force(q_bits, kv, lens, window, rk, rv, hkv, n_sink=0, group=128):
     """Pure-Python textbook attention over the dequantised, un-rotated cache
     (positions below min(n_sink, n - w) and the last w = min(n, W) are the raw
-    bf16 tokens)."""
+    bf16 tokens).  Each run of ``group`` rotated channels is encoded on its own
+    with the single-group encoder."""
     bsz, hq, d = q_bits.shape
     g = hq // hkv
     out = np.zeros((bsz, hq, d))
@@ -61,13 +62,18 @@ def brute_force(q_bits, kv, lens, window, rk, rv, hkv, n_sink=0):
             h = j // g
             kx = ref.bf16_to_f64(k_bits[:, h])
             vx = ref.bf16_to_f64(v_bits[:, h])
-            ck, sk, zk, _ = ref.quantize(ref.rotate(rk[h], kx))
-            cv, sv, zv, _ = ref.quantize(ref.rotate(rv[h], vx))
+            kx_r, vx_r = ref.rotate(rk[h], kx), ref.rotate(rv[h], vx)
+            k_hat, v_hat = np.empty_like(kx_r), np.empty_like(vx_r)
+            for c0 in range(0, d, group):
+                ck, sk, zk, _ = ref.quantize(kx_r[:, c0:c0 + group])
+                cv, sv, zv, _ = ref.quantize(vx_r[:, c0:c0 + group])
+                k_hat[:, c0:c0 + group] = zk[:, None] + ck * sk[:, None]
+                v_hat[:, c0:c0 + group] = zv[:, None] + cv * sv[:, None]
             keys, vals = [], []
             for t in range(n):
                 if ns <= t < hist:
-                    kr = zk[t] + ck[t] * sk[t]
-                    vr = zv[t] + cv[t] * sv[t]
+                    kr = k_hat[t]
+                    vr = v_hat[t]
                     keys.append(rk[h].T @ kr)
                     vals.append(rv[h].T @ vr)
                 else:
