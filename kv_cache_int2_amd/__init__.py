@@ -19,10 +19,10 @@ __all__ = [
     "OscarError", "OscarShape", "make_shape", "oscar_calibrate", "oscar_quantize_append",
     "oscar_decode_workspace_bytes", "oscar_decode_attn", "oscar_bf16_append",
     "oscar_bf16_decode_attn", "oscar_hbm_copy", "oscar_timing_begin", "oscar_timing_end",
-    "oscar_strerror", "BLOCK_BYTES", "BF16_BLOCK_ELEMS", "PAGE_SIZE", "HEAD_DIM",
+    "oscar_strerror", "BLOCK_BYTES", "BF16_BLOCK_ELEMS", "PAGE_SIZE", "HEAD_DIM", "block_bytes",
 ]
 
-BLOCK_BYTES = 1152
+BLOCK_BYTES = 1152  # bytes per (page, KV head) block at group size 128
 BF16_BLOCK_ELEMS = 4096  # bf16 comparator pool: K [16][128] then V^T [128][16] per (page, KV head)
 PAGE_SIZE = 16
 HEAD_DIM = 128
@@ -37,6 +37,21 @@ class OscarError(RuntimeError):
 def make_shape(n_q_heads: int, n_kv_heads: int, window: int = 128, head_dim: int = 128,
                group_size: int = 128, page_size: int = 16, n_sink: int = 0) -> OscarShape:
     return OscarShape(n_q_heads, n_kv_heads, head_dim, group_size, page_size, window, n_sink)
+
+
+def block_bytes(group_size: int = 128) -> int:
+    """Bytes per (page, KV head) block of the INT2 pool: 1024 of codes plus one
+    8-byte record per token and quantisation group (1152, 1280, 1536 for
+    groups of 128, 64, 32 channels)."""
+    return 1024 + 8 * PAGE_SIZE * (HEAD_DIM // group_size)
+
+
+def _check_pool(shape, pool) -> None:
+    if pool is None:
+        return
+    want = shape.n_kv_heads * block_bytes(shape.group_size) if shape.group_size in (32, 64, 128) else None
+    if want is not None and pool.numel() != pool.shape[0] * want:
+        raise ValueError(f"pool: expected [n_pages][{shape.n_kv_heads}][{block_bytes(shape.group_size)}] bytes")
 
 
 def _check(fn: str, status: int) -> None:
@@ -99,6 +114,7 @@ def oscar_calibrate(shape: OscarShape, q_cal: np.ndarray, k_cal: np.ndarray, v_c
 def oscar_quantize_append(shape, r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,
                           pool, win_k=None, win_v=None, stream=None) -> None:
     b16, i32, u8, _ = _dt()
+    _check_pool(shape, pool)
     _check("oscar_quantize_append", lib.oscar_quantize_append(
         C.byref(shape), _dev(r_k, b16, "r_k"), _dev(r_v, b16, "r_v"), _dev(k_new, b16, "k_new"),
         _dev(v_new, b16, "v_new"), int(k_new.shape[0]), _dev(seq_idx, i32, "seq_idx"),
@@ -117,6 +133,7 @@ def oscar_decode_workspace_bytes(shape, batch: int, max_seq_len: int) -> int:
 def oscar_decode_attn(shape, r_k, r_v, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v,
                       out, workspace, stream=None) -> None:
     b16, i32, u8, f32 = _dt()
+    _check_pool(shape, pool)
     _check("oscar_decode_attn", lib.oscar_decode_attn(
         C.byref(shape), _dev(r_k, b16, "r_k"), _dev(r_v, b16, "r_v"), _dev(q, b16, "q"),
         int(q.shape[0]), _dev(seq_lens, i32, "seq_lens"), int(max_seq_len),

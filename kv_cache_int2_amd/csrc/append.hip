@@ -19,6 +19,10 @@
 //    a partial page falls back to per-token atomic and/or on the channel words.
 // The k-slot -> input channel map (lane group g, step s, slot j -> 32g + 8s + j)
 // is the same for both operands, so the hardware's internal k order is moot.
+// Groups: with NG = 128 / g groups per token, group j is rotated channels
+// [g j, g (j + 1)); the channels 16m + .. a lane holds for accumulator m all fall
+// in group m NG / 8, so each group's min and max are reduced on their own and
+// every group of every token gets its own record at 1024 + 8 (NG slot + j).
 // Codes: t = (x' - z) / s is evaluated as x' * (1/s) - z * (1/s) (one FMA; the
 // reciprocal once per token); it differs from the quotient by a few ulp, so a
 // code can only differ next to a rounding boundary.  The scale itself is the
@@ -39,6 +43,7 @@ struct AppendParams {
   const int32_t* block_table;
   const int32_t* len_after;
   uint8_t* pool;
+  int block;   // bytes per (page, KV head) block: 1024 + 128 NG
   int64_t n_tokens;
   int64_t n_pages;
   int batch, max_pages, hkv, window, tiles_per_wg;
@@ -109,7 +114,7 @@ __device__ __forceinline__ TokInfo resolve(const AppendParams& p, int64_t tok, i
   if (b < 0 || b >= p.batch || ps < 0 || (ps >> 4) >= p.max_pages) return ti;
   int page = p.block_table[(int64_t)b * p.max_pages + (ps >> 4)];
   if (page < 0 || page >= p.n_pages) return ti;
-  ti.blk = p.pool + ((int64_t)page * p.hkv + h) * kBlock;
+  ti.blk = p.pool + ((int64_t)page * p.hkv + h) * p.block;
   ti.slot = ps & 15;
   ti.b = b;
   ti.pos = ps;
@@ -118,10 +123,11 @@ __device__ __forceinline__ TokInfo resolve(const AppendParams& p, int64_t tok, i
   return ti;
 }
 
-template <int KIND>
+template <int KIND, int NG>
 __device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4* r_lds, int64_t t0, int h,
                                               int lane) {
   constexpr int NT = kAppendTiles;
+  constexpr int MPG = 8 / NG;  // accumulators m per group
   const int g = lane >> 4, r = lane & 15;
 
   // X operand of tile j: token t0 + 16 j + r, input channels 32g .. 32g + 31
@@ -168,53 +174,82 @@ __device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4
 
     if (KIND == 0) {
       // acc[j][m][i] = x'[token tj + r][channel 16m + 4g + i]: row segment g
-      float mn = acc[j][0][0], mx = acc[j][0][0];
+      Quant q[NG];
 #pragma unroll
-      for (int m = 0; m < 8; ++m)
+      for (int gr = 0; gr < NG; ++gr) {
+        float mn = acc[j][gr * MPG][0], mx = acc[j][gr * MPG][0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          mn = fminf(mn, acc[j][m][i]);
-          mx = fmaxf(mx, acc[j][m][i]);
-        }
-      const Quant q = quant_params(min_rows(mn), max_rows(mx));
+        for (int m = gr * MPG; m < (gr + 1) * MPG; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            mn = fminf(mn, acc[j][m][i]);
+            mx = fmaxf(mx, acc[j][m][i]);
+          }
+        q[gr] = quant_params(min_rows(mn), max_rows(mx));
+      }
       uint32_t w[2] = {0u, 0u};
 #pragma unroll
       for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[m >> 2] |= encode(acc[j][m][i], q.inv, q.zi) << (8 * (m & 3) + 2 * i);
+        for (int i = 0; i < 4; ++i)
+          w[m >> 2] |= encode(acc[j][m][i], q[m / MPG].inv, q[m / MPG].zi) << (8 * (m & 3) + 2 * i);
       if (ti.blk) {
         *reinterpret_cast<uint2*>(ti.blk + kKCodes + 32 * ti.slot + 8 * g) = make_uint2(w[0], w[1]);
-        if (g == 0) *reinterpret_cast<uint32_t*>(ti.blk + kMeta + 8 * ti.slot) = q.sz;
+        // lane group g < NG writes group g's K scale and zero
+#pragma unroll
+        for (int gr = 0; gr < NG; ++gr)
+          if (g == gr) *reinterpret_cast<uint32_t*>(ti.blk + kMeta + 8 * (NG * ti.slot + gr)) = q[gr].sz;
       }
     } else {
       // acc[j][m][i] = x'[token tj + 4g + i][channel 16m + r]
-      float mn[4], mx[4];
+      float mn[4][NG], mx[4][NG];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        mn[i] = acc[j][0][i];
-        mx[i] = acc[j][0][i];
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int m = 1; m < 8; ++m) {
-          mn[i] = fminf(mn[i], acc[j][m][i]);
-          mx[i] = fmaxf(mx[i], acc[j][m][i]);
+        for (int gr = 0; gr < NG; ++gr) {
+          float lo = acc[j][gr * MPG][i], hi = lo;
+#pragma unroll
+          for (int m = gr * MPG + 1; m < (gr + 1) * MPG; ++m) {
+            lo = fminf(lo, acc[j][m][i]);
+            hi = fmaxf(hi, acc[j][m][i]);
+          }
+          mn[i][gr] = row_min16(lo);
+          mx[i][gr] = row_max16(hi);
         }
-        mn[i] = row_min16(mn[i]);
-        mx[i] = row_max16(mx[i]);
-      }
-      // lane r of each quad takes token 4g + (r & 3); the quad then shares them
-      const int mi = r & 3;
-      const float mn_l = mi == 0 ? mn[0] : mi == 1 ? mn[1] : mi == 2 ? mn[2] : mn[3];
-      const float mx_l = mi == 0 ? mx[0] : mi == 1 ? mx[1] : mi == 2 ? mx[2] : mx[3];
+      // lane r of each row takes token 4g + (r & 3), group (r >> 2) mod NG; the
+      // others then read them: within the quad (NG = 1) or the row
+      const int mi = r & 3, mk = (r >> 2) % NG;
+      float mn_l = mn[0][0], mx_l = mx[0][0];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int gr = 0; gr < NG; ++gr) {
+          const bool sel = mi == i && mk == gr;
+          mn_l = sel ? mn[i][gr] : mn_l;
+          mx_l = sel ? mx[i][gr] : mx_l;
+        }
       const Quant ql = quant_params(mn_l, mx_l);
-      Quant q[4];
-      q[0] = Quant{quad_bcast<0>(ql.sz), __uint_as_float(quad_bcast<0>(__float_as_uint(ql.inv))),
-                   __uint_as_float(quad_bcast<0>(__float_as_uint(ql.zi)))};
-      q[1] = Quant{quad_bcast<1>(ql.sz), __uint_as_float(quad_bcast<1>(__float_as_uint(ql.inv))),
-                   __uint_as_float(quad_bcast<1>(__float_as_uint(ql.zi)))};
-      q[2] = Quant{quad_bcast<2>(ql.sz), __uint_as_float(quad_bcast<2>(__float_as_uint(ql.inv))),
-                   __uint_as_float(quad_bcast<2>(__float_as_uint(ql.zi)))};
-      q[3] = Quant{quad_bcast<3>(ql.sz), __uint_as_float(quad_bcast<3>(__float_as_uint(ql.inv))),
-                   __uint_as_float(quad_bcast<3>(__float_as_uint(ql.zi)))};
+      Quant q[4][NG];
+      if constexpr (NG == 1) {
+        q[0][0] = Quant{quad_bcast<0>(ql.sz), __uint_as_float(quad_bcast<0>(__float_as_uint(ql.inv))),
+                        __uint_as_float(quad_bcast<0>(__float_as_uint(ql.zi)))};
+        q[1][0] = Quant{quad_bcast<1>(ql.sz), __uint_as_float(quad_bcast<1>(__float_as_uint(ql.inv))),
+                        __uint_as_float(quad_bcast<1>(__float_as_uint(ql.zi)))};
+        q[2][0] = Quant{quad_bcast<2>(ql.sz), __uint_as_float(quad_bcast<2>(__float_as_uint(ql.inv))),
+                        __uint_as_float(quad_bcast<2>(__float_as_uint(ql.zi)))};
+        q[3][0] = Quant{quad_bcast<3>(ql.sz), __uint_as_float(quad_bcast<3>(__float_as_uint(ql.inv))),
+                        __uint_as_float(quad_bcast<3>(__float_as_uint(ql.zi)))};
+      } else {
+        const int row0 = lane & 48;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int gr = 0; gr < NG; ++gr) {
+            const int src = row0 + 4 * gr + i;
+            q[i][gr] = Quant{(uint32_t)__shfl((int)ql.sz, src), __shfl(ql.inv, src), __shfl(ql.zi, src)};
+          }
+      }
+      const bool rec_lane = r < 4 * NG;  // lane r stores the record of token 4g + mi, group mk
       // fast path: the tile's 16 tokens are slots 0..15 of one page, in order
       const int b0 = __builtin_amdgcn_readfirstlane(ti.b), pos0 = __builtin_amdgcn_readfirstlane(ti.pos);
       const uintptr_t bp = reinterpret_cast<uintptr_t>(ti.blk);
@@ -228,17 +263,15 @@ __device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4
         for (int m = 0; m < 8; ++m) {
           uint32_t d = 0;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) d |= encode(acc[j][m][i], q[i].inv, q[i].zi) << (2 * (4 * g + i));
+          for (int i = 0; i < 4; ++i) d |= encode(acc[j][m][i], q[i][m / MPG].inv, q[i][m / MPG].zi) << (2 * (4 * g + i));
           w[m] = or_rows(d);
         }
         uint32_t* vw = reinterpret_cast<uint32_t*>(blk0 + kVCodes);
 #pragma unroll
         for (int m = 0; m < 8; ++m)
           if ((m >> 1) == g) vw[16 * m + r] = w[m];
-        // token 4g + i is slot 4g + i; lane r == i stores its scale / zero
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (r == i) *reinterpret_cast<uint32_t*>(blk0 + kMeta + 8 * (4 * g + i) + 4) = q[i].sz;
+        // token 4g + i is slot 4g + i
+        if (rec_lane) *reinterpret_cast<uint32_t*>(blk0 + kMeta + 8 * (NG * (4 * g + mi) + mk) + 4) = ql.sz;
       } else {
         // per-token info of the 4 tokens this lane holds codes for
         uint8_t* tblk[4];
@@ -256,15 +289,16 @@ __device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4
 #pragma unroll
           for (int m = 0; m < 8; ++m) {
             atomicAnd(&vw[16 * m + r], clr);
-            atomicOr(&vw[16 * m + r], encode(acc[j][m][i], q[i].inv, q[i].zi) << (2 * tslot[i]));
+            atomicOr(&vw[16 * m + r], encode(acc[j][m][i], q[i][m / MPG].inv, q[i][m / MPG].zi) << (2 * tslot[i]));
           }
-          if (r == i) *reinterpret_cast<uint32_t*>(tblk[i] + kMeta + 8 * tslot[i] + 4) = q[i].sz;
+          if (rec_lane && mi == i) *reinterpret_cast<uint32_t*>(tblk[i] + kMeta + 8 * (NG * tslot[i] + mk) + 4) = ql.sz;
         }
       }
     }
   }
 }
 
+template <int NG>
 __global__ __launch_bounds__(256, 4) void append_kernel(AppendParams p) {
   __shared__ uint4 r_lds[128 * kRowU4];
   const int h = blockIdx.y;
@@ -277,9 +311,9 @@ __global__ __launch_bounds__(256, 4) void append_kernel(AppendParams p) {
     const int64_t t0 = ((int64_t)blockIdx.x * p.tiles_per_wg + it) * kAppendTokens + wave * 16 * kAppendTiles;
     if (t0 >= p.n_tokens) break;
     if (kind == 0)
-      process_tiles<0>(p, r_lds, t0, h, lane);
+      process_tiles<0, NG>(p, r_lds, t0, h, lane);
     else
-      process_tiles<1>(p, r_lds, t0, h, lane);
+      process_tiles<1, NG>(p, r_lds, t0, h, lane);
   }
 }
 
@@ -317,6 +351,7 @@ extern "C" int oscar_quantize_append(const oscar_shape* shape, const uint16_t* r
   p.block_table = block_table;
   p.len_after = seq_len_after;
   p.pool = pool;
+  p.block = block_bytes(shape->group_size);
   p.n_tokens = n_tokens;
   p.n_pages = n_pages;
   p.batch = batch;
@@ -331,7 +366,11 @@ extern "C" int oscar_quantize_append(const oscar_shape* shape, const uint16_t* r
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int slot = -1;
   timing_record_begin(s, 3, &slot);
-  append_kernel<<<grid, 256, 0, s>>>(p);
+  switch (kD / shape->group_size) {
+    case 1: append_kernel<1><<<grid, 256, 0, s>>>(p); break;
+    case 2: append_kernel<2><<<grid, 256, 0, s>>>(p); break;
+    default: append_kernel<4><<<grid, 256, 0, s>>>(p); break;
+  }
   hipError_t e = hipGetLastError();
   timing_record_end(s, slot);
   return e == hipSuccess ? OSCAR_OK : OSCAR_EHIP;

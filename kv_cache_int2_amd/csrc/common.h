@@ -12,8 +12,11 @@ namespace oscar {
 
 constexpr int kD = 128;          // head dim
 constexpr int kPage = 16;        // tokens per page
-constexpr int kBlock = 1152;     // bytes per (page, KV head) block
-constexpr int kKCodes = 0, kVCodes = 512, kMeta = 1024;  // token t's record {Ks, Kz, Vs, Vz} fp16 at kMeta + 8t
+constexpr int kBlock = 1152;     // bytes per (page, KV head) block at group size 128
+// K codes, V codes, records: the record {Ks, Kz, Vs, Vz} fp16 of group j of
+// token t sits at kMeta + 8 (NG t + j), NG = 128 / group size
+constexpr int kKCodes = 0, kVCodes = 512, kMeta = 1024;
+inline int block_bytes(int group_size) { return kMeta + 8 * kPage * (kD / group_size); }
 constexpr int kMaxWindow = 1024;
 constexpr int kWinChunk = 32;  // window tokens per decode workgroup (one window partial each)
 constexpr int kPartStride = 2 + kD;  // (m, l, acc[128]) per (batch, q head, split)
@@ -23,7 +26,8 @@ constexpr int kMaxSplit = 2048;      // tokens per split at most: 16 tiles of 12
 inline int check_shape(const oscar_shape* s) {
   if (!s) return OSCAR_EINVAL;
   if (s->n_kv_heads < 1 || s->n_q_heads < 1 || s->window < 0) return OSCAR_EINVAL;
-  if (s->head_dim != kD || s->group_size != kD || s->page_size != kPage) return OSCAR_EUNSUPPORTED;
+  if (s->head_dim != kD || s->page_size != kPage) return OSCAR_EUNSUPPORTED;
+  if (s->group_size != 32 && s->group_size != 64 && s->group_size != kD) return OSCAR_EUNSUPPORTED;
   if (s->n_q_heads % s->n_kv_heads) return OSCAR_EINVAL;
   int g = s->n_q_heads / s->n_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return OSCAR_EUNSUPPORTED;
@@ -72,10 +76,19 @@ int device_cu_count();
 inline int split_heads_per_wg(int n_kv_heads) { return n_kv_heads % 4 == 0 ? 4 : (n_kv_heads % 2 == 0 ? 2 : 1); }
 
 // Resident workgroups of the persistent INT2 split kernel.
+// Query heads of one INT2 merge unit: up to 8 at whole-token groups, up to 4
+// with finer groups (the per-group scores and weights of 8 heads exceed the
+// split kernel's register budget; a KV head with more query heads is then read
+// once per unit).
+inline int int2_unit_heads(int gqa, int ng) {
+  const int cap = ng > 1 ? 4 : 8;
+  return gqa > cap ? cap : gqa;
+}
+
 inline int split_wg_count(int gqa, int n_cu) { return (n_cu > 0 ? n_cu : 256) * split_wgs_per_cu(gqa); }
 
 // Workspace layout (bytes, each region 256-aligned):
-//   qsum         float [B][Hq]                      sum of the rotated query's channels
+//   qsum         float [B][Hq][ng]                  sums of the rotated query over each quantisation group
 //   qop          int   [B][Hkv][ceil(G/4)][64][9]   per-lane fp8 score operand (8 dwords) + E8M0 scale
 //   part         float  bf16 comparator: [B][Hq][n_splits][130] split partials (m, l, acc[128]);
 //                       INT2: [n_wg + units][4][gw][130] partials of the persistent workgroups'
@@ -86,18 +99,18 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct WorkspaceLayout {
   size_t qsum, qop, part, wpart, tile_prefix, total;
 };
-inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int window, int n_sink,
+inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int window, int n_sink, int ng,
                                         const SplitPlan& p, int n_cu) {
   const int gqa = n_q_heads / n_kv_heads;
   const size_t g4 = (size_t)((gqa + 3) / 4);
-  const size_t gw = (size_t)(gqa > 8 ? 8 : gqa);
+  const size_t gw = (size_t)int2_unit_heads(gqa, ng);
   const size_t units = (size_t)batch * n_q_heads / (gw * (size_t)split_heads_per_wg(n_kv_heads));
   const size_t part_bf16 = (size_t)batch * n_q_heads * p.n_splits * kPartStride;
   const size_t n_wg = (size_t)split_wg_count(gqa, n_cu);
   const size_t part_int2 = (n_wg + units) * 4 * gw * kPartStride;
   WorkspaceLayout w{};
   w.qsum = 0;
-  w.qop = w.qsum + align256((size_t)batch * n_q_heads * sizeof(float));
+  w.qop = w.qsum + align256((size_t)batch * n_q_heads * ng * sizeof(float));
   w.part = w.qop + align256((size_t)batch * n_kv_heads * g4 * 64 * 9 * sizeof(int));
   w.wpart = w.part + align256((part_bf16 > part_int2 ? part_bf16 : part_int2) * sizeof(float));
   const size_t n_wchunks = (size_t)((window + kWinChunk - 1) / kWinChunk + (n_sink + kWinChunk - 1) / kWinChunk);

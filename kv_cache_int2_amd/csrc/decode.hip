@@ -108,7 +108,7 @@ __device__ __forceinline__ int exponent_above(float x) {  // E with |x| < 2^E (0
 }
 
 struct SplitParams {
-  const float* qsum;          // [B][Hq]      (INT2 path)
+  const float* qsum;          // [B][Hq][ng]  (INT2 path) sums of q' over each quantisation group
   const int* qop;             // [B][Hkv][ceil(G/4)][64][9] (INT2 path)
   const uint16_t* q;          // [B][Hq][128] bf16 queries
   const int32_t* seq_lens;
@@ -132,6 +132,8 @@ struct SplitParams {
   int gw;                     // query heads a unit really has (<= G of the kernel's instantiation)
   int n_wg;                   // INT2: persistent workgroups of the split kernel
   int hw;                     // INT2: KV heads a split workgroup reads side by side (1, 2 or 4)
+  int block;                  // INT2: bytes per (page, KV head) block, 1024 + 128 ng
+  int ng;                     // INT2: quantisation groups per token (1, 2 or 4)
   float scale_log2;           // log2(e) / sqrt(d)
 };
 
@@ -252,7 +254,7 @@ __device__ void window_chunk(const SplitParams& p, int b, int h, int c, int G, f
 // Query preparation, once per (sequence, KV head):
 //   q' = R_K[h] q for its G query heads (thread pair (c, half): 64 inputs of
 //   output channel c from 8 x 16-byte loads of R's row);
-//   qsum[head] = sum_c q'_c;
+//   qsum[head][j] = sum of q'_c over the channels c of quantisation group j;
 //   the fp8 score operand of every 4-head group: lane (lg, lr) holds term lr%4 of
 //   q'_(head lr/4) at the 32 channels its k-slots map to, plus the row's E8M0
 //   scale (2^(E - 7 - 4 term), |q'| < 2^E), exactly as the split kernel's MFMA
@@ -316,8 +318,9 @@ __global__ __launch_bounds__(256) void prep_kernel(SplitParams p, const uint16_t
     }
   }
   __syncthreads();
-  if (tid < G * 16) {  // 16 threads per head: sum and max |q'|
+  if (tid < G * 16) {  // 16 threads per head: group sums and max |q'|
     const int g = tid >> 4, j = tid & 15;
+    const int tpg = 16 / p.ng;  // threads per group (8 channels each)
     float s = 0.f, mx = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -326,13 +329,12 @@ __global__ __launch_bounds__(256) void prep_kernel(SplitParams p, const uint16_t
     }
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) {
-      s += __shfl_xor(s, o);
+      const float so = __shfl_xor(s, o);
+      s = o < tpg ? s + so : s;
       mx = fmaxf(mx, __shfl_xor(mx, o));
     }
-    if (j == 0) {
-      qsum_out[(int64_t)b * hq + h * G + g] = s;
-      qexp[g] = exponent_above(mx);
-    }
+    if (j % tpg == 0) qsum_out[((int64_t)b * hq + h * G + g) * p.ng + j / tpg] = s;
+    if (j == 0) qexp[g] = exponent_above(mx);
   }
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
@@ -388,10 +390,12 @@ __device__ __forceinline__ void combine_and_store(const float* cm, const float* 
   }
 }
 
-// Raw bytes of one 128-token tile (8 pages) as one lane needs them.
+// Raw bytes of one 128-token tile (8 pages) as one lane needs them; NG
+// quantisation groups per token.
+template <int NG>
 struct Tile {
-  uint2 kc[8];    // K row bytes 8lg..8lg+7 of token lr, per page
-  uint2 meta[8];  // token lr's record {Ks, Kz, Vs, Vz} (any value past the history end)
+  uint2 kc[8];        // K row bytes 8lg..8lg+7 of token lr, per page
+  uint2 meta[8][NG];  // token lr's records {Ks, Kz, Vs, Vz}, one per group (any value past the history end)
   uint4 vlo[2], vhi[2];  // V words of channels 8lr..8lr+7, pages 2lg and 2lg+1
   uint32_t page_ok;      // bit pp: page pp of the tile exists in this split and in the pool
 };
@@ -433,11 +437,12 @@ __device__ __forceinline__ TileTable table_ready(const SplitParams& p, int raw, 
 // address is a scalar and a lane only adds its fixed offset), and a missing
 // page is read as page 0 and masked, so the memory system sees the whole tile
 // at once.
+template <int NG>
 __device__ __forceinline__ void load_tile(const SplitParams& p, const TileTable& tt, int j, int h, int pbase,
-                                          int t_end, int lg, int lr, Tile& t) {
+                                          int t_end, int lg, int lr, Tile<NG>& t) {
   t.page_ok = (uint32_t)(tt.live >> (8 * j)) & 0xffu;
   const uint32_t off_k = kKCodes + 32 * lr + 8 * lg;
-  const uint32_t off_m = kMeta + 8 * lr;
+  const uint32_t off_m = kMeta + 8 * NG * lr;
   const uint32_t off_v = kVCodes + 32 * lr;
   int pages[8];
 #pragma unroll
@@ -447,9 +452,18 @@ __device__ __forceinline__ void load_tile(const SplitParams& p, const TileTable&
   }
 #pragma unroll
   for (int pp = 0; pp < 8; ++pp) {
-    const uint8_t* blk = p.pool + ((int64_t)pages[pp] * p.hkv + h) * kBlock;
+    const uint8_t* blk = p.pool + ((int64_t)pages[pp] * p.hkv + h) * p.block;
     t.kc[pp] = *reinterpret_cast<const uint2*>(blk + off_k);
-    t.meta[pp] = *reinterpret_cast<const uint2*>(blk + off_m);
+    if constexpr (NG == 1) {
+      t.meta[pp][0] = *reinterpret_cast<const uint2*>(blk + off_m);
+    } else {
+#pragma unroll
+      for (int q2 = 0; q2 < NG; q2 += 2) {
+        const uint4 m2 = *reinterpret_cast<const uint4*>(blk + off_m + 8 * q2);
+        t.meta[pp][q2] = make_uint2(m2.x, m2.y);
+        t.meta[pp][q2 + 1] = make_uint2(m2.z, m2.w);
+      }
+    }
   }
   // V words: lane group lg takes pages 2lg and 2lg + 1 (entries of lanes
   // 8j + 2lg + qq, fetched across lanes)
@@ -457,7 +471,7 @@ __device__ __forceinline__ void load_tile(const SplitParams& p, const TileTable&
   for (int qq = 0; qq < 2; ++qq) {
     int pv = __builtin_amdgcn_ds_bpermute(4 * (8 * j + 2 * lg + qq), tt.ent);
     pv = pv < 0 ? 0 : pv;
-    const uint8_t* blk = p.pool + ((int64_t)pv * p.hkv + h) * kBlock + off_v;
+    const uint8_t* blk = p.pool + ((int64_t)pv * p.hkv + h) * p.block + off_v;
     t.vlo[qq] = *reinterpret_cast<const uint4*>(blk);
     t.vhi[qq] = *reinterpret_cast<const uint4*>(blk + 16);
   }
@@ -474,49 +488,80 @@ __device__ __forceinline__ float pin(float x) {
   return x;
 }
 
-// Running state of one wave: accumulators, running max, partial sums.
-template <int NRG>
+// Running state of one wave: accumulators, running max, partial sums (the
+// midpoint sums per quantisation group).
+template <int NRG, int NG>
 struct WaveState {
   f32x4 acc[NRG][8];
-  float m_run[NRG], l_part[NRG], az_part[NRG];
+  float m_run[NRG], l_part[NRG], az_part[NRG][NG];
 };
 
-template <int G, int NRG, bool FULL>  // FULL: all 8 pages exist and every token is below t_end
-__device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t, int pbase, int t_beg, int t_end,
-                                             int lg, int lr, const i32x8* qa, const int* qsc, const float* qsr,
-                                             uint8_t* wt, WaveState<NRG>& st) {
-  const int slot_pos = 8 * (lr & 1) + (lr >> 1);  // k position of token lr within its page's 16
-  // ---- scores: raw[rg][pp] = q'_(4rg+lg) . code(token lr of page pp) ----
-  float raw[NRG][8];
-#pragma unroll
-  for (int pp = 0; pp < 8; ++pp) {
-    i32x8 bk;
-    bk[0] = (int)(t.kc[pp].x & 0x33333333u);
-    bk[1] = (int)((t.kc[pp].x >> 2) & 0x33333333u);
-    bk[2] = (int)(t.kc[pp].y & 0x33333333u);
-    bk[3] = (int)((t.kc[pp].y >> 2) & 0x33333333u);
-    bk[4] = bk[5] = bk[6] = bk[7] = 0;
-#pragma unroll
-    for (int rg = 0; rg < NRG; ++rg) {
-      const f32x4 c = mfma_f8_f4(qa[rg], bk, f32x4{0.f, 0.f, 0.f, 0.f}, qsc[rg], kScaleCode);
-      raw[rg][pp] = pin((c[0] + c[1]) + (c[2] + c[3]));
-    }
+// Group of the K-operand dword half (0: bytes 0..3 of the row segment, 1: bytes
+// 4..7) and its byte mask: byte m of a segment holds channels 16 m + 4 lg + i,
+// so group jg of NG holds bytes [8 jg / NG, 8 (jg + 1) / NG).
+template <int NG>
+__device__ __forceinline__ void k_operand_group(const uint2 kc, int jg, i32x8& bk) {
+  const uint32_t lo = kc.x & 0x33333333u, hi = (kc.x >> 2) & 0x33333333u;
+  const uint32_t lo1 = kc.y & 0x33333333u, hi1 = (kc.y >> 2) & 0x33333333u;
+  if constexpr (NG == 1) {
+    bk[0] = (int)lo;
+    bk[1] = (int)hi;
+    bk[2] = (int)lo1;
+    bk[3] = (int)hi1;
+  } else {
+    const int half = NG == 2 ? jg : jg >> 1;
+    const uint32_t mask = NG == 2 ? 0xffffffffu : ((jg & 1) ? 0xffff0000u : 0x0000ffffu);
+    bk[0] = half == 0 ? (int)(lo & mask) : 0;
+    bk[1] = half == 0 ? (int)(hi & mask) : 0;
+    bk[2] = half == 1 ? (int)(lo1 & mask) : 0;
+    bk[3] = half == 1 ? (int)(hi1 & mask) : 0;
   }
-  // ---- online softmax, weights, w terms -> LDS ----
+  bk[4] = bk[5] = bk[6] = bk[7] = 0;
+}
+
+template <int G, int NRG, bool FULL, int NG>  // FULL: all 8 pages exist and every token is below t_end
+__device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG>& t, int pbase, int t_beg, int t_end,
+                                             int lg, int lr, const i32x8* qa, const int* qsc, const float (*qsr)[NG],
+                                             uint8_t* wt, WaveState<NRG, NG>& st) {
+  const int slot_pos = 8 * (lr & 1) + (lr >> 1);  // k position of token lr within its page's 16
   // slots past the history end or on a missing page may hold anything: their
-  // record must not reach the per-tile scale exponent or the sums
-  uint2 meta[8];
+  // records must not reach the per-tile scale exponent or the sums
+  bool live[8];
 #pragma unroll
   for (int pp = 0; pp < 8; ++pp) {
     const int tok = (pbase + pp) * 16 + lr;
-    const bool live = FULL || (((t.page_ok >> pp) & 1u) && tok >= t_beg && tok < t_end);
-    meta[pp].x = live ? t.meta[pp].x : 0u;
-    meta[pp].y = live ? t.meta[pp].y : 0u;
+    live[pp] = FULL || (((t.page_ok >> pp) & 1u) && tok >= t_beg && tok < t_end);
   }
-  float wsum[NRG];
+  // ---- scores: sc[rg][pp] = sum over groups jg of ks_jg (q'_(4rg+lg) . code) + kz_jg qsum_jg,
+  // the dot product over group jg's channels of token lr of page pp ----
+  float sc[NRG][8];
+#pragma unroll
+  for (int pp = 0; pp < 8; ++pp) {
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg) sc[rg][pp] = 0.f;
+#pragma unroll
+    for (int jg = 0; jg < NG; ++jg) {
+      i32x8 bk;
+      k_operand_group<NG>(t.kc[pp], jg, bk);
+      const float ks = h2f((uint16_t)(t.meta[pp][jg].x & 0xffffu));
+      const float kz = h2f((uint16_t)(t.meta[pp][jg].x >> 16));
+#pragma unroll
+      for (int rg = 0; rg < NRG; ++rg) {
+        const f32x4 c = mfma_f8_f4(qa[rg], bk, f32x4{0.f, 0.f, 0.f, 0.f}, qsc[rg], kScaleCode);
+        sc[rg][pp] = pin(sc[rg][pp] + (kz * qsr[rg][jg] + ks * ((c[0] + c[1]) + (c[2] + c[3]))));
+      }
+    }
+  }
+  // ---- online softmax, weights, w terms -> LDS ----
+  // value scale and midpoint of (page pp, group jg), zero on a dead slot
+  auto vs_of = [&](int pp, int jg) { return live[pp] ? h2f((uint16_t)(t.meta[pp][jg].y & 0xffffu)) : 0.f; };
+  auto vz_of = [&](int pp, int jg) { return live[pp] ? h2f((uint16_t)(t.meta[pp][jg].y >> 16)) : 0.f; };
+  float wsum[NRG][NG];
   float vsmax = 0.f;
 #pragma unroll
-  for (int pp = 0; pp < 8; ++pp) vsmax = fmaxf(vsmax, h2f((uint16_t)(meta[pp].y & 0xffffu)));
+  for (int pp = 0; pp < 8; ++pp)
+#pragma unroll
+    for (int jg = 0; jg < NG; ++jg) vsmax = fmaxf(vsmax, vs_of(pp, jg));
   vsmax = row_max16(vsmax);
   const int wexp = exponent_above(vsmax);  // every w = p vs <= vsmax < 2^wexp
   const float wmul = ldexpf(1.f, 7 - wexp);  // w * wmul < 128, exact (a power of two)
@@ -527,13 +572,9 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t
     float mx = kNegInf;
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
-      const int tok = (pbase + pp) * 16 + lr;
-      const bool ok = hv && (FULL || (tok >= t_beg && tok < t_end && ((t.page_ok >> pp) & 1u)));
-      const float ks = h2f((uint16_t)(meta[pp].x & 0xffffu));
-      const float kz = h2f((uint16_t)(meta[pp].x >> 16));
       // computed on every lane, then masked: a select, not a branch
-      const float v = pin((kz * qsr[rg] + ks * raw[rg][pp]) * p.scale_log2);
-      lgt[pp] = ok ? v : kNegInf;
+      const float v = pin(sc[rg][pp] * p.scale_log2);
+      lgt[pp] = hv && live[pp] ? v : kNegInf;
       mx = fmaxf(mx, lgt[pp]);
     }
     mx = row_max16(mx);
@@ -543,33 +584,40 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t
 #pragma unroll
       for (int nn = 0; nn < 8; ++nn) st.acc[rg][nn] *= alpha;
       st.l_part[rg] *= alpha;
-      st.az_part[rg] *= alpha;
+#pragma unroll
+      for (int jg = 0; jg < NG; ++jg) st.az_part[rg][jg] *= alpha;
       st.m_run[rg] = m_new;
     }
-    float w[8];
-    float ws = 0.f;
     const float m_safe = st.m_run[rg] == kNegInf ? 0.f : st.m_run[rg];  // exp2(-inf - m_safe) = 0
+    float pv[8];
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
-      const float pv = exp2f(lgt[pp] - m_safe);
-      const float vs = h2f((uint16_t)(meta[pp].y & 0xffffu));
-      const float vz = h2f((uint16_t)(meta[pp].y >> 16));
-      st.l_part[rg] += pv;
-      st.az_part[rg] = fmaf(pv, fmaf(1.5f, vs, vz), st.az_part[rg]);
-      w[pp] = pv * vs;
-      ws += w[pp];
+      pv[pp] = exp2f(lgt[pp] - m_safe);
+      st.l_part[rg] += pv[pp];
     }
-    wsum[rg] = row_sum16(ws);
-    uint8_t* tile_rg = wt + rg * 2048;
 #pragma unroll
-    for (int pp = 0; pp < 8; pp += 2) {
-      uint32_t tt[kWTerms];
-      split_terms<kWTerms>(w[pp] * wmul, w[pp + 1] * wmul, tt);
+    for (int jg = 0; jg < NG; ++jg) {  // one group's weights at a time (registers)
+      float w[8];
+      float ws = 0.f;
 #pragma unroll
-      for (int j = 0; j < kWTerms; ++j) {
-        uint8_t* row = tile_rg + (4 * lg + j) * 128 + slot_pos;
-        row[16 * pp] = (uint8_t)(tt[j] & 0xffu);
-        row[16 * (pp + 1)] = (uint8_t)(tt[j] >> 8);
+      for (int pp = 0; pp < 8; ++pp) {
+        const float vs = vs_of(pp, jg), vz = vz_of(pp, jg);
+        st.az_part[rg][jg] = fmaf(pv[pp], fmaf(1.5f, vs, vz), st.az_part[rg][jg]);
+        w[pp] = pv[pp] * vs;
+        ws += w[pp];
+      }
+      wsum[rg][jg] = row_sum16(ws);
+      uint8_t* tile_rg = wt + (rg * NG + jg) * 2048;
+#pragma unroll
+      for (int pp = 0; pp < 8; pp += 2) {
+        uint32_t tt[kWTerms];
+        split_terms<kWTerms>(w[pp] * wmul, w[pp + 1] * wmul, tt);
+#pragma unroll
+        for (int j = 0; j < kWTerms; ++j) {
+          uint8_t* row = tile_rg + (4 * lg + j) * 128 + slot_pos;
+          row[16 * pp] = (uint8_t)(tt[j] & 0xffu);
+          row[16 * (pp + 1)] = (uint8_t)(tt[j] >> 8);
+        }
       }
     }
   }
@@ -578,36 +626,51 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile& t
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // ---- values: acc[rg][nn] += w terms x V codes (channels 8lr + nn) ----
+  // with NG > 1 the column of lane lr (channels 8 lr .. 8 lr + 7) belongs to
+  // group lr / (16 / NG); the MFMA of group jg sees only its own columns' codes
   const int wsc = clamp_scale(kScaleOne + wexp - 7 - 4 * (lr & 3));
+  const int my_grp = lr / (16 / NG);
+  float corr[NRG];
 #pragma unroll
-  for (int rg = 0; rg < NRG; ++rg) {
-    const uint8_t* row = wt + rg * 2048 + lr * 128;
-    const uint4 a0 = *reinterpret_cast<const uint4*>(row + 16 * lg);
-    const uint4 a1 = *reinterpret_cast<const uint4*>(row + 64 + 16 * lg);
-    i32x8 wa;
-    wa[0] = (int)a0.x;
-    wa[1] = (int)a0.y;
-    wa[2] = (int)a0.z;
-    wa[3] = (int)a0.w;
-    wa[4] = (int)a1.x;
-    wa[5] = (int)a1.y;
-    wa[6] = (int)a1.z;
-    wa[7] = (int)a1.w;
-    const float corr = 1.5f * wsum[rg];
+  for (int rg = 0; rg < NRG; ++rg) corr[rg] = 0.f;
+#pragma unroll
+  for (int jg = 0; jg < NG; ++jg) {
+    const bool mine = NG == 1 || my_grp == jg;
+    i32x8 wa[NRG];
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg) {
+      const uint8_t* row = wt + (rg * NG + jg) * 2048 + lr * 128;
+      const uint4 a0 = *reinterpret_cast<const uint4*>(row + 16 * lg);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(row + 64 + 16 * lg);
+      wa[rg][0] = (int)a0.x;
+      wa[rg][1] = (int)a0.y;
+      wa[rg][2] = (int)a0.z;
+      wa[rg][3] = (int)a0.w;
+      wa[rg][4] = (int)a1.x;
+      wa[rg][5] = (int)a1.y;
+      wa[rg][6] = (int)a1.z;
+      wa[rg][7] = (int)a1.w;
+      corr[rg] = mine ? 1.5f * wsum[rg][jg] : corr[rg];
+    }
+    // codes of the group's columns only (each (group, nn) operand built once, used by every row group)
 #pragma unroll
     for (int nn = 0; nn < 8; ++nn) {
       const uint32_t v0 = nn < 4 ? (&t.vlo[0].x)[nn] : (&t.vhi[0].x)[nn - 4];
       const uint32_t v1 = nn < 4 ? (&t.vlo[1].x)[nn] : (&t.vhi[1].x)[nn - 4];
       i32x8 bv;
-      bv[0] = (int)(v0 & 0x33333333u);
-      bv[1] = (int)((v0 >> 2) & 0x33333333u);
-      bv[2] = (int)(v1 & 0x33333333u);
-      bv[3] = (int)((v1 >> 2) & 0x33333333u);
+      bv[0] = mine ? (int)(v0 & 0x33333333u) : 0;
+      bv[1] = mine ? (int)((v0 >> 2) & 0x33333333u) : 0;
+      bv[2] = mine ? (int)(v1 & 0x33333333u) : 0;
+      bv[3] = mine ? (int)((v1 >> 2) & 0x33333333u) : 0;
       bv[4] = bv[5] = bv[6] = bv[7] = 0;
-      st.acc[rg][nn] = mfma_f8_f4(wa, bv, st.acc[rg][nn], wsc, kScaleCode);
-      st.acc[rg][nn][0] -= corr;
+#pragma unroll
+      for (int rg = 0; rg < NRG; ++rg) st.acc[rg][nn] = mfma_f8_f4(wa[rg], bv, st.acc[rg][nn], wsc, kScaleCode);
     }
   }
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn) st.acc[rg][nn][0] -= corr[rg];
   __builtin_amdgcn_wave_barrier();
 }
 
@@ -651,10 +714,10 @@ __device__ __forceinline__ int find_unit(const int* tp, int units, int64_t t) {
   return a;
 }
 
-template <int G>
+template <int G, int NG>
 __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
   constexpr int NRG = (G + 3) / 4;  // MFMA row groups of 4 heads
-  __shared__ __align__(16) uint8_t smem[4 * NRG * 2048];  // per-wave w-term tiles
+  __shared__ __align__(16) uint8_t smem[4 * NRG * NG * 2048];  // per-wave w-term tiles
 
   const int hg_per_seq = p.hkv / p.hw;  // KV head groups per sequence
   const int per_seq = hg_per_seq * p.gsub;
@@ -662,7 +725,7 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lr = lane & 15;
   const int ts = 4 / p.hw;  // waves sharing a head (tile stride)
-  uint8_t* wt = smem + wave * (NRG * 2048);
+  uint8_t* wt = smem + wave * (NRG * NG * 2048);
   const int ncb = (p.gw * p.gsub + 3) / 4;
   const int64_t wave_part = (int64_t)p.gw * kPartStride;  // floats of one wave's partial
   // equal shares [T w / nw, T (w + 1) / nw) of the T flattened tiles
@@ -699,26 +762,30 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
     // score operands prepared once per (sequence, KV head)
     i32x8 qa[NRG];
     int qsc[NRG];
-    float qsr[NRG];
+    float qsr[NRG][NG];
 #pragma unroll
     for (int rg = 0; rg < NRG; ++rg) {
       const int* src = p.qop + ((((int64_t)b * p.hkv + h) * ncb + (sub * p.gw) / 4 + rg) * 64 + lane) * 9;
 #pragma unroll
       for (int i = 0; i < 8; ++i) qa[rg][i] = src[i];
       qsc[rg] = src[8];
-      qsr[rg] = (4 * rg + lg < p.gw) ? p.qsum[(int64_t)b * p.hq + hq0 + 4 * rg + lg] : 0.f;
+      const bool hv = 4 * rg + lg < p.gw;
+      const float* qs = p.qsum + ((int64_t)b * p.hq + hq0 + (hv ? 4 * rg + lg : 0)) * NG;
+#pragma unroll
+      for (int jg = 0; jg < NG; ++jg) qsr[rg][jg] = hv ? qs[jg] : 0.f;
     }
-    WaveState<NRG> st;
+    WaveState<NRG, NG> st;
 #pragma unroll
     for (int rg = 0; rg < NRG; ++rg) {
       st.m_run[rg] = kNegInf;
       st.l_part[rg] = 0.f;
-      st.az_part[rg] = 0.f;
+#pragma unroll
+      for (int jg = 0; jg < NG; ++jg) st.az_part[rg][jg] = 0.f;
 #pragma unroll
       for (int nn = 0; nn < 8; ++nn) st.acc[rg][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // the w-term tile: rows of an unused term (the 4th) must read 0
-    for (int i = lane; i < NRG * 2048 / 16; i += 64) reinterpret_cast<uint4*>(wt)[i] = make_uint4(0, 0, 0, 0);
+    // the w-term tiles: rows of an unused term (the 4th) must read 0
+    for (int i = lane; i < NRG * NG * 2048 / 16; i += 64) reinterpret_cast<uint4*>(wt)[i] = make_uint4(0, 0, 0, 0);
 
     // step s: the wave's tiles 2s and 2s + 1, i.e. tiles a + ph + ts k of the
     // unit; a step with one tile computes an empty (all-masked) second one
@@ -728,32 +795,32 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
     auto pbase_of = [&](int k) { return P0 + 8 * (ph + ts * k); };
     TileTable tab = table_ready(p, table_load(btr, P0, P1, ph, ts, 0), P0, P1, ph, ts, 0, ntw);
     int raw_next = table_load(btr, P0, P1, ph, ts, 2);
-    if constexpr (NRG > 1) {  // one tile in flight per wave (registers)
+    if constexpr (NRG > 1 || NG > 2) {  // one tile in flight per wave (registers)
       for (int s = 0;; ++s) {
         const int k = 2 * s;
-        Tile t;
+        Tile<NG> t;
         load_tile(p, tab, 0, h, pbase_of(k), t_end, lg, lr, t);
-        compute_tile<G, NRG, false>(p, t, pbase_of(k), t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
+        compute_tile<G, NRG, false, NG>(p, t, pbase_of(k), t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
         load_tile(p, tab, 1, h, pbase_of(k + 1), t_end, lg, lr, t);
-        compute_tile<G, NRG, false>(p, t, pbase_of(k + 1), t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
+        compute_tile<G, NRG, false, NG>(p, t, pbase_of(k + 1), t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
         if (s + 1 >= ns) break;
         tab = table_ready(p, raw_next, P0, P1, ph, ts, k + 2, ntw);
         raw_next = table_load(btr, P0, P1, ph, ts, k + 4);
       }
     } else {  // two tiles in flight per wave: tile k + 1's loads go out before tile k is computed
-      Tile ta, tb;
+      Tile<NG> ta, tb;
       load_tile(p, tab, 0, h, pbase_of(0), t_end, lg, lr, ta);
       for (int s = 0;; ++s) {
         const int k = 2 * s;
         load_tile(p, tab, 1, h, pbase_of(k + 1), t_end, lg, lr, tb);
-        compute_tile<G, NRG, false>(p, ta, pbase_of(k), t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
+        compute_tile<G, NRG, false, NG>(p, ta, pbase_of(k), t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
         const bool more = s + 1 < ns;
         // past the last step the table is empty: tile k + 2 re-reads page 0's
         // block (cache resident) and is never computed
         tab = table_ready(p, raw_next, P0, P1, ph, ts, k + 2, more ? ntw : 0);
         raw_next = table_load(btr, P0, P1, ph, ts, k + 4);
         load_tile(p, tab, 0, h, pbase_of(k + 2), t_end, lg, lr, ta);
-        compute_tile<G, NRG, false>(p, tb, pbase_of(k + 1), t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
+        compute_tile<G, NRG, false, NG>(p, tb, pbase_of(k + 1), t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
         if (!more) break;
       }
     }
@@ -769,7 +836,14 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
         for (int i = 0; i < 4; ++i) st.acc[rg][nn][i] = pin(st.acc[rg][nn][i]);
 #pragma unroll
     for (int rg = 0; rg < NRG; ++rg) {
-      const float l = row_sum16(st.l_part[rg]), az = row_sum16(st.az_part[rg]);
+      const float l = row_sum16(st.l_part[rg]);
+      // midpoint sum of the group of this lane's channels 8 lr .. 8 lr + 7
+      float az = 0.f;
+#pragma unroll
+      for (int jg = 0; jg < NG; ++jg) {
+        const float a = row_sum16(st.az_part[rg][jg]);
+        az = (NG == 1 || lr / (16 / NG) == jg) ? a : az;
+      }
       const int head = 4 * rg + lg;
       if (head < p.gw) {
         float* d = dst + head * kPartStride;
@@ -1170,8 +1244,12 @@ int launch_decode(bool int2, const SplitParams& sp, const uint16_t* r_k, int bat
   int slot = -1;
   timing_record_begin(s, int2 ? 1 : 2, &slot);
   if (int2) {
-    constexpr int GW = G > 8 ? 8 : (G < 4 ? 4 : G);
-    int2_split_kernel<GW><<<sp.n_wg, 256, 0, s>>>(sp);
+    constexpr int GW = G > 8 ? 8 : (G < 4 ? 4 : G);  // whole-token groups; 4 heads with finer groups
+    switch (sp.ng) {
+      case 1: int2_split_kernel<GW, 1><<<sp.n_wg, 256, 0, s>>>(sp); break;
+      case 2: int2_split_kernel<4, 2><<<sp.n_wg, 256, 0, s>>>(sp); break;
+      default: int2_split_kernel<4, 4><<<sp.n_wg, 256, 0, s>>>(sp); break;
+    }
   } else {
     bf16_split_kernel<G><<<dim3(sp.n_splits, sp.hkv, batch), 256, 0, s>>>(sp);
   }
@@ -1203,6 +1281,7 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   const int n_cu = device_cu_count();
   const SplitPlan plan = plan_splits(batch, shape->n_kv_heads, gqa, max_seq_len, n_cu);
   const WorkspaceLayout wl = workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads, shape->window, shape->n_sink,
+                                              kD / shape->group_size,
                                               plan, n_cu);
   if (workspace_bytes < wl.total) return OSCAR_ENOSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return OSCAR_EINVAL;
@@ -1236,12 +1315,15 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   sp.n_wchunks = sp.n_wwin + (sp.n_sink + kWinChunk - 1) / kWinChunk;
   sp.split = plan.split;
   sp.n_splits = plan.n_splits;
-  // INT2: at most 8 query heads per merge unit (register budget of the MFMA
-  // tiles); G < 4 runs the 4-head instantiation masking the missing heads
-  sp.gw = int2 ? (gqa > 8 ? 8 : gqa) : gqa;
+  // INT2: at most 8 (4 with finer groups) query heads per merge unit (register
+  // budget of the MFMA tiles); G < 4 runs the 4-head instantiation masking the
+  // missing heads
+  sp.gw = int2 ? int2_unit_heads(gqa, kD / shape->group_size) : gqa;
   sp.gsub = gqa / sp.gw;
   sp.n_wg = int2 ? split_wg_count(gqa, n_cu) : 0;
   sp.hw = split_heads_per_wg(shape->n_kv_heads);
+  sp.block = block_bytes(shape->group_size);
+  sp.ng = kD / shape->group_size;
   sp.scale_log2 = kLog2e / sqrtf((float)kD);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (shape->n_q_heads / shape->n_kv_heads) {
@@ -1298,6 +1380,7 @@ extern "C" size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t
   if (check_shape(shape) != OSCAR_OK || batch < 1 || max_seq_len < 0) return 0;
   const int n_cu = device_cu_count();
   return workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads, shape->window, shape->n_sink,
+                          kD / shape->group_size,
                           plan_splits(batch, shape->n_kv_heads, shape->n_q_heads / shape->n_kv_heads, max_seq_len,
                                       n_cu),
                           n_cu)

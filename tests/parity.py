@@ -39,26 +39,35 @@ def near_code_boundary(t, tol=REL):
     return np.min(np.abs(t[..., None] - np.array([0.5, 1.5, 2.5])), axis=-1) <= tol
 
 
-def gpu_group_fields(pool, page, h, slot):
-    """(k_codes[128], v_codes[128], ks, kz, vs, vz) as stored in a pool block."""
+def gpu_group_fields(pool, page, h, slot, group=128):
+    """(k_codes[128], v_codes[128], ks, kz, vs, vz) as stored in a pool block;
+    the four fp16 fields are lists over the slot's d / group records."""
     blk = pool[page, h]
+    ng = 128 // group
     kc = ref.unpack_k_rows(blk[ref.K_CODES + 32 * slot: ref.K_CODES + 32 * slot + 32])
     vc = ref.unpack_v_words(ref.v_words(blk))[slot]
-    f = lambda fld: int(np.ascontiguousarray(blk[ref.META + 8 * slot + fld: ref.META + 8 * slot + fld + 2]).view(np.uint16)[0])
+
+    def f(fld):
+        out = []
+        for j in range(ng):
+            a = ref.META + 8 * (ng * slot + j) + fld
+            out.append(int(np.ascontiguousarray(blk[a:a + 2]).view(np.uint16)[0]))
+        return out
     return kc, vc, f(ref.K_SCALE), f(ref.K_ZERO), f(ref.V_SCALE), f(ref.V_ZERO)
 
 
-def clear_group(pool, page, h, slot):
+def clear_group(pool, page, h, slot, group=128):
     blk = pool[page, h]
+    ng = 128 // group
     blk[ref.K_CODES + 32 * slot: ref.K_CODES + 32 * slot + 32] = 0
     w = ref.v_words(blk).copy() & ~np.uint32(3 << (2 * slot))
     blk[ref.V_CODES:ref.V_CODES + 512] = w.astype("<u4").view(np.uint8)
-    blk[ref.META + 8 * slot: ref.META + 8 * slot + 8] = 0
+    blk[ref.META + 8 * ng * slot: ref.META + 8 * ng * (slot + 1)] = 0
 
 
 def check_group(xr, codes_gpu, s_bits_gpu, z_bits_gpu):
-    """Apply the encoder rule to one group.  xr: the oracle's exact rotation
-    (fp64 [128]).  Returns (n_mismatch, n_excluded)."""
+    """Apply the encoder rule to one group.  xr: the oracle's exact rotation of
+    the group's channels (fp64 [group]).  Returns (n_mismatch, n_excluded)."""
     c, s16, z16, diag = ref.quantize(xr[None, :])
     c, s16, z16 = c[0], float(s16[0]), float(z16[0])
     sig, m, t = float(diag["sigma"][0]), float(diag["m"][0]), diag["t"][0]
@@ -76,7 +85,7 @@ def check_group(xr, codes_gpu, s_bits_gpu, z_bits_gpu):
         zg = np.float32(np.uint16(z_bits_gpu).view(np.float16))
         x32 = np.asarray(xr, np.float64).astype(np.float32)
         t = ((x32 - zg).astype(np.float32) / (sg if sg != 0 else np.float32(1))).astype(np.float32)
-        c = np.zeros(128, np.int64) if sg == 0 else np.clip(np.rint(t), 0, 3).astype(np.int64)
+        c = np.zeros(len(xr), np.int64) if sg == 0 else np.clip(np.rint(t), 0, 3).astype(np.int64)
     amb = near_code_boundary(t)
     diff = c != codes_gpu
     bad += int(np.sum(diff & ~amb))
@@ -84,10 +93,11 @@ def check_group(xr, codes_gpu, s_bits_gpu, z_bits_gpu):
 
 
 def check_append(pool_before, pool_gpu, rk, rv, k_bits, v_bits, seq_idx, pos, block_table,
-                 sample=None):
+                 sample=None, group=128):
     """Compare a device-appended pool with the oracle's encoding of the same
-    tokens.  ``sample``: indices of tokens to check (default all); with all
-    tokens checked, every other byte of the pool must be untouched."""
+    tokens, group by group.  ``sample``: indices of tokens to check (default
+    all); with all tokens checked, every other byte of the pool must be
+    untouched."""
     hkv = pool_gpu.shape[1]
     idx = np.arange(len(pos)) if sample is None else np.asarray(sample)
     kb = ref.bf16_to_f64(np.asarray(k_bits)[idx])
@@ -102,16 +112,21 @@ def check_append(pool_before, pool_gpu, rk, rv, k_bits, v_bits, seq_idx, pos, bl
         page = int(block_table[b][p // 16])
         slot = p % 16
         for h in range(hkv):
-            kc, vc, ks, kz, vs, vz = gpu_group_fields(pool_gpu, page, h, slot)
-            m1, e1 = check_group(kr[n_i, h], kc, ks, kz)
-            m2, e2 = check_group(vr[n_i, h], vc, vs, vz)
+            kc, vc, ks, kz, vs, vz = gpu_group_fields(pool_gpu, page, h, slot, group)
+            m1 = e1 = m2 = e2 = 0
+            for j in range(128 // group):
+                c = slice(group * j, group * (j + 1))
+                a, e = check_group(kr[n_i, h, c], kc[c], ks[j], kz[j])
+                m1, e1 = m1 + a, e1 + e
+                a, e = check_group(vr[n_i, h, c], vc[c], vs[j], vz[j])
+                m2, e2 = m2 + a, e2 + e
             if (m1 or m2) and mism < 6:
                 print(f"  mismatch: token {i} (seq {b}, pos {p}) head {h}: K {m1} V {m2}", flush=True)
             mism += m1 + m2
             excl += e1 + e2
             if rest_gpu is not None:
-                clear_group(rest_gpu, page, h, slot)
-                clear_group(rest_ref, page, h, slot)
+                clear_group(rest_gpu, page, h, slot, group)
+                clear_group(rest_ref, page, h, slot, group)
     stray = 0 if rest_gpu is None else int(np.sum(rest_gpu != rest_ref))
     if stray:
         where = np.argwhere(rest_gpu != rest_ref)[:6]

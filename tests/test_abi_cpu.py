@@ -42,7 +42,8 @@ def test_strerror():
 
 
 def bad_shapes():
-    return [K.make_shape(32, 8, head_dim=64), K.make_shape(32, 8, group_size=32),
+    return [K.make_shape(32, 8, head_dim=64), K.make_shape(32, 8, group_size=16),
+            K.make_shape(32, 8, group_size=48), K.make_shape(32, 8, group_size=0),
             K.make_shape(32, 8, page_size=32), K.make_shape(24, 8), K.make_shape(32, 8, window=4096),
             K.make_shape(32, 8, n_sink=-1), K.make_shape(32, 8, n_sink=2048)]
 
@@ -80,8 +81,10 @@ def test_host_validation_before_launch():
                                  fake, fake, 1 << 30, None) == EINVAL
     assert lib.oscar_quantize_append(C.byref(sink_only), fake, fake, fake, fake, 1, fake, fake, 1, fake, 1, fake,
                                      fake, 1, None, None, None) == EINVAL
-    # the sink chunks enlarge the workspace
+    # the sink chunks enlarge the workspace; so do finer groups (per-group query sums)
     assert lib.oscar_decode_workspace_bytes(C.byref(K.make_shape(32, 8, n_sink=64)), 8, 100000) > ws
+    for g in (32, 64):
+        assert lib.oscar_decode_workspace_bytes(C.byref(K.make_shape(32, 8, group_size=g)), 8, 100000) > 0
     assert lib.oscar_hbm_copy(fake, fake, 17, None) == EINVAL
     assert lib.oscar_timing_end(None, None, 0, None) == EINVAL
 

@@ -57,11 +57,12 @@ def rotations(cfg, hkv=8):
     return ref.bf16_bits(rk), ref.bf16_bits(rv)
 
 
-def make_spec(cfg, lens, window=128, hq=None, hkv=8, n_sink=0):
+def make_spec(cfg, lens, window=128, hq=None, hkv=8, n_sink=0, group=128):
     s = wl.spec(cfg, batch=len(lens))
     s.seq_lens = np.asarray(lens, np.int32)
     s.window = window
     s.n_sink = n_sink
+    s.group_size = group
     if hq is not None:
         s.n_q_heads = hq
     s.n_kv_heads = hkv
@@ -88,7 +89,7 @@ def ring_rows(s):
 
 
 def run_append(K, s, rk, rv, k, v, si, ps, bt, pool0, wk0, wv0, lens_after):
-    shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window, n_sink=s.n_sink)
+    shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window, n_sink=s.n_sink, group_size=s.group_size)
     pool = D(pool0)
     wk = D(wk0) if s.window + s.n_sink > 0 else None
     wv = D(wv0) if s.window + s.n_sink > 0 else None
@@ -103,7 +104,7 @@ def append_case(K, s, order="inorder", split_at=None, seed=0):
     rk, rv = rotations(s.cfg, s.n_kv_heads)
     rkf, rvf = ref.bf16_to_f64(rk), ref.bf16_to_f64(rv)
     bt, n_pages = wl.page_table(s)
-    pool0 = rng.integers(0, 256, (n_pages, s.n_kv_heads, ref.BLOCK), dtype=np.uint8)
+    pool0 = rng.integers(0, 256, (n_pages, s.n_kv_heads, ref.block_bytes(s.group_size)), dtype=np.uint8)
     wsh = (s.batch, ring_rows(s), s.n_kv_heads, 128)
     wk0 = rng.integers(0, 65536, wsh, dtype=np.uint16)
     wv0 = rng.integers(0, 65536, wsh, dtype=np.uint16)
@@ -117,9 +118,9 @@ def append_case(K, s, order="inorder", split_at=None, seed=0):
         if s.window + s.n_sink > 0:
             wk_g, wv_g = wk_g2, wv_g2
         ref.append_ref(rkf, rvf, k[a:b], v[a:b], si[a:b], ps[a:b], bt, s.seq_lens, pool_ref, wk_ref, wv_ref,
-                       s.window, s.n_sink)
-    mism, excl, stray = P.check_append(pool0, pool_g, rkf, rvf, k, v, si, ps, bt)
-    log(f"append {s.cfg} lens={list(s.seq_lens)} W={s.window} sinks={s.n_sink} {order}: "
+                       s.window, s.n_sink, s.group_size)
+    mism, excl, stray = P.check_append(pool0, pool_g, rkf, rvf, k, v, si, ps, bt, group=s.group_size)
+    log(f"append {s.cfg} lens={list(s.seq_lens)} W={s.window} sinks={s.n_sink} g={s.group_size} {order}: "
         f"mismatches={mism} excluded={excl} stray={stray}")
     assert mism == 0 and stray == 0
     if s.window + s.n_sink > 0:
@@ -195,17 +196,17 @@ def oracle_cache(s, seed=0):
     bt, n_pages = wl.page_table(s)
     rng = np.random.default_rng(seed)
     # unused slots hold random bytes (the decode must never read them)
-    pool = rng.integers(0, 256, (n_pages, s.n_kv_heads, ref.BLOCK), dtype=np.uint8)
+    pool = rng.integers(0, 256, (n_pages, s.n_kv_heads, ref.block_bytes(s.group_size)), dtype=np.uint8)
     wk = np.zeros((s.batch, ring_rows(s), s.n_kv_heads, 128), np.uint16)
     wv = np.zeros_like(wk)
     k, v, si, ps = token_list(s)
-    ref.append_ref(rkf, rvf, k, v, si, ps, bt, s.seq_lens, pool, wk, wv, s.window, s.n_sink)
+    ref.append_ref(rkf, rvf, k, v, si, ps, bt, s.seq_lens, pool, wk, wv, s.window, s.n_sink, s.group_size)
     q = wl.decode_queries(s)[:, :s.n_q_heads]
     return rk, rv, rkf, rvf, bt, pool, wk, wv, q
 
 
 def run_decode(K, s, rk, rv, q, bt, pool, wk, wv, max_len=None):
-    shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window, n_sink=s.n_sink)
+    shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window, n_sink=s.n_sink, group_size=s.group_size)
     max_len = int(s.seq_lens.max()) if max_len is None else max_len
     ws = torch.empty(K.oscar_decode_workspace_bytes(shape, s.batch, max_len), dtype=torch.uint8, device=DEV)
     out = torch.full((s.batch, s.n_q_heads, 128), float("nan"), dtype=torch.float32, device=DEV)
