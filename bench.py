@@ -71,6 +71,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--group", type=int, default=128, choices=(128, 64, 32),
+                    help="rotated channels per INT2 scale/zero pair (128 = one group per token)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the prefill-ingest (append) leg")
@@ -97,7 +99,9 @@ def main():
     B, HQ, HKV, W = s.batch, s.n_q_heads, s.n_kv_heads, s.window
     lens = s.seq_lens.astype(np.int64)
     nmax = int(lens.max())
-    shape = K.make_shape(HQ, HKV, W)
+    G = args.group
+    shape = K.make_shape(HQ, HKV, W, group_size=G)
+    tok_bytes = 64 + 8 * (128 // G)  # INT2 bytes per token and KV head: codes + one record per group
 
     def T(a):
         a = np.ascontiguousarray(a)
@@ -116,7 +120,7 @@ def main():
     L = args.layers
     bt, n_pages = wl.page_table(s)
     btd, lensd = T(bt), T(lens.astype(np.int32))
-    pools = [torch.zeros((n_pages, HKV, K.BLOCK_BYTES), dtype=torch.uint8, device=dev) for _ in range(L)]
+    pools = [torch.zeros((n_pages, HKV, K.block_bytes(G)), dtype=torch.uint8, device=dev) for _ in range(L)]
     wks = [torch.zeros((B, W, HKV, 128), dtype=torch.int16, device=dev) for _ in range(L)]
     wvs = [torch.zeros((B, W, HKV, 128), dtype=torch.int16, device=dev) for _ in range(L)]
     kvp = [] if args.no_bf16 else [torch.zeros((n_pages, HKV, K.BF16_BLOCK_ELEMS), dtype=torch.int16, device=dev)
@@ -199,12 +203,12 @@ def main():
     # ---- algorithmic bytes ----
     hist = np.maximum(lens - W, 0)
     win = np.minimum(lens, W)
-    b_hist = float(hist.sum() * HKV * 72)
+    b_hist = float(hist.sum() * HKV * tok_bytes)
     b_win = float(win.sum() * HKV * 512)
     b_rot = 2 * HKV * 128 * 128 * 2
     b_q_out = B * HQ * 128 * (2 + 4)
     b_bt = float(sum(-(-int(n) // 16) for n in lens) * 4)
-    b_append = B * HKV * (2 * 256 + 72 + 2 * 256) + b_rot
+    b_append = B * HKV * (2 * 256 + tok_bytes + 2 * 256) + b_rot
     step_bytes_int2 = b_hist + b_win + b_rot + b_q_out + b_bt + b_append
     b_bf16_kv = float(lens.sum() * HKV * 512)
     step_bytes_bf16 = b_bf16_kv + b_q_out + b_bt + B * HKV * 2 * 2 * 256
@@ -224,12 +228,12 @@ def main():
         }
     assert torch.isfinite(out).all()
 
-    res_append = None if args.no_append else append_leg(K, torch, dev, shape, rkd, rvd, args)
+    res_append = None if args.no_append else append_leg(K, torch, dev, shape, rkd, rvd, args, tok_bytes)
 
     # the split kernel also attends the bf16 window and merges (last workgroup of each unit)
     b_split = b_hist + b_win + HKV * 128 * 128 * 2 + b_bt + b_q_out
     achieved = b_split / split_s / 1e9 if split_s else None
-    traffic = load_traffic(b_split)
+    traffic = load_traffic(b_split) if G == 128 else None  # the committed counters cover group 128
     line = {
         "metric": "INT2 decode-attn HBM GB/s (% of peak) + decode tokens/s at 100K ctx vs bf16 KV",
         "value": step_bytes_int2 / dt / 1e9,
@@ -244,7 +248,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded Gaussian K/V, 4 key outlier channels x20; no dataset exists for this path)",
         "config": {"workload": f"long-context decode step: append 1 token/seq + INT2 decode, B={B}, n={nmax}, "
-                               f"{HQ}q/{HKV}kv heads, d=128, group 128, 16-token scattered pages, bf16 window {W}",
+                               f"{HQ}q/{HKV}kv heads, d=128, group {G}, 16-token scattered pages, bf16 window {W}",
                    "layers_rotated": L, "pct_of_hbm_peak": 100 * step_bytes_int2 / dt / 1e9 / PEAK_HBM_GBS,
                    "decode_tokens_per_s": B / dt, "step_bytes": step_bytes_int2},
         "bf16_kv": res_bf16,
@@ -269,12 +273,13 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def append_leg(K, torch, dev, shape, rkd, rvd, args):
+def append_leg(K, torch, dev, shape, rkd, rvd, args, tok_bytes=72):
     """Prefill ingest: oscar_quantize_append of 65536 new tokens x 8 KV heads into
     empty pages of one sequence (bf16 Gaussian K/V with outlier channels), timed
     on the append kernel's own events.  Algorithmic bytes per call: bf16 K and V
-    read (512 B per token and KV head), codes + scale/zero written (72 B), the
-    last 128 tokens written to the bf16 window (512 B), both rotations read."""
+    read (512 B per token and KV head), codes + scale/zero records written
+    (tok_bytes: 72 B at one group per token), the last 128 tokens written to the
+    bf16 window (512 B), both rotations read."""
     import workloads as wl
 
     s4 = wl.spec(4)
@@ -290,7 +295,7 @@ def append_leg(K, torch, dev, shape, rkd, rvd, args):
 
     kd, vd, sid, psd, btd = T(k), T(v), T(si), T(ps), T(bt)
     lens = T(np.array([n], np.int32))
-    pool = torch.zeros((n_pages, hkv, K.BLOCK_BYTES), dtype=torch.uint8, device=dev)
+    pool = torch.zeros((n_pages, hkv, K.block_bytes(shape.group_size)), dtype=torch.uint8, device=dev)
     wk = torch.zeros((1, w, hkv, 128), dtype=torch.int16, device=dev)
     wv = torch.zeros_like(wk)
     for _ in range(2):
@@ -303,7 +308,7 @@ def append_leg(K, torch, dev, shape, rkd, rvd, args):
     torch.cuda.synchronize()
     ms, kinds = K.oscar_timing_end(4 * reps + 8)
     t = float(np.mean([m for m, kk in zip(ms, kinds) if kk == 3])) / 1e3
-    byts = n * hkv * (512 + 72) + min(n, w) * hkv * 512 + 2 * hkv * 128 * 128 * 2
+    byts = n * hkv * (512 + tok_bytes) + min(n, w) * hkv * 512 + 2 * hkv * 128 * 128 * 2
     flops = 2 * 2 * n * hkv * 128 * 128
     log(f"append 65536 tokens: {t * 1e6:.1f} us, {byts / t / 1e9:.0f} GB/s, rotation {flops / t / 1e12:.1f} TFLOP/s")
     return {"workload": "prefill ingest: 65536 bf16 K/V tokens x 8 KV heads into empty pages (one sequence)",
@@ -314,7 +319,8 @@ def append_leg(K, torch, dev, shape, rkd, rvd, args):
 
 def quality_leg(K, wl, torch):
     """Quality of the three rotations on the 2048-token workload and on a
-    shrunk copy of the 32K-context one (same distributions)."""
+    shrunk copy of the 32K-context one (same distributions), at each group size
+    (128, 64, 32 rotated channels per scale/zero pair)."""
     from kv_cache_int2_amd import quality
 
     res = {}
@@ -322,10 +328,12 @@ def quality_leg(K, wl, torch):
         shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window)
         q_cal, k_cal, v_cal = wl.calibration_set(s)
         rot = quality.rotations(shape, q_cal, k_cal, v_cal, K.oscar_calibrate)
-        t = time.perf_counter()
-        res[label] = quality.measure(K, s, rot, wl, torch)
-        log(f"quality {label}: {time.perf_counter() - t:.1f}s " +
-            " | ".join(f"{k}: " + ", ".join(f"{m} {v:.3g}" for m, v in r.items()) for k, r in res[label].items()))
+        for g in (128, 64, 32):
+            key = label if g == 128 else f"{label}_g{g}"
+            t = time.perf_counter()
+            res[key] = quality.measure(K, s, rot, wl, torch, group=g)
+            log(f"quality {key}: {time.perf_counter() - t:.1f}s " +
+                " | ".join(f"{k}: " + ", ".join(f"{m} {v:.3g}" for m, v in r.items()) for k, r in res[key].items()))
     print(json.dumps({"quality": res, "data": "synthetic (seeded Gaussian K/V, 4 key outlier channels x20)"}))
 
 

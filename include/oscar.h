@@ -34,20 +34,25 @@
  *     the pool are skipped by the kernels rather than written.
  *
  * Supported shape (anything else returns OSCAR_EUNSUPPORTED): head_dim 128,
- * group_size 128 (one INT2 group per token vector), page_size 16,
+ * group_size 128 (one INT2 group per token vector), 64 or 32 (the token's
+ * rotated channels in runs of that many, each with its own scale and zero:
+ * 2.5 or 3 bits per element with the metadata; P1 «Что придумали в Together
+ * AI»), page_size 16,
  * n_q_heads = G * n_kv_heads with G in {1, 2, 4, 8, 16}, 0 <= window <= 1024,
  * 0 <= n_sink <= 1024.
  *
- * Page block (one per page and KV head, 1152 bytes, 128-byte aligned within a
- * 128-byte aligned pool; pool = uint8 [n_pages][n_kv_heads][1152]):
+ * Page block (one per page and KV head, BLOCK = 1024 + 128 ng bytes with
+ * ng = 128 / group_size groups per token: 1152, 1280 or 1536; pool = uint8
+ * [n_pages][n_kv_heads][BLOCK], 16-byte aligned):
  *   [   0,  512)  K codes: 16 token rows x 32 B; channel c in row byte
  *                 8 ((c >> 2) & 3) + (c >> 4), bits 2 (c & 3)
  *   [ 512, 1024)  V codes: 128 channel words (uint32, little endian); token slot
  *                 j of the page at bits 2j..2j+1
- *   [1024, 1152)  16 token records of 8 bytes, slot j at 1024 + 8j:
- *                 fp16 K scale, K zero, V scale, V zero
+ *   [1024, BLOCK) 16 ng records of 8 bytes, group g of slot j at
+ *                 1024 + 8 (ng j + g): fp16 K scale, K zero, V scale, V zero
  * A token at position pos of sequence b lives in page block_table[b][pos / 16],
- * slot pos % 16.  Dequantised rotated value of channel c: zero + code * scale.
+ * slot pos % 16.  Dequantised rotated value of channel c: zero + code * scale
+ * of the record of group c / group_size.
  * bf16 ring: [batch][window + n_sink][n_kv_heads][128]: recent position pos in row
  * pos % window, sink position pos < n_sink in row window + pos.
  */
@@ -73,7 +78,7 @@ typedef struct oscar_shape {
   int32_t n_q_heads;   /* query heads (G * n_kv_heads) */
   int32_t n_kv_heads;  /* key/value heads */
   int32_t head_dim;    /* d; must be 128 */
-  int32_t group_size;  /* channels per INT2 group; must be 128 */
+  int32_t group_size;  /* rotated channels per INT2 scale/zero pair: 128, 64 or 32 */
   int32_t page_size;   /* tokens per page; must be 16 */
   int32_t window;      /* most recent tokens also kept in bf16 (0 = none) */
   int32_t n_sink;      /* first tokens of a sequence also kept in bf16 (attention sinks; 0 = none) */
@@ -81,7 +86,8 @@ typedef struct oscar_shape {
 
 #define OSCAR_HEAD_DIM 128
 #define OSCAR_PAGE_SIZE 16
-#define OSCAR_BLOCK_BYTES 1152
+#define OSCAR_BLOCK_BYTES 1152 /* page block bytes at group_size 128 */
+#define OSCAR_BLOCK_BYTES_FOR_GROUP(g) (1024 + 8 * 16 * (128 / (g)))
 
 /*
  * Offline calibration, host only, synchronous (P1 «Что придумали в Together AI»,
@@ -114,7 +120,8 @@ int oscar_calibrate(const oscar_shape* shape, const float* q_cal, int64_t n_q,
  * For each token i (any order; positions must be distinct per sequence):
  *   b = seq_idx[i], p = pos[i]; for each KV head h and for K (R = r_k) and V (r_v):
  *   x' = R[h] x (bf16 inputs, fp32 accumulation on the matrix cores);
- *   m = min x', M = max x'; scale = fp16_rne((M - m) / 3); zero = fp16_rne(m);
+ *   per group of group_size consecutive channels of x' (the whole token at 128):
+ *   m = min, M = max; scale = fp16_rne((M - m) / 3); zero = fp16_rne(m);
  *   code_c = clamp(rint((x'_c - zero) / scale), 0, 3) (all 0 if scale == 0);
  *   written to page block_table[b][p / 16], slot p % 16, in the layout above.
  *   If p >= seq_len_after[b] - window, the raw bf16 k/v also go to ring row
@@ -126,7 +133,7 @@ int oscar_calibrate(const oscar_shape* shape, const float* q_cal, int64_t n_q,
  *   seq_idx, pos int32 [n_tokens]
  *   block_table  int32 [batch][max_pages_per_seq]
  *   seq_len_after int32 [batch]: sequence length once this call's tokens are in
- *   pool         uint8 [n_pages][n_kv_heads][1152], updated in place (other slots kept)
+ *   pool         uint8 [n_pages][n_kv_heads][BLOCK], updated in place (other slots kept)
  *   win_k, win_v bf16 [batch][window + n_sink][n_kv_heads][128] (may be NULL if
  *                window + n_sink == 0)
  * n_tokens == 0 is a no-op.  Errors: OSCAR_EINVAL, OSCAR_EUNSUPPORTED, OSCAR_EHIP.
@@ -151,7 +158,8 @@ size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int
  * the output un-rotated by the value transform; P2 «OSCAR има значение…»: bf16
  * sink and recent tokens + INT2 history).  With n = seq_lens[b],
  * w = min(n, window) and s = min(n_sink, n - w):
- *   history s <= t < n - w: s_t = (R_K q) . (zero + code * scale)_t / sqrt(d) (INT2 K)
+ *   history s <= t < n - w: s_t = (R_K q) . (zero + code * scale)_t / sqrt(d) (INT2 K;
+ *                           zero and scale of each channel's group)
  *   sinks t < s and window t >= n - w: s_t = q . k_t / sqrt(d)               (bf16 K)
  *   out = (R_V^T sum_hist p_t v'_t + sum_sink,win p_t v_t) / sum_all p_t,
  *   p = exp(s - max s); query head j uses KV head j / G.

@@ -38,7 +38,11 @@ import numpy as np
 
 D = 128
 PAGE = 16
-BLOCK = 1152
+
+
+def block_bytes(group: int = D) -> int:
+    """Bytes of one (page, KV head) block: codes plus one 8-byte record per token and group."""
+    return 1024 + 8 * PAGE * (D // group)
 
 
 def hadamard_rotation(d: int = D) -> np.ndarray:
@@ -75,16 +79,18 @@ def rotations(shape, q_cal, k_cal, v_cal, lib_calibrate) -> dict:
     return {"oscar": (rk, rv), "hadamard": (had, had.copy()), "identity": (eye, eye.copy())}
 
 
-def dequantize_history(pool: np.ndarray, bt_row: np.ndarray, n_hist: int, h: int):
+def dequantize_history(pool: np.ndarray, bt_row: np.ndarray, n_hist: int, h: int, group: int = D):
     """Rotated-domain K and V (fp64 [n_hist][d]) of positions 0 .. n_hist - 1 of
-    one sequence and KV head, decoded from the 1152-byte page blocks: K codes
-    (token row of 32 bytes, channel c in byte 8 ((c >> 2) & 3) + (c >> 4) at bits
-    2 (c & 3)), V codes (channel word c, slot j at bits 2 j), then per token
-    {K scale, K zero, V scale, V zero} fp16; value = zero + code * scale."""
+    one sequence and KV head, decoded from the page blocks: K codes (token row
+    of 32 bytes, channel c in byte 8 ((c >> 2) & 3) + (c >> 4) at bits 2 (c & 3)),
+    V codes (channel word c, slot j at bits 2 j), then per token and group of
+    ``group`` channels {K scale, K zero, V scale, V zero} fp16; value = zero +
+    code * scale of the channel's group."""
     if n_hist == 0:
         return np.zeros((0, D)), np.zeros((0, D))
     n_pg = -(-n_hist // PAGE)
-    blk = pool[np.asarray(bt_row[:n_pg], np.int64), h]            # [pages][1152]
+    ng = D // group
+    blk = pool[np.asarray(bt_row[:n_pg], np.int64), h]            # [pages][block bytes]
     c = np.arange(D)
     kbyte = 8 * ((c >> 2) & 3) + (c >> 4)
     krows = blk[:, :512].reshape(n_pg, PAGE, 32)
@@ -92,18 +98,19 @@ def dequantize_history(pool: np.ndarray, bt_row: np.ndarray, n_hist: int, h: int
     vw = np.ascontiguousarray(blk[:, 512:1024]).view(np.uint32).reshape(n_pg, D)
     slots = np.arange(PAGE)
     vc = (vw[:, None, :] >> (2 * slots[None, :, None]).astype(np.uint32)) & 3  # [pages][16][d]
-    meta = np.ascontiguousarray(blk[:, 1024:]).view(np.uint16).reshape(n_pg, PAGE, 4)
-    ks, kz, vs, vz = (_fp16_f64(meta[..., i])[..., None] for i in range(4))
+    meta = np.ascontiguousarray(blk[:, 1024:]).view(np.uint16).reshape(n_pg, PAGE, ng, 4)
+    ks, kz, vs, vz = (np.repeat(_fp16_f64(meta[..., i]), group, axis=-1) for i in range(4))
     k = (kz + kc * ks).reshape(-1, D)[:n_hist]
     v = (vz + vc * vs).reshape(-1, D)[:n_hist]
     return k, v
 
 
-def measure(K, s, rot: dict, workloads, torch) -> dict:
+def measure(K, s, rot: dict, workloads, torch, group: int = D) -> dict:
     """Metrics of each rotation in ``rot`` on workload spec ``s`` (one full
-    prefill through ``oscar_quantize_append``, one ``oscar_decode_attn``)."""
+    prefill through ``oscar_quantize_append``, one ``oscar_decode_attn``) with
+    quantisation groups of ``group`` rotated channels."""
     dev = torch.device("cuda:0")
-    shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window)
+    shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window, group_size=group)
     q_bits = workloads.decode_queries(s)
     q = _bf16_f64(q_bits)
     bt, n_pages = workloads.page_table(s)
@@ -114,7 +121,7 @@ def measure(K, s, rot: dict, workloads, torch) -> dict:
     T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     results = {}
     for name, (rk, rv) in rot.items():
-        pool = torch.zeros((n_pages, s.n_kv_heads, BLOCK), dtype=torch.uint8, device=dev)
+        pool = torch.zeros((n_pages, s.n_kv_heads, block_bytes(group)), dtype=torch.uint8, device=dev)
         wsh = (s.batch, max(s.window, 1), s.n_kv_heads, D)
         wk = torch.zeros(wsh, dtype=torch.int16, device=dev)
         wv = torch.zeros(wsh, dtype=torch.int16, device=dev)
@@ -140,7 +147,7 @@ def measure(K, s, rot: dict, workloads, torch) -> dict:
             hist = n - w
             kb, vb = _bf16_f64(kv[b][0]), _bf16_f64(kv[b][1])          # [n][Hkv][d]
             for h in range(s.n_kv_heads):
-                kq, _ = dequantize_history(pool_h, bt[b], hist, h)       # rotated domain
+                kq, _ = dequantize_history(pool_h, bt[b], hist, h, group)  # rotated domain
                 k_hat = kq @ rkf[h]                                      # R^T applied: x = R^T x'
                 dk = kb[:hist, h] - k_hat
                 sig_err += float(np.einsum("ti,ij,tj->", dk, sig[h], dk)) / D

@@ -48,3 +48,25 @@ def test_decode_groups(K, group, cfg, lens, window, hq, n_sink):
     log(f"decode g={group} lens={lens} W={window} Hq={hq} sinks={n_sink}: max rel err {err.max():.3e}")
     assert np.isfinite(got).all()
     assert err.max() <= P.ATTN_TOL
+
+
+@pytest.mark.parametrize("group", [64, 32])
+def test_full_longctx_groups(K, group):
+    """The long-context decode workload (B = 8, n = 100000, 32 q / 8 KV heads) at
+    a finer group size: sampled append records and codes, every group spanning
+    codes 0..3, and sampled decode outputs on oracle-encoded sequences."""
+    import workloads as wl
+    from test_gpu_parity import check_sampled, codes_span_levels, decode_full, full_cache, oracle_overwrite
+    from test_gpu_parity import sampled_append_check
+
+    s = wl.spec(3)
+    s.group_size = group
+    log(f"config 3 g={group} full: building cache")
+    c = full_cache(K, s, keep=(2, 7))
+    q = wl.decode_queries(s)
+    pool = sampled_append_check(s, c, 7, n_sample=256, seed=31)
+    codes_span_levels(pool, c["bt"], s.seq_lens[:1], group=group)
+    oracle = {b: oracle_overwrite(s, c, b) for b in (2, 7)}
+    got = decode_full(K, s, c, q, s.seq_lens)
+    assert np.isfinite(got).all()
+    check_sampled(s, c, q, got, [(2, 3), (7, 0)], oracle)

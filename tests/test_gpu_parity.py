@@ -322,12 +322,12 @@ def test_bf16_comparator_small(K):
 def full_cache(K, s, keep=()):
     """Prefill every sequence of workload s through the HIP append; returns the
     device state and the host token arrays of the sequences in ``keep``."""
-    shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window)
+    shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window, group_size=s.group_size)
     rk, rv = rotations(s.cfg)
     rkd, rvd = D(rk), D(rv)
     bt, n_pages = wl.page_table(s)
     btd, lensd = D(bt), D(s.seq_lens)
-    pool = torch.zeros((n_pages, 8, K.BLOCK_BYTES), dtype=torch.uint8, device=DEV)
+    pool = torch.zeros((n_pages, 8, K.block_bytes(s.group_size)), dtype=torch.uint8, device=DEV)
     wk = torch.zeros((s.batch, s.window, 8, 128), dtype=torch.int16, device=DEV)
     wv = torch.zeros_like(wk)
     kept = {}
@@ -366,7 +366,7 @@ def oracle_overwrite(s, c, b, extra=None):
     wk = np.zeros((s.window, 8, 128), np.uint16)
     wv = np.zeros_like(wk)
     ref.append_sequence_ref(ref.bf16_to_f64(c["rk"]), ref.bf16_to_f64(c["rv"]), k, v, np.arange(n_pg, dtype=np.int32),
-                            local, wk, wv, s.window)
+                            local, wk, wv, s.window, group=s.group_size)
     c["pool"].index_copy_(0, pages, D(local))
     c["wk"][b] = D(wk)
     c["wv"][b] = D(wv)
@@ -383,10 +383,10 @@ def check_sampled(s, c, q, got, pairs, oracle):
         local, wk, wv, n = oracle[b]
         row = np.arange(local.shape[0], dtype=np.int32)[None]
         want = ref.decode_ref(rkf, rvf, q[b:b + 1], np.array([n]), row, local, wk[None], wv[None], s.window,
-                              pairs=[(0, h)])[0, h * g:(h + 1) * g]
+                              pairs=[(0, h)], group=s.group_size)[0, h * g:(h + 1) * g]
         err = P.attn_rel_err(got[b, h * g:(h + 1) * g], want)
         worst = max(worst, float(err.max()))
-    log(f"config {s.cfg}: sampled pairs {pairs}: max rel err {worst:.3e}")
+    log(f"config {s.cfg} g={s.group_size}: sampled pairs {pairs}: max rel err {worst:.3e}")
     assert worst <= P.ATTN_TOL
 
 
@@ -398,25 +398,25 @@ def sampled_append_check(s, c, b, n_sample=512, seed=0):
     pos = np.arange(len(k), dtype=np.int32)
     si = np.full(len(k), b, np.int32)
     mism, excl, _ = P.check_append(None, pool, ref.bf16_to_f64(c["rk"]), ref.bf16_to_f64(c["rv"]), k, v, si, pos,
-                                   c["bt"], sample=idx)
-    log(f"config {s.cfg} seq {b}: {len(idx)} sampled tokens, mismatches={mism} excluded={excl}")
+                                   c["bt"], sample=idx, group=s.group_size)
+    log(f"config {s.cfg} g={s.group_size} seq {b}: {len(idx)} sampled tokens, mismatches={mism} excluded={excl}")
     assert mism == 0
     return pool
 
 
-def codes_span_levels(pool, bt, lens, hkv=8):
+def codes_span_levels(pool, bt, lens, hkv=8, group=128):
     """Every written group holds codes 0 and 3 (its min and max), any size."""
     for b in range(len(lens)):
         n = int(lens[b])
         pages = bt[b][:(n + 15) // 16]
         for c0 in range(0, len(pages), 256):
             pg = pages[c0:c0 + 256]
-            blk = pool[pg]                                                   # [np][hkv][1152]
+            blk = pool[pg]                                                   # [np][hkv][block bytes]
             kc = ref.unpack_k_rows(blk[..., :512].reshape(len(pg), hkv, 16, 32)).astype(np.int8)
             vc = ref.unpack_v_words(ref.v_words(blk)).astype(np.int8)       # [np][hkv][16][128]
             ntok = min(16 * len(pg), n - 16 * c0)
             for cc in (kc, vc):
-                cc = cc.transpose(0, 2, 1, 3).reshape(-1, hkv, 128)[:ntok]
+                cc = cc.transpose(0, 2, 1, 3).reshape(-1, hkv, 128 // group, group)[:ntok]
                 assert (cc.min(-1) == 0).all() and (cc.max(-1) == 3).all()
 
 

@@ -2,6 +2,7 @@
 rotation is the oracle's P_br (H / sqrt d), and its decoder of the page blocks
 reads exactly what the oracle's reader reads from a pool the oracle encoded."""
 import numpy as np
+import pytest
 
 import workloads as wl
 from kv_cache_int2_amd import quality
@@ -16,13 +17,15 @@ def test_hadamard_rotation_is_the_oracles():
     assert np.allclose(got @ got.T, np.eye(128), atol=1e-12)
 
 
-def test_dequantize_history_matches_oracle_reader(rng):
-    s, bt, pool, wk, wv, rk, rv, kv, q = build(rng, (70, 33, 16), 8)
+@pytest.mark.parametrize("group", [128, 64, 32])
+def test_dequantize_history_matches_oracle_reader(rng, group):
+    s, bt, pool, wk, wv, rk, rv, kv, q = build(rng, (70, 33, 16), 8, group=group)
+    assert quality.block_bytes(group) == pool.shape[-1]
     for b, n in enumerate(s.seq_lens):
         hist = int(n) - min(int(n), 8)
         for h in range(s.n_kv_heads):
-            k0, v0 = ref.read_history(pool, bt[b], hist, h) if hist else (np.zeros((0, 128)),) * 2
-            k1, v1 = quality.dequantize_history(pool, bt[b], hist, h)
+            k0, v0 = ref.read_history(pool, bt[b], hist, h, group) if hist else (np.zeros((0, 128)),) * 2
+            k1, v1 = quality.dequantize_history(pool, bt[b], hist, h, group)
             assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
 
 
