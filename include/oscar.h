@@ -71,7 +71,10 @@ typedef enum oscar_status {
   OSCAR_EINVAL = -1,        /* null pointer, negative size, inconsistent arguments */
   OSCAR_EUNSUPPORTED = -2,  /* shape outside the supported set above */
   OSCAR_EHIP = -3,          /* a HIP runtime call or kernel launch failed */
-  OSCAR_ENOSPACE = -4       /* workspace too small, or max_seq_len exceeds the block table */
+  OSCAR_ENOSPACE = -4,      /* workspace too small, or max_seq_len exceeds the block table */
+  OSCAR_EIO = -5,           /* a file could not be opened, read or written */
+  OSCAR_EFORMAT = -6        /* a file is not a rotation file of this version, is damaged
+                               (checksum, size), or does not match the caller's shape */
 } oscar_status;
 
 typedef struct oscar_shape {
@@ -112,6 +115,55 @@ typedef struct oscar_shape {
 int oscar_calibrate(const oscar_shape* shape, const float* q_cal, int64_t n_q,
                     const float* k_cal, const float* v_cal, int64_t n_kv,
                     uint16_t* r_k, uint16_t* r_v, double* eig_k, double* eig_v);
+
+/*
+ * oscar_calibrate for every layer of a model in one call, host only,
+ * synchronous: the n_layers * n_kv_heads heads are independent and run on a
+ * pool of host threads.  q_cal float [n_layers][n_kv_heads][n_q][128]; k_cal,
+ * v_cal float [n_layers][n_kv_heads][n_kv][128]; r_k, r_v out bf16 bits
+ * [n_layers][n_kv_heads][128][128]; eig_k, eig_v out double
+ * [n_layers][n_kv_heads][128] or NULL.  Layer l's results are bit-identical to
+ * oscar_calibrate on layer l's inputs.  Errors as oscar_calibrate, and
+ * OSCAR_EINVAL for n_layers < 1.
+ */
+int oscar_calibrate_layers(const oscar_shape* shape, int32_t n_layers, const float* q_cal, int64_t n_q,
+                           const float* k_cal, const float* v_cal, int64_t n_kv,
+                           uint16_t* r_k, uint16_t* r_v, double* eig_k, double* eig_v);
+
+/*
+ * Rotation files: a model's calibrated rotations, stored once and loaded at
+ * start (the pages ship precomputed rotations per supported model and treat
+ * calibration as a once-per-model step: P1 «Открытый код — это серьёзно»;
+ * P2 «OSCAR има значение…»; P4 «OSCAR: figyelem-tudatos…»).  Layout (little
+ * endian): a 64-byte header -- "OSCARROT", u32 version 1, u32 header bytes 64,
+ * u32 head_dim, u32 n_layers, u32 n_kv_heads, u32 group_size, u32 flags (bit 0:
+ * eigenvalues present), u32 0, u64 payload bytes, u32 CRC-32 of the payload,
+ * u32 CRC-32 of header bytes [0, 52), 8 zero bytes -- then per layer R_K bf16
+ * [n_kv_heads][128][128], R_V likewise, and with flag bit 0 eig_K, eig_V double
+ * [n_kv_heads][128].  CRC-32: reflected polynomial 0xEDB88320, initial value
+ * and final xor 0xFFFFFFFF.  All buffers are host memory, layer-major as in
+ * oscar_calibrate_layers; calls are synchronous.
+ *   oscar_rotation_file_bytes: the file size (0 for n_layers or n_kv_heads < 1).
+ *   oscar_rotation_write: writes (replaces) `path`; eig_k and eig_v both NULL
+ *     (no eigenvalues) or both set.  The shape gives n_kv_heads and group_size.
+ *   oscar_rotation_read_info: the header's n_layers, n_kv_heads, group_size and
+ *     whether eigenvalues are present (any out pointer may be NULL).
+ *   oscar_rotation_read: reads a file whose header matches shape (n_kv_heads,
+ *     group_size) and n_layers; eig_k/eig_v may be NULL (not read) or both set
+ *     (the file must hold them).
+ * Errors: OSCAR_EINVAL (null or inconsistent arguments), OSCAR_EUNSUPPORTED
+ * (shape), OSCAR_EIO (cannot open, read or write the file), OSCAR_EFORMAT (bad
+ * magic, version or checksum, wrong size, truncated or trailing bytes, header
+ * not matching the shape).  Nothing is written to the outputs on error.
+ */
+size_t oscar_rotation_file_bytes(int32_t n_layers, int32_t n_kv_heads, int32_t with_eigenvalues);
+int oscar_rotation_write(const char* path, const oscar_shape* shape, int32_t n_layers,
+                         const uint16_t* r_k, const uint16_t* r_v, const double* eig_k,
+                         const double* eig_v);
+int oscar_rotation_read_info(const char* path, int32_t* n_layers, int32_t* n_kv_heads,
+                             int32_t* group_size, int32_t* has_eigenvalues);
+int oscar_rotation_read(const char* path, const oscar_shape* shape, int32_t n_layers, uint16_t* r_k,
+                        uint16_t* r_v, double* eig_k, double* eig_v);
 
 /*
  * Online rotate -> quantise -> pack of new tokens into the paged INT2 cache,

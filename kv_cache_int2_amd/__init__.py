@@ -10,6 +10,7 @@ tensors holding the bit patterns.
 from __future__ import annotations
 
 import ctypes as C
+import os
 
 import numpy as np
 
@@ -20,6 +21,8 @@ __all__ = [
     "oscar_decode_workspace_bytes", "oscar_decode_attn", "oscar_bf16_append",
     "oscar_bf16_decode_attn", "oscar_hbm_copy", "oscar_timing_begin", "oscar_timing_end",
     "oscar_strerror", "BLOCK_BYTES", "BF16_BLOCK_ELEMS", "PAGE_SIZE", "HEAD_DIM", "block_bytes",
+    "oscar_calibrate_layers", "oscar_rotation_file_bytes", "oscar_rotation_write", "oscar_rotation_read_info",
+    "oscar_rotation_read",
 ]
 
 BLOCK_BYTES = 1152  # bytes per (page, KV head) block at group size 128
@@ -109,6 +112,70 @@ def oscar_calibrate(shape: OscarShape, q_cal: np.ndarray, k_cal: np.ndarray, v_c
         C.byref(shape), q.ctypes.data, q.shape[1], k.ctypes.data, v.ctypes.data, k.shape[1],
         rk.ctypes.data, rv.ctypes.data, ek.ctypes.data, ev.ctypes.data))
     return rk, rv, ek, ev
+
+
+def oscar_calibrate_layers(shape: OscarShape, q_cal: np.ndarray, k_cal: np.ndarray, v_cal: np.ndarray):
+    """Host calibration of every layer at once.  q_cal float32 [L][Hkv][n_q][128];
+    k_cal, v_cal float32 [L][Hkv][n_kv][128].  Returns (r_k, r_v) uint16
+    [L][Hkv][128][128] and (eig_k, eig_v) float64 [L][Hkv][128]."""
+    q = np.ascontiguousarray(q_cal, dtype=np.float32)
+    k = np.ascontiguousarray(k_cal, dtype=np.float32)
+    v = np.ascontiguousarray(v_cal, dtype=np.float32)
+    hkv = shape.n_kv_heads
+    if q.ndim != 4 or k.shape != v.shape or k.ndim != 4 or q.shape[:2] != k.shape[:2] or q.shape[1] != hkv:
+        raise ValueError("calibration arrays must be [L][Hkv][n][128]")
+    n_layers = q.shape[0]
+    rk = np.empty((n_layers, hkv, 128, 128), np.uint16)
+    rv = np.empty_like(rk)
+    ek = np.empty((n_layers, hkv, 128), np.float64)
+    ev = np.empty_like(ek)
+    _check("oscar_calibrate_layers", lib.oscar_calibrate_layers(
+        C.byref(shape), n_layers, q.ctypes.data, q.shape[2], k.ctypes.data, v.ctypes.data, k.shape[2],
+        rk.ctypes.data, rv.ctypes.data, ek.ctypes.data, ev.ctypes.data))
+    return rk, rv, ek, ev
+
+
+def oscar_rotation_file_bytes(n_layers: int, n_kv_heads: int, with_eigenvalues: bool = True) -> int:
+    return int(lib.oscar_rotation_file_bytes(int(n_layers), int(n_kv_heads), int(bool(with_eigenvalues))))
+
+
+def oscar_rotation_write(path: str, shape: OscarShape, r_k: np.ndarray, r_v: np.ndarray,
+                         eig_k: np.ndarray | None = None, eig_v: np.ndarray | None = None) -> None:
+    """Write rotations uint16 [L][Hkv][128][128] (and eigenvalues float64
+    [L][Hkv][128], optional) to a rotation file."""
+    rk = np.ascontiguousarray(r_k, dtype=np.uint16)
+    rv = np.ascontiguousarray(r_v, dtype=np.uint16)
+    if rk.ndim != 4 or rk.shape != rv.shape or rk.shape[1:] != (shape.n_kv_heads, 128, 128):
+        raise ValueError("rotations must be [L][Hkv][128][128]")
+    ek = None if eig_k is None else np.ascontiguousarray(eig_k, dtype=np.float64)
+    ev = None if eig_v is None else np.ascontiguousarray(eig_v, dtype=np.float64)
+    for e in (ek, ev):
+        if e is not None and e.shape != rk.shape[:3]:
+            raise ValueError("eigenvalues must be [L][Hkv][128]")
+    _check("oscar_rotation_write", lib.oscar_rotation_write(
+        os.fsencode(path), C.byref(shape), rk.shape[0], rk.ctypes.data, rv.ctypes.data,
+        None if ek is None else ek.ctypes.data, None if ev is None else ev.ctypes.data))
+
+
+def oscar_rotation_read_info(path: str) -> dict:
+    """Header of a rotation file: n_layers, n_kv_heads, group_size, has_eigenvalues."""
+    vals = [C.c_int32() for _ in range(4)]
+    _check("oscar_rotation_read_info", lib.oscar_rotation_read_info(os.fsencode(path), *[C.byref(x) for x in vals]))
+    return dict(zip(("n_layers", "n_kv_heads", "group_size", "has_eigenvalues"), (int(x.value) for x in vals)))
+
+
+def oscar_rotation_read(path: str, shape: OscarShape, n_layers: int, eigenvalues: bool = False):
+    """Rotations (r_k, r_v) uint16 [L][Hkv][128][128] of a rotation file whose
+    header matches shape and n_layers; with ``eigenvalues`` also (eig_k, eig_v)."""
+    hkv = shape.n_kv_heads
+    rk = np.empty((n_layers, hkv, 128, 128), np.uint16)
+    rv = np.empty_like(rk)
+    ek = np.empty((n_layers, hkv, 128), np.float64) if eigenvalues else None
+    ev = np.empty_like(ek) if eigenvalues else None
+    _check("oscar_rotation_read", lib.oscar_rotation_read(
+        os.fsencode(path), C.byref(shape), int(n_layers), rk.ctypes.data, rv.ctypes.data,
+        None if ek is None else ek.ctypes.data, None if ev is None else ev.ctypes.data))
+    return (rk, rv, ek, ev) if eigenvalues else (rk, rv)
 
 
 def oscar_quantize_append(shape, r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,

@@ -25,6 +25,12 @@ SHAPE = C.POINTER(OscarShape)
 # name -> (restype, argtypes); mirrors include/oscar.h
 SIGNATURES = {
     "oscar_calibrate": (C.c_int, [SHAPE, P, I64, P, P, I64, P, P, P, P]),
+    "oscar_calibrate_layers": (C.c_int, [SHAPE, I32, P, I64, P, P, I64, P, P, P, P]),
+    "oscar_rotation_file_bytes": (SZ, [I32, I32, I32]),
+    "oscar_rotation_write": (C.c_int, [C.c_char_p, SHAPE, I32, P, P, P, P]),
+    "oscar_rotation_read_info": (C.c_int, [C.c_char_p, C.POINTER(I32), C.POINTER(I32), C.POINTER(I32),
+                                           C.POINTER(I32)]),
+    "oscar_rotation_read": (C.c_int, [C.c_char_p, SHAPE, I32, P, P, P, P]),
     "oscar_quantize_append": (C.c_int, [SHAPE, P, P, P, P, I64, P, P, I32, P, I32, P, P, I64, P, P, P]),
     "oscar_decode_workspace_bytes": (SZ, [SHAPE, I32, I32]),
     "oscar_decode_attn": (C.c_int, [SHAPE, P, P, P, I32, P, I32, P, I32, P, I64, P, P, P, P, SZ, P]),

@@ -196,20 +196,22 @@ bool finite_all(const float* p, int64_t n) {
 
 }  // namespace
 
-extern "C" int oscar_calibrate(const oscar_shape* shape, const float* q_cal, int64_t n_q,
-                               const float* k_cal, const float* v_cal, int64_t n_kv, uint16_t* r_k,
-                               uint16_t* r_v, double* eig_k, double* eig_v) {
+namespace {
+
+// Calibrates n_layers x Hkv independent heads on a pool of host threads.
+int calibrate_all(const oscar_shape* shape, int n_layers, const float* q_cal, int64_t n_q, const float* k_cal,
+                  const float* v_cal, int64_t n_kv, uint16_t* r_k, uint16_t* r_v, double* eig_k, double* eig_v) {
   int st = oscar::check_shape(shape);
   if (st != OSCAR_OK) return st;
-  if (!q_cal || !k_cal || !v_cal || !r_k || !r_v || n_q < 1 || n_kv < 1) return OSCAR_EINVAL;
-  const int hkv = shape->n_kv_heads;
-  if (!finite_all(q_cal, (int64_t)hkv * n_q * D) || !finite_all(k_cal, (int64_t)hkv * n_kv * D) ||
-      !finite_all(v_cal, (int64_t)hkv * n_kv * D))
+  if (!q_cal || !k_cal || !v_cal || !r_k || !r_v || n_q < 1 || n_kv < 1 || n_layers < 1) return OSCAR_EINVAL;
+  const int64_t heads = (int64_t)n_layers * shape->n_kv_heads;
+  if (!finite_all(q_cal, heads * n_q * D) || !finite_all(k_cal, heads * n_kv * D) ||
+      !finite_all(v_cal, heads * n_kv * D))
     return OSCAR_EINVAL;
   std::vector<std::thread> pool;
   unsigned hw = std::max(1u, std::thread::hardware_concurrency());
   std::vector<HeadJob> jobs;
-  for (int h = 0; h < hkv; ++h)
+  for (int64_t h = 0; h < heads; ++h)  // layer-major: head h of the flattened [n_layers][Hkv]
     jobs.push_back(HeadJob{q_cal + (size_t)h * n_q * D, k_cal + (size_t)h * n_kv * D,
                            v_cal + (size_t)h * n_kv * D, n_q, n_kv, r_k + (size_t)h * D * D,
                            r_v + (size_t)h * D * D, eig_k ? eig_k + (size_t)h * D : nullptr,
@@ -222,4 +224,18 @@ extern "C" int oscar_calibrate(const oscar_shape* shape, const float* q_cal, int
     for (auto& th : pool) th.join();
   }
   return OSCAR_OK;
+}
+
+}  // namespace
+
+extern "C" int oscar_calibrate(const oscar_shape* shape, const float* q_cal, int64_t n_q,
+                               const float* k_cal, const float* v_cal, int64_t n_kv, uint16_t* r_k,
+                               uint16_t* r_v, double* eig_k, double* eig_v) {
+  return calibrate_all(shape, 1, q_cal, n_q, k_cal, v_cal, n_kv, r_k, r_v, eig_k, eig_v);
+}
+
+extern "C" int oscar_calibrate_layers(const oscar_shape* shape, int32_t n_layers, const float* q_cal, int64_t n_q,
+                                      const float* k_cal, const float* v_cal, int64_t n_kv, uint16_t* r_k,
+                                      uint16_t* r_v, double* eig_k, double* eig_v) {
+  return calibrate_all(shape, n_layers, q_cal, n_q, k_cal, v_cal, n_kv, r_k, r_v, eig_k, eig_v);
 }

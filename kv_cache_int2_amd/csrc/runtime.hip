@@ -115,6 +115,8 @@ extern "C" const char* oscar_strerror(int status) {
     case OSCAR_EUNSUPPORTED: return "unsupported shape";
     case OSCAR_EHIP: return "HIP runtime or launch failure";
     case OSCAR_ENOSPACE: return "workspace too small or sequence longer than the block table";
+    case OSCAR_EIO: return "file could not be opened, read or written";
+    case OSCAR_EFORMAT: return "not a rotation file of this format, damaged, or not matching the shape";
   }
   return "unknown status";
 }
