@@ -232,6 +232,38 @@ int oscar_decode_attn(const oscar_shape* shape, const uint16_t* r_k, const uint1
                       void* stream);
 
 /*
+ * Layer-batched forms: the caches of n_layers layers (every layer holding the
+ * same sequences, as the layers of one model do) in one call, one launch per
+ * kernel instead of one per layer (the rotation-file workflow calibrates and
+ * stores every layer of a model at once; P2 «OSCAR има значение…»).
+ * Per-layer buffers are stacked layer-major, each layer exactly as for the
+ * single-layer call: r_k, r_v [n_layers][n_kv_heads][128][128]; k_new, v_new
+ * [n_layers][n_tokens][n_kv_heads][128]; q [n_layers][batch][n_q_heads][128];
+ * pool [n_layers][n_pages][n_kv_heads][BLOCK]; win_k, win_v
+ * [n_layers][batch][window + n_sink][n_kv_heads][128]; out
+ * [n_layers][batch][n_q_heads][128].  seq_idx, pos, block_table, seq_lens and
+ * seq_len_after are shared by all layers (a page id names the same slot in every
+ * layer's pool).  Layer l's results are those of the single-layer call on layer
+ * l's buffers.  The decode workspace is oscar_decode_layers_workspace_bytes.
+ * Errors as the single-layer calls; OSCAR_EINVAL also for n_layers < 1 or
+ * n_layers * batch > 65535 (decode), n_layers > 32767 (append).
+ */
+int oscar_quantize_append_layers(const oscar_shape* shape, int32_t n_layers, const uint16_t* r_k,
+                                 const uint16_t* r_v, const uint16_t* k_new, const uint16_t* v_new,
+                                 int64_t n_tokens, const int32_t* seq_idx, const int32_t* pos, int32_t batch,
+                                 const int32_t* block_table, int32_t max_pages_per_seq,
+                                 const int32_t* seq_len_after, uint8_t* pool, int64_t n_pages,
+                                 uint16_t* win_k, uint16_t* win_v, void* stream);
+size_t oscar_decode_layers_workspace_bytes(const oscar_shape* shape, int32_t n_layers, int32_t batch,
+                                           int32_t max_seq_len);
+int oscar_decode_attn_layers(const oscar_shape* shape, int32_t n_layers, const uint16_t* r_k,
+                             const uint16_t* r_v, const uint16_t* q, int32_t batch, const int32_t* seq_lens,
+                             int32_t max_seq_len, const int32_t* block_table, int32_t max_pages_per_seq,
+                             const uint8_t* pool, int64_t n_pages, const uint16_t* win_k,
+                             const uint16_t* win_v, float* out, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
  * bf16-KV comparator (not part of the method; the baseline the INT2 decode is
  * measured against, P2 «OSCAR има значение…» and P3 «Resultados e Métricas de
  * Desempenho» quote decode speed against a BF16 cache).  Paged bf16 pool:

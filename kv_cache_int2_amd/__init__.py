@@ -22,7 +22,8 @@ __all__ = [
     "oscar_bf16_decode_attn", "oscar_hbm_copy", "oscar_timing_begin", "oscar_timing_end",
     "oscar_strerror", "BLOCK_BYTES", "BF16_BLOCK_ELEMS", "PAGE_SIZE", "HEAD_DIM", "block_bytes",
     "oscar_calibrate_layers", "oscar_rotation_file_bytes", "oscar_rotation_write", "oscar_rotation_read_info",
-    "oscar_rotation_read",
+    "oscar_rotation_read", "oscar_quantize_append_layers", "oscar_decode_layers_workspace_bytes",
+    "oscar_decode_attn_layers",
 ]
 
 BLOCK_BYTES = 1152  # bytes per (page, KV head) block at group size 128
@@ -206,6 +207,52 @@ def oscar_decode_attn(shape, r_k, r_v, q, seq_lens, max_seq_len, block_table, po
         int(q.shape[0]), _dev(seq_lens, i32, "seq_lens"), int(max_seq_len),
         _dev(block_table, i32, "block_table"), int(block_table.shape[1]), _dev(pool, u8, "pool"),
         int(pool.shape[0]), _dev(win_k, b16, "win_k"), _dev(win_v, b16, "win_v"),
+        _dev(out, f32, "out"), _dev(workspace, u8, "workspace"), int(workspace.numel()),
+        _stream(stream)))
+
+
+def oscar_quantize_append_layers(shape, r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,
+                                 pool, win_k=None, win_v=None, stream=None) -> None:
+    """Layer-batched append: r_k, r_v [L][Hkv][128][128]; k_new, v_new
+    [L][T][Hkv][128]; pool [L][n_pages][Hkv][block]; rings [L][B][W + S][Hkv][128]."""
+    b16, i32, u8, _ = _dt()
+    n_layers = int(pool.shape[0])
+    for name, t in (("r_k", r_k), ("r_v", r_v), ("k_new", k_new), ("v_new", v_new)):
+        if t.shape[0] != n_layers:
+            raise ValueError(f"{name}: leading (layer) dimension must be {n_layers}")
+    if pool.dim() != 4 or pool.shape[2] != shape.n_kv_heads or pool.shape[3] != block_bytes(shape.group_size):
+        raise ValueError("pool must be [L][n_pages][Hkv][block bytes]")
+    _check("oscar_quantize_append_layers", lib.oscar_quantize_append_layers(
+        C.byref(shape), n_layers, _dev(r_k, b16, "r_k"), _dev(r_v, b16, "r_v"), _dev(k_new, b16, "k_new"),
+        _dev(v_new, b16, "v_new"), int(k_new.shape[1]), _dev(seq_idx, i32, "seq_idx"),
+        _dev(pos, i32, "pos"), int(block_table.shape[0]), _dev(block_table, i32, "block_table"),
+        int(block_table.shape[1]), _dev(seq_len_after, i32, "seq_len_after"), _dev(pool, u8, "pool"),
+        int(pool.shape[1]), _dev(win_k, b16, "win_k"), _dev(win_v, b16, "win_v"), _stream(stream)))
+
+
+def oscar_decode_layers_workspace_bytes(shape, n_layers: int, batch: int, max_seq_len: int) -> int:
+    n = lib.oscar_decode_layers_workspace_bytes(C.byref(shape), int(n_layers), int(batch), int(max_seq_len))
+    if n == 0:
+        raise OscarError("oscar_decode_layers_workspace_bytes", -1)
+    return int(n)
+
+
+def oscar_decode_attn_layers(shape, r_k, r_v, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v,
+                             out, workspace, stream=None) -> None:
+    """Layer-batched decode: q [L][B][Hq][128], out [L][B][Hq][128] float32,
+    other per-layer buffers stacked as for oscar_quantize_append_layers."""
+    b16, i32, u8, f32 = _dt()
+    n_layers = int(pool.shape[0])
+    for name, t in (("r_k", r_k), ("r_v", r_v), ("q", q), ("out", out)):
+        if t.shape[0] != n_layers:
+            raise ValueError(f"{name}: leading (layer) dimension must be {n_layers}")
+    if pool.dim() != 4 or pool.shape[2] != shape.n_kv_heads or pool.shape[3] != block_bytes(shape.group_size):
+        raise ValueError("pool must be [L][n_pages][Hkv][block bytes]")
+    _check("oscar_decode_attn_layers", lib.oscar_decode_attn_layers(
+        C.byref(shape), n_layers, _dev(r_k, b16, "r_k"), _dev(r_v, b16, "r_v"), _dev(q, b16, "q"),
+        int(q.shape[1]), _dev(seq_lens, i32, "seq_lens"), int(max_seq_len),
+        _dev(block_table, i32, "block_table"), int(block_table.shape[1]), _dev(pool, u8, "pool"),
+        int(pool.shape[1]), _dev(win_k, b16, "win_k"), _dev(win_v, b16, "win_v"),
         _dev(out, f32, "out"), _dev(workspace, u8, "workspace"), int(workspace.numel()),
         _stream(stream)))
 

@@ -33,6 +33,10 @@ SIGNATURES = {
     "oscar_rotation_read": (C.c_int, [C.c_char_p, SHAPE, I32, P, P, P, P]),
     "oscar_quantize_append": (C.c_int, [SHAPE, P, P, P, P, I64, P, P, I32, P, I32, P, P, I64, P, P, P]),
     "oscar_decode_workspace_bytes": (SZ, [SHAPE, I32, I32]),
+    "oscar_quantize_append_layers": (C.c_int, [SHAPE, I32, P, P, P, P, I64, P, P, I32, P, I32, P, P, I64, P, P,
+                                               P]),
+    "oscar_decode_layers_workspace_bytes": (SZ, [SHAPE, I32, I32, I32]),
+    "oscar_decode_attn_layers": (C.c_int, [SHAPE, I32, P, P, P, I32, P, I32, P, I32, P, I64, P, P, P, P, SZ, P]),
     "oscar_decode_attn": (C.c_int, [SHAPE, P, P, P, I32, P, I32, P, I32, P, I64, P, P, P, P, SZ, P]),
     "oscar_bf16_append": (C.c_int, [SHAPE, P, P, I64, P, P, I32, P, I32, P, I64, P]),
     "oscar_bf16_decode_attn": (C.c_int, [SHAPE, P, I32, P, I32, P, I32, P, I64, P, P, SZ, P]),

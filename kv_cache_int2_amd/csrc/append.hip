@@ -49,6 +49,10 @@ struct AppendParams {
   int batch, max_pages, hkv, window, tiles_per_wg;
   int n_sink;  // leading positions also kept in bf16 (ring rows window + pos)
   int ring;    // ring rows per sequence: window + n_sink
+  // layers appended in one launch: rotations, tokens, rings and pools stacked
+  // layer-major with these strides (elements; pool in bytes); positions, block
+  // table and lengths shared by all layers
+  int64_t ls_rot, ls_x, ls_win, ls_pool;
 };
 
 constexpr int kRowU4 = 17;  // LDS row stride of R in uint4 (16 + 1 pad: 272 B)
@@ -302,8 +306,17 @@ template <int NG>
 __global__ __launch_bounds__(256, 4) void append_kernel(AppendParams p) {
   __shared__ uint4 r_lds[128 * kRowU4];
   const int h = blockIdx.y;
-  const int kind = blockIdx.z;
-  const uint4* rg = reinterpret_cast<const uint4*>(p.r[kind] + (int64_t)h * kD * kD);
+  const int kind = blockIdx.z & 1, layer = blockIdx.z >> 1;
+  if (layer > 0) {  // static indices only: the parameters stay in scalar registers
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      p.r[k] += layer * p.ls_rot;
+      p.x[k] += layer * p.ls_x;
+      if (p.win[k]) p.win[k] += layer * p.ls_win;
+    }
+    p.pool += layer * p.ls_pool;
+  }
+  const uint4* rg = reinterpret_cast<const uint4*>((kind ? p.r[1] : p.r[0]) + (int64_t)h * kD * kD);
   for (int i = threadIdx.x; i < 128 * 16; i += 256) r_lds[(i >> 4) * kRowU4 + (i & 15)] = rg[i];
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -320,16 +333,17 @@ __global__ __launch_bounds__(256, 4) void append_kernel(AppendParams p) {
 }  // namespace
 }  // namespace oscar
 
-extern "C" int oscar_quantize_append(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
-                                     const uint16_t* k_new, const uint16_t* v_new, int64_t n_tokens,
-                                     const int32_t* seq_idx, const int32_t* pos, int32_t batch,
-                                     const int32_t* block_table, int32_t max_pages_per_seq,
-                                     const int32_t* seq_len_after, uint8_t* pool, int64_t n_pages,
-                                     uint16_t* win_k, uint16_t* win_v, void* stream) {
+extern "C" int oscar_quantize_append_layers(const oscar_shape* shape, int32_t n_layers, const uint16_t* r_k,
+                                            const uint16_t* r_v, const uint16_t* k_new, const uint16_t* v_new,
+                                            int64_t n_tokens, const int32_t* seq_idx, const int32_t* pos,
+                                            int32_t batch, const int32_t* block_table, int32_t max_pages_per_seq,
+                                            const int32_t* seq_len_after, uint8_t* pool, int64_t n_pages,
+                                            uint16_t* win_k, uint16_t* win_v, void* stream) {
   using namespace oscar;
   int st = check_shape(shape);
   if (st != OSCAR_OK) return st;
   if (n_tokens < 0 || batch < 1 || max_pages_per_seq < 1 || n_pages < 1) return OSCAR_EINVAL;
+  if (n_layers < 1 || n_layers > 32767) return OSCAR_EINVAL;
   if (n_tokens == 0) return OSCAR_OK;
   if (!r_k || !r_v || !k_new || !v_new || !seq_idx || !pos || !block_table || !seq_len_after || !pool)
     return OSCAR_EINVAL;
@@ -360,9 +374,13 @@ extern "C" int oscar_quantize_append(const oscar_shape* shape, const uint16_t* r
   p.window = shape->window;
   p.n_sink = shape->n_sink;
   p.ring = shape->window + shape->n_sink;
+  p.ls_rot = (int64_t)p.hkv * kD * kD;
+  p.ls_x = n_tokens * p.hkv * kD;
+  p.ls_win = (int64_t)batch * p.ring * p.hkv * kD;
+  p.ls_pool = n_pages * p.hkv * p.block;
   const int64_t tiles = (n_tokens + kAppendTokens - 1) / kAppendTokens;  // workgroup iterations
   p.tiles_per_wg = tiles >= 512 ? 4 : (tiles >= 128 ? 2 : 1);
-  dim3 grid((unsigned)((tiles + p.tiles_per_wg - 1) / p.tiles_per_wg), (unsigned)p.hkv, 2);
+  dim3 grid((unsigned)((tiles + p.tiles_per_wg - 1) / p.tiles_per_wg), (unsigned)p.hkv, 2 * (unsigned)n_layers);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int slot = -1;
   timing_record_begin(s, 3, &slot);
@@ -374,4 +392,14 @@ extern "C" int oscar_quantize_append(const oscar_shape* shape, const uint16_t* r
   hipError_t e = hipGetLastError();
   timing_record_end(s, slot);
   return e == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
+}
+
+extern "C" int oscar_quantize_append(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
+                                     const uint16_t* k_new, const uint16_t* v_new, int64_t n_tokens,
+                                     const int32_t* seq_idx, const int32_t* pos, int32_t batch,
+                                     const int32_t* block_table, int32_t max_pages_per_seq,
+                                     const int32_t* seq_len_after, uint8_t* pool, int64_t n_pages,
+                                     uint16_t* win_k, uint16_t* win_v, void* stream) {
+  return oscar_quantize_append_layers(shape, 1, r_k, r_v, k_new, v_new, n_tokens, seq_idx, pos, batch, block_table,
+                                      max_pages_per_seq, seq_len_after, pool, n_pages, win_k, win_v, stream);
 }

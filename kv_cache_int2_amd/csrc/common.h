@@ -99,24 +99,28 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct WorkspaceLayout {
   size_t qsum, qop, part, wpart, tile_prefix, total;
 };
+// n_layers > 1 (INT2 only): the per-layer regions (qsum, qop, wpart) repeat
+// for every layer; the split partials and the tile prefix cover the units of
+// all layers.  The stride of a per-layer region is its size rounded to 256 B.
 inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int window, int n_sink, int ng,
-                                        const SplitPlan& p, int n_cu) {
+                                        const SplitPlan& p, int n_cu, int n_layers = 1) {
   const int gqa = n_q_heads / n_kv_heads;
   const size_t g4 = (size_t)((gqa + 3) / 4);
   const size_t gw = (size_t)int2_unit_heads(gqa, ng);
-  const size_t units = (size_t)batch * n_q_heads / (gw * (size_t)split_heads_per_wg(n_kv_heads));
+  const size_t L = (size_t)n_layers;
+  const size_t units = L * batch * n_q_heads / (gw * (size_t)split_heads_per_wg(n_kv_heads));
   const size_t part_bf16 = (size_t)batch * n_q_heads * p.n_splits * kPartStride;
   const size_t n_wg = (size_t)split_wg_count(gqa, n_cu);
   const size_t part_int2 = (n_wg + units) * 4 * gw * kPartStride;
   WorkspaceLayout w{};
   w.qsum = 0;
-  w.qop = w.qsum + align256((size_t)batch * n_q_heads * ng * sizeof(float));
-  w.part = w.qop + align256((size_t)batch * n_kv_heads * g4 * 64 * 9 * sizeof(int));
+  w.qop = w.qsum + L * align256((size_t)batch * n_q_heads * ng * sizeof(float));
+  w.part = w.qop + L * align256((size_t)batch * n_kv_heads * g4 * 64 * 9 * sizeof(int));
   w.wpart = w.part + align256((part_bf16 > part_int2 ? part_bf16 : part_int2) * sizeof(float));
   const size_t n_wchunks = (size_t)((window + kWinChunk - 1) / kWinChunk + (n_sink + kWinChunk - 1) / kWinChunk);
   // at least one partial: the merge reads chunk 0 of its head unconditionally
   const size_t n_wparts = (size_t)batch * n_q_heads * n_wchunks;
-  w.tile_prefix = w.wpart + align256((n_wparts > 0 ? n_wparts : 1) * kPartStride * sizeof(float));
+  w.tile_prefix = w.wpart + L * align256((n_wparts > 0 ? n_wparts : 1) * kPartStride * sizeof(float));
   w.total = w.tile_prefix + align256((units + 1) * sizeof(int));
   return w;
 }

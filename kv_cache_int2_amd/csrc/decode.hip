@@ -135,7 +135,31 @@ struct SplitParams {
   int block;                  // INT2: bytes per (page, KV head) block, 1024 + 128 ng
   int ng;                     // INT2: quantisation groups per token (1, 2 or 4)
   float scale_log2;           // log2(e) / sqrt(d)
+  // INT2: layers decoded in one call.  q, out, r_v (and r_k), pool, the rings
+  // and the per-layer workspace regions are stacked layer-major with these
+  // strides (elements of each buffer's type; pool in bytes); the block table
+  // and lengths are shared; the split partials and the tile prefix span all
+  // layers (units layer-major).
+  int n_layers;
+  int64_t ls_q, ls_out, ls_rot, ls_pool, ls_win, ls_qsum, ls_qop, ls_wpart;
 };
+
+// The parameters of layer l: every per-layer buffer advanced by l strides.
+__device__ __forceinline__ SplitParams layer_params(const SplitParams& p, int l) {
+  SplitParams r = p;
+  if (l > 0) {
+    r.q += l * p.ls_q;
+    r.out += l * p.ls_out;
+    r.r_v += l * p.ls_rot;
+    r.pool += l * p.ls_pool;
+    r.win_k += l * p.ls_win;
+    r.win_v += l * p.ls_win;
+    r.qsum += l * p.ls_qsum;
+    r.qop += l * p.ls_qop;
+    r.wpart += l * p.ls_wpart;
+  }
+  return r;
+}
 
 // Sequence length as the kernels see it: clamped to [0, max_len].
 __device__ __forceinline__ int seq_len_of(const SplitParams& p, int b) {
@@ -261,31 +285,43 @@ __device__ void window_chunk(const SplitParams& p, int b, int h, int c, int G, f
 //   consumes it.
 // ---------------------------------------------------------------------------
 template <int G>
-__global__ __launch_bounds__(256) void prep_kernel(SplitParams p, const uint16_t* __restrict__ r_k) {
+__global__ __launch_bounds__(256) void prep_kernel(SplitParams p0, const uint16_t* __restrict__ r_k0) {
   constexpr int NCB = (G + 3) / 4;  // 4-head operand groups
   constexpr int kQBytes = 2 * G * kD * 4 + G * 4;
   constexpr int kSmem = kQBytes > window_smem_bytes<G>() ? kQBytes : window_smem_bytes<G>();
   __shared__ __align__(16) float smem_f[kSmem / 4];
-  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int layer = blockIdx.x / p0.batch, b = blockIdx.x % p0.batch, h = blockIdx.y, tid = threadIdx.x;
+  const SplitParams p = layer_params(p0, layer);
+  const uint16_t* r_k = r_k0 + layer * p0.ls_rot;
   const int hq = p.hq, hkv = p.hkv;
   if (blockIdx.z > 0) {  // chunk z - 1 of the bf16 window of this (sequence, KV head)
     window_chunk<G>(p, b, h, blockIdx.z - 1, G, smem_f);
     return;
   }
-  // first history tile of the units (b, head group, sub) in the flattened order
-  // (sequence-major, then KV head group, then head subset), written by the first
-  // head of each group; the last group also closes the array
-  if (tid < 64 && h % p.hw == 0) {  // wave 0: tiles of the sequences before b, summed across lanes
-    int pb = 0;
-    for (int bb = tid; bb < b; bb += 64) pb += hist_tiles(p, bb);
+  // first history tile of the units (layer, b, head group, sub) in the
+  // flattened order (layer-major, then sequence, KV head group, head subset),
+  // written by the first head of each group; the last group also closes the
+  // array.  Every layer has the same sequences, hence the same T tiles.
+  if (tid < 64 && h % p.hw == 0) {  // wave 0: tiles of the sequences before b and of all, summed across lanes
+    int pb = 0, pt = 0;
+    for (int bb = tid; bb < p.batch; bb += 64) {
+      const int tt = hist_tiles(p, bb);
+      pb += bb < b ? tt : 0;
+      pt += tt;
+    }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) pb += __shfl_xor(pb, o);
+    for (int o = 32; o > 0; o >>= 1) {
+      pb += __shfl_xor(pb, o);
+      pt += __shfl_xor(pt, o);
+    }
     const int tb = hist_tiles(p, b);
     const int hgp = h / p.hw, per_seq = (hkv / p.hw) * p.gsub;
+    const int64_t u0 = (int64_t)layer * p.batch * per_seq, t0 = (int64_t)layer * per_seq * pt;
     for (int sub = tid; sub < p.gsub; sub += 64)
-      p.tile_prefix[(int64_t)b * per_seq + hgp * p.gsub + sub] = per_seq * pb + (hgp * p.gsub + sub) * tb;
-    if (tid == 0 && b == p.batch - 1 && h == hkv - p.hw)
-      p.tile_prefix[(int64_t)p.batch * per_seq] = per_seq * (pb + tb);
+      p.tile_prefix[u0 + (int64_t)b * per_seq + hgp * p.gsub + sub] =
+          (int)(t0 + per_seq * pb + (hgp * p.gsub + sub) * tb);
+    if (tid == 0 && layer == p.n_layers - 1 && b == p.batch - 1 && h == hkv - p.hw)
+      p.tile_prefix[u0 + (int64_t)p.batch * per_seq] = (int)(t0 + (int64_t)per_seq * pt);
   }
   float (*qs)[kD] = reinterpret_cast<float (*)[kD]>(smem_f);
   float (*qraw)[kD] = reinterpret_cast<float (*)[kD]>(smem_f + G * kD);
@@ -721,7 +757,8 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
 
   const int hg_per_seq = p.hkv / p.hw;  // KV head groups per sequence
   const int per_seq = hg_per_seq * p.gsub;
-  const int units = p.batch * per_seq;
+  const int units_layer = p.batch * per_seq;
+  const int units = p.n_layers * units_layer;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lr = lane & 15;
   const int ts = 4 / p.hw;  // waves sharing a head (tile stride)
@@ -751,7 +788,9 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
 
   // Steps [0, ns) of phase ph, KV head hv of the group, in tiles [a, e) of
   // unit u (indices within the unit); the wave's partial to dst.
-  auto run_steps = [&](int u, int a, int e, int ph, int hv, int ns, float* dst) {
+  auto run_steps = [&](int ug, int a, int e, int ph, int hv, int ns, float* dst) {
+    const int layer = ug / units_layer, u = ug % units_layer;
+    const SplitParams pl = layer_params(p, layer);
     const int b = u / per_seq, hs = u % per_seq, hgp = hs / p.gsub, sub = hs % p.gsub;
     const int h = hgp * p.hw + hv;                   // the KV head
     const int hq0 = h * p.gw * p.gsub + sub * p.gw;  // first query head of the unit
@@ -765,12 +804,12 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
     float qsr[NRG][NG];
 #pragma unroll
     for (int rg = 0; rg < NRG; ++rg) {
-      const int* src = p.qop + ((((int64_t)b * p.hkv + h) * ncb + (sub * p.gw) / 4 + rg) * 64 + lane) * 9;
+      const int* src = pl.qop + ((((int64_t)b * p.hkv + h) * ncb + (sub * p.gw) / 4 + rg) * 64 + lane) * 9;
 #pragma unroll
       for (int i = 0; i < 8; ++i) qa[rg][i] = src[i];
       qsc[rg] = src[8];
       const bool hv = 4 * rg + lg < p.gw;
-      const float* qs = p.qsum + ((int64_t)b * p.hq + hq0 + (hv ? 4 * rg + lg : 0)) * NG;
+      const float* qs = pl.qsum + ((int64_t)b * p.hq + hq0 + (hv ? 4 * rg + lg : 0)) * NG;
 #pragma unroll
       for (int jg = 0; jg < NG; ++jg) qsr[rg][jg] = hv ? qs[jg] : 0.f;
     }
@@ -799,9 +838,9 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
       for (int s = 0;; ++s) {
         const int k = 2 * s;
         Tile<NG> t;
-        load_tile(p, tab, 0, h, pbase_of(k), t_end, lg, lr, t);
+        load_tile(pl, tab, 0, h, pbase_of(k), t_end, lg, lr, t);
         compute_tile<G, NRG, false, NG>(p, t, pbase_of(k), t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
-        load_tile(p, tab, 1, h, pbase_of(k + 1), t_end, lg, lr, t);
+        load_tile(pl, tab, 1, h, pbase_of(k + 1), t_end, lg, lr, t);
         compute_tile<G, NRG, false, NG>(p, t, pbase_of(k + 1), t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
         if (s + 1 >= ns) break;
         tab = table_ready(p, raw_next, P0, P1, ph, ts, k + 2, ntw);
@@ -809,17 +848,17 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
       }
     } else {  // two tiles in flight per wave: tile k + 1's loads go out before tile k is computed
       Tile<NG> ta, tb;
-      load_tile(p, tab, 0, h, pbase_of(0), t_end, lg, lr, ta);
+      load_tile(pl, tab, 0, h, pbase_of(0), t_end, lg, lr, ta);
       for (int s = 0;; ++s) {
         const int k = 2 * s;
-        load_tile(p, tab, 1, h, pbase_of(k + 1), t_end, lg, lr, tb);
+        load_tile(pl, tab, 1, h, pbase_of(k + 1), t_end, lg, lr, tb);
         compute_tile<G, NRG, false, NG>(p, ta, pbase_of(k), t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
         const bool more = s + 1 < ns;
         // past the last step the table is empty: tile k + 2 re-reads page 0's
         // block (cache resident) and is never computed
         tab = table_ready(p, raw_next, P0, P1, ph, ts, k + 2, more ? ntw : 0);
         raw_next = table_load(btr, P0, P1, ph, ts, k + 4);
-        load_tile(p, tab, 0, h, pbase_of(k + 2), t_end, lg, lr, ta);
+        load_tile(pl, tab, 0, h, pbase_of(k + 2), t_end, lg, lr, ta);
         compute_tile<G, NRG, false, NG>(p, tb, pbase_of(k + 1), t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
         if (!more) break;
       }
@@ -1068,8 +1107,10 @@ constexpr int kMergePass = 32;  // partials per pass
 constexpr int kMergeWin = 8;    // window / sink chunk partials held in registers
 constexpr int kMergeHeads = 4;  // q heads per workgroup at most (one per wave)
 
-__global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq, int mh) {
-  const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+__global__ __launch_bounds__(256) void merge_kernel(SplitParams p0, int gq, int mh) {
+  const int layer = blockIdx.y / p0.batch, b = blockIdx.y % p0.batch;
+  const SplitParams p = layer_params(p0, layer);
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool active = wave < mh;
   const int hq = blockIdx.x * mh + (active ? wave : 0), h = hq / gq;
   const bool int2 = p.r_v != nullptr;
@@ -1085,8 +1126,8 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p, int gq, int m
   if (int2) {
     const int jq = hq % gq, sub = jq / p.gw, g = jq % p.gw;
     const int per_seq = (p.hkv / p.hw) * p.gsub;
-    const int u = b * per_seq + (h / p.hw) * p.gsub + sub;
-    const int64_t T = p.tile_prefix[p.batch * per_seq];
+    const int u = (layer * p.batch + b) * per_seq + (h / p.hw) * p.gsub + sub;
+    const int64_t T = p.tile_prefix[p.n_layers * p.batch * per_seq];
     const int64_t nw = T < p.n_wg ? T : p.n_wg;
     const int64_t su = p.tile_prefix[u], su1 = p.tile_prefix[u + 1];
     int64_t w_lo = 0;
@@ -1238,7 +1279,7 @@ template <int G>
 int launch_decode(bool int2, const SplitParams& sp, const uint16_t* r_k, int batch, hipStream_t s) {
   if (int2) {
     // z = 0: rotated query and its MFMA operands, the tile prefix; z > 0: the bf16 window chunks
-    prep_kernel<G><<<dim3(batch, sp.hkv, 1 + sp.n_wchunks), 256, 0, s>>>(sp, r_k);
+    prep_kernel<G><<<dim3(batch * sp.n_layers, sp.hkv, 1 + sp.n_wchunks), 256, 0, s>>>(sp, r_k);
     if (hipGetLastError() != hipSuccess) return OSCAR_EHIP;
   }
   int slot = -1;
@@ -1258,9 +1299,10 @@ int launch_decode(bool int2, const SplitParams& sp, const uint16_t* r_k, int bat
   // heads per merge workgroup: the R_V tile is loaded once for all of them,
   // as long as about two workgroups per CU remain
   int mh = 1;
-  while (2 * mh <= kMergeHeads && 2 * mh <= G && (int64_t)batch * sp.hq / (2 * mh) >= 2 * (int64_t)device_cu_count())
+  const int64_t rows = (int64_t)batch * sp.n_layers;
+  while (2 * mh <= kMergeHeads && 2 * mh <= G && rows * sp.hq / (2 * mh) >= 2 * (int64_t)device_cu_count())
     mh *= 2;
-  merge_kernel<<<dim3(sp.hq / mh, batch), 256, 0, s>>>(sp, G, mh);
+  merge_kernel<<<dim3(sp.hq / mh, (unsigned)rows), 256, 0, s>>>(sp, G, mh);
   return hipGetLastError() == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
 }
 
@@ -1268,10 +1310,11 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
                   const uint16_t* q, int32_t batch, const int32_t* seq_lens, int32_t max_seq_len,
                   const int32_t* block_table, int32_t max_pages_per_seq, const uint8_t* pool,
                   const uint16_t* kv_pool, int64_t n_pages, const uint16_t* win_k, const uint16_t* win_v,
-                  float* out, void* workspace, size_t workspace_bytes, void* stream) {
+                  float* out, void* workspace, size_t workspace_bytes, void* stream, int n_layers = 1) {
   int st = check_shape(shape);
   if (st != OSCAR_OK) return st;
   if (batch < 1 || max_seq_len < 0 || max_pages_per_seq < 1 || n_pages < 1) return OSCAR_EINVAL;
+  if (n_layers < 1 || (!int2 && n_layers != 1) || (int64_t)n_layers * batch > 65535) return OSCAR_EINVAL;
   if (!q || !seq_lens || !block_table || !out || !workspace) return OSCAR_EINVAL;
   if (int2 && (!r_k || !r_v || !pool)) return OSCAR_EINVAL;
   if (int2 && shape->window + shape->n_sink > 0 && (!win_k || !win_v)) return OSCAR_EINVAL;
@@ -1281,8 +1324,7 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   const int n_cu = device_cu_count();
   const SplitPlan plan = plan_splits(batch, shape->n_kv_heads, gqa, max_seq_len, n_cu);
   const WorkspaceLayout wl = workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads, shape->window, shape->n_sink,
-                                              kD / shape->group_size,
-                                              plan, n_cu);
+                                              kD / shape->group_size, plan, n_cu, n_layers);
   if (workspace_bytes < wl.total) return OSCAR_ENOSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return OSCAR_EINVAL;
 
@@ -1324,6 +1366,19 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   sp.hw = split_heads_per_wg(shape->n_kv_heads);
   sp.block = block_bytes(shape->group_size);
   sp.ng = kD / shape->group_size;
+  // per-layer strides (layer-major stacking of every per-layer buffer)
+  sp.n_layers = n_layers;
+  sp.ls_q = (int64_t)batch * sp.hq * kD;
+  sp.ls_out = (int64_t)batch * sp.hq * kD;
+  sp.ls_rot = (int64_t)sp.hkv * kD * kD;
+  sp.ls_pool = n_pages * sp.hkv * sp.block;
+  sp.ls_win = (int64_t)batch * sp.ring * sp.hkv * kD;
+  sp.ls_qsum = (int64_t)(align256((size_t)batch * sp.hq * sp.ng * sizeof(float)) / sizeof(float));
+  sp.ls_qop = (int64_t)(align256((size_t)batch * sp.hkv * ((gqa + 3) / 4) * 64 * 9 * sizeof(int)) / sizeof(int));
+  {
+    const size_t nwp = (size_t)batch * sp.hq * sp.n_wchunks;
+    sp.ls_wpart = (int64_t)(align256((nwp > 0 ? nwp : 1) * kPartStride * sizeof(float)) / sizeof(float));
+  }
   sp.scale_log2 = kLog2e / sqrtf((float)kD);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (shape->n_q_heads / shape->n_kv_heads) {
@@ -1376,14 +1431,19 @@ __global__ __launch_bounds__(256) void bf16_append_kernel(const uint16_t* __rest
 }  // namespace oscar
 
 extern "C" size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int32_t max_seq_len) {
+  return oscar_decode_layers_workspace_bytes(shape, 1, batch, max_seq_len);
+}
+
+extern "C" size_t oscar_decode_layers_workspace_bytes(const oscar_shape* shape, int32_t n_layers, int32_t batch,
+                                                      int32_t max_seq_len) {
   using namespace oscar;
-  if (check_shape(shape) != OSCAR_OK || batch < 1 || max_seq_len < 0) return 0;
+  if (check_shape(shape) != OSCAR_OK || batch < 1 || max_seq_len < 0 || n_layers < 1) return 0;
   const int n_cu = device_cu_count();
   return workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads, shape->window, shape->n_sink,
                           kD / shape->group_size,
                           plan_splits(batch, shape->n_kv_heads, shape->n_q_heads / shape->n_kv_heads, max_seq_len,
                                       n_cu),
-                          n_cu)
+                          n_cu, n_layers)
       .total;
 }
 
@@ -1395,6 +1455,17 @@ extern "C" int oscar_decode_attn(const oscar_shape* shape, const uint16_t* r_k, 
   return oscar::decode_common(true, shape, r_k, r_v, q, batch, seq_lens, max_seq_len, block_table,
                               max_pages_per_seq, pool, nullptr, n_pages, win_k, win_v, out, workspace,
                               workspace_bytes, stream);
+}
+
+extern "C" int oscar_decode_attn_layers(const oscar_shape* shape, int32_t n_layers, const uint16_t* r_k,
+                                        const uint16_t* r_v, const uint16_t* q, int32_t batch,
+                                        const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
+                                        int32_t max_pages_per_seq, const uint8_t* pool, int64_t n_pages,
+                                        const uint16_t* win_k, const uint16_t* win_v, float* out, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return oscar::decode_common(true, shape, r_k, r_v, q, batch, seq_lens, max_seq_len, block_table,
+                              max_pages_per_seq, pool, nullptr, n_pages, win_k, win_v, out, workspace,
+                              workspace_bytes, stream, n_layers);
 }
 
 extern "C" int oscar_bf16_decode_attn(const oscar_shape* shape, const uint16_t* q, int32_t batch,
