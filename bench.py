@@ -76,6 +76,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the prefill-ingest (append) leg")
+    ap.add_argument("--no-layers-leg", action="store_true", help="skip the layer-batched decode leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="decode time the oracle baseline spends")
     ap.add_argument("--quality", action="store_true",
                     help="instead of the benchmark: cache quality of the OSCAR, Hadamard-only and identity "
@@ -120,9 +121,12 @@ def main():
     L = args.layers
     bt, n_pages = wl.page_table(s)
     btd, lensd = T(bt), T(lens.astype(np.int32))
-    pools = [torch.zeros((n_pages, HKV, K.block_bytes(G)), dtype=torch.uint8, device=dev) for _ in range(L)]
-    wks = [torch.zeros((B, W, HKV, 128), dtype=torch.int16, device=dev) for _ in range(L)]
-    wvs = [torch.zeros((B, W, HKV, 128), dtype=torch.int16, device=dev) for _ in range(L)]
+    # stacked layer-major (each layer a contiguous view), so the layer-batched
+    # decode can take all of them at once
+    pool_all = torch.zeros((L, n_pages, HKV, K.block_bytes(G)), dtype=torch.uint8, device=dev)
+    wk_all = torch.zeros((L, B, W, HKV, 128), dtype=torch.int16, device=dev)
+    wv_all = torch.zeros((L, B, W, HKV, 128), dtype=torch.int16, device=dev)
+    pools, wks, wvs = list(pool_all), list(wk_all), list(wv_all)
     kvp = [] if args.no_bf16 else [torch.zeros((n_pages, HKV, K.BF16_BLOCK_ELEMS), dtype=torch.int16, device=dev)
                                    for _ in range(L)]
     cur_k = np.empty((B, HKV, 128), np.uint16)
@@ -230,6 +234,44 @@ def main():
 
     res_append = None if args.no_append else append_leg(K, torch, dev, shape, rkd, rvd, args, tok_bytes)
 
+    # ---- layer batching: the L layers' decodes as L calls vs one call ----
+    res_layers = None
+    if not args.no_layers_leg and L > 1:
+        q_all = q.unsqueeze(0).expand(L, -1, -1, -1).contiguous()
+        rk_all = rkd.unsqueeze(0).expand(L, -1, -1, -1).contiguous()
+        rv_all = rvd.unsqueeze(0).expand(L, -1, -1, -1).contiguous()
+        out_all = torch.empty((L, B, HQ, 128), dtype=torch.float32, device=dev)
+        ws_all = torch.empty(K.oscar_decode_layers_workspace_bytes(shape, L, B, nmax), dtype=torch.uint8, device=dev)
+
+        def per_layer():
+            for l in range(L):
+                K.oscar_decode_attn(shape, rkd, rvd, q, lensd, nmax, btd, pools[l], wks[l], wvs[l], out_all[l], ws)
+
+        def batched():
+            K.oscar_decode_attn_layers(shape, rk_all, rv_all, q_all, lensd, nmax, btd, pool_all, wk_all, wv_all,
+                                       out_all, ws_all)
+
+        def time_it(fn, reps=10):
+            for _ in range(2):
+                fn()
+            busy = torch.empty(2, 512 << 20, dtype=torch.uint8, device=dev)
+            for _ in range(12):
+                K.oscar_hbm_copy(busy[0], busy[1])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            del busy
+            return e0.elapsed_time(e1) / reps
+        t_sep, t_one = time_it(per_layer), time_it(batched)
+        b_dec = b_hist + b_win + b_rot + b_q_out + b_bt
+        res_layers = {"n_layers": L, "per_layer_calls_ms": t_sep, "one_call_ms": t_one, "speedup": t_sep / t_one,
+                      "one_call_gbs": L * b_dec / (t_one / 1e3) / 1e9,
+                      "workload": f"decode of {L} layers' caches (B={B}, n={nmax}) without the append"}
+        log(f"{L} layers: {t_sep:.3f} ms as {L} calls, {t_one:.3f} ms as one call ({t_sep / t_one:.2f}x)")
+
     # the split kernel also attends the bf16 window and merges (last workgroup of each unit)
     b_split = b_hist + b_win + HKV * 128 * 128 * 2 + b_bt + b_q_out
     achieved = b_split / split_s / 1e9 if split_s else None
@@ -255,6 +297,7 @@ def main():
         "speedup_vs_bf16": (res_bf16["ms_per_step"] / (dt * 1e3)) if res_bf16 else None,
         "hbm_probe_copy_gbs": probe_gbs,
         "append": res_append,
+        "layers_batched": res_layers,
         "roofline": {
             "kernel": "int2_split_kernel",
             "bound": "hbm",
