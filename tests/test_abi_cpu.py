@@ -89,6 +89,31 @@ def test_host_validation_before_launch():
     assert lib.oscar_timing_end(None, None, 0, None) == EINVAL
 
 
+def test_layered_entry_points_validate_on_host():
+    lib = _lib.lib
+    good = K.make_shape(32, 8)
+    fake = C.c_void_p(256)
+    one = lib.oscar_decode_layers_workspace_bytes(C.byref(good), 1, 8, 100000)
+    assert one == lib.oscar_decode_workspace_bytes(C.byref(good), 8, 100000)
+    four = lib.oscar_decode_layers_workspace_bytes(C.byref(good), 4, 8, 100000)
+    assert four > one
+    assert lib.oscar_decode_layers_workspace_bytes(C.byref(good), 0, 8, 100000) == 0
+    for n_layers in (0, -1):
+        assert lib.oscar_decode_attn_layers(C.byref(good), n_layers, fake, fake, fake, 8, fake, 100, fake, 16, fake,
+                                            1, fake, fake, fake, fake, 1 << 30, None) == EINVAL
+        assert lib.oscar_quantize_append_layers(C.byref(good), n_layers, fake, fake, fake, fake, 1, fake, fake, 1,
+                                                fake, 1, fake, fake, 1, fake, fake, None) == EINVAL
+    # n_layers * batch beyond one grid dimension
+    assert lib.oscar_decode_attn_layers(C.byref(good), 4096, fake, fake, fake, 32, fake, 100, fake, 16, fake, 1,
+                                        fake, fake, fake, fake, 1 << 40, None) == EINVAL
+    # a workspace sized for fewer layers is refused
+    assert lib.oscar_decode_attn_layers(C.byref(good), 4, fake, fake, fake, 8, fake, 100000, fake,
+                                        100000 // 16 + 1, fake, 1, fake, fake, fake, fake, one, None) == ENOSPACE
+    # zero tokens is a no-op for any layer count
+    assert lib.oscar_quantize_append_layers(C.byref(good), 3, *([None] * 4), 0, None, None, 1, None, 1, None, None,
+                                            1, None, None, None) == 0
+
+
 def test_calibrate_rejects_bad_input():
     s = K.make_shape(32, 8)
     q = np.zeros((8, 4, 128), np.float32)
