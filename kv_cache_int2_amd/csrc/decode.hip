@@ -663,7 +663,11 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
 
   // ---- values: acc[rg][nn] += w terms x V codes (channels 8lr + nn) ----
   // with NG > 1 the column of lane lr (channels 8 lr .. 8 lr + 7) belongs to
-  // group lr / (16 / NG); the MFMA of group jg sees only its own columns' codes
+  // group lr / (16 / NG).  The MFMA of group jg scales the codes of the other
+  // groups' columns by 2^-127 (E8M0 0) instead of 2 (its B scale is per lane,
+  // i.e. per column): their products with group jg's weights land ~2^-128 below
+  // the true terms, under fp32 resolution of any accumulator they join, and no
+  // instruction is spent masking them.
   const int wsc = clamp_scale(kScaleOne + wexp - 7 - 4 * (lr & 3));
   const int my_grp = lr / (16 / NG);
   float corr[NRG];
@@ -672,6 +676,7 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
 #pragma unroll
   for (int jg = 0; jg < NG; ++jg) {
     const bool mine = NG == 1 || my_grp == jg;
+    const int sb = mine ? kScaleCode : 0;
     i32x8 wa[NRG];
 #pragma unroll
     for (int rg = 0; rg < NRG; ++rg) {
@@ -688,19 +693,18 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
       wa[rg][7] = (int)a1.w;
       corr[rg] = mine ? 1.5f * wsum[rg][jg] : corr[rg];
     }
-    // codes of the group's columns only (each (group, nn) operand built once, used by every row group)
 #pragma unroll
     for (int nn = 0; nn < 8; ++nn) {
       const uint32_t v0 = nn < 4 ? (&t.vlo[0].x)[nn] : (&t.vhi[0].x)[nn - 4];
       const uint32_t v1 = nn < 4 ? (&t.vlo[1].x)[nn] : (&t.vhi[1].x)[nn - 4];
       i32x8 bv;
-      bv[0] = mine ? (int)(v0 & 0x33333333u) : 0;
-      bv[1] = mine ? (int)((v0 >> 2) & 0x33333333u) : 0;
-      bv[2] = mine ? (int)(v1 & 0x33333333u) : 0;
-      bv[3] = mine ? (int)((v1 >> 2) & 0x33333333u) : 0;
+      bv[0] = (int)(v0 & 0x33333333u);
+      bv[1] = (int)((v0 >> 2) & 0x33333333u);
+      bv[2] = (int)(v1 & 0x33333333u);
+      bv[3] = (int)((v1 >> 2) & 0x33333333u);
       bv[4] = bv[5] = bv[6] = bv[7] = 0;
 #pragma unroll
-      for (int rg = 0; rg < NRG; ++rg) st.acc[rg][nn] = mfma_f8_f4(wa[rg], bv, st.acc[rg][nn], wsc, kScaleCode);
+      for (int rg = 0; rg < NRG; ++rg) st.acc[rg][nn] = mfma_f8_f4(wa[rg], bv, st.acc[rg][nn], wsc, sb);
     }
   }
 #pragma unroll
