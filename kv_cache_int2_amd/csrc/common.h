@@ -12,7 +12,6 @@ namespace oscar {
 
 constexpr int kD = 128;          // head dim
 constexpr int kPage = 16;        // tokens per page
-constexpr int kBlock = 1152;     // bytes per (page, KV head) block at group size 128
 // K codes, V codes, records: the record {Ks, Kz, Vs, Vz} fp16 of group j of
 // token t sits at kMeta + 8 (NG t + j), NG = 128 / group size
 constexpr int kKCodes = 0, kVCodes = 512, kMeta = 1024;

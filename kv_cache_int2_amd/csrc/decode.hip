@@ -6,13 +6,19 @@
 // (aiforradalom.hu) «OSCAR: figyelem-tudatos…» (bf16 recent tokens, INT2
 // history, paged attention).
 //
-// Kernels (one call = three launches on the caller's stream):
-//   prep_q        grid (B, Hkv):          q' = R_K q for the G heads of a KV head,
-//                                         its channel sums and fp8 score operands
-//   int2_split    grid (splits, Hkv, B):  online softmax over one history range,
-//                                         partial (m, l, acc'[128]) per q head
-//   merge         grid (B, Hkv):          log-sum-exp merge of the splits,
-//                                         R_V^T acc', bf16 window, normalise
+// Kernels (one call = three launches on the caller's stream; L layers of a
+// layer-batched call share them):
+//   prep          grid (L B, Hkv, 1 + chunks): z = 0: q' = R_K q for the G heads
+//                                         of a KV head, its group sums, the fp8
+//                                         score operands and the tile prefix;
+//                                         z > 0: one 32-token chunk of the bf16
+//                                         window or sinks, partial per q head
+//   int2_split    grid (2 per CU), persistent: equal shares of the flattened
+//                                         history tiles of every (layer, sequence,
+//                                         KV head group); partial (m, l, acc'[128])
+//                                         per wave, q head and unit touched
+//   merge         grid (Hq / mh, L B):    log-sum-exp merge of the partials,
+//                                         R_V^T acc', window / sink chunks, normalise
 // Scores are kept in the log2 domain: logit * log2(e) / sqrt(d).
 //
 // INT2 split kernel.  Both contractions of a 128-token tile (8 pages) run on the
