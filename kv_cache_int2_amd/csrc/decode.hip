@@ -148,6 +148,9 @@ struct SplitParams {
   // layers (units layer-major).
   int n_layers;
   int64_t ls_q, ls_out, ls_rot, ls_pool, ls_win, ls_qsum, ls_qop, ls_wpart;
+  // INT2: share weights of the split workgroups: wf for the first hf, ws for
+  // the rest (see share_begin)
+  int wf, ws, hf;
 };
 
 // The parameters of layer l: every per-layer buffer advanced by l strides.
@@ -165,6 +168,40 @@ __device__ __forceinline__ SplitParams layer_params(const SplitParams& p, int l)
     r.wpart += l * p.ls_wpart;
   }
   return r;
+}
+
+// Shares of the persistent split kernel.  Workgroup w takes the flattened tiles
+// [share_begin(w), share_begin(w + 1)).  The first hf workgroups weigh wf, the
+// others ws: workgroups w and w + hf share a CU, and the one dispatched first
+// has the older waves, which win the CU's issue arbitration, so it streams
+// faster and is given the larger share (with equal shares it finished ~15 us
+// before its partner at 100K context, every CU alike).
+struct ShareWeights {
+  int64_t wf, ws, hf, total;
+};
+// With fewer than 4 tiles per workgroup the shares are equal, so that every
+// workgroup keeps at least one tile (the weights satisfy wf <= 3 ws).
+__device__ __forceinline__ ShareWeights share_weights(const SplitParams& p, int64_t T, int nw) {
+  const bool weigh = T >= 4 * (int64_t)nw;
+  ShareWeights s;
+  s.wf = weigh ? p.wf : 1;
+  s.ws = weigh ? p.ws : 1;
+  s.hf = p.hf < nw ? p.hf : nw;
+  s.total = s.wf * s.hf + s.ws * (nw - s.hf);
+  return s;
+}
+__device__ __forceinline__ int64_t share_begin(const SplitParams& p, int64_t T, int nw, int w) {
+  const ShareWeights s = share_weights(p, T, nw);
+  const int64_t cum = w <= s.hf ? s.wf * w : s.wf * s.hf + s.ws * (w - s.hf);
+  return T * cum / s.total;
+}
+// The workgroup whose share holds tile t (0 <= t < T): the largest w with
+// share_begin(w) <= t, i.e. with cum(w) <= ((t + 1) total - 1) / T.
+__device__ __forceinline__ int64_t share_owner(const SplitParams& p, int64_t T, int nw, int64_t t) {
+  const ShareWeights s = share_weights(p, T, nw);
+  const int64_t c = ((t + 1) * s.total - 1) / T;
+  const int64_t w = c < s.wf * s.hf ? c / s.wf : s.hf + (c - s.wf * s.hf) / s.ws;
+  return w < nw - 1 ? w : nw - 1;
 }
 
 // Sequence length as the kernels see it: clamped to [0, max_len].
@@ -911,7 +948,7 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
 
   // ---- the workgroup's range: one wave partial per unit it touches, at (w + u, wave) ----
   if (w < nw) {
-    const int64_t lo = T * w / nw, hi = T * (w + 1) / nw;
+    const int64_t lo = share_begin(p, T, nw, w), hi = share_begin(p, T, nw, w + 1);
     const int ph = wave / p.hw, hv = wave % p.hw;
     int a, e;
     for (int u = find_unit(p.tile_prefix, units, lo); u < units && segment(u, lo, hi, a, e); ++u) {
@@ -1143,8 +1180,8 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p0, int gq, int 
     int64_t w_lo = 0;
     ns = 0;
     if (su1 > su) {  // workgroup of tile t: ((t + 1) nw - 1) / T
-      w_lo = ((su + 1) * nw - 1) / T;
-      ns = (int)((su1 * nw - 1) / T - w_lo + 1);
+      w_lo = share_owner(p, T, (int)nw, su);
+      ns = (int)(share_owner(p, T, (int)nw, su1 - 1) - w_lo + 1);
     }
     hw = p.hw;
     ts = 4 / hw;
@@ -1374,6 +1411,12 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   sp.gsub = gqa / sp.gw;
   sp.n_wg = int2 ? split_wg_count(gqa, n_cu) : 0;
   sp.hw = split_heads_per_wg(shape->n_kv_heads);
+  // the older workgroup of each CU takes 1.5 times the share of the younger:
+  // a sweep of 20:20 .. 26:14 at 100K context was fastest at 24:16 (split
+  // 93.8 us against 98.1 us with equal shares)
+  sp.wf = 24;
+  sp.ws = 16;
+  sp.hf = sp.n_wg / 2;
   sp.block = block_bytes(shape->group_size);
   sp.ng = kD / shape->group_size;
   // per-layer strides (layer-major stacking of every per-layer buffer)
