@@ -71,6 +71,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--window", type=int, default=None, help="bf16 recent-token window (default: the workload's)")
+    ap.add_argument("--sinks", type=int, default=0, help="leading positions also kept in bf16 (attention sinks)")
     ap.add_argument("--group", type=int, default=128, choices=(128, 64, 32),
                     help="rotated channels per INT2 scale/zero pair (128 = one group per token)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -97,11 +99,14 @@ def main():
         quality_leg(K, wl, torch)
         return
     s = wl.spec(args.config)
-    B, HQ, HKV, W = s.batch, s.n_q_heads, s.n_kv_heads, s.window
+    if args.window is not None:
+        s.window = args.window
+    s.n_sink = args.sinks
+    B, HQ, HKV, W, S = s.batch, s.n_q_heads, s.n_kv_heads, s.window, s.n_sink
     lens = s.seq_lens.astype(np.int64)
     nmax = int(lens.max())
     G = args.group
-    shape = K.make_shape(HQ, HKV, W, group_size=G)
+    shape = K.make_shape(HQ, HKV, W, group_size=G, n_sink=S)
     tok_bytes = 64 + 8 * (128 // G)  # INT2 bytes per token and KV head: codes + one record per group
 
     def T(a):
@@ -124,8 +129,8 @@ def main():
     # stacked layer-major (each layer a contiguous view), so the layer-batched
     # decode can take all of them at once
     pool_all = torch.zeros((L, n_pages, HKV, K.block_bytes(G)), dtype=torch.uint8, device=dev)
-    wk_all = torch.zeros((L, B, W, HKV, 128), dtype=torch.int16, device=dev)
-    wv_all = torch.zeros((L, B, W, HKV, 128), dtype=torch.int16, device=dev)
+    wk_all = torch.zeros((L, B, max(W + S, 1), HKV, 128), dtype=torch.int16, device=dev)
+    wv_all = torch.zeros((L, B, max(W + S, 1), HKV, 128), dtype=torch.int16, device=dev)
     pools, wks, wvs = list(pool_all), list(wk_all), list(wv_all)
     kvp = [] if args.no_bf16 else [torch.zeros((n_pages, HKV, K.BF16_BLOCK_ELEMS), dtype=torch.int16, device=dev)
                                    for _ in range(L)]
@@ -205,10 +210,11 @@ def main():
     log(f"HBM copy probe: {probe_gbs:.0f} GB/s (read + write)")
 
     # ---- algorithmic bytes ----
-    hist = np.maximum(lens - W, 0)
     win = np.minimum(lens, W)
+    sink = np.minimum(S, lens - win)           # bf16 sink positions read by the decode
+    hist = lens - win - sink                   # INT2 history positions
     b_hist = float(hist.sum() * HKV * tok_bytes)
-    b_win = float(win.sum() * HKV * 512)
+    b_win = float((win + sink).sum() * HKV * 512)
     b_rot = 2 * HKV * 128 * 128 * 2
     b_q_out = B * HQ * 128 * (2 + 4)
     b_bt = float(sum(-(-int(n) // 16) for n in lens) * 4)
@@ -290,7 +296,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded Gaussian K/V, 4 key outlier channels x20; no dataset exists for this path)",
         "config": {"workload": f"long-context decode step: append 1 token/seq + INT2 decode, B={B}, n={nmax}, "
-                               f"{HQ}q/{HKV}kv heads, d=128, group {G}, 16-token scattered pages, bf16 window {W}",
+                               f"{HQ}q/{HKV}kv heads, d=128, group {G}, 16-token scattered pages, bf16 window {W}"
+                               + (f" + {S} sink tokens" if S else ""),
                    "layers_rotated": L, "pct_of_hbm_peak": 100 * step_bytes_int2 / dt / 1e9 / PEAK_HBM_GBS,
                    "decode_tokens_per_s": B / dt, "step_bytes": step_bytes_int2},
         "bf16_kv": res_bf16,
@@ -311,7 +318,7 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and G == 128 and S == 0:  # the oracle sample covers the default cache form
         line["cpu_baseline"] = cpu_baseline(s, rk, rv, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
