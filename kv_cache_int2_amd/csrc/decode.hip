@@ -763,16 +763,15 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
 // INT2 history attention on the matrix cores, persistent.
 // The history tiles (128 tokens) of every merge unit (sequence, group of hw
 // adjacent KV heads, head subset) form one flattened sequence, unit after
-// unit.  Workgroup w of the nw resident workgroups takes tiles
-// [w T / nw, (w + 1) T / nw): every workgroup the same amount of work, whatever
-// the lengths.  Each wave works alone (no barrier in the kernel): wave v takes
-// KV head hw g + v % hw of group g and, of the range's tiles of a unit, those
-// congruent to v / hw modulo 4 / hw, and writes one partial per unit its range
-// touches, at (slot w + u, v) - unique, as consecutive ranges share at most one
-// unit.  At 100K context the workgroups' finish times spread over ~25 % of the
-// kernel (CUs stream at different rates); handing steps out dynamically through
-// device-scope atomics (a shared chunk counter, or per-wave claim words with
-// stealing) measured slower than this static split on this part.
+// unit.  Workgroup w of the nw resident workgroups takes the tiles
+// [share_begin(w), share_begin(w + 1)): a fixed share whatever the lengths,
+// larger for the older of the two workgroups of a CU.  Each wave works alone
+// (no barrier in the kernel): wave v takes KV head hw g + v % hw of group g and,
+// of the range's tiles of a unit, those congruent to v / hw modulo 4 / hw, and
+// writes one partial per unit its range touches, at (slot w + u, v) - unique,
+// as consecutive ranges share at most one unit.  Handing steps out dynamically
+// through device-scope atomics (a shared chunk counter, or per-wave claim words
+// with stealing) measured slower than these static shares on this part.
 // Lane l = 16 lg + lr:
 //   score MFMA output: head 4 rg + lg, token lr of the page;
 //   value accumulators: head 4 rg + lg, channels 8 lr + n (n = 0..7);
