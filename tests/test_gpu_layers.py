@@ -35,6 +35,8 @@ def stack(arrs):
     (5, [600, 129, 128], 128, 64, 0, 128),
     (1, [1500, 200], 256, 32, 64, 64),
     (1, [0, 700, 5], 128, 32, 0, 32),
+    (1, [900, 260], 0, 128, 40, 64),      # G = 16, no window but sinks, groups of 64
+    (1, [1300], 64, 16, 0, 128),          # G = 2, a window of two chunks
 ])
 def test_layers_append_and_decode(K, cfg, lens, window, hq, n_sink, group):
     n_layers = 3
