@@ -288,6 +288,10 @@ int oscar_bf16_decode_attn(const oscar_shape* shape, const uint16_t* q, int32_t 
  * oscar_hbm_copy: plain streaming copy of `bytes` (multiple of 16, both pointers
  *   16-byte aligned) from src to dst on the device; used to calibrate HBM
  *   counters and as an in-session bandwidth probe.
+ * oscar_gpu_wait: enqueues a one-wave kernel that returns after `microseconds`
+ *   (0 .. 10^7) of the device's wall clock and touches no memory; it holds the
+ *   stream while the host enqueues the launches to be timed behind it, without
+ *   leaving dirty cache lines the way a copy would.
  * oscar_timing_begin(capacity): from now on every append / decode call also
  *   records a pair of HIP events on its stream around its main kernel, up to
  *   `capacity` pairs.  oscar_timing_end copies the elapsed milliseconds and the
@@ -297,6 +301,7 @@ int oscar_bf16_decode_attn(const oscar_shape* shape, const uint16_t* q, int32_t 
  *   Not thread-safe; meant for one benchmarking thread.
  */
 int oscar_hbm_copy(const void* src, void* dst, size_t bytes, void* stream);
+int oscar_gpu_wait(int64_t microseconds, void* stream);
 int oscar_timing_begin(int32_t capacity);
 int oscar_timing_end(float* ms, int32_t* kinds, int32_t capacity, int32_t* n);
 

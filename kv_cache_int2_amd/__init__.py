@@ -19,7 +19,7 @@ from ._lib import OscarShape, lib
 __all__ = [
     "OscarError", "OscarShape", "make_shape", "oscar_calibrate", "oscar_quantize_append",
     "oscar_decode_workspace_bytes", "oscar_decode_attn", "oscar_bf16_append",
-    "oscar_bf16_decode_attn", "oscar_hbm_copy", "oscar_timing_begin", "oscar_timing_end",
+    "oscar_bf16_decode_attn", "oscar_hbm_copy", "oscar_gpu_wait", "oscar_timing_begin", "oscar_timing_end",
     "oscar_strerror", "BLOCK_BYTES", "BF16_BLOCK_ELEMS", "PAGE_SIZE", "HEAD_DIM", "block_bytes",
     "oscar_calibrate_layers", "oscar_rotation_file_bytes", "oscar_rotation_write", "oscar_rotation_read_info",
     "oscar_rotation_read", "oscar_quantize_append_layers", "oscar_decode_layers_workspace_bytes",
@@ -281,6 +281,11 @@ def oscar_hbm_copy(src, dst, nbytes: int | None = None, stream=None) -> None:
     if src.device.type != "cuda" or dst.device.type != "cuda":
         raise ValueError("oscar_hbm_copy: tensors must be on the GPU")
     _check("oscar_hbm_copy", lib.oscar_hbm_copy(src.data_ptr(), dst.data_ptr(), n, _stream(stream)))
+
+
+def oscar_gpu_wait(microseconds: int, stream=None) -> None:
+    """Hold the stream for `microseconds` of device time without touching memory."""
+    _check("oscar_gpu_wait", lib.oscar_gpu_wait(int(microseconds), _stream(stream)))
 
 
 def oscar_timing_begin(capacity: int) -> None:

@@ -41,6 +41,7 @@ SIGNATURES = {
     "oscar_bf16_append": (C.c_int, [SHAPE, P, P, I64, P, P, I32, P, I32, P, I64, P]),
     "oscar_bf16_decode_attn": (C.c_int, [SHAPE, P, I32, P, I32, P, I32, P, I64, P, P, SZ, P]),
     "oscar_hbm_copy": (C.c_int, [P, P, SZ, P]),
+    "oscar_gpu_wait": (C.c_int, [I64, P]),
     "oscar_timing_begin": (C.c_int, [I32]),
     "oscar_timing_end": (C.c_int, [P, P, I32, C.POINTER(I32)]),
     "oscar_strerror": (C.c_char_p, [C.c_int]),

@@ -1,7 +1,8 @@
 // Measurement helpers, the device's compute-unit count and status strings: a
 // streaming copy kernel (HBM probe and the known-size reference for HBM traffic
-// counters) and opt-in event-pair recording around the main kernel of each
-// append / decode call.
+// counters), a timed wait kernel that holds a stream without touching memory,
+// and opt-in event-pair recording around the main kernel of each append /
+// decode call.
 #include <vector>
 
 #include "common.h"
@@ -21,6 +22,17 @@ Timing g_timing;
 __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
+// One wave that returns once `ticks` of the constant-rate wall clock have
+// passed, sleeping between reads; at most `max_iter` sleeps, so it also ends
+// should the clock not advance.
+__global__ __launch_bounds__(64) void wait_kernel(uint64_t ticks, int64_t max_iter) {
+  const uint64_t t0 = wall_clock64();
+  for (int64_t i = 0; i < max_iter; ++i) {
+    if (wall_clock64() - t0 >= ticks) break;
+    __builtin_amdgcn_s_sleep(32);
+  }
 }
 
 }  // namespace
@@ -105,6 +117,18 @@ extern "C" int oscar_hbm_copy(const void* src, void* dst, size_t bytes, void* st
   if (blocks > 256 * 64) blocks = 256 * 64;
   oscar::copy_kernel<<<(unsigned)blocks, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
       static_cast<const uint4*>(src), static_cast<uint4*>(dst), n);
+  return hipGetLastError() == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
+}
+
+extern "C" int oscar_gpu_wait(int64_t microseconds, void* stream) {
+  if (microseconds < 0 || microseconds > 10000000) return OSCAR_EINVAL;
+  if (microseconds == 0) return OSCAR_OK;
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return OSCAR_EHIP;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz < 1) return OSCAR_EHIP;
+  const uint64_t ticks = (uint64_t)microseconds * (uint64_t)khz / 1000u;
+  // a sleep of 32 x 64 clocks lasts >= 0.5 us below 4 GHz: 64 sleeps per us are ample
+  oscar::wait_kernel<<<1, 64, 0, reinterpret_cast<hipStream_t>(stream)>>>(ticks, 64 * microseconds + 64);
   return hipGetLastError() == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
 }
 

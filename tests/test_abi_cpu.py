@@ -86,6 +86,9 @@ def test_host_validation_before_launch():
     for g in (32, 64):
         assert lib.oscar_decode_workspace_bytes(C.byref(K.make_shape(32, 8, group_size=g)), 8, 100000) > 0
     assert lib.oscar_hbm_copy(fake, fake, 17, None) == EINVAL
+    assert lib.oscar_gpu_wait(-1, None) == EINVAL
+    assert lib.oscar_gpu_wait(10000001, None) == EINVAL
+    assert lib.oscar_gpu_wait(0, None) == 0
     assert lib.oscar_timing_end(None, None, 0, None) == EINVAL
 
 

@@ -315,6 +315,17 @@ def test_bf16_comparator_small(K):
     assert P.attn_rel_err(H(out), want).max() <= P.ATTN_TOL
 
 
+def test_gpu_wait_holds_the_stream(K):
+    """The measurement helper that holds a stream: the event pair around a 2 ms
+    wait spans at least most of it, and the stream drains."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    K.oscar_gpu_wait(2000)
+    e1.record()
+    torch.cuda.synchronize()
+    assert 1.5 <= e0.elapsed_time(e1) <= 200.0
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads (sampled checks)
 # ---------------------------------------------------------------------------
