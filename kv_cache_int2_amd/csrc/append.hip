@@ -100,8 +100,7 @@ __device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, LANE * 0x55, 0xf, 0xf, true);
 }
 
-// Resolve token `tok`: returns its block base (or nullptr if it must be skipped)
-// and slot; also whether it enters the bf16 window and its window slot.
+// Destination of one token (see resolve).
 struct TokInfo {
   uint8_t* blk;
   int slot;
@@ -111,25 +110,52 @@ struct TokInfo {
   bool in_sink;  // sink: ring row window + pos
 };
 
-__device__ __forceinline__ TokInfo resolve(const AppendParams& p, int64_t tok, int h) {
+// Indices of the tokens of one wave's 16-token tile(s) (token t0 + 16 j + r):
+// raw sequence and position (-1 past the last token), then block-table entry
+// and sequence length.  The first tile's are loaded while the rotation is
+// staged, so their chain of dependent loads is off the critical path.
+struct TileIdx {
+  int b[kAppendTiles], ps[kAppendTiles];
+  int2 pl[kAppendTiles];  // lookup(b, ps)
+};
+
+__device__ __forceinline__ void load_idx(const AppendParams& p, int64_t t0, int lane, TileIdx& in) {
+  const int r = lane & 15;
+#pragma unroll
+  for (int j = 0; j < kAppendTiles; ++j) {
+    const int64_t tok = t0 + 16 * j + r;
+    const bool valid = tok < p.n_tokens;
+    in.b[j] = valid ? p.seq_idx[tok] : -1;
+    in.ps[j] = valid ? p.pos[tok] : -1;
+  }
+}
+
+// Block-table entry and length of a token's sequence (-1 when the token is
+// skipped); loaded ahead, so only plain integers stay live until the token is
+// written.
+__device__ __forceinline__ int2 lookup(const AppendParams& p, int b, int ps) {
+  if (b < 0 || b >= p.batch || ps < 0 || (ps >> 4) >= p.max_pages) return make_int2(-1, 0);
+  return make_int2(p.block_table[(int64_t)b * p.max_pages + (ps >> 4)], p.len_after[b]);
+}
+
+// Where a token goes: its block base (nullptr if it must be skipped) and slot;
+// also whether it enters the bf16 window and its window slot.
+__device__ __forceinline__ TokInfo resolve(const AppendParams& p, int b, int ps, int2 pl, int h) {
   TokInfo ti{nullptr, 0, 0, 0, false, false};
-  if (tok >= p.n_tokens) return ti;
-  int b = p.seq_idx[tok], ps = p.pos[tok];
-  if (b < 0 || b >= p.batch || ps < 0 || (ps >> 4) >= p.max_pages) return ti;
-  int page = p.block_table[(int64_t)b * p.max_pages + (ps >> 4)];
+  const int page = pl.x;
   if (page < 0 || page >= p.n_pages) return ti;
   ti.blk = p.pool + ((int64_t)page * p.hkv + h) * p.block;
   ti.slot = ps & 15;
   ti.b = b;
   ti.pos = ps;
-  ti.in_win = p.window > 0 && ps >= p.len_after[b] - p.window;
+  ti.in_win = p.window > 0 && ps >= pl.y - p.window;
   ti.in_sink = ps < p.n_sink;
   return ti;
 }
 
 template <int KIND, int NG>
-__device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4* r_lds, int64_t t0, int h,
-                                              int lane) {
+__device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4* r_lds, const TileIdx& in,
+                                              int64_t t0, int h, int lane) {
   constexpr int NT = kAppendTiles;
   constexpr int MPG = 8 / NG;  // accumulators m per group
   const int g = lane >> 4, r = lane & 15;
@@ -162,7 +188,7 @@ __device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4
   for (int j = 0; j < NT; ++j) {
     const int64_t tj = t0 + 16 * j;
     if (tj >= p.n_tokens) break;  // uniform: the wave's tokens are contiguous
-    TokInfo ti = resolve(p, tj + r, h);
+    const TokInfo ti = resolve(p, in.b[j], in.ps[j], in.pl[j], h);
 
     // raw bf16 copies into the ring (same for K and V): recent tokens, sinks
     if (ti.blk && ti.in_win) {
@@ -316,17 +342,40 @@ __global__ __launch_bounds__(256, 4) void append_kernel(AppendParams p) {
     }
     p.pool += layer * p.ls_pool;
   }
-  const uint4* rg = reinterpret_cast<const uint4*>((kind ? p.r[1] : p.r[0]) + (int64_t)h * kD * kD);
-  for (int i = threadIdx.x; i < 128 * 16; i += 256) r_lds[(i >> 4) * kRowU4 + (i & 15)] = rg[i];
-  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  auto tile0 = [&](int it) {
+    return ((int64_t)blockIdx.x * p.tiles_per_wg + it) * kAppendTokens + wave * 16 * kAppendTiles;
+  };
+  // the first tile's token indices go out before the rotation is staged
+  TileIdx in;
+  const bool any = tile0(0) < p.n_tokens;  // uniform across the wave
+  if (any) load_idx(p, tile0(0), lane, in);
+  const uint4* rg = reinterpret_cast<const uint4*>((kind ? p.r[1] : p.r[0]) + (int64_t)h * kD * kD);
+  uint4 rr[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) rr[k] = rg[threadIdx.x + 256 * k];
+  if (any) {
+#pragma unroll
+    for (int j = 0; j < kAppendTiles; ++j) in.pl[j] = lookup(p, in.b[j], in.ps[j]);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    r_lds[(i >> 4) * kRowU4 + (i & 15)] = rr[k];
+  }
+  __syncthreads();
   for (int it = 0; it < p.tiles_per_wg; ++it) {
-    const int64_t t0 = ((int64_t)blockIdx.x * p.tiles_per_wg + it) * kAppendTokens + wave * 16 * kAppendTiles;
+    const int64_t t0 = tile0(it);
     if (t0 >= p.n_tokens) break;
+    if (it > 0) {
+      load_idx(p, t0, lane, in);
+#pragma unroll
+      for (int j = 0; j < kAppendTiles; ++j) in.pl[j] = lookup(p, in.b[j], in.ps[j]);
+    }
     if (kind == 0)
-      process_tiles<0, NG>(p, r_lds, t0, h, lane);
+      process_tiles<0, NG>(p, r_lds, in, t0, h, lane);
     else
-      process_tiles<1, NG>(p, r_lds, t0, h, lane);
+      process_tiles<1, NG>(p, r_lds, in, t0, h, lane);
   }
 }
 
