@@ -364,14 +364,19 @@ __global__ __launch_bounds__(256, 4) void append_kernel(AppendParams p) {
     r_lds[(i >> 4) * kRowU4 + (i & 15)] = rr[k];
   }
   __syncthreads();
+  TileIdx nxt;  // raw indices of the next tile, loaded while this one is processed
   for (int it = 0; it < p.tiles_per_wg; ++it) {
     const int64_t t0 = tile0(it);
     if (t0 >= p.n_tokens) break;
     if (it > 0) {
-      load_idx(p, t0, lane, in);
 #pragma unroll
-      for (int j = 0; j < kAppendTiles; ++j) in.pl[j] = lookup(p, in.b[j], in.ps[j]);
+      for (int j = 0; j < kAppendTiles; ++j) {
+        in.b[j] = nxt.b[j];
+        in.ps[j] = nxt.ps[j];
+        in.pl[j] = lookup(p, in.b[j], in.ps[j]);
+      }
     }
+    if (it + 1 < p.tiles_per_wg && tile0(it + 1) < p.n_tokens) load_idx(p, tile0(it + 1), lane, nxt);
     if (kind == 0)
       process_tiles<0, NG>(p, r_lds, in, t0, h, lane);
     else
