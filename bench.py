@@ -480,6 +480,24 @@ def summarize_trace(directory: str, command: str) -> str:
             continue
         out.append(f"  {k:44s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                    f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}")
+    # the INT2 decode step kernel by kernel: append, prep, split, merge in
+    # launch order, and the idle gap before each (medians over the steps)
+    trace = sorted(_csv_rows(directory, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    names = ["append_kernel", "prep_kernel", "int2_split_kernel", "merge_kernel"]
+    dur, gap = {n: [] for n in names}, {n: [] for n in names}
+    for i in range(3, len(trace)):
+        seq = trace[i - 3:i + 1]
+        if all(_short_kernel(r["Kernel_Name"]).startswith(n) for r, n in zip(seq, names)):
+            for j, (r, n) in enumerate(zip(seq, names)):
+                dur[n].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+                if j:
+                    gap[n].append((int(r["Start_Timestamp"]) - int(seq[j - 1]["End_Timestamp"])) / 1e3)
+    if dur["int2_split_kernel"]:
+        out += ["#", f"# INT2 decode step, kernel by kernel ({len(dur['int2_split_kernel'])} steps; the tracer "
+                "itself lengthens the gaps)", f"# {'kernel':44s} {'median_us':>10s} {'gap_before_us':>14s}"]
+        for n in names:
+            g = f"{np.median(gap[n]):14.2f}" if gap[n] else f"{'-':>14s}"
+            out.append(f"  {n:44s} {np.median(dur[n]):10.2f} {g}")
     return "\n".join(out) + "\n"
 
 
@@ -494,8 +512,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, command: str) -> str:
                 continue
             acc.setdefault(_short_kernel(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
         out = {k: float(np.mean(v)) for k, v in acc.items()}
-        # the copy kernel also runs the smaller queue-filling copies of the timed
-        # passes: the probe's dispatches are the largest ones
+        # only the probe's dispatches (the largest copies) calibrate the scale
         cp = np.asarray(acc["copy_kernel"])
         out["copy_kernel"] = float(np.mean(cp[cp > 0.5 * cp.max()]))
         return out
