@@ -221,7 +221,9 @@ size_t oscar_decode_workspace_bytes(const oscar_shape* shape, int32_t batch, int
  *     a sequence of length 0 has no position to attend and gets out = 0
  *   block_table, pool, win_k, win_v as for oscar_quantize_append
  *   out float [batch][n_q_heads][128]
- *   workspace >= oscar_decode_workspace_bytes(shape, batch, max_seq_len) bytes
+ *   workspace >= oscar_decode_workspace_bytes(shape, batch, max_seq_len) bytes,
+ *     256-byte aligned; r_k, r_v, q, pool, win_k, win_v 16-byte aligned
+ *     (OSCAR_EINVAL otherwise)
  * Errors: OSCAR_EINVAL, OSCAR_EUNSUPPORTED, OSCAR_ENOSPACE, OSCAR_EHIP.
  */
 int oscar_decode_attn(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
@@ -272,7 +274,8 @@ int oscar_decode_attn_layers(const oscar_shape* shape, int32_t n_layers, const u
  * channel c at element 2048 + 16 c + j), same block table semantics.
  * oscar_bf16_append scatters k_new/v_new [n_tokens][n_kv_heads][128] into it;
  * oscar_bf16_decode_attn is plain softmax attention over all seq_lens[b]
- * positions, fp32 output [batch][n_q_heads][128], same workspace rule.
+ * positions, fp32 output [batch][n_q_heads][128], same workspace and alignment
+ * rules (q and kv_pool 16-byte aligned).
  */
 int oscar_bf16_append(const oscar_shape* shape, const uint16_t* k_new, const uint16_t* v_new,
                       int64_t n_tokens, const int32_t* seq_idx, const int32_t* pos, int32_t batch,

@@ -319,8 +319,8 @@ __device__ void window_chunk(const SplitParams& p, int b, int h, int c, int G, f
 
 // ---------------------------------------------------------------------------
 // Query preparation, once per (sequence, KV head):
-//   q' = R_K[h] q for its G query heads (thread pair (c, half): 64 inputs of
-//   output channel c from 8 x 16-byte loads of R's row);
+//   q' = R_K[h] q for its G <= 16 query heads on the matrix cores (bf16 in,
+//   fp32 out; each wave 32 output channels);
 //   qsum[head][j] = sum of q'_c over the channels c of quantisation group j;
 //   the fp8 score operand of every 4-head group: lane (lg, lr) holds term lr%4 of
 //   q'_(head lr/4) at the 32 channels its k-slots map to, plus the row's E8M0
@@ -330,6 +330,7 @@ __device__ void window_chunk(const SplitParams& p, int b, int h, int c, int G, f
 template <int G>
 __global__ __launch_bounds__(256) void prep_kernel(SplitParams p0, const uint16_t* __restrict__ r_k0) {
   constexpr int NCB = (G + 3) / 4;  // 4-head operand groups
+  static_assert(G <= 16, "the heads are the 16 columns of one MFMA");
   constexpr int kQBytes = 2 * G * kD * 4 + G * 4;
   constexpr int kSmem = kQBytes > window_smem_bytes<G>() ? kQBytes : window_smem_bytes<G>();
   __shared__ __align__(16) float smem_f[kSmem / 4];
@@ -367,33 +368,38 @@ __global__ __launch_bounds__(256) void prep_kernel(SplitParams p0, const uint16_
       p.tile_prefix[u0 + (int64_t)p.batch * per_seq] = (int)(t0 + (int64_t)per_seq * pt);
   }
   float (*qs)[kD] = reinterpret_cast<float (*)[kD]>(smem_f);
-  float (*qraw)[kD] = reinterpret_cast<float (*)[kD]>(smem_f + G * kD);
   int* qexp = reinterpret_cast<int*>(smem_f + 2 * G * kD);
-  const uint16_t* q = p.q;
   float* qsum_out = const_cast<float*>(p.qsum);
   int* qop = const_cast<int*>(p.qop);
   {
-    const int c = tid >> 1, half = tid & 1;
-    const uint4* rrow = reinterpret_cast<const uint4*>(r_k + ((int64_t)h * kD + c) * kD + 64 * half);
-    uint4 rv[8];
+    // q' = R_K q on the matrix cores (v_mfma_f32_16x16x32_bf16, exact bf16
+    // products, fp32 sums): wave v computes output channels 32 v .. 32 v + 31
+    // as two 16-row blocks; A = rows of R_K, B = q^T with the G heads as
+    // columns (zero past G).  Lane (g, r) supplies A row r and B column r at
+    // k = 8 g .. 8 g + 7 of each 32-wide k step and ends with channels
+    // 16 cb + 4 g + i of head r.
+    const int g = (tid & 63) >> 4, r = tid & 15, wv = tid >> 6;
+    const uint4* qrow = reinterpret_cast<const uint4*>(p.q + ((int64_t)b * hq + h * G + (r < G ? r : 0)) * kD);
+    uint4 bq[4], ra[2][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rv[i] = rrow[i];
-    for (int e = tid; e < G * kD; e += 256) qraw[e / kD][e % kD] = bf16_to_f32(q[((int64_t)b * hq + h * G) * kD + e]);
-    __syncthreads();
-#pragma unroll 1
-    for (int j = 0; j < G; ++j) {
-      float acc = 0.f;
+    for (int ks = 0; ks < 4; ++ks) bq[ks] = r < G ? qrow[4 * ks + g] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t w[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
+    for (int blk = 0; blk < 2; ++blk) {
+      const uint4* rrow = reinterpret_cast<const uint4*>(r_k + ((int64_t)h * kD + 16 * (2 * wv + blk) + r) * kD);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float2 qv = *reinterpret_cast<const float2*>(&qraw[j][64 * half + 8 * i + 2 * u]);
-          acc = fmaf(bf16lo(w[u]), qv.x, fmaf(bf16hi(w[u]), qv.y, acc));
-        }
+      for (int ks = 0; ks < 4; ++ks) ra[blk][ks] = rrow[4 * ks + g];
+    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra[blk][ks]),
+                                                      __builtin_bit_cast(bf16x8, bq[ks]), acc, 0, 0, 0);
+      if (r < G) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qs[r][16 * (2 * wv + blk) + 4 * g + i] = acc[i];
       }
-      acc += __shfl_xor(acc, 1);
-      if (half == 0) qs[j][c] = acc;
     }
   }
   __syncthreads();
@@ -1373,6 +1379,11 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
                                               kD / shape->group_size, plan, n_cu, n_layers);
   if (workspace_bytes < wl.total) return OSCAR_ENOSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return OSCAR_EINVAL;
+  // rows are read as 16-byte vectors
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(r_k) | reinterpret_cast<uintptr_t>(r_v) |
+       reinterpret_cast<uintptr_t>(pool) | reinterpret_cast<uintptr_t>(kv_pool) |
+       reinterpret_cast<uintptr_t>(win_k) | reinterpret_cast<uintptr_t>(win_v)) & 15)
+    return OSCAR_EINVAL;
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   SplitParams sp{};

@@ -73,6 +73,12 @@ def test_host_validation_before_launch():
     assert lib.oscar_decode_attn(*args, ws - 1, None) == ENOSPACE
     args[8] = 100
     assert lib.oscar_decode_attn(*args, ws, None) == ENOSPACE
+    # rows are read as 16-byte vectors: a misaligned query or rotation is refused
+    args[8] = 100000 // 16 + 1
+    for i in (1, 3):  # r_k, q
+        bad = list(args)
+        bad[i] = C.c_void_p(258)
+        assert lib.oscar_decode_attn(*bad, ws, None) == EINVAL
     assert lib.oscar_decode_attn(C.byref(good), None, None, None, 8, None, 10, None, 1, None, 1, None, None,
                                  None, None, 0, None) == EINVAL
     # sinks without a window still need the ring
