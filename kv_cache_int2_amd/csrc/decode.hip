@@ -1166,6 +1166,33 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p0, int gq, int 
   const bool active = wave < mh;
   const int hq = blockIdx.x * mh + (active ? wave : 0), h = hq / gq;
   const bool int2 = p.r_v != nullptr;
+  __shared__ float a1s[kMergeHeads][kD];
+  __shared__ float o1p[kMergeHeads][16][kD + 4];
+
+  // The loads that depend on nothing else go out first, so that they are in
+  // flight while the partials' places are looked up.
+  // R_V tile (INT2): thread (cg, jg) takes channels 8cg..8cg+7 of rows 8jg..8jg+7
+  const int cg = tid & 15, jg = tid >> 4;
+  uint4 rv[8];
+  if (int2) {
+    const uint16_t* r = p.r_v + ((int64_t)h * kD + 8 * jg) * kD + 8 * cg;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rv[j] = *reinterpret_cast<const uint4*>(r + j * kD);
+  }
+  // window / sink chunk partials (INT2): channels lane and lane + 64 of the first kMergeWin chunks
+  const float* wp = p.wpart + ((int64_t)b * p.hq + hq) * p.n_wchunks * kPartStride;
+  const int nwc = int2 && active ? p.n_wchunks : 0;
+  // (m, l) are loaded per lane (lane & 1) and read out only where they are
+  // used: as uniform values they would be scalar loads waited for at once
+  float wv0[kMergeWin], wv1[kMergeWin], wml[kMergeWin];
+#pragma unroll
+  for (int cc = 0; cc < kMergeWin; ++cc) {
+    const float* wc = wp + (cc < nwc ? cc : 0) * kPartStride;  // in the workspace even when unused
+    wv0[cc] = wc[2 + lane];
+    wv1[cc] = wc[2 + 64 + lane];
+    wml[cc] = wc[lane & 1];
+  }
+
   // partials of this wave's head: INT2 - the wave partials (w + u, v) of the ts
   // waves v of this head in each workgroup w whose tile range touches unit u,
   // at p.part + ((4 (w + u) + v) gw + g) 130 (partial s: workgroup w_lo + s / ts,
@@ -1205,32 +1232,6 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p0, int gq, int 
   auto part_at = [&](int s) {
     return base + (int64_t)(int2 ? 4 * (w0 + (s >> tsh)) + hw * (s & (ts - 1)) : s) * stride;
   };
-
-  __shared__ float a1s[kMergeHeads][kD];
-  __shared__ float o1p[kMergeHeads][16][kD + 4];
-
-  // R_V tile (INT2): thread (cg, jg) takes channels 8cg..8cg+7 of rows 8jg..8jg+7
-  const int cg = tid & 15, jg = tid >> 4;
-  uint4 rv[8];
-  if (int2) {
-    const uint16_t* r = p.r_v + ((int64_t)h * kD + 8 * jg) * kD + 8 * cg;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) rv[j] = *reinterpret_cast<const uint4*>(r + j * kD);
-  }
-  // window / sink chunk partials (INT2): channels lane and lane + 64 of the first kMergeWin chunks
-  const float* wp = p.wpart + ((int64_t)b * p.hq + hq) * p.n_wchunks * kPartStride;
-  const int nwc = int2 && active ? p.n_wchunks : 0;
-  float wv0[kMergeWin], wv1[kMergeWin], wm[kMergeWin], wl[kMergeWin];
-#pragma unroll
-  for (int cc = 0; cc < kMergeWin; ++cc) {
-    const bool ok = cc < nwc;
-    const float* wc = wp + (ok ? cc : 0) * kPartStride;  // in the workspace even when unused
-    const float v0 = wc[2 + lane], v1 = wc[2 + 64 + lane], m = wc[0], l = wc[1];
-    wv0[cc] = ok ? v0 : 0.f;
-    wv1[cc] = ok ? v1 : 0.f;
-    wm[cc] = ok ? m : kNegInf;
-    wl[cc] = ok ? l : 0.f;
-  }
 
   // the head's partials: lane s of a pass holds partial s0 + s's (m, l)
   float M = kNegInf, acc0 = 0.f, acc1 = 0.f, lsum = 0.f;  // M, lsum: the same on every lane
@@ -1301,6 +1302,15 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p0, int gq, int 
   for (int k = 0; k < 16; ++k) {
     o1[0] += o1p[wave][k][lane];
     o1[1] += o1p[wave][k][lane + 64];
+  }
+  float wm[kMergeWin], wl[kMergeWin];
+#pragma unroll
+  for (int cc = 0; cc < kMergeWin; ++cc) {
+    const bool ok = cc < nwc;
+    wm[cc] = ok ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wml[cc]), 0)) : kNegInf;
+    wl[cc] = ok ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wml[cc]), 1)) : 0.f;
+    wv0[cc] = ok ? wv0[cc] : 0.f;
+    wv1[cc] = ok ? wv1[cc] : 0.f;
   }
   float Mx = M;
 #pragma unroll
