@@ -153,22 +153,38 @@ __device__ __forceinline__ TokInfo resolve(const AppendParams& p, int b, int ps,
   return ti;
 }
 
-template <int KIND, int NG>
-__device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4* r_lds, const TileIdx& in,
-                                              int64_t t0, int h, int lane) {
-  constexpr int NT = kAppendTiles;
-  constexpr int MPG = 8 / NG;  // accumulators m per group
+// X operand of tile j of a wave: token t0 + 16 j + r, input channels
+// 32 g .. 32 g + 31 (zero past the last token)
+template <int KIND>
+__device__ __forceinline__ void load_x(const AppendParams& p, int64_t t0, int h, int lane,
+                                       uint4 (&xv)[kAppendTiles][4]) {
   const int g = lane >> 4, r = lane & 15;
-
-  // X operand of tile j: token t0 + 16 j + r, input channels 32g .. 32g + 31
-  uint4 xv[NT][4];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
+  for (int j = 0; j < kAppendTiles; ++j) {
     const int64_t tok = t0 + 16 * j + r;
     const bool valid = tok < p.n_tokens;
     const uint4* xp = reinterpret_cast<const uint4*>(p.x[KIND] + ((valid ? tok : 0) * p.hkv + h) * kD + 32 * g);
 #pragma unroll
     for (int s = 0; s < 4; ++s) xv[j][s] = valid ? xp[s] : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// PRE: the tile's X rows were loaded by the caller (xpre); otherwise they are
+// loaded here.
+template <int KIND, int NG, bool PRE>
+__device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4* r_lds, const TileIdx& in,
+                                              const uint4 (&xpre)[kAppendTiles][4], int64_t t0, int h, int lane) {
+  constexpr int NT = kAppendTiles;
+  constexpr int MPG = 8 / NG;  // accumulators m per group
+  const int g = lane >> 4, r = lane & 15;
+  uint4 xv[NT][4];
+  if constexpr (PRE) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xv[j][s] = xpre[j][s];
+  } else {
+    load_x<KIND>(p, t0, h, lane, xv);
   }
 
   f32x4 acc[NT][8];
@@ -328,7 +344,9 @@ __device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4
   }
 }
 
-template <int NG>
+// ONE: every workgroup has a single iteration (tiles_per_wg == 1, as for
+// decode-time appends); its X rows then also go out before R is staged.
+template <int NG, bool ONE>
 __global__ __launch_bounds__(256, 4) void append_kernel(AppendParams p) {
   __shared__ uint4 r_lds[128 * kRowU4];
   const int h = blockIdx.y;
@@ -346,10 +364,20 @@ __global__ __launch_bounds__(256, 4) void append_kernel(AppendParams p) {
   auto tile0 = [&](int it) {
     return ((int64_t)blockIdx.x * p.tiles_per_wg + it) * kAppendTokens + wave * 16 * kAppendTiles;
   };
-  // the first tile's token indices go out before the rotation is staged
+  // the first tile's token indices (and with ONE its rows) go out before the
+  // rotation is staged
   TileIdx in;
+  uint4 xv[kAppendTiles][4];
   const bool any = tile0(0) < p.n_tokens;  // uniform across the wave
-  if (any) load_idx(p, tile0(0), lane, in);
+  if (any) {
+    load_idx(p, tile0(0), lane, in);
+    if constexpr (ONE) {
+      if (kind == 0)
+        load_x<0>(p, tile0(0), h, lane, xv);
+      else
+        load_x<1>(p, tile0(0), h, lane, xv);
+    }
+  }
   const uint4* rg = reinterpret_cast<const uint4*>((kind ? p.r[1] : p.r[0]) + (int64_t)h * kD * kD);
   uint4 rr[8];
 #pragma unroll
@@ -364,6 +392,15 @@ __global__ __launch_bounds__(256, 4) void append_kernel(AppendParams p) {
     r_lds[(i >> 4) * kRowU4 + (i & 15)] = rr[k];
   }
   __syncthreads();
+  if constexpr (ONE) {
+    if (any) {
+      if (kind == 0)
+        process_tiles<0, NG, true>(p, r_lds, in, xv, tile0(0), h, lane);
+      else
+        process_tiles<1, NG, true>(p, r_lds, in, xv, tile0(0), h, lane);
+    }
+    return;
+  }
   TileIdx nxt;  // raw indices of the next tile, loaded while this one is processed
   for (int it = 0; it < p.tiles_per_wg; ++it) {
     const int64_t t0 = tile0(it);
@@ -378,9 +415,9 @@ __global__ __launch_bounds__(256, 4) void append_kernel(AppendParams p) {
     }
     if (it + 1 < p.tiles_per_wg && tile0(it + 1) < p.n_tokens) load_idx(p, tile0(it + 1), lane, nxt);
     if (kind == 0)
-      process_tiles<0, NG>(p, r_lds, in, t0, h, lane);
+      process_tiles<0, NG, false>(p, r_lds, in, xv, t0, h, lane);
     else
-      process_tiles<1, NG>(p, r_lds, in, t0, h, lane);
+      process_tiles<1, NG, false>(p, r_lds, in, xv, t0, h, lane);
   }
 }
 
@@ -438,10 +475,11 @@ extern "C" int oscar_quantize_append_layers(const oscar_shape* shape, int32_t n_
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int slot = -1;
   timing_record_begin(s, 3, &slot);
+  const bool one = p.tiles_per_wg == 1;
   switch (kD / shape->group_size) {
-    case 1: append_kernel<1><<<grid, 256, 0, s>>>(p); break;
-    case 2: append_kernel<2><<<grid, 256, 0, s>>>(p); break;
-    default: append_kernel<4><<<grid, 256, 0, s>>>(p); break;
+    case 1: one ? append_kernel<1, true><<<grid, 256, 0, s>>>(p) : append_kernel<1, false><<<grid, 256, 0, s>>>(p); break;
+    case 2: one ? append_kernel<2, true><<<grid, 256, 0, s>>>(p) : append_kernel<2, false><<<grid, 256, 0, s>>>(p); break;
+    default: one ? append_kernel<4, true><<<grid, 256, 0, s>>>(p) : append_kernel<4, false><<<grid, 256, 0, s>>>(p); break;
   }
   hipError_t e = hipGetLastError();
   timing_record_end(s, slot);
