@@ -273,6 +273,23 @@ def test_decode_kv_head_counts(K, hkv, hq):
     assert err.max() <= P.ATTN_TOL
 
 
+def test_decode_batch_above_64(K):
+    """130 short ragged sequences (some empty, some shorter than the window):
+    the per-sequence loops of the tile prefix run over several lane passes and
+    the units outnumber the lanes of a wave."""
+    lens = [int(x) for x in np.random.default_rng(7).integers(0, 700, 130)]
+    lens[3] = 0
+    lens[77] = 129
+    s = make_spec(1, lens, 128, 32)
+    rk, rv, rkf, rvf, bt, pool, wk, wv, q = oracle_cache(s)
+    got = run_decode(K, s, rk, rv, q, bt, pool, wk, wv)
+    want = ref.decode_ref(rkf, rvf, q, s.seq_lens, bt, pool, wk, wv, 128)
+    err = P.attn_rel_err(got, want)
+    log(f"decode B=130: max rel err {err.max():.3e}")
+    assert np.isfinite(got).all()
+    assert err.max() <= P.ATTN_TOL
+
+
 def test_decode_every_sequence_empty(K):
     """seq_lens all 0 (and max_seq_len 0) over an existing cache: zeros."""
     s = make_spec(1, [40, 300])
