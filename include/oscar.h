@@ -296,8 +296,8 @@ int oscar_bf16_decode_attn(const oscar_shape* shape, const uint16_t* q, int32_t 
  *   stream while the host enqueues the launches to be timed behind it, without
  *   leaving dirty cache lines the way a copy would.
  * oscar_timing_begin(capacity): from now on every append / decode call also
- *   records a pair of HIP events on its stream around its main kernel, up to
- *   `capacity` pairs.  oscar_timing_end copies the elapsed milliseconds and the
+ *   attaches a pair of HIP events to the dispatch of its main kernel (stamped
+ *   at that kernel's start and end on its stream), up to `capacity` pairs.  oscar_timing_end copies the elapsed milliseconds and the
  *   kernel kind (1 INT2 decode split kernel, 2 bf16 decode split kernel,
  *   3 INT2 append) of each recorded pair into ms/kinds (host arrays of
  *   `capacity`), sets *n, synchronises the events and stops recording.

@@ -473,17 +473,15 @@ extern "C" int oscar_quantize_append_layers(const oscar_shape* shape, int32_t n_
   p.tiles_per_wg = tiles >= 512 ? 4 : (tiles >= 128 ? 2 : 1);
   dim3 grid((unsigned)((tiles + p.tiles_per_wg - 1) / p.tiles_per_wg), (unsigned)p.hkv, 2 * (unsigned)n_layers);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  int slot = -1;
-  timing_record_begin(s, 3, &slot);
+  const TimedLaunch tl = timing_events(3);
   const bool one = p.tiles_per_wg == 1;
+  auto go = [&](auto kernel) { hipExtLaunchKernelGGL(kernel, grid, dim3(256), 0, s, tl.start, tl.stop, 0, p); };
   switch (kD / shape->group_size) {
-    case 1: one ? append_kernel<1, true><<<grid, 256, 0, s>>>(p) : append_kernel<1, false><<<grid, 256, 0, s>>>(p); break;
-    case 2: one ? append_kernel<2, true><<<grid, 256, 0, s>>>(p) : append_kernel<2, false><<<grid, 256, 0, s>>>(p); break;
-    default: one ? append_kernel<4, true><<<grid, 256, 0, s>>>(p) : append_kernel<4, false><<<grid, 256, 0, s>>>(p); break;
+    case 1: one ? go(append_kernel<1, true>) : go(append_kernel<1, false>); break;
+    case 2: one ? go(append_kernel<2, true>) : go(append_kernel<2, false>); break;
+    default: one ? go(append_kernel<4, true>) : go(append_kernel<4, false>); break;
   }
-  hipError_t e = hipGetLastError();
-  timing_record_end(s, slot);
-  return e == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
+  return hipGetLastError() == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
 }
 
 extern "C" int oscar_quantize_append(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cstddef>
 #include <cstdint>
@@ -124,9 +125,14 @@ inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads
   return w;
 }
 
-// Event-pair recording around main kernels (measurement only).
-void timing_record_begin(hipStream_t st, int kind, int* slot);
-void timing_record_end(hipStream_t st, int slot);
+// Event pair of the next main-kernel launch while timing is on (measurement
+// only), else two null events.  The kernel is launched with
+// hipExtLaunchKernelGGL, which stamps the events at the dispatch's own start
+// and end, so the pair spans the kernel and nothing queued around it.
+struct TimedLaunch {
+  hipEvent_t start, stop;
+};
+TimedLaunch timing_events(int kind);
 
 }  // namespace oscar
 

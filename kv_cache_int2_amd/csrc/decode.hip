@@ -1344,20 +1344,20 @@ int launch_decode(bool int2, const SplitParams& sp, const uint16_t* r_k, int bat
     prep_kernel<G><<<dim3(batch * sp.n_layers, sp.hkv, 1 + sp.n_wchunks), 256, 0, s>>>(sp, r_k);
     if (hipGetLastError() != hipSuccess) return OSCAR_EHIP;
   }
-  int slot = -1;
-  timing_record_begin(s, int2 ? 1 : 2, &slot);
+  const TimedLaunch tl = timing_events(int2 ? 1 : 2);
   if (int2) {
     constexpr int GW = G > 8 ? 8 : (G < 4 ? 4 : G);  // whole-token groups; 4 heads with finer groups
+    auto go = [&](auto kernel) { hipExtLaunchKernelGGL(kernel, dim3(sp.n_wg), dim3(256), 0, s, tl.start, tl.stop, 0, sp); };
     switch (sp.ng) {
-      case 1: int2_split_kernel<GW, 1><<<sp.n_wg, 256, 0, s>>>(sp); break;
-      case 2: int2_split_kernel<4, 2><<<sp.n_wg, 256, 0, s>>>(sp); break;
-      default: int2_split_kernel<4, 4><<<sp.n_wg, 256, 0, s>>>(sp); break;
+      case 1: go(int2_split_kernel<GW, 1>); break;
+      case 2: go(int2_split_kernel<4, 2>); break;
+      default: go(int2_split_kernel<4, 4>); break;
     }
   } else {
-    bf16_split_kernel<G><<<dim3(sp.n_splits, sp.hkv, batch), 256, 0, s>>>(sp);
+    hipExtLaunchKernelGGL(bf16_split_kernel<G>, dim3(sp.n_splits, sp.hkv, batch), dim3(256), 0, s, tl.start, tl.stop,
+                          0, sp);
   }
   if (hipGetLastError() != hipSuccess) return OSCAR_EHIP;
-  timing_record_end(s, slot);
   // heads per merge workgroup: the R_V tile is loaded once for all of them,
   // as long as about two workgroups per CU remain
   int mh = 1;

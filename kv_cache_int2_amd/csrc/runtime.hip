@@ -1,8 +1,8 @@
 // Measurement helpers, the device's compute-unit count and status strings: a
 // streaming copy kernel (HBM probe and the known-size reference for HBM traffic
 // counters), a timed wait kernel that holds a stream without touching memory,
-// and opt-in event-pair recording around the main kernel of each append /
-// decode call.
+// and opt-in event pairs attached to the dispatch of the main kernel of each
+// append / decode call.
 #include <vector>
 
 #include "common.h"
@@ -50,17 +50,14 @@ int device_cu_count() {
   return n;
 }
 
-void timing_record_begin(hipStream_t st, int kind, int* slot) {
-  *slot = -1;
-  if (!g_timing.on || g_timing.used >= g_timing.capacity) return;
-  *slot = g_timing.used++;
-  g_timing.kind[*slot] = kind;
-  (void)hipEventRecord(g_timing.start[*slot], st);
-}
-
-void timing_record_end(hipStream_t st, int slot) {
-  if (slot < 0) return;
-  (void)hipEventRecord(g_timing.stop[slot], st);
+TimedLaunch timing_events(int kind) {
+  TimedLaunch t{nullptr, nullptr};
+  if (!g_timing.on || g_timing.used >= g_timing.capacity) return t;
+  const int slot = g_timing.used++;
+  g_timing.kind[slot] = kind;
+  t.start = g_timing.start[slot];
+  t.stop = g_timing.stop[slot];
+  return t;
 }
 
 }  // namespace oscar
