@@ -176,7 +176,8 @@ def main():
 
     def timed(step, kind):
         """Wall time per step over the timed steps (no instrumentation), then the
-        same steps again with HIP events attached to the split kernel's dispatch for its duration."""
+        same steps again with HIP events attached to the split kernel's dispatch
+        for its duration."""
         for i in range(args.warmup):
             step(i)
         torch.cuda.synchronize()
