@@ -87,7 +87,8 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the prefill-ingest (append) leg")
     ap.add_argument("--no-layers-leg", action="store_true", help="skip the layer-batched decode leg")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="decode time the oracle baseline spends")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="decode time of each oracle baseline leg (one process; process pool)")
     ap.add_argument("--quality", action="store_true",
                     help="instead of the benchmark: cache quality of the OSCAR, Hadamard-only and identity "
                          "rotations through the same kernels (one JSON line)")
@@ -164,20 +165,26 @@ def main():
     ws = torch.empty(K.oscar_decode_workspace_bytes(shape, B, nmax), dtype=torch.uint8, device=dev)
     out = torch.empty((B, HQ, 128), dtype=torch.float32, device=dev)
 
-    def step_int2(i):
+    def step_int2(i, ev=None):
         l = i % L
         K.oscar_quantize_append(shape, rkd, rvd, cur_kd, cur_vd, cur_si, cur_pos, btd, lensd, pools[l], wks[l], wvs[l])
-        K.oscar_decode_attn(shape, rkd, rvd, q, lensd, nmax, btd, pools[l], wks[l], wvs[l], out, ws)
+        if ev is None:
+            K.oscar_decode_attn(shape, rkd, rvd, q, lensd, nmax, btd, pools[l], wks[l], wvs[l], out, ws)
+        else:
+            K.oscar_decode_attn_timed(shape, rkd, rvd, q, lensd, nmax, btd, pools[l], wks[l], wvs[l], out, ws, *ev)
 
-    def step_bf16(i):
+    def step_bf16(i, ev=None):
         l = i % L
         K.oscar_bf16_append(shape, cur_kd, cur_vd, cur_si, cur_pos, btd, kvp[l])
-        K.oscar_bf16_decode_attn(shape, q, lensd, nmax, btd, kvp[l], out, ws)
+        if ev is None:
+            K.oscar_bf16_decode_attn(shape, q, lensd, nmax, btd, kvp[l], out, ws)
+        else:
+            K.oscar_bf16_decode_attn_timed(shape, q, lensd, nmax, btd, kvp[l], out, ws, *ev)
 
-    def timed(step, kind):
+    def timed(step):
         """Wall time per step over the timed steps (no instrumentation), then the
-        same steps again with HIP events attached to the split kernel's dispatch
-        for its duration."""
+        same steps again with a pair of events attached to each split kernel's
+        dispatch for its duration.  Returns (s per step, mean split s, all split s)."""
         for i in range(args.warmup):
             step(i)
         torch.cuda.synchronize()
@@ -186,35 +193,20 @@ def main():
             step(args.warmup + i)
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t) / args.steps
-        cap = 4 * args.steps + 8
+        evs = [(K.Event(), K.Event()) for _ in range(args.steps)]
         # a 3 ms wait queued first: the host has enqueued every step before the
         # GPU reaches them, so no launch gap of the host falls between an event
         # and the kernel it brackets (the wait touches no memory, so it leaves
         # no dirty cache lines behind for the first step to write back)
         K.oscar_gpu_wait(3000)
-        K.oscar_timing_begin(cap)
         for i in range(args.steps):
-            step(args.warmup + i)
+            step(args.warmup + i, evs[i])
         torch.cuda.synchronize()
-        ms, kinds = K.oscar_timing_end(cap)
-        kern = [m for m, k in zip(ms, kinds) if k == kind]
-        return dt, float(np.mean(kern)) / 1e3 if kern else None, kern
+        kern = [K.Event.elapsed_ms(a, b) for a, b in evs]
+        return dt, float(np.mean(kern)) / 1e3, kern
 
-    # ---- in-session HBM probe (streaming copy, 2 GiB each way) ----
-    nb = 2 << 30
-    a = torch.empty(nb, dtype=torch.uint8, device=dev)
-    c = torch.empty(nb, dtype=torch.uint8, device=dev)
-    K.oscar_hbm_copy(a, c)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
-        K.oscar_hbm_copy(a, c)
-    e1.record()
-    torch.cuda.synchronize()
-    probe_gbs = 2 * nb * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
-    del a, c
-    log(f"HBM copy probe: {probe_gbs:.0f} GB/s (read + write)")
+    # ---- in-session HBM probes ----
+    probe = hbm_probes(K, torch, dev, pool_all, n_pages * L)
 
     # ---- algorithmic bytes ----
     win = np.minimum(lens, W)
@@ -230,14 +222,14 @@ def main():
     b_bf16_kv = float(lens.sum() * HKV * 512)
     step_bytes_bf16 = b_bf16_kv + b_q_out + b_bt + B * HKV * 2 * 2 * 256
 
-    dt, split_s, split_all = timed(step_int2, 1)
+    dt, split_s, split_all = timed(step_int2)
     if split_all:
         sa = np.asarray(split_all)
         log(f"split launches (ms): first {sa[0]:.4f} min {sa.min():.4f} median {np.median(sa):.4f} max {sa.max():.4f}")
     log(f"INT2 step {dt * 1e3:.3f} ms, split kernel {split_s * 1e3 if split_s else float('nan'):.3f} ms")
     res_bf16 = None
     if kvp:
-        dtb, split_b, _ = timed(step_bf16, 2)
+        dtb, split_b, _ = timed(step_bf16)
         log(f"bf16 step {dtb * 1e3:.3f} ms, split kernel {split_b * 1e3 if split_b else float('nan'):.3f} ms")
         res_bf16 = {
             "ms_per_step": dtb * 1e3,
@@ -305,7 +297,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "int2 codes as fp4 x e4m3 terms (MFMA), f32 accumulate",
         "data": "synthetic (seeded Gaussian K/V, 4 key outlier channels x20; no dataset exists for this path)",
         "config": {"workload": f"long-context decode step: append 1 token/seq + INT2 decode, B={B}, n={nmax}, "
                                f"{HQ}q/{HKV}kv heads, d=128, group {G}, 16-token scattered pages, bf16 window {W}"
@@ -314,7 +306,7 @@ def main():
                    "decode_tokens_per_s": B / dt, "step_bytes": step_bytes_int2},
         "bf16_kv": res_bf16,
         "speedup_vs_bf16": (res_bf16["ms_per_step"] / (dt * 1e3)) if res_bf16 else None,
-        "hbm_probe_copy_gbs": probe_gbs,
+        "hbm_probe": probe,
         "append": res_append,
         "layers_batched": res_layers,
         "roofline": {
@@ -333,6 +325,48 @@ def main():
     if not args.no_cpu_baseline and G == 128 and S == 0:  # the oracle sample covers the default cache form
         line["cpu_baseline"] = cpu_baseline(s, rk, rv, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def hbm_probes(K, torch, dev, pool_all, n_pages_total):
+    """In-session HBM ceilings: the copy kernel (2 GiB each way; also the scale of
+    the traffic counters) and the read probe over the layer caches (n pages of
+    9216 bytes, larger than the 256 MB Infinity Cache), sequentially and through
+    random tables of whole pages (9216 B), half pages (the 4 KV heads a split
+    workgroup reads side by side, 4608 B) and single KV-head blocks (1152 B)."""
+    res = {}
+    nb = 2 << 30
+    a = torch.empty(nb, dtype=torch.uint8, device=dev)
+    c = torch.empty(nb, dtype=torch.uint8, device=dev)
+    K.oscar_hbm_copy(a, c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        K.oscar_hbm_copy(a, c)
+    e1.record()
+    torch.cuda.synchronize()
+    res["copy_gbs"] = 2 * nb * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del a, c
+    page = int(pool_all.shape[-1] * pool_all.shape[-2])
+    total = n_pages_total * page
+    sink = torch.empty(65536, dtype=torch.int32, device=dev)
+    gen = np.random.default_rng(1234)
+    for name, bb, table in (("seq_read_gbs", page, False), ("page_read_gbs", page, True),
+                            ("half_page_read_gbs", page // 2, True), ("head_block_read_gbs", page // 8, True)):
+        n = total // bb
+        blocks = torch.from_numpy(gen.permutation(n).astype(np.int32)).to(dev) if table else None
+        K.oscar_hbm_read(pool_all, bb, blocks, n, sink)
+        torch.cuda.synchronize()
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            K.oscar_hbm_read(pool_all, bb, blocks, n, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = total * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    res["bytes_per_read"] = total
+    log("HBM probes (GB/s): " + ", ".join(f"{k} {v:.0f}" for k, v in res.items() if k.endswith("gbs")))
+    return res
 
 
 def append_leg(K, torch, dev, shape, rkd, rvd, args, tok_bytes=72):
@@ -364,12 +398,11 @@ def append_leg(K, torch, dev, shape, rkd, rvd, args, tok_bytes=72):
         K.oscar_quantize_append(shape, rkd, rvd, kd, vd, sid, psd, btd, lens, pool, wk, wv)
     torch.cuda.synchronize()
     reps = 10
-    K.oscar_timing_begin(4 * reps + 8)
-    for _ in range(reps):
-        K.oscar_quantize_append(shape, rkd, rvd, kd, vd, sid, psd, btd, lens, pool, wk, wv)
+    evs = [(K.Event(), K.Event()) for _ in range(reps)]
+    for i in range(reps):
+        K.oscar_quantize_append_timed(shape, rkd, rvd, kd, vd, sid, psd, btd, lens, pool, wk, wv, *evs[i])
     torch.cuda.synchronize()
-    ms, kinds = K.oscar_timing_end(4 * reps + 8)
-    t = float(np.mean([m for m, kk in zip(ms, kinds) if kk == 3])) / 1e3
+    t = float(np.mean([K.Event.elapsed_ms(a, b) for a, b in evs])) / 1e3
     byts = n * hkv * (512 + tok_bytes) + min(n, w) * hkv * 512 + 2 * hkv * 128 * 128 * 2
     flops = 2 * 2 * n * hkv * 128 * 128
     log(f"append 65536 tokens: {t * 1e6:.1f} us, {byts / t / 1e9:.0f} GB/s, rotation {flops / t / 1e12:.1f} TFLOP/s")
@@ -383,7 +416,7 @@ def quality_leg(K, wl, torch):
     """Quality of the three rotations on the 2048-token workload and on a
     shrunk copy of the 32K-context one (same distributions), at each group size
     (128, 64, 32 rotated channels per scale/zero pair)."""
-    from kv_cache_int2_amd import quality
+    import quality
 
     res = {}
     for label, s in (("B1_n2048", wl.spec(1)), ("B2_n8192", wl.spec(2, batch=2, seq_len=8192))):
@@ -399,13 +432,80 @@ def quality_leg(K, wl, torch):
     print(json.dumps({"quality": res, "data": "synthetic (seeded Gaussian K/V, 4 key outlier channels x20)"}))
 
 
+def _oracle_unit(s, rkf, rvf, b, h):
+    """The oracle's cache of one (sequence, KV head) unit at full context
+    (its own single-head pool and ring; building it is not timed)."""
+    import workloads as wl
+    from oracle import oscar_ref as ref
+
+    n = int(s.seq_lens[b])
+    k, v = wl.context_kv(s, b)
+    s1 = wl.Spec(cfg=s.cfg, name=s.name, batch=1, n_q_heads=s.gqa, n_kv_heads=1,
+                 seq_lens=np.array([n], np.int32), window=s.window)
+    bt, n_pages = wl.page_table(s1)
+    pool = np.zeros((n_pages, 1, ref.BLOCK), np.uint8)
+    wk = np.zeros((1, s.window, 1, 128), np.uint16)
+    wv = np.zeros_like(wk)
+    ref.append_sequence_ref(rkf[h:h + 1], rvf[h:h + 1], np.ascontiguousarray(k[:, h:h + 1]),
+                            np.ascontiguousarray(v[:, h:h + 1]), bt[0], pool, wk[0], wv[0], s.window)
+    return n, bt, pool, wk, wv
+
+
+def _oracle_decode(s, rkf, rvf, q, b, h, unit):
+    """One oracle decode of a unit; returns its algorithmic cache bytes."""
+    from oracle import oscar_ref as ref
+
+    n, bt, pool, wk, wv = unit
+    ref.decode_ref(rkf[h:h + 1], rvf[h:h + 1], q[b:b + 1, h * s.gqa:(h + 1) * s.gqa], np.array([n]), bt, pool, wk,
+                   wv, s.window)
+    w = min(n, s.window)
+    return (n - w) * 72 + w * 512
+
+
+_BARRIER = None
+
+
+def _pool_init(barrier):
+    global _BARRIER
+    _BARRIER = barrier
+
+
+def _pool_worker(task):
+    """Worker of the process-pool leg: build one unit, wait for every worker,
+    then decode it repeatedly for `seconds` of wall time (BLAS on one thread)."""
+    from threadpoolctl import threadpool_limits
+
+    import workloads as wl
+    from oracle import oscar_ref as ref
+
+    cfg, rk_bits, rv_bits, b, h, seconds = task
+    s = wl.spec(cfg)
+    rkf, rvf = ref.bf16_to_f64(rk_bits), ref.bf16_to_f64(rv_bits)
+    q = wl.decode_queries(s)
+    with threadpool_limits(limits=1):
+        unit = _oracle_unit(s, rkf, rvf, b, h)
+        _BARRIER.wait(timeout=600)  # a worker that failed to build breaks the barrier instead of hanging it
+        t0 = time.perf_counter()
+        nbytes, calls = 0, 0
+        while time.perf_counter() - t0 < seconds:
+            nbytes += _oracle_decode(s, rkf, rvf, q, b, h, unit)
+            calls += 1
+        return nbytes, calls, time.perf_counter() - t0
+
+
 def cpu_baseline(s, rk_bits, rv_bits, target_s: float, max_units: int = 3):
     """The oracle (numpy fp64, untuned) decoding a bounded sample of the same
-    workload on the host, BLAS pinned to one thread: up to ``max_units``
-    (sequence, KV head) pairs at full context, each with its own oracle-built
-    pool (building it is not timed), decoded round robin until ``target_s``
-    seconds of decode time have been spent.  Throughput is in the bench's unit:
-    algorithmic cache bytes of the decoded units per second."""
+    workload on the host's cores, in the bench's unit (algorithmic cache bytes
+    of the decoded (sequence, KV head) units per second):
+      * one process, BLAS on one thread: up to ``max_units`` units at full
+        context decoded round robin until ``target_s`` s of decode time;
+      * a pool of P processes (P = the cores this process may run on, at most
+        16), one unit each (P distinct units), all decoding their unit
+        repeatedly for ``target_s`` s of wall time after a common barrier.
+    ``value`` is the pool's aggregate rate; ``cores`` = P."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
     from threadpoolctl import threadpool_limits
 
     import workloads as wl
@@ -413,38 +513,46 @@ def cpu_baseline(s, rk_bits, rv_bits, target_s: float, max_units: int = 3):
 
     rkf, rvf = ref.bf16_to_f64(rk_bits), ref.bf16_to_f64(rv_bits)
     q = wl.decode_queries(s)
+    units_per_step = s.batch * s.n_kv_heads
+    pairs = [(u % s.batch, (u // s.batch + 3 * u) % s.n_kv_heads) for u in range(units_per_step)]
     units = []
     with threadpool_limits(limits=1):
         for u in range(max_units):
-            b, h = u % s.batch, (3 * u) % s.n_kv_heads
-            n = int(s.seq_lens[b])
-            k, v = wl.context_kv(s, b)
-            s1 = wl.Spec(cfg=s.cfg, name=s.name, batch=1, n_q_heads=s.gqa, n_kv_heads=1,
-                         seq_lens=np.array([n], np.int32), window=s.window)
-            bt, n_pages = wl.page_table(s1)
-            pool = np.zeros((n_pages, 1, ref.BLOCK), np.uint8)
-            wk = np.zeros((1, s.window, 1, 128), np.uint16)
-            wv = np.zeros_like(wk)
-            ref.append_sequence_ref(rkf[h:h + 1], rvf[h:h + 1], k[:, h:h + 1], v[:, h:h + 1], bt[0], pool, wk[0],
-                                    wv[0], s.window)
-            units.append((b, h, n, bt, pool, wk, wv))
-            del k, v
+            b, h = pairs[u]
+            units.append((b, h, _oracle_unit(s, rkf, rvf, b, h)))
         total_t, total_bytes, calls = 0.0, 0.0, 0
         while total_t < target_s:
-            b, h, n, bt, pool, wk, wv = units[calls % len(units)]
-            qq = q[b:b + 1, h * s.gqa:(h + 1) * s.gqa]
+            b, h, unit = units[calls % len(units)]
             t = time.perf_counter()
-            ref.decode_ref(rkf[h:h + 1], rvf[h:h + 1], qq, np.array([n]), bt, pool, wk, wv, s.window)
+            total_bytes += _oracle_decode(s, rkf, rvf, q, b, h, unit)
             total_t += time.perf_counter() - t
-            w = min(n, s.window)
-            total_bytes += (n - w) * 72 + w * 512
             calls += 1
-    units_per_step = s.batch * s.n_kv_heads
-    return {"value": total_bytes / total_t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{calls} decode calls (oracle decode_ref: unpack pool bytes + fp64 attention) over "
-                      f"{len(units)} of the {units_per_step} (sequence, KV head) units at n={int(s.seq_lens.max())}, "
-                      f"round robin, {total_t:.1f} s of decode time on 1 thread",
-            "decode_tokens_per_s_equiv": s.batch / (total_t / calls * units_per_step)}
+    del units
+    single = {"value": total_bytes / total_t / 1e9, "cores": 1,
+              "sample": f"{calls} decode calls over {max_units} of the {units_per_step} (sequence, KV head) units, "
+                        f"round robin, {total_t:.1f} s of decode time"}
+    log(f"oracle, 1 process: {single['value']:.3f} GB/s")
+
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    P = max(1, min(16, avail, units_per_step))
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(P)
+    tasks = [(s.cfg, rk_bits, rv_bits, *pairs[i], target_s) for i in range(P)]
+    with ProcessPoolExecutor(max_workers=P, mp_context=ctx, initializer=_pool_init, initargs=(barrier,)) as ex:
+        res = list(ex.map(_pool_worker, tasks))
+    p_bytes = sum(r[0] for r in res)
+    p_calls = sum(r[1] for r in res)
+    p_wall = max(r[2] for r in res)
+    value = p_bytes / p_wall / 1e9
+    log(f"oracle, {P} processes: {value:.3f} GB/s")
+    return {"value": value, "unit": "GB/s", "cores": P, "kind": "oracle",
+            "sample": f"process pool of {P} (numpy fp64 oracle decode_ref, BLAS on one thread each): {P} distinct "
+                      f"of the {units_per_step} (sequence, KV head) units at n={int(s.seq_lens.max())}, one per "
+                      f"process, {p_calls} decode calls in {p_wall:.1f} s of wall time after a common barrier",
+            "host_cpus": os.cpu_count(), "host_cpus_available": avail,
+            "single_process": single,
+            "decode_tokens_per_s_equiv": s.batch * value * 1e9 / (
+                s.batch * s.n_kv_heads * ((int(s.seq_lens.max()) - s.window) * 72 + s.window * 512))}
 
 
 # ---------------------------------------------------------------------------

@@ -289,24 +289,55 @@ int oscar_bf16_decode_attn(const oscar_shape* shape, const uint16_t* q, int32_t 
 /*
  * Measurement helpers (not part of the method).
  * oscar_hbm_copy: plain streaming copy of `bytes` (multiple of 16, both pointers
- *   16-byte aligned) from src to dst on the device; used to calibrate HBM
- *   counters and as an in-session bandwidth probe.
+ *   16-byte aligned) from src to dst on the device; the known-size reference
+ *   that HBM traffic counters are scaled by.
+ * oscar_hbm_read: streaming read probe: reads n_blocks blocks of block_bytes
+ *   (multiple of 16, 16 .. 2^20) each from the device buffer src (16-byte
+ *   aligned), block i at src + blocks[i] * block_bytes (device int32 table, read
+ *   in order) or, with blocks NULL, at src + i * block_bytes.  Workgroup w of
+ *   n_workgroups (0 = 8 per compute unit, at most OSCAR_READ_MAX_WORKGROUPS)
+ *   reads the w-th equal share of the concatenated blocks, 16 bytes per load,
+ *   and stores the XOR of what it read to sink[w] (device uint32
+ *   [n_workgroups or 8 x compute units]).  It measures the HBM read ceiling of
+ *   the decode's access shapes: whole pages or single KV-head blocks scattered
+ *   through a block table, or one sequential stream.
  * oscar_gpu_wait: enqueues a one-wave kernel that returns after `microseconds`
  *   (0 .. 10^7) of the device's wall clock and touches no memory; it holds the
  *   stream while the host enqueues the launches to be timed behind it, without
  *   leaving dirty cache lines the way a copy would.
- * oscar_timing_begin(capacity): from now on every append / decode call also
- *   attaches a pair of HIP events to the dispatch of its main kernel (stamped
- *   at that kernel's start and end on its stream), up to `capacity` pairs.  oscar_timing_end copies the elapsed milliseconds and the
- *   kernel kind (1 INT2 decode split kernel, 2 bf16 decode split kernel,
- *   3 INT2 append) of each recorded pair into ms/kinds (host arrays of
- *   `capacity`), sets *n, synchronises the events and stops recording.
- *   Not thread-safe; meant for one benchmarking thread.
+ * oscar_event_create / oscar_event_destroy: a HIP event (hipEvent_t, timing
+ *   enabled) owned by the caller.  oscar_event_elapsed_ms waits for `stop` and
+ *   returns the milliseconds between two recorded events.
+ * The *_timed entry points take the same arguments as their plain forms plus
+ *   two such events (both NULL, or both set): the events are attached to the
+ *   dispatch of the call's main kernel (the append kernel; the INT2 or bf16
+ *   decode split kernel) and are stamped at that kernel's own start and end on
+ *   its stream.  The library keeps no timing state between calls.
  */
+#define OSCAR_READ_MAX_WORKGROUPS 65536
 int oscar_hbm_copy(const void* src, void* dst, size_t bytes, void* stream);
+int oscar_hbm_read(const void* src, int64_t block_bytes, const int32_t* blocks, int64_t n_blocks, uint32_t* sink,
+                   int32_t n_workgroups, void* stream);
 int oscar_gpu_wait(int64_t microseconds, void* stream);
-int oscar_timing_begin(int32_t capacity);
-int oscar_timing_end(float* ms, int32_t* kinds, int32_t capacity, int32_t* n);
+int oscar_event_create(void** event);
+int oscar_event_destroy(void* event);
+int oscar_event_elapsed_ms(void* start, void* stop, float* ms);
+int oscar_quantize_append_timed(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
+                                const uint16_t* k_new, const uint16_t* v_new, int64_t n_tokens,
+                                const int32_t* seq_idx, const int32_t* pos, int32_t batch,
+                                const int32_t* block_table, int32_t max_pages_per_seq,
+                                const int32_t* seq_len_after, uint8_t* pool, int64_t n_pages, uint16_t* win_k,
+                                uint16_t* win_v, void* stream, void* ev_start, void* ev_stop);
+int oscar_decode_attn_timed(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
+                            const uint16_t* q, int32_t batch, const int32_t* seq_lens, int32_t max_seq_len,
+                            const int32_t* block_table, int32_t max_pages_per_seq, const uint8_t* pool,
+                            int64_t n_pages, const uint16_t* win_k, const uint16_t* win_v, float* out,
+                            void* workspace, size_t workspace_bytes, void* stream, void* ev_start, void* ev_stop);
+int oscar_bf16_decode_attn_timed(const oscar_shape* shape, const uint16_t* q, int32_t batch,
+                                 const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
+                                 int32_t max_pages_per_seq, const uint16_t* kv_pool, int64_t n_pages, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream, void* ev_start,
+                                 void* ev_stop);
 
 /* Static description of a status code. */
 const char* oscar_strerror(int status);

@@ -19,7 +19,8 @@ from ._lib import OscarShape, lib
 __all__ = [
     "OscarError", "OscarShape", "make_shape", "oscar_calibrate", "oscar_quantize_append",
     "oscar_decode_workspace_bytes", "oscar_decode_attn", "oscar_bf16_append",
-    "oscar_bf16_decode_attn", "oscar_hbm_copy", "oscar_gpu_wait", "oscar_timing_begin", "oscar_timing_end",
+    "oscar_bf16_decode_attn", "oscar_hbm_copy", "oscar_hbm_read", "oscar_gpu_wait", "Event",
+    "oscar_quantize_append_timed", "oscar_decode_attn_timed", "oscar_bf16_decode_attn_timed",
     "oscar_strerror", "BLOCK_BYTES", "BF16_BLOCK_ELEMS", "PAGE_SIZE", "HEAD_DIM", "block_bytes",
     "oscar_calibrate_layers", "oscar_rotation_file_bytes", "oscar_rotation_write", "oscar_rotation_read_info",
     "oscar_rotation_read", "oscar_quantize_append_layers", "oscar_decode_layers_workspace_bytes",
@@ -50,12 +51,38 @@ def block_bytes(group_size: int = 128) -> int:
     return 1024 + 8 * PAGE_SIZE * (HEAD_DIM // group_size)
 
 
-def _check_pool(shape, pool) -> None:
-    if pool is None:
+def _want(t, dims, name):
+    """t must be a tensor/array of len(dims) dimensions; an int entry of dims
+    fixes that dimension, a (">=", n) entry bounds it from below, None leaves it
+    free.  Raises ValueError otherwise."""
+    if t is None:
+        raise ValueError(f"{name}: missing")
+    shape = tuple(int(x) for x in t.shape)
+    ok = len(shape) == len(dims)
+    if ok:
+        for have, want in zip(shape, dims):
+            if want is None:
+                continue
+            if isinstance(want, tuple):
+                if have < want[1]:
+                    ok = False
+            elif have != want:
+                ok = False
+    if not ok:
+        txt = ", ".join("*" if w is None else (f">={w[1]}" if isinstance(w, tuple) else str(w)) for w in dims)
+        raise ValueError(f"{name}: shape {list(shape)}, expected [{txt}]")
+
+
+def _ring_rows(shape) -> int:
+    return int(shape.window) + int(shape.n_sink)
+
+
+def _check_rings(shape, win_k, win_v, batch, lead=()):
+    """bf16 rings [*lead][>= batch][W + n_sink][Hkv][128], required when W + n_sink > 0."""
+    if _ring_rows(shape) == 0:
         return
-    want = shape.n_kv_heads * block_bytes(shape.group_size) if shape.group_size in (32, 64, 128) else None
-    if want is not None and pool.numel() != pool.shape[0] * want:
-        raise ValueError(f"pool: expected [n_pages][{shape.n_kv_heads}][{block_bytes(shape.group_size)}] bytes")
+    for name, w in (("win_k", win_k), ("win_v", win_v)):
+        _want(w, (*lead, (">=", batch), _ring_rows(shape), shape.n_kv_heads, HEAD_DIM), name)
 
 
 def _check(fn: str, status: int) -> None:
@@ -103,7 +130,8 @@ def oscar_calibrate(shape: OscarShape, q_cal: np.ndarray, k_cal: np.ndarray, v_c
     k = np.ascontiguousarray(k_cal, dtype=np.float32)
     v = np.ascontiguousarray(v_cal, dtype=np.float32)
     hkv = shape.n_kv_heads
-    if q.ndim != 3 or k.shape != v.shape or k.ndim != 3 or q.shape[0] != hkv or k.shape[0] != hkv:
+    if (q.ndim != 3 or k.shape != v.shape or k.ndim != 3 or q.shape[0] != hkv or k.shape[0] != hkv
+            or q.shape[2] != HEAD_DIM or k.shape[2] != HEAD_DIM):
         raise ValueError("calibration arrays must be [Hkv][n][128]")
     rk = np.empty((hkv, 128, 128), np.uint16)
     rv = np.empty_like(rk)
@@ -123,7 +151,8 @@ def oscar_calibrate_layers(shape: OscarShape, q_cal: np.ndarray, k_cal: np.ndarr
     k = np.ascontiguousarray(k_cal, dtype=np.float32)
     v = np.ascontiguousarray(v_cal, dtype=np.float32)
     hkv = shape.n_kv_heads
-    if q.ndim != 4 or k.shape != v.shape or k.ndim != 4 or q.shape[:2] != k.shape[:2] or q.shape[1] != hkv:
+    if (q.ndim != 4 or k.shape != v.shape or k.ndim != 4 or q.shape[:2] != k.shape[:2] or q.shape[1] != hkv
+            or q.shape[3] != HEAD_DIM or k.shape[3] != HEAD_DIM):
         raise ValueError("calibration arrays must be [L][Hkv][n][128]")
     n_layers = q.shape[0]
     rk = np.empty((n_layers, hkv, 128, 128), np.uint16)
@@ -179,16 +208,51 @@ def oscar_rotation_read(path: str, shape: OscarShape, n_layers: int, eigenvalues
     return (rk, rv, ek, ev) if eigenvalues else (rk, rv)
 
 
+def _append_checks(shape, r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after, pool, win_k, win_v,
+                   lead=()):
+    hkv = shape.n_kv_heads
+    _want(r_k, (*lead, hkv, HEAD_DIM, HEAD_DIM), "r_k")
+    _want(r_v, (*lead, hkv, HEAD_DIM, HEAD_DIM), "r_v")
+    _want(k_new, (*lead, None, hkv, HEAD_DIM), "k_new")
+    n_tokens = int(k_new.shape[len(lead)])
+    _want(v_new, (*lead, n_tokens, hkv, HEAD_DIM), "v_new")
+    _want(seq_idx, (n_tokens,), "seq_idx")
+    _want(pos, (n_tokens,), "pos")
+    _want(block_table, (None, None), "block_table")
+    batch = int(block_table.shape[0])
+    _want(seq_len_after, (batch,), "seq_len_after")
+    _want(pool, (*lead, None, hkv, block_bytes(shape.group_size)), "pool")
+    if n_tokens > 0:  # an empty append touches nothing
+        _check_rings(shape, win_k, win_v, batch, lead)
+    return n_tokens, batch
+
+
+def _append_args(shape, r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after, pool, win_k, win_v,
+                 stream):
+    b16, i32, u8, _ = _dt()
+    n_tokens, batch = _append_checks(shape, r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,
+                                     pool, win_k, win_v)
+    return (C.byref(shape), _dev(r_k, b16, "r_k"), _dev(r_v, b16, "r_v"), _dev(k_new, b16, "k_new"),
+            _dev(v_new, b16, "v_new"), n_tokens, _dev(seq_idx, i32, "seq_idx"), _dev(pos, i32, "pos"), batch,
+            _dev(block_table, i32, "block_table"), int(block_table.shape[1]),
+            _dev(seq_len_after, i32, "seq_len_after"), _dev(pool, u8, "pool"), int(pool.shape[0]),
+            _dev(win_k, b16, "win_k"), _dev(win_v, b16, "win_v"), _stream(stream))
+
+
 def oscar_quantize_append(shape, r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,
                           pool, win_k=None, win_v=None, stream=None) -> None:
-    b16, i32, u8, _ = _dt()
-    _check_pool(shape, pool)
     _check("oscar_quantize_append", lib.oscar_quantize_append(
-        C.byref(shape), _dev(r_k, b16, "r_k"), _dev(r_v, b16, "r_v"), _dev(k_new, b16, "k_new"),
-        _dev(v_new, b16, "v_new"), int(k_new.shape[0]), _dev(seq_idx, i32, "seq_idx"),
-        _dev(pos, i32, "pos"), int(block_table.shape[0]), _dev(block_table, i32, "block_table"),
-        int(block_table.shape[1]), _dev(seq_len_after, i32, "seq_len_after"), _dev(pool, u8, "pool"),
-        int(pool.shape[0]), _dev(win_k, b16, "win_k"), _dev(win_v, b16, "win_v"), _stream(stream)))
+        *_append_args(shape, r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after, pool, win_k, win_v,
+                      stream)))
+
+
+def oscar_quantize_append_timed(shape, r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,
+                                pool, win_k, win_v, start, stop, stream=None) -> None:
+    """oscar_quantize_append with the Event pair (start, stop) attached to the
+    append kernel's dispatch."""
+    _check("oscar_quantize_append_timed", lib.oscar_quantize_append_timed(
+        *_append_args(shape, r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after, pool, win_k, win_v,
+                      stream), start.handle, stop.handle))
 
 
 def oscar_decode_workspace_bytes(shape, batch: int, max_seq_len: int) -> int:
@@ -198,17 +262,45 @@ def oscar_decode_workspace_bytes(shape, batch: int, max_seq_len: int) -> int:
     return int(n)
 
 
+def _decode_checks(shape, r_k, r_v, q, seq_lens, block_table, pool, win_k, win_v, out, lead=()):
+    hkv, hq = shape.n_kv_heads, shape.n_q_heads
+    _want(q, (*lead, None, hq, HEAD_DIM), "q")
+    batch = int(q.shape[len(lead)])
+    _want(r_k, (*lead, hkv, HEAD_DIM, HEAD_DIM), "r_k")
+    _want(r_v, (*lead, hkv, HEAD_DIM, HEAD_DIM), "r_v")
+    _want(seq_lens, (batch,), "seq_lens")
+    _want(block_table, ((">=", batch), None), "block_table")
+    _want(pool, (*lead, None, hkv, block_bytes(shape.group_size)), "pool")
+    _check_rings(shape, win_k, win_v, batch, lead)
+    _want(out, (*lead, batch, hq, HEAD_DIM), "out")
+    return batch
+
+
+def _decode_args(shape, r_k, r_v, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v, out, workspace,
+                 stream):
+    b16, i32, u8, f32 = _dt()
+    batch = _decode_checks(shape, r_k, r_v, q, seq_lens, block_table, pool, win_k, win_v, out)
+    return (C.byref(shape), _dev(r_k, b16, "r_k"), _dev(r_v, b16, "r_v"), _dev(q, b16, "q"), batch,
+            _dev(seq_lens, i32, "seq_lens"), int(max_seq_len), _dev(block_table, i32, "block_table"),
+            int(block_table.shape[1]), _dev(pool, u8, "pool"), int(pool.shape[0]), _dev(win_k, b16, "win_k"),
+            _dev(win_v, b16, "win_v"), _dev(out, f32, "out"), _dev(workspace, u8, "workspace"),
+            int(workspace.numel()), _stream(stream))
+
+
 def oscar_decode_attn(shape, r_k, r_v, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v,
                       out, workspace, stream=None) -> None:
-    b16, i32, u8, f32 = _dt()
-    _check_pool(shape, pool)
     _check("oscar_decode_attn", lib.oscar_decode_attn(
-        C.byref(shape), _dev(r_k, b16, "r_k"), _dev(r_v, b16, "r_v"), _dev(q, b16, "q"),
-        int(q.shape[0]), _dev(seq_lens, i32, "seq_lens"), int(max_seq_len),
-        _dev(block_table, i32, "block_table"), int(block_table.shape[1]), _dev(pool, u8, "pool"),
-        int(pool.shape[0]), _dev(win_k, b16, "win_k"), _dev(win_v, b16, "win_v"),
-        _dev(out, f32, "out"), _dev(workspace, u8, "workspace"), int(workspace.numel()),
-        _stream(stream)))
+        *_decode_args(shape, r_k, r_v, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v, out, workspace,
+                      stream)))
+
+
+def oscar_decode_attn_timed(shape, r_k, r_v, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v,
+                            out, workspace, start, stop, stream=None) -> None:
+    """oscar_decode_attn with the Event pair (start, stop) attached to the INT2
+    split kernel's dispatch."""
+    _check("oscar_decode_attn_timed", lib.oscar_decode_attn_timed(
+        *_decode_args(shape, r_k, r_v, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v, out, workspace,
+                      stream), start.handle, stop.handle))
 
 
 def oscar_quantize_append_layers(shape, r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,
@@ -216,12 +308,10 @@ def oscar_quantize_append_layers(shape, r_k, r_v, k_new, v_new, seq_idx, pos, bl
     """Layer-batched append: r_k, r_v [L][Hkv][128][128]; k_new, v_new
     [L][T][Hkv][128]; pool [L][n_pages][Hkv][block]; rings [L][B][W + S][Hkv][128]."""
     b16, i32, u8, _ = _dt()
+    _want(pool, (None, None, shape.n_kv_heads, block_bytes(shape.group_size)), "pool")
     n_layers = int(pool.shape[0])
-    for name, t in (("r_k", r_k), ("r_v", r_v), ("k_new", k_new), ("v_new", v_new)):
-        if t.shape[0] != n_layers:
-            raise ValueError(f"{name}: leading (layer) dimension must be {n_layers}")
-    if pool.dim() != 4 or pool.shape[2] != shape.n_kv_heads or pool.shape[3] != block_bytes(shape.group_size):
-        raise ValueError("pool must be [L][n_pages][Hkv][block bytes]")
+    _append_checks(shape, r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after, pool, win_k, win_v,
+                   lead=(n_layers,))
     _check("oscar_quantize_append_layers", lib.oscar_quantize_append_layers(
         C.byref(shape), n_layers, _dev(r_k, b16, "r_k"), _dev(r_v, b16, "r_v"), _dev(k_new, b16, "k_new"),
         _dev(v_new, b16, "v_new"), int(k_new.shape[1]), _dev(seq_idx, i32, "seq_idx"),
@@ -242,12 +332,9 @@ def oscar_decode_attn_layers(shape, r_k, r_v, q, seq_lens, max_seq_len, block_ta
     """Layer-batched decode: q [L][B][Hq][128], out [L][B][Hq][128] float32,
     other per-layer buffers stacked as for oscar_quantize_append_layers."""
     b16, i32, u8, f32 = _dt()
+    _want(pool, (None, None, shape.n_kv_heads, block_bytes(shape.group_size)), "pool")
     n_layers = int(pool.shape[0])
-    for name, t in (("r_k", r_k), ("r_v", r_v), ("q", q), ("out", out)):
-        if t.shape[0] != n_layers:
-            raise ValueError(f"{name}: leading (layer) dimension must be {n_layers}")
-    if pool.dim() != 4 or pool.shape[2] != shape.n_kv_heads or pool.shape[3] != block_bytes(shape.group_size):
-        raise ValueError("pool must be [L][n_pages][Hkv][block bytes]")
+    _decode_checks(shape, r_k, r_v, q, seq_lens, block_table, pool, win_k, win_v, out, lead=(n_layers,))
     _check("oscar_decode_attn_layers", lib.oscar_decode_attn_layers(
         C.byref(shape), n_layers, _dev(r_k, b16, "r_k"), _dev(r_v, b16, "r_v"), _dev(q, b16, "q"),
         int(q.shape[1]), _dev(seq_lens, i32, "seq_lens"), int(max_seq_len),
@@ -259,28 +346,76 @@ def oscar_decode_attn_layers(shape, r_k, r_v, q, seq_lens, max_seq_len, block_ta
 
 def oscar_bf16_append(shape, k_new, v_new, seq_idx, pos, block_table, kv_pool, stream=None) -> None:
     b16, i32, _, _ = _dt()
+    hkv = shape.n_kv_heads
+    _want(k_new, (None, hkv, HEAD_DIM), "k_new")
+    n_tokens = int(k_new.shape[0])
+    _want(v_new, (n_tokens, hkv, HEAD_DIM), "v_new")
+    _want(seq_idx, (n_tokens,), "seq_idx")
+    _want(pos, (n_tokens,), "pos")
+    _want(block_table, (None, None), "block_table")
+    _want(kv_pool, (None, hkv, BF16_BLOCK_ELEMS), "kv_pool")
     _check("oscar_bf16_append", lib.oscar_bf16_append(
-        C.byref(shape), _dev(k_new, b16, "k_new"), _dev(v_new, b16, "v_new"), int(k_new.shape[0]),
+        C.byref(shape), _dev(k_new, b16, "k_new"), _dev(v_new, b16, "v_new"), n_tokens,
         _dev(seq_idx, i32, "seq_idx"), _dev(pos, i32, "pos"), int(block_table.shape[0]),
         _dev(block_table, i32, "block_table"), int(block_table.shape[1]),
         _dev(kv_pool, b16, "kv_pool"), int(kv_pool.shape[0]), _stream(stream)))
 
 
+def _bf16_decode_args(shape, q, seq_lens, max_seq_len, block_table, kv_pool, out, workspace, stream):
+    b16, i32, u8, f32 = _dt()
+    hq = shape.n_q_heads
+    _want(q, (None, hq, HEAD_DIM), "q")
+    batch = int(q.shape[0])
+    _want(seq_lens, (batch,), "seq_lens")
+    _want(block_table, ((">=", batch), None), "block_table")
+    _want(kv_pool, (None, shape.n_kv_heads, BF16_BLOCK_ELEMS), "kv_pool")
+    _want(out, (batch, hq, HEAD_DIM), "out")
+    return (C.byref(shape), _dev(q, b16, "q"), batch, _dev(seq_lens, i32, "seq_lens"), int(max_seq_len),
+            _dev(block_table, i32, "block_table"), int(block_table.shape[1]), _dev(kv_pool, b16, "kv_pool"),
+            int(kv_pool.shape[0]), _dev(out, f32, "out"), _dev(workspace, u8, "workspace"), int(workspace.numel()),
+            _stream(stream))
+
+
 def oscar_bf16_decode_attn(shape, q, seq_lens, max_seq_len, block_table, kv_pool, out, workspace,
                            stream=None) -> None:
-    b16, i32, u8, f32 = _dt()
     _check("oscar_bf16_decode_attn", lib.oscar_bf16_decode_attn(
-        C.byref(shape), _dev(q, b16, "q"), int(q.shape[0]), _dev(seq_lens, i32, "seq_lens"),
-        int(max_seq_len), _dev(block_table, i32, "block_table"), int(block_table.shape[1]),
-        _dev(kv_pool, b16, "kv_pool"), int(kv_pool.shape[0]), _dev(out, f32, "out"),
-        _dev(workspace, u8, "workspace"), int(workspace.numel()), _stream(stream)))
+        *_bf16_decode_args(shape, q, seq_lens, max_seq_len, block_table, kv_pool, out, workspace, stream)))
+
+
+def oscar_bf16_decode_attn_timed(shape, q, seq_lens, max_seq_len, block_table, kv_pool, out, workspace, start,
+                                 stop, stream=None) -> None:
+    _check("oscar_bf16_decode_attn_timed", lib.oscar_bf16_decode_attn_timed(
+        *_bf16_decode_args(shape, q, seq_lens, max_seq_len, block_table, kv_pool, out, workspace, stream),
+        start.handle, stop.handle))
 
 
 def oscar_hbm_copy(src, dst, nbytes: int | None = None, stream=None) -> None:
     n = int(src.numel() * src.element_size()) if nbytes is None else int(nbytes)
     if src.device.type != "cuda" or dst.device.type != "cuda":
         raise ValueError("oscar_hbm_copy: tensors must be on the GPU")
+    if n > src.numel() * src.element_size() or n > dst.numel() * dst.element_size():
+        raise ValueError("oscar_hbm_copy: nbytes exceeds a buffer")
     _check("oscar_hbm_copy", lib.oscar_hbm_copy(src.data_ptr(), dst.data_ptr(), n, _stream(stream)))
+
+
+def oscar_hbm_read(src, block_bytes_: int, blocks, n_blocks: int, sink, n_workgroups: int = 0, stream=None) -> None:
+    """Read probe: n_blocks blocks of block_bytes_ from the device buffer src,
+    block i at blocks[i] (int32 device tensor) or, with blocks None, at i;
+    sink: int32/uint32 device tensor of at least n_workgroups (0: 8 per CU) words."""
+    _, i32, _, _ = _dt()
+    import torch
+
+    nbytes = src.numel() * src.element_size()
+    if blocks is None:
+        if n_blocks * block_bytes_ > nbytes:
+            raise ValueError("oscar_hbm_read: the blocks exceed src")
+    else:
+        _want(blocks, ((">=", n_blocks),), "blocks")
+    if sink.dtype not in (torch.int32, torch.uint32) or sink.device.type != "cuda":
+        raise TypeError("sink: int32 device tensor")
+    _check("oscar_hbm_read", lib.oscar_hbm_read(
+        src.data_ptr(), int(block_bytes_), _dev(blocks, i32, "blocks"), int(n_blocks), sink.data_ptr(),
+        int(n_workgroups), _stream(stream)))
 
 
 def oscar_gpu_wait(microseconds: int, stream=None) -> None:
@@ -288,17 +423,25 @@ def oscar_gpu_wait(microseconds: int, stream=None) -> None:
     _check("oscar_gpu_wait", lib.oscar_gpu_wait(int(microseconds), _stream(stream)))
 
 
-def oscar_timing_begin(capacity: int) -> None:
-    _check("oscar_timing_begin", lib.oscar_timing_begin(int(capacity)))
+class Event:
+    """A HIP event owned by the caller (oscar_event_create).  Pass a pair to the
+    *_timed entry points; ``elapsed_ms(start, stop)`` waits for stop."""
 
+    def __init__(self):
+        h = C.c_void_p()
+        _check("oscar_event_create", lib.oscar_event_create(C.byref(h)))
+        self.handle = h.value
 
-def oscar_timing_end(capacity: int):
-    """Returns (ms, kinds) lists for the recorded main-kernel launches."""
-    ms = (C.c_float * capacity)()
-    kinds = (C.c_int32 * capacity)()
-    n = C.c_int32(0)
-    _check("oscar_timing_end", lib.oscar_timing_end(ms, kinds, int(capacity), C.byref(n)))
-    return list(ms[:n.value]), list(kinds[:n.value])
+    def __del__(self):
+        h, self.handle = getattr(self, "handle", None), None
+        if h:
+            lib.oscar_event_destroy(h)
+
+    @staticmethod
+    def elapsed_ms(start: "Event", stop: "Event") -> float:
+        ms = C.c_float()
+        _check("oscar_event_elapsed_ms", lib.oscar_event_elapsed_ms(start.handle, stop.handle, C.byref(ms)))
+        return float(ms.value)
 
 
 def oscar_strerror(status: int) -> str:

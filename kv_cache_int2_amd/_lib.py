@@ -41,9 +41,14 @@ SIGNATURES = {
     "oscar_bf16_append": (C.c_int, [SHAPE, P, P, I64, P, P, I32, P, I32, P, I64, P]),
     "oscar_bf16_decode_attn": (C.c_int, [SHAPE, P, I32, P, I32, P, I32, P, I64, P, P, SZ, P]),
     "oscar_hbm_copy": (C.c_int, [P, P, SZ, P]),
+    "oscar_hbm_read": (C.c_int, [P, I64, P, I64, P, I32, P]),
     "oscar_gpu_wait": (C.c_int, [I64, P]),
-    "oscar_timing_begin": (C.c_int, [I32]),
-    "oscar_timing_end": (C.c_int, [P, P, I32, C.POINTER(I32)]),
+    "oscar_event_create": (C.c_int, [C.POINTER(P)]),
+    "oscar_event_destroy": (C.c_int, [P]),
+    "oscar_event_elapsed_ms": (C.c_int, [P, P, C.POINTER(C.c_float)]),
+    "oscar_quantize_append_timed": (C.c_int, [SHAPE, P, P, P, P, I64, P, P, I32, P, I32, P, P, I64, P, P, P, P, P]),
+    "oscar_decode_attn_timed": (C.c_int, [SHAPE, P, P, P, I32, P, I32, P, I32, P, I64, P, P, P, P, SZ, P, P, P]),
+    "oscar_bf16_decode_attn_timed": (C.c_int, [SHAPE, P, I32, P, I32, P, I32, P, I64, P, P, SZ, P, P, P]),
     "oscar_strerror": (C.c_char_p, [C.c_int]),
 }
 

@@ -424,15 +424,17 @@ __global__ __launch_bounds__(256, 4) void append_kernel(AppendParams p) {
 }  // namespace
 }  // namespace oscar
 
-extern "C" int oscar_quantize_append_layers(const oscar_shape* shape, int32_t n_layers, const uint16_t* r_k,
-                                            const uint16_t* r_v, const uint16_t* k_new, const uint16_t* v_new,
-                                            int64_t n_tokens, const int32_t* seq_idx, const int32_t* pos,
-                                            int32_t batch, const int32_t* block_table, int32_t max_pages_per_seq,
-                                            const int32_t* seq_len_after, uint8_t* pool, int64_t n_pages,
-                                            uint16_t* win_k, uint16_t* win_v, void* stream) {
-  using namespace oscar;
+namespace oscar {
+namespace {
+
+int append_impl(const oscar_shape* shape, int32_t n_layers, const uint16_t* r_k, const uint16_t* r_v,
+                const uint16_t* k_new, const uint16_t* v_new, int64_t n_tokens, const int32_t* seq_idx,
+                const int32_t* pos, int32_t batch, const int32_t* block_table, int32_t max_pages_per_seq,
+                const int32_t* seq_len_after, uint8_t* pool, int64_t n_pages, uint16_t* win_k, uint16_t* win_v,
+                void* stream, TimedLaunch tl) {
   int st = check_shape(shape);
   if (st != OSCAR_OK) return st;
+  if (check_events(tl) != OSCAR_OK) return OSCAR_EINVAL;
   if (n_tokens < 0 || batch < 1 || max_pages_per_seq < 1 || n_pages < 1) return OSCAR_EINVAL;
   if (n_layers < 1 || n_layers > 32767) return OSCAR_EINVAL;
   if (n_tokens == 0) return OSCAR_OK;
@@ -473,7 +475,6 @@ extern "C" int oscar_quantize_append_layers(const oscar_shape* shape, int32_t n_
   p.tiles_per_wg = tiles >= 512 ? 4 : (tiles >= 128 ? 2 : 1);
   dim3 grid((unsigned)((tiles + p.tiles_per_wg - 1) / p.tiles_per_wg), (unsigned)p.hkv, 2 * (unsigned)n_layers);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const TimedLaunch tl = timing_events(3);
   const bool one = p.tiles_per_wg == 1;
   auto go = [&](auto kernel) { hipExtLaunchKernelGGL(kernel, grid, dim3(256), 0, s, tl.start, tl.stop, 0, p); };
   switch (kD / shape->group_size) {
@@ -484,12 +485,39 @@ extern "C" int oscar_quantize_append_layers(const oscar_shape* shape, int32_t n_
   return hipGetLastError() == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
 }
 
+}  // namespace
+}  // namespace oscar
+
+extern "C" int oscar_quantize_append_layers(const oscar_shape* shape, int32_t n_layers, const uint16_t* r_k,
+                                            const uint16_t* r_v, const uint16_t* k_new, const uint16_t* v_new,
+                                            int64_t n_tokens, const int32_t* seq_idx, const int32_t* pos,
+                                            int32_t batch, const int32_t* block_table, int32_t max_pages_per_seq,
+                                            const int32_t* seq_len_after, uint8_t* pool, int64_t n_pages,
+                                            uint16_t* win_k, uint16_t* win_v, void* stream) {
+  return oscar::append_impl(shape, n_layers, r_k, r_v, k_new, v_new, n_tokens, seq_idx, pos, batch, block_table,
+                            max_pages_per_seq, seq_len_after, pool, n_pages, win_k, win_v, stream,
+                            oscar::TimedLaunch{nullptr, nullptr});
+}
+
 extern "C" int oscar_quantize_append(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
                                      const uint16_t* k_new, const uint16_t* v_new, int64_t n_tokens,
                                      const int32_t* seq_idx, const int32_t* pos, int32_t batch,
                                      const int32_t* block_table, int32_t max_pages_per_seq,
                                      const int32_t* seq_len_after, uint8_t* pool, int64_t n_pages,
                                      uint16_t* win_k, uint16_t* win_v, void* stream) {
-  return oscar_quantize_append_layers(shape, 1, r_k, r_v, k_new, v_new, n_tokens, seq_idx, pos, batch, block_table,
-                                      max_pages_per_seq, seq_len_after, pool, n_pages, win_k, win_v, stream);
+  return oscar::append_impl(shape, 1, r_k, r_v, k_new, v_new, n_tokens, seq_idx, pos, batch, block_table,
+                            max_pages_per_seq, seq_len_after, pool, n_pages, win_k, win_v, stream,
+                            oscar::TimedLaunch{nullptr, nullptr});
+}
+
+extern "C" int oscar_quantize_append_timed(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
+                                           const uint16_t* k_new, const uint16_t* v_new, int64_t n_tokens,
+                                           const int32_t* seq_idx, const int32_t* pos, int32_t batch,
+                                           const int32_t* block_table, int32_t max_pages_per_seq,
+                                           const int32_t* seq_len_after, uint8_t* pool, int64_t n_pages,
+                                           uint16_t* win_k, uint16_t* win_v, void* stream, void* ev_start,
+                                           void* ev_stop) {
+  return oscar::append_impl(shape, 1, r_k, r_v, k_new, v_new, n_tokens, seq_idx, pos, batch, block_table,
+                            max_pages_per_seq, seq_len_after, pool, n_pages, win_k, win_v, stream,
+                            oscar::TimedLaunch{static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop)});
 }

@@ -102,14 +102,16 @@ struct WorkspaceLayout {
 // n_layers > 1 (INT2 only): the per-layer regions (qsum, qop, wpart) repeat
 // for every layer; the split partials and the tile prefix cover the units of
 // all layers.  The stride of a per-layer region is its size rounded to 256 B.
+// int2_only: the partials region sized for the INT2 decode alone (the bf16
+// comparator's split partials left out).
 inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads, int window, int n_sink, int ng,
-                                        const SplitPlan& p, int n_cu, int n_layers = 1) {
+                                        const SplitPlan& p, int n_cu, int n_layers = 1, bool int2_only = false) {
   const int gqa = n_q_heads / n_kv_heads;
   const size_t g4 = (size_t)((gqa + 3) / 4);
   const size_t gw = (size_t)int2_unit_heads(gqa, ng);
   const size_t L = (size_t)n_layers;
   const size_t units = L * batch * n_q_heads / (gw * (size_t)split_heads_per_wg(n_kv_heads));
-  const size_t part_bf16 = (size_t)batch * n_q_heads * p.n_splits * kPartStride;
+  const size_t part_bf16 = int2_only ? 0 : (size_t)batch * n_q_heads * p.n_splits * kPartStride;
   const size_t n_wg = (size_t)split_wg_count(gqa, n_cu);
   const size_t part_int2 = (n_wg + units) * 4 * gw * kPartStride;
   WorkspaceLayout w{};
@@ -125,14 +127,25 @@ inline WorkspaceLayout workspace_layout(int batch, int n_q_heads, int n_kv_heads
   return w;
 }
 
-// Event pair of the next main-kernel launch while timing is on (measurement
-// only), else two null events.  The kernel is launched with
-// hipExtLaunchKernelGGL, which stamps the events at the dispatch's own start
-// and end, so the pair spans the kernel and nothing queued around it.
+// Event pair attached to the dispatch of a call's main kernel (both null when
+// the call is not timed).  The kernel is launched with hipExtLaunchKernelGGL,
+// which stamps the events at the dispatch's own start and end, so the pair
+// spans the kernel and nothing queued around it.
 struct TimedLaunch {
   hipEvent_t start, stop;
 };
-TimedLaunch timing_events(int kind);
+// OSCAR_OK when both events or neither are given.
+int check_events(const TimedLaunch& t);
+
+// One decode call (INT2 with int2 set, else the bf16 comparator): argument
+// checks, split plan, workspace layout (int2_only: without the comparator's
+// partials) and the launches on `stream`.  Returns an oscar_status.
+int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
+                  const uint16_t* q, int32_t batch, const int32_t* seq_lens, int32_t max_seq_len,
+                  const int32_t* block_table, int32_t max_pages_per_seq, const uint8_t* pool,
+                  const uint16_t* kv_pool, int64_t n_pages, const uint16_t* win_k, const uint16_t* win_v,
+                  float* out, void* workspace, size_t workspace_bytes, void* stream, int n_layers = 1,
+                  TimedLaunch tl = TimedLaunch{nullptr, nullptr}, bool int2_only = false);
 
 }  // namespace oscar
 

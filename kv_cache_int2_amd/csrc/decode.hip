@@ -1338,13 +1338,12 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p0, int gq, int 
 }
 
 template <int G>
-int launch_decode(bool int2, const SplitParams& sp, const uint16_t* r_k, int batch, hipStream_t s) {
+int launch_decode(bool int2, const SplitParams& sp, const uint16_t* r_k, int batch, hipStream_t s, TimedLaunch tl) {
   if (int2) {
     // z = 0: rotated query and its MFMA operands, the tile prefix; z > 0: the bf16 window chunks
     prep_kernel<G><<<dim3(batch * sp.n_layers, sp.hkv, 1 + sp.n_wchunks), 256, 0, s>>>(sp, r_k);
     if (hipGetLastError() != hipSuccess) return OSCAR_EHIP;
   }
-  const TimedLaunch tl = timing_events(int2 ? 1 : 2);
   if (int2) {
     constexpr int GW = G > 8 ? 8 : (G < 4 ? 4 : G);  // whole-token groups; 4 heads with finer groups
     auto go = [&](auto kernel) { hipExtLaunchKernelGGL(kernel, dim3(sp.n_wg), dim3(256), 0, s, tl.start, tl.stop, 0, sp); };
@@ -1368,13 +1367,19 @@ int launch_decode(bool int2, const SplitParams& sp, const uint16_t* r_k, int bat
   return hipGetLastError() == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
 }
 
+}  // namespace
+
+// Validation, split plan, workspace layout and the three launches of a decode
+// call (declared in common.h).
 int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
                   const uint16_t* q, int32_t batch, const int32_t* seq_lens, int32_t max_seq_len,
                   const int32_t* block_table, int32_t max_pages_per_seq, const uint8_t* pool,
                   const uint16_t* kv_pool, int64_t n_pages, const uint16_t* win_k, const uint16_t* win_v,
-                  float* out, void* workspace, size_t workspace_bytes, void* stream, int n_layers = 1) {
+                  float* out, void* workspace, size_t workspace_bytes, void* stream, int n_layers, TimedLaunch tl,
+                  bool int2_only) {
   int st = check_shape(shape);
   if (st != OSCAR_OK) return st;
+  if (check_events(tl) != OSCAR_OK) return OSCAR_EINVAL;
   if (batch < 1 || max_seq_len < 0 || max_pages_per_seq < 1 || n_pages < 1) return OSCAR_EINVAL;
   if (n_layers < 1 || (!int2 && n_layers != 1) || (int64_t)n_layers * batch > 65535) return OSCAR_EINVAL;
   if (!q || !seq_lens || !block_table || !out || !workspace) return OSCAR_EINVAL;
@@ -1386,7 +1391,7 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   const int n_cu = device_cu_count();
   const SplitPlan plan = plan_splits(batch, shape->n_kv_heads, gqa, max_seq_len, n_cu);
   const WorkspaceLayout wl = workspace_layout(batch, shape->n_q_heads, shape->n_kv_heads, shape->window, shape->n_sink,
-                                              kD / shape->group_size, plan, n_cu, n_layers);
+                                              kD / shape->group_size, plan, n_cu, n_layers, int2_only);
   if (workspace_bytes < wl.total) return OSCAR_ENOSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return OSCAR_EINVAL;
   // rows are read as 16-byte vectors
@@ -1455,14 +1460,16 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   sp.scale_log2 = kLog2e / sqrtf((float)kD);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (shape->n_q_heads / shape->n_kv_heads) {
-    case 1: return launch_decode<1>(int2, sp, r_k, batch, s);
-    case 2: return launch_decode<2>(int2, sp, r_k, batch, s);
-    case 4: return launch_decode<4>(int2, sp, r_k, batch, s);
-    case 8: return launch_decode<8>(int2, sp, r_k, batch, s);
-    case 16: return launch_decode<16>(int2, sp, r_k, batch, s);
+    case 1: return launch_decode<1>(int2, sp, r_k, batch, s, tl);
+    case 2: return launch_decode<2>(int2, sp, r_k, batch, s, tl);
+    case 4: return launch_decode<4>(int2, sp, r_k, batch, s, tl);
+    case 8: return launch_decode<8>(int2, sp, r_k, batch, s, tl);
+    case 16: return launch_decode<16>(int2, sp, r_k, batch, s, tl);
   }
   return OSCAR_EUNSUPPORTED;
 }
+
+namespace {
 
 // bf16 comparator append: K rows into [page][Hkv] elements [16 slot][128],
 // V into the transposed part, element 2048 + 16 c + slot.
@@ -1569,4 +1576,27 @@ extern "C" int oscar_bf16_append(const oscar_shape* shape, const uint16_t* k_new
       k_new, v_new, n_tokens, seq_idx, pos, batch, block_table, max_pages_per_seq, kv_pool, n_pages,
       shape->n_kv_heads);
   return hipGetLastError() == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
+}
+
+extern "C" int oscar_decode_attn_timed(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
+                                       const uint16_t* q, int32_t batch, const int32_t* seq_lens,
+                                       int32_t max_seq_len, const int32_t* block_table, int32_t max_pages_per_seq,
+                                       const uint8_t* pool, int64_t n_pages, const uint16_t* win_k,
+                                       const uint16_t* win_v, float* out, void* workspace, size_t workspace_bytes,
+                                       void* stream, void* ev_start, void* ev_stop) {
+  return oscar::decode_common(true, shape, r_k, r_v, q, batch, seq_lens, max_seq_len, block_table,
+                              max_pages_per_seq, pool, nullptr, n_pages, win_k, win_v, out, workspace,
+                              workspace_bytes, stream, 1,
+                              oscar::TimedLaunch{static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop)});
+}
+
+extern "C" int oscar_bf16_decode_attn_timed(const oscar_shape* shape, const uint16_t* q, int32_t batch,
+                                            const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
+                                            int32_t max_pages_per_seq, const uint16_t* kv_pool, int64_t n_pages,
+                                            float* out, void* workspace, size_t workspace_bytes, void* stream,
+                                            void* ev_start, void* ev_stop) {
+  return oscar::decode_common(false, shape, nullptr, nullptr, q, batch, seq_lens, max_seq_len, block_table,
+                              max_pages_per_seq, nullptr, kv_pool, n_pages, nullptr, nullptr, out, workspace,
+                              workspace_bytes, stream, 1,
+                              oscar::TimedLaunch{static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop)});
 }

@@ -1,27 +1,64 @@
 // Measurement helpers, the device's compute-unit count and status strings: a
-// streaming copy kernel (HBM probe and the known-size reference for HBM traffic
-// counters), a timed wait kernel that holds a stream without touching memory,
-// and opt-in event pairs attached to the dispatch of the main kernel of each
-// append / decode call.
-#include <vector>
-
+// streaming copy kernel (the known-size reference for HBM traffic counters), a
+// streaming read kernel over whole or scattered blocks (the in-session HBM
+// ceilings of the decode's access shapes), a timed wait kernel that holds a
+// stream without touching memory, and thin wrappers of HIP events for the
+// timed entry points.  The library keeps no timing state of its own: the
+// caller creates the events and passes them to each timed call.
 #include "common.h"
 
 namespace oscar {
 namespace {
 
-struct Timing {
-  bool on = false;
-  int capacity = 0;
-  int used = 0;
-  std::vector<hipEvent_t> start, stop;
-  std::vector<int> kind;
-};
-Timing g_timing;
-
 __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
+// Read probe.  The blocks (cpb 16-byte chunks each) are concatenated in table
+// order and workgroup w reads the chunks [w N / nw, (w + 1) N / nw) of that
+// stream, 8 loads of 16 bytes in flight per thread; chunk c lies in block
+// c / cpb of the table (found in fp64, exact after one correction since the
+// quotient is off by less than one).  Without a table, chunk c is src[c].  The
+// XOR of everything a workgroup read goes to sink[w], so no load can be dropped.
+constexpr int kReadUnroll = 8;
+__global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ src, const int32_t* __restrict__ blocks,
+                                                   int64_t n_blocks, int cpb, double inv_cpb,
+                                                   uint32_t* __restrict__ sink) {
+  const int64_t N = n_blocks * cpb;
+  const int64_t lo = N * blockIdx.x / gridDim.x, hi = N * (blockIdx.x + 1) / gridDim.x;
+  uint32_t x = 0;
+  for (int64_t c0 = lo + threadIdx.x; c0 < hi; c0 += 256 * kReadUnroll) {
+    uint4 v[kReadUnroll];
+#pragma unroll
+    for (int j = 0; j < kReadUnroll; ++j) {
+      const int64_t c = c0 + 256 * j;
+      const int64_t cc = c < hi ? c : hi - 1;  // a clamped duplicate past the range is read but not used
+      int64_t at = cc;
+      if (blocks) {
+        int64_t blk = (int64_t)((double)cc * inv_cpb);
+        int64_t off = cc - blk * cpb;
+        if (off < 0) {
+          blk -= 1;
+          off += cpb;
+        } else if (off >= cpb) {
+          blk += 1;
+          off -= cpb;
+        }
+        at = (int64_t)blocks[blk] * cpb + off;
+      }
+      v[j] = src[at];
+    }
+#pragma unroll
+    for (int j = 0; j < kReadUnroll; ++j)
+      x ^= c0 + 256 * j < hi ? (v[j].x ^ v[j].y ^ v[j].z ^ v[j].w) : 0u;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x ^= (uint32_t)__shfl_xor((int)x, o);
+  __shared__ uint32_t red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
 // One wave that returns once `ticks` of the constant-rate wall clock have
@@ -50,59 +87,31 @@ int device_cu_count() {
   return n;
 }
 
-TimedLaunch timing_events(int kind) {
-  TimedLaunch t{nullptr, nullptr};
-  if (!g_timing.on || g_timing.used >= g_timing.capacity) return t;
-  const int slot = g_timing.used++;
-  g_timing.kind[slot] = kind;
-  t.start = g_timing.start[slot];
-  t.stop = g_timing.stop[slot];
-  return t;
+int check_events(const TimedLaunch& t) {
+  return (t.start == nullptr) == (t.stop == nullptr) ? OSCAR_OK : OSCAR_EINVAL;
 }
 
 }  // namespace oscar
 
-extern "C" int oscar_timing_begin(int32_t capacity) {
-  using oscar::g_timing;
-  if (capacity < 1 || g_timing.on) return OSCAR_EINVAL;
-  g_timing.start.assign(capacity, nullptr);
-  g_timing.stop.assign(capacity, nullptr);
-  g_timing.kind.assign(capacity, 0);
-  for (int i = 0; i < capacity; ++i) {
-    if (hipEventCreate(&g_timing.start[i]) != hipSuccess || hipEventCreate(&g_timing.stop[i]) != hipSuccess)
-      return OSCAR_EHIP;
-  }
-  g_timing.capacity = capacity;
-  g_timing.used = 0;
-  g_timing.on = true;
+extern "C" int oscar_event_create(void** event) {
+  if (!event) return OSCAR_EINVAL;
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return OSCAR_EHIP;
+  *event = e;
   return OSCAR_OK;
 }
 
-extern "C" int oscar_timing_end(float* ms, int32_t* kinds, int32_t capacity, int32_t* n) {
-  using oscar::g_timing;
-  if (!g_timing.on) return OSCAR_EINVAL;
-  int status = OSCAR_OK;
-  int k = 0;
-  for (int i = 0; i < g_timing.used; ++i) {
-    if (hipEventSynchronize(g_timing.stop[i]) != hipSuccess) {
-      status = OSCAR_EHIP;
-      continue;
-    }
-    float t = 0.f;
-    if (hipEventElapsedTime(&t, g_timing.start[i], g_timing.stop[i]) != hipSuccess) status = OSCAR_EHIP;
-    if (ms && kinds && k < capacity) {
-      ms[k] = t;
-      kinds[k] = g_timing.kind[i];
-      ++k;
-    }
-  }
-  if (n) *n = k;
-  for (int i = 0; i < g_timing.capacity; ++i) {
-    (void)hipEventDestroy(g_timing.start[i]);
-    (void)hipEventDestroy(g_timing.stop[i]);
-  }
-  g_timing = oscar::Timing{};
-  return status;
+extern "C" int oscar_event_destroy(void* event) {
+  if (!event) return OSCAR_EINVAL;
+  return hipEventDestroy(static_cast<hipEvent_t>(event)) == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
+}
+
+extern "C" int oscar_event_elapsed_ms(void* start, void* stop, float* ms) {
+  if (!start || !stop || !ms) return OSCAR_EINVAL;
+  if (hipEventSynchronize(static_cast<hipEvent_t>(stop)) != hipSuccess) return OSCAR_EHIP;
+  return hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)) == hipSuccess
+             ? OSCAR_OK
+             : OSCAR_EHIP;
 }
 
 extern "C" int oscar_hbm_copy(const void* src, void* dst, size_t bytes, void* stream) {
@@ -114,6 +123,20 @@ extern "C" int oscar_hbm_copy(const void* src, void* dst, size_t bytes, void* st
   if (blocks > 256 * 64) blocks = 256 * 64;
   oscar::copy_kernel<<<(unsigned)blocks, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
       static_cast<const uint4*>(src), static_cast<uint4*>(dst), n);
+  return hipGetLastError() == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
+}
+
+extern "C" int oscar_hbm_read(const void* src, int64_t block_bytes, const int32_t* blocks, int64_t n_blocks,
+                              uint32_t* sink, int32_t n_workgroups, void* stream) {
+  if (!src || !sink || block_bytes < 16 || (block_bytes & 15) || block_bytes > (1 << 20) || n_blocks < 0 ||
+      n_workgroups < 0 || n_workgroups > OSCAR_READ_MAX_WORKGROUPS || (reinterpret_cast<uintptr_t>(src) & 15))
+    return OSCAR_EINVAL;
+  if (n_blocks == 0) return OSCAR_OK;
+  const int cpb = (int)(block_bytes / 16);
+  if (n_blocks > ((int64_t)1 << 40) / cpb) return OSCAR_EINVAL;
+  const int wg = n_workgroups > 0 ? n_workgroups : 8 * oscar::device_cu_count();
+  oscar::read_kernel<<<(unsigned)wg, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint4*>(src), blocks, n_blocks, cpb, 1.0 / (double)cpb, sink);
   return hipGetLastError() == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
 }
 

@@ -95,7 +95,26 @@ def test_host_validation_before_launch():
     assert lib.oscar_gpu_wait(-1, None) == EINVAL
     assert lib.oscar_gpu_wait(10000001, None) == EINVAL
     assert lib.oscar_gpu_wait(0, None) == 0
-    assert lib.oscar_timing_end(None, None, 0, None) == EINVAL
+    # read probe: sizes, alignment, workgroup count
+    sink = C.c_void_p(1024)
+    assert lib.oscar_hbm_read(fake, 1152, None, 0, sink, 0, None) == 0  # nothing to read
+    assert lib.oscar_hbm_read(fake, 1000, None, 1, sink, 0, None) == EINVAL  # not a multiple of 16
+    assert lib.oscar_hbm_read(fake, 0, None, 1, sink, 0, None) == EINVAL
+    assert lib.oscar_hbm_read(fake, (1 << 20) + 16, None, 1, sink, 0, None) == EINVAL
+    assert lib.oscar_hbm_read(C.c_void_p(264), 1152, None, 1, sink, 0, None) == EINVAL  # misaligned
+    assert lib.oscar_hbm_read(fake, 1152, None, 1, None, 0, None) == EINVAL
+    assert lib.oscar_hbm_read(fake, 1152, None, 1, sink, 65537, None) == EINVAL
+    assert lib.oscar_hbm_read(fake, 1152, None, -1, sink, 0, None) == EINVAL
+    # events: null arguments, and a timed call with only one of the two events
+    assert lib.oscar_event_create(None) == EINVAL
+    assert lib.oscar_event_destroy(None) == EINVAL
+    assert lib.oscar_event_elapsed_ms(None, None, None) == EINVAL
+    assert lib.oscar_decode_attn_timed(*args, ws, None, fake, None) == EINVAL
+    assert lib.oscar_decode_attn_timed(*args, ws, None, None, fake) == EINVAL
+    assert lib.oscar_quantize_append_timed(C.byref(good), fake, fake, fake, fake, 1, fake, fake, 1, fake, 1, fake,
+                                           fake, 1, fake, fake, None, fake, None) == EINVAL
+    assert lib.oscar_bf16_decode_attn_timed(C.byref(good), fake, 8, fake, 10, fake, 1, fake, 1, fake, fake,
+                                            1 << 30, None, None, fake) == EINVAL
 
 
 def test_layered_entry_points_validate_on_host():
@@ -179,3 +198,58 @@ def test_calibrate_special_case_diagonal():
     u[perm, np.arange(d)] = 1.0  # eigenvector k is axis perm[k] (energies sorted descending)
     want = ref.apply_bitrev_rows(ref.hadamard(d) / np.sqrt(d) @ u.T)
     assert np.array_equal(rk[0], ref.bf16_bits(want))
+
+
+class _Fake:
+    """Stands in for a device tensor in the binding's shape checks (which run
+    before any pointer is taken)."""
+
+    def __init__(self, *shape):
+        self.shape = tuple(shape)
+
+
+def test_binding_checks_shapes_before_the_call():
+    """The Python binding refuses buffers whose shapes do not fit the shape
+    struct and the derived batch / token counts (an undersized ring or query
+    would otherwise be read or written past its end on the device)."""
+    F = _Fake
+    shape = K.make_shape(32, 8, window=128, n_sink=4)
+    rk = F(8, 128, 128)
+    blk = K.block_bytes(128)
+    good_append = dict(r_k=rk, r_v=rk, k_new=F(10, 8, 128), v_new=F(10, 8, 128), seq_idx=F(10), pos=F(10),
+                       block_table=F(2, 7), seq_len_after=F(2), pool=F(14, 8, blk), win_k=F(2, 132, 8, 128),
+                       win_v=F(2, 132, 8, 128))
+    assert K._append_checks(shape, **good_append) == (10, 2)
+    bad = [("v_new", F(9, 8, 128)), ("pos", F(11)), ("seq_idx", F(10, 1)), ("seq_len_after", F(1)),
+           ("win_k", F(2, 128, 8, 128)),  # ring without the sink rows
+           ("win_v", F(1, 132, 8, 128)),  # fewer sequences than the block table
+           ("pool", F(14, 8, 1280)), ("r_k", F(8, 128, 64)), ("k_new", F(10, 4, 128))]
+    for name, t in bad:
+        kw = dict(good_append, **{name: t})
+        with pytest.raises(ValueError, match=name):
+            K._append_checks(shape, **kw)
+    # an empty append needs no ring
+    empty = dict(good_append, k_new=F(0, 8, 128), v_new=F(0, 8, 128), seq_idx=F(0), pos=F(0), win_k=None,
+                 win_v=None)
+    assert K._append_checks(shape, **empty) == (0, 2)
+
+    good_dec = dict(r_k=rk, r_v=rk, q=F(3, 32, 128), seq_lens=F(3), block_table=F(3, 9), pool=F(20, 8, blk),
+                    win_k=F(3, 132, 8, 128), win_v=F(3, 132, 8, 128), out=F(3, 32, 128))
+    assert K._decode_checks(shape, **good_dec) == 3
+    bad = [("q", F(3, 16, 128)), ("seq_lens", F(2)), ("block_table", F(2, 9)), ("out", F(2, 32, 128)),
+           ("out", F(3, 32, 64)), ("win_k", F(2, 132, 8, 128)), ("win_v", None), ("r_v", F(4, 128, 128))]
+    for name, t in bad:
+        kw = dict(good_dec, **{name: t})
+        with pytest.raises(ValueError, match=name):
+            K._decode_checks(shape, **kw)
+    # layer-batched: every per-layer buffer carries the layer count
+    lay = dict(r_k=F(2, 8, 128, 128), r_v=F(2, 8, 128, 128), q=F(2, 3, 32, 128), seq_lens=F(3),
+               block_table=F(3, 9), pool=F(2, 20, 8, blk), win_k=F(2, 3, 132, 8, 128), win_v=F(2, 3, 132, 8, 128),
+               out=F(2, 3, 32, 128))
+    assert K._decode_checks(shape, lead=(2,), **lay) == 3
+    with pytest.raises(ValueError, match="out"):
+        K._decode_checks(shape, lead=(2,), **dict(lay, out=F(1, 3, 32, 128)))
+    # calibration arrays with a head dim other than 128
+    with pytest.raises(ValueError):
+        K.oscar_calibrate(K.make_shape(32, 8), np.zeros((8, 4, 64), np.float32), np.zeros((8, 4, 64), np.float32),
+                          np.zeros((8, 4, 64), np.float32))
