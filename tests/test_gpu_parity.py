@@ -57,6 +57,22 @@ def rotations(cfg, hkv=8):
     return ref.bf16_bits(rk), ref.bf16_bits(rv)
 
 
+@functools.lru_cache(maxsize=None)
+def arm_rotation(arm, hkv=8):
+    """bf16 bits (r_k, r_v) [Hkv][128][128] of a comparison rotation of the
+    quality harness, the same for keys and values: "hadamard" is the fixed
+    transform alone, P_br (H / sqrt d) (the oracle's Sylvester matrix with
+    bit-reversed rows); "identity" is plain per-token INT2."""
+    if arm == "hadamard":
+        r = ref.apply_bitrev_rows(ref.hadamard()) / np.sqrt(128)
+    elif arm == "identity":
+        r = np.eye(128)
+    else:
+        raise ValueError(arm)
+    bits = np.ascontiguousarray(np.broadcast_to(ref.bf16_bits(r), (hkv, 128, 128)))
+    return bits, bits.copy()
+
+
 def make_spec(cfg, lens, window=128, hq=None, hkv=8, n_sink=0, group=128):
     s = wl.spec(cfg, batch=len(lens))
     s.seq_lens = np.asarray(lens, np.int32)
@@ -99,9 +115,9 @@ def run_append(K, s, rk, rv, k, v, si, ps, bt, pool0, wk0, wv0, lens_after):
     return H(pool), (H(wk, np.uint16) if wk is not None else None), (H(wv, np.uint16) if wv is not None else None)
 
 
-def append_case(K, s, order="inorder", split_at=None, seed=0):
+def append_case(K, s, order="inorder", split_at=None, seed=0, rot=None):
     rng = np.random.default_rng(seed)
-    rk, rv = rotations(s.cfg, s.n_kv_heads)
+    rk, rv = rotations(s.cfg, s.n_kv_heads) if rot is None else rot
     rkf, rvf = ref.bf16_to_f64(rk), ref.bf16_to_f64(rv)
     bt, n_pages = wl.page_table(s)
     pool0 = rng.integers(0, 256, (n_pages, s.n_kv_heads, ref.block_bytes(s.group_size)), dtype=np.uint8)
@@ -190,8 +206,8 @@ def test_append_empty_is_noop(K):
 # decode on oracle-built caches
 # ---------------------------------------------------------------------------
 
-def oracle_cache(s, seed=0):
-    rk, rv = rotations(s.cfg, s.n_kv_heads)
+def oracle_cache(s, seed=0, rot=None):
+    rk, rv = rotations(s.cfg, s.n_kv_heads) if rot is None else rot
     rkf, rvf = ref.bf16_to_f64(rk), ref.bf16_to_f64(rv)
     bt, n_pages = wl.page_table(s)
     rng = np.random.default_rng(seed)
@@ -347,11 +363,13 @@ def test_gpu_wait_holds_the_stream(K):
 # full-size workloads (sampled checks)
 # ---------------------------------------------------------------------------
 
-def full_cache(K, s, keep=()):
-    """Prefill every sequence of workload s through the HIP append; returns the
-    device state and the host token arrays of the sequences in ``keep``."""
+def full_cache(K, s, keep=(), rot=None, tokens=None):
+    """Prefill every sequence of workload s through the HIP append (rotation
+    ``rot``, default the oracle's calibration); returns the device state and the
+    host token arrays of the sequences in ``keep``.  ``tokens(b)``, if given,
+    returns sequence b's (k, v, seq_idx, pos) instead of drawing them."""
     shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window, group_size=s.group_size)
-    rk, rv = rotations(s.cfg)
+    rk, rv = rotations(s.cfg) if rot is None else rot
     rkd, rvd = D(rk), D(rv)
     bt, n_pages = wl.page_table(s)
     btd, lensd = D(bt), D(s.seq_lens)
@@ -360,7 +378,7 @@ def full_cache(K, s, keep=()):
     wv = torch.zeros_like(wk)
     kept = {}
     for b in range(s.batch):
-        k, v, si, ps = wl.prefill_tokens(s, b)
+        k, v, si, ps = wl.prefill_tokens(s, b) if tokens is None else tokens(b)
         K.oscar_quantize_append(shape, rkd, rvd, D(k), D(v), D(si), D(ps), btd, lensd, pool, wk, wv)
         if b in keep:
             kept[b] = (k, v)
@@ -378,23 +396,31 @@ def decode_full(K, s, c, q, lens):
     return H(out)
 
 
-def oracle_overwrite(s, c, b, extra=None):
-    """Encode sequence b with the oracle (its tokens plus ``extra``) and upload
-    the bytes of its pages and its window ring into the device cache, so the
-    device decode of b runs on exactly the oracle's cache.  Returns the oracle's
-    local copy (pool rows of b's pages, window ring) for ``decode_ref``."""
+def oracle_overwrite(s, c, b, extra=None, heads=None):
+    """Encode sequence b with the oracle (its tokens plus ``extra``; the KV heads
+    in ``heads``, default all) and upload those heads' blocks of its pages and
+    their window rows into the device cache, so the device decode of (b, h) runs
+    on exactly the oracle's cache.  Returns the oracle's local copy (pool rows of
+    b's pages, window ring) for ``decode_ref``."""
     k, v = c["kept"][b]
     if extra is not None:
         k = np.concatenate([k, extra[0]])
         v = np.concatenate([v, extra[1]])
+    hs = list(range(s.n_kv_heads)) if heads is None else list(heads)
     n = len(k)
     n_pg = -(-n // 16)
     pages = torch.from_numpy(c["bt"][b][:n_pg].astype(np.int64)).to(DEV)
     local = H(c["pool"].index_select(0, pages))
-    wk = np.zeros((s.window, 8, 128), np.uint16)
-    wv = np.zeros_like(wk)
-    ref.append_sequence_ref(ref.bf16_to_f64(c["rk"]), ref.bf16_to_f64(c["rv"]), k, v, np.arange(n_pg, dtype=np.int32),
-                            local, wk, wv, s.window, group=s.group_size)
+    wk = H(c["wk"][b], np.uint16).copy()
+    wv = H(c["wv"][b], np.uint16).copy()
+    sub = np.ascontiguousarray(local[:, hs])
+    wks, wvs = np.ascontiguousarray(wk[:, hs]), np.ascontiguousarray(wv[:, hs])
+    ref.append_sequence_ref(ref.bf16_to_f64(c["rk"][hs]), ref.bf16_to_f64(c["rv"][hs]),
+                            np.ascontiguousarray(k[:, hs]), np.ascontiguousarray(v[:, hs]),
+                            np.arange(n_pg, dtype=np.int32), sub, wks, wvs, s.window, group=s.group_size)
+    local[:, hs] = sub
+    wk[:, hs] = wks
+    wv[:, hs] = wvs
     c["pool"].index_copy_(0, pages, D(local))
     c["wk"][b] = D(wk)
     c["wv"][b] = D(wv)
@@ -483,16 +509,75 @@ def test_full_config2(K):
     check_sampled(s, c, q, got, [(3, 0), (3, 5), (11, 7)], oracle)
 
 
-def test_full_config3(K):
+@functools.lru_cache(maxsize=1)
+def config3_tokens():
+    """Every sequence's prefill tokens of the long-context workload, drawn once
+    for the tests that build its cache (about 3.3 GB of bf16 on the host)."""
     s = wl.spec(3)
+    return s, {b: wl.prefill_tokens(s, b) for b in range(s.batch)}
+
+
+def test_full_config3(K):
+    """Long-context workload at full size, in the bench's launch configuration:
+    two KV heads of every sequence (one in each group of 4 heads a split
+    workgroup reads side by side, so every merge unit, and with it the share
+    boundaries of every one of its workgroups, is covered) decoded from
+    oracle-encoded blocks and compared with the oracle."""
+    s, toks = config3_tokens()
     log("config 3 full: building cache")
-    c = full_cache(K, s, keep=(2, 7))
+    c = full_cache(K, s, keep=tuple(range(s.batch)), tokens=toks.__getitem__)
     q = wl.decode_queries(s)
     sampled_append_check(s, c, 7, n_sample=512, seed=3)
-    oracle = {b: oracle_overwrite(s, c, b) for b in (2, 7)}
+    pairs = [(b, h) for b in range(s.batch) for h in (b % 4, 4 + (3 * b + 1) % 4)]
+    oracle = {b: oracle_overwrite(s, c, b, heads=[h for bb, h in pairs if bb == b]) for b in range(s.batch)}
     got = decode_full(K, s, c, q, s.seq_lens)
     assert np.isfinite(got).all()
-    check_sampled(s, c, q, got, [(2, 1), (7, 6)], oracle)
+    check_sampled(s, c, q, got, pairs, oracle)
+
+
+@pytest.mark.parametrize("arm", ["hadamard", "identity"])
+def test_arm_append(K, arm):
+    """The quality harness's comparison rotations through the append kernel:
+    codes, scales and zeros under the encoder rule, bf16 ring byte-exact."""
+    append_case(K, make_spec(1, [300, 37, 129], window=100), order="shuffled", seed=11, rot=arm_rotation(arm))
+    append_case(K, make_spec(1, [77, 200], window=0), seed=12, rot=arm_rotation(arm))
+
+
+@pytest.mark.parametrize("arm", ["hadamard", "identity"])
+@pytest.mark.parametrize("cfg,lens,window,hq", [
+    (1, [1000, 777], 128, 32),
+    (5, [600, 129, 128], 128, 64),
+    (1, [4100, 2500, 16], 128, 32),
+    (1, [0, 700], 128, 8),
+])
+def test_arm_decode_small(K, arm, cfg, lens, window, hq):
+    """Decode under the comparison rotations on oracle-built caches, every
+    output compared with the oracle."""
+    s = make_spec(cfg, lens, window, hq)
+    rot = arm_rotation(arm)
+    rk, rv, rkf, rvf, bt, pool, wk, wv, q = oracle_cache(s, rot=rot)
+    got = run_decode(K, s, rk, rv, q, bt, pool, wk, wv)
+    want = ref.decode_ref(rkf, rvf, q, s.seq_lens, bt, pool, wk, wv, window)
+    err = P.attn_rel_err(got, want)
+    log(f"decode {arm} lens={lens} W={window} Hq={hq}: max rel err {err.max():.3e}")
+    assert np.isfinite(got).all()
+    assert err.max() <= P.ATTN_TOL
+
+
+@pytest.mark.parametrize("arm", ["hadamard", "identity"])
+def test_full_config3_arm(K, arm):
+    """Long-context workload at full size under a comparison rotation: sampled
+    append records and sampled (sequence, KV head) outputs against the oracle."""
+    s, toks = config3_tokens()
+    log(f"config 3 full, {arm}: building cache")
+    c = full_cache(K, s, keep=(1, 6), rot=arm_rotation(arm), tokens=toks.__getitem__)
+    q = wl.decode_queries(s)
+    sampled_append_check(s, c, 6, n_sample=256, seed=13)
+    pairs = [(1, 2), (1, 5), (6, 0), (6, 7)]
+    oracle = {b: oracle_overwrite(s, c, b, heads=[h for bb, h in pairs if bb == b]) for b in (1, 6)}
+    got = decode_full(K, s, c, q, s.seq_lens)
+    assert np.isfinite(got).all()
+    check_sampled(s, c, q, got, pairs, oracle)
 
 
 def test_full_config5_two_steps(K):

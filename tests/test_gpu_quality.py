@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 def test_quality_harness_small():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     import kv_cache_int2_amd as K
-    from kv_cache_int2_amd import quality
+    import quality
 
     s = wl.spec(1, batch=2, seq_len=700)
     shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window)
@@ -38,7 +38,7 @@ def test_quality_finer_groups_reduce_error():
     channels per group for every rotation."""
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     import kv_cache_int2_amd as K
-    from kv_cache_int2_amd import quality
+    import quality
 
     s = wl.spec(1, batch=2, seq_len=700)
     shape = K.make_shape(s.n_q_heads, s.n_kv_heads, s.window)

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import workloads as wl
-from kv_cache_int2_amd import quality
+import quality
 from oracle import oscar_ref as ref
 from test_oracle_decode import build, orthogonal
 
