@@ -24,13 +24,15 @@ __all__ = [
     "oscar_strerror", "BLOCK_BYTES", "BF16_BLOCK_ELEMS", "PAGE_SIZE", "HEAD_DIM", "block_bytes",
     "oscar_calibrate_layers", "oscar_rotation_file_bytes", "oscar_rotation_write", "oscar_rotation_read_info",
     "oscar_rotation_read", "oscar_quantize_append_layers", "oscar_decode_layers_workspace_bytes",
-    "oscar_decode_attn_layers",
+    "oscar_decode_attn_layers", "oscar_decode_attn_noalloc", "oscar_decode_noalloc_scratch_bytes",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 BLOCK_BYTES = 1152  # bytes per (page, KV head) block at group size 128
 BF16_BLOCK_ELEMS = 4096  # bf16 comparator pool: K [16][128] then V^T [128][16] per (page, KV head)
 PAGE_SIZE = 16
 HEAD_DIM = 128
+NOALLOC_SCRATCH_BYTES = 32 << 20  # the library's static decode scratch per device
 
 
 class OscarError(RuntimeError):
@@ -51,13 +53,20 @@ def block_bytes(group_size: int = 128) -> int:
     return 1024 + 8 * PAGE_SIZE * (HEAD_DIM // group_size)
 
 
+_SHAPES_SEEN: set = set()
+
+
 def _want(t, dims, name):
     """t must be a tensor/array of len(dims) dimensions; an int entry of dims
     fixes that dimension, a (">=", n) entry bounds it from below, None leaves it
-    free.  Raises ValueError otherwise."""
+    free.  Raises ValueError otherwise.  (Shapes already accepted against the
+    same dims are remembered, so a serving loop pays one set look-up.)"""
     if t is None:
         raise ValueError(f"{name}: missing")
-    shape = tuple(int(x) for x in t.shape)
+    key = (tuple(t.shape), dims)
+    if key in _SHAPES_SEEN:
+        return
+    shape = key[0]
     ok = len(shape) == len(dims)
     if ok:
         for have, want in zip(shape, dims):
@@ -71,6 +80,8 @@ def _want(t, dims, name):
     if not ok:
         txt = ", ".join("*" if w is None else (f">={w[1]}" if isinstance(w, tuple) else str(w)) for w in dims)
         raise ValueError(f"{name}: shape {list(shape)}, expected [{txt}]")
+    if len(_SHAPES_SEEN) < 4096:
+        _SHAPES_SEEN.add(key)
 
 
 def _ring_rows(shape) -> int:
@@ -301,6 +312,26 @@ def oscar_decode_attn_timed(shape, r_k, r_v, q, seq_lens, max_seq_len, block_tab
     _check("oscar_decode_attn_timed", lib.oscar_decode_attn_timed(
         *_decode_args(shape, r_k, r_v, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v, out, workspace,
                       stream), start.handle, stop.handle))
+
+
+def oscar_decode_noalloc_scratch_bytes(shape, batch: int, max_seq_len: int) -> int:
+    n = lib.oscar_decode_noalloc_scratch_bytes(C.byref(shape), int(batch), int(max_seq_len))
+    if n == 0:
+        raise OscarError("oscar_decode_noalloc_scratch_bytes", -1)
+    return int(n)
+
+
+def oscar_decode_attn_noalloc(shape, r_k, r_v, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v, out,
+                              stream=None) -> None:
+    """oscar_decode_attn with the library's static scratch instead of a
+    workspace: no device allocation (calls overlapping on one GPU race)."""
+    b16, i32, u8, f32 = _dt()
+    batch = _decode_checks(shape, r_k, r_v, q, seq_lens, block_table, pool, win_k, win_v, out)
+    _check("oscar_decode_attn_noalloc", lib.oscar_decode_attn_noalloc(
+        C.byref(shape), _dev(r_k, b16, "r_k"), _dev(r_v, b16, "r_v"), _dev(q, b16, "q"), batch,
+        _dev(seq_lens, i32, "seq_lens"), int(max_seq_len), _dev(block_table, i32, "block_table"),
+        int(block_table.shape[1]), _dev(pool, u8, "pool"), int(pool.shape[0]), _dev(win_k, b16, "win_k"),
+        _dev(win_v, b16, "win_v"), _dev(out, f32, "out"), _stream(stream)))
 
 
 def oscar_quantize_append_layers(shape, r_k, r_v, k_new, v_new, seq_idx, pos, block_table, seq_len_after,

@@ -26,15 +26,16 @@
 // as the fp4 (e2m1) operand: a code c zero-extended to a nibble is exactly the
 // e2m1 value c/2, so (w & 0x33333333) and ((w >> 2) & 0x33333333) turn 16 packed
 // codes into two ready operand dwords.  The other operand is carried as fp8
-// (e4m3) terms x = t0 + t1/16 + t2/256 (+ t3/4096), each the RNE of the
-// remaining residual, one term per MFMA row, with the power-of-two factors in
-// the E8M0 operand scales: four terms (~16 significant bits) for q' in the
-// scores, three (~12 bits; their rounding is random across tokens) for the
-// softmax weights in the values.  Rows are (head, term): 4 heads per MFMA.
-//   scores: A = q' terms [(head, term) x 128 channels], B = K codes [128 x 16 tokens]
-//   values: A = w terms  [(head, term) x 128 tokens],  B = V codes [128 x 16 channels]
+// (e4m3) fixed-point digits (see digits_pair): v 2^(3 - E) = d0 + d1/16 +
+// d2/256 + d3/4096, |d_j| <= 8, one digit per MFMA row, the powers of two in the
+// E8M0 operand scales; every product is a small integer, so the matrix cores sum
+// them exactly.  E is the query head's exponent for q' (scores) and, for the
+// softmax weights (values), the exponent of the largest weight of the head in
+// the tile.  Rows are (head, digit): 4 heads per MFMA.
+//   scores: A = q' digits [(head, digit) x 128 channels], B = K codes [128 x 16 tokens]
+//   values: A = w digits  [(head, digit) x 128 tokens],  B = V codes [128 x 16 channels]
 // The score output leaves one (head, token) per lane after an in-lane sum of
-// the four term rows, so the softmax runs on full lanes.  The w terms go to a
+// the four digit rows, so the softmax runs on full lanes.  The w digits go to a
 // per-wave LDS tile to reach the A-operand layout.
 //
 // gfx950 operand layout of this instruction (16 x 16 output, lane l: column
@@ -86,26 +87,36 @@ __device__ __forceinline__ int clamp_len(int n, int max_pages) {
 
 __device__ __forceinline__ int clamp_scale(int s) { return s < 1 ? 1 : (s > 254 ? 254 : s); }
 
-// NT e4m3 terms of a pair of values (|x| < 128): term j of a in byte 0 and of
-// b in byte 1 of out[j]; each term is the RNE of the remaining residual x 16^j.
-template <int NT>
-__device__ __forceinline__ void split_terms(float a, float b, uint32_t out[NT]) {
+// Fixed-point digits of the fp8 (e4m3) operands of both INT2 contractions.  The
+// scaled fp8 x fp4 MFMA sums a row's products exactly only while they span a
+// narrow range: with products spread over the e4m3 range the measured sum is cut
+// to ~2^-10 .. 2^-12 of the largest product, always downward.  So every fp8
+// operand is a small integer: a value v with |v| < 2^E is written through
+// x = v 2^(3 - E), |x| < 8, as x = d0 + d1/16 + d2/256 + d3/4096 with each d_j
+// the RNE of the remaining residual (|d_j| <= 8, exact in e4m3); digit j sits in
+// the MFMA row of term j, whose E8M0 scale is 2^(E - 3 - 4 j).  Every product is
+// then an integer of magnitude <= 24 and every dot product exact; v is carried
+// to 2^-13 of 2^E.
+constexpr int kDigits = 4;
+
+// Digits of a pair of values (|a|, |b| < 8): digit j of a in byte 0 and of b in
+// byte 1 of out[j]; ra, rb the residuals left after the last digit (in units of
+// 16^-(kDigits - 1)), so a = sum_j d_j 16^-j + ra 16^-(kDigits - 1).
+__device__ __forceinline__ void digits_pair(float a, float b, uint32_t out[kDigits], float& ra, float& rb) {
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    out[j] = (uint32_t)pk & 0xffffu;
-    if (j < NT - 1) {
-      a = (a - __builtin_amdgcn_cvt_f32_fp8(pk, 0)) * 16.f;
-      b = (b - __builtin_amdgcn_cvt_f32_fp8(pk, 1)) * 16.f;
+  for (int j = 0; j < kDigits; ++j) {
+    const float da = __builtin_rintf(a), db = __builtin_rintf(b);
+    out[j] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(da, db, 0, false) & 0xffffu;
+    a -= da;
+    b -= db;
+    if (j < kDigits - 1) {
+      a *= 16.f;
+      b *= 16.f;
     }
   }
+  ra = a;
+  rb = b;
 }
-__device__ __forceinline__ void split4(float a, float b, uint32_t out[4]) { split_terms<4>(a, b, out); }
-
-// Terms of the softmax-weight operand of the value MFMA: 3 terms (~12
-// significant bits; their rounding is random across tokens, so the output's
-// relative error stays near 2^-12).  The fourth row of each head stays zero.
-constexpr int kWTerms = 3;
 
 __device__ __forceinline__ int exponent_above(float x) {  // E with |x| < 2^E (0 for x == 0)
   int e = 0;
@@ -321,11 +332,13 @@ __device__ void window_chunk(const SplitParams& p, int b, int h, int c, int G, f
 // Query preparation, once per (sequence, KV head):
 //   q' = R_K[h] q for its G <= 16 query heads on the matrix cores (bf16 in,
 //   fp32 out; each wave 32 output channels);
-//   qsum[head][j] = sum of q'_c over the channels c of quantisation group j;
-//   the fp8 score operand of every 4-head group: lane (lg, lr) holds term lr%4 of
-//   q'_(head lr/4) at the 32 channels its k-slots map to, plus the row's E8M0
-//   scale (2^(E - 7 - 4 term), |q'| < 2^E), exactly as the split kernel's MFMA
-//   consumes it.
+//   q' is kept scaled by log2(e) / sqrt(d), so the scores come out in the log2
+//   domain; qsum[head][j] = sum of that q' over the channels of quantisation
+//   group j;
+//   the fp8 score operand of every 4-head group: lane (lg, lr) holds digit lr % 4
+//   of q'_(head lr / 4) at the 32 channels its k-slots map to, plus the row's
+//   E8M0 scale (2^(E - 3 - 4 digit), |q'| < 2^E), exactly as the split kernel's
+//   MFMA consumes it.
 // ---------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(256) void prep_kernel(SplitParams p0, const uint16_t* __restrict__ r_k0) {
@@ -398,7 +411,7 @@ __global__ __launch_bounds__(256) void prep_kernel(SplitParams p0, const uint16_
                                                       __builtin_bit_cast(bf16x8, bq[ks]), acc, 0, 0, 0);
       if (r < G) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qs[r][16 * (2 * wv + blk) + 4 * g + i] = acc[i];
+        for (int i = 0; i < 4; ++i) qs[r][16 * (2 * wv + blk) + 4 * g + i] = acc[i] * p.scale_log2;
       }
     }
   }
@@ -431,13 +444,14 @@ __global__ __launch_bounds__(256) void prep_kernel(SplitParams p0, const uint16_
     int sc = kScaleOne;
     if (head < G) {
       const int E = qexp[head];
-      sc = clamp_scale(kScaleOne + E - 7 - 4 * term);
+      sc = clamp_scale(kScaleOne + E - 3 - 4 * term);
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const float a = ldexpf(qs[head][k_channel(k_of_fp8(lg, 8 * q4 + e))], 7 - E);
-        const float c = ldexpf(qs[head][k_channel(k_of_fp8(lg, 8 * q4 + e + 1))], 7 - E);
-        uint32_t t[4];
-        split4(a, c, t);
+        const float a = ldexpf(qs[head][k_channel(k_of_fp8(lg, 8 * q4 + e))], 3 - E);
+        const float c = ldexpf(qs[head][k_channel(k_of_fp8(lg, 8 * q4 + e + 1))], 3 - E);
+        uint32_t t[kDigits];
+        float ra, rc;
+        digits_pair(a, c, t, ra, rc);
         op[e >> 2] |= (int)(t[term] << (8 * (e & 3)));
       }
     }
@@ -617,7 +631,8 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
     const int tok = (pbase + pp) * 16 + lr;
     live[pp] = FULL || (((t.page_ok >> pp) & 1u) && tok >= t_beg && tok < t_end);
   }
-  // ---- scores: sc[rg][pp] = sum over groups jg of ks_jg (q'_(4rg+lg) . code) + kz_jg qsum_jg,
+  // ---- scores (log2 domain; q' and its group sums arrive scaled by log2(e)/sqrt(d)):
+  // sc[rg][pp] = sum over groups jg of ks_jg (q'_(4rg+lg) . code) + kz_jg qsum_jg,
   // the dot product over group jg's channels of token lr of page pp ----
   float sc[NRG][8];
 #pragma unroll
@@ -633,23 +648,13 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
 #pragma unroll
       for (int rg = 0; rg < NRG; ++rg) {
         const f32x4 c = mfma_f8_f4(qa[rg], bk, f32x4{0.f, 0.f, 0.f, 0.f}, qsc[rg], kScaleCode);
-        sc[rg][pp] = pin(sc[rg][pp] + (kz * qsr[rg][jg] + ks * ((c[0] + c[1]) + (c[2] + c[3]))));
+        sc[rg][pp] = pin(sc[rg][pp] + fmaf(kz, qsr[rg][jg], ks * ((c[0] + c[1]) + (c[2] + c[3]))));
       }
     }
   }
-  // ---- online softmax, weights, w terms -> LDS ----
-  // value scale and midpoint of (page pp, group jg), zero on a dead slot
-  auto vs_of = [&](int pp, int jg) { return live[pp] ? h2f((uint16_t)(t.meta[pp][jg].y & 0xffffu)) : 0.f; };
-  auto vz_of = [&](int pp, int jg) { return live[pp] ? h2f((uint16_t)(t.meta[pp][jg].y >> 16)) : 0.f; };
-  float wsum[NRG][NG];
-  float vsmax = 0.f;
-#pragma unroll
-  for (int pp = 0; pp < 8; ++pp)
-#pragma unroll
-    for (int jg = 0; jg < NG; ++jg) vsmax = fmaxf(vsmax, vs_of(pp, jg));
-  vsmax = row_max16(vsmax);
-  const int wexp = exponent_above(vsmax);  // every w = p vs <= vsmax < 2^wexp
-  const float wmul = ldexpf(1.f, 7 - wexp);  // w * wmul < 128, exact (a power of two)
+  // ---- online softmax, weights, weight digits -> LDS ----
+  float wsum[NRG][NG];  // sum of the weights as the digits carry them
+  int wexp[NRG][NG];    // every weight of this lane's head and group below 2^wexp
 #pragma unroll
   for (int rg = 0; rg < NRG; ++rg) {
     const bool hv = 4 * rg + lg < p.gw;
@@ -658,14 +663,13 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
       // computed on every lane, then masked: a select, not a branch
-      const float v = pin(sc[rg][pp] * p.scale_log2);
-      lgt[pp] = hv && live[pp] ? v : kNegInf;
+      lgt[pp] = hv && live[pp] ? sc[rg][pp] : kNegInf;
       mx = fmaxf(mx, lgt[pp]);
     }
     mx = row_max16(mx);
     const float m_new = fmaxf(st.m_run[rg], mx);
     if (__any(m_new > st.m_run[rg])) {
-      const float alpha = (m_new == kNegInf) ? 1.f : exp2f(st.m_run[rg] - m_new);
+      const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(st.m_run[rg] - m_new);
 #pragma unroll
       for (int nn = 0; nn < 8; ++nn) st.acc[rg][nn] *= alpha;
       st.l_part[rg] *= alpha;
@@ -677,47 +681,62 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
     float pv[8];
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
-      pv[pp] = exp2f(lgt[pp] - m_safe);
+      // the hardware exp2: p <= 1, and a p below 2^-126 may read as 0
+      pv[pp] = __builtin_amdgcn_exp2f(lgt[pp] - m_safe);
       st.l_part[rg] += pv[pp];
     }
 #pragma unroll
     for (int jg = 0; jg < NG; ++jg) {  // one group's weights at a time (registers)
       float w[8];
-      float ws = 0.f;
+      float ws = 0.f, wmax = 0.f;
 #pragma unroll
       for (int pp = 0; pp < 8; ++pp) {
-        const float vs = vs_of(pp, jg), vz = vz_of(pp, jg);
+        // value scale and zero of (page pp, group jg); a dead slot's record may
+        // hold anything (NaN included), so it is replaced by zeros first
+        const uint32_t vrec = live[pp] ? t.meta[pp][jg].y : 0u;
+        const float vs = h2f((uint16_t)(vrec & 0xffffu)), vz = h2f((uint16_t)(vrec >> 16));
         st.az_part[rg][jg] = fmaf(pv[pp], fmaf(1.5f, vs, vz), st.az_part[rg][jg]);
         w[pp] = pv[pp] * vs;
         ws += w[pp];
+        wmax = fmaxf(wmax, w[pp]);
       }
-      wsum[rg][jg] = row_sum16(ws);
+      const int e = exponent_above(row_max16(wmax));  // this head's weights in the tile are < 2^e
+      const float wmul = ldexpf(1.f, 3 - e);           // w wmul < 8, exact (a power of two)
+      float rsum = 0.f;
       uint8_t* tile_rg = wt + (rg * NG + jg) * 2048;
 #pragma unroll
       for (int pp = 0; pp < 8; pp += 2) {
-        uint32_t tt[kWTerms];
-        split_terms<kWTerms>(w[pp] * wmul, w[pp + 1] * wmul, tt);
+        uint32_t tt[kDigits];
+        float ra, rb;
+        digits_pair(w[pp] * wmul, w[pp + 1] * wmul, tt, ra, rb);
+        rsum += ra + rb;
 #pragma unroll
-        for (int j = 0; j < kWTerms; ++j) {
+        for (int j = 0; j < kDigits; ++j) {
           uint8_t* row = tile_rg + (4 * lg + j) * 128 + slot_pos;
           row[16 * pp] = (uint8_t)(tt[j] & 0xffu);
           row[16 * (pp + 1)] = (uint8_t)(tt[j] >> 8);
         }
       }
+      // the digits carry w - r 16^-3 / wmul: the correction below must take the
+      // same sum, or its rounding would shift every channel alike
+      wsum[rg][jg] = row_sum16(fmaf(-rsum, ldexpf(1.f, e - 3 - 4 * (kDigits - 1)), ws));
+      wexp[rg][jg] = e;
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // ---- values: acc[rg][nn] += w terms x V codes (channels 8lr + nn) ----
+  // ---- values: acc[rg][nn] += weight digits x V codes (channels 8lr + nn) ----
   // with NG > 1 the column of lane lr (channels 8 lr .. 8 lr + 7) belongs to
   // group lr / (16 / NG).  The MFMA of group jg scales the codes of the other
   // groups' columns by 2^-127 (E8M0 0) instead of 2 (its B scale is per lane,
   // i.e. per column): their products with group jg's weights land ~2^-128 below
-  // the true terms, under fp32 resolution of any accumulator they join, and no
+  // the true products, under fp32 resolution of any accumulator they join, and no
   // instruction is spent masking them.
-  const int wsc = clamp_scale(kScaleOne + wexp - 7 - 4 * (lr & 3));
+  // A-operand scale of row lr (head lr / 4 of the row group, digit lr % 4): that
+  // head's exponent lives on the lanes of row lr / 4
+  const int src_row = 4 * 16 * (lr >> 2);
   const int my_grp = lr / (16 / NG);
   float corr[NRG];
 #pragma unroll
@@ -727,6 +746,7 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
     const bool mine = NG == 1 || my_grp == jg;
     const int sb = mine ? kScaleCode : 0;
     i32x8 wa[NRG];
+    int wsc[NRG];
 #pragma unroll
     for (int rg = 0; rg < NRG; ++rg) {
       const uint8_t* row = wt + (rg * NG + jg) * 2048 + lr * 128;
@@ -740,6 +760,8 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
       wa[rg][5] = (int)a1.y;
       wa[rg][6] = (int)a1.z;
       wa[rg][7] = (int)a1.w;
+      const int eh = __builtin_amdgcn_ds_bpermute(src_row, wexp[rg][jg]);
+      wsc[rg] = clamp_scale(kScaleOne + eh - 3 - 4 * (lr & 3));
       corr[rg] = mine ? 1.5f * wsum[rg][jg] : corr[rg];
     }
 #pragma unroll
@@ -753,7 +775,7 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
       bv[3] = (int)((v1 >> 2) & 0x33333333u);
       bv[4] = bv[5] = bv[6] = bv[7] = 0;
 #pragma unroll
-      for (int rg = 0; rg < NRG; ++rg) st.acc[rg][nn] = mfma_f8_f4(wa[rg], bv, st.acc[rg][nn], wsc, sb);
+      for (int rg = 0; rg < NRG; ++rg) st.acc[rg][nn] = mfma_f8_f4(wa[rg], bv, st.acc[rg][nn], wsc[rg], sb);
     }
   }
 #pragma unroll
@@ -805,7 +827,7 @@ __device__ __forceinline__ int find_unit(const int* tp, int units, int64_t t) {
 template <int G, int NG>
 __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
   constexpr int NRG = (G + 3) / 4;  // MFMA row groups of 4 heads
-  __shared__ __align__(16) uint8_t smem[4 * NRG * NG * 2048];  // per-wave w-term tiles
+  __shared__ __align__(16) uint8_t smem[4 * NRG * NG * 2048];  // per-wave weight-digit tiles
 
   const int hg_per_seq = p.hkv / p.hw;  // KV head groups per sequence
   const int per_seq = hg_per_seq * p.gsub;
@@ -875,8 +897,7 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
 #pragma unroll
       for (int nn = 0; nn < 8; ++nn) st.acc[rg][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // the w-term tiles: rows of an unused term (the 4th) must read 0
-    for (int i = lane; i < NRG * NG * 2048 / 16; i += 64) reinterpret_cast<uint4*>(wt)[i] = make_uint4(0, 0, 0, 0);
+    // (the weight-digit tiles need no clearing: every tile writes all their rows)
 
     // step s: the wave's tiles 2s and 2s + 1, i.e. tiles a + ph + ts k of the
     // unit; a step with one tile computes an empty (all-masked) second one
