@@ -234,6 +234,28 @@ int oscar_decode_attn(const oscar_shape* shape, const uint16_t* r_k, const uint1
                       void* stream);
 
 /*
+ * Decode attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * oscar_decode_attn without the workspace arguments; results are those of
+ * oscar_decode_attn on the same inputs.  The scratch regions live in a static
+ * device array of the library, OSCAR_NOALLOC_SCRATCH_BYTES per device, held
+ * until the process ends; the call allocates nothing.  Every call on a device
+ * shares that device's array: calls that overlap on one device (concurrent
+ * streams, several host threads) race and must be serialised by the caller.
+ * oscar_decode_noalloc_scratch_bytes gives the scratch bytes a call needs
+ * (0 on invalid arguments); a call needing more than
+ * OSCAR_NOALLOC_SCRATCH_BYTES returns OSCAR_ENOSPACE before any launch.
+ * Errors as oscar_decode_attn.
+ */
+#define OSCAR_NOALLOC_SCRATCH_BYTES (32u << 20)
+size_t oscar_decode_noalloc_scratch_bytes(const oscar_shape* shape, int32_t batch, int32_t max_seq_len);
+int oscar_decode_attn_noalloc(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
+                              const uint16_t* q, int32_t batch, const int32_t* seq_lens, int32_t max_seq_len,
+                              const int32_t* block_table, int32_t max_pages_per_seq, const uint8_t* pool,
+                              int64_t n_pages, const uint16_t* win_k, const uint16_t* win_v, float* out,
+                              void* stream);
+
+/*
  * Layer-batched forms: the caches of n_layers layers (every layer holding the
  * same sequences, as the layers of one model do) in one call, one launch per
  * kernel instead of one per layer (the rotation-file workflow calibrates and

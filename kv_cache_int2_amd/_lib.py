@@ -38,6 +38,8 @@ SIGNATURES = {
     "oscar_decode_layers_workspace_bytes": (SZ, [SHAPE, I32, I32, I32]),
     "oscar_decode_attn_layers": (C.c_int, [SHAPE, I32, P, P, P, I32, P, I32, P, I32, P, I64, P, P, P, P, SZ, P]),
     "oscar_decode_attn": (C.c_int, [SHAPE, P, P, P, I32, P, I32, P, I32, P, I64, P, P, P, P, SZ, P]),
+    "oscar_decode_noalloc_scratch_bytes": (SZ, [SHAPE, I32, I32]),
+    "oscar_decode_attn_noalloc": (C.c_int, [SHAPE, P, P, P, I32, P, I32, P, I32, P, I64, P, P, P, P]),
     "oscar_bf16_append": (C.c_int, [SHAPE, P, P, I64, P, P, I32, P, I32, P, I64, P]),
     "oscar_bf16_decode_attn": (C.c_int, [SHAPE, P, I32, P, I32, P, I32, P, I64, P, P, SZ, P]),
     "oscar_hbm_copy": (C.c_int, [P, P, SZ, P]),

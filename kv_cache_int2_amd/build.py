@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkv_cache_int2_amd.so")
-SOURCES = ["calibrate.cpp", "rotation_file.cpp", "append.hip", "decode.hip", "runtime.hip"]
+SOURCES = ["calibrate.cpp", "rotation_file.cpp", "append.hip", "decode.hip", "noalloc.hip", "runtime.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -253,3 +253,23 @@ def test_binding_checks_shapes_before_the_call():
     with pytest.raises(ValueError):
         K.oscar_calibrate(K.make_shape(32, 8), np.zeros((8, 4, 64), np.float32), np.zeros((8, 4, 64), np.float32),
                           np.zeros((8, 4, 64), np.float32))
+
+
+def test_noalloc_entry_point_refuses_oversized_calls_on_the_host():
+    """The allocation-free decode checks its scratch need against the static
+    array before anything touches the device."""
+    lib = _lib.lib
+    fake = C.c_void_p(256)
+    small = K.make_shape(32, 8)
+    need = lib.oscar_decode_noalloc_scratch_bytes(C.byref(small), 8, 100000)
+    assert 0 < need <= K.NOALLOC_SCRATCH_BYTES
+    # the workspace form's size includes the comparator's partials; the static
+    # scratch holds only what the INT2 decode uses
+    assert need <= lib.oscar_decode_workspace_bytes(C.byref(small), 8, 100000)
+    big = K.make_shape(64, 8, window=1024, n_sink=1024, group_size=32)
+    assert lib.oscar_decode_noalloc_scratch_bytes(C.byref(big), 64, 131073) > K.NOALLOC_SCRATCH_BYTES
+    assert lib.oscar_decode_attn_noalloc(C.byref(big), fake, fake, fake, 64, fake, 131073, fake, 8193, fake, 1, fake,
+                                         fake, fake, None) == ENOSPACE
+    assert lib.oscar_decode_noalloc_scratch_bytes(C.byref(K.make_shape(32, 8, group_size=48)), 8, 10) == 0
+    assert lib.oscar_decode_attn_noalloc(C.byref(K.make_shape(24, 8)), fake, fake, fake, 8, fake, 10, fake, 1, fake,
+                                         1, fake, fake, fake, None) == EUNSUP
