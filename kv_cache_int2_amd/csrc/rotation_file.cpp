@@ -90,6 +90,8 @@ int read_header(FILE* f, Info& info) {
   if (crc != get32(h + 52)) return OSCAR_EFORMAT;
   if (get32(h + 8) != kVersion || get32(h + 12) != kHeader || get32(h + 16) != (uint32_t)oscar::kD)
     return OSCAR_EFORMAT;
+  // reserved: u32 at 36 and the 8 bytes after the header checksum are zero
+  if (get32(h + 36) != 0 || get64(h + 56) != 0) return OSCAR_EFORMAT;
   info.n_layers = get32(h + 20);
   info.hkv = get32(h + 24);
   info.group = get32(h + 28);

@@ -74,6 +74,8 @@ def decode(data: bytes):
         raise ValueError("not a rotation file, or damaged header")
     if version != VERSION or header != HEADER or d != D or flags & ~1 or group not in (32, 64, 128):
         raise ValueError("unsupported header")
+    if zero != 0 or data[56:HEADER] != bytes(HEADER - 56):
+        raise ValueError("reserved header bytes not zero")
     eig = bool(flags & 1)
     per_layer = hkv * D * D * 2 * 2 + (hkv * D * 8 * 2 if eig else 0)
     body = data[HEADER:]

@@ -89,6 +89,7 @@ def test_damaged_and_mismatched_files_are_refused(rng, tmp_path):
         "truncated": good[:-1],
         "trailing byte": good + b"\0",
         "short header": good[:40],
+        "reserved bytes after the header checksum": good[:60] + bytes([good[60] ^ 1]) + good[61:],
     }
     for name, data in cases.items():
         p.write_bytes(data)
