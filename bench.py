@@ -181,6 +181,8 @@ def main():
         else:
             K.oscar_bf16_decode_attn_timed(shape, q, lensd, nmax, btd, kvp[l], out, ws, *ev)
 
+    host_ms = {}
+
     def timed(step):
         """Wall time per step over the timed steps (no instrumentation), then the
         same steps again with a pair of events attached to each split kernel's
@@ -191,8 +193,10 @@ def main():
         t = time.perf_counter()
         for i in range(args.steps):
             step(args.warmup + i)
+        t_enq = time.perf_counter()
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t) / args.steps
+        host_ms[step.__name__] = (t_enq - t) / args.steps * 1e3
         evs = [(K.Event(), K.Event()) for _ in range(args.steps)]
         # a 3 ms wait queued first: the host has enqueued every step before the
         # GPU reaches them, so no launch gap of the host falls between an event
@@ -307,6 +311,7 @@ def main():
         "bf16_kv": res_bf16,
         "speedup_vs_bf16": (res_bf16["ms_per_step"] / (dt * 1e3)) if res_bf16 else None,
         "hbm_probe": probe,
+        "host_enqueue_ms_per_step": host_ms.get("step_int2"),
         "append": res_append,
         "layers_batched": res_layers,
         "roofline": {

@@ -105,24 +105,30 @@ def _dev(t, dtypes, name):
     """Device pointer of a contiguous torch tensor (None -> NULL)."""
     if t is None:
         return None
-    import torch
-
-    if not isinstance(t, torch.Tensor):
-        raise TypeError(f"{name}: expected a torch tensor")
-    if t.device.type != "cuda":
+    try:
+        if t.is_cuda and t.dtype in dtypes and t.is_contiguous():
+            return t.data_ptr()
+    except AttributeError:
+        raise TypeError(f"{name}: expected a torch tensor") from None
+    if not t.is_cuda:
         raise ValueError(f"{name}: must be on the GPU")
-    if not t.is_contiguous():
-        raise ValueError(f"{name}: must be contiguous")
     if t.dtype not in dtypes:
-        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
-    return t.data_ptr()
+        raise TypeError(f"{name}: dtype {t.dtype} not in {sorted(str(d) for d in dtypes)}")
+    raise ValueError(f"{name}: must be contiguous")
+
+
+_DTYPES = None
 
 
 def _dt():
-    import torch
+    """(bf16-like, int32, uint8, float32) dtype sets accepted for the buffers."""
+    global _DTYPES
+    if _DTYPES is None:
+        import torch
 
-    b16 = (torch.bfloat16, torch.int16, torch.uint16, torch.float16)
-    return b16, (torch.int32,), (torch.uint8,), (torch.float32,)
+        _DTYPES = (frozenset((torch.bfloat16, torch.int16, torch.uint16, torch.float16)),
+                   frozenset((torch.int32,)), frozenset((torch.uint8,)), frozenset((torch.float32,)))
+    return _DTYPES
 
 
 def _stream(stream):

@@ -476,7 +476,7 @@ int append_impl(const oscar_shape* shape, int32_t n_layers, const uint16_t* r_k,
   dim3 grid((unsigned)((tiles + p.tiles_per_wg - 1) / p.tiles_per_wg), (unsigned)p.hkv, 2 * (unsigned)n_layers);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool one = p.tiles_per_wg == 1;
-  auto go = [&](auto kernel) { hipExtLaunchKernelGGL(kernel, grid, dim3(256), 0, s, tl.start, tl.stop, 0, p); };
+  auto go = [&](auto kernel) { launch(kernel, grid, dim3(256), s, tl, p); };
   switch (kD / shape->group_size) {
     case 1: one ? go(append_kernel<1, true>) : go(append_kernel<1, false>); break;
     case 2: one ? go(append_kernel<2, true>) : go(append_kernel<2, false>); break;

@@ -137,6 +137,19 @@ struct TimedLaunch {
 // OSCAR_OK when both events or neither are given.
 int check_events(const TimedLaunch& t);
 
+// Launches kernel on stream s; with events, through hipExtLaunchKernelGGL so
+// that they are stamped at the dispatch's own start and end.  Without events
+// the plain launch is used: attaching events delays the dispatch's start by
+// about 6 us behind the preceding kernel on the same stream, a cost that only
+// timed calls should pay.
+template <typename Kernel, typename... Args>
+inline void launch(Kernel kernel, dim3 grid, dim3 block, hipStream_t s, const TimedLaunch& tl, Args... args) {
+  if (tl.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, tl.start, tl.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
+
 // One decode call (INT2 with int2 set, else the bf16 comparator): argument
 // checks, split plan, workspace layout (int2_only: without the comparator's
 // partials) and the launches on `stream`.  Returns an oscar_status.
