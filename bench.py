@@ -87,6 +87,8 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the prefill-ingest (append) leg")
     ap.add_argument("--no-layers-leg", action="store_true", help="skip the layer-batched decode leg")
+    ap.add_argument("--append-only", action="store_true",
+                    help="only the prefill-ingest (append) leg, as one JSON line (for profiling it alone)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="decode time of each oracle baseline leg (one process; process pool)")
     ap.add_argument("--quality", action="store_true",
@@ -106,6 +108,23 @@ def main():
     torch.cuda.set_device(dev)
     if args.quality:
         quality_leg(K, wl, torch)
+        return
+    if args.append_only:
+        s1 = wl.spec(args.config)
+        shape = K.make_shape(s1.n_q_heads, s1.n_kv_heads, s1.window, group_size=args.group)
+        rk, rv, _, _ = K.oscar_calibrate(shape, *wl.calibration_set(s1))
+        rkd, rvd = (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev) for a in (rk, rv))
+        res = append_leg(K, torch, dev, shape, rkd, rvd, args, 64 + 8 * (128 // args.group))
+        # two launches of the copy probe (2 GiB each way): the known-size
+        # dispatch that scales the traffic counters of a profiled run
+        a = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+        c = torch.empty_like(a)
+        for _ in range(2):
+            K.oscar_hbm_copy(a, c)
+        torch.cuda.synchronize()
+        del a, c
+        print(json.dumps({"append": res, "data": "synthetic (seeded Gaussian K/V, 4 key outlier channels x20)"}),
+              flush=True)
         return
     s = wl.spec(args.config)
     if args.window is not None:
@@ -615,7 +634,7 @@ def summarize_trace(directory: str, command: str) -> str:
     return "\n".join(out) + "\n"
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str, command: str) -> str:
+def summarize_pmc(fetch_dir: str, write_dir: str, command: str, bench_json: str = None) -> str:
     """HBM bytes per launch of the INT2 split kernel from FETCH_SIZE and WRITE_SIZE
     runs (KiB per dispatch), each scaled by what the same counter reads for the
     copy probe of known size (2 GiB read + 2 GiB written per launch)."""
@@ -657,15 +676,70 @@ def summarize_pmc(fetch_dir: str, write_dir: str, command: str) -> str:
         if k.startswith("at::"):
             continue
         lines.append(f"# {k:40s} FETCH_SIZE {fetch[k]:12.1f} KiB  WRITE_SIZE {write.get(k, float('nan')):12.1f} KiB (raw)")
+    if bench_json:
+        # second check of the fetch scale: the read probe's dispatches each read
+        # bytes_per_read bytes (sequential and through random page tables)
+        line = [json.loads(x) for x in open(bench_json) if x.startswith("{")][-1]
+        nbytes = float(line["hbm_probe"]["bytes_per_read"])
+        reads = [float(r["Counter_Value"]) * 1024.0 for r in _csv_rows(fetch_dir, "counter_collection.csv")
+                 if r["Counter_Name"] == "FETCH_SIZE" and _short_kernel(r["Kernel_Name"]) == "read_kernel"]
+        if reads:
+            sc = nbytes / np.asarray(reads)
+            lines.append(f"read_probe_bytes_per_launch: {nbytes:.0f}")
+            lines.append(f"read_probe_fetch_scale: min {sc.min():.4f} median {np.median(sc):.4f} max {sc.max():.4f} "
+                         f"({len(sc)} dispatches)")
     return "\n".join(lines) + "\n"
+
+
+def summarize_counters(command: str, dirs) -> str:
+    """Per-kernel means per dispatch of every counter in one or more
+    `rocprofv3 --pmc` runs (one pass each), for this library's kernels and the
+    probes, with derived fractions.  GRBM_GUI_ACTIVE comes summed over the 8
+    XCDs, so a dispatch lasts GRBM_GUI_ACTIVE / 8 cycles; SQ_ACTIVE_INST_* count
+    quad-cycles (a wave64 VALU instruction issues over 4 cycles) summed over the
+    1024 SIMDs, SQ_VALU_MFMA_BUSY_CYCLES cycles summed over the SIMDs."""
+    acc = {}
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            k = _short_kernel(r["Kernel_Name"])
+            if k.startswith("at::") or "elementwise" in k or "rocclr" in k:
+                continue
+            acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = ["# rocprofv3 --pmc counters, mean per dispatch", f"# command: {command}", "#"]
+    for k in sorted(acc):
+        c = {n: float(np.mean(v)) for n, v in acc[k].items()}
+        n = max(len(v) for v in acc[k].values())
+        out.append(f"{k}  ({n} dispatches)")
+        for name in sorted(c):
+            out.append(f"  {name:34s} {c[name]:16.1f}")
+        if c.get("GRBM_GUI_ACTIVE"):
+            simd = 1024 * c["GRBM_GUI_ACTIVE"] / 8  # SIMD-cycles of the dispatch
+            out.append(f"  {'=> dispatch cycles (per XCD)':34s} {c['GRBM_GUI_ACTIVE'] / 8:16.0f}")
+            for cnt, label, mul in (("SQ_ACTIVE_INST_ANY", "issue busy", 4), ("SQ_ACTIVE_INST_VALU", "VALU busy", 4),
+                                    ("SQ_ACTIVE_INST_LDS", "LDS issue busy", 4),
+                                    ("SQ_VALU_MFMA_BUSY_CYCLES", "MFMA busy", 1)):
+                if cnt in c:
+                    out.append(f"  {'=> ' + label + ' (per SIMD)':34s} {mul * c[cnt] / simd:16.3f}")
+        cp = acc.get("copy_kernel", {})
+        for cnt in ("FETCH_SIZE", "WRITE_SIZE"):
+            if cnt in c and cp.get(cnt):
+                ref = np.asarray(cp[cnt])
+                scale = float(2 << 30) / (1024.0 * float(np.mean(ref[ref > 0.5 * ref.max()])))
+                out.append(f"  {'=> ' + cnt + ' bytes (x%.3f)' % scale:34s} {1024.0 * c[cnt] * scale:16.0f}")
+        if c.get("SQ_INSTS_LDS") and "SQ_LDS_BANK_CONFLICT" in c:
+            out.append(f"  {'=> conflict cycles per LDS inst':34s} {c['SQ_LDS_BANK_CONFLICT'] / c['SQ_INSTS_LDS']:16.3f}")
+    return "\n".join(out) + "\n"
 
 
 if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
         # bench.py --summarize-trace DIR "COMMAND"
         sys.stdout.write(summarize_trace(sys.argv[2], sys.argv[3]))
+    elif len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
+        # bench.py --summarize-counters "COMMAND" DIR [DIR ...]
+        sys.stdout.write(summarize_counters(sys.argv[2], sys.argv[3:]))
     elif len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
-        # bench.py --summarize-pmc FETCH_DIR WRITE_DIR "COMMAND"
-        sys.stdout.write(summarize_pmc(sys.argv[2], sys.argv[3], sys.argv[4]))
+        # bench.py --summarize-pmc FETCH_DIR WRITE_DIR "COMMAND" [BENCH_JSON_OUTPUT]
+        sys.stdout.write(summarize_pmc(sys.argv[2], sys.argv[3], sys.argv[4], *sys.argv[5:6]))
     else:
         main()

@@ -55,6 +55,15 @@ struct AppendParams {
   int64_t ls_rot, ls_x, ls_win, ls_pool;
 };
 
+// f(integral_constant<int, k>) for k = 0 .. N-1, unrolled at compile time
+template <int N, int K = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (K < N) {
+    f(std::integral_constant<int, K>{});
+    static_for<N, K + 1>(f);
+  }
+}
+
 constexpr int kRowU4 = 17;  // LDS row stride of R in uint4 (16 + 1 pad: 272 B)
 #ifndef OSCAR_APPEND_TILES
 #define OSCAR_APPEND_TILES 1
@@ -67,11 +76,47 @@ __device__ __forceinline__ f32x4 mfma(uint4 a, uint4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// code = clamp(rint(t), 0, 3) with t = x * inv - zi
-__device__ __forceinline__ uint32_t encode(float v, float inv, float zi) {
-  const float t = __builtin_amdgcn_fmed3f(fmaf(v, inv, -zi), 0.f, 3.f);
-  return (uint32_t)__builtin_rintf(t);
+// Code of x' as a float's bits: u = kRound + clamp(rint(x' * inv - zi), 0, 3).
+// Adding 1.5 * 2^23 rounds t (|t| < 2^22) to an integer, ties to even, in the
+// low mantissa bits, so the bits of u are kRoundBits + code.  A packed word is
+// then the sum of such bits shifted into place, less the shifted kRoundBits
+// (a constant; all of it lies at bit 22 and up, before the shift).  A NaN
+// t clamps to the low bound (v_med3 returns the smallest operand), code 0.
+constexpr float kRound = 12582912.0f;
+constexpr uint32_t kRoundBits = 0x4B400000u;
+__device__ __forceinline__ uint32_t code_bits(float v, float inv, float zi) {
+  const float u = fmaf(v, inv, -zi) + kRound;
+  return __float_as_uint(__builtin_amdgcn_fmed3f(u, kRound, kRound + 3.0f));
 }
+// (x << S) + c as one v_lshl_add_u32: left to itself the compiler splits a chain
+// of these into shifts and three-operand adds, one instruction more per pair.
+template <int S>
+__device__ __forceinline__ uint32_t lshl_add(uint32_t x, uint32_t c) {
+  uint32_t d;
+  asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(d) : "v"(x), "n"(S), "v"(c));
+  return d;
+}
+// sum of kRoundBits << s over the shifts 8 m + 2 i (m, i = 0..3) of a K word
+constexpr uint32_t k_word_bias() {
+  uint32_t c = 0;
+  for (int m = 0; m < 4; ++m)
+    for (int i = 0; i < 4; ++i) c += kRoundBits << (8 * m + 2 * i);
+  return c;
+}
+
+// Order-preserving map of fp32 bits to int32 (its own inverse): integer
+// min/max take a DPP operand for free, where fminf/fmaxf would first quiet
+// both operands.  -0 orders just below +0.
+__device__ __forceinline__ int f2key(float x) {
+  const int b = __float_as_int(x);
+  return b ^ ((b >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float key2f(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7fffffff)); }
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xf, 0xf, true);
+}
+constexpr int kDppRor4 = 0x124, kDppRor8 = 0x128;  // row_ror by 4, 8 lanes
 
 // Scale and zero of a group from its min and max: s16 = fp16((max - min) / 3),
 // z16 = fp16(min); codes are taken against the stored (fp16) values.  The
@@ -233,12 +278,12 @@ __device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4
           }
         q[gr] = quant_params(min_rows(mn), max_rows(mx));
       }
-      uint32_t w[2] = {0u, 0u};
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          w[m >> 2] |= encode(acc[j][m][i], q[m / MPG].inv, q[m / MPG].zi) << (8 * (m & 3) + 2 * i);
+      constexpr uint32_t kBias = k_word_bias();
+      uint32_t w[2] = {0u - kBias, 0u - kBias};
+      static_for<32>([&](auto mi_) {
+        constexpr int m = decltype(mi_)::value >> 2, i = decltype(mi_)::value & 3;
+        w[m >> 2] = lshl_add<8 * (m & 3) + 2 * i>(code_bits(acc[j][m][i], q[m / MPG].inv, q[m / MPG].zi), w[m >> 2]);
+      });
       if (ti.blk) {
         *reinterpret_cast<uint2*>(ti.blk + kKCodes + 32 * ti.slot + 8 * g) = make_uint2(w[0], w[1]);
         // lane group g < NG writes group g's K scale and zero
@@ -247,8 +292,13 @@ __device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4
           if (g == gr) *reinterpret_cast<uint32_t*>(ti.blk + kMeta + 8 * (NG * ti.slot + gr)) = q[gr].sz;
       }
     } else {
-      // acc[j][m][i] = x'[token tj + 4g + i][channel 16m + r]
-      float mn[4][NG], mx[4][NG];
+      // acc[j][m][i] = x'[token tj + 4g + i][channel 16m + r].  Per-token min
+      // and max: over m in the lane, then over the row's 16 lanes.  Lanes r and
+      // r^1 combine, and each keeps the tokens with i & 1 == r & 1; then lanes
+      // r and r^2, keeping token i == r & 3; rotating the row by 4 and 8 lanes
+      // finishes it.  Every lane ends with the min and max of each group of
+      // token 4g + (r & 3).
+      int kmn[4][NG], kmx[4][NG];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -259,42 +309,55 @@ __device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4
             lo = fminf(lo, acc[j][m][i]);
             hi = fmaxf(hi, acc[j][m][i]);
           }
-          mn[i][gr] = row_min16(lo);
-          mx[i][gr] = row_max16(hi);
+          kmn[i][gr] = f2key(lo);
+          kmx[i][gr] = f2key(hi);
         }
-      // lane r of each row takes token 4g + (r & 3), group (r >> 2) mod NG; the
-      // others then read them: within the quad (NG = 1) or the row
-      const int mi = r & 3, mk = (r >> 2) % NG;
-      float mn_l = mn[0][0], mx_l = mx[0][0];
+      const bool odd1 = r & 1, odd2 = r & 2;
+      int pmn[2][NG], pmx[2][NG];  // tokens 2 h + (r & 1)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int gr = 0; gr < NG; ++gr) {
-          const bool sel = mi == i && mk == gr;
-          mn_l = sel ? mn[i][gr] : mn_l;
-          mx_l = sel ? mx[i][gr] : mx_l;
+          const int e0 = min(kmn[2 * h][gr], dpp_i32<kDppSwap1>(kmn[2 * h][gr]));
+          const int e1 = min(kmn[2 * h + 1][gr], dpp_i32<kDppSwap1>(kmn[2 * h + 1][gr]));
+          pmn[h][gr] = odd1 ? e1 : e0;
+          const int f0 = max(kmx[2 * h][gr], dpp_i32<kDppSwap1>(kmx[2 * h][gr]));
+          const int f1 = max(kmx[2 * h + 1][gr], dpp_i32<kDppSwap1>(kmx[2 * h + 1][gr]));
+          pmx[h][gr] = odd1 ? f1 : f0;
         }
-      const Quant ql = quant_params(mn_l, mx_l);
-      Quant q[4][NG];
-      if constexpr (NG == 1) {
-        q[0][0] = Quant{quad_bcast<0>(ql.sz), __uint_as_float(quad_bcast<0>(__float_as_uint(ql.inv))),
-                        __uint_as_float(quad_bcast<0>(__float_as_uint(ql.zi)))};
-        q[1][0] = Quant{quad_bcast<1>(ql.sz), __uint_as_float(quad_bcast<1>(__float_as_uint(ql.inv))),
-                        __uint_as_float(quad_bcast<1>(__float_as_uint(ql.zi)))};
-        q[2][0] = Quant{quad_bcast<2>(ql.sz), __uint_as_float(quad_bcast<2>(__float_as_uint(ql.inv))),
-                        __uint_as_float(quad_bcast<2>(__float_as_uint(ql.zi)))};
-        q[3][0] = Quant{quad_bcast<3>(ql.sz), __uint_as_float(quad_bcast<3>(__float_as_uint(ql.inv))),
-                        __uint_as_float(quad_bcast<3>(__float_as_uint(ql.zi)))};
-      } else {
-        const int row0 = lane & 48;
+      Quant qo[NG];  // this lane's token 4g + (r & 3)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int gr = 0; gr < NG; ++gr) {
-            const int src = row0 + 4 * gr + i;
-            q[i][gr] = Quant{(uint32_t)__shfl((int)ql.sz, src), __shfl(ql.inv, src), __shfl(ql.zi, src)};
-          }
+      for (int gr = 0; gr < NG; ++gr) {
+        const int e0 = min(pmn[0][gr], dpp_i32<kDppSwap2>(pmn[0][gr]));
+        const int e1 = min(pmn[1][gr], dpp_i32<kDppSwap2>(pmn[1][gr]));
+        int lo = odd2 ? e1 : e0;
+        const int f0 = max(pmx[0][gr], dpp_i32<kDppSwap2>(pmx[0][gr]));
+        const int f1 = max(pmx[1][gr], dpp_i32<kDppSwap2>(pmx[1][gr]));
+        int hi = odd2 ? f1 : f0;
+        lo = min(lo, dpp_i32<kDppRor4>(lo));
+        hi = max(hi, dpp_i32<kDppRor4>(hi));
+        lo = min(lo, dpp_i32<kDppRor8>(lo));
+        hi = max(hi, dpp_i32<kDppRor8>(hi));
+        qo[gr] = quant_params(key2f(lo), key2f(hi));
       }
+      // token 4g + i's inverse scale and scaled zero from lane i of the quad
+      float inv[4][NG], zi[4][NG];
+#pragma unroll
+      for (int gr = 0; gr < NG; ++gr) {
+        const uint32_t iv = __float_as_uint(qo[gr].inv), zv = __float_as_uint(qo[gr].zi);
+        inv[0][gr] = __uint_as_float(quad_bcast<0>(iv));
+        inv[1][gr] = __uint_as_float(quad_bcast<1>(iv));
+        inv[2][gr] = __uint_as_float(quad_bcast<2>(iv));
+        inv[3][gr] = __uint_as_float(quad_bcast<3>(iv));
+        zi[0][gr] = __uint_as_float(quad_bcast<0>(zv));
+        zi[1][gr] = __uint_as_float(quad_bcast<1>(zv));
+        zi[2][gr] = __uint_as_float(quad_bcast<2>(zv));
+        zi[3][gr] = __uint_as_float(quad_bcast<3>(zv));
+      }
+      const int mi = r & 3, mk = (r >> 2) % NG;
+      uint32_t rec_sz = qo[0].sz;
+#pragma unroll
+      for (int gr = 1; gr < NG; ++gr) rec_sz = mk == gr ? qo[gr].sz : rec_sz;
       const bool rec_lane = r < 4 * NG;  // lane r stores the record of token 4g + mi, group mk
       // fast path: the tile's 16 tokens are slots 0..15 of one page, in order
       const int b0 = __builtin_amdgcn_readfirstlane(ti.b), pos0 = __builtin_amdgcn_readfirstlane(ti.pos);
@@ -304,20 +367,19 @@ __device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4
           (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bp));
       const bool mine = ti.blk != nullptr && ti.b == b0 && ti.pos == pos0 + r && (pos0 & 15) == 0;
       if (__all(mine)) {
-        uint32_t w[8];
+        // byte g of channel word 16 m + r holds tokens 4g .. 4g + 3: the low
+        // byte of the shifted code bits (kRoundBits lies above it)
+        uint8_t* vb = blk0 + kVCodes + 4 * r + g;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          uint32_t d = 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) d |= encode(acc[j][m][i], q[i][m / MPG].inv, q[i][m / MPG].zi) << (2 * (4 * g + i));
-          w[m] = or_rows(d);
+          uint32_t d = code_bits(acc[j][m][0], inv[0][m / MPG], zi[0][m / MPG]);
+          d = lshl_add<2>(code_bits(acc[j][m][1], inv[1][m / MPG], zi[1][m / MPG]), d);
+          d = lshl_add<4>(code_bits(acc[j][m][2], inv[2][m / MPG], zi[2][m / MPG]), d);
+          d = lshl_add<6>(code_bits(acc[j][m][3], inv[3][m / MPG], zi[3][m / MPG]), d);
+          vb[64 * m] = (uint8_t)d;
         }
-        uint32_t* vw = reinterpret_cast<uint32_t*>(blk0 + kVCodes);
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-          if ((m >> 1) == g) vw[16 * m + r] = w[m];
         // token 4g + i is slot 4g + i
-        if (rec_lane) *reinterpret_cast<uint32_t*>(blk0 + kMeta + 8 * (NG * (4 * g + mi) + mk) + 4) = ql.sz;
+        if (rec_lane) *reinterpret_cast<uint32_t*>(blk0 + kMeta + 8 * (NG * (4 * g + mi) + mk) + 4) = rec_sz;
       } else {
         // per-token info of the 4 tokens this lane holds codes for
         uint8_t* tblk[4];
@@ -335,9 +397,9 @@ __device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4
 #pragma unroll
           for (int m = 0; m < 8; ++m) {
             atomicAnd(&vw[16 * m + r], clr);
-            atomicOr(&vw[16 * m + r], encode(acc[j][m][i], q[i][m / MPG].inv, q[i][m / MPG].zi) << (2 * tslot[i]));
+            atomicOr(&vw[16 * m + r], (code_bits(acc[j][m][i], inv[i][m / MPG], zi[i][m / MPG]) & 3u) << (2 * tslot[i]));
           }
-          if (rec_lane && mi == i) *reinterpret_cast<uint32_t*>(tblk[i] + kMeta + 8 * (NG * tslot[i] + mk) + 4) = ql.sz;
+          if (rec_lane && mi == i) *reinterpret_cast<uint32_t*>(tblk[i] + kMeta + 8 * (NG * tslot[i] + mk) + 4) = rec_sz;
         }
       }
     }
