@@ -7,18 +7,20 @@
 // One workgroup = 4 waves = 64 tokens per iteration of one (KV head, K|V).
 // R (128 x 128 bf16) is staged once per workgroup in LDS.  Each wave rotates its
 // 16-token tile(s) with v_mfma_f32_16x16x32_bf16; every R tile read from LDS
-// feeds every token tile of the wave.  One tile per wave by default: at ~114
+// feeds every token tile of the wave.  One tile per wave by default: at ~110
 // VGPRs four waves share each SIMD, which measured faster than two tiles per
 // wave (fewer LDS reads of R) at two waves per SIMD.
 //  - keys use A = R, B = X^T: a lane ends with channels 16m + 4g + i (m = 0..7,
 //    i = 0..3) of ONE token, exactly the 8-byte segment g of the token's K row,
 //    so it writes that segment itself;
-//  - values use A = X, B = R^T: a lane ends with 4 tokens x 8 channels, so the
-//    channel-major V words (16 slots x 2 bits) are OR-ed over the 4 lane groups
-//    with permlane swaps and a whole aligned page is written with plain stores;
-//    a partial page falls back to per-token atomic and/or on the channel words.
-// The k-slot -> input channel map (lane group g, step s, slot j -> 32g + 8s + j)
-// is the same for both operands, so the hardware's internal k order is moot.
+//  - values use A = X, B = R^T: a lane ends with 4 tokens x 8 channels, that is
+//    byte g (slots 4g .. 4g + 3) of 8 channel-major V words (16 slots x 2 bits),
+//    and stores those bytes itself when the tile is a whole aligned page; a
+//    partial page falls back to per-token atomic and/or on the channel words.
+// The k-slot -> input channel map (lane group g, step s, slot j -> 32s + 8g + j)
+// is the same for both operands, so the hardware's internal k order is moot;
+// it makes the four lanes of a token read (and copy to the ring) one whole
+// 64-byte line per step.
 // Groups: with NG = 128 / g groups per token, group j is rotated channels
 // [g j, g (j + 1)); the channels 16m + .. a lane holds for accumulator m all fall
 // in group m NG / 8, so each group's min and max are reduced on their own and
@@ -64,7 +66,10 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-constexpr int kRowU4 = 17;  // LDS row stride of R in uint4 (16 + 1 pad: 272 B)
+// R in LDS: row o (output channel) holds its 16 chunks of 8 bf16 (k) at chunk
+// c ^ (o & 15), so the 16 rows a step reads at one chunk fall in 16 different
+// bank groups; unpadded, R takes exactly 32 KiB and five workgroups fit a CU.
+__device__ __forceinline__ int r_slot(int o, int c) { return o * 16 + (c ^ (o & 15)); }
 #ifndef OSCAR_APPEND_TILES
 #define OSCAR_APPEND_TILES 1
 #endif
@@ -199,18 +204,21 @@ __device__ __forceinline__ TokInfo resolve(const AppendParams& p, int b, int ps,
 }
 
 // X operand of tile j of a wave: token t0 + 16 j + r, input channels
-// 32 g .. 32 g + 31 (zero past the last token)
+// 32 s + 8 g .. 32 s + 8 g + 7 at step s (zero past the last token)
 template <int KIND>
 __device__ __forceinline__ void load_x(const AppendParams& p, int64_t t0, int h, int lane,
                                        uint4 (&xv)[kAppendTiles][4]) {
   const int g = lane >> 4, r = lane & 15;
 #pragma unroll
   for (int j = 0; j < kAppendTiles; ++j) {
-    const int64_t tok = t0 + 16 * j + r;
-    const bool valid = tok < p.n_tokens;
-    const uint4* xp = reinterpret_cast<const uint4*>(p.x[KIND] + ((valid ? tok : 0) * p.hkv + h) * kD + 32 * g);
+    // wave-uniform row base and a 32-bit lane offset (a token row is hkv * 256 B)
+    const int64_t tj = t0 + 16 * j;
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(p.x[KIND]) + (tj * p.hkv + h) * (2 * kD);
+    const bool valid = tj + r < p.n_tokens;
+    const uint32_t off = valid ? (uint32_t)r * (uint32_t)(p.hkv * 2 * kD) + 16u * g : 0u;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) xv[j][s] = valid ? xp[s] : make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < 4; ++s)
+      xv[j][s] = valid ? *reinterpret_cast<const uint4*>(xb + off + 64 * s) : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -239,7 +247,7 @@ __device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4
     for (int j = 0; j < NT; ++j) acc[j][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint4 rv = r_lds[(16 * m + r) * kRowU4 + 4 * g + s];
+      const uint4 rv = r_lds[r_slot(16 * m + r, 4 * s + g)];
 #pragma unroll
       for (int j = 0; j < NT; ++j) acc[j][m] = KIND == 0 ? mfma(rv, xv[j][s], acc[j][m]) : mfma(xv[j][s], rv, acc[j][m]);
     }
@@ -253,14 +261,14 @@ __device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4
 
     // raw bf16 copies into the ring (same for K and V): recent tokens, sinks
     if (ti.blk && ti.in_win) {
-      uint4* wp = reinterpret_cast<uint4*>(p.win[KIND] + (((int64_t)ti.b * p.ring + ti.pos % p.window) * p.hkv + h) * kD + 32 * g);
+      uint4* wp = reinterpret_cast<uint4*>(p.win[KIND] + (((int64_t)ti.b * p.ring + ti.pos % p.window) * p.hkv + h) * kD);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) wp[s] = xv[j][s];
+      for (int s = 0; s < 4; ++s) wp[4 * s + g] = xv[j][s];
     }
     if (ti.blk && ti.in_sink) {
-      uint4* wp = reinterpret_cast<uint4*>(p.win[KIND] + (((int64_t)ti.b * p.ring + p.window + ti.pos) * p.hkv + h) * kD + 32 * g);
+      uint4* wp = reinterpret_cast<uint4*>(p.win[KIND] + (((int64_t)ti.b * p.ring + p.window + ti.pos) * p.hkv + h) * kD);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) wp[s] = xv[j][s];
+      for (int s = 0; s < 4; ++s) wp[4 * s + g] = xv[j][s];
     }
 
     if (KIND == 0) {
@@ -410,7 +418,7 @@ __device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4
 // decode-time appends); its X rows then also go out before R is staged.
 template <int NG, bool ONE>
 __global__ __launch_bounds__(256, 4) void append_kernel(AppendParams p) {
-  __shared__ uint4 r_lds[128 * kRowU4];
+  __shared__ uint4 r_lds[128 * 16];
   const int h = blockIdx.y;
   const int kind = blockIdx.z & 1, layer = blockIdx.z >> 1;
   if (layer > 0) {  // static indices only: the parameters stay in scalar registers
@@ -422,7 +430,7 @@ __global__ __launch_bounds__(256, 4) void append_kernel(AppendParams p) {
     }
     p.pool += layer * p.ls_pool;
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   auto tile0 = [&](int it) {
     return ((int64_t)blockIdx.x * p.tiles_per_wg + it) * kAppendTokens + wave * 16 * kAppendTiles;
   };
@@ -451,7 +459,7 @@ __global__ __launch_bounds__(256, 4) void append_kernel(AppendParams p) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int i = threadIdx.x + 256 * k;
-    r_lds[(i >> 4) * kRowU4 + (i & 15)] = rr[k];
+    r_lds[r_slot(i >> 4, i & 15)] = rr[k];
   }
   __syncthreads();
   if constexpr (ONE) {
@@ -533,8 +541,16 @@ int append_impl(const oscar_shape* shape, int32_t n_layers, const uint16_t* r_k,
   p.ls_x = n_tokens * p.hkv * kD;
   p.ls_win = (int64_t)batch * p.ring * p.hkv * kD;
   p.ls_pool = n_pages * p.hkv * p.block;
-  const int64_t tiles = (n_tokens + kAppendTokens - 1) / kAppendTokens;  // workgroup iterations
-  p.tiles_per_wg = tiles >= 512 ? 4 : (tiles >= 128 ? 2 : 1);
+  // One launch-wide round of workgroups: as many as the device holds at once
+  // (4 per CU), each taking an equal run of 64-token iterations of one KV
+  // head, K or V, so the rotation is staged once per run and no partly filled
+  // second round trails the first (measured: 76 us for 65536 tokens x 8
+  // heads, against 82 us with 4 iterations per workgroup).
+  const int64_t tiles = (n_tokens + kAppendTokens - 1) / kAppendTokens;  // iterations per (head, K|V)
+  const int64_t slots = 4 * (int64_t)device_cu_count();
+  const int64_t streams = 2 * (int64_t)p.hkv * n_layers;
+  const int64_t tpw = (tiles * streams + slots - 1) / slots;
+  p.tiles_per_wg = (int)(tpw < 1 ? 1 : (tpw > tiles ? tiles : (tpw > (1 << 30) ? (1 << 30) : tpw)));
   dim3 grid((unsigned)((tiles + p.tiles_per_wg - 1) / p.tiles_per_wg), (unsigned)p.hkv, 2 * (unsigned)n_layers);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool one = p.tiles_per_wg == 1;
