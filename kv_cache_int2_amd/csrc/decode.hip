@@ -75,6 +75,24 @@ __device__ __forceinline__ uint4 load_nt4(const void* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// The same loads through a buffer resource on a block whose base is uniform
+// (a scalar register quad): the lane's 32-bit offset is the whole per-lane
+// address, so no 64-bit vector address arithmetic is spent per load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* blk) {
+  // raw buffer, no stride, no range limit in practice; dword 3 as this
+  // generation's raw buffer loads take it
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blk), 0, 0x7fffffff, 0x00020000);
+}
+constexpr int kBufNT = 2;  // cache policy: non-temporal
+__device__ __forceinline__ uint2 buffer_nt2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kBufNT);
+  return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ uint4 buffer_nt4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kBufNT);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 constexpr int kScaleOne = 127;   // E8M0 1.0
 constexpr int kScaleCode = 128;  // E8M0 2.0: an fp4 code nibble c reads as c / 2
 
@@ -150,6 +168,27 @@ __device__ __forceinline__ void digits_quad(float (&x)[4], uint32_t out[kDigits]
     }
   }
   rsum = (x[0] + x[1]) + (x[2] + x[3]);
+}
+
+// Row maxima as integer maxima, which take their DPP operand for free (a float
+// max first quiets both operands).  Non-negative floats order as their bits;
+// any float (-inf included) orders as b ^ ((b >> 31) & 0x7fffffff), which is its
+// own inverse.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xf, 0xf, true);
+}
+__device__ __forceinline__ int row_max16_i32(int v) {
+  v = max(v, dpp_i32<kDppSwap1>(v));
+  v = max(v, dpp_i32<kDppSwap2>(v));
+  v = max(v, dpp_i32<kDppHalfMirror>(v));
+  return max(v, dpp_i32<kDppMirror>(v));
+}
+__device__ __forceinline__ float row_max16_nonneg(float x) { return __int_as_float(row_max16_i32(__float_as_int(x))); }
+__device__ __forceinline__ float row_max16_any(float x) {
+  const int b = __float_as_int(x);
+  const int k = row_max16_i32(b ^ ((b >> 31) & 0x7fffffff));
+  return __int_as_float(k ^ ((k >> 31) & 0x7fffffff));
 }
 
 __device__ __forceinline__ int exponent_above(float x) {  // E with |x| < 2^E (0 for x == 0)
@@ -582,14 +621,14 @@ __device__ __forceinline__ void load_tile(const uint8_t* base_h, uint32_t stride
 #pragma unroll
   for (int pp = 0; pp < 8; ++pp) {
     const int e = __builtin_amdgcn_readlane(tt.ent, 8 * j + pp);
-    const uint8_t* blk = base_h + (uint64_t)(uint32_t)(e < 0 ? 0 : e) * stride;
-    t.kc[pp] = load_nt2(blk + off_k);
+    const __amdgpu_buffer_rsrc_t blk = block_rsrc(base_h + (uint64_t)(uint32_t)(e < 0 ? 0 : e) * stride);
+    t.kc[pp] = buffer_nt2(blk, off_k);
     if constexpr (NG == 1) {
-      t.meta[pp][0] = load_nt2(blk + off_m);
+      t.meta[pp][0] = buffer_nt2(blk, off_m);
     } else {
 #pragma unroll
       for (int q2 = 0; q2 < NG; q2 += 2) {
-        const uint4 m2 = load_nt4(blk + off_m + 8 * q2);
+        const uint4 m2 = buffer_nt4(blk, off_m + 8 * q2);
         t.meta[pp][q2] = make_uint2(m2.x, m2.y);
         t.meta[pp][q2 + 1] = make_uint2(m2.z, m2.w);
       }
@@ -615,6 +654,9 @@ __device__ __forceinline__ void load_tile(const uint8_t* base_h, uint32_t stride
 __device__ __forceinline__ float pin(float x) {
   asm volatile("" : "+v"(x));
   return x;
+}
+__device__ __forceinline__ void pin8(f32x4 (&c)[8]) {
+  asm volatile("" : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(c[4]), "+v"(c[5]), "+v"(c[6]), "+v"(c[7]));
 }
 
 // Running state of one wave: accumulators, running max, partial sums (the
@@ -666,19 +708,25 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
   // the dot product over group jg's channels of token lr of page pp ----
   float sc[NRG][8];
 #pragma unroll
-  for (int pp = 0; pp < 8; ++pp) {
+  for (int jg = 0; jg < NG; ++jg) {
 #pragma unroll
-    for (int rg = 0; rg < NRG; ++rg) sc[rg][pp] = 0.f;
+    for (int rg = 0; rg < NRG; ++rg) {
+      // the 8 pages' MFMAs first, all pinned at one point (every lane active),
+      // then their sums: no result is waited for right behind its MFMA
+      f32x4 c[8];
 #pragma unroll
-    for (int jg = 0; jg < NG; ++jg) {
-      i32x8 bk;
-      k_operand_group<NG>(t.kc[pp], jg, bk);
-      const float ks = h2f((uint16_t)(t.meta[pp][jg].x & 0xffffu));
-      const float kz = h2f((uint16_t)(t.meta[pp][jg].x >> 16));
+      for (int pp = 0; pp < 8; ++pp) {
+        i32x8 bk;
+        k_operand_group<NG>(t.kc[pp], jg, bk);
+        c[pp] = mfma_f8_f4(qa[rg], bk, f32x4{0.f, 0.f, 0.f, 0.f}, qsc[rg], kScaleCode);
+      }
+      pin8(c);
 #pragma unroll
-      for (int rg = 0; rg < NRG; ++rg) {
-        const f32x4 c = mfma_f8_f4(qa[rg], bk, f32x4{0.f, 0.f, 0.f, 0.f}, qsc[rg], kScaleCode);
-        sc[rg][pp] = pin(sc[rg][pp] + fmaf(kz, qsr[rg][jg], ks * ((c[0] + c[1]) + (c[2] + c[3]))));
+      for (int pp = 0; pp < 8; ++pp) {
+        const float ks = h2f((uint16_t)(t.meta[pp][jg].x & 0xffffu));
+        const float kz = h2f((uint16_t)(t.meta[pp][jg].x >> 16));
+        const float term = fmaf(kz, qsr[rg][jg], ks * ((c[pp][0] + c[pp][1]) + (c[pp][2] + c[pp][3])));
+        sc[rg][pp] = jg == 0 ? term : sc[rg][pp] + term;
       }
     }
   }
@@ -696,7 +744,7 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
       lgt[pp] = hv && live[pp] ? sc[rg][pp] : kNegInf;
       mx = fmaxf(mx, lgt[pp]);
     }
-    mx = row_max16(mx);
+    mx = row_max16_any(mx);
     const float m_new = fmaxf(st.m_run[rg], mx);
     if (__any(m_new > st.m_run[rg])) {
       const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(st.m_run[rg] - m_new);
@@ -730,7 +778,7 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
         ws += w[pp];
         wmax = fmaxf(wmax, w[pp]);
       }
-      const int e = exponent_above(row_max16(wmax));  // this head's weights in the tile are < 2^e
+      const int e = exponent_above(row_max16_nonneg(wmax));  // this head's weights in the tile are < 2^e
       const float wmul = ldexpf(1.f, 3 - e);           // w wmul < 8, exact (a power of two)
       float rsum = 0.f;
       uint8_t* tile_rg = wt + (rg * NG + jg) * 2048;
