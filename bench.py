@@ -263,6 +263,25 @@ def main():
         }
     assert torch.isfinite(out).all()
 
+    # ---- the decode call alone (prep, split, merge), back to back on layer 0 ----
+    def call_time(reps=20):
+        for _ in range(2):
+            K.oscar_decode_attn(shape, rkd, rvd, q, lensd, nmax, btd, pools[0], wks[0], wvs[0], out, ws)
+        K.oscar_gpu_wait(3000)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            K.oscar_decode_attn(shape, rkd, rvd, q, lensd, nmax, btd, pools[0], wks[0], wvs[0], out, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3
+    b_call = b_hist + b_win + b_rot + b_q_out + b_bt
+    t_call = call_time()
+    res_call = {"ms": t_call * 1e3, "bytes": b_call, "gbs": b_call / t_call / 1e9,
+                "frac_hbm": b_call / t_call / 1e9 / PEAK_HBM_GBS,
+                "workload": "one oscar_decode_attn call (prep, split, merge kernels), calls back to back"}
+    log(f"decode call {t_call * 1e6:.1f} us, {b_call / t_call / 1e9:.0f} GB/s")
+
     res_append = None if args.no_append else append_leg(K, torch, dev, shape, rkd, rvd, args, tok_bytes)
 
     # ---- layer batching: the L layers' decodes as L calls vs one call ----
@@ -329,6 +348,7 @@ def main():
                    "decode_tokens_per_s": B / dt, "step_bytes": step_bytes_int2},
         "bf16_kv": res_bf16,
         "speedup_vs_bf16": (res_bf16["ms_per_step"] / (dt * 1e3)) if res_bf16 else None,
+        "decode_call": res_call,
         "hbm_probe": probe,
         "host_enqueue_ms_per_step": host_ms.get("step_int2"),
         "append": res_append,
@@ -379,15 +399,16 @@ def hbm_probes(K, torch, dev, pool_all, n_pages_total):
                             ("half_page_read_gbs", page // 2, True), ("head_block_read_gbs", page // 8, True)):
         n = total // bb
         blocks = torch.from_numpy(gen.permutation(n).astype(np.int32)).to(dev) if table else None
-        K.oscar_hbm_read(pool_all, bb, blocks, n, sink)
-        torch.cuda.synchronize()
-        reps = 5
-        e0.record()
-        for _ in range(reps):
-            K.oscar_hbm_read(pool_all, bb, blocks, n, sink)
-        e1.record()
-        torch.cuda.synchronize()
-        res[name] = total * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+        for nt in (False, True):  # plain loads, and the non-temporal hint the decode's loads carry
+            K.oscar_hbm_read(pool_all, bb, blocks, n, sink, nt=nt)
+            torch.cuda.synchronize()
+            reps = 5
+            e0.record()
+            for _ in range(reps):
+                K.oscar_hbm_read(pool_all, bb, blocks, n, sink, nt=nt)
+            e1.record()
+            torch.cuda.synchronize()
+            res[name.replace("_gbs", "_nt_gbs") if nt else name] = total * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
     res["bytes_per_read"] = total
     log("HBM probes (GB/s): " + ", ".join(f"{k} {v:.0f}" for k, v in res.items() if k.endswith("gbs")))
     return res

@@ -322,7 +322,8 @@ int oscar_bf16_decode_attn(const oscar_shape* shape, const uint16_t* q, int32_t 
  *   and stores the XOR of what it read to sink[w] (device uint32
  *   [n_workgroups or 8 x compute units]).  It measures the HBM read ceiling of
  *   the decode's access shapes: whole pages or single KV-head blocks scattered
- *   through a block table, or one sequential stream.
+ *   through a block table, or one sequential stream.  oscar_hbm_read_nt: the
+ *   same with the non-temporal load hint the decode's loads carry.
  * oscar_gpu_wait: enqueues a one-wave kernel that returns after `microseconds`
  *   (0 .. 10^7) of the device's wall clock and touches no memory; it holds the
  *   stream while the host enqueues the launches to be timed behind it, without
@@ -340,6 +341,8 @@ int oscar_bf16_decode_attn(const oscar_shape* shape, const uint16_t* q, int32_t 
 int oscar_hbm_copy(const void* src, void* dst, size_t bytes, void* stream);
 int oscar_hbm_read(const void* src, int64_t block_bytes, const int32_t* blocks, int64_t n_blocks, uint32_t* sink,
                    int32_t n_workgroups, void* stream);
+int oscar_hbm_read_nt(const void* src, int64_t block_bytes, const int32_t* blocks, int64_t n_blocks,
+                      uint32_t* sink, int32_t n_workgroups, void* stream);
 int oscar_gpu_wait(int64_t microseconds, void* stream);
 int oscar_event_create(void** event);
 int oscar_event_destroy(void* event);

@@ -435,10 +435,12 @@ def oscar_hbm_copy(src, dst, nbytes: int | None = None, stream=None) -> None:
     _check("oscar_hbm_copy", lib.oscar_hbm_copy(src.data_ptr(), dst.data_ptr(), n, _stream(stream)))
 
 
-def oscar_hbm_read(src, block_bytes_: int, blocks, n_blocks: int, sink, n_workgroups: int = 0, stream=None) -> None:
+def oscar_hbm_read(src, block_bytes_: int, blocks, n_blocks: int, sink, n_workgroups: int = 0, stream=None,
+                   nt: bool = False) -> None:
     """Read probe: n_blocks blocks of block_bytes_ from the device buffer src,
     block i at blocks[i] (int32 device tensor) or, with blocks None, at i;
-    sink: int32/uint32 device tensor of at least n_workgroups (0: 8 per CU) words."""
+    sink: int32/uint32 device tensor of at least n_workgroups (0: 8 per CU) words.
+    nt: the loads carry the non-temporal hint (oscar_hbm_read_nt)."""
     _, i32, _, _ = _dt()
     import torch
 
@@ -450,7 +452,8 @@ def oscar_hbm_read(src, block_bytes_: int, blocks, n_blocks: int, sink, n_workgr
         _want(blocks, ((">=", n_blocks),), "blocks")
     if sink.dtype not in (torch.int32, torch.uint32) or sink.device.type != "cuda":
         raise TypeError("sink: int32 device tensor")
-    _check("oscar_hbm_read", lib.oscar_hbm_read(
+    fn = "oscar_hbm_read_nt" if nt else "oscar_hbm_read"
+    _check(fn, getattr(lib, fn)(
         src.data_ptr(), int(block_bytes_), _dev(blocks, i32, "blocks"), int(n_blocks), sink.data_ptr(),
         int(n_workgroups), _stream(stream)))
 

@@ -44,6 +44,7 @@ SIGNATURES = {
     "oscar_bf16_decode_attn": (C.c_int, [SHAPE, P, I32, P, I32, P, I32, P, I64, P, P, SZ, P]),
     "oscar_hbm_copy": (C.c_int, [P, P, SZ, P]),
     "oscar_hbm_read": (C.c_int, [P, I64, P, I64, P, I32, P]),
+    "oscar_hbm_read_nt": (C.c_int, [P, I64, P, I64, P, I32, P]),
     "oscar_gpu_wait": (C.c_int, [I64, P]),
     "oscar_event_create": (C.c_int, [C.POINTER(P)]),
     "oscar_event_destroy": (C.c_int, [P]),

@@ -567,7 +567,7 @@ __device__ __forceinline__ void combine_and_store(const float* cm, const float* 
 template <int NG>
 struct Tile {
   uint2 kc[8];        // K row bytes 8lg..8lg+7 of token lr, per page
-  uint2 meta[8][NG];  // token lr's records {Ks, Kz, Vs, Vz}, one per group (any value past the history end)
+  uint4 rec[NG];      // 16 bytes of the tile's records (see load_tile); any value past the history end
   uint4 vlo[2], vhi[2];  // V words of channels 8lr..8lr+7, pages 2lg and 2lg+1
   uint32_t page_ok;      // bit pp: page pp of the tile exists in this split and in the pool
 };
@@ -616,23 +616,22 @@ __device__ __forceinline__ void load_tile(const uint8_t* base_h, uint32_t stride
                                           int lr, Tile<NG>& t) {
   t.page_ok = (uint32_t)(tt.live >> (8 * j)) & 0xffu;
   const uint32_t off_k = kKCodes + 32 * lr + 8 * lg;
-  const uint32_t off_m = kMeta + 8 * NG * lr;
   const uint32_t off_v = kVCodes + 32 * lr;
 #pragma unroll
   for (int pp = 0; pp < 8; ++pp) {
     const int e = __builtin_amdgcn_readlane(tt.ent, 8 * j + pp);
     const __amdgpu_buffer_rsrc_t blk = block_rsrc(base_h + (uint64_t)(uint32_t)(e < 0 ? 0 : e) * stride);
     t.kc[pp] = buffer_nt2(blk, off_k);
-    if constexpr (NG == 1) {
-      t.meta[pp][0] = buffer_nt2(blk, off_m);
-    } else {
+  }
+  // records: one 16-byte chunk per lane and group block, lane 8 p + c taking
+  // chunk c of page p's 128 NG record bytes (every lane a distinct address;
+  // the lanes of one token read them from LDS, see spread_records)
+  {
+    const int lane = threadIdx.x & 63;
+    const int pr = __builtin_amdgcn_ds_bpermute(4 * (8 * j + (lane >> 3)), tt.ent);
+    const uint8_t* blk = base_h + (uint64_t)(uint32_t)(pr < 0 ? 0 : pr) * stride + kMeta + 16 * (lane & 7);
 #pragma unroll
-      for (int q2 = 0; q2 < NG; q2 += 2) {
-        const uint4 m2 = buffer_nt4(blk, off_m + 8 * q2);
-        t.meta[pp][q2] = make_uint2(m2.x, m2.y);
-        t.meta[pp][q2 + 1] = make_uint2(m2.z, m2.w);
-      }
-    }
+    for (int k = 0; k < NG; ++k) t.rec[k] = load_nt4(blk + 128 * k);
   }
   // V words: lane group lg takes pages 2lg and 2lg + 1 (entries of lanes
   // 8j + 2lg + qq, fetched across lanes)
@@ -690,10 +689,40 @@ __device__ __forceinline__ void k_operand_group(const uint2 kc, int jg, i32x8& b
   bk[4] = bk[5] = bk[6] = bk[7] = 0;
 }
 
+// The tile's records reach the lanes that use them through the wave's LDS
+// region rb (128 NG bytes per page): token lr's records of page pp, one per
+// group, into meta[pp][jg] ({Ks, Kz} in .x, {Vs, Vz} in .y).
+template <int NG>
+__device__ __forceinline__ void spread_records(const Tile<NG>& t, uint8_t* rb, int lr, uint2 (&meta)[8][NG]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < NG; ++k)
+    *reinterpret_cast<uint4*>(rb + (lane >> 3) * 128 * NG + 128 * k + 16 * (lane & 7)) = t.rec[k];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int pp = 0; pp < 8; ++pp) {
+    const uint8_t* src = rb + pp * 128 * NG + 8 * NG * lr;
+    if constexpr (NG == 1) {
+      meta[pp][0] = *reinterpret_cast<const uint2*>(src);
+    } else {
+#pragma unroll
+      for (int q2 = 0; q2 < NG; q2 += 2) {
+        const uint4 m2 = *reinterpret_cast<const uint4*>(src + 8 * q2);
+        meta[pp][q2] = make_uint2(m2.x, m2.y);
+        meta[pp][q2 + 1] = make_uint2(m2.z, m2.w);
+      }
+    }
+  }
+}
+
 template <int G, int NRG, bool FULL, int NG>  // FULL: all 8 pages exist and every token is below t_end
 __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG>& t, int pbase, int t_beg, int t_end,
                                              int lg, int lr, const i32x8* qa, const int* qsc, const float (*qsr)[NG],
-                                             uint8_t* wt, WaveState<NRG, NG>& st) {
+                                             uint8_t* wt, uint8_t* rb, WaveState<NRG, NG>& st) {
+  uint2 meta[8][NG];
+  spread_records(t, rb, lr, meta);
   const int slot_pos = 8 * (lr & 1) + (lr >> 1);  // k position of token lr within its page's 16
   // slots past the history end or on a missing page may hold anything: their
   // records must not reach the per-tile scale exponent or the sums
@@ -723,8 +752,8 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
       pin8(c);
 #pragma unroll
       for (int pp = 0; pp < 8; ++pp) {
-        const float ks = h2f((uint16_t)(t.meta[pp][jg].x & 0xffffu));
-        const float kz = h2f((uint16_t)(t.meta[pp][jg].x >> 16));
+        const float ks = h2f((uint16_t)(meta[pp][jg].x & 0xffffu));
+        const float kz = h2f((uint16_t)(meta[pp][jg].x >> 16));
         const float term = fmaf(kz, qsr[rg][jg], ks * ((c[pp][0] + c[pp][1]) + (c[pp][2] + c[pp][3])));
         sc[rg][pp] = jg == 0 ? term : sc[rg][pp] + term;
       }
@@ -771,7 +800,7 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
       for (int pp = 0; pp < 8; ++pp) {
         // value scale and zero of (page pp, group jg); a dead slot's record may
         // hold anything (NaN included), so it is replaced by zeros first
-        const uint32_t vrec = live[pp] ? t.meta[pp][jg].y : 0u;
+        const uint32_t vrec = live[pp] ? meta[pp][jg].y : 0u;
         const float vs = h2f((uint16_t)(vrec & 0xffffu)), vz = h2f((uint16_t)(vrec >> 16));
         st.az_part[rg][jg] = fmaf(pv[pp], fmaf(1.5f, vs, vz), st.az_part[rg][jg]);
         w[pp] = pv[pp] * vs;
@@ -907,6 +936,7 @@ template <int G, int NG>
 __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
   constexpr int NRG = (G + 3) / 4;  // MFMA row groups of 4 heads
   __shared__ __align__(16) uint8_t smem[4 * NRG * NG * 2048];  // per-wave weight-digit tiles
+  __shared__ __align__(16) uint8_t recs[4 * NG * 1024];         // per-wave record staging
 
   const int hg_per_seq = p.hkv / p.hw;  // KV head groups per sequence
   const int per_seq = hg_per_seq * p.gsub;
@@ -916,6 +946,7 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
   const int lg = lane >> 4, lr = lane & 15;
   const int ts = 4 / p.hw;  // waves sharing a head (tile stride)
   uint8_t* wt = smem + wave * (NRG * NG * 2048);
+  uint8_t* rb = recs + wave * (NG * 1024);
   const int ncb = (p.gw * p.gsub + 3) / 4;
   const int64_t wave_part = (int64_t)p.gw * kPartStride;  // floats of one wave's partial
   // equal shares [T w / nw, T (w + 1) / nw) of the T flattened tiles
@@ -989,7 +1020,7 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
     TileTable tab = table_ready(p, table_load(btr, P0, P1, ph, ts, 0), P0, P1, ph, ts, 0, ntw);
     int raw_next = table_load(btr, P0, P1, ph, ts, 2);
     auto compute = [&](const Tile<NG>& t, int pbase) {
-      compute_tile<G, NRG, false, NG>(p, t, pbase, t_beg, t_end, lg, lr, qa, qsc, qsr, wt, st);
+      compute_tile<G, NRG, false, NG>(p, t, pbase, t_beg, t_end, lg, lr, qa, qsc, qsr, wt, rb, st);
     };
     if constexpr (NRG > 1 || NG > 2) {  // one tile in flight per wave (registers)
       for (int s = 0;; ++s) {

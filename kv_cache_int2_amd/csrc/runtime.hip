@@ -22,6 +22,7 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src
 // quotient is off by less than one).  Without a table, chunk c is src[c].  The
 // XOR of everything a workgroup read goes to sink[w], so no load can be dropped.
 constexpr int kReadUnroll = 8;
+template <bool NT>  // NT: the loads carry the non-temporal hint, as the decode's do
 __global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ src, const int32_t* __restrict__ blocks,
                                                    int64_t n_blocks, int cpb, double inv_cpb,
                                                    uint32_t* __restrict__ sink) {
@@ -47,7 +48,13 @@ __global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ src
         }
         at = (int64_t)blocks[blk] * cpb + off;
       }
-      v[j] = src[at];
+      if constexpr (NT) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + at));
+        v[j] = make_uint4(t[0], t[1], t[2], t[3]);
+      } else {
+        v[j] = src[at];
+      }
     }
 #pragma unroll
     for (int j = 0; j < kReadUnroll; ++j)
@@ -126,18 +133,33 @@ extern "C" int oscar_hbm_copy(const void* src, void* dst, size_t bytes, void* st
   return hipGetLastError() == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
 }
 
-extern "C" int oscar_hbm_read(const void* src, int64_t block_bytes, const int32_t* blocks, int64_t n_blocks,
-                              uint32_t* sink, int32_t n_workgroups, void* stream) {
+namespace oscar {
+namespace {
+int hbm_read(bool nt, const void* src, int64_t block_bytes, const int32_t* blocks, int64_t n_blocks, uint32_t* sink,
+             int32_t n_workgroups, void* stream) {
   if (!src || !sink || block_bytes < 16 || (block_bytes & 15) || block_bytes > (1 << 20) || n_blocks < 0 ||
       n_workgroups < 0 || n_workgroups > OSCAR_READ_MAX_WORKGROUPS || (reinterpret_cast<uintptr_t>(src) & 15))
     return OSCAR_EINVAL;
   if (n_blocks == 0) return OSCAR_OK;
   const int cpb = (int)(block_bytes / 16);
   if (n_blocks > ((int64_t)1 << 40) / cpb) return OSCAR_EINVAL;
-  const int wg = n_workgroups > 0 ? n_workgroups : 8 * oscar::device_cu_count();
-  oscar::read_kernel<<<(unsigned)wg, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
-      static_cast<const uint4*>(src), blocks, n_blocks, cpb, 1.0 / (double)cpb, sink);
+  const int wg = n_workgroups > 0 ? n_workgroups : 8 * device_cu_count();
+  auto kernel = nt ? read_kernel<true> : read_kernel<false>;
+  kernel<<<(unsigned)wg, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(static_cast<const uint4*>(src), blocks,
+                                                                         n_blocks, cpb, 1.0 / (double)cpb, sink);
   return hipGetLastError() == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
+}
+}  // namespace
+}  // namespace oscar
+
+extern "C" int oscar_hbm_read(const void* src, int64_t block_bytes, const int32_t* blocks, int64_t n_blocks,
+                              uint32_t* sink, int32_t n_workgroups, void* stream) {
+  return oscar::hbm_read(false, src, block_bytes, blocks, n_blocks, sink, n_workgroups, stream);
+}
+
+extern "C" int oscar_hbm_read_nt(const void* src, int64_t block_bytes, const int32_t* blocks, int64_t n_blocks,
+                                 uint32_t* sink, int32_t n_workgroups, void* stream) {
+  return oscar::hbm_read(true, src, block_bytes, blocks, n_blocks, sink, n_workgroups, stream);
 }
 
 extern "C" int oscar_gpu_wait(int64_t microseconds, void* stream) {
