@@ -568,7 +568,7 @@ template <int NG>
 struct Tile {
   uint2 kc[8];        // K row bytes 8lg..8lg+7 of token lr, per page
   uint4 rec[NG];      // 16 bytes of the tile's records (see load_tile); any value past the history end
-  uint4 vlo[2], vhi[2];  // V words of channels 8lr..8lr+7, pages 2lg and 2lg+1
+  uint4 vlo[2], vhi[2];  // V words of channels 4lr..4lr+3 (lo), 64+4lr..64+4lr+3 (hi), pages 2lg and 2lg+1
   uint32_t page_ok;      // bit pp: page pp of the tile exists in this split and in the pool
 };
 
@@ -616,7 +616,7 @@ __device__ __forceinline__ void load_tile(const uint8_t* base_h, uint32_t stride
                                           int lr, Tile<NG>& t) {
   t.page_ok = (uint32_t)(tt.live >> (8 * j)) & 0xffu;
   const uint32_t off_k = kKCodes + 32 * lr + 8 * lg;
-  const uint32_t off_v = kVCodes + 32 * lr;
+  const uint32_t off_v = kVCodes + 16 * lr;  // 16 lanes read 256 contiguous bytes per half
 #pragma unroll
   for (int pp = 0; pp < 8; ++pp) {
     const int e = __builtin_amdgcn_readlane(tt.ent, 8 * j + pp);
@@ -640,7 +640,7 @@ __device__ __forceinline__ void load_tile(const uint8_t* base_h, uint32_t stride
     const int pv = __builtin_amdgcn_ds_bpermute(4 * (8 * j + 2 * lg + qq), tt.ent);
     const uint8_t* blk = base_h + (uint64_t)(uint32_t)(pv < 0 ? 0 : pv) * stride + off_v;
     t.vlo[qq] = load_nt4(blk);
-    t.vhi[qq] = load_nt4(blk + 16);
+    t.vhi[qq] = load_nt4(blk + 256);
   }
   // no use of the loaded registers here: the caller computes another tile
   // while these loads are in flight
@@ -835,24 +835,25 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // ---- values: acc[rg][nn] += weight digits x V codes (channels 8lr + nn) ----
-  // with NG > 1 the column of lane lr (channels 8 lr .. 8 lr + 7) belongs to
-  // group lr / (16 / NG).  The MFMA of group jg scales the codes of the other
-  // groups' columns by 2^-127 (E8M0 0) instead of 2 (its B scale is per lane,
-  // i.e. per column): their products with group jg's weights land ~2^-128 below
-  // the true products, under fp32 resolution of any accumulator they join, and no
-  // instruction is spent masking them.
+  // ---- values: acc[rg][nn] += weight digits x V codes (channel vch(nn) of
+  // column lr: 4 lr + nn for nn < 4, 64 + 4 lr + nn - 4 above) ----
+  // with NG > 1 the column's channel in the MFMAs nn < 4 belongs to group
+  // lr NG / 32, in nn >= 4 to group NG / 2 + lr NG / 32.  The MFMA of group jg
+  // scales the codes of the other groups' columns by 2^-127 (E8M0 0) instead of
+  // 2 (its B scale is per lane, i.e. per column): their products with group jg's
+  // weights land ~2^-128 below the true products, under fp32 resolution of any
+  // accumulator they join, and no instruction is spent masking them.
   // A-operand scale of row lr (head lr / 4 of the row group, digit lr % 4): that
   // head's exponent lives on the lanes of row lr / 4
   const int src_row = 4 * 16 * (lr >> 2);
-  const int my_grp = lr / (16 / NG);
-  float corr[NRG];
+  const int grp_lo = lr * NG / 32, grp_hi = NG / 2 + lr * NG / 32;
+  float corr_lo[NRG], corr_hi[NRG];
 #pragma unroll
-  for (int rg = 0; rg < NRG; ++rg) corr[rg] = 0.f;
+  for (int rg = 0; rg < NRG; ++rg) corr_lo[rg] = corr_hi[rg] = 0.f;
 #pragma unroll
   for (int jg = 0; jg < NG; ++jg) {
-    const bool mine = NG == 1 || my_grp == jg;
-    const int sb = mine ? kScaleCode : 0;
+    const bool mine_lo = NG == 1 || grp_lo == jg, mine_hi = NG == 1 || grp_hi == jg;
+    const int sb_lo = mine_lo ? kScaleCode : 0, sb_hi = mine_hi ? kScaleCode : 0;
     i32x8 wa[NRG];
     int wsc[NRG];
 #pragma unroll
@@ -870,7 +871,8 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
       wa[rg][7] = (int)a1.w;
       const int eh = __builtin_amdgcn_ds_bpermute(src_row, wexp[rg][jg]);
       wsc[rg] = clamp_scale(kScaleOne + eh - 3 - 4 * (lr & 3));
-      corr[rg] = mine ? 1.5f * wsum[rg][jg] : corr[rg];
+      corr_lo[rg] = mine_lo ? 1.5f * wsum[rg][jg] : corr_lo[rg];
+      corr_hi[rg] = mine_hi ? 1.5f * wsum[rg][jg] : corr_hi[rg];
     }
 #pragma unroll
     for (int nn = 0; nn < 8; ++nn) {
@@ -883,13 +885,14 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
       bv[3] = (int)((v1 >> 2) & 0x33333333u);
       bv[4] = bv[5] = bv[6] = bv[7] = 0;
 #pragma unroll
-      for (int rg = 0; rg < NRG; ++rg) st.acc[rg][nn] = mfma_f8_f4(wa[rg], bv, st.acc[rg][nn], wsc[rg], sb);
+      for (int rg = 0; rg < NRG; ++rg)
+        st.acc[rg][nn] = mfma_f8_f4(wa[rg], bv, st.acc[rg][nn], wsc[rg], nn < 4 ? sb_lo : sb_hi);
     }
   }
 #pragma unroll
   for (int rg = 0; rg < NRG; ++rg)
 #pragma unroll
-    for (int nn = 0; nn < 8; ++nn) st.acc[rg][nn][0] -= corr[rg];
+    for (int nn = 0; nn < 8; ++nn) st.acc[rg][nn][0] -= nn < 4 ? corr_lo[rg] : corr_hi[rg];
   __builtin_amdgcn_wave_barrier();
 }
 
@@ -910,9 +913,10 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
 // with stealing) measured slower than these static shares on this part.
 // Lane l = 16 lg + lr:
 //   score MFMA output: head 4 rg + lg, token lr of the page;
-//   value accumulators: head 4 rg + lg, channels 8 lr + n (n = 0..7);
-//   loads per tile: K row bytes 8lg..8lg+7 of token lr and its metadata record
-//   for each of the 8 pages; V words of channels 8lr..8lr+7 for pages 2lg, 2lg+1.
+//   value accumulators: head 4 rg + lg, channels 4 lr + n and 64 + 4 lr + n (n = 0..3);
+//   loads per tile: K row bytes 8lg..8lg+7 of token lr for each of the 8 pages,
+//   the tile's records (one 16-byte chunk per lane);
+//   V words of those 8 channels for pages 2lg, 2lg+1.
 // Each wave keeps two tiles in flight (the loads of its next tile go out before
 // the current one is computed); two workgroups per CU.
 // ---------------------------------------------------------------------------
@@ -1052,7 +1056,8 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
       }
     }
 
-    // ---- the wave's partial: lane (lg, lr) holds channels 8 lr .. 8 lr + 7 of head 4 rg + lg ----
+    // ---- the wave's partial: lane (lg, lr) holds channels 4 lr .. 4 lr + 3 and
+    // 64 + 4 lr .. 64 + 4 lr + 3 of head 4 rg + lg ----
     // (the accumulators are pinned here, with every lane active: otherwise the
     // last tile's value MFMAs could be sunk into the per-lane store branch)
 #pragma unroll
@@ -1064,22 +1069,25 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
 #pragma unroll
     for (int rg = 0; rg < NRG; ++rg) {
       const float l = row_sum16(st.l_part[rg]);
-      // midpoint sum of the group of this lane's channels 8 lr .. 8 lr + 7
-      float az = 0.f;
+      // midpoint sums of the groups of this lane's two channel runs
+      float az_lo = 0.f, az_hi = 0.f;
 #pragma unroll
       for (int jg = 0; jg < NG; ++jg) {
         const float a = row_sum16(st.az_part[rg][jg]);
-        az = (NG == 1 || lr / (16 / NG) == jg) ? a : az;
+        az_lo = (NG == 1 || lr * NG / 32 == jg) ? a : az_lo;
+        az_hi = (NG == 1 || NG / 2 + lr * NG / 32 == jg) ? a : az_hi;
       }
       const int head = 4 * rg + lg;
       if (head < p.gw) {
         float* d = dst + head * kPartStride;
 #pragma unroll
         for (int nn = 0; nn < 8; nn += 2) {
+          const float az = nn < 4 ? az_lo : az_hi;
           const float x0 = (st.acc[rg][nn][0] + st.acc[rg][nn][1]) + (st.acc[rg][nn][2] + st.acc[rg][nn][3]) + az;
           const float x1 =
               (st.acc[rg][nn + 1][0] + st.acc[rg][nn + 1][1]) + (st.acc[rg][nn + 1][2] + st.acc[rg][nn + 1][3]) + az;
-          *reinterpret_cast<float2*>(d + 2 + 8 * lr + nn) = make_float2(x0, x1);
+          const int ch = nn < 4 ? 4 * lr + nn : 64 + 4 * lr + nn - 4;
+          *reinterpret_cast<float2*>(d + 2 + ch) = make_float2(x0, x1);
         }
         if (lr == 0) *reinterpret_cast<float2*>(d) = make_float2(st.m_run[rg], l);
       }
