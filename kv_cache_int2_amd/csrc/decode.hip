@@ -568,6 +568,7 @@ template <int NG>
 struct Tile {
   uint2 kc[8];        // K row bytes 8lg..8lg+7 of token lr, per page
   uint4 rec[NG];      // 16 bytes of the tile's records (see load_tile); any value past the history end
+  uint2 meta[8][NG];  // or, without the LDS spread: token lr's records, one per page and group
   uint4 vlo[2], vhi[2];  // V words of channels 4lr..4lr+3 (lo), 64+4lr..64+4lr+3 (hi), pages 2lg and 2lg+1
   uint32_t page_ok;      // bit pp: page pp of the tile exists in this split and in the pool
 };
@@ -611,7 +612,10 @@ __device__ __forceinline__ TileTable table_ready(const SplitParams& p, int raw, 
 // 32-bit offset; a missing page is read as page 0 and masked, so the memory
 // system sees the whole tile at once.  base_h: the KV head's block in page 0;
 // stride: bytes per page (all KV heads).
-template <int NG>
+// REC: the records come as one 16-byte chunk per lane (spread through LDS by
+// spread_records); otherwise each lane loads its token's records itself (the
+// register-heavier instantiations, where the LDS spread's live range spills).
+template <int NG, bool REC = true>
 __device__ __forceinline__ void load_tile(const uint8_t* base_h, uint32_t stride, const TileTable& tt, int j, int lg,
                                           int lr, Tile<NG>& t) {
   t.page_ok = (uint32_t)(tt.live >> (8 * j)) & 0xffu;
@@ -622,11 +626,24 @@ __device__ __forceinline__ void load_tile(const uint8_t* base_h, uint32_t stride
     const int e = __builtin_amdgcn_readlane(tt.ent, 8 * j + pp);
     const __amdgpu_buffer_rsrc_t blk = block_rsrc(base_h + (uint64_t)(uint32_t)(e < 0 ? 0 : e) * stride);
     t.kc[pp] = buffer_nt2(blk, off_k);
+    if constexpr (!REC) {
+      const uint32_t off_m = kMeta + 8 * NG * lr;
+      if constexpr (NG == 1) {
+        t.meta[pp][0] = buffer_nt2(blk, off_m);
+      } else {
+#pragma unroll
+        for (int q2 = 0; q2 < NG; q2 += 2) {
+          const uint4 m2 = buffer_nt4(blk, off_m + 8 * q2);
+          t.meta[pp][q2] = make_uint2(m2.x, m2.y);
+          t.meta[pp][q2 + 1] = make_uint2(m2.z, m2.w);
+        }
+      }
+    }
   }
   // records: one 16-byte chunk per lane and group block, lane 8 p + c taking
   // chunk c of page p's 128 NG record bytes (every lane a distinct address;
   // the lanes of one token read them from LDS, see spread_records)
-  {
+  if constexpr (REC) {
     const int lane = threadIdx.x & 63;
     const int pr = __builtin_amdgcn_ds_bpermute(4 * (8 * j + (lane >> 3)), tt.ent);
     const uint8_t* blk = base_h + (uint64_t)(uint32_t)(pr < 0 ? 0 : pr) * stride + kMeta + 16 * (lane & 7);
@@ -717,12 +734,19 @@ __device__ __forceinline__ void spread_records(const Tile<NG>& t, uint8_t* rb, i
   }
 }
 
-template <int G, int NRG, bool FULL, int NG>  // FULL: all 8 pages exist and every token is below t_end
+template <int G, int NRG, bool FULL, int NG, bool REC>  // FULL: all 8 pages exist and every token is below t_end
 __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG>& t, int pbase, int t_beg, int t_end,
                                              int lg, int lr, const i32x8* qa, const int* qsc, const float (*qsr)[NG],
                                              uint8_t* wt, uint8_t* rb, WaveState<NRG, NG>& st) {
   uint2 meta[8][NG];
-  spread_records(t, rb, lr, meta);
+  if constexpr (REC) {
+    spread_records(t, rb, lr, meta);
+  } else {
+#pragma unroll
+    for (int pp = 0; pp < 8; ++pp)
+#pragma unroll
+      for (int jg = 0; jg < NG; ++jg) meta[pp][jg] = t.meta[pp][jg];
+  }
   const int slot_pos = 8 * (lr & 1) + (lr >> 1);  // k position of token lr within its page's 16
   // slots past the history end or on a missing page may hold anything: their
   // records must not reach the per-tile scale exponent or the sums
@@ -736,6 +760,24 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
   // sc[rg][pp] = sum over groups jg of ks_jg (q'_(4rg+lg) . code) + kz_jg qsum_jg,
   // the dot product over group jg's channels of token lr of page pp ----
   float sc[NRG][8];
+  if constexpr (NRG > 1) {  // registers: one page at a time, each score pinned
+#pragma unroll
+    for (int pp = 0; pp < 8; ++pp) {
+#pragma unroll
+      for (int jg = 0; jg < NG; ++jg) {
+        i32x8 bk;
+        k_operand_group<NG>(t.kc[pp], jg, bk);
+        const float ks = h2f((uint16_t)(meta[pp][jg].x & 0xffffu));
+        const float kz = h2f((uint16_t)(meta[pp][jg].x >> 16));
+#pragma unroll
+        for (int rg = 0; rg < NRG; ++rg) {
+          const f32x4 c = mfma_f8_f4(qa[rg], bk, f32x4{0.f, 0.f, 0.f, 0.f}, qsc[rg], kScaleCode);
+          const float term = fmaf(kz, qsr[rg][jg], ks * ((c[0] + c[1]) + (c[2] + c[3])));
+          sc[rg][pp] = pin(jg == 0 ? term : sc[rg][pp] + term);
+        }
+      }
+    }
+  } else {
 #pragma unroll
   for (int jg = 0; jg < NG; ++jg) {
 #pragma unroll
@@ -758,6 +800,7 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
         sc[rg][pp] = jg == 0 ? term : sc[rg][pp] + term;
       }
     }
+  }
   }
   // ---- online softmax, weights, weight digits -> LDS ----
   float wsum[NRG][NG];  // sum of the weights as the digits carry them
@@ -939,8 +982,9 @@ __device__ __forceinline__ int find_unit(const int* tp, int units, int64_t t) {
 template <int G, int NG>
 __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
   constexpr int NRG = (G + 3) / 4;  // MFMA row groups of 4 heads
-  __shared__ __align__(16) uint8_t smem[4 * NRG * NG * 2048];  // per-wave weight-digit tiles
-  __shared__ __align__(16) uint8_t recs[4 * NG * 1024];         // per-wave record staging
+  constexpr bool kRecLds = NRG == 1 && NG <= 2;  // records spread through LDS (see load_tile)
+  __shared__ __align__(16) uint8_t smem[4 * NRG * NG * 2048];        // per-wave weight-digit tiles
+  __shared__ __align__(16) uint8_t recs[kRecLds ? 4 * NG * 1024 : 16];  // per-wave record staging
 
   const int hg_per_seq = p.hkv / p.hw;  // KV head groups per sequence
   const int per_seq = hg_per_seq * p.gsub;
@@ -1024,15 +1068,15 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
     TileTable tab = table_ready(p, table_load(btr, P0, P1, ph, ts, 0), P0, P1, ph, ts, 0, ntw);
     int raw_next = table_load(btr, P0, P1, ph, ts, 2);
     auto compute = [&](const Tile<NG>& t, int pbase) {
-      compute_tile<G, NRG, false, NG>(p, t, pbase, t_beg, t_end, lg, lr, qa, qsc, qsr, wt, rb, st);
+      compute_tile<G, NRG, false, NG, kRecLds>(p, t, pbase, t_beg, t_end, lg, lr, qa, qsc, qsr, wt, rb, st);
     };
     if constexpr (NRG > 1 || NG > 2) {  // one tile in flight per wave (registers)
       for (int s = 0;; ++s) {
         const int k = 2 * s;
         Tile<NG> t;
-        load_tile(base_h, stride, tab, 0, lg, lr, t);
+        load_tile<NG, kRecLds>(base_h, stride, tab, 0, lg, lr, t);
         compute(t, pbase_of(k));
-        load_tile(base_h, stride, tab, 1, lg, lr, t);
+        load_tile<NG, kRecLds>(base_h, stride, tab, 1, lg, lr, t);
         compute(t, pbase_of(k + 1));
         if (s + 1 >= ns) break;
         tab = table_ready(p, raw_next, P0, P1, ph, ts, k + 2, ntw);
@@ -1040,17 +1084,17 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
       }
     } else {  // two tiles in flight per wave: tile k + 1's loads go out before tile k is computed
       Tile<NG> ta, tb;
-      load_tile(base_h, stride, tab, 0, lg, lr, ta);
+      load_tile<NG, kRecLds>(base_h, stride, tab, 0, lg, lr, ta);
       for (int s = 0;; ++s) {
         const int k = 2 * s;
-        load_tile(base_h, stride, tab, 1, lg, lr, tb);
+        load_tile<NG, kRecLds>(base_h, stride, tab, 1, lg, lr, tb);
         compute(ta, pbase_of(k));
         const bool more = s + 1 < ns;
         // past the last step the table is empty: tile k + 2 re-reads page 0's
         // block (cache resident) and is never computed
         tab = table_ready(p, raw_next, P0, P1, ph, ts, k + 2, more ? ntw : 0);
         raw_next = table_load(btr, P0, P1, ph, ts, k + 4);
-        load_tile(base_h, stride, tab, 0, lg, lr, ta);
+        load_tile<NG, kRecLds>(base_h, stride, tab, 0, lg, lr, ta);
         compute(tb, pbase_of(k + 1));
         if (!more) break;
       }
