@@ -261,7 +261,7 @@ __device__ __forceinline__ SplitParams layer_params(const SplitParams& p, int l)
 // faster and is given the larger share (with equal shares it finished ~15 us
 // before its partner at 100K context, every CU alike).
 struct ShareWeights {
-  int64_t wf, ws, hf, total;
+  int wf, ws, hf, total;  // total = wf hf + ws (nw - hf) <= 26 x 2^16
 };
 // With fewer than 4 tiles per workgroup the shares are equal, so that every
 // workgroup keeps at least one tile (the weights satisfy wf <= 3 ws).
@@ -274,17 +274,26 @@ __device__ __forceinline__ ShareWeights share_weights(const SplitParams& p, int6
   s.total = s.wf * s.hf + s.ws * (nw - s.hf);
   return s;
 }
+// floor(a / b) for 0 <= a < 2^52, 0 < b < 2^31: the fp64 quotient (correctly
+// rounded, so at most one off after the floor) corrected with integer
+// products, instead of a 64-bit integer division's long instruction sequence.
+__device__ __forceinline__ int64_t div_floor(int64_t a, int64_t b) {
+  int64_t q = (int64_t)((double)a / (double)b);
+  if (q * b > a) q -= 1;
+  else if ((q + 1) * b <= a) q += 1;
+  return q;
+}
 __device__ __forceinline__ int64_t share_begin(const SplitParams& p, int64_t T, int nw, int w) {
   const ShareWeights s = share_weights(p, T, nw);
-  const int64_t cum = w <= s.hf ? s.wf * w : s.wf * s.hf + s.ws * (w - s.hf);
-  return T * cum / s.total;
+  const int cum = w <= s.hf ? s.wf * w : s.wf * s.hf + s.ws * (w - s.hf);
+  return div_floor(T * cum, s.total);
 }
 // The workgroup whose share holds tile t (0 <= t < T): the largest w with
 // share_begin(w) <= t, i.e. with cum(w) <= ((t + 1) total - 1) / T.
 __device__ __forceinline__ int64_t share_owner(const SplitParams& p, int64_t T, int nw, int64_t t) {
   const ShareWeights s = share_weights(p, T, nw);
-  const int64_t c = ((t + 1) * s.total - 1) / T;
-  const int64_t w = c < s.wf * s.hf ? c / s.wf : s.hf + (c - s.wf * s.hf) / s.ws;
+  const int c = (int)div_floor((t + 1) * s.total - 1, T);
+  const int w = c < s.wf * s.hf ? c / s.wf : s.hf + (c - s.wf * s.hf) / s.ws;
   return w < nw - 1 ? w : nw - 1;
 }
 
