@@ -702,13 +702,14 @@ def summarize_pmc(fetch_dir: str, write_dir: str, command: str, bench_json: str 
         # bytes_per_read bytes (sequential and through random page tables)
         line = [json.loads(x) for x in open(bench_json) if x.startswith("{")][-1]
         nbytes = float(line["hbm_probe"]["bytes_per_read"])
-        reads = [float(r["Counter_Value"]) * 1024.0 for r in _csv_rows(fetch_dir, "counter_collection.csv")
-                 if r["Counter_Name"] == "FETCH_SIZE" and _short_kernel(r["Kernel_Name"]) == "read_kernel"]
-        if reads:
-            sc = nbytes / np.asarray(reads)
-            lines.append(f"read_probe_bytes_per_launch: {nbytes:.0f}")
-            lines.append(f"read_probe_fetch_scale: min {sc.min():.4f} median {np.median(sc):.4f} max {sc.max():.4f} "
-                         f"({len(sc)} dispatches)")
+        lines.append(f"read_probe_bytes_per_launch: {nbytes:.0f}")
+        for variant, tag in (("read_kernel", ""), ("read_kernel<false>", ""), ("read_kernel<true>", "_nt")):
+            reads = [float(r["Counter_Value"]) * 1024.0 for r in _csv_rows(fetch_dir, "counter_collection.csv")
+                     if r["Counter_Name"] == "FETCH_SIZE" and _short_kernel(r["Kernel_Name"]) == variant]
+            if reads:
+                sc = nbytes / np.asarray(reads)
+                lines.append(f"read_probe{tag}_fetch_scale: min {sc.min():.4f} median {np.median(sc):.4f} "
+                             f"max {sc.max():.4f} ({len(sc)} dispatches)")
     return "\n".join(lines) + "\n"
 
 
