@@ -192,6 +192,10 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
 }
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xf, 0xf, true);
+}
 constexpr int kDppSwap1 = 0xB1;       // quad_perm [1, 0, 3, 2]
 constexpr int kDppSwap2 = 0x4E;       // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within each 8 lanes

@@ -174,10 +174,6 @@ __device__ __forceinline__ void digits_quad(float (&x)[4], uint32_t out[kDigits]
 // max first quiets both operands).  Non-negative floats order as their bits;
 // any float (-inf included) orders as b ^ ((b >> 31) & 0x7fffffff), which is its
 // own inverse.
-template <int CTRL>
-__device__ __forceinline__ int dpp_i32(int x) {
-  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xf, 0xf, true);
-}
 __device__ __forceinline__ int row_max16_i32(int v) {
   v = max(v, dpp_i32<kDppSwap1>(v));
   v = max(v, dpp_i32<kDppSwap2>(v));

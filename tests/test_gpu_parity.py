@@ -168,6 +168,18 @@ def test_append_sinks_no_window(K):
     append_case(K, make_spec(1, [77, 20], window=0, n_sink=64), split_at=30, seed=6)
 
 
+def test_append_inorder_many_iterations(K):
+    # over 4096 tokens per launch (on 256 CUs): workgroups run more than one
+    # 128-token iteration, the next tile's rows loaded while the current one is
+    # encoded; the second sequence ends in a partial page
+    append_case(K, make_spec(1, [4500, 337], window=100), seed=7)
+
+
+def test_append_shuffled_many_iterations(K):
+    # the same with the tokens shuffled: every tile takes the per-token path
+    append_case(K, make_spec(1, [2500, 1700, 701], window=64, n_sink=16), order="shuffled", seed=8)
+
+
 def test_append_single_tokens(K):
     s = make_spec(5, [40, 17, 1, 99, 64], hq=64)
     rng = np.random.default_rng(4)
