@@ -3,9 +3,11 @@
 Workload: long-context decode, batch 8, 100000 tokens per sequence, 32 q / 8 KV
 heads, head_dim 128, INT2 history + 128-token bf16 window, 16-token pages
 scattered in a shared pool (synthetic Gaussian K/V with 4 key outlier channels
-x20, seeded).  One step = append the current token of every sequence
-(oscar_quantize_append) + decode attention over the whole context
-(oscar_decode_attn).  Calibration runs once beforehand (it is an offline,
+x20, seeded).  One step = append the current token of every sequence + decode
+attention over the whole context, as one oscar_decode_step (the appends run in
+the decode's query-preparation launch); the same step as the two plain calls
+(oscar_quantize_append, oscar_decode_attn) is timed beside it.  Calibration runs
+once beforehand (it is an offline,
 once-per-model step).  The same step on a bf16 paged cache (oscar_bf16_append +
 oscar_bf16_decode_attn) on identical inputs is timed in the same session.
 
@@ -187,6 +189,18 @@ def main():
     out = torch.empty((B, HQ, 128), dtype=torch.float32, device=dev)
 
     def step_int2(i, ev=None):
+        # the fused step: the newest token's append runs in the decode's
+        # query-preparation launch
+        l = i % L
+        if ev is None:
+            K.oscar_decode_step(shape, rkd, rvd, cur_kd, cur_vd, q, lensd, nmax, btd, pools[l], wks[l], wvs[l],
+                                out, ws)
+        else:
+            K.oscar_decode_step_timed(shape, rkd, rvd, cur_kd, cur_vd, q, lensd, nmax, btd, pools[l], wks[l], wvs[l],
+                                      out, ws, *ev)
+
+    def step_int2_two_calls(i, ev=None):
+        # the same step as two calls: oscar_quantize_append, oscar_decode_attn
         l = i % L
         K.oscar_quantize_append(shape, rkd, rvd, cur_kd, cur_vd, cur_si, cur_pos, btd, lensd, pools[l], wks[l], wvs[l])
         if ev is None:
@@ -252,6 +266,12 @@ def main():
         sa = np.asarray(split_all)
         log(f"split launches (ms): first {sa[0]:.4f} min {sa.min():.4f} median {np.median(sa):.4f} max {sa.max():.4f}")
     log(f"INT2 step {dt * 1e3:.3f} ms, split kernel {split_s * 1e3 if split_s else float('nan'):.3f} ms")
+    # the same step as the two plain calls (append, then decode)
+    dt2, split_s2, _ = timed(step_int2_two_calls)
+    res_two = {"ms_per_step": dt2 * 1e3, "gbs": step_bytes_int2 / dt2 / 1e9,
+               "split_kernel_ms": split_s2 * 1e3 if split_s2 else None,
+               "workload": "the same step as oscar_quantize_append + oscar_decode_attn"}
+    log(f"INT2 step as two calls {dt2 * 1e3:.3f} ms")
     res_bf16 = None
     if kvp:
         dtb, split_b, _ = timed(step_bf16)
@@ -343,13 +363,15 @@ def main():
         "vs_baseline": None,
         "dtype": "int2 codes as fp4 x e4m3 terms (MFMA), f32 accumulate",
         "data": "synthetic (seeded Gaussian K/V, 4 key outlier channels x20; no dataset exists for this path)",
-        "config": {"workload": f"long-context decode step: append 1 token/seq + INT2 decode, B={B}, n={nmax}, "
+        "config": {"workload": f"long-context decode step (oscar_decode_step): append 1 token/seq + INT2 decode, "
+                               f"B={B}, n={nmax}, "
                                f"{HQ}q/{HKV}kv heads, d=128, group {G}, 16-token scattered pages, bf16 window {W}"
                                + (f" + {S} sink tokens" if S else ""),
                    "layers_rotated": L, "pct_of_hbm_peak": 100 * step_bytes_int2 / dt / 1e9 / PEAK_HBM_GBS,
                    "decode_tokens_per_s": B / dt, "step_bytes": step_bytes_int2},
         "bf16_kv": res_bf16,
         "speedup_vs_bf16": (res_bf16["ms_per_step"] / (dt * 1e3)) if res_bf16 else None,
+        "step_two_calls": res_two,
         "decode_call": res_call,
         "hbm_probe": probe,
         "host_enqueue_ms_per_step": host_ms.get("step_int2"),

@@ -256,6 +256,36 @@ int oscar_decode_attn_noalloc(const oscar_shape* shape, const uint16_t* r_k, con
                               void* stream);
 
 /*
+ * One decode step: appending the newest token of every sequence, then decode
+ * attention over the whole sequence (P2 «OSCAR има значение…»: each generated
+ * token's K/V enter the cache, recent ones in bf16, before the next query is
+ * answered; P1 «Что придумали в Together AI» for the rotation of both).
+ * k_new, v_new: bf16 [batch][n_kv_heads][128], token b of sequence b at
+ * position seq_lens[b] - 1 (seq_lens are the lengths after the append); a
+ * sequence with seq_lens[b] < 1 or > max_seq_len gets no new token.  Every
+ * other argument as for oscar_decode_attn, except that pool, win_k and win_v
+ * are written.  The pool, the rings and out end exactly as after
+ * oscar_quantize_append (seq_idx[b] = b, pos[b] = seq_lens[b] - 1,
+ * seq_len_after = seq_lens) followed by oscar_decode_attn on the same stream:
+ * the appends run in the decode's query-preparation launch, whose window
+ * workgroups read the new tokens from k_new / v_new instead of the ring rows
+ * being written.  Errors as the two calls; OSCAR_EINVAL also for a NULL k_new
+ * or v_new or either not 16-byte aligned.  The _timed form takes two events as
+ * the other *_timed entry points (attached to the split kernel).
+ */
+int oscar_decode_step(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v, const uint16_t* k_new,
+                      const uint16_t* v_new, const uint16_t* q, int32_t batch, const int32_t* seq_lens,
+                      int32_t max_seq_len, const int32_t* block_table, int32_t max_pages_per_seq, uint8_t* pool,
+                      int64_t n_pages, uint16_t* win_k, uint16_t* win_v, float* out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+int oscar_decode_step_timed(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
+                            const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q, int32_t batch,
+                            const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
+                            int32_t max_pages_per_seq, uint8_t* pool, int64_t n_pages, uint16_t* win_k,
+                            uint16_t* win_v, float* out, void* workspace, size_t workspace_bytes, void* stream,
+                            void* ev_start, void* ev_stop);
+
+/*
  * Layer-batched forms: the caches of n_layers layers (every layer holding the
  * same sequences, as the layers of one model do) in one call, one launch per
  * kernel instead of one per layer (the rotation-file workflow calibrates and

@@ -21,6 +21,7 @@ __all__ = [
     "oscar_decode_workspace_bytes", "oscar_decode_attn", "oscar_bf16_append",
     "oscar_bf16_decode_attn", "oscar_hbm_copy", "oscar_hbm_read", "oscar_gpu_wait", "Event",
     "oscar_quantize_append_timed", "oscar_decode_attn_timed", "oscar_bf16_decode_attn_timed",
+    "oscar_decode_step", "oscar_decode_step_timed",
     "oscar_strerror", "BLOCK_BYTES", "BF16_BLOCK_ELEMS", "PAGE_SIZE", "HEAD_DIM", "block_bytes",
     "oscar_calibrate_layers", "oscar_rotation_file_bytes", "oscar_rotation_write", "oscar_rotation_read_info",
     "oscar_rotation_read", "oscar_quantize_append_layers", "oscar_decode_layers_workspace_bytes",
@@ -309,6 +310,40 @@ def oscar_decode_attn(shape, r_k, r_v, q, seq_lens, max_seq_len, block_table, po
     _check("oscar_decode_attn", lib.oscar_decode_attn(
         *_decode_args(shape, r_k, r_v, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v, out, workspace,
                       stream)))
+
+
+def _step_args(shape, r_k, r_v, k_new, v_new, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v, out,
+               workspace, stream):
+    b16, i32, u8, f32 = _dt()
+    batch = _decode_checks(shape, r_k, r_v, q, seq_lens, block_table, pool, win_k, win_v, out)
+    _want(k_new, (batch, shape.n_kv_heads, HEAD_DIM), "k_new")
+    _want(v_new, (batch, shape.n_kv_heads, HEAD_DIM), "v_new")
+    return (C.byref(shape), _dev(r_k, b16, "r_k"), _dev(r_v, b16, "r_v"), _dev(k_new, b16, "k_new"),
+            _dev(v_new, b16, "v_new"), _dev(q, b16, "q"), batch, _dev(seq_lens, i32, "seq_lens"), int(max_seq_len),
+            _dev(block_table, i32, "block_table"), int(block_table.shape[1]), _dev(pool, u8, "pool"),
+            int(pool.shape[0]), _dev(win_k, b16, "win_k"), _dev(win_v, b16, "win_v"), _dev(out, f32, "out"),
+            _dev(workspace, u8, "workspace"), int(workspace.numel()), _stream(stream))
+
+
+def oscar_decode_step(shape, r_k, r_v, k_new, v_new, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v,
+                      out, workspace, stream=None) -> None:
+    """One decode step: the new token (k_new[b], v_new[b]) [B][Hkv][128] of
+    every sequence b appended at position seq_lens[b] - 1 (seq_lens: the
+    lengths after it), then decode attention over the whole sequence; the
+    same pool, rings and output as oscar_quantize_append followed by
+    oscar_decode_attn, one launch fewer."""
+    _check("oscar_decode_step", lib.oscar_decode_step(
+        *_step_args(shape, r_k, r_v, k_new, v_new, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v, out,
+                    workspace, stream)))
+
+
+def oscar_decode_step_timed(shape, r_k, r_v, k_new, v_new, q, seq_lens, max_seq_len, block_table, pool, win_k,
+                            win_v, out, workspace, start, stop, stream=None) -> None:
+    """oscar_decode_step with the Event pair (start, stop) attached to the
+    split kernel's launch."""
+    _check("oscar_decode_step_timed", lib.oscar_decode_step_timed(
+        *_step_args(shape, r_k, r_v, k_new, v_new, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v, out,
+                    workspace, stream), start.handle, stop.handle))
 
 
 def oscar_decode_attn_timed(shape, r_k, r_v, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v,

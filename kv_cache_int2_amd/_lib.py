@@ -51,6 +51,9 @@ SIGNATURES = {
     "oscar_event_elapsed_ms": (C.c_int, [P, P, C.POINTER(C.c_float)]),
     "oscar_quantize_append_timed": (C.c_int, [SHAPE, P, P, P, P, I64, P, P, I32, P, I32, P, P, I64, P, P, P, P, P]),
     "oscar_decode_attn_timed": (C.c_int, [SHAPE, P, P, P, I32, P, I32, P, I32, P, I64, P, P, P, P, SZ, P, P, P]),
+    "oscar_decode_step": (C.c_int, [SHAPE, P, P, P, P, P, I32, P, I32, P, I32, P, I64, P, P, P, P, SZ, P]),
+    "oscar_decode_step_timed": (C.c_int, [SHAPE, P, P, P, P, P, I32, P, I32, P, I32, P, I64, P, P, P, P, SZ, P, P,
+                                          P]),
     "oscar_bf16_decode_attn_timed": (C.c_int, [SHAPE, P, I32, P, I32, P, I32, P, I64, P, P, SZ, P, P, P]),
     "oscar_strerror": (C.c_char_p, [C.c_int]),
 }

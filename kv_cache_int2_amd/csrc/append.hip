@@ -36,6 +36,10 @@ __global__ __launch_bounds__(kAppendThreads) __attribute__((amdgpu_waves_per_eu(
   // branch on it
   auto body = [&](auto kind_c) {
     constexpr int KIND = decltype(kind_c)::value;
+    if constexpr (ONE) {
+      append_one<KIND, NG, kAppendThreads, false>(p, r_lds, h, tile0(0), lane);
+      return;
+    }
     // the first tile's token indices and rows go out before the rotation is
     // staged
     TileIdx in;
@@ -43,30 +47,16 @@ __global__ __launch_bounds__(kAppendThreads) __attribute__((amdgpu_waves_per_eu(
     const bool any = tile0(0) < p.n_tokens;  // uniform across the wave
     if (any) {
       load_idx(p, tile0(0), lane, in);
-      if constexpr (ONE)
-        load_x<KIND>(p, tile0(0), h, lane, xv);
-      else
-        dma_x<KIND>(p, tile0(0), h, lane, xbuf);
+      dma_x<KIND>(p, tile0(0), h, lane, xbuf);
     }
-    const uint4* rg = reinterpret_cast<const uint4*>(p.r[KIND] + (int64_t)h * kD * kD);
-    constexpr int kRPer = 128 * 16 / kAppendThreads;  // R chunks staged per thread
-    uint4 rr[kRPer];
-#pragma unroll
-    for (int k = 0; k < kRPer; ++k) rr[k] = rg[threadIdx.x + kAppendThreads * k];
+    RStage<kAppendThreads> rs;
+    r_load<kAppendThreads>(p.r[KIND], h, rs);
     if (any) {
 #pragma unroll
       for (int j = 0; j < kAppendTiles; ++j) in.pl[j] = lookup(p, in.b[j], in.ps[j]);
     }
-#pragma unroll
-    for (int k = 0; k < kRPer; ++k) {
-      const int i = threadIdx.x + kAppendThreads * k;
-      r_lds[r_slot(i >> 4, i & 15)] = rr[k];
-    }
+    r_store<kAppendThreads>(r_lds, rs);
     __syncthreads();
-    if constexpr (ONE) {
-      if (any) process_tiles<KIND, NG>(p, r_lds, in, xv, tile0(0), h, lane, [] {});
-      return;
-    }
     TileIdx nxt;  // raw indices of the next tile, loaded while this one is processed
     for (int it = 0; it < p.tiles_per_wg; ++it) {
       const int64_t t0 = tile0(it);

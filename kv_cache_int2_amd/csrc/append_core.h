@@ -57,6 +57,7 @@ struct AppendParams {
   int64_t n_pages;
   int batch, max_pages, hkv, window, tiles_per_wg;
   int n_sink;  // leading positions also kept in bf16 (ring rows window + pos)
+  int max_len;  // the fused decode step's max_seq_len (implicit token indices only)
   int ring;    // ring rows per sequence: window + n_sink
   // layers appended in one launch: rotations, tokens, rings and pools stacked
   // layer-major with these strides (elements; pool in bytes); positions, block
@@ -188,6 +189,10 @@ struct TileIdx {
   int2 pl[kAppendTiles];  // lookup(b, ps)
 };
 
+// IMPLICIT (the fused decode step): token t is the newest token of sequence
+// t, at position len_after[t] - 1; a sequence whose length is not in
+// [1, max_len] gets none.  seq_idx and pos are not read.
+template <bool IMPLICIT = false>
 __device__ __forceinline__ void load_idx(const AppendParams& p, int64_t t0, int lane, TileIdx& in) {
   const int r = lane & 15;
 #pragma unroll
@@ -195,7 +200,15 @@ __device__ __forceinline__ void load_idx(const AppendParams& p, int64_t t0, int 
     const int64_t tok = t0 + 16 * j + r;
     const bool valid = tok < p.n_tokens;
     const int64_t tc = valid ? tok : p.n_tokens - 1;  // every lane loads: no branch
-    const int b = p.seq_idx[tc], ps = p.pos[tc];
+    int b, ps;
+    if constexpr (IMPLICIT) {
+      const int n = p.len_after[tc];
+      b = (int)tc;
+      ps = n >= 1 && n <= p.max_len ? n - 1 : -1;
+    } else {
+      b = p.seq_idx[tc];
+      ps = p.pos[tc];
+    }
     in.b[j] = valid ? b : -1;
     in.ps[j] = valid ? ps : -1;
   }
@@ -466,6 +479,52 @@ __device__ __forceinline__ void process_tiles(const AppendParams& p, const uint4
       }
     }
   }
+}
+
+// R of (head h, kind KIND) staged in LDS by THREADS threads: loaded into
+// registers first (r_load), written swizzled after other loads have been
+// issued (r_store); the caller passes the barrier.
+template <int THREADS>
+struct RStage {
+  uint4 v[128 * 16 / THREADS];
+};
+template <int THREADS>
+__device__ __forceinline__ void r_load(const uint16_t* r, int h, RStage<THREADS>& rs) {
+  const uint4* rg = reinterpret_cast<const uint4*>(r + (int64_t)h * kD * kD);
+#pragma unroll
+  for (int k = 0; k < 128 * 16 / THREADS; ++k) rs.v[k] = rg[threadIdx.x + THREADS * k];
+}
+template <int THREADS>
+__device__ __forceinline__ void r_store(uint4* r_lds, const RStage<THREADS>& rs) {
+#pragma unroll
+  for (int k = 0; k < 128 * 16 / THREADS; ++k) {
+    const int i = threadIdx.x + THREADS * k;
+    r_lds[r_slot(i >> 4, i & 15)] = rs.v[k];
+  }
+}
+
+// A workgroup of THREADS / 64 waves with one 16-token tile per wave (the
+// wave's first token t0): the tile's indices and rows go out before R is
+// staged, so their latency overlaps its load.  Every thread of the workgroup
+// calls it (it passes a barrier); r_lds is 32 KiB of LDS.
+template <int KIND, int NG, int THREADS, bool IMPLICIT>
+__device__ __forceinline__ void append_one(const AppendParams& p, uint4* r_lds, int h, int64_t t0, int lane) {
+  TileIdx in;
+  uint4 xv[kAppendTiles][4];
+  const bool any = t0 < p.n_tokens;  // uniform across the wave
+  if (any) {
+    load_idx<IMPLICIT>(p, t0, lane, in);
+    load_x<KIND>(p, t0, h, lane, xv);
+  }
+  RStage<THREADS> rs;
+  r_load<THREADS>(p.r[KIND], h, rs);
+  if (any) {
+#pragma unroll
+    for (int j = 0; j < kAppendTiles; ++j) in.pl[j] = lookup(p, in.b[j], in.ps[j]);
+  }
+  r_store<THREADS>(r_lds, rs);
+  __syncthreads();
+  if (any) process_tiles<KIND, NG>(p, r_lds, in, xv, t0, h, lane, [] {});
 }
 
 }  // namespace

@@ -158,7 +158,8 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
                   const int32_t* block_table, int32_t max_pages_per_seq, const uint8_t* pool,
                   const uint16_t* kv_pool, int64_t n_pages, const uint16_t* win_k, const uint16_t* win_v,
                   float* out, void* workspace, size_t workspace_bytes, void* stream, int n_layers = 1,
-                  TimedLaunch tl = TimedLaunch{nullptr, nullptr}, bool int2_only = false);
+                  TimedLaunch tl = TimedLaunch{nullptr, nullptr}, bool int2_only = false,
+                  const uint16_t* k_new = nullptr, const uint16_t* v_new = nullptr);
 
 }  // namespace oscar
 

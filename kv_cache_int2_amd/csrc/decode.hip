@@ -50,7 +50,7 @@
 // split (p zero + p scale code) makes two terms ~2.5 sigma sum p that cancel to a
 // long-context output ~ sigma sum p / sqrt(n); their fp32 rounding would be
 // amplified by that ratio (~300x at 100K tokens).
-#include "common.h"
+#include "append_core.h"
 
 namespace oscar {
 namespace {
@@ -231,6 +231,11 @@ struct SplitParams {
   // INT2: share weights of the split workgroups: wf for the first hf, ws for
   // the rest (see share_begin)
   int wf, ws, hf;
+  // INT2, the fused decode step only (else null): the newest token of every
+  // sequence, [B][Hkv][128] bf16, appended by the prep kernel while the window
+  // chunks read it from here instead of the ring row being written
+  const uint16_t* k_new;
+  const uint16_t* v_new;
 };
 
 // The parameters of layer l: every per-layer buffer advanced by l strides.
@@ -348,6 +353,13 @@ __device__ void window_chunk(const SplitParams& p, int b, int h, int c, int G, f
     const int64_t row = (((int64_t)b * p.ring + slot) * p.hkv + h) * kD + 16 * part;
     const uint4* kr = reinterpret_cast<const uint4*>(p.win_k + row);
     const uint4* vr = reinterpret_cast<const uint4*>(p.win_v + row);
+    // the fused step's newest token (position n - 1, appended by this launch
+    // when the length is not clamped) comes from the new-token rows
+    if (p.k_new && valid && cs + t == n - 1 && p.seq_lens[b] == n) {
+      const int64_t nrow = ((int64_t)b * p.hkv + h) * kD + 16 * part;
+      kr = reinterpret_cast<const uint4*>(p.k_new + nrow);
+      vr = reinterpret_cast<const uint4*>(p.v_new + nrow);
+    }
     kk[0] = kr[0]; kk[1] = kr[1];
     vv[0] = vr[0]; vv[1] = vr[1];
   }
@@ -418,14 +430,35 @@ __device__ void window_chunk(const SplitParams& p, int b, int h, int c, int G, f
 //   E8M0 scale (2^(E - 3 - 4 digit), |q'| < 2^E), exactly as the split kernel's
 //   MFMA consumes it.
 // ---------------------------------------------------------------------------
-template <int G>
-__global__ __launch_bounds__(256) void prep_kernel(SplitParams p0, const uint16_t* __restrict__ r_k0) {
+//
+// NGA > 0 (the fused decode step, NGA quantisation groups per token): planes
+// z = 1 + n_wchunks + kind also append the newest token of every sequence
+// (kind 0: keys, 1: values) for KV head blockIdx.y, 64 sequences per
+// workgroup, exactly as the append kernel would (its device code, 4 waves of
+// one 16-token tile each).
+template <int G, int NGA>
+__global__ __launch_bounds__(256) void prep_kernel(SplitParams p0, const uint16_t* __restrict__ r_k0,
+                                                   AppendParams ap) {
   constexpr int NCB = (G + 3) / 4;  // 4-head operand groups
   static_assert(G <= 16, "the heads are the 16 columns of one MFMA");
   constexpr int kQBytes = 2 * G * kD * 4 + G * 4;
-  constexpr int kSmem = kQBytes > window_smem_bytes<G>() ? kQBytes : window_smem_bytes<G>();
+  constexpr int kSmem0 = kQBytes > window_smem_bytes<G>() ? kQBytes : window_smem_bytes<G>();
+  constexpr int kSmem = NGA > 0 && kSmem0 < 128 * 16 * 16 ? 128 * 16 * 16 : kSmem0;  // R of the append: 32 KiB
   __shared__ __align__(16) float smem_f[kSmem / 4];
   const int layer = blockIdx.x / p0.batch, b = blockIdx.x % p0.batch, h = blockIdx.y, tid = threadIdx.x;
+  if constexpr (NGA > 0) {
+    if ((int)blockIdx.z > p0.n_wchunks) {  // the newest tokens, one launch with the query preparation
+      const int64_t t_wg = (int64_t)blockIdx.x * 64;
+      if (t_wg >= ap.n_tokens) return;  // uniform over the workgroup
+      const int64_t t0 = t_wg + 16 * (tid >> 6);
+      uint4* r_lds = reinterpret_cast<uint4*>(smem_f);
+      if ((int)blockIdx.z == p0.n_wchunks + 1)
+        append_one<0, NGA, 256, true>(ap, r_lds, h, t0, tid & 63);
+      else
+        append_one<1, NGA, 256, true>(ap, r_lds, h, t0, tid & 63);
+      return;
+    }
+  }
   const SplitParams p = layer_params(p0, layer);
   const uint16_t* r_k = r_k0 + layer * p0.ls_rot;
   const int hq = p.hq, hkv = p.hkv;
@@ -1531,10 +1564,22 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p0, int gq, int 
 }
 
 template <int G>
-int launch_decode(bool int2, const SplitParams& sp, const uint16_t* r_k, int batch, hipStream_t s, TimedLaunch tl) {
+int launch_decode(bool int2, const SplitParams& sp, const uint16_t* r_k, int batch, hipStream_t s, TimedLaunch tl,
+                  const AppendParams* ap) {
   if (int2) {
-    // z = 0: rotated query and its MFMA operands, the tile prefix; z > 0: the bf16 window chunks
-    prep_kernel<G><<<dim3(batch * sp.n_layers, sp.hkv, 1 + sp.n_wchunks), 256, 0, s>>>(sp, r_k);
+    // z = 0: rotated query and its MFMA operands, the tile prefix; z > 0: the
+    // bf16 window chunks; with ap (the fused step) two more planes append the
+    // newest tokens' keys and values
+    const dim3 grid(batch * sp.n_layers, sp.hkv, 1 + sp.n_wchunks + (ap ? 2 : 0));
+    if (!ap) {
+      prep_kernel<G, 0><<<grid, 256, 0, s>>>(sp, r_k, AppendParams{});
+    } else {
+      switch (sp.ng) {
+        case 1: prep_kernel<G, 1><<<grid, 256, 0, s>>>(sp, r_k, *ap); break;
+        case 2: prep_kernel<G, 2><<<grid, 256, 0, s>>>(sp, r_k, *ap); break;
+        default: prep_kernel<G, 4><<<grid, 256, 0, s>>>(sp, r_k, *ap); break;
+      }
+    }
     if (hipGetLastError() != hipSuccess) return OSCAR_EHIP;
   }
   if (int2) {
@@ -1568,7 +1613,7 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
                   const int32_t* block_table, int32_t max_pages_per_seq, const uint8_t* pool,
                   const uint16_t* kv_pool, int64_t n_pages, const uint16_t* win_k, const uint16_t* win_v,
                   float* out, void* workspace, size_t workspace_bytes, void* stream, int n_layers, TimedLaunch tl,
-                  bool int2_only) {
+                  bool int2_only, const uint16_t* k_new, const uint16_t* v_new) {
   int st = check_shape(shape);
   if (st != OSCAR_OK) return st;
   if (check_events(tl) != OSCAR_OK) return OSCAR_EINVAL;
@@ -1579,6 +1624,8 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   if (int2 && shape->window + shape->n_sink > 0 && (!win_k || !win_v)) return OSCAR_EINVAL;
   if (!int2 && !kv_pool) return OSCAR_EINVAL;
   if ((int64_t)max_seq_len > (int64_t)max_pages_per_seq * kPage) return OSCAR_ENOSPACE;
+  const bool fused = k_new != nullptr || v_new != nullptr;  // the decode step: append, then attend
+  if (fused && (!int2 || n_layers != 1 || !k_new || !v_new)) return OSCAR_EINVAL;
   const int gqa = shape->n_q_heads / shape->n_kv_heads;
   const int n_cu = device_cu_count();
   const SplitPlan plan = plan_splits(batch, shape->n_kv_heads, gqa, max_seq_len, n_cu);
@@ -1589,7 +1636,8 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
   // rows are read as 16-byte vectors
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(r_k) | reinterpret_cast<uintptr_t>(r_v) |
        reinterpret_cast<uintptr_t>(pool) | reinterpret_cast<uintptr_t>(kv_pool) |
-       reinterpret_cast<uintptr_t>(win_k) | reinterpret_cast<uintptr_t>(win_v)) & 15)
+       reinterpret_cast<uintptr_t>(win_k) | reinterpret_cast<uintptr_t>(win_v) |
+       reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
     return OSCAR_EINVAL;
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -1650,13 +1698,41 @@ int decode_common(bool int2, const oscar_shape* shape, const uint16_t* r_k, cons
     sp.ls_wpart = (int64_t)(align256((nwp > 0 ? nwp : 1) * kPartStride * sizeof(float)) / sizeof(float));
   }
   sp.scale_log2 = kLog2e / sqrtf((float)kD);
+  // the fused step's append: token b of k_new / v_new at position
+  // seq_lens[b] - 1 of sequence b (seq_idx and pos implicit)
+  AppendParams ap{};
+  if (fused) {
+    sp.k_new = k_new;
+    sp.v_new = v_new;
+    ap.r[0] = r_k;
+    ap.r[1] = r_v;
+    ap.x[0] = k_new;
+    ap.x[1] = v_new;
+    ap.win[0] = const_cast<uint16_t*>(win_k);
+    ap.win[1] = const_cast<uint16_t*>(win_v);
+    ap.block_table = block_table;
+    ap.len_after = seq_lens;
+    ap.pool = const_cast<uint8_t*>(pool);
+    ap.block = sp.block;
+    ap.n_tokens = batch;
+    ap.n_pages = n_pages;
+    ap.batch = batch;
+    ap.max_pages = max_pages_per_seq;
+    ap.hkv = sp.hkv;
+    ap.window = sp.window;
+    ap.tiles_per_wg = 1;
+    ap.n_sink = sp.n_sink;
+    ap.ring = sp.ring;
+    ap.max_len = max_seq_len;
+  }
+  const AppendParams* app = fused ? &ap : nullptr;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (shape->n_q_heads / shape->n_kv_heads) {
-    case 1: return launch_decode<1>(int2, sp, r_k, batch, s, tl);
-    case 2: return launch_decode<2>(int2, sp, r_k, batch, s, tl);
-    case 4: return launch_decode<4>(int2, sp, r_k, batch, s, tl);
-    case 8: return launch_decode<8>(int2, sp, r_k, batch, s, tl);
-    case 16: return launch_decode<16>(int2, sp, r_k, batch, s, tl);
+    case 1: return launch_decode<1>(int2, sp, r_k, batch, s, tl, app);
+    case 2: return launch_decode<2>(int2, sp, r_k, batch, s, tl, app);
+    case 4: return launch_decode<4>(int2, sp, r_k, batch, s, tl, app);
+    case 8: return launch_decode<8>(int2, sp, r_k, batch, s, tl, app);
+    case 16: return launch_decode<16>(int2, sp, r_k, batch, s, tl, app);
   }
   return OSCAR_EUNSUPPORTED;
 }
@@ -1780,6 +1856,30 @@ extern "C" int oscar_decode_attn_timed(const oscar_shape* shape, const uint16_t*
                               max_pages_per_seq, pool, nullptr, n_pages, win_k, win_v, out, workspace,
                               workspace_bytes, stream, 1,
                               oscar::TimedLaunch{static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop)});
+}
+extern "C" int oscar_decode_step(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
+                                 const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q, int32_t batch,
+                                 const int32_t* seq_lens, int32_t max_seq_len, const int32_t* block_table,
+                                 int32_t max_pages_per_seq, uint8_t* pool, int64_t n_pages, uint16_t* win_k,
+                                 uint16_t* win_v, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_new || !v_new) return OSCAR_EINVAL;
+  return oscar::decode_common(true, shape, r_k, r_v, q, batch, seq_lens, max_seq_len, block_table,
+                              max_pages_per_seq, pool, nullptr, n_pages, win_k, win_v, out, workspace,
+                              workspace_bytes, stream, 1, oscar::TimedLaunch{nullptr, nullptr}, false, k_new, v_new);
+}
+extern "C" int oscar_decode_step_timed(const oscar_shape* shape, const uint16_t* r_k, const uint16_t* r_v,
+                                       const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
+                                       int32_t batch, const int32_t* seq_lens, int32_t max_seq_len,
+                                       const int32_t* block_table, int32_t max_pages_per_seq, uint8_t* pool,
+                                       int64_t n_pages, uint16_t* win_k, uint16_t* win_v, float* out,
+                                       void* workspace, size_t workspace_bytes, void* stream, void* ev_start,
+                                       void* ev_stop) {
+  if (!k_new || !v_new) return OSCAR_EINVAL;
+  return oscar::decode_common(true, shape, r_k, r_v, q, batch, seq_lens, max_seq_len, block_table,
+                              max_pages_per_seq, pool, nullptr, n_pages, win_k, win_v, out, workspace,
+                              workspace_bytes, stream, 1,
+                              oscar::TimedLaunch{static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop)},
+                              false, k_new, v_new);
 }
 
 extern "C" int oscar_bf16_decode_attn_timed(const oscar_shape* shape, const uint16_t* q, int32_t batch,

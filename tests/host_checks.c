@@ -90,6 +90,16 @@ static int validate(void) {
   EXPECT(oscar_decode_attn_timed(&good, f, f, f, 8, f, 10, f, 1, f, 1, f, f, f, f, ws, 0, f, 0) == OSCAR_EINVAL);
   EXPECT(oscar_quantize_append_timed(&good, f, f, f, f, 1, f, f, 1, f, 1, f, f, 1, f, f, 0, 0, f) == OSCAR_EINVAL);
   EXPECT(oscar_bf16_decode_attn_timed(&good, f, 8, f, 10, f, 1, f, 1, f, f, ws, 0, f, 0) == OSCAR_EINVAL);
+  /* the fused decode step: new-token rows required and aligned, then the decode's checks */
+  EXPECT(oscar_decode_step(&good, f, f, 0, f, f, 8, f, 10, f, 1, f, 1, f, f, f, f, ws, 0) == OSCAR_EINVAL);
+  EXPECT(oscar_decode_step(&good, f, f, f, 0, f, 8, f, 10, f, 1, f, 1, f, f, f, f, ws, 0) == OSCAR_EINVAL);
+  EXPECT(oscar_decode_step(&good, f, f, mis, f, f, 8, f, 100000, f, 100000 / 16 + 1, f, 1, f, f, f, f, ws, 0) ==
+         OSCAR_EINVAL);
+  EXPECT(oscar_decode_step(&good, f, f, f, f, f, 8, f, 100000, f, 100000 / 16 + 1, f, 1, f, f, f, f, ws - 1, 0) ==
+         OSCAR_ENOSPACE);
+  EXPECT(oscar_decode_step(&good, f, f, f, f, f, 0, f, 10, f, 1, f, 1, f, f, f, f, ws, 0) == OSCAR_EINVAL);
+  EXPECT(oscar_decode_step_timed(&good, f, f, f, f, f, 8, f, 10, f, 1, f, 1, f, f, f, f, ws, 0, f, 0) ==
+         OSCAR_EINVAL);
   /* sinks without a window still need the ring */
   oscar_shape sink_only = shape_of(32, 8, 0, 4, 128);
   EXPECT(oscar_decode_attn(&sink_only, f, f, f, 8, f, 10, f, 1, f, 1, 0, 0, f, f, (size_t)1 << 30, 0) ==

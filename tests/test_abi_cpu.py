@@ -115,6 +115,16 @@ def test_host_validation_before_launch():
                                            fake, 1, fake, fake, None, fake, None) == EINVAL
     assert lib.oscar_bf16_decode_attn_timed(C.byref(good), fake, 8, fake, 10, fake, 1, fake, 1, fake, fake,
                                             1 << 30, None, None, fake) == EINVAL
+    # the fused decode step: both new-token row arrays, 16-byte aligned, then
+    # the decode's own checks
+    step = [C.byref(good), fake, fake, fake, fake, fake, 8, fake, 100000, fake, 100000 // 16 + 1, fake, 1, fake,
+            fake, fake, fake]
+    for i, v in ((3, None), (4, None), (3, C.c_void_p(258)), (4, C.c_void_p(258))):
+        bad = list(step)
+        bad[i] = v
+        assert lib.oscar_decode_step(*bad, ws, None) == EINVAL
+    assert lib.oscar_decode_step(*step, ws - 1, None) == ENOSPACE
+    assert lib.oscar_decode_step_timed(*step, ws, None, fake, None) == EINVAL
 
 
 def test_layered_entry_points_validate_on_host():
