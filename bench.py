@@ -24,6 +24,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -78,9 +79,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # enough warm-up steps (~3 ms of decode) for the GPU to leave its idle
-    # clocks: the first ~10 steps after an idle host gap run up to 15 % slower
-    ap.add_argument("--warmup", type=int, default=30)
+    # enough warm-up steps (~10 ms of decode) for the GPU to leave its idle
+    # clocks: the first steps after an idle host gap run up to 15 % slower
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--window", type=int, default=None, help="bf16 recent-token window (default: the workload's)")
@@ -266,12 +267,30 @@ def main():
         sa = np.asarray(split_all)
         log(f"split launches (ms): first {sa[0]:.4f} min {sa.min():.4f} median {np.median(sa):.4f} max {sa.max():.4f}")
     log(f"INT2 step {dt * 1e3:.3f} ms, split kernel {split_s * 1e3 if split_s else float('nan'):.3f} ms")
-    # the same step as the two plain calls (append, then decode)
-    dt2, split_s2, _ = timed(step_int2_two_calls)
-    res_two = {"ms_per_step": dt2 * 1e3, "gbs": step_bytes_int2 / dt2 / 1e9,
-               "split_kernel_ms": split_s2 * 1e3 if split_s2 else None,
-               "workload": "the same step as oscar_quantize_append + oscar_decode_attn"}
-    log(f"INT2 step as two calls {dt2 * 1e3:.3f} ms")
+    # the same step as the two plain calls (append, then decode) against the
+    # fused call: 3 alternating rounds of 60 warm-up + 50 timed steps each
+    # (wall time), so that neither form gets the GPU's better or worse clocks
+    def wall_per_step(step, n=50, warm=60):
+        for i in range(warm):
+            step(i)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(n):
+            step(warm + i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / n
+
+    rounds = {"fused": [], "two_calls": []}
+    for _ in range(3):
+        rounds["fused"].append(wall_per_step(step_int2))
+        rounds["two_calls"].append(wall_per_step(step_int2_two_calls))
+    res_two = {"fused_ms": [round(x * 1e3, 4) for x in rounds["fused"]],
+               "two_calls_ms": [round(x * 1e3, 4) for x in rounds["two_calls"]],
+               "two_calls_median_ms": float(np.median(rounds["two_calls"])) * 1e3,
+               "fused_median_ms": float(np.median(rounds["fused"])) * 1e3,
+               "workload": "the step as oscar_decode_step (fused) and as oscar_quantize_append + oscar_decode_attn "
+                           "(two calls), alternating rounds"}
+    log(f"step fused / two calls (ms, 3 alternating rounds): {res_two['fused_ms']} / {res_two['two_calls_ms']}")
     res_bf16 = None
     if kvp:
         dtb, split_b, _ = timed(step_bf16)
@@ -371,7 +390,7 @@ def main():
                    "decode_tokens_per_s": B / dt, "step_bytes": step_bytes_int2},
         "bf16_kv": res_bf16,
         "speedup_vs_bf16": (res_bf16["ms_per_step"] / (dt * 1e3)) if res_bf16 else None,
-        "step_two_calls": res_two,
+        "step_fused_vs_two_calls": res_two,
         "decode_call": res_call,
         "hbm_probe": probe,
         "host_enqueue_ms_per_step": host_ms.get("step_int2"),
@@ -661,24 +680,32 @@ def summarize_trace(directory: str, command: str) -> str:
             continue
         out.append(f"  {k:44s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                    f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}")
-    # the INT2 decode step kernel by kernel: append, prep, split, merge in
-    # launch order, and the idle gap before each (medians over the steps)
+    # the INT2 decode step kernel by kernel in launch order (prep, split,
+    # merge; in the two-call form an append kernel before them), with the idle
+    # gap before each (medians over the steps)
     trace = sorted(_csv_rows(directory, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
-    names = ["append_kernel", "prep_kernel", "int2_split_kernel", "merge_kernel"]
-    dur, gap = {n: [] for n in names}, {n: [] for n in names}
-    for i in range(3, len(trace)):
-        seq = trace[i - 3:i + 1]
-        if all(_short_kernel(r["Kernel_Name"]).startswith(n) for r, n in zip(seq, names)):
+    forms = {"fused step (oscar_decode_step)": ["prep_kernel", "int2_split_kernel", "merge_kernel"],
+             "two calls (append kernel, then oscar_decode_attn)": ["append_kernel", "prep_kernel",
+                                                                     "int2_split_kernel", "merge_kernel"]}
+    for title, names in forms.items():
+        k = len(names)
+        dur, gap = {n: [] for n in names}, {n: [] for n in names}
+        for i in range(k - 1, len(trace)):
+            seq = trace[i - k + 1:i + 1]
+            if not all(_short_kernel(r["Kernel_Name"]).startswith(n) for r, n in zip(seq, names)):
+                continue
+            if k == 3 and not re.fullmatch(r"prep_kernel<\d+,[124]>", _short_kernel(seq[0]["Kernel_Name"]).replace(" ", "")):
+                continue  # a plain decode call (its prep kernel appends nothing)
             for j, (r, n) in enumerate(zip(seq, names)):
                 dur[n].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
                 if j:
                     gap[n].append((int(r["Start_Timestamp"]) - int(seq[j - 1]["End_Timestamp"])) / 1e3)
-    if dur["int2_split_kernel"]:
-        out += ["#", f"# INT2 decode step, kernel by kernel ({len(dur['int2_split_kernel'])} steps; the tracer "
-                "itself lengthens the gaps)", f"# {'kernel':44s} {'median_us':>10s} {'gap_before_us':>14s}"]
-        for n in names:
-            g = f"{np.median(gap[n]):14.2f}" if gap[n] else f"{'-':>14s}"
-            out.append(f"  {n:44s} {np.median(dur[n]):10.2f} {g}")
+        if dur["int2_split_kernel"]:
+            out += ["#", f"# INT2 decode step, {title}, kernel by kernel ({len(dur['int2_split_kernel'])} steps; "
+                    "the tracer itself lengthens the gaps)", f"# {'kernel':44s} {'median_us':>10s} {'gap_before_us':>14s}"]
+            for n in names:
+                g = f"{np.median(gap[n]):14.2f}" if gap[n] else f"{'-':>14s}"
+                out.append(f"  {n:44s} {np.median(dur[n]):10.2f} {g}")
     return "\n".join(out) + "\n"
 
 
