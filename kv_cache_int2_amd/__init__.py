@@ -312,12 +312,17 @@ def oscar_decode_attn(shape, r_k, r_v, q, seq_lens, max_seq_len, block_table, po
                       stream)))
 
 
-def _step_args(shape, r_k, r_v, k_new, v_new, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v, out,
-               workspace, stream):
-    b16, i32, u8, f32 = _dt()
+def _step_checks(shape, r_k, r_v, k_new, v_new, q, seq_lens, block_table, pool, win_k, win_v, out):
     batch = _decode_checks(shape, r_k, r_v, q, seq_lens, block_table, pool, win_k, win_v, out)
     _want(k_new, (batch, shape.n_kv_heads, HEAD_DIM), "k_new")
     _want(v_new, (batch, shape.n_kv_heads, HEAD_DIM), "v_new")
+    return batch
+
+
+def _step_args(shape, r_k, r_v, k_new, v_new, q, seq_lens, max_seq_len, block_table, pool, win_k, win_v, out,
+               workspace, stream):
+    b16, i32, u8, f32 = _dt()
+    batch = _step_checks(shape, r_k, r_v, k_new, v_new, q, seq_lens, block_table, pool, win_k, win_v, out)
     return (C.byref(shape), _dev(r_k, b16, "r_k"), _dev(r_v, b16, "r_v"), _dev(k_new, b16, "k_new"),
             _dev(v_new, b16, "v_new"), _dev(q, b16, "q"), batch, _dev(seq_lens, i32, "seq_lens"), int(max_seq_len),
             _dev(block_table, i32, "block_table"), int(block_table.shape[1]), _dev(pool, u8, "pool"),

@@ -252,6 +252,13 @@ def test_binding_checks_shapes_before_the_call():
         kw = dict(good_dec, **{name: t})
         with pytest.raises(ValueError, match=name):
             K._decode_checks(shape, **kw)
+    # the decode step: one new K/V row per sequence and KV head
+    good_step = dict(good_dec, k_new=F(3, 8, 128), v_new=F(3, 8, 128))
+    assert K._step_checks(shape, **good_step) == 3
+    for name, t in (("k_new", F(2, 8, 128)), ("v_new", F(3, 4, 128)), ("k_new", F(3, 8, 64)),
+                    ("q", F(3, 16, 128))):
+        with pytest.raises(ValueError, match=name):
+            K._step_checks(shape, **dict(good_step, **{name: t}))
     # layer-batched: every per-layer buffer carries the layer count
     lay = dict(r_k=F(2, 8, 128, 128), r_v=F(2, 8, 128, 128), q=F(2, 3, 32, 128), seq_lens=F(3),
                block_table=F(3, 9), pool=F(2, 20, 8, blk), win_k=F(2, 3, 132, 8, 128), win_v=F(2, 3, 132, 8, 128),
