@@ -78,7 +78,7 @@ def load_traffic(split_launch_bytes_alg: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     # enough warm-up steps (~10 ms of decode) for the GPU to leave its idle
     # clocks: the first steps after an idle host gap run up to 15 % slower
     ap.add_argument("--warmup", type=int, default=100)
