@@ -239,19 +239,19 @@ struct SplitParams {
 };
 
 // The parameters of layer l: every per-layer buffer advanced by l strides.
+// Without a branch, so that the kernel argument loads are issued together at
+// the kernel's start rather than in dependent rounds.
 __device__ __forceinline__ SplitParams layer_params(const SplitParams& p, int l) {
   SplitParams r = p;
-  if (l > 0) {
-    r.q += l * p.ls_q;
-    r.out += l * p.ls_out;
-    r.r_v += l * p.ls_rot;
-    r.pool += l * p.ls_pool;
-    r.win_k += l * p.ls_win;
-    r.win_v += l * p.ls_win;
-    r.qsum += l * p.ls_qsum;
-    r.qop += l * p.ls_qop;
-    r.wpart += l * p.ls_wpart;
-  }
+  r.q += l * p.ls_q;
+  r.out += l * p.ls_out;
+  r.r_v += l * p.ls_rot;
+  r.pool += l * p.ls_pool;
+  r.win_k += l * p.ls_win;
+  r.win_v += l * p.ls_win;
+  r.qsum += l * p.ls_qsum;
+  r.qop += l * p.ls_qop;
+  r.wpart += l * p.ls_wpart;
   return r;
 }
 
@@ -349,7 +349,10 @@ __device__ void window_chunk(const SplitParams& p, int b, int h, int c, int G, f
   const bool valid = t < nt;
   uint4 kk[2], vv[2];
   {
-    const int slot = !valid ? 0 : sink ? p.window + cs + t : (cs + t) % p.window;
+    // ring row of window position cs + t: (cs mod W) + t, less W once it
+    // passes W (t < nt <= w <= W), instead of a per-lane division
+    const int cw = sink ? 0 : cs % p.window;  // uniform
+    const int slot = !valid ? 0 : sink ? p.window + cs + t : (cw + t >= p.window ? cw + t - p.window : cw + t);
     const int64_t row = (((int64_t)b * p.ring + slot) * p.hkv + h) * kD + 16 * part;
     const uint4* kr = reinterpret_cast<const uint4*>(p.win_k + row);
     const uint4* vr = reinterpret_cast<const uint4*>(p.win_v + row);
@@ -1370,30 +1373,44 @@ __global__ __launch_bounds__(256) void bf16_split_kernel(SplitParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// merge: one workgroup per (sequence, group of mh q heads of one KV head),
-// wave v < mh taking head mh x + v; mh (1, 2 or 4, dividing G) is chosen on the
-// host so that the grid still has about two workgroups per CU.  Each wave merges its head's partials
-// (log-sum-exp): every load of a pass (the (m, l) of up to 32 partials on its
-// lanes, the accumulators of channels lane and lane + 64) is issued before any
-// is used, the passes keep a running max, and the wave reduces the (m, l)
-// values itself.  INT2: the workgroup's R_V tile (loaded once for its MH
-// heads) un-rotates every head, then each wave merges its head's window and
-// sink chunk partials and normalises.  A head with no position at all gets
-// zeros.
+// merge: one workgroup per (sequence, group of MH q heads of one KV head);
+// MH (1, 2 or 4, dividing G) is chosen on the host so that the grid still has
+// about two workgroups per CU.  The 4 / MH waves of a head share its partials
+// (wave s of the head takes partials s, s + 4 / MH, ...).  A pass of a wave
+// covers up to NP of its partials, NP (8, 16 or 32) the smallest that holds
+// them all when it can: the (m, l) of partial i0 + i sit on lane i, whose
+// address the wave reads out of that lane for the accumulator loads
+// (channels lane and lane + 64), and every load of a pass is issued before
+// any is used; the passes keep a running max.  The short kernel's time is its
+// serial instruction count, so nothing is executed for partials a wave does
+// not have beyond the pass's padding.  The waves of a head meet in LDS
+// (log-sum-exp over their (m, l, acc)).  INT2: the workgroup's R_V tile
+// (loaded once for its MH heads) un-rotates every head, then the first wave of
+// each head merges the window and sink chunk partials and normalises.  A head
+// with no position at all gets zeros.
 // ---------------------------------------------------------------------------
-constexpr int kMergePass = 32;  // partials per pass
-constexpr int kMergeWin = 8;    // window / sink chunk partials held in registers
-constexpr int kMergeHeads = 4;  // q heads per workgroup at most (one per wave)
+constexpr int kMergeWin = 4;    // window / sink chunk partials held in registers (a 128-token window)
+constexpr int kMergeHeads = 4;  // q heads per workgroup at most
 
-__global__ __launch_bounds__(256) void merge_kernel(SplitParams p0, int gq, int mh) {
+__device__ __forceinline__ const float* readlane_ptr(const float* p, int lane) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane), hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), lane);
+  return reinterpret_cast<const float*>(((uint64_t)hi << 32) | lo);
+}
+
+template <int MH, bool INT2>
+__global__ __launch_bounds__(256) void merge_kernel(SplitParams p0, int gq) {
+  constexpr int LW = MH == 1 ? 2 : MH == 2 ? 1 : 0, WPH = 1 << LW;  // waves per head
   const int layer = blockIdx.y / p0.batch, b = blockIdx.y % p0.batch;
   const SplitParams p = layer_params(p0, layer);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool active = wave < mh;
-  const int hq = blockIdx.x * mh + (active ? wave : 0), h = hq / gq;
-  const bool int2 = p.r_v != nullptr;
-  __shared__ float a1s[kMergeHeads][kD];
-  __shared__ float o1p[kMergeHeads][16][kD + 4];
+  const int m = wave >> LW, sub = wave & (WPH - 1);  // head slot, this wave's share of its partials
+  const bool lead = sub == 0;  // merges the window partials and stores the head
+  const int hq = blockIdx.x * MH + m, h = hq / gq;  // one KV head for the workgroup (MH divides G)
+  constexpr bool int2 = INT2;  // INT2 cache (partials in the rotated basis) or bf16 cache
+  __shared__ float accs[4][kD];  // per wave: its (unnormalised) accumulator
+  __shared__ float mls[4][2];    // per wave: its running max and sum
+  __shared__ float o1p[MH][16][kD + 4];
 
   // The loads that depend on nothing else go out first, so that they are in
   // flight while the partials' places are looked up.
@@ -1405,9 +1422,10 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p0, int gq, int 
 #pragma unroll
     for (int j = 0; j < 8; ++j) rv[j] = *reinterpret_cast<const uint4*>(r + j * kD);
   }
-  // window / sink chunk partials (INT2): channels lane and lane + 64 of the first kMergeWin chunks
+  // window / sink chunk partials (INT2, first wave of a head): channels lane
+  // and lane + 64 of the first kMergeWin chunks
   const float* wp = p.wpart + ((int64_t)b * p.hq + hq) * p.n_wchunks * kPartStride;
-  const int nwc = int2 && active ? p.n_wchunks : 0;
+  const int nwc = int2 && lead ? p.n_wchunks : 0;
   // (m, l) are loaded per lane (lane & 1) and read out only where they are
   // used: as uniform values they would be scalar loads waited for at once
   float wv0[kMergeWin], wv1[kMergeWin], wml[kMergeWin];
@@ -1419,7 +1437,7 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p0, int gq, int 
     wml[cc] = wc[lane & 1];
   }
 
-  // partials of this wave's head: INT2 - the wave partials (w + u, v) of the ts
+  // partials of this head: INT2 - the wave partials (w + u, v) of the ts
   // waves v of this head in each workgroup w whose tile range touches unit u,
   // at p.part + ((4 (w + u) + v) gw + g) 130 (partial s: workgroup w_lo + s / ts,
   // wave hv + hw (s % ts)); bf16 - the splits of the sequence (partial s at
@@ -1429,15 +1447,17 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p0, int gq, int 
   int64_t stride;
   int ts = 1, hw = 1, w0 = 0;
   if (int2) {
-    const int jq = hq % gq, sub = jq / p.gw, g = jq % p.gw;
+    const int jq = hq % gq, hsub = jq / p.gw, g = jq % p.gw;
     const int per_seq = (p.hkv / p.hw) * p.gsub;
-    const int u = (layer * p.batch + b) * per_seq + (h / p.hw) * p.gsub + sub;
+    const int u = (layer * p.batch + b) * per_seq + (h / p.hw) * p.gsub + hsub;
     const int64_t T = p.tile_prefix[p.n_layers * p.batch * per_seq];
     const int64_t nw = T < p.n_wg ? T : p.n_wg;
     const int64_t su = p.tile_prefix[u], su1 = p.tile_prefix[u + 1];
     int64_t w_lo = 0;
     ns = 0;
-    if (su1 > su) {  // workgroup of tile t: ((t + 1) nw - 1) / T
+    // (T > 0 holds whenever su1 > su; testing it keeps T's load beside those
+    // of su and su1 instead of a round trip later)
+    if (su1 > su && T > 0) {  // workgroup of tile t: ((t + 1) nw - 1) / T
       w_lo = share_owner(p, T, (int)nw, su);
       ns = (int)(share_owner(p, T, (int)nw, su1 - 1) - w_lo + 1);
     }
@@ -1453,64 +1473,100 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p0, int gq, int 
     base = p.part + ((int64_t)b * p.hq + hq) * p.n_splits * kPartStride;
     stride = kPartStride;
   }
-  if (!active) ns = 0;
   const int tsh = ts == 4 ? 2 : ts == 2 ? 1 : 0;  // ts = 4 / hw: 1, 2 or 4
-  auto part_at = [&](int s) {
-    return base + (int64_t)(int2 ? 4 * (w0 + (s >> tsh)) + hw * (s & (ts - 1)) : s) * stride;
-  };
+  // this wave's partials: s = sub + WPH i, i < nmine
+  const int nmine = ns > sub ? (ns - sub + WPH - 1) >> LW : 0;
 
-  // the head's partials: lane s of a pass holds partial s0 + s's (m, l)
   float M = kNegInf, acc0 = 0.f, acc1 = 0.f, lsum = 0.f;  // M, lsum: the same on every lane
-  for (int s0 = 0; s0 < ns; s0 += kMergePass) {
-    const int cnt = min(kMergePass, ns - s0);
-    // loads first, at clamped indices (no branch around a load)
-    const float* pl = part_at(s0 + min(lane, cnt - 1));
-    const float ml_raw = pl[0], ll_raw = pl[1];
-    float x0[kMergePass], x1[kMergePass];
+  auto pass = [&](int i0, auto np) {
+    constexpr int NP = decltype(np)::value;
+    const int cnt = min(NP, nmine - i0);
+    // lane i: the wave's partial i0 + i, clamped (no branch around a load)
+    const int s = sub + ((i0 + min(lane, cnt - 1)) << LW);
+    const float* pl = base + (int64_t)(int2 ? 4 * (w0 + (s >> tsh)) + hw * (s & (ts - 1)) : s) * stride;
+    const float2 mlv = *reinterpret_cast<const float2*>(pl);
+    float x0[NP], x1[NP];
 #pragma unroll
-    for (int k = 0; k < kMergePass; ++k) {
-      const float* pk = part_at(s0 + min(k, cnt - 1));
+    for (int k = 0; k < NP; ++k) {
+      const float* pk = readlane_ptr(pl, k);
       x0[k] = pk[2 + lane];
       x1[k] = pk[2 + 64 + lane];
     }
-    const float ml = lane < cnt ? ml_raw : kNegInf;
-    const float ll = lane < cnt ? ll_raw : 0.f;
+    const float ml = lane < cnt ? mlv.x : kNegInf;
+    const float ll = lane < cnt ? mlv.y : 0.f;
     const float Mn = fmaxf(M, wave_max64(ml));
     const float alpha = M == kNegInf ? 0.f : exp2f(M - Mn);
-    const float f = ml == kNegInf ? 0.f : exp2f(ml - Mn);  // weight of partial s0 + lane
+    const float f = ml == kNegInf ? 0.f : exp2f(ml - Mn);  // weight of partial i0 + lane, 0 past cnt
     acc0 *= alpha;
     acc1 *= alpha;
     lsum = lsum * alpha + wave_sum64(f * ll);
 #pragma unroll
-    for (int k = 0; k < kMergePass; ++k) {
-      // unconditional (weight 0 past cnt, x finite): a guarded FMA would let the
-      // compiler sink the loads of x into the guard
-      const float fs = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(f), k));
-      const float wk = k < cnt ? fs : 0.f;
-      acc0 = fmaf(wk, x0[k], acc0);
-      acc1 = fmaf(wk, x1[k], acc1);
+    for (int k = 0; k < NP; ++k) {
+      // lanes past cnt carry weight 0 and the (finite) accumulator of a valid partial
+      const float fk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(f), k));
+      acc0 = fmaf(fk, x0[k], acc0);
+      acc1 = fmaf(fk, x1[k], acc1);
     }
     M = Mn;
+  };
+  if (nmine > 0) {
+    if (nmine <= 8) {
+      pass(0, std::integral_constant<int, 8>{});
+    } else if (nmine <= 16) {
+      pass(0, std::integral_constant<int, 16>{});
+    } else {
+      for (int i0 = 0; i0 < nmine; i0 += 32) pass(i0, std::integral_constant<int, 32>{});
+    }
   }
+  accs[wave][lane] = acc0;
+  accs[wave][lane + 64] = acc1;
+  if (lane == 0) {
+    mls[wave][0] = M;
+    mls[wave][1] = lsum;
+  }
+  __syncthreads();
+  // the waves of head slot mm: weights relative to the head's max, and its (M, l)
+  auto head_weights = [&](int mm, float* f, float& Mh, float& lh) {
+    Mh = kNegInf;
+#pragma unroll
+    for (int s = 0; s < WPH; ++s) Mh = fmaxf(Mh, mls[(mm << LW) + s][0]);
+    lh = 0.f;
+#pragma unroll
+    for (int s = 0; s < WPH; ++s) {
+      const float ms = mls[(mm << LW) + s][0];
+      f[s] = ms == kNegInf ? 0.f : exp2f(ms - Mh);
+      lh = fmaf(f[s], mls[(mm << LW) + s][1], lh);
+    }
+  };
   float* dst = p.out + ((int64_t)b * p.hq + hq) * kD;
   if (!int2) {
-    if (active) {
-      dst[lane] = lsum > 0.f ? acc0 / lsum : 0.f;
-      dst[lane + 64] = lsum > 0.f ? acc1 / lsum : 0.f;
+    if (lead) {
+      float f[WPH], Mh, lh;
+      head_weights(m, f, Mh, lh);
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int s = 0; s < WPH; ++s) {
+        a0 = fmaf(f[s], accs[wave + s][lane], a0);
+        a1 = fmaf(f[s], accs[wave + s][lane + 64], a1);
+      }
+      dst[lane] = lh > 0.f ? a0 / lh : 0.f;
+      dst[lane + 64] = lh > 0.f ? a1 / lh : 0.f;
     }
     return;
   }
-  a1s[wave][lane] = acc0;
-  a1s[wave][lane + 64] = acc1;
-  __syncthreads();
   // o1 = R_V^T a1 of every head from the register tile, partial sums over 8 rows per thread
-  for (int m = 0; m < mh; ++m) {
+#pragma unroll
+  for (int mm = 0; mm < MH; ++mm) {
+    float f[WPH], Mh, lh;
+    head_weights(mm, f, Mh, lh);
     float o[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float aj = a1s[m][8 * jg + j];
+      float aj = 0.f;
+#pragma unroll
+      for (int s = 0; s < WPH; ++s) aj = fmaf(f[s], accs[(mm << LW) + s][8 * jg + j], aj);
       const uint32_t u[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -1519,15 +1575,17 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p0, int gq, int 
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o1p[m][jg][8 * cg + i] = o[i];
+    for (int i = 0; i < 8; ++i) o1p[mm][jg][8 * cg + i] = o[i];
   }
   __syncthreads();
-  if (!active) return;
+  if (!lead) return;
+  float fh[WPH], Mh, lh;
+  head_weights(m, fh, Mh, lh);
   float o1[2] = {0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    o1[0] += o1p[wave][k][lane];
-    o1[1] += o1p[wave][k][lane + 64];
+    o1[0] += o1p[m][k][lane];
+    o1[1] += o1p[m][k][lane + 64];
   }
   float wm[kMergeWin], wl[kMergeWin];
 #pragma unroll
@@ -1538,12 +1596,12 @@ __global__ __launch_bounds__(256) void merge_kernel(SplitParams p0, int gq, int 
     wv0[cc] = ok ? wv0[cc] : 0.f;
     wv1[cc] = ok ? wv1[cc] : 0.f;
   }
-  float Mx = M;
+  float Mx = Mh;
 #pragma unroll
   for (int cc = 0; cc < kMergeWin; ++cc) Mx = fmaxf(Mx, wm[cc]);
   for (int cc = kMergeWin; cc < nwc; ++cc) Mx = fmaxf(Mx, wp[cc * kPartStride]);
-  const float f1 = M == kNegInf ? 0.f : exp2f(M - Mx);
-  float den = f1 * lsum, num0 = f1 * o1[0], num1 = f1 * o1[1];
+  const float f1 = Mh == kNegInf ? 0.f : exp2f(Mh - Mx);
+  float den = f1 * lh, num0 = f1 * o1[0], num1 = f1 * o1[1];
 #pragma unroll
   for (int cc = 0; cc < kMergeWin; ++cc) {
     const float f2 = wm[cc] == kNegInf ? 0.f : exp2f(wm[cc] - Mx);
@@ -1600,7 +1658,21 @@ int launch_decode(bool int2, const SplitParams& sp, const uint16_t* r_k, int bat
   const int64_t rows = (int64_t)batch * sp.n_layers;
   while (2 * mh <= kMergeHeads && 2 * mh <= G && rows * sp.hq / (2 * mh) >= 2 * (int64_t)device_cu_count())
     mh *= 2;
-  merge_kernel<<<dim3(sp.hq / mh, (unsigned)rows), 256, 0, s>>>(sp, G, mh);
+  const dim3 mgrid(sp.hq / mh, (unsigned)rows);
+  auto merge = [&](auto kernel) { kernel<<<mgrid, 256, 0, s>>>(sp, G); };
+  if (int2) {
+    switch (mh) {
+      case 1: merge(merge_kernel<1, true>); break;
+      case 2: merge(merge_kernel<2, true>); break;
+      default: merge(merge_kernel<4, true>); break;
+    }
+  } else {
+    switch (mh) {
+      case 1: merge(merge_kernel<1, false>); break;
+      case 2: merge(merge_kernel<2, false>); break;
+      default: merge(merge_kernel<4, false>); break;
+    }
+  }
   return hipGetLastError() == hipSuccess ? OSCAR_OK : OSCAR_EHIP;
 }
 
