@@ -366,7 +366,15 @@ __device__ void window_chunk(const SplitParams& p, int b, int h, int c, int G, f
     kk[0] = kr[0]; kk[1] = kr[1];
     vv[0] = vr[0]; vv[1] = vr[1];
   }
-  for (int e = tid; e < G * kD; e += 256) qs[e] = bf16_to_f32(p.q[((int64_t)b * p.hq + hq0) * kD + e]);
+  // the G heads' queries (contiguous rows), 8 channels a thread: one load in
+  // flight with the key and value rows (a clamped one past 16 G threads)
+  const uint4 qv = reinterpret_cast<const uint4*>(p.q + ((int64_t)b * p.hq + hq0) * kD)[tid < 16 * G ? tid : 0];
+  if (tid < 16 * G) {
+    const uint32_t u[4] = {qv.x, qv.y, qv.z, qv.w};
+    float4* d = reinterpret_cast<float4*>(qs + 8 * tid);
+    d[0] = make_float4(bf16lo(u[0]), bf16hi(u[0]), bf16lo(u[1]), bf16hi(u[1]));
+    d[1] = make_float4(bf16lo(u[2]), bf16hi(u[2]), bf16lo(u[3]), bf16hi(u[3]));
+  }
   {
     uint32_t* d = vs + t * 65 + 8 * part;
     const uint32_t u[8] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w, vv[1].x, vv[1].y, vv[1].z, vv[1].w};
@@ -469,23 +477,47 @@ __global__ __launch_bounds__(256) void prep_kernel(SplitParams p0, const uint16_
     window_chunk<G>(p, b, h, blockIdx.z - 1, G, smem_f);
     return;
   }
+  // The rotation's operands go out first: the query rows and R_K rows below do
+  // not depend on the tile prefix, so both wait on one round trip.
+  // q' = R_K q on the matrix cores (v_mfma_f32_16x16x32_bf16, exact bf16
+  // products, fp32 sums): wave v computes output channels 32 v .. 32 v + 31
+  // as two 16-row blocks; A = rows of R_K, B = q^T with the G heads as
+  // columns (zero past G).  Lane (g, r) supplies A row r and B column r at
+  // k = 8 g .. 8 g + 7 of each 32-wide k step and ends with channels
+  // 16 cb + 4 g + i of head r.
+  const int mg = (tid & 63) >> 4, mr = tid & 15, mw = tid >> 6;
+  uint4 bq[4], ra[2][4];
+  {
+    // rows past G read head 0's (a clamped row, no branch around the load)
+    // and are zeroed before use
+    const uint4* qrow = reinterpret_cast<const uint4*>(p.q + ((int64_t)b * hq + h * G + (mr < G ? mr : 0)) * kD);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) bq[ks] = qrow[4 * ks + mg];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const uint4* rrow = reinterpret_cast<const uint4*>(r_k + ((int64_t)h * kD + 16 * (2 * mw + blk) + mr) * kD);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) ra[blk][ks] = rrow[4 * ks + mg];
+    }
+  }
   // first history tile of the units (layer, b, head group, sub) in the
   // flattened order (layer-major, then sequence, KV head group, head subset),
   // written by the first head of each group; the last group also closes the
   // array.  Every layer has the same sequences, hence the same T tiles.
-  if (tid < 64 && h % p.hw == 0) {  // wave 0: tiles of the sequences before b and of all, summed across lanes
-    int pb = 0, pt = 0;
+  if (tid < 64 && h % p.hw == 0) {  // wave 0: tiles of the sequences before b, of b and of all, summed across lanes
+    int pb = 0, pt = 0, tb = 0;
     for (int bb = tid; bb < p.batch; bb += 64) {
       const int tt = hist_tiles(p, bb);
       pb += bb < b ? tt : 0;
+      tb += bb == b ? tt : 0;
       pt += tt;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       pb += __shfl_xor(pb, o);
+      tb += __shfl_xor(tb, o);
       pt += __shfl_xor(pt, o);
     }
-    const int tb = hist_tiles(p, b);
     const int hgp = h / p.hw, per_seq = (hkv / p.hw) * p.gsub;
     const int64_t u0 = (int64_t)layer * p.batch * per_seq, t0 = (int64_t)layer * per_seq * pt;
     for (int sub = tid; sub < p.gsub; sub += 64)
@@ -499,22 +531,9 @@ __global__ __launch_bounds__(256) void prep_kernel(SplitParams p0, const uint16_
   float* qsum_out = const_cast<float*>(p.qsum);
   int* qop = const_cast<int*>(p.qop);
   {
-    // q' = R_K q on the matrix cores (v_mfma_f32_16x16x32_bf16, exact bf16
-    // products, fp32 sums): wave v computes output channels 32 v .. 32 v + 31
-    // as two 16-row blocks; A = rows of R_K, B = q^T with the G heads as
-    // columns (zero past G).  Lane (g, r) supplies A row r and B column r at
-    // k = 8 g .. 8 g + 7 of each 32-wide k step and ends with channels
-    // 16 cb + 4 g + i of head r.
-    const int g = (tid & 63) >> 4, r = tid & 15, wv = tid >> 6;
-    const uint4* qrow = reinterpret_cast<const uint4*>(p.q + ((int64_t)b * hq + h * G + (r < G ? r : 0)) * kD);
-    uint4 bq[4], ra[2][4];
+    if (mr >= G) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) bq[ks] = r < G ? qrow[4 * ks + g] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const uint4* rrow = reinterpret_cast<const uint4*>(r_k + ((int64_t)h * kD + 16 * (2 * wv + blk) + r) * kD);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) ra[blk][ks] = rrow[4 * ks + g];
+      for (int ks = 0; ks < 4; ++ks) bq[ks] = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -523,9 +542,9 @@ __global__ __launch_bounds__(256) void prep_kernel(SplitParams p0, const uint16_
       for (int ks = 0; ks < 4; ++ks)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra[blk][ks]),
                                                       __builtin_bit_cast(bf16x8, bq[ks]), acc, 0, 0, 0);
-      if (r < G) {
+      if (mr < G) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qs[r][16 * (2 * wv + blk) + 4 * g + i] = acc[i] * p.scale_log2;
+        for (int i = 0; i < 4; ++i) qs[mr][16 * (2 * mw + blk) + 4 * mg + i] = acc[i] * p.scale_log2;
       }
     }
   }
