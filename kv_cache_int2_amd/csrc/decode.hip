@@ -151,23 +151,38 @@ __device__ __forceinline__ void digits_pair(float a, float b, uint32_t out[kDigi
   rb = b;
 }
 
-// The same digits for four values at once (the split kernel's weights):
-// digit j of x[i] in byte i of out[j]; rsum = the sum of the four residuals.
-__device__ __forceinline__ void digits_quad(float (&x)[4], uint32_t out[kDigits], float& rsum) {
-#pragma unroll
-  for (int j = 0; j < kDigits; ++j) {
-    float d[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) d[i] = __builtin_rintf(x[i]);
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(d[0], d[1], 0, false);
-    out[j] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(d[2], d[3], lo, true);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] -= d[i];
-      if (j < kDigits - 1) x[i] *= 16.f;
-    }
+// The split kernel's weights are never negative, so their digits need no sign:
+// x = w 2^(3 - e) in [0, 8) is carried as X = rint(4096 x) < 2^16, whose four
+// hexadecimal digits (X = 4096 d0 + 256 d1 + 16 d2 + d3, d0 <= 8, others
+// <= 15) are the same 1/4096 grid the signed digits above reach.  An e4m3 byte
+// n <= 16 is exactly n 2^-9 (the subnormals and the first binade are evenly
+// spaced), so each digit, taken out of X as an integer, already is its fp8
+// operand byte; the row's E8M0 scale carries the 2^9.  Adding 1.5 2^23 to
+// 4096 x (one FMA; the product is exact, a power of two) rounds it to an
+// integer, ties to even, in the low mantissa bits: the bits are kRoundBits + X.
+// Every product with a code is then a multiple of 2^-10 of at most 22.5 2^-9,
+// within the range the MFMA sums exactly.  (kRound = 1.5 2^23 and its bits
+// kRoundBits come with the append's device code, which rounds the same way.)
+constexpr int kDigitByteExp = 9;          // e4m3 byte n (n <= 16) reads as n 2^-9
+constexpr int kMinWeightExp = -100;       // weights below 2^-100 code as 0
+
+// kRoundBits + rint(w fix): fix = 2^(15 - e) with every weight below 2^e
+__device__ __forceinline__ uint32_t weight_fixed(float w, float fix) { return __float_as_uint(fmaf(w, fix, kRound)); }
+// digit j (0 = most significant) of X from weight_fixed's bits, in the low
+// byte (the fp8 operand byte; only that byte is stored): one bit-field
+// extract (written out: the compiler would split it into a shift and an AND),
+// and for digit 0 a plain shift (bits 16..21 of u are zero)
+template <int J>
+__device__ __forceinline__ uint32_t weight_digit(uint32_t u) {
+  if constexpr (J == 0) {
+    return u >> 12;
+  } else if constexpr (J == 3) {
+    return u & 15u;
+  } else {
+    uint32_t d;
+    asm("v_bfe_u32 %0, %1, %2, 4" : "=v"(d) : "v"(u), "n"(12 - 4 * J));
+    return d;
   }
-  rsum = (x[0] + x[1]) + (x[2] + x[3]);
 }
 
 // Row maxima as integer maxima, which take their DPP operand for free (a float
@@ -898,7 +913,7 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
 #pragma unroll
     for (int jg = 0; jg < NG; ++jg) {  // one group's weights at a time (registers)
       float w[8];
-      float ws = 0.f, wmax = 0.f;
+      float wmax = 0.f;
 #pragma unroll
       for (int pp = 0; pp < 8; ++pp) {
         // value scale and zero of (page pp, group jg); a dead slot's record may
@@ -907,30 +922,29 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
         const float vs = h2f((uint16_t)(vrec & 0xffffu)), vz = h2f((uint16_t)(vrec >> 16));
         st.az_part[rg][jg] = fmaf(pv[pp], fmaf(1.5f, vs, vz), st.az_part[rg][jg]);
         w[pp] = pv[pp] * vs;
-        ws += w[pp];
         wmax = fmaxf(wmax, w[pp]);
       }
-      const int e = exponent_above(row_max16_nonneg(wmax));  // this head's weights in the tile are < 2^e
-      const float wmul = ldexpf(1.f, 3 - e);           // w wmul < 8, exact (a power of two)
-      float rsum = 0.f;
-      uint8_t* tile_rg = wt + (rg * NG + jg) * 2048;
+      // this head's weights in the tile are < 2^e.  The floor keeps 2^(15 - e)
+      // finite: a weight below 2^-100 codes as 0, and since a nonzero fp16
+      // scale is at least 2^-24, its p is then below 2^-76 of the partial's
+      // largest (which is 1)
+      const int e = max(exponent_above(row_max16_nonneg(wmax)), kMinWeightExp);
+      const float fix = ldexpf(1.f, 15 - e);  // w fix = 4096 w 2^(3 - e) < 2^15, exact
+      uint32_t xsum = 0u;  // sum of the lane's kRoundBits + X (mod 2^32)
+      uint8_t* col = wt + (rg * NG + jg) * 2048 + (4 * lg) * 128 + slot_pos;
 #pragma unroll
-      for (int pp = 0; pp < 8; pp += 4) {
-        float x[4] = {w[pp] * wmul, w[pp + 1] * wmul, w[pp + 2] * wmul, w[pp + 3] * wmul};
-        uint32_t tt[kDigits];
-        float r4;
-        digits_quad(x, tt, r4);
-        rsum += r4;
-#pragma unroll
-        for (int j = 0; j < kDigits; ++j) {
-          uint8_t* row = tile_rg + (4 * lg + j) * 128 + slot_pos;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) row[16 * (pp + i)] = (uint8_t)(tt[j] >> (8 * i));
-        }
+      for (int pp = 0; pp < 8; ++pp) {
+        const uint32_t u = weight_fixed(w[pp], fix);
+        xsum += u;
+        col[0 * 128 + 16 * pp] = (uint8_t)weight_digit<0>(u);
+        col[1 * 128 + 16 * pp] = (uint8_t)weight_digit<1>(u);
+        col[2 * 128 + 16 * pp] = (uint8_t)weight_digit<2>(u);
+        col[3 * 128 + 16 * pp] = (uint8_t)weight_digit<3>(u);
       }
-      // the digits carry w - r 16^-3 / wmul: the correction below must take the
-      // same sum, or its rounding would shift every channel alike
-      wsum[rg][jg] = row_sum16(fmaf(-rsum, ldexpf(1.f, e - 3 - 4 * (kDigits - 1)), ws));
+      // the digits carry X 2^(e - 15), not w: the correction below takes the
+      // same sum, or its rounding would shift every channel alike (the 16 lanes'
+      // X sum to below 2^22, exact in fp32)
+      wsum[rg][jg] = row_sum16((float)(xsum - 8u * kRoundBits)) * ldexpf(1.f, e - 15);
       wexp[rg][jg] = e;
     }
   }
@@ -946,8 +960,9 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
   // 2 (its B scale is per lane, i.e. per column): their products with group jg's
   // weights land ~2^-128 below the true products, under fp32 resolution of any
   // accumulator they join, and no instruction is spent masking them.
-  // A-operand scale of row lr (head lr / 4 of the row group, digit lr % 4): that
-  // head's exponent lives on the lanes of row lr / 4
+  // A-operand scale of row lr (head lr / 4 of the row group, digit lr % 4, a
+  // byte n of which reads n 2^-9): that head's exponent lives on the lanes of
+  // row lr / 4
   const int src_row = 4 * 16 * (lr >> 2);
   const int grp_lo = lr * NG / 32, grp_hi = NG / 2 + lr * NG / 32;
   float corr_lo[NRG], corr_hi[NRG];
@@ -973,7 +988,7 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
       wa[rg][6] = (int)a1.z;
       wa[rg][7] = (int)a1.w;
       const int eh = __builtin_amdgcn_ds_bpermute(src_row, wexp[rg][jg]);
-      wsc[rg] = clamp_scale(kScaleOne + eh - 3 - 4 * (lr & 3));
+      wsc[rg] = clamp_scale(kScaleOne + kDigitByteExp + eh - 3 - 4 * (lr & 3));
       corr_lo[rg] = mine_lo ? 1.5f * wsum[rg][jg] : corr_lo[rg];
       corr_hi[rg] = mine_hi ? 1.5f * wsum[rg][jg] : corr_hi[rg];
     }
