@@ -26,12 +26,14 @@
 // as the fp4 (e2m1) operand: a code c zero-extended to a nibble is exactly the
 // e2m1 value c/2, so (w & 0x33333333) and ((w >> 2) & 0x33333333) turn 16 packed
 // codes into two ready operand dwords.  The other operand is carried as fp8
-// (e4m3) fixed-point digits (see digits_pair): v 2^(3 - E) = d0 + d1/16 +
-// d2/256 + d3/4096, |d_j| <= 8, one digit per MFMA row, the powers of two in the
-// E8M0 operand scales; every product is a small integer, so the matrix cores sum
-// them exactly.  E is the query head's exponent for q' (scores) and, for the
-// softmax weights (values), the exponent of the largest weight of the head in
-// the tile.  Rows are (head, digit): 4 heads per MFMA.
+// (e4m3) fixed-point digits: v 2^(3 - E) = d0 + d1/16 + d2/256 + d3/4096, one
+// digit per MFMA row, the powers of two in the E8M0 operand scales; every
+// product is a small multiple of one power of two, so the matrix cores sum them
+// exactly.  q' (scores) takes signed digits |d_j| <= 8 (see digits_pair), E its
+// head's exponent; the softmax weights (values), never negative, take the hex
+// digits of one rounding to the 1/4096 grid as raw e4m3 bytes (see
+// weight_fixed), E the exponent of the largest weight of the head in the tile.
+// Rows are (head, digit): 4 heads per MFMA.
 //   scores: A = q' digits [(head, digit) x 128 channels], B = K codes [128 x 16 tokens]
 //   values: A = w digits  [(head, digit) x 128 tokens],  B = V codes [128 x 16 channels]
 // The score output leaves one (head, token) per lane after an in-lane sum of
