@@ -166,7 +166,7 @@ __device__ __forceinline__ void digits_pair(float a, float b, uint32_t out[kDigi
 // within the range the MFMA sums exactly.  (kRound = 1.5 2^23 and its bits
 // kRoundBits come with the append's device code, which rounds the same way.)
 constexpr int kDigitByteExp = 9;          // e4m3 byte n (n <= 16) reads as n 2^-9
-constexpr int kMinWeightExp = -100;       // weights below 2^-100 code as 0
+constexpr int kMinWeightExp = -100;       // floor of a tile's weight exponent
 
 // kRoundBits + rint(w fix): fix = 2^(15 - e) with every weight below 2^e
 __device__ __forceinline__ uint32_t weight_fixed(float w, float fix) { return __float_as_uint(fmaf(w, fix, kRound)); }
@@ -927,9 +927,10 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
         wmax = fmaxf(wmax, w[pp]);
       }
       // this head's weights in the tile are < 2^e.  The floor keeps 2^(15 - e)
-      // finite: a weight below 2^-100 codes as 0, and since a nonzero fp16
-      // scale is at least 2^-24, its p is then below 2^-76 of the partial's
-      // largest (which is 1)
+      // finite: weights below 2^-100 then sit on a grid of 2^-115 (below
+      // 2^-116 they code as 0), an absolute error under 2^-92 of the
+      // partial's largest weight (p = 1 there, and a nonzero fp16 scale is at
+      // least 2^-24)
       const int e = max(exponent_above(row_max16_nonneg(wmax)), kMinWeightExp);
       const float fix = ldexpf(1.f, 15 - e);  // w fix = 4096 w 2^(3 - e) < 2^15, exact
       uint32_t xsum = 0u;  // sum of the lane's kRoundBits + X (mod 2^32)
