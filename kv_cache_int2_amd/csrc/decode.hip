@@ -740,6 +740,45 @@ __device__ __forceinline__ void load_tile(const uint8_t* base_h, uint32_t stride
   // while these loads are in flight
 }
 
+// The same loads in two parts, for the loop that keeps one tile in flight:
+// load_tile_k the K-code rows and the records (all that phase 1 of
+// compute_tile reads), load_tile_v the V words (all that phase 2 reads).
+template <int NG>
+__device__ __forceinline__ void load_tile_k(const uint8_t* base_h, uint32_t stride, const TileTable& tt, int j, int lg,
+                                            int lr, Tile<NG>& t) {
+  t.page_ok = (uint32_t)(tt.live >> (8 * j)) & 0xffu;
+  const uint32_t off_k = kKCodes + 32 * lr + 8 * lg;
+  const uint32_t off_m = kMeta + 8 * NG * lr;
+#pragma unroll
+  for (int pp = 0; pp < 8; ++pp) {
+    const int e = __builtin_amdgcn_readlane(tt.ent, 8 * j + pp);
+    const __amdgpu_buffer_rsrc_t blk = block_rsrc(base_h + (uint64_t)(uint32_t)(e < 0 ? 0 : e) * stride);
+    t.kc[pp] = buffer_nt2(blk, off_k);
+    if constexpr (NG == 1) {
+      t.meta[pp][0] = buffer_nt2(blk, off_m);
+    } else {
+#pragma unroll
+      for (int q2 = 0; q2 < NG; q2 += 2) {
+        const uint4 m2 = buffer_nt4(blk, off_m + 8 * q2);
+        t.meta[pp][q2] = make_uint2(m2.x, m2.y);
+        t.meta[pp][q2 + 1] = make_uint2(m2.z, m2.w);
+      }
+    }
+  }
+}
+template <int NG>
+__device__ __forceinline__ void load_tile_v(const uint8_t* base_h, uint32_t stride, const TileTable& tt, int j, int lg,
+                                            int lr, Tile<NG>& t) {
+  const uint32_t off_v = kVCodes + 16 * lr;
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    const int pv = __builtin_amdgcn_ds_bpermute(4 * (8 * j + 2 * lg + qq), tt.ent);
+    const uint8_t* blk = base_h + (uint64_t)(uint32_t)(pv < 0 ? 0 : pv) * stride + off_v;
+    t.vlo[qq] = load_nt4(blk);
+    t.vhi[qq] = load_nt4(blk + 256);
+  }
+}
+
 // Pins a value at this point of the program.  The matrix instructions read
 // their operands across all 64 lanes, so they must run with every lane active:
 // without the pin the compiler may sink an MFMA whose result is only used under
@@ -811,10 +850,35 @@ __device__ __forceinline__ void spread_records(const Tile<NG>& t, uint8_t* rb, i
   }
 }
 
-template <int G, int NRG, bool FULL, int NG, bool REC>  // FULL: all 8 pages exist and every token is below t_end
+// What phase 1 of compute_tile leaves for phase 2, beside the wave's LDS
+// digit tile: the weights' digit sums (midpoint correction) and exponents.
+template <int NRG, int NG>
+struct TileWeights {
+  float wsum[NRG][NG];
+  int wexp[NRG][NG];
+};
+
+// PHASE 0: the whole tile.  PHASE 1: scores, softmax and the weight digits
+// only (reads the tile's K codes and records; leaves tw); PHASE 2: the value
+// MFMAs only (reads the tile's V codes and tw), so that a caller can load the
+// next tile's K part while phase 2 runs and its V part while phase 1 runs.
+template <int G, int NRG, bool FULL, int NG, bool REC, int PHASE = 0>  // FULL: all 8 pages exist and every token is below t_end
 __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG>& t, int pbase, int t_beg, int t_end,
                                              int lg, int lr, const i32x8* qa, const int* qsc, const float (*qsr)[NG],
-                                             uint8_t* wt, uint8_t* rb, WaveState<NRG, NG>& st) {
+                                             uint8_t* wt, uint8_t* rb, WaveState<NRG, NG>& st,
+                                             TileWeights<NRG, NG>* tw = nullptr) {
+  float wsum[NRG][NG];  // sum of the weights as the digits carry them
+  int wexp[NRG][NG];    // every weight of this lane's head and group below 2^wexp
+  if constexpr (PHASE == 2) {
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+      for (int jg = 0; jg < NG; ++jg) {
+        wsum[rg][jg] = tw->wsum[rg][jg];
+        wexp[rg][jg] = tw->wexp[rg][jg];
+      }
+  }
+  if constexpr (PHASE != 2) {
   uint2 meta[8][NG];
   if constexpr (REC) {
     spread_records(t, rb, lr, meta);
@@ -880,8 +944,6 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
   }
   }
   // ---- online softmax, weights, weight digits -> LDS ----
-  float wsum[NRG][NG];  // sum of the weights as the digits carry them
-  int wexp[NRG][NG];    // every weight of this lane's head and group below 2^wexp
 #pragma unroll
   for (int rg = 0; rg < NRG; ++rg) {
     const bool hv = 4 * rg + lg < p.gw;
@@ -954,6 +1016,17 @@ __device__ __forceinline__ void compute_tile(const SplitParams& p, const Tile<NG
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }  // phase 1
+  if constexpr (PHASE == 1) {
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+      for (int jg = 0; jg < NG; ++jg) {
+        tw->wsum[rg][jg] = wsum[rg][jg];
+        tw->wexp[rg][jg] = wexp[rg][jg];
+      }
+    return;
+  }
 
   // ---- values: acc[rg][nn] += weight digits x V codes (channel vch(nn) of
   // column lr: 4 lr + nn for nn < 4, 64 + 4 lr + nn - 4 above) ----
@@ -1148,17 +1221,37 @@ __global__ __launch_bounds__(256, 2) void int2_split_kernel(SplitParams p) {
     auto compute = [&](const Tile<NG>& t, int pbase) {
       compute_tile<G, NRG, false, NG, kRecLds>(p, t, pbase, t_beg, t_end, lg, lr, qa, qsc, qsr, wt, rb, st);
     };
-    if constexpr (NRG > 1 || NG > 2) {  // one tile in flight per wave (registers)
+    if constexpr (NRG > 1 || NG > 2) {
+      // registers for one tile only, its two parts loaded a phase ahead: tile
+      // k + 1's K codes and records go out while tile k's values are computed
+      // (tile k's K part is dead by then), its V codes while its own scores
+      // are.  Past the last step the table is empty and the loads re-read page
+      // 0's blocks (cache resident), never computed.
+      static_assert(!kRecLds, "the two-part loads read each token's records per lane");
+      Tile<NG> t;
+      TileWeights<NRG, NG> tw;
+      auto phase1 = [&](int pbase) {
+        compute_tile<G, NRG, false, NG, false, 1>(p, t, pbase, t_beg, t_end, lg, lr, qa, qsc, qsr, wt, rb, st, &tw);
+      };
+      auto phase2 = [&] {
+        compute_tile<G, NRG, false, NG, false, 2>(p, t, 0, t_beg, t_end, lg, lr, qa, qsc, qsr, wt, rb, st, &tw);
+      };
+      load_tile_k<NG>(base_h, stride, tab, 0, lg, lr, t);
+      load_tile_v<NG>(base_h, stride, tab, 0, lg, lr, t);
       for (int s = 0;; ++s) {
         const int k = 2 * s;
-        Tile<NG> t;
-        load_tile<NG, kRecLds>(base_h, stride, tab, 0, lg, lr, t);
-        compute(t, pbase_of(k));
-        load_tile<NG, kRecLds>(base_h, stride, tab, 1, lg, lr, t);
-        compute(t, pbase_of(k + 1));
-        if (s + 1 >= ns) break;
-        tab = table_ready(p, raw_next, P0, P1, ph, ts, k + 2, ntw);
+        phase1(pbase_of(k));
+        load_tile_k<NG>(base_h, stride, tab, 1, lg, lr, t);
+        phase2();
+        load_tile_v<NG>(base_h, stride, tab, 1, lg, lr, t);
+        phase1(pbase_of(k + 1));
+        const bool more = s + 1 < ns;
+        tab = table_ready(p, raw_next, P0, P1, ph, ts, k + 2, more ? ntw : 0);
         raw_next = table_load(btr, P0, P1, ph, ts, k + 4);
+        load_tile_k<NG>(base_h, stride, tab, 0, lg, lr, t);
+        phase2();
+        load_tile_v<NG>(base_h, stride, tab, 0, lg, lr, t);
+        if (!more) break;
       }
     } else {  // two tiles in flight per wave: tile k + 1's loads go out before tile k is computed
       Tile<NG> ta, tb;
