@@ -368,7 +368,10 @@ def main():
     b_qop = B * HQ * (4 * 128 + 4 * (128 // G))
     b_split = b_hist + b_bt_hist + b_qop
     achieved = b_split / split_s / 1e9 if split_s else None
-    traffic = load_traffic(b_split) if G == 128 else None  # the committed counters cover group 128
+    # the committed counters were taken on the long-context workload at its own
+    # window, group 128 and no sinks: any other workload reports no traffic
+    same_workload = args.config == 3 and G == 128 and S == 0 and args.window is None
+    traffic = load_traffic(b_split) if same_workload else None
     line = {
         "metric": "INT2 decode-attn HBM GB/s (% of peak) + decode tokens/s at 100K ctx vs bf16 KV",
         "value": step_bytes_int2 / dt / 1e9,
